@@ -1,0 +1,299 @@
+"""Attention references (oracle side; test infrastructure only).
+
+Three results are computed, all on one (batch, head) slice with float64
+arithmetic unless a step says otherwise:
+
+* ``exact_attention`` -- softmax(q k^T / sqrt(D)) v on the unquantised bf16
+  inputs: the ground truth the error criterion is measured against.
+* ``plain_mx_attention`` -- the "exp-then-quantize" path: MX operands, exact
+  max and exact exp, then the probabilities MX-quantised before the PV
+  product.  Its error is the floor set by quantising the GEMM operands
+  (Fused-Softmax for efficient quantized attention, summary; EFQ-Softmax:
+  Exp-Free Quantization for Softmax, abstract).
+* ``fused_attention`` -- Fused-Softmax attention as specified below.
+
+Fused-Softmax, as the pages outline it and as read here
+-------------------------------------------------------
+The pages say that softmax is reformulated and approximated so that its
+dominant work folds into the attention GEMMs: the max subtraction and the
+exponential go into the score product, the exponential is approximated "with
+a fast method" and fused with the MX quantisation of P, probabilities are
+summed on the matrix cores, and the row max is frozen speculatively with a
+fallback when the guess is wrong (Fused-Softmax for efficient quantized
+attention, summary; Moving softmax to matrix operations speeds up AI
+inference by over 2x, "Read it as" and the "How it works" figure).  They give
+no formulas, so each step below is a reading:
+
+1. q, k are MX-quantised along D, v along the key axis (blocks of 32 keys
+   aligned at key 0): the MX blocks lie along each product's reduction axis.
+2. s_ij = sum_d q^_id k^_jd.  Key j is visible to row i if j < S and, when
+   causal, j <= i.
+3. Frozen max (``frozen_max``): from the visible keys among the first 128,
+   m~_i = fp32(max(window max, mean + z_i * std) + bias), population std,
+   z_i = sqrt(2 ln n_i) + 1 with n_i the row's visible keys.  The pages fix
+   no rule; the mean + z*std term is the expected Gaussian extreme over n_i
+   keys plus one standard deviation of margin, so that a well-behaved row
+   rarely exceeds it.  ``bias`` is a test hook (0 in normal use).
+4. Exponential folded into the product.  With d_ij = fp32(s_ij - m~_i)
+   (the max subtraction, one rounding) and t_ij = log2(e) d_ij / sqrt(D),
+   the probability is the bit-pattern exponential: the float32 number whose
+   bit pattern is the integer 2**23 * (127 + x) has the value
+   2**floor(x) * (1 + frac(x)), i.e. 2**x linearly interpolated between
+   integer exponents.  One fp32 FMA,
+       y_ij = fp32(beta * d_ij + 2**23 * (127 + emax + Delta_b - kappa_i)),
+       beta = fp32(2**23 * log2(e) / sqrt(D)),
+   followed by truncation to an unsigned integer (0 below zero) gives those
+   bits with 16 or more fraction bits of x.
+5. MX quantisation of P.  Per block b of 32 keys of a row (keys
+   [32b, 32b+32), visible keys only), E_b = E_top + floor(c_b / 2**M) with
+   c_b = round_half_even(alpha * max_j d_ij), alpha = beta / 2**(23-M): the
+   binade of the block's largest value counted in element codes.  The block
+   is shifted up by Delta_b = min(E_top - (E_b - kappa_i), 127 - emax) whole
+   binades so that its largest value lands in the top binade, and its E8M0
+   scale is 2**-(emax + Delta_b).  Each element is the value of step 4
+   rounded to the nearest element (ties to even, saturating at the largest
+   finite one), which puts values below the normal range on the subnormal
+   grid by value; P~_ij = decode(code_ij) * 2**-(emax + Delta_b), about
+   2**(t_ij - kappa_i).
+6. Fallback: a row whose guess was too low has some block with E_b > E_top
+   (its scores exceed m~ by at least the top binade's headroom).  The row is
+   recomputed with its reference raised by the whole number of binades
+   kappa_i = max(0, max_b E_b - E_top).  Raising the reference by whole
+   binades leaves every code of the row unchanged and lowers every block
+   scale by 2**kappa_i (except where a block shift reaches the E8M0 floor),
+   so the kernel can realise the recomputation as an exact power-of-two
+   rescale of its running sums.
+7. O_i = sum_j P~_ij v^_j, l_i = sum_j P~_ij (the same quantised P~ in both,
+   as EFQ-Softmax does for its numerator and denominator), and
+   out_i = bf16(O_i / l_i).
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional, Sequence, Tuple
+
+import numpy as np
+
+from .mx import (FORMATS, BLOCK, Format, decode, encode_values, round_to_format,
+                 mx_quantize, mx_dequantize, bf16_round)
+
+WINDOW = 128          # keys that feed the frozen-max guess
+Z_MARGIN = 1.0        # standard deviations above the expected Gaussian extreme
+LOG2E = 1.0 / math.log(2.0)
+
+
+def rel_l2(a: np.ndarray, b: np.ndarray) -> float:
+    """||a - b||_2 / ||b||_2 over all elements."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm((a - b).ravel()) / np.linalg.norm(b.ravel()))
+
+
+def _fmt(f) -> Format:
+    return f if isinstance(f, Format) else FORMATS[f]
+
+
+def _rows(rows, S) -> np.ndarray:
+    return np.arange(S) if rows is None else np.asarray(rows, np.int64)
+
+
+def _visible(rows: np.ndarray, S: int, causal: bool) -> np.ndarray:
+    j = np.arange(S)[None, :]
+    if causal:
+        return j <= rows[:, None]
+    return np.ones((rows.size, S), dtype=bool)
+
+
+def quantized_operands(q, k, v, fmt):
+    """Dequantised q^, k^ (blocks along D) and v^ (blocks along keys)."""
+    f = _fmt(fmt)
+    S = k.shape[0]
+    qh = mx_dequantize(*mx_quantize(q, f), f)[:, : q.shape[1]]
+    kh = mx_dequantize(*mx_quantize(k, f), f)[:, : k.shape[1]]
+    vt = mx_dequantize(*mx_quantize(np.ascontiguousarray(v.T), f), f)[:, :S]
+    return qh, kh, np.ascontiguousarray(vt.T)
+
+
+def exact_attention(q, k, v, causal: bool = False, rows=None) -> np.ndarray:
+    """float64 softmax(q k^T / sqrt(D)) v for one head; q, k, v are [S, D]."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    S, D = k.shape
+    rows = _rows(rows, S)
+    s = (q[rows] @ k.T) / math.sqrt(D)
+    vis = _visible(rows, S, causal)
+    s = np.where(vis, s, -np.inf)
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p = p / p.sum(axis=1, keepdims=True)
+    return p @ v
+
+
+def frozen_max(s: np.ndarray, vis: np.ndarray, bias: float = 0.0) -> np.ndarray:
+    """Speculative row max from the first WINDOW keys (step 3 of the module doc).
+
+    ``s``: float64 scores [R, S]; ``vis``: visibility [R, S].  Returns fp32
+    values as float64.  The pages say only that the max is fixed
+    speculatively and frozen before the fused product (Moving softmax to
+    matrix operations speeds up AI inference by over 2x, "Read it as" and
+    the "How it works" figure); the window, the extreme-value term and its
+    margin are this build's reading.
+    """
+    w = vis[:, :WINDOW]
+    sw = s[:, :WINDOW]
+    cnt = w.sum(axis=1)
+    n_vis = vis.sum(axis=1)
+    wmax = np.where(w, sw, -np.inf).max(axis=1)
+    mean = np.where(w, sw, 0.0).sum(axis=1) / cnt
+    var = np.where(w, (sw - mean[:, None]) ** 2, 0.0).sum(axis=1) / cnt
+    z = np.sqrt(2.0 * np.log(n_vis)) + Z_MARGIN
+    guess = np.maximum(wmax, mean + z * np.sqrt(var)) + bias
+    return guess.astype(np.float32).astype(np.float64)
+
+
+def fused_beta(D: int) -> float:
+    """beta = fp32(2**23 * log2(e) / sqrt(D)): score units -> fp32 exponent-field units."""
+    return float(np.float32((2 ** 23) * LOG2E / math.sqrt(D)))
+
+
+def fused_alpha(fmt, D: int) -> float:
+    """alpha = beta / 2**(23-M): score units -> element-code units (exact in fp32)."""
+    f = _fmt(fmt)
+    return fused_beta(D) / 2 ** (23 - f.mbits)
+
+
+def fma_f32(a: np.ndarray, b: np.ndarray, c: np.ndarray) -> np.ndarray:
+    """fp32 fused multiply-add of fp32 operands, rounded once (nearest, ties even).
+
+    a*b is exact in float64; a + c is resolved with an error-free two-sum so
+    that the single rounding to fp32 is exact even on float64 ties.
+    """
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    c = np.asarray(c, np.float64)
+    p = a * b
+    s = p + c
+    bb = s - p
+    err = (p - (s - bb)) + (c - bb)
+    with np.errstate(invalid="ignore", over="ignore"):
+        r = s.astype(np.float32).astype(np.float64)
+        up = r > s
+        other = np.where(up, np.nextafter(r.astype(np.float32), np.float32(-np.inf)),
+                         np.nextafter(r.astype(np.float32), np.float32(np.inf))).astype(np.float64)
+        lo = np.where(up, other, r)
+        hi = np.where(up, r, other)
+        tie = np.isfinite(s) & ((s - lo) == (hi - s))
+    r = np.where(tie & (err > 0), hi, np.where(tie & (err < 0), lo, r))
+    return r
+
+
+def bits_to_f32(u: np.ndarray) -> np.ndarray:
+    """float32 value (as float64) of unsigned 32-bit patterns."""
+    return np.asarray(u, np.uint64).astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def trunc_u32(y: np.ndarray) -> np.ndarray:
+    """Truncate toward zero to an unsigned 32-bit integer; below zero or NaN give 0."""
+    y = np.asarray(y, np.float64)
+    y = np.where(np.isnan(y), 0.0, y)
+    return np.clip(np.trunc(y), 0, 2.0 ** 32 - 1).astype(np.uint64)
+
+
+def fused_probabilities(s: np.ndarray, m_tilde: np.ndarray, vis: np.ndarray, fmt,
+                        D: int) -> Dict[str, np.ndarray]:
+    """Steps 4-6 of the module doc for rows of scores ``s`` [R, S].
+
+    Returns the P~ values (float64), the element codes, the per-block shifts
+    Delta, the E8M0 scale bytes of P~ and the per-row binade offset kappa
+    (> 0 for rows that fell back).
+    """
+    f = _fmt(fmt)
+    M = f.mbits
+    E_top = f.emax + f.bias
+    cap = 127 - f.emax
+    R, S = s.shape
+    beta = fused_beta(D)
+    alpha = fused_alpha(f, D)
+    d = (s - m_tilde[:, None]).astype(np.float32).astype(np.float64)
+    d = np.where(vis, d, -np.inf)
+    nb = (S + BLOCK - 1) // BLOCK
+    dp = np.full((R, nb * BLOCK), -np.inf)
+    dp[:, :S] = d
+    g = dp.reshape(R, nb, BLOCK).max(axis=2)         # -inf for blocks with no visible key
+    c = np.rint(alpha * g)                            # alpha*g is exact in float64
+    E = E_top + np.floor(c / (2 ** M))
+    kappa = np.maximum(0.0, np.max(E, axis=1) - E_top)
+    Eb = E - kappa[:, None]
+    delta = np.where(np.isfinite(Eb), np.minimum(E_top - Eb, cap), cap)
+    delta_full = np.repeat(delta, BLOCK, axis=1)[:, :S]
+    base = (2.0 ** 23) * (127 + f.emax + delta_full - kappa[:, None])
+    y = fma_f32(np.float64(beta), np.where(vis, d, 0.0), base)
+    y = np.where(vis, y, -np.inf)
+    p = bits_to_f32(trunc_u32(y))
+    vals = round_to_format(p, f)
+    code = encode_values(vals, f).astype(np.int64)
+    P = vals * np.ldexp(1.0, (-f.emax - delta_full).astype(np.int32))
+    return {
+        "P": P,
+        "codes": code,
+        "delta": delta.astype(np.int64),
+        "scale_bytes": (127 - f.emax - delta).astype(np.int64),
+        "kappa": kappa.astype(np.int64),
+    }
+
+
+def fused_attention(q, k, v, fmt, causal: bool = False, rows=None, bias: float = 0.0,
+                    return_info: bool = False):
+    """Fused-Softmax attention output (bf16 values as float64) for one head.
+
+    ``q, k, v`` are [S, D] arrays of bf16 values; ``rows`` selects query rows
+    (all by default).  With ``return_info`` also returns the frozen max, the
+    fallback offsets and the P~ values.
+    """
+    f = _fmt(fmt)
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    S, D = k.shape
+    rows = _rows(rows, S)
+    qh, kh, vh = quantized_operands(q[rows] if rows.size else q[:0], k, v, f)
+    s = qh @ kh.T
+    vis = _visible(rows, S, causal)
+    m_tilde = frozen_max(s, vis, bias)
+    fp = fused_probabilities(s, m_tilde, vis, f, D)
+    P = fp["P"]
+    O = P @ vh
+    l = P.sum(axis=1)
+    out = bf16_round(O / l[:, None])
+    if not return_info:
+        return out
+    info = dict(fp)
+    info.update(m_tilde=m_tilde, l=l, scores=s)
+    return out, info
+
+
+def plain_mx_attention(q, k, v, fmt, causal: bool = False, rows=None) -> np.ndarray:
+    """Exp-then-quantize attention (bf16 values as float64) for one head.
+
+    The same MX operands as ``fused_attention``; exact row max and exact exp
+    in float64; P MX-quantised along the keys (blocks of 32 aligned at key 0,
+    the same blocks as the fused path); out = bf16(sum P^ v^ / sum P^).
+    """
+    f = _fmt(fmt)
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    S, D = k.shape
+    rows = _rows(rows, S)
+    qh, kh, vh = quantized_operands(q[rows], k, v, f)
+    s = qh @ kh.T
+    vis = _visible(rows, S, causal)
+    s = np.where(vis, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    P = np.where(vis, np.exp((s - m) / math.sqrt(D)), 0.0)
+    Pq = mx_dequantize(*mx_quantize(P, f), f)[:, :S]
+    O = Pq @ vh
+    l = Pq.sum(axis=1)
+    return bf16_round(O / l[:, None])
