@@ -1,0 +1,156 @@
+/*
+ * fsa.h -- C ABI of the MI355X (gfx950) fused-softmax MX attention library.
+ *
+ * The operation is the forward pass of Fused-Softmax Attention: FlashAttention-
+ * style attention whose Q K^T and P V products run on MX-quantised operands
+ * (MXFP8 E4M3, MXFP6 E2M3, MXFP4 E2M1: 32-element blocks sharing one E8M0
+ * scale), with the row max frozen speculatively, the exponential approximated
+ * and folded together with the MX quantisation of P into the products, the
+ * probabilities summed on the matrix cores, and a fallback for rows whose
+ * scores exceed the frozen max ("Fused-Softmax for efficient quantized
+ * attention", summary; "Moving softmax to matrix operations speeds up AI
+ * inference by over 2x", "Read it as" and the "How it works" figure).  The
+ * pages give the method only in outline; the exact definitions the kernels
+ * implement (frozen-max rule, code map, fallback) are the ones written out
+ * step by step in the oracle's module documentation.
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers (HIP device memory, e.g. torch
+ *     tensors on a ROCm device).  The caller owns them; the library never
+ *     frees caller memory.  Outputs must not alias inputs.
+ *   - bf16 tensors are row-major and contiguous.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default
+ *     stream.  Calls only enqueue work (no host synchronisation); inputs must
+ *     stay alive until the stream has run the work.  Device faults surface at
+ *     the caller's next synchronisation, not from the call.
+ *   - Return value: FSA_OK (0) or a negative fsa_status.  Argument errors are
+ *     detected before anything is enqueued.  No C++ exception crosses the ABI.
+ *   - Calls on distinct streams are thread-safe.  The library keeps a per-
+ *     device workspace (quantised operands) that it allocates on first use and
+ *     grows as needed; calls that share a device and overlap in time on
+ *     different streams serialise on the workspace through stream ordering of
+ *     the caller's choosing, so give concurrent attention calls on one device
+ *     the same stream.
+ */
+#ifndef FSA_H
+#define FSA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fsa_status {
+  FSA_OK = 0,
+  FSA_ERR_INVALID_ARG = -1,  /* null pointer, non-positive or overflowing size, bad enum */
+  FSA_ERR_UNSUPPORTED = -2,  /* valid but not implemented (e.g. head dim other than 64/128) */
+  FSA_ERR_HIP = -3,          /* a HIP runtime call or kernel launch failed */
+  FSA_ERR_NO_MEMORY = -4     /* workspace allocation failed */
+} fsa_status;
+
+typedef enum fsa_fmt {
+  FSA_MXFP8_E4M3 = 0,
+  FSA_MXFP6_E2M3 = 1,
+  FSA_MXFP4_E2M1 = 2
+} fsa_fmt;
+
+/*
+ * fsa_quantize_mx -- MX block quantisation of a bf16 tensor.
+ *
+ * MX operands of the attention products (Fused-Softmax for efficient
+ * quantized attention, summary: "MXFP8, MXFP6 and MXFP4 kernels"); encodings
+ * and block-scale rule of the OCP Microscaling Formats v1.0 specification:
+ * scale X = clamp(floor(log2(amax)) - emax, -127, 127) (X = -127 for an
+ * all-zero block), elements x / 2^X rounded to nearest-even and saturated to
+ * the largest finite magnitude, the input's sign kept on zeros; a block that
+ * holds NaN or Inf gets scale byte 0xFF and zero codes.
+ *
+ * x_bf16 : device, bf16 [batch][rows][cols].
+ * block_along_rows == 0 : blocks are 32 consecutive elements along `cols`.
+ *     codes  : device, [batch][rows][ceil(cols/32)*32 * bits/8] bytes.
+ *     scales : device, [batch][rows][ceil(cols/32)] E8M0 bytes.
+ * block_along_rows == 1 : blocks run along `rows`; the output is transposed.
+ *     codes  : device, [batch][cols][ceil(rows/32)*32 * bits/8] bytes.
+ *     scales : device, [batch][cols][ceil(rows/32)] E8M0 bytes.
+ * Packing (bits = 8, 6, 4): FP8 one byte per element; FP6 a little-endian
+ * bit stream with element i of a block at bits [6i, 6i+6) (24 bytes per
+ * block); FP4 two elements per byte, the lower-indexed in the low nibble.
+ * Padding elements of a partial tail block have code 0.
+ * Errors: FSA_ERR_INVALID_ARG for null pointers, sizes <= 0, more than 2^31
+ * blocks, an unknown fmt or block_along_rows not 0/1; FSA_ERR_HIP if the
+ * launch fails.
+ */
+int fsa_quantize_mx(const void* x_bf16, void* codes, void* scales_e8m0,
+                    int64_t batch, int64_t rows, int64_t cols,
+                    int fmt, int block_along_rows, void* stream);
+
+/*
+ * fsa_attention_fwd -- fused-softmax attention forward with MX operands.
+ *
+ * q, k, v : device, bf16 [B][H][S][D]; out : device, bf16 [B][H][S][D].
+ * Softmax scale 1/sqrt(D).  D must be 64 or 128 (else FSA_ERR_UNSUPPORTED).
+ * fmt : element format of Q, K, V and P (fsa_fmt).  causal : 0 or 1 (key j
+ * visible to query i iff j <= i).
+ * The call MX-quantises Q, K (blocks along D) and V (blocks along the keys)
+ * into the library workspace, then runs one fused kernel: frozen max from
+ * the first 128 keys, scores with the max subtraction folded into the
+ * matrix-core accumulator, the bit-pattern exponential and MX quantisation
+ * of P in the accumulator epilogue, P V and the row sums (P times a ones
+ * block) on the matrix cores, and the whole-binade fallback for rows whose
+ * scores exceed the frozen max, applied as an exact power-of-two rescale.
+ * Errors: FSA_ERR_INVALID_ARG (null pointers, non-positive sizes, B*H*S*D
+ * beyond 2^40, unknown fmt, causal not 0/1), FSA_ERR_UNSUPPORTED (D not
+ * 64/128), FSA_ERR_NO_MEMORY (workspace), FSA_ERR_HIP (launch).
+ */
+int fsa_attention_fwd(const void* q, const void* k, const void* v, void* out,
+                      int B, int H, int S, int D, int fmt, int causal, void* stream);
+
+/*
+ * fsa_attention_bf16_ref -- plain BF16 flash attention (in-house baseline).
+ *
+ * The "BF16 attention" the pages compare against (Fused-Softmax for
+ * efficient quantized attention, summary; the "Softmax (Vector)" path of the
+ * "How it works" figure): bf16 matrix-core products with fp32 accumulation,
+ * exact exponential, online row max and rescaling on the vector units.
+ * Same tensor layout and errors as fsa_attention_fwd (no fmt).
+ */
+int fsa_attention_bf16_ref(const void* q, const void* k, const void* v, void* out,
+                           int B, int H, int S, int D, int causal, void* stream);
+
+/* Test and benchmark hooks for fsa_attention_fwd_ex.  Zero-initialise. */
+typedef struct fsa_options {
+  /* Added to every frozen max (score units).  A large negative value makes
+   * every row fall back; 0 in normal use. */
+  float guess_bias;
+  /* Optional device int32 [B][H][S]: receives each row's fallback offset in
+   * binades (0 for rows whose scores stayed under the frozen max). */
+  int32_t* row_kappa;
+  /* Optional device float [B][H][S]: receives each row's frozen max. */
+  float* row_max_guess;
+  /* Optional hipEvent_t (as void*) recorded on `stream` between the
+   * quantisation kernels and the attention kernel, for kernel-only timing. */
+  void* event_after_quantize;
+  /* Optional host array of H fsa_fmt values: per-head element format (one
+   * launch for a hybrid schedule).  NULL: every head uses `fmt`. */
+  const int* head_fmt;
+} fsa_options;
+
+/* fsa_attention_fwd with hooks; opt may be NULL.  Same errors. */
+int fsa_attention_fwd_ex(const void* q, const void* k, const void* v, void* out,
+                         int B, int H, int S, int D, int fmt, int causal,
+                         const fsa_options* opt, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* fsa_strerror(int status);
+
+/* Frees the current device's workspace.  Call only when no enqueued work
+ * still uses it (e.g. after a device synchronise).  Returns FSA_OK or
+ * FSA_ERR_HIP. */
+int fsa_release_workspace(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FSA_H */

@@ -1,0 +1,125 @@
+// Device-side definitions shared by the MX quantiser and the fused attention
+// kernel (gfx950 / CDNA4).
+//
+// Element formats are those of the OCP Microscaling Formats v1.0
+// specification, which the pages name as MXFP8, MXFP6 and MXFP4
+// (Fused-Softmax for efficient quantized attention, summary).
+//
+// Matrix-core facts used here (scaled MFMA V_MFMA_SCALE_F32_16X16X128_F8F6F4,
+// measured on gfx950 with one-hot probes):
+//   * A is 16 x 128 (rows x K), B is 128 x 16 (K x columns), C is 16 x 16;
+//     lane l = 16*g + r holds row r of A / column r of B, and C rows 4g..4g+3
+//     of column r.
+//   * FP6 and FP4 operands: lane (g, r) holds the 32 consecutive K elements
+//     [32g, 32g+32) (a little-endian bit stream, element i at bit bits*i) and
+//     its scale byte applies to exactly those: one lane = one MX block.
+//   * FP8 operands: lane (g, r) holds K elements [16g, 16g+16) in bytes 0-15
+//     and [64+16g, 64+16g+16) in bytes 16-31; the scale for K block c
+//     (elements [32c, 32c+32)) is the scale operand of lane group c.
+//   * The scaled conversions divide by their scale operand, round to nearest
+//     even; FP4/FP6 saturate, FP8 overflows to NaN.  The FP6 32-element
+//     conversion places element i of its first source at bit 12i and element
+//     i of its second source at bit 12i+6.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fsa {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v6i __attribute__((ext_vector_type(6)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef short v2s __attribute__((ext_vector_type(2)));
+
+enum { FMT_E4M3 = 0, FMT_E2M3 = 1, FMT_E2M1 = 2 };
+
+// Per-format constants.  emax: exponent of the largest normal binade;
+// e_top: its biased exponent; cap: the largest upward block shift that keeps
+// the E8M0 byte 127 - emax - shift >= 0.
+template <int F> struct Fmt;
+template <> struct Fmt<FMT_E4M3> {
+  static constexpr int bits = 8, mbits = 3, bias = 7, emax = 8, e_top = 15;
+  static constexpr int mfma = 0;                 // cbsz / blgp operand format code
+  static constexpr float maxval = 448.0f;
+  static constexpr uint32_t one_code = 0x38;     // 1.0
+};
+template <> struct Fmt<FMT_E2M3> {
+  static constexpr int bits = 6, mbits = 3, bias = 1, emax = 2, e_top = 3;
+  static constexpr int mfma = 2;
+  static constexpr float maxval = 7.5f;
+  static constexpr uint32_t one_code = 0x08;
+};
+template <> struct Fmt<FMT_E2M1> {
+  static constexpr int bits = 4, mbits = 1, bias = 1, emax = 2, e_top = 3;
+  static constexpr int mfma = 4;
+  static constexpr float maxval = 6.0f;
+  static constexpr uint32_t one_code = 0x2;
+};
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// floor(log2(a)) of a finite a > 0 (fp32 subnormals included).
+__device__ __forceinline__ int floor_log2(float a) {
+  uint32_t u = __float_as_uint(a);
+  int e = (int)((u >> 23) & 0xFF);
+  if (e != 0) return e - 127;
+  return (31 - __clz(u & 0x7FFFFF)) - 149;
+}
+
+// 2^n as float for -126 <= n <= 127.
+__device__ __forceinline__ float exp2i(int n) {
+  return __uint_as_float((uint32_t)(n + 127) << 23);
+}
+
+// Convert 32 fp32 values (already divided by the block scale) to packed
+// element codes with round-to-nearest-even and saturation.  Output words
+// follow the operand packing: FP8 8 words, FP6 6 words, FP4 4 words.
+template <int F> struct Pack32;
+
+template <> struct Pack32<FMT_E4M3> {
+  static __device__ __forceinline__ void run(const float* y, uint32_t* w) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v2s lo = {0, 0};
+      float a0 = __builtin_fminf(__builtin_fmaxf(y[4 * i + 0], -448.0f), 448.0f);
+      float a1 = __builtin_fminf(__builtin_fmaxf(y[4 * i + 1], -448.0f), 448.0f);
+      float a2 = __builtin_fminf(__builtin_fmaxf(y[4 * i + 2], -448.0f), 448.0f);
+      float a3 = __builtin_fminf(__builtin_fmaxf(y[4 * i + 3], -448.0f), 448.0f);
+      lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, a0, a1, 1.0f, false);
+      lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, a2, a3, 1.0f, true);
+      w[i] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+    }
+  }
+};
+
+template <> struct Pack32<FMT_E2M3> {
+  static __device__ __forceinline__ void run(const float* y, uint32_t* w) {
+    v16f ev, od;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { ev[i] = y[2 * i]; od[i] = y[2 * i + 1]; }
+    v6i r = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) w[i] = (uint32_t)r[i];
+  }
+};
+
+template <> struct Pack32<FMT_E2M1> {
+  static __device__ __forceinline__ void run(const float* y, uint32_t* w) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t r = 0;
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * i + 0], y[8 * i + 1], 1.0f, 0);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * i + 2], y[8 * i + 3], 1.0f, 1);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * i + 4], y[8 * i + 5], 1.0f, 2);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * i + 6], y[8 * i + 7], 1.0f, 3);
+      w[i] = r;
+    }
+  }
+};
+
+}  // namespace fsa

@@ -1,0 +1,62 @@
+// Host-visible launch interfaces between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fsa {
+
+// MX quantiser geometry.  MODE 0: blocks along `cols`; output row o in
+// [0, batch*out_rows) maps to input row o % out_rows (rows >= `rows` are
+// padding and get zero codes and scale byte 0).  MODE 1: blocks along
+// `rows`, output row o in [0, batch*cols) is input column o % cols
+// (out_rows must equal cols).  Blocks b >= ceil(valid/32) up to nb_out are
+// zero padding.
+struct QuantArgs {
+  const uint16_t* x;
+  uint8_t* codes;
+  uint8_t* scales;
+  int64_t batch, rows, cols;
+  int64_t out_rows;      // output rows per batch
+  int64_t nb_out;        // blocks per output row
+  int64_t code_stride;   // bytes between output code rows
+  int64_t scale_stride;  // bytes between output scale rows
+};
+
+hipError_t launch_mx_quant(const QuantArgs& a, int fmt, int mode, hipStream_t stream);
+
+// Fused attention over MX operands prepared by the quantiser, for the heads
+// [h0, h0+hrun) of every batch entry.  Workspace slabs are indexed by
+// w = b*hrun + (h - h0):
+//   Q^ codes [BH][sq_alloc][D*bits/8], scales [BH][sq_alloc][D/32]
+//   K^ codes [BH][sk_alloc][D*bits/8], scales [BH][sk_alloc][D/32]
+//   V^ (transposed) codes [BH][D][sk_alloc*bits/8], scales [BH][D][sk_alloc/32]
+// sq_alloc covers every query tile of the grid, sk_alloc every key tile; the
+// padding holds zero codes.
+struct AttnArgs {
+  const uint8_t* qc; const uint8_t* qs;
+  const uint8_t* kc; const uint8_t* ks;
+  const uint8_t* vc; const uint8_t* vs;
+  uint16_t* out;                 // bf16 [B][H][S][D]
+  int32_t* row_kappa;            // optional [B][H][S]
+  float* row_mguess;             // optional [B][H][S]
+  int B, H, S;
+  int h0, hrun;                  // heads [h0, h0+hrun) of each batch entry
+  int sq_alloc, sk_alloc;
+  float alpha, beta, bias;
+};
+
+hipError_t launch_fsa_fwd(const AttnArgs& a, int fmt, int D, int causal, hipStream_t stream);
+int fsa_queries_per_workgroup();
+
+// Plain BF16 flash attention.
+struct Bf16Args {
+  const uint16_t* q; const uint16_t* k; const uint16_t* v;
+  uint16_t* out;
+  int BH, S;
+  float scale_log2;              // log2(e) / sqrt(D)
+};
+
+hipError_t launch_bf16_fa(const Bf16Args& a, int D, int causal, hipStream_t stream);
+
+}  // namespace fsa

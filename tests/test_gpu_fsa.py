@@ -1,0 +1,170 @@
+"""Fused-softmax attention on the GPU against the float64 oracle.
+
+Bar: relative L2 <= 2e-3 against the oracle's fused result on the same
+inputs, and on the small workload the error against exact attention stays
+within 1.1x the exp-then-quantize error.  Fallback offsets agree row by row
+(except rows within rounding of the overflow threshold, which are counted).
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+
+import workloads as W
+import oracle as O
+from gpu_helpers import announce, to_dev, from_dev_bf16, rel_l2
+
+pytestmark = pytest.mark.gpu
+FMTS = ["e4m3", "e2m3", "e2m1"]
+TOL = 2e-3
+
+
+def _run(q, k, v, fmt, causal=False, **kw):
+    import torch
+    import softmax_mx_quantize_amd as fsa
+    out, kap, mg = fsa.attention_fwd(to_dev(q), to_dev(k), to_dev(v), fmt, causal,
+                                     return_rows=True, **kw)
+    torch.cuda.synchronize()
+    return from_dev_bf16(out), kap.cpu().numpy(), mg.cpu().numpy()
+
+
+def _oracle_heads(q, k, v, fmts, causal=False, rows=None, bias=0.0):
+    B, H = q.shape[:2]
+    outs, kaps = [], []
+    for b in range(B):
+        for h in range(H):
+            qh, kh, vh = (W.bf16_bits_to_f64(x[b, h]) for x in (q, k, v))
+            o, info = O.fused_attention(qh, kh, vh, fmts[h], causal, rows=rows, bias=bias,
+                                        return_info=True)
+            outs.append(o)
+            kaps.append(info["kappa"])
+    return np.stack(outs), np.stack(kaps)
+
+
+def _check(gpu_out, gpu_kap, ref_out, ref_kap, rows=None):
+    B, H, S, D = gpu_out.shape
+    g = gpu_out.reshape(B * H, S, D)
+    kk = gpu_kap.reshape(B * H, S)
+    if rows is not None:
+        g = g[:, rows]
+        kk = kk[:, rows]
+    err = rel_l2(g, ref_out)
+    assert err <= TOL, err
+    agree = np.mean(kk == ref_kap)
+    assert agree >= 0.99, agree
+    return err
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_ragged_all_rows(fmt, D, causal):
+    S = 333                       # 3 key tiles, ragged; 3 query workgroups
+    announce("fsa small", fmt, D, causal, S)
+    q, k, v = (W.random_bf16((2, 2, S, D), seed, 1.3) for seed in (1, 2, 3))
+    g, kap, _ = _run(q, k, v, fmt, causal)
+    ref, rk = _oracle_heads(q, k, v, [fmt] * 2, causal)
+    _check(g, kap, ref, rk)
+
+
+@pytest.mark.parametrize("S", [1, 17, 128, 129, 640])
+def test_edge_lengths(S):
+    announce("fsa edge", S)
+    for fmt in FMTS:
+        for causal in (False, True):
+            q, k, v = (W.random_bf16((1, 1, S, 128), seed, 1.0) for seed in (4, 5, 6))
+            g, kap, _ = _run(q, k, v, fmt, causal)
+            ref, rk = _oracle_heads(q, k, v, [fmt], causal)
+            _check(g, kap, ref, rk)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_v_ones_gives_exactly_one(fmt):
+    announce("fsa v=1", fmt)
+    q, k = (W.random_bf16((1, 2, 300, 128), seed, 2.0) for seed in (7, 8))
+    v = W.f32_to_bf16_bits(np.ones((1, 2, 300, 128), np.float32))
+    for causal in (False, True):
+        g, _, _ = _run(q, k, v, fmt, causal)
+        assert np.array_equal(g, np.ones_like(g))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_forced_fallback_every_row(fmt):
+    announce("fsa forced fallback", fmt)
+    q, k, v = (W.random_bf16((1, 2, 400, 128), seed, 1.0) for seed in (9, 10, 11))
+    g, kap, _ = _run(q, k, v, fmt, False, guess_bias=-60.0)
+    assert np.all(kap > 0)
+    ref, rk = _oracle_heads(q, k, v, [fmt] * 2, False, bias=-60.0)
+    _check(g, kap, ref, rk)
+
+
+def test_tiny_workload_parity_and_error_criterion():
+    w = W.WORKLOADS["tiny"]
+    announce("fsa tiny workload")
+    q, k, v = W.generate(w)
+    g, kap, _ = _run(q, k, v, "e4m3")
+    ref, rk = _oracle_heads(q, k, v, list(w.head_fmts))
+    _check(g, kap, ref, rk)
+    ex, pl = [], []
+    for h in range(w.H):
+        qh, kh, vh = (W.bf16_bits_to_f64(x[0, h]) for x in (q, k, v))
+        ex.append(O.exact_attention(qh, kh, vh))
+        pl.append(O.plain_mx_attention(qh, kh, vh, "e4m3"))
+    ex, pl = np.stack(ex), np.stack(pl)
+    assert rel_l2(g[0], ex) <= 1.1 * rel_l2(pl, ex)
+
+
+def test_deterministic():
+    announce("fsa determinism")
+    q, k, v = (W.random_bf16((1, 4, 1000, 128), seed, 1.0) for seed in (12, 13, 14))
+    a, _, _ = _run(q, k, v, "e2m1")
+    b, _, _ = _run(q, k, v, "e2m1")
+    assert np.array_equal(a, b)
+
+
+def _full_size(name, heads, n_rows, head_fmt_call=True):
+    w = W.WORKLOADS[name]
+    announce("fsa full size", name)
+    q, k, v = W.generate(w)
+    hf = list(w.head_fmts)
+    uniform = len(set(hf)) == 1
+    if uniform:
+        g, kap, _ = _run(q, k, v, hf[0], w.causal)
+    else:
+        g, kap, _ = _run(q, k, v, hf[0], w.causal, head_fmt=hf)
+    rng = np.random.default_rng(99)
+    rows = np.sort(rng.choice(w.S, size=n_rows, replace=False))
+    errs = []
+    for h in heads:
+        extra = W.outlier_rows(w, 0, h)
+        rws = np.unique(np.concatenate([rows, extra[:16]]))
+        qh, kh, vh = (W.bf16_bits_to_f64(x[0, h]) for x in (q, k, v))
+        ref, info = O.fused_attention(qh, kh, vh, hf[h], w.causal, rows=rws, return_info=True)
+        errs.append(rel_l2(g[0, h, rws], ref))
+        assert errs[-1] <= TOL, (h, errs[-1])
+        assert np.mean(kap[0, h, rws] == info["kappa"]) >= 0.97
+        if extra.size:
+            # the planted rows fell back on the GPU too
+            assert np.mean(kap[0, h, extra] > 0) >= 0.9
+    return g, kap
+
+
+def test_full_size_video_dit_e4m3_sampled():
+    _full_size("video_dit_e4m3", heads=(0, 17, 39), n_rows=24)
+
+
+def test_full_size_video_dit_e2m3_sampled():
+    _full_size("video_dit_e2m3", heads=(3, 21), n_rows=24)
+
+
+def test_full_size_video_dit_e2m1_sampled():
+    _full_size("video_dit_e2m1", heads=(5, 30), n_rows=24)
+
+
+def test_full_size_outliers_e2m1_sampled():
+    _full_size("outliers_e2m1", heads=(0, 27), n_rows=16)
+
+
+def test_full_size_hybrid_long_sampled():
+    g, kap = _full_size("hybrid_long", heads=(0, 19, 20, 39), n_rows=8)

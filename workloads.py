@@ -81,9 +81,13 @@ WORKLOADS: Dict[str, Workload] = {
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (nearest, ties to even); returns uint16 bits."""
-    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    rounded = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
-    return rounded.astype(np.uint16)
+    b = np.array(x, dtype=np.float32, copy=True).view(np.uint32)
+    t = np.right_shift(b, np.uint32(16))
+    np.bitwise_and(t, np.uint32(1), out=t)
+    np.add(t, np.uint32(0x7FFF), out=t)
+    np.add(b, t, out=b)
+    np.right_shift(b, np.uint32(16), out=b)
+    return b.astype(np.uint16)
 
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -150,17 +154,27 @@ def outlier_rows(w: Workload, b: int, h: int) -> np.ndarray:
     return np.sort(r.choice(w.S, size=n, replace=False))
 
 
-def generate(w: Workload, heads: Optional[Sequence[Tuple[int, int]]] = None,
-             S: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """bf16 bits of q, k, v, each ``[B, H, S, D]`` (all heads), as uint16."""
+def generate(w: Workload, S: Optional[int] = None,
+             workers: int = 8) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """bf16 bits of q, k, v, each ``[B, H, S, D]`` (all heads), as uint16.
+
+    Heads are drawn in parallel threads; each head has its own streams, so
+    the result does not depend on the number of workers.
+    """
+    import concurrent.futures
     S = w.S if S is None else S
     shape = (w.B, w.H, S, w.D)
     q = np.empty(shape, np.uint16)
     k = np.empty(shape, np.uint16)
     v = np.empty(shape, np.uint16)
-    for b in range(w.B):
-        for h in range(w.H):
-            q[b, h], k[b, h], v[b, h] = generate_head(w, b, h, S)
+
+    def one(bh):
+        b, h = bh
+        q[b, h], k[b, h], v[b, h] = generate_head(w, b, h, S)
+
+    jobs = [(b, h) for b in range(w.B) for h in range(w.H)]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, workers)) as ex:
+        list(ex.map(one, jobs))
     return q, k, v
 
 
