@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Throughput of the fused-softmax MX attention forward on one MI355X.
+
+One step = one call of ``fsa_attention_fwd`` on the 16K-token Video-DiT-shaped
+workload (B=1, H=40, S=16384, D=128, non-causal, MXFP8 E4M3): MX quantisation
+of Q, K, V plus the fused attention kernel, inputs resident in HBM.  The same
+inputs are also timed with E2M3 and E2M1 operands and through the BF16
+flash-attention baseline.  FLOPs are 4*B*H*S^2*D (halved for causal).
+
+Prints ONE JSON line.  Options:
+  --gpus N        only 1 is supported (the path is a single-GPU kernel)
+  --steps K       timed steps (default 20)
+  --warmup W      untimed steps first (default 3)
+  --no-cpu        skip the CPU-oracle baseline
+  --only FMT      time only one element format (e4m3, e2m3, e2m1)
+  --copy-bytes N  also run one plain device copy of N bytes (counter calibration)
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"e4m3": 5000.0, "e2m3": 10100.0, "e2m1": 10100.0, "bf16": 2500.0}
+METRIC = "attention fwd TFLOP/s and % of MX MFMA peak (MXFP8/6/4, S=16K, D=128)"
+KERNEL_SOURCES = ("softmax_mx_quantize_amd/csrc/fsa_fwd.hip",
+                  "softmax_mx_quantize_amd/csrc/fsa_device.h")
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(fmt: str):
+    """HBM traffic per launch measured with rocprofv3 counters, if the kernel
+    source is unchanged since the measurement."""
+    p = os.path.join(ROOT, "profiles", "fsa_fwd_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("kernel_hash") != kernel_hash():
+        return None
+    return d.get("bytes_per_launch", {}).get(fmt)
+
+
+def time_fsa(fsa, torch, q, k, v, fmt, steps, warmup):
+    """Whole-step time (ms) and fused-kernel time (ms, from HIP events on the
+    stream the library launches on)."""
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fsa.attention_fwd(q, k, v, fmt, False, out=out)
+    torch.cuda.synchronize()
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for m in mids:          # create the underlying HIP events before the library records them
+        m.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fsa.attention_fwd(q, k, v, fmt, False, out=out, event_after_quantize=mids[i])
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    kern_ms = sum(m.elapsed_time(e) for m, e in zip(mids, ends)) / steps
+    return wall_ms, kern_ms, out
+
+
+def time_bf16(fsa, torch, q, k, v, steps, warmup):
+    out = torch.empty_like(q)
+    for _ in range(warmup):
+        fsa.attention_bf16_ref(q, k, v, False, out=out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fsa.attention_bf16_ref(q, k, v, False, out=out)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def cpu_baseline(w, budget_s: float = 15.0):
+    """The oracle as it stands, on a bounded sample: all keys for a growing
+    number of query rows of head 0, until about `budget_s` seconds of work."""
+    import numpy as np
+    import workloads as W
+    import oracle as O
+    q, k, v = (W.bf16_bits_to_f64(x) for x in W.generate_head(w, 0, 0))
+    rows_done, t_used, n = 0, 0.0, 8
+    rng = np.random.default_rng(0)
+    while t_used < budget_s:
+        rows = np.sort(rng.choice(w.S, n, replace=False))
+        t0 = time.perf_counter()
+        O.fused_attention(q, k, v, w.head_fmts[0], w.causal, rows=rows)
+        t_used += time.perf_counter() - t0
+        rows_done += n
+        n = min(2 * n, 256)
+    flops = 4.0 * rows_done * w.S * w.D
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except Exception:
+        cores = os.cpu_count()
+    return {
+        "value": flops / t_used / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": "%d query rows of head 0 against all %d keys (float64 numpy oracle incl. "
+                  "MX quantisation of that head's K and V per call), %.1f s" % (rows_done, w.S, t_used),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", default=None)
+    ap.add_argument("--copy-bytes", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: only --gpus 1 is supported; the fused attention path runs on one GPU "
+              "(heads shard across GPUs with no communication, see the design notes)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import softmax_mx_quantize_amd as fsa
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+    w = W.WORKLOADS["video_dit_e4m3"]
+    print("[bench] generating %s inputs" % w.name, file=sys.stderr, flush=True)
+    qb, kb, vb = W.generate(w)
+    dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = dev(qb), dev(kb), dev(vb)
+    flops = w.flops
+
+    fmts = [args.only] if args.only else ["e4m3", "e2m3", "e2m1"]
+    per = {}
+    for fmt in fmts:
+        print("[bench] timing fused %s" % fmt, file=sys.stderr, flush=True)
+        wall_ms, kern_ms, _ = time_fsa(fsa, torch, q, k, v, fmt, args.steps, args.warmup)
+        per[fmt] = {
+            "ms_per_step": wall_ms,
+            "tflops": flops / (wall_ms * 1e-3) / 1e12,
+            "kernel_ms": kern_ms,
+            "kernel_tflops": flops / (kern_ms * 1e-3) / 1e12,
+            "kernel_frac_of_peak": flops / (kern_ms * 1e-3) / 1e12 / PEAK_TFLOPS[fmt],
+            "peak_tflops": PEAK_TFLOPS[fmt],
+        }
+    bf16 = None
+    if not args.only:
+        print("[bench] timing bf16 baseline", file=sys.stderr, flush=True)
+        bms = time_bf16(fsa, torch, q, k, v, args.steps, args.warmup)
+        bf16 = {"ms_per_step": bms, "tflops": flops / (bms * 1e-3) / 1e12,
+                "frac_of_peak": flops / (bms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"]}
+        for fmt in fmts:
+            per[fmt]["speedup_vs_bf16"] = bms / per[fmt]["ms_per_step"]
+
+    if args.copy_bytes:
+        n = args.copy_bytes // 4
+        a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    head = fmts[0]
+    res = per[head]
+    traffic = stored_traffic(head)
+    line = {
+        "metric": METRIC,
+        "value": res["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"e4m3": "mxfp8_e4m3", "e2m3": "mxfp6_e2m3", "e2m1": "mxfp4_e2m1"}[head],
+        "data": "synthetic (seeded N(0,1) bf16, per-head gain U[0.5,2] on q and k)",
+        "config": {"workload": w.name if head == "e4m3" else "video_dit_" + head,
+                   "B": w.B, "H": w.H, "S": w.S, "D": w.D, "causal": w.causal,
+                   "fmt": head, "seed": w.seed},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": res["kernel_tflops"],
+            "peak": PEAK_TFLOPS[head],
+            "unit": "TFLOP/s",
+            "frac": res["kernel_frac_of_peak"],
+            "traffic": traffic,
+        },
+        "formats": per,
+        "bf16_baseline": bf16,
+    }
+    if not args.no_cpu:
+        print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -176,9 +176,9 @@ def test_planted_outliers_fall_back():
     rows = W.outlier_rows(ws, 0, 0)
     assert rows.size == 40
     out, info = O.fused_attention(q, k, v, "e2m1", rows=rows, return_info=True)
-    # the planted score is +8 sigma of the unmodified row; raising q's norm to plant it
-    # also widens the row's own spread, so a few rows stay within the guess's margin
-    assert np.mean(info["kappa"] > 0) >= 0.9
+    # the planted score is +8 sigma of the row (q keeps its norm): it always
+    # exceeds the guess by more than the top binade's headroom
+    assert np.mean(info["kappa"] > 0) >= 0.97
     # after the fallback the rows are as accurate as exp-then-quantize ones
     ex = O.exact_attention(q, k, v, rows=rows)
     pl = O.plain_mx_attention(q, k, v, "e2m1", rows=rows)

@@ -130,7 +130,9 @@ def generate_head(w: Workload, b: int, h: int,
     if w.outlier_frac > 0.0:
         # Give each chosen row one key whose raw score is outlier_sigma * sqrt(D),
         # i.e. +8 standard deviations of a unit-variance score after the 1/sqrt(D)
-        # softmax scale.  The key lies outside the first 128 keys.
+        # softmax scale.  q_i is rotated toward k_j with its norm kept, so the
+        # row's other scores keep their spread.  The key lies outside the first
+        # 128 keys.
         r = _rng(w.seed, _T_OUTLIER, b, h)
         n = int(math.floor(w.outlier_frac * S))
         rows = r.choice(S, size=n, replace=False)
@@ -139,8 +141,12 @@ def generate_head(w: Workload, b: int, h: int,
         target = w.outlier_sigma * math.sqrt(D)
         for i, j in zip(rows, keys):
             kj = kf[j]
+            u = kj / np.linalg.norm(kj)
             qi = q[i].astype(np.float64)
-            qi = qi + ((target - qi @ kj) / (kj @ kj)) * kj
+            c = target / np.linalg.norm(kj)               # wanted component along k_j
+            perp = qi - (qi @ u) * u
+            rest = max(qi @ qi - c * c, 0.0)
+            qi = c * u + math.sqrt(rest) * perp / max(np.linalg.norm(perp), 1e-30)
             q[i] = qi.astype(np.float32)
     return f32_to_bf16_bits(q), kb, f32_to_bf16_bits(v)
 
