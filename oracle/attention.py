@@ -40,25 +40,28 @@ no formulas, so each step below is a reading:
    bit pattern is the integer 2**23 * (127 + x) has the value
    2**floor(x) * (1 + frac(x)), i.e. 2**x linearly interpolated between
    integer exponents.  One fp32 FMA,
-       y_ij = fp32(beta * d_ij + 2**23 * (127 + emax + Delta_b - kappa_i)),
+       y_ij = fp32(beta * d_ij + 2**23 * (127 + pl + Delta_b - kappa_i)),
        beta = fp32(2**23 * log2(e) / sqrt(D)),
    followed by truncation to an unsigned integer (0 below zero) gives those
    bits with 16 or more fraction bits of x.
 5. MX quantisation of P.  Per block b of 32 keys of a row (keys
-   [32b, 32b+32), visible keys only), E_b = E_top + floor(c_b / 2**M) with
+   [32b, 32b+32), visible keys only), e_b = floor(c_b / 2**M) with
    c_b = round_half_even(alpha * max_j d_ij), alpha = beta / 2**(23-M): the
-   binade of the block's largest value counted in element codes.  The block
-   is shifted up by Delta_b = min(E_top - (E_b - kappa_i), 127 - emax) whole
-   binades so that its largest value lands in the top binade, and its E8M0
-   scale is 2**-(emax + Delta_b).  Each element is the value of step 4
-   rounded to the nearest element (ties to even, saturating at the largest
-   finite one), which puts values below the normal range on the subnormal
-   grid by value; P~_ij = decode(code_ij) * 2**-(emax + Delta_b), about
-   2**(t_ij - kappa_i).
-6. Fallback: a row whose guess was too low has some block with E_b > E_top
-   (its scores exceed m~ by at least the top binade's headroom).  The row is
+   binade of the block's largest value relative to the guess, counted in
+   element codes.  The block is shifted up by
+   Delta_b = min(kappa_i - e_b, 127 - pl) whole binades so that its largest
+   value lands in the placement binade 2**pl: the top binade (pl = emax) for
+   E2M3 and E2M1; for E4M3 the binade below it (pl = emax - 1), which keeps
+   rounding away from E4M3's NaN pattern at no cost in precision (every
+   normal E4M3 binade has the same 3 mantissa bits).  The block's E8M0 scale
+   is 2**-(pl + Delta_b).  Each element is the value of step 4 rounded to the
+   nearest element (ties to even, saturating at the largest finite one),
+   which puts values below the normal range on the subnormal grid by value;
+   P~_ij = decode(code_ij) * 2**-(pl + Delta_b), about 2**(t_ij - kappa_i).
+6. Fallback: a row whose guess was too low has some block with e_b > 0
+   (its scores exceed m~ by a whole binade in the code domain).  The row is
    recomputed with its reference raised by the whole number of binades
-   kappa_i = max(0, max_b E_b - E_top).  Raising the reference by whole
+   kappa_i = max(0, max_b e_b).  Raising the reference by whole
    binades leaves every code of the row unchanged and lowers every block
    scale by 2**kappa_i (except where a block shift reaches the E8M0 floor),
    so the kernel can realise the recomputation as an exact power-of-two
@@ -201,6 +204,13 @@ def trunc_u32(y: np.ndarray) -> np.ndarray:
     return np.clip(np.trunc(y), 0, 2.0 ** 32 - 1).astype(np.uint64)
 
 
+def placement_exponent(fmt) -> int:
+    """Binade 2**pl in which a block's largest probability is placed: the top
+    normal binade, except E4M3 where it is the one below (see step 5)."""
+    f = _fmt(fmt)
+    return f.emax - 1 if f.name == "e4m3" else f.emax
+
+
 def fused_probabilities(s: np.ndarray, m_tilde: np.ndarray, vis: np.ndarray, fmt,
                         D: int) -> Dict[str, np.ndarray]:
     """Steps 4-6 of the module doc for rows of scores ``s`` [R, S].
@@ -211,8 +221,8 @@ def fused_probabilities(s: np.ndarray, m_tilde: np.ndarray, vis: np.ndarray, fmt
     """
     f = _fmt(fmt)
     M = f.mbits
-    E_top = f.emax + f.bias
-    cap = 127 - f.emax
+    pl = placement_exponent(f)
+    cap = 127 - pl
     R, S = s.shape
     beta = fused_beta(D)
     alpha = fused_alpha(f, D)
@@ -223,23 +233,22 @@ def fused_probabilities(s: np.ndarray, m_tilde: np.ndarray, vis: np.ndarray, fmt
     dp[:, :S] = d
     g = dp.reshape(R, nb, BLOCK).max(axis=2)         # -inf for blocks with no visible key
     c = np.rint(alpha * g)                            # alpha*g is exact in float64
-    E = E_top + np.floor(c / (2 ** M))
-    kappa = np.maximum(0.0, np.max(E, axis=1) - E_top)
-    Eb = E - kappa[:, None]
-    delta = np.where(np.isfinite(Eb), np.minimum(E_top - Eb, cap), cap)
+    e = np.floor(c / (2 ** M))                        # block binade relative to the guess
+    kappa = np.maximum(0.0, np.max(e, axis=1))
+    delta = np.where(np.isfinite(e), np.minimum(kappa[:, None] - e, cap), cap)
     delta_full = np.repeat(delta, BLOCK, axis=1)[:, :S]
-    base = (2.0 ** 23) * (127 + f.emax + delta_full - kappa[:, None])
+    base = (2.0 ** 23) * (127 + pl + delta_full - kappa[:, None])
     y = fma_f32(np.float64(beta), np.where(vis, d, 0.0), base)
     y = np.where(vis, y, -np.inf)
     p = bits_to_f32(trunc_u32(y))
     vals = round_to_format(p, f)
     code = encode_values(vals, f).astype(np.int64)
-    P = vals * np.ldexp(1.0, (-f.emax - delta_full).astype(np.int32))
+    P = vals * np.ldexp(1.0, (-pl - delta_full).astype(np.int32))
     return {
         "P": P,
         "codes": code,
         "delta": delta.astype(np.int64),
-        "scale_bytes": (127 - f.emax - delta).astype(np.int64),
+        "scale_bytes": (127 - pl - delta).astype(np.int64),
         "kappa": kappa.astype(np.int64),
     }
 

@@ -118,12 +118,13 @@ def test_probability_map_against_independent_route(fmt):
         t = d * L2E / math.sqrt(D)
         # block binade from the largest score, in element codes
         tmax_code = round(fused_alpha(f, D) * d.max())        # Python round: half to even
-        E = f.emax + f.bias + math.floor(tmax_code / 2 ** f.mbits)
-        delta = min(f.emax + f.bias - E, 127 - f.emax)
+        e = math.floor(tmax_code / 2 ** f.mbits)
+        pl = f.emax - 1 if fmt == "e4m3" else f.emax
+        delta = min(-e, 127 - pl)
         assert fp["kappa"][i] == 0 and fp["delta"][i, 0] == delta
         for j in range(32):
-            p = _mitchell_value(f.emax + delta + t[j])
-            want = _nearest(table, min(p, f.max_value * 2)) * 2.0 ** (-f.emax - delta)
+            p = _mitchell_value(pl + delta + t[j])
+            want = _nearest(table, min(p, f.max_value * 2)) * 2.0 ** (-pl - delta)
             got = fp["P"][i, j]
             # the kernel's fp32 FMA keeps >= 16 fraction bits of x; allow the
             # rare element whose value sits within that rounding of a tie
