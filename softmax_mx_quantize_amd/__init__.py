@@ -6,7 +6,7 @@ C ABI and its contract are declared in ``include/fsa.h``; the functions here
 have the same names without the ``fsa_`` prefix.
 
 Importing the package loads the shared library and fails loudly if it has not
-been built (``python -m softmax_mx_quantize_amd.build``).
+been built (``python softmax_mx_quantize_amd/build.py``).
 """
 
 from __future__ import annotations
@@ -16,7 +16,7 @@ import os
 from typing import Optional, Sequence, Tuple, Union
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfsa.so")
+LIB_PATH = os.environ.get("FSA_LIB_PATH") or os.path.join(_HERE, "libfsa.so")
 
 FMT = {"e4m3": 0, "e2m3": 1, "e2m1": 2}
 BITS = {0: 8, 1: 6, 2: 4}
@@ -43,7 +43,7 @@ class Options(ctypes.Structure):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError("libfsa.so is not built: run `python -m softmax_mx_quantize_amd.build`")
+        raise ImportError("libfsa.so is not built: run `python softmax_mx_quantize_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.fsa_quantize_mx.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, vp]

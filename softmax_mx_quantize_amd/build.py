@@ -1,7 +1,8 @@
 """Build libfsa.so (HIP, gfx950) in the package directory.
 
-Run as ``python -m softmax_mx_quantize_amd.build`` or through
-``__graft_entry__.build()``.  Every call recompiles.  Compiles each source
+Run as ``python softmax_mx_quantize_amd/build.py`` or through
+``__graft_entry__.build()`` (not with ``-m``: that imports the package, which
+needs the library this script builds).  Every call recompiles.  Compiles each source
 with hipcc in parallel, then links a shared library.
 """
 
@@ -16,10 +17,15 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-BUILD = os.path.join(PKG, "_build")
-LIB = os.path.join(PKG, "libfsa.so")
+BUILD = os.environ.get("FSA_BUILD_DIR") or os.path.join(PKG, "_build")
+LIB = os.environ.get("FSA_LIB_OUT") or os.path.join(PKG, "libfsa.so")
 
 SOURCES = ["fsa_api.cpp", "mx_quant.hip", "fsa_fwd.hip", "bf16_fa.hip"]
+
+# Per-source options.  The fused kernel's epilogue consumes the score MFMA
+# results on the vector units; asking for the VGPR form of every MFMA keeps
+# them out of AGPRs (no accvgpr moves in the loop).
+SOURCE_FLAGS = {"fsa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 # Packed fp32 VALU instructions are disabled on purpose (the target feature is
 # switched off for the device pass; the host pass ignores it with a warning).
@@ -39,7 +45,9 @@ def _hipcc() -> str:
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [_hipcc()] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    extra = os.environ.get("FSA_EXTRA_HIPFLAGS", "").split()
+    cmd = ([_hipcc()] + FLAGS + SOURCE_FLAGS.get(src, []) + extra + lang +
+           ["-c", os.path.join(CSRC, src), "-o", obj])
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
@@ -55,7 +63,9 @@ def build(verbose: bool = True) -> str:
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [_hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs
+    # -z defs: an unresolved symbol (e.g. a kernel template that was never
+    # instantiated) fails the link instead of the first dlopen.
+    cmd = [_hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", "-Wl,-z,defs", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)

@@ -25,6 +25,9 @@ bool fmt_ok(int fmt) { return fmt == FSA_MXFP8_E4M3 || fmt == FSA_MXFP6_E2M3 || 
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
+// fsa_fmt -> kernel format index
+int kern_fmt(int fmt) { return fmt == FSA_MXFP8_E4M3 ? 0 : (fmt == FSA_MXFP6_E2M3 ? 1 : 2); }
+
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
@@ -72,6 +75,7 @@ struct Carver {
 
 struct RunLayout {
   int h0, hrun, fmt;
+  int64_t sq_alloc;
   size_t qc, qs, kc, ks, vc, vs;
 };
 
@@ -167,13 +171,14 @@ int fsa_attention_fwd_ex(const void* q, const void* k, const void* v, void* out,
     h = e;
   }
 
-  const int qw = fsa::fsa_queries_per_workgroup();
-  const int64_t sq_alloc = round_up(S, qw);
   const int64_t sk_alloc = round_up(S, kKeyTile);
   Carver cv;
   for (RunLayout& rl : runs) {
     const int bits = fmt_bits(rl.fmt);
     const int64_t nbh = (int64_t)B * rl.hrun;
+    // Q^ rows cover every query row the run's grid touches
+    rl.sq_alloc = round_up(S, fsa::fsa_queries_per_workgroup(kern_fmt(rl.fmt)));
+    const int64_t sq_alloc = rl.sq_alloc;
     rl.qc = cv.take((size_t)(nbh * sq_alloc * D * bits / 8));
     rl.qs = cv.take((size_t)(nbh * sq_alloc * (D / 32)));
     rl.kc = cv.take((size_t)(nbh * sk_alloc * D * bits / 8));
@@ -194,6 +199,7 @@ int fsa_attention_fwd_ex(const void* q, const void* k, const void* v, void* out,
   for (const RunLayout& rl : runs) {
     const int bits = fmt_bits(rl.fmt);
     const int64_t rb = (int64_t)D * bits / 8;
+    const int64_t sq_alloc = rl.sq_alloc;
     for (int b = 0; b < B; ++b) {
       const int64_t src = ((int64_t)b * H + rl.h0) * S * D;
       const int64_t w0 = (int64_t)b * rl.hrun;
@@ -224,15 +230,14 @@ int fsa_attention_fwd_ex(const void* q, const void* k, const void* v, void* out,
     a.row_mguess = opt ? opt->row_max_guess : nullptr;
     a.B = B; a.H = H; a.S = S;
     a.h0 = rl.h0; a.hrun = rl.hrun;
-    a.sq_alloc = (int)sq_alloc; a.sk_alloc = (int)sk_alloc;
+    a.sq_alloc = (int)rl.sq_alloc; a.sk_alloc = (int)sk_alloc;
     // beta = fp32(2^23 log2(e) / sqrt(D)); alpha = beta / 2^(23-M) exactly
     const double log2e = 1.0 / std::log(2.0);
     const float beta = (float)((8388608.0 * log2e) / std::sqrt((double)D));
     a.beta = beta;
     a.alpha = std::ldexp(beta, -(23 - fmt_mbits(rl.fmt)));
     a.bias = opt ? opt->guess_bias : 0.0f;
-    if (fsa::launch_fsa_fwd(a, rl.fmt == FSA_MXFP8_E4M3 ? 0 : (rl.fmt == FSA_MXFP6_E2M3 ? 1 : 2),
-                            D, causal, stream) != hipSuccess)
+    if (fsa::launch_fsa_fwd(a, kern_fmt(rl.fmt), D, causal, stream) != hipSuccess)
       return FSA_ERR_HIP;
   }
   return FSA_OK;

@@ -78,37 +78,49 @@ __device__ __forceinline__ float exp2i(int n) {
 
 // Convert 32 fp32 values (already divided by the block scale) to packed
 // element codes with round-to-nearest-even and saturation.  Output words
-// follow the operand packing: FP8 8 words, FP6 6 words, FP4 4 words.
-template <int F> struct Pack32;
+// follow the operand packing: FP8 8 words, FP6 6 words, FP4 4 words.  FP8
+// saturation needs an explicit clamp (the conversion overflows to NaN);
+// callers whose values provably stay in range pass CLAMP = false.
+template <int F, bool CLAMP> struct Pack32;
 
-template <> struct Pack32<FMT_E4M3> {
+template <bool CLAMP> struct Pack32<FMT_E4M3, CLAMP> {
+  static __device__ __forceinline__ float sat(float v) {
+    return CLAMP ? __builtin_fminf(__builtin_fmaxf(v, -448.0f), 448.0f) : v;
+  }
   static __device__ __forceinline__ void run(const float* y, uint32_t* w) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       v2s lo = {0, 0};
-      float a0 = __builtin_fminf(__builtin_fmaxf(y[4 * i + 0], -448.0f), 448.0f);
-      float a1 = __builtin_fminf(__builtin_fmaxf(y[4 * i + 1], -448.0f), 448.0f);
-      float a2 = __builtin_fminf(__builtin_fmaxf(y[4 * i + 2], -448.0f), 448.0f);
-      float a3 = __builtin_fminf(__builtin_fmaxf(y[4 * i + 3], -448.0f), 448.0f);
-      lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, a0, a1, 1.0f, false);
-      lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, a2, a3, 1.0f, true);
+      lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, sat(y[4 * i + 0]), sat(y[4 * i + 1]), 1.0f, false);
+      lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, sat(y[4 * i + 2]), sat(y[4 * i + 3]), 1.0f, true);
       w[i] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
     }
   }
 };
 
-template <> struct Pack32<FMT_E2M3> {
+// The 32-element FP6 conversion reads 32 source VGPRs over several cycles.
+// Issued through the builtin, the compiler may give it a destination that
+// overlaps its sources and rewrite those sources on the next instruction,
+// which corrupts the result.  Issue it with an early-clobber destination and
+// wait states before anything can overwrite its sources.
+template <bool CLAMP> struct Pack32<FMT_E2M3, CLAMP> {
   static __device__ __forceinline__ void run(const float* y, uint32_t* w) {
     v16f ev, od;
 #pragma unroll
     for (int i = 0; i < 16; ++i) { ev[i] = y[2 * i]; od[i] = y[2 * i + 1]; }
-    v6i r = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f);
+    v6i r;
+    asm volatile(
+        "v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, 1.0\n\t"
+        "s_nop 7\n\t"
+        "s_nop 7"
+        : "=&v"(r)
+        : "v"(ev), "v"(od));
 #pragma unroll
     for (int i = 0; i < 6; ++i) w[i] = (uint32_t)r[i];
   }
 };
 
-template <> struct Pack32<FMT_E2M1> {
+template <bool CLAMP> struct Pack32<FMT_E2M1, CLAMP> {
   static __device__ __forceinline__ void run(const float* y, uint32_t* w) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

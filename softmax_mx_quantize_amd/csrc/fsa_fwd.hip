@@ -16,16 +16,18 @@
 //   4. O^T += V^T P~^T and l += 1 P~^T on the matrix cores (same P~ in
 //      numerator and denominator, as EFQ-Softmax: Exp-Free Quantization for
 //      Softmax, abstract, uses it);
-//   5. a row whose block overflows the top binade is re-based by whole
+//   5. a row whose block overflows the placement binade is re-based by whole
 //      binades: its running O and l are scaled by an exact power of two and
 //      the remaining blocks use the raised reference (the fallback);
 //   6. out = bf16(O / l).
 //
 // Work decomposition.  One workgroup = 4 waves = 4*16*NSUB query rows of one
 // (batch, head).  Key tiles of 128 keys (K^ rows and the matching V^T
-// columns) are staged in LDS and shared by the 4 waves.  Each wave keeps its
-// queries' Q^ fragments, O^T accumulators and row sums in registers; there is
-// no online max and no rescaling except on fallback.
+// columns, with their E8M0 scales) stream through a two-stage LDS ring filled
+// by direct global->LDS loads: tile t+2 is in flight while tile t+1 waits and
+// tile t is computed.  Each wave keeps its queries' Q^ fragments, O^T
+// accumulators and row sums in registers; there is no online max and no
+// rescaling except on fallback.
 //
 // Register layout (16x16x128 scaled MFMA).  Lane (g, r) = 16g + r.  The score
 // tile is computed transposed (keys as rows, queries as columns) so that a
@@ -34,21 +36,40 @@
 // supply as the B operand of the P V product.  For FP6/FP4 that is one whole
 // MX block of P; for FP8 it is two half blocks, completed with the lane
 // 16 apart.
+//
+// LDS layout.  Every K^ row and V^T row occupies 128 bytes (8 chunks of 16
+// bytes; FP6/FP4 rows leave chunks unused).  Chunk c of row R is stored at
+// chunk c ^ f(R): the XOR swizzle makes the 8 lanes that read the same
+// logical chunk of 8 different rows hit 8 different bank groups.
+#include <type_traits>
+
 #include "fsa_device.h"
 #include "fsa_internal.h"
+
+// Waves per workgroup for each element format (overridable at build time).
+#ifndef FSA_NW8
+#define FSA_NW8 4
+#endif
+#ifndef FSA_NW6
+#define FSA_NW6 4
+#endif
+#ifndef FSA_NW4
+#define FSA_NW4 4
+#endif
 
 namespace fsa {
 
 namespace {
 
 constexpr int KT = 128;          // keys per tile
-constexpr int NWAVES = 4;
 constexpr float MAGIC = 12582912.0f;   // 1.5 * 2^23: float + MAGIC rounds to an integer
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ uint32_t cvt_u32_trunc(float y) {
   // Truncation toward zero with saturation; negative and NaN give 0.
   uint32_t u;
-  asm volatile("v_cvt_u32_f32 %0, %1" : "=v"(u) : "v"(y));
+  asm("v_cvt_u32_f32 %0, %1" : "=v"(u) : "v"(y));
   return u;
 }
 
@@ -58,20 +79,58 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   return (uint16_t)(u >> 16);
 }
 
-// Position p (0..31) of a lane's operand list -> key (or K index) within the
-// 128-wide K dimension, for lane group g.
+// Position p (0..31) of a lane's operand list -> index along the 128-wide K
+// dimension for lane group g.
 template <int F>
 __device__ __forceinline__ int kpos(int g, int p) {
   if (Fmt<F>::bits == 8) return p < 16 ? 16 * g + p : 64 + 16 * g + (p - 16);
   return 32 * g + p;
 }
 
-// Copy a lane's operand bytes for one row from LDS: the 32 K elements this
-// lane group holds along a row of D (or 128) elements.  `row` points at the
-// row's first byte; `len` is the row's valid element count (elements past it
-// read as zero codes).
+// XOR swizzles (16-byte chunk index within a 128-byte LDS row).
+template <int F, int D>
+__device__ __forceinline__ int swz_k(int row) {
+  if (D != 128) return 0;
+  const int hi = Fmt<F>::bits == 8 ? (row >> 4) & 1 : (row >> 5) & 1;
+  return (row & 3) | (hi << 2);
+}
+__device__ __forceinline__ int swz_v(int row) { return row & 7; }
+
+// A lane's 32 operand elements along a 128-byte swizzled LDS row.  `len` is
+// the number of valid K elements of the row (elements past it are zero).
 template <int F>
-__device__ __forceinline__ v8i load_operand(const uint8_t* row, int g, int len) {
+__device__ __forceinline__ v8i lds_operand(const uint8_t* row, int sw, int g, int len) {
+  v8i o = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (Fmt<F>::bits == 8) {
+    if (16 * g < len) {
+      uint4 a = *reinterpret_cast<const uint4*>(row + 16 * (g ^ sw));
+      o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+    }
+    if (64 + 16 * g < len) {
+      uint4 b = *reinterpret_cast<const uint4*>(row + 16 * ((4 + g) ^ sw));
+      o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+    }
+  } else if (Fmt<F>::bits == 6) {
+    if (32 * g < len) {
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const int off = 24 * g + 8 * i;
+        uint2 a = *reinterpret_cast<const uint2*>(row + 16 * ((off >> 4) ^ sw) + (off & 15));
+        o[2 * i] = a.x; o[2 * i + 1] = a.y;
+      }
+    }
+  } else {
+    if (32 * g < len) {
+      uint4 a = *reinterpret_cast<const uint4*>(row + 16 * (g ^ sw));
+      o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+    }
+  }
+  return o;
+}
+
+// The same 32 elements straight from global memory (unswizzled row).
+template <int F>
+__device__ __forceinline__ v8i global_operand(const uint8_t* row, int g, int len) {
   v8i o = {0, 0, 0, 0, 0, 0, 0, 0};
   if (Fmt<F>::bits == 8) {
     if (16 * g < len) {
@@ -125,27 +184,58 @@ __device__ __forceinline__ v8i ones_operand() {
   return o;
 }
 
+// Scale operand of the P~ B operand.  FP6/FP4: the lane's own block.  FP8:
+// lane group c supplies the scale of key block c; blocks 0/2 are the low/high
+// halves held by groups 0-1, blocks 1/3 those held by groups 2-3, so groups
+// 1 and 2 take the value from the lane 48 apart (a branch-free exchange).
+template <int BITS>
+__device__ __forceinline__ int p_scale(int s_lo, int s_hi, int g) {
+  if (BITS != 8) return s_lo;
+  const int give = g >= 2 ? s_lo : s_hi;            // what the partner needs
+  const int got = __shfl_xor(give, 48);
+  const int own = g < 2 ? s_lo : s_hi;
+  const bool cross = (g == 1) | (g == 2);
+  return cross ? got : own;
+}
+
+__device__ __forceinline__ void dma16(const void* g, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 4, 0, 0);
+}
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N of this wave's memory loads are still outstanding
+// (loads complete in issue order for the counter).
+template <int N>
+__device__ __forceinline__ void wait_dma_keep() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
 }  // namespace
 
-template <int F, int D, bool CAUSAL, int NSUB>
-__global__ void __launch_bounds__(256, 1) fsa_fwd_kernel(AttnArgs a) {
+template <int F, int D, bool CAUSAL, int NSUB, int NWAVES>
+__global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES * 64))) fsa_fwd_kernel(AttnArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)  // buffer-resource types exist only in the device pass
   constexpr int BITS = Fmt<F>::bits;
   constexpr int MB = Fmt<F>::mbits;
-  constexpr int EMAX = Fmt<F>::emax;
-  constexpr int ETOP = Fmt<F>::e_top;
-  constexpr int CAP = 127 - EMAX;
-  constexpr int RB = D * BITS / 8;          // bytes per Q^/K^ row
-  constexpr int VRB = KT * BITS / 8;        // bytes per V^T tile row
+  constexpr int PL = F == FMT_E4M3 ? Fmt<F>::emax - 1 : Fmt<F>::emax;   // placement binade
+  constexpr int CAP = 127 - PL;
+  constexpr int RB = D * BITS / 8;          // bytes per Q^/K^ row (global)
+  constexpr int RS = 128;                   // bytes per K^/V^T row (LDS)
+  constexpr int NCH = RS / 16;              // 16-byte chunks per LDS row
+  constexpr int KCH_VALID = RB / 16 > 0 ? RB / 16 : 1;
+  constexpr int VCH_VALID = KT * BITS / 8 / 16;
+  constexpr int VRB = KT * BITS / 8;        // bytes per V^T tile row (global)
   constexpr int NDB = D / 32;               // MX blocks per Q^/K^ row
   constexpr int NDT = D / 16;               // 16-wide output tiles along D
-  constexpr int KRS = RB + 16;              // LDS row stride (padded)
-  constexpr int VRS = VRB + 16;
   constexpr int QW = NWAVES * 16 * NSUB;    // queries per workgroup
+  constexpr int K_BYTES = KT * RS;
+  constexpr int V_BYTES = D * RS;
+  constexpr int KS_BYTES = KT * NDB;
+  constexpr int VS_BYTES = D * 4;
+  constexpr int STAGE = K_BYTES + V_BYTES + KS_BYTES + VS_BYTES;
 
-  __shared__ __align__(16) uint8_t k_lds[KT * KRS];
-  __shared__ __align__(16) uint8_t ks_lds[KT * NDB];
-  __shared__ __align__(16) uint8_t v_lds[D * VRS];
-  __shared__ __align__(16) uint32_t vs_lds[D];
+  constexpr int NSTAGE = 3;                 // LDS ring depth (tiles in flight + 1)
+  __shared__ __align__(16) uint8_t lds[NSTAGE * STAGE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -153,14 +243,22 @@ __global__ void __launch_bounds__(256, 1) fsa_fwd_kernel(AttnArgs a) {
   const int g = lane >> 4;
   const int r = lane & 15;
 
+  // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
+  // contiguous run of (head, query tile) work items so that the workgroups
+  // sharing one XCD's L2 work on the same head's K^ and V^.
+  const int nq = (a.S + QW - 1) / QW;
+  const int n_items = nq * a.B * a.hrun;
+  const int per_xcd = (n_items + 7) / 8;
+  const int item = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (item >= n_items) return;
   // workspace slabs are indexed by the launch's own (batch, head) order;
   // outputs by the global head index
-  const int64_t wi = blockIdx.y;
-  const int b = blockIdx.y / a.hrun;
-  const int h = a.h0 + (blockIdx.y - b * a.hrun);
+  const int64_t wi = item / nq;
+  const int b = (int)wi / a.hrun;
+  const int h = a.h0 + ((int)wi - b * a.hrun);
   const int64_t bh = (int64_t)b * a.H + h;
   const int S = a.S;
-  const int q_wg = blockIdx.x * QW;
+  const int q_wg = (item - (int)wi * nq) * QW;
   const int q_wave = q_wg + wave * 16 * NSUB;
 
   const uint8_t* kc = a.kc + wi * (int64_t)a.sk_alloc * RB;
@@ -169,6 +267,74 @@ __global__ void __launch_bounds__(256, 1) fsa_fwd_kernel(AttnArgs a) {
   const uint8_t* vc = a.vc + wi * (int64_t)D * v_row;
   const int vs_row = a.sk_alloc / 32;
   const uint8_t* vs = a.vs + wi * (int64_t)D * vs_row;
+
+  int n_tiles = (S + KT - 1) / KT;
+  if (CAUSAL) {
+    const int last_q = q_wg + QW - 1 < S - 1 ? q_wg + QW - 1 : S - 1;
+    const int t_need = last_q / KT + 1;
+    n_tiles = t_need < n_tiles ? t_need : n_tiles;
+  }
+
+  // Direct global->LDS copy of key tile t into stage st with buffer loads:
+  // each wave moves 1 KB per instruction (8 LDS rows of 8 chunks); lane i
+  // fills physical chunk i%8 of row i/8 with the logical chunk the swizzle
+  // maps there (unused chunks of FP6/FP4 rows re-read chunk 0 of their row).
+  // The lane's byte offset inside the head's slab is fixed for the whole
+  // sweep; the tile's offset goes in the scalar offset, so issuing a tile
+  // costs no vector instructions.
+  constexpr int NK_DMA = KT * NCH / 64 / NWAVES;      // per wave, per tile
+  constexpr int NV_DMA = D * NCH / 64 / NWAVES;
+  constexpr int NKS = KS_BYTES / 256;
+  const __amdgpu_buffer_rsrc_t k_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)kc, (short)0, a.sk_alloc * RB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t v_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)vc, (short)0, (int)(D * v_row), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ks_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)ks, (short)0, a.sk_alloc * NDB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vs_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)vs, (short)0, D * vs_row, 0x00020000);
+  int k_voff[NK_DMA], v_voff[NV_DMA];
+#pragma unroll
+  for (int k = 0; k < NK_DMA; ++k) {
+    const int row = (wave + NWAVES * k) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz_k<F, D>(row);
+    k_voff[k] = row * RB + (c < KCH_VALID ? c : 0) * 16;
+  }
+#pragma unroll
+  for (int k = 0; k < NV_DMA; ++k) {
+    const int row = (wave + NWAVES * k) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz_v(row);
+    v_voff[k] = row * (int)v_row + (c < VCH_VALID ? c : 0) * 16;
+  }
+  // scales: NKS K-scale dwords and D/64 V-scale dwords, one per wave (waves
+  // past them re-load the first K-scale dword to keep the count uniform)
+  const bool s_is_v = wave >= NKS && wave < NKS + D / 64;
+  const int s_voff = wave < NKS ? wave * 256 + lane * 4
+                                : (s_is_v ? ((wave - NKS) * 64 + lane) * vs_row : lane * 4);
+  const int s_lds = wave < NKS ? K_BYTES + V_BYTES + wave * 256
+                               : (s_is_v ? K_BYTES + V_BYTES + KS_BYTES + (wave - NKS) * 256
+                                         : K_BYTES + V_BYTES);
+  auto issue_tile = [&](int t, int st) {
+    uint8_t* base = lds + st * STAGE;
+#pragma unroll
+    for (int k = 0; k < NK_DMA; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (lds_void*)(base + (wave + NWAVES * k) * 1024),
+                                               16, k_voff[k], t * KT * RB, 0, 0);
+#pragma unroll
+    for (int k = 0; k < NV_DMA; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc, (lds_void*)(base + K_BYTES + (wave + NWAVES * k) * 1024),
+                                               16, v_voff[k], t * VRB, 0, 0);
+    if (s_is_v)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vs_rsrc, (lds_void*)(base + s_lds), 4, s_voff,
+                                               t * (KT / 32), 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ks_rsrc, (lds_void*)(base + s_lds), 4, s_voff,
+                                               t * KT * NDB, 0, 0);
+  };
+  // DMA instructions each wave issues per tile
+  constexpr int DMA_PER_TILE = NK_DMA + NV_DMA + 1;
+
+  if (n_tiles > 0) issue_tile(0, 0);
 
   // ---- Q^ fragments (B operand of the score product), one per subtile
   v8i qf[NSUB];
@@ -179,65 +345,35 @@ __global__ void __launch_bounds__(256, 1) fsa_fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
       const int q = q_wave + 16 * s + r;
-      qf[s] = load_operand<F>(qc + (int64_t)q * RB, g, D);
+      qf[s] = global_operand<F>(qc + (int64_t)q * RB, g, D);
       qsc[s] = g < NDB ? (int)qs[(int64_t)q * NDB + g] : 127;
     }
   }
 
-  // ---- key-tile range
-  int n_tiles = (S + KT - 1) / KT;
-  if (CAUSAL) {
-    const int last_q = q_wg + QW - 1 < S - 1 ? q_wg + QW - 1 : S - 1;
-    const int t_need = last_q / KT + 1;
-    n_tiles = t_need < n_tiles ? t_need : n_tiles;
-  }
-
-  auto load_tile = [&](int t) {
-    // K^ rows [t*KT, t*KT+KT): contiguous in global memory
-    constexpr int KCH = KT * RB / 16;
-    const uint8_t* src = kc + (int64_t)t * KT * RB;
-    for (int c = tid; c < KCH; c += 256) {
-      const int row = c / (RB / 16), col = c - row * (RB / 16);
-      *reinterpret_cast<uint4*>(k_lds + row * KRS + col * 16) =
-          *reinterpret_cast<const uint4*>(src + (int64_t)c * 16);
-    }
-    constexpr int KSCH = KT * NDB / 16;
-    const uint8_t* ssrc = ks + (int64_t)t * KT * NDB;
-    for (int c = tid; c < KSCH; c += 256)
-      *reinterpret_cast<uint4*>(ks_lds + c * 16) = *reinterpret_cast<const uint4*>(ssrc + c * 16);
-    // V^T rows d in [0, D), columns = this tile's keys
-    constexpr int VCH = D * VRB / 16;
-    for (int c = tid; c < VCH; c += 256) {
-      const int row = c / (VRB / 16), col = c - row * (VRB / 16);
-      *reinterpret_cast<uint4*>(v_lds + row * VRS + col * 16) =
-          *reinterpret_cast<const uint4*>(vc + row * v_row + (int64_t)t * VRB + col * 16);
-    }
-    if (tid < D)
-      vs_lds[tid] = *reinterpret_cast<const uint32_t*>(vs + (int64_t)tid * vs_row + t * (KT / 32));
-  };
-
-  // A operand of the score product for 16-key slice j: row R of the slice is
-  // key kpos(R/4, 4j + R%4) of the tile, so that output row 4g+i lands on the
-  // lane's operand position 4j+i.
-  auto k_frag = [&](int j, int& sc) -> v8i {
+  // A operand of the score product for 16-key slice j of the tile in stage
+  // st: row R of the slice is key kpos(R/4, 4j + R%4), so that output row
+  // 4g+i lands on the lane's operand position 4j+i.
+  auto k_frag = [&](int st, int j, int& sc) -> v8i {
     const int kk = kpos<F>(r >> 2, 4 * j + (r & 3));
-    sc = g < NDB ? (int)ks_lds[kk * NDB + g] : 127;
-    return load_operand<F>(k_lds + kk * KRS, g, D);
+    const uint8_t* base = lds + st * STAGE;
+    sc = g < NDB ? (int)base[K_BYTES + V_BYTES + kk * NDB + g] : 127;
+    return lds_operand<F>(base + kk * RS, swz_k<F, D>(kk), g, D);
   };
 
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
 
   // ---- frozen max from the first tile (keys [0, 128))
   float mg[NSUB];
+  wait_dma();
+  __syncthreads();
+  if (n_tiles > 1) issue_tile(1, 1);
+  if (n_tiles > 2) issue_tile(2, 2);
   {
-    __syncthreads();
-    load_tile(0);
-    __syncthreads();
     v4f acc[NSUB][8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       int sc;
-      const v8i kf = k_frag(j, sc);
+      const v8i kf = k_frag(0, j, sc);
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) acc[s][j] = mfma<F>(kf, qf[s], zero4, sc, qsc[s]);
     }
@@ -276,13 +412,21 @@ __global__ void __launch_bounds__(256, 1) fsa_fwd_kernel(AttnArgs a) {
   }
 
   // ---- main sweep
+  // A block whose largest score exceeds the guess by e_b > 0 binades keeps
+  // its codes and takes an E8M0 scale 2^e_b above the guess's: exactly the
+  // row the oracle re-bases by kappa = max e_b, scaled by 2^kappa in both
+  // O and l.  Only a row beyond EXT binades (scale bytes or fp32 sums could
+  // overflow) is recomputed after the sweep with the re-basing made explicit.
+  constexpr int EXT = 64;
   v4f O[NSUB][NDT];
   v4f L[NSUB];
-  int kap[NSUB];
+  int kmax[NSUB];
+  v4f minit[NSUB];
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
     L[s] = zero4;
-    kap[s] = 0;
+    kmax[s] = -1000000;
+    minit[s] = v4f{-mg[s], -mg[s], -mg[s], -mg[s]};
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) O[s][dt] = zero4;
   }
@@ -290,30 +434,67 @@ __global__ void __launch_bounds__(256, 1) fsa_fwd_kernel(AttnArgs a) {
   const float alpha = a.alpha, beta = a.beta;
   const float gmin = -2097152.0f / alpha;    // keeps alpha*g inside the MAGIC window
 
-  for (int t = 0; t < n_tiles; ++t) {
-    if (t > 0) {
-      __syncthreads();
-      load_tile(t);
-      __syncthreads();
-    }
-    const int key0 = t * KT;
-    const bool need_mask = (key0 + KT > S) || (CAUSAL && key0 + KT - 1 > q_wave);
+  // Lane-constant LDS byte offsets.  For slice j of the score product the
+  // lane's K^ row is kk0 + 4j (+48 for the FP8 high half), and its swizzle
+  // does not depend on j; V^T row 16dt + r likewise.  Every fragment read is
+  // a base register plus a compile-time offset.
+  const int kk0 = BITS == 8 ? 16 * (r >> 2) + (r & 3) : 32 * (r >> 2) + (r & 3);
+  const int ksw = swz_k<F, D>(kk0);
+  const int vsw = swz_v(r);
+  int k_off[3], v_off[3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    int lo;
+    if (BITS == 8) lo = i == 0 ? 16 * g : 64 + 16 * g;
+    else if (BITS == 6) lo = 24 * g + 8 * i;
+    else lo = 16 * g;
+    k_off[i] = kk0 * RS + 16 * ((lo >> 4) ^ ksw) + (lo & 15);
+    v_off[i] = K_BYTES + r * RS + 16 * ((lo >> 4) ^ vsw) + (lo & 15);
+  }
+  const int ks_off = K_BYTES + V_BYTES + kk0 * NDB + (g < NDB ? g : 0);
+  const int vs_off = K_BYTES + V_BYTES + KS_BYTES + r * 4 + g;
+  const bool k_live = 32 * g < D;               // FP6/FP4 lane groups past D
+  const bool k_hi = 64 + 16 * g < D;            // FP8 high half present
 
+  auto frag = [&](const uint8_t* base, const int* off, int imm, bool live, bool hi) -> v8i {
+    v8i o = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (BITS == 8) {
+      if (live) {
+        const uint4 a0 = *reinterpret_cast<const uint4*>(base + off[0] + imm);
+        o[0] = a0.x; o[1] = a0.y; o[2] = a0.z; o[3] = a0.w;
+      }
+      if (hi) {
+        const uint4 a1 = *reinterpret_cast<const uint4*>(base + off[1] + imm);
+        o[4] = a1.x; o[5] = a1.y; o[6] = a1.z; o[7] = a1.w;
+      }
+    } else if (BITS == 6) {
+      if (live) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+          const uint2 a = *reinterpret_cast<const uint2*>(base + off[i] + imm);
+          o[2 * i] = a.x; o[2 * i + 1] = a.y;
+        }
+      }
+    } else if (live) {
+      const uint4 a0 = *reinterpret_cast<const uint4*>(base + off[0] + imm);
+      o[0] = a0.x; o[1] = a0.y; o[2] = a0.z; o[3] = a0.w;
+    }
+    return o;
+  };
+
+  // One key tile: scores, fused exponential + MX quantisation of P, P V.
+  auto tile = [&](const uint8_t* base, int key0, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     v4f acc[NSUB][8];
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      const v4f init = {-mg[s], -mg[s], -mg[s], -mg[s]};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[s][j] = init;
-    }
-#pragma unroll
     for (int j = 0; j < 8; ++j) {
-      int sc;
-      const v8i kf = k_frag(j, sc);
+      const int jrow = 4 * j + ((BITS == 8 && j >= 4) ? 48 : 0);
+      const int sc = g < NDB ? (int)base[ks_off + jrow * NDB] : 127;
+      const v8i kf = frag(base, k_off, jrow * RS, BITS == 8 ? 16 * g < D : k_live,
+                          BITS == 8 ? k_hi : false);
 #pragma unroll
-      for (int s = 0; s < NSUB; ++s) acc[s][j] = mfma<F>(kf, qf[s], acc[s][j], sc, qsc[s]);
+      for (int s = 0; s < NSUB; ++s) acc[s][j] = mfma<F>(kf, qf[s], minit[s], sc, qsc[s]);
     }
-
     v8i pw[NSUB];
     int psc[NSUB];
 #pragma unroll
@@ -321,7 +502,7 @@ __global__ void __launch_bounds__(256, 1) fsa_fwd_kernel(AttnArgs a) {
       float x[32];
 #pragma unroll
       for (int p = 0; p < 32; ++p) x[p] = acc[s][p >> 2][p & 3];
-      if (need_mask) {
+      if (MASKED) {
         const int q = q_wave + 16 * s + r;
 #pragma unroll
         for (int p = 0; p < 32; ++p) {
@@ -331,9 +512,15 @@ __global__ void __launch_bounds__(256, 1) fsa_fwd_kernel(AttnArgs a) {
         }
       }
       // block maxima: one block per lane (FP6/FP4) or two half blocks (FP8)
-      float m0 = x[0], m1 = x[16];
+      float m0 = __builtin_fmaxf(__builtin_fmaxf(x[0], x[1]), x[2]);
+      float m1 = __builtin_fmaxf(__builtin_fmaxf(x[16], x[17]), x[18]);
 #pragma unroll
-      for (int p = 1; p < 16; ++p) { m0 = __builtin_fmaxf(m0, x[p]); m1 = __builtin_fmaxf(m1, x[16 + p]); }
+      for (int p = 3; p < 15; p += 2) {
+        m0 = __builtin_fmaxf(__builtin_fmaxf(m0, x[p]), x[p + 1]);
+        m1 = __builtin_fmaxf(__builtin_fmaxf(m1, x[16 + p]), x[17 + p]);
+      }
+      m0 = __builtin_fmaxf(m0, x[15]);
+      m1 = __builtin_fmaxf(m1, x[31]);
       if (BITS == 8) {
         m0 = __builtin_fmaxf(m0, __shfl_xor(m0, 16));
         m1 = __builtin_fmaxf(m1, __shfl_xor(m1, 16));
@@ -341,33 +528,19 @@ __global__ void __launch_bounds__(256, 1) fsa_fwd_kernel(AttnArgs a) {
         m0 = __builtin_fmaxf(m0, m1);
         m1 = m0;
       }
-      // block binade E = e_top + floor(round(alpha * max) / 2^M)
+      // block binade relative to the guess: floor(round(alpha * max) / 2^M)
       auto binade = [&](float m) -> int {
         const float mc = __builtin_fmaxf(m, gmin);
         const float tt = __builtin_fmaf(alpha, mc, MAGIC);
         const int c = (int)(__float_as_uint(tt) - __float_as_uint(MAGIC));
-        return ETOP + (c >> MB);
+        return c >> MB;
       };
-      int E0 = binade(m0), E1 = binade(m1);
-      // fallback: any block above the top binade re-bases its row
-      const bool over = (E0 - kap[s] > ETOP) || (E1 - kap[s] > ETOP);
-      if (__builtin_amdgcn_ballot_w64(over) != 0) {
-        int em = E0 > E1 ? E0 : E1;
-        em = max(em, __shfl_xor(em, 16));
-        em = max(em, __shfl_xor(em, 32));
-        const int nk = max(kap[s], em - ETOP);
-        if (nk != kap[s]) {
-          const float f = __builtin_ldexpf(1.0f, kap[s] - nk);
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) O[s][dt] *= f;
-          L[s] *= f;
-          kap[s] = nk;
-        }
-      }
-      const int d0 = min(ETOP - (E0 - kap[s]), CAP);
-      const int d1 = min(ETOP - (E1 - kap[s]), CAP);
-      const float base0 = (float)(127 + EMAX + d0 - kap[s]) * 8388608.0f;
-      const float base1 = (float)(127 + EMAX + d1 - kap[s]) * 8388608.0f;
+      const int e0 = binade(m0), e1 = binade(m1);
+      kmax[s] = max(kmax[s], max(e0, e1));
+      const int d0 = min(-min(e0, EXT), CAP);
+      const int d1 = min(-min(e1, EXT), CAP);
+      const float base0 = (float)(127 + PL + d0) * 8388608.0f;
+      const float base1 = (float)(127 + PL + d1) * 8388608.0f;
       float pv[32];
 #pragma unroll
       for (int p = 0; p < 32; ++p) {
@@ -375,31 +548,135 @@ __global__ void __launch_bounds__(256, 1) fsa_fwd_kernel(AttnArgs a) {
         pv[p] = __uint_as_float(cvt_u32_trunc(y));
       }
       uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      Pack32<F>::run(pv, w);
+      Pack32<F, false>::run(pv, w);
 #pragma unroll
       for (int i = 0; i < 8; ++i) pw[s][i] = (int)w[i];
-      const int s0 = 127 - EMAX - d0, s1 = 127 - EMAX - d1;
-      if (BITS == 8) {
-        // lane group c supplies the scale of key block c: blocks 0/2 live in
-        // groups 0-1 (low/high half), blocks 1/3 in groups 2-3.
-        const int o0 = __shfl_xor(s0, 48), o1 = __shfl_xor(s1, 48);
-        psc[s] = g == 0 ? s0 : (g == 1 ? o0 : (g == 2 ? o1 : s1));
-      } else {
-        psc[s] = s0;
-      }
+      psc[s] = p_scale<BITS>(127 - PL - d0, 127 - PL - d1, g);
     }
-
     // P V and the row sums on the matrix cores
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const int d = 16 * dt + r;
-      const v8i vf = load_operand<F>(v_lds + d * VRS, g, KT);
-      const int vsc = (int)((vs_lds[d] >> (8 * g)) & 0xFF);
+      const v8i vf = frag(base, v_off, 16 * dt * RS, true, true);
+      const int vsc = (int)base[vs_off + 64 * dt];
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) O[s][dt] = mfma<F>(vf, pw[s], O[s][dt], vsc, psc[s]);
     }
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) L[s] = mfma<F>(ones, pw[s], L[s], 127, psc[s]);
+  };
+
+  // tiles [0, n_clean) need no masking for any row of this wave
+  int n_clean = S / KT;
+  if (CAUSAL) {
+    const int c2 = (q_wave + 1) / KT;          // key0 + KT - 1 <= q_wave
+    n_clean = c2 < n_clean ? c2 : n_clean;
+  }
+  n_clean = n_clean < n_tiles ? n_clean : n_tiles;
+  // Two loops so that the clean tiles' code carries no masking at all.
+  auto advance = [&](int t, int st) {
+    // tile t+1 must have landed (tile t+2 may still be in flight); after the
+    // barrier every wave is done with stage st, which takes tile t+3
+    if (t + 2 < n_tiles) wait_dma_keep<DMA_PER_TILE>();
+    else wait_dma();
+    __syncthreads();
+    if (t + 3 < n_tiles) issue_tile(t + 3, st);
+  };
+  int t = 0, st = 0;
+  for (; t < n_clean; ++t) {
+    tile(lds + st * STAGE, t * KT, std::false_type{});
+    advance(t, st);
+    st = st == NSTAGE - 1 ? 0 : st + 1;
+  }
+  for (; t < n_tiles; ++t) {
+    tile(lds + st * STAGE, t * KT, std::true_type{});
+    advance(t, st);
+    st = st == NSTAGE - 1 ? 0 : st + 1;
+  }
+
+  // row offsets in binades (the oracle's kappa)
+  int kap[NSUB];
+  bool extreme = false;
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    int k = kmax[s];
+    k = max(k, __shfl_xor(k, 16));
+    k = max(k, __shfl_xor(k, 32));
+    kap[s] = k > 0 ? k : 0;
+    extreme |= kap[s] > EXT;
+  }
+  if (__builtin_amdgcn_ballot_w64(extreme) != 0) {
+    // Cold path: rows whose scores exceed the guess by more than EXT
+    // binades.  Recompute this wave's rows with the re-based reference
+    // (Delta_b = min(kappa - e_b, CAP)), reading K^ and V^T from global memory.
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      L[s] = zero4;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) O[s][dt] = zero4;
+    }
+    for (int t = 0; t < n_tiles; ++t) {
+      const int key0 = t * KT;
+      v4f acc[NSUB][8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int kk = kpos<F>(r >> 2, 4 * j + (r & 3));
+        const int sc = g < NDB ? (int)ks[(int64_t)(key0 + kk) * NDB + g] : 127;
+        const v8i kf = global_operand<F>(kc + (int64_t)(key0 + kk) * RB, g, D);
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) acc[s][j] = mfma<F>(kf, qf[s], minit[s], sc, qsc[s]);
+      }
+      v8i pw[NSUB];
+      int psc[NSUB];
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) {
+        const int q = q_wave + 16 * s + r;
+        float x[32];
+#pragma unroll
+        for (int p = 0; p < 32; ++p) {
+          const int key = key0 + kpos<F>(g, p);
+          const bool vis = key < S && (!CAUSAL || key <= q);
+          x[p] = vis ? acc[s][p >> 2][p & 3] : -INFINITY;
+        }
+        float m0 = x[0], m1 = x[16];
+#pragma unroll
+        for (int p = 1; p < 16; ++p) { m0 = __builtin_fmaxf(m0, x[p]); m1 = __builtin_fmaxf(m1, x[16 + p]); }
+        if (BITS == 8) {
+          m0 = __builtin_fmaxf(m0, __shfl_xor(m0, 16));
+          m1 = __builtin_fmaxf(m1, __shfl_xor(m1, 16));
+        } else {
+          m0 = __builtin_fmaxf(m0, m1);
+          m1 = m0;
+        }
+        auto binade = [&](float m) -> int {
+          const float mc = __builtin_fmaxf(m, gmin);
+          const float tt = __builtin_fmaf(alpha, mc, MAGIC);
+          return (int)(__float_as_uint(tt) - __float_as_uint(MAGIC)) >> MB;
+        };
+        const int e0 = binade(m0), e1 = binade(m1);
+        const int d0 = min(kap[s] - e0, CAP), d1 = min(kap[s] - e1, CAP);
+        const float base0 = (float)(127 + PL + d0 - kap[s]) * 8388608.0f;
+        const float base1 = (float)(127 + PL + d1 - kap[s]) * 8388608.0f;
+        float pv[32];
+#pragma unroll
+        for (int p = 0; p < 32; ++p)
+          pv[p] = __uint_as_float(cvt_u32_trunc(__builtin_fmaf(beta, x[p], p < 16 ? base0 : base1)));
+        uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        Pack32<F, false>::run(pv, w);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pw[s][i] = (int)w[i];
+        psc[s] = p_scale<BITS>(127 - PL - d0, 127 - PL - d1, g);
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int d = 16 * dt + r;
+        const v8i vf = global_operand<F>(vc + d * v_row + (int64_t)t * VRB, g, KT);
+        const int vsc = (int)vs[(int64_t)d * vs_row + t * (KT / 32) + g];
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) O[s][dt] = mfma<F>(vf, pw[s], O[s][dt], vsc, psc[s]);
+      }
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) L[s] = mfma<F>(ones, pw[s], L[s], 127, psc[s]);
+    }
   }
 
   // ---- normalise and store: lane (g, r) holds O[q][16dt + 4g + i]
@@ -421,14 +698,32 @@ __global__ void __launch_bounds__(256, 1) fsa_fwd_kernel(AttnArgs a) {
       }
     }
   }
+#endif  // __HIP_DEVICE_COMPILE__
 }
+
+// Query subtiles (16 rows each) per wave.  More subtiles reuse every K^/V^T
+// fragment read from LDS for more rows; the count is capped by the 256
+// architectural VGPRs the score accumulators and the epilogue need.
+template <int F> struct Nsub;
+template <> struct Nsub<FMT_E4M3> { static constexpr int value = 2; };
+template <> struct Nsub<FMT_E2M3> { static constexpr int value = 2; };
+template <> struct Nsub<FMT_E2M1> { static constexpr int value = 2; };
+// Waves per workgroup: 8 puts two waves on each SIMD, so one wave's vector
+// epilogue runs while the other's MFMAs occupy the matrix core; FP8's larger
+// operands leave room for only one wave per SIMD.
+template <int F> struct Nwaves;
+template <> struct Nwaves<FMT_E4M3> { static constexpr int value = FSA_NW8; };
+template <> struct Nwaves<FMT_E2M3> { static constexpr int value = FSA_NW6; };
+template <> struct Nwaves<FMT_E2M1> { static constexpr int value = FSA_NW4; };
 
 template <int F, int D, bool CAUSAL>
 static hipError_t launch3(const AttnArgs& a, hipStream_t stream) {
-  constexpr int NSUB = 2;
+  constexpr int NSUB = Nsub<F>::value;
+  constexpr int NWAVES = Nwaves<F>::value;
   constexpr int QW = NWAVES * 16 * NSUB;
-  dim3 grid((a.S + QW - 1) / QW, a.B * a.hrun);
-  hipLaunchKernelGGL((fsa_fwd_kernel<F, D, CAUSAL, NSUB>), grid, dim3(256), 0, stream, a);
+  const int n_items = (a.S + QW - 1) / QW * a.B * a.hrun;
+  dim3 grid((n_items + 7) / 8 * 8);
+  hipLaunchKernelGGL((fsa_fwd_kernel<F, D, CAUSAL, NSUB, NWAVES>), grid, dim3(NWAVES * 64), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -438,7 +733,11 @@ static hipError_t launch2(const AttnArgs& a, int D, int causal, hipStream_t stre
   return causal ? launch3<F, 64, true>(a, stream) : launch3<F, 64, false>(a, stream);
 }
 
-int fsa_queries_per_workgroup() { return NWAVES * 16 * 2; }
+int fsa_queries_per_workgroup(int fmt) {
+  if (fmt == FMT_E4M3) return Nwaves<FMT_E4M3>::value * 16 * Nsub<FMT_E4M3>::value;
+  if (fmt == FMT_E2M3) return Nwaves<FMT_E2M3>::value * 16 * Nsub<FMT_E2M3>::value;
+  return Nwaves<FMT_E2M1>::value * 16 * Nsub<FMT_E2M1>::value;
+}
 
 hipError_t launch_fsa_fwd(const AttnArgs& a, int fmt, int D, int causal, hipStream_t stream) {
   if (fmt == FMT_E4M3) return launch2<FMT_E4M3>(a, D, causal, stream);

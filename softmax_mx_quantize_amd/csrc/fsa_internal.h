@@ -47,7 +47,7 @@ struct AttnArgs {
 };
 
 hipError_t launch_fsa_fwd(const AttnArgs& a, int fmt, int D, int causal, hipStream_t stream);
-int fsa_queries_per_workgroup();
+int fsa_queries_per_workgroup(int fmt);   // query rows one workgroup covers
 
 // Plain BF16 flash attention.
 struct Bf16Args {

@@ -86,7 +86,7 @@ __global__ void __launch_bounds__(256) mx_quant_kernel(QuantArgs a) {
 #pragma unroll
   for (int j = 0; j < 32; ++j) y[j] = __builtin_ldexpf(v[j], -X);
   uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  Pack32<F>::run(y, w);
+  Pack32<F, true>::run(y, w);
   uint8_t sbyte = (uint8_t)(X + 127);
   if (bad) {
 #pragma unroll
