@@ -14,6 +14,13 @@ Prints ONE JSON line.  Options:
   --no-cpu        skip the CPU-oracle baseline
   --only FMT      time only one element format (e4m3, e2m3, e2m1)
   --copy-bytes N  also run one plain device copy of N bytes (counter calibration)
+  --write-traffic FETCH_DB WRITE_DB
+                  no timing: read two rocprofv3 --pmc result databases (one
+                  with FETCH_SIZE, one with WRITE_SIZE) of a run with
+                  --copy-bytes, scale the fused kernel's per-dispatch counters
+                  by the copy kernel's bytes-per-count, and write
+                  profiles/fsa_fwd_traffic.json (tagged with the kernel-source
+                  hash, so a later kernel change invalidates it)
 """
 
 from __future__ import annotations
@@ -53,6 +60,55 @@ def stored_traffic(fmt: str):
     if d.get("kernel_hash") != kernel_hash():
         return None
     return d.get("bytes_per_launch", {}).get(fmt)
+
+
+FMT_OF_TEMPLATE = {"0": "e4m3", "1": "e2m3", "2": "e2m1"}
+
+
+def _pmc_per_kernel(db_path: str, counter: str):
+    """Average per-dispatch value of `counter` (summed over its instances)
+    for each kernel name in a rocprofv3 results database."""
+    import sqlite3
+    import collections
+    db = sqlite3.connect(db_path)
+    rows = db.execute("select dispatch_id, kernel_name, counter_name, value "
+                      "from counters_collection").fetchall()
+    per_dispatch = collections.defaultdict(float)
+    names = {}
+    for did, kn, cn, val in rows:
+        if cn == counter:
+            per_dispatch[did] += val
+            names[did] = kn
+    by_kernel = collections.defaultdict(list)
+    for did, v in per_dispatch.items():
+        by_kernel[names[did]].append(v)
+    return {k: sum(v) / len(v) for k, v in by_kernel.items()}
+
+
+def write_traffic(fetch_db: str, write_db: str, copy_bytes: int) -> dict:
+    fetch = _pmc_per_kernel(fetch_db, "FETCH_SIZE")
+    write = _pmc_per_kernel(write_db, "WRITE_SIZE")
+    copy = [k for k in fetch if "neg_kernel" in k]
+    if len(copy) != 1:
+        raise RuntimeError("expected one copy (neg) kernel in the counter run, found %r" % copy)
+    # FETCH_SIZE / WRITE_SIZE are in KiB; the copy reads and writes copy_bytes
+    f_scale = copy_bytes / (fetch[copy[0]] * 1024.0)
+    w_scale = copy_bytes / (write[copy[0]] * 1024.0)
+    out = {"kernel_hash": kernel_hash(), "copy_bytes": copy_bytes,
+           "fetch_bytes_per_count_byte": f_scale, "write_bytes_per_count_byte": w_scale,
+           "bytes_per_launch": {}, "fetch_bytes": {}, "write_bytes": {}}
+    for k in fetch:
+        if "fsa_fwd_kernel<" not in k:
+            continue
+        fmt = FMT_OF_TEMPLATE[k.split("fsa_fwd_kernel<")[1].split(",")[0].strip()]
+        fb = fetch[k] * 1024.0 * f_scale
+        wb = write.get(k, 0.0) * 1024.0 * w_scale
+        out["fetch_bytes"][fmt] = fb
+        out["write_bytes"][fmt] = wb
+        out["bytes_per_launch"][fmt] = fb + wb
+    with open(os.path.join(ROOT, "profiles", "fsa_fwd_traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    return out
 
 
 def time_fsa(fsa, torch, q, k, v, fmt, steps, warmup):
@@ -129,7 +185,14 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default=None)
     ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"))
     args = ap.parse_args()
+    if args.write_traffic:
+        if not args.copy_bytes:
+            print("bench.py: --write-traffic needs the --copy-bytes of the counter run", file=sys.stderr)
+            return 2
+        print(json.dumps(write_traffic(*args.write_traffic, args.copy_bytes)))
+        return 0
     if args.gpus != 1:
         print("bench.py: only --gpus 1 is supported; the fused attention path runs on one GPU "
               "(heads shard across GPUs with no communication, see the design notes)",
@@ -174,11 +237,12 @@ def main() -> int:
             per[fmt]["speedup_vs_bf16"] = bms / per[fmt]["ms_per_step"]
 
     if args.copy_bytes:
+        # a plain streaming kernel of known traffic: reads and writes copy_bytes
         n = args.copy_bytes // 4
         a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
         b = torch.empty_like(a)
         torch.cuda.synchronize()
-        b.copy_(a)
+        torch.neg(a, out=b)
         torch.cuda.synchronize()
 
     head = fmts[0]

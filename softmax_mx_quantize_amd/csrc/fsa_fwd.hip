@@ -51,10 +51,10 @@
 #define FSA_NW8 4
 #endif
 #ifndef FSA_NW6
-#define FSA_NW6 4
+#define FSA_NW6 8
 #endif
 #ifndef FSA_NW4
-#define FSA_NW4 4
+#define FSA_NW4 8
 #endif
 
 namespace fsa {
