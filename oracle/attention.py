@@ -24,48 +24,54 @@ attention, summary; Moving softmax to matrix operations speeds up AI
 inference by over 2x, "Read it as" and the "How it works" figure).  They give
 no formulas, so each step below is a reading:
 
-1. q, k are MX-quantised along D, v along the key axis (blocks of 32 keys
-   aligned at key 0): the MX blocks lie along each product's reduction axis.
-2. s_ij = sum_d q^_id k^_jd.  Key j is visible to row i if j < S and, when
-   causal, j <= i.
+1. The softmax scale goes into Q: q' = fp32(q * c) with
+   c = fp32(log2(e) / sqrt(D)), so that scores come out in binades of the
+   probability.  q' and k are MX-quantised along D, v along the key axis
+   (blocks of 32 keys aligned at key 0): the MX blocks lie along each
+   product's reduction axis.
+2. s_ij = sum_d q'^_id k^_jd (log2-domain scores).  Key j is visible to row i
+   if j < S and, when causal, j <= i.
 3. Frozen max (``frozen_max``): from the visible keys among the first 128,
    m~_i = fp32(max(window max, mean + z_i * std) + bias), population std,
    z_i = sqrt(2 ln n_i) + 1 with n_i the row's visible keys.  The pages fix
    no rule; the mean + z*std term is the expected Gaussian extreme over n_i
    keys plus one standard deviation of margin, so that a well-behaved row
-   rarely exceeds it.  ``bias`` is a test hook (0 in normal use).
-4. Exponential folded into the product.  With d_ij = fp32(s_ij - m~_i)
-   (the max subtraction, one rounding) and t_ij = log2(e) d_ij / sqrt(D),
-   the probability is the bit-pattern exponential: the float32 number whose
-   bit pattern is the integer 2**23 * (127 + x) has the value
+   rarely exceeds it.  ``bias`` (binades) is a test hook, 0 in normal use.
+4. Exponential folded into the score product.  The float32 number whose bit
+   pattern is the integer 2**23 * (127 + x) has the value
    2**floor(x) * (1 + frac(x)), i.e. 2**x linearly interpolated between
-   integer exponents.  One fp32 FMA,
-       y_ij = fp32(beta * d_ij + 2**23 * (127 + pl + Delta_b - kappa_i)),
-       beta = fp32(2**23 * log2(e) / sqrt(D)),
-   followed by truncation to an unsigned integer (0 below zero) gives those
-   bits with 16 or more fraction bits of x.
+   integer exponents (the bit-pattern exponential).  The score product itself
+   produces that integer: with 2**23 folded into q's power-of-two block scale
+   and the accumulator started at fp32(2**23 * (127 + R - kappa_i - m~_i)),
+       y_ij = fp32(2**23 * s_ij + fp32(2**23 * (127 + R - kappa_i) - 2**23 * m~_i)),
+   one rounding at the product's output (R = 62, below).  Truncation to an
+   unsigned integer (0 below zero) gives the bits of
+   p_ij = 2**(t_ij + R - kappa_i), t_ij = s_ij - m~_i, with 16 or more
+   fraction bits of t.  R only places the value inside fp32's range: scores
+   from 188 binades below the reference to 66 above give normal numbers.
 5. MX quantisation of P.  Per block b of 32 keys of a row (keys
-   [32b, 32b+32), visible keys only), e_b = floor(c_b / 2**M) with
-   c_b = round_half_even(alpha * max_j d_ij), alpha = beta / 2**(23-M): the
-   binade of the block's largest value relative to the guess, counted in
-   element codes.  The block is shifted up by
+   [32b, 32b+32), visible keys only), with y0 the kappa = 0 values of step 4,
+   c_b = round_half_even(2**M * (max_j y0_ij / 2**23 - 127 - R)) and
+   e_b = floor(c_b / 2**M): the binade of the block's largest value relative
+   to the guess, counted in element codes.  The block is shifted up by
    Delta_b = min(kappa_i - e_b, 127 - pl) whole binades so that its largest
    value lands in the placement binade 2**pl: the top binade (pl = emax) for
    E2M3 and E2M1; for E4M3 the binade below it (pl = emax - 1), which keeps
    rounding away from E4M3's NaN pattern at no cost in precision (every
-   normal E4M3 binade has the same 3 mantissa bits).  The block's E8M0 scale
-   is 2**-(pl + Delta_b).  Each element is the value of step 4 rounded to the
-   nearest element (ties to even, saturating at the largest finite one),
-   which puts values below the normal range on the subnormal grid by value;
+   normal E4M3 binade has the same 3 mantissa bits).  Each element is
+   p_ij * 2**(pl + Delta_b - R) (an exact power-of-two rescale) rounded to
+   the nearest element (ties to even, saturating at the largest finite one),
+   which puts values below the normal range on the subnormal grid by value.
+   The block's E8M0 scale is 2**-(pl + Delta_b) and
    P~_ij = decode(code_ij) * 2**-(pl + Delta_b), about 2**(t_ij - kappa_i).
 6. Fallback: a row whose guess was too low has some block with e_b > 0
    (its scores exceed m~ by a whole binade in the code domain).  The row is
    recomputed with its reference raised by the whole number of binades
-   kappa_i = max(0, max_b e_b).  Raising the reference by whole
-   binades leaves every code of the row unchanged and lowers every block
-   scale by 2**kappa_i (except where a block shift reaches the E8M0 floor),
-   so the kernel can realise the recomputation as an exact power-of-two
-   rescale of its running sums.
+   kappa_i = max(0, max_b e_b).  Raising the reference by whole binades
+   leaves every code of the row unchanged (up to the fp32 rounding of y) and
+   lowers every block scale by 2**kappa_i (except where a block shift
+   reaches the E8M0 floor), so the kernel can realise the recomputation as
+   an exact power-of-two rescale of its running sums.
 7. O_i = sum_j P~_ij v^_j, l_i = sum_j P~_ij (the same quantised P~ in both,
    as EFQ-Softmax does for its numerator and denominator), and
    out_i = bf16(O_i / l_i).
@@ -83,6 +89,7 @@ from .mx import (FORMATS, BLOCK, Format, decode, encode_values, round_to_format,
 
 WINDOW = 128          # keys that feed the frozen-max guess
 Z_MARGIN = 1.0        # standard deviations above the expected Gaussian extreme
+REF_BINADE = 62       # R of step 4: where a score equal to the reference lands
 LOG2E = 1.0 / math.log(2.0)
 
 
@@ -108,10 +115,24 @@ def _visible(rows: np.ndarray, S: int, causal: bool) -> np.ndarray:
     return np.ones((rows.size, S), dtype=bool)
 
 
-def quantized_operands(q, k, v, fmt):
-    """Dequantised q^, k^ (blocks along D) and v^ (blocks along keys)."""
+def score_scale(D: int) -> float:
+    """c = fp32(log2(e) / sqrt(D)): the softmax scale in binades (step 1)."""
+    return float(np.float32(LOG2E / math.sqrt(D)))
+
+
+def prescale_q(q: np.ndarray) -> np.ndarray:
+    """q' = fp32(q * c), element by element in fp32 (step 1)."""
+    c = np.float32(score_scale(q.shape[1]))
+    return (np.asarray(q, np.float64).astype(np.float32) * c).astype(np.float64)
+
+
+def quantized_operands(q, k, v, fmt, prescale: bool = False):
+    """Dequantised q^ (of q' when ``prescale``), k^ (blocks along D) and
+    v^ (blocks along keys)."""
     f = _fmt(fmt)
     S = k.shape[0]
+    if prescale:
+        q = prescale_q(q)
     qh = mx_dequantize(*mx_quantize(q, f), f)[:, : q.shape[1]]
     kh = mx_dequantize(*mx_quantize(k, f), f)[:, : k.shape[1]]
     vt = mx_dequantize(*mx_quantize(np.ascontiguousarray(v.T), f), f)[:, :S]
@@ -154,17 +175,6 @@ def frozen_max(s: np.ndarray, vis: np.ndarray, bias: float = 0.0) -> np.ndarray:
     z = np.sqrt(2.0 * np.log(n_vis)) + Z_MARGIN
     guess = np.maximum(wmax, mean + z * np.sqrt(var)) + bias
     return guess.astype(np.float32).astype(np.float64)
-
-
-def fused_beta(D: int) -> float:
-    """beta = fp32(2**23 * log2(e) / sqrt(D)): score units -> fp32 exponent-field units."""
-    return float(np.float32((2 ** 23) * LOG2E / math.sqrt(D)))
-
-
-def fused_alpha(fmt, D: int) -> float:
-    """alpha = beta / 2**(23-M): score units -> element-code units (exact in fp32)."""
-    f = _fmt(fmt)
-    return fused_beta(D) / 2 ** (23 - f.mbits)
 
 
 def fma_f32(a: np.ndarray, b: np.ndarray, c: np.ndarray) -> np.ndarray:
@@ -211,9 +221,21 @@ def placement_exponent(fmt) -> int:
     return f.emax - 1 if f.name == "e4m3" else f.emax
 
 
-def fused_probabilities(s: np.ndarray, m_tilde: np.ndarray, vis: np.ndarray, fmt,
-                        D: int) -> Dict[str, np.ndarray]:
-    """Steps 4-6 of the module doc for rows of scores ``s`` [R, S].
+def reference_addend(m_tilde: np.ndarray, kappa: np.ndarray) -> np.ndarray:
+    """fp32(2**23 * (127 + R - kappa) - 2**23 * m~): the accumulator start of
+    the score product (step 4), one rounding."""
+    a = (2.0 ** 23) * (127 + REF_BINADE - np.asarray(kappa, np.float64)) - (2.0 ** 23) * m_tilde
+    return a.astype(np.float32).astype(np.float64)
+
+
+def exponent_field_values(s: np.ndarray, addend: np.ndarray) -> np.ndarray:
+    """y = fp32(2**23 * s + addend) for rows of log2-domain scores (step 4)."""
+    return fma_f32(np.float64(2.0 ** 23), s, addend[:, None])
+
+
+def fused_probabilities(s: np.ndarray, m_tilde: np.ndarray, vis: np.ndarray,
+                        fmt) -> Dict[str, np.ndarray]:
+    """Steps 4-6 of the module doc for rows of log2-domain scores ``s`` [R, S].
 
     Returns the P~ values (float64), the element codes, the per-block shifts
     Delta, the E8M0 scale bytes of P~ and the per-row binade offset kappa
@@ -224,23 +246,22 @@ def fused_probabilities(s: np.ndarray, m_tilde: np.ndarray, vis: np.ndarray, fmt
     pl = placement_exponent(f)
     cap = 127 - pl
     R, S = s.shape
-    beta = fused_beta(D)
-    alpha = fused_alpha(f, D)
-    d = (s - m_tilde[:, None]).astype(np.float32).astype(np.float64)
-    d = np.where(vis, d, -np.inf)
     nb = (S + BLOCK - 1) // BLOCK
-    dp = np.full((R, nb * BLOCK), -np.inf)
-    dp[:, :S] = d
-    g = dp.reshape(R, nb, BLOCK).max(axis=2)         # -inf for blocks with no visible key
-    c = np.rint(alpha * g)                            # alpha*g is exact in float64
-    e = np.floor(c / (2 ** M))                        # block binade relative to the guess
+    s0 = np.where(vis, s, 0.0)
+    # guess-relative block binades from the kappa = 0 values
+    y0 = exponent_field_values(s0, reference_addend(m_tilde, np.zeros(R)))
+    yp = np.full((R, nb * BLOCK), -np.inf)
+    yp[:, :S] = np.where(vis, y0, -np.inf)
+    g = yp.reshape(R, nb, BLOCK).max(axis=2)          # -inf for blocks with no visible key
+    c = np.rint((2 ** M) * (g / 2.0 ** 23 - 127 - REF_BINADE))   # exact in float64
+    e = np.floor(c / (2 ** M))
     kappa = np.maximum(0.0, np.max(e, axis=1))
     delta = np.where(np.isfinite(e), np.minimum(kappa[:, None] - e, cap), cap)
     delta_full = np.repeat(delta, BLOCK, axis=1)[:, :S]
-    base = (2.0 ** 23) * (127 + pl + delta_full - kappa[:, None])
-    y = fma_f32(np.float64(beta), np.where(vis, d, 0.0), base)
+    y = exponent_field_values(s0, reference_addend(m_tilde, kappa))
     y = np.where(vis, y, -np.inf)
     p = bits_to_f32(trunc_u32(y))
+    p = p * np.ldexp(1.0, (pl + delta_full - REF_BINADE).astype(np.int32))
     vals = round_to_format(p, f)
     code = encode_values(vals, f).astype(np.int64)
     P = vals * np.ldexp(1.0, (-pl - delta_full).astype(np.int32))
@@ -258,8 +279,9 @@ def fused_attention(q, k, v, fmt, causal: bool = False, rows=None, bias: float =
     """Fused-Softmax attention output (bf16 values as float64) for one head.
 
     ``q, k, v`` are [S, D] arrays of bf16 values; ``rows`` selects query rows
-    (all by default).  With ``return_info`` also returns the frozen max, the
-    fallback offsets and the P~ values.
+    (all by default); ``bias`` is added to the frozen max (binades).  With
+    ``return_info`` also returns the frozen max, the fallback offsets, the
+    log2-domain scores and the P~ values.
     """
     f = _fmt(fmt)
     q = np.asarray(q, np.float64)
@@ -267,11 +289,11 @@ def fused_attention(q, k, v, fmt, causal: bool = False, rows=None, bias: float =
     v = np.asarray(v, np.float64)
     S, D = k.shape
     rows = _rows(rows, S)
-    qh, kh, vh = quantized_operands(q[rows] if rows.size else q[:0], k, v, f)
+    qh, kh, vh = quantized_operands(q[rows] if rows.size else q[:0], k, v, f, prescale=True)
     s = qh @ kh.T
     vis = _visible(rows, S, causal)
     m_tilde = frozen_max(s, vis, bias)
-    fp = fused_probabilities(s, m_tilde, vis, f, D)
+    fp = fused_probabilities(s, m_tilde, vis, f)
     P = fp["P"]
     O = P @ vh
     l = P.sum(axis=1)

@@ -93,9 +93,33 @@ def test_v_ones_gives_exactly_one(fmt):
 def test_forced_fallback_every_row(fmt):
     announce("fsa forced fallback", fmt)
     q, k, v = (W.random_bf16((1, 2, 400, 128), seed, 1.0) for seed in (9, 10, 11))
-    g, kap, _ = _run(q, k, v, fmt, False, guess_bias=-60.0)
+    g, kap, _ = _run(q, k, v, fmt, False, guess_bias=-8.0)
     assert np.all(kap > 0)
-    ref, rk = _oracle_heads(q, k, v, [fmt] * 2, False, bias=-60.0)
+    ref, rk = _oracle_heads(q, k, v, [fmt] * 2, False, bias=-8.0)
+    _check(g, kap, ref, rk)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_rows_far_above_the_guess(fmt):
+    """Rows whose scores exceed the frozen max by far more than the in-loop
+    block shifts reach (64 binades) are recomputed with the re-based
+    reference; their neighbours in the same wave must come out unchanged."""
+    announce("fsa far fallback", fmt)
+    S, D = 300, 128
+    q, k, v = (W.bf16_bits_to_f64(W.random_bf16((1, 1, S, D), seed, 1.0)) for seed in (12, 13, 14))
+    c = O.attention.score_scale(D)
+    for i, j in ((5, 140), (77, 290), (200, 131)):
+        # q_i along k_j, scaled so that this one score is ~300 binades
+        q[0, 0, i] = k[0, 0, j] * (300.0 / (c * float(k[0, 0, j] @ k[0, 0, j])))
+    q, k, v = (W.f32_to_bf16_bits(x.astype(np.float32)) for x in (q, k, v))
+    g, kap, _ = _run(q, k, v, fmt, False)
+    ref, rk = _oracle_heads(q, k, v, [fmt], False)
+    assert np.all(rk[0, [5, 77, 200]] > 64)
+    _check(g, kap, ref, rk)
+    # the whole tensor far above the guess: every row takes the re-based path
+    g, kap, _ = _run(q, k, v, fmt, False, guess_bias=-100.0)
+    ref, rk = _oracle_heads(q, k, v, [fmt], False, bias=-100.0)
+    assert np.all(rk > 64)
     _check(g, kap, ref, rk)
 
 
