@@ -92,12 +92,14 @@ int fsa_quantize_mx(const void* x_bf16, void* codes, void* scales_e8m0,
  * Softmax scale 1/sqrt(D).  D must be 64 or 128 (else FSA_ERR_UNSUPPORTED).
  * fmt : element format of Q, K, V and P (fsa_fmt).  causal : 0 or 1 (key j
  * visible to query i iff j <= i).
- * The call MX-quantises Q, K (blocks along D) and V (blocks along the keys)
- * into the library workspace, then runs one fused kernel: frozen max from
- * the first 128 keys, scores with the max subtraction folded into the
- * matrix-core accumulator, the bit-pattern exponential and MX quantisation
- * of P in the accumulator epilogue, P V and the row sums (P times a ones
- * block) on the matrix cores, and the whole-binade fallback for rows whose
+ * The call MX-quantises Q times log2(e)/sqrt(D), K (blocks along D) and V
+ * (blocks along the keys) into the library workspace, then runs one fused
+ * kernel: frozen max from the first 128 keys, a score product whose fp32
+ * output already is the bit-pattern exponential's exponent field (softmax
+ * scale in Q, 2^23 in Q's block scale, max subtraction in the accumulator
+ * start), MX quantisation of P in the accumulator epilogue (block shifts
+ * applied through the conversion scale), P V and the row sums (P times a
+ * ones block) on the matrix cores, and the whole-binade fallback for rows whose
  * scores exceed the frozen max, applied as an exact power-of-two rescale.
  * Errors: FSA_ERR_INVALID_ARG (null pointers, non-positive sizes, B*H*S*D
  * beyond 2^40, unknown fmt, causal not 0/1), FSA_ERR_UNSUPPORTED (D not
@@ -120,13 +122,15 @@ int fsa_attention_bf16_ref(const void* q, const void* k, const void* v, void* ou
 
 /* Test and benchmark hooks for fsa_attention_fwd_ex.  Zero-initialise. */
 typedef struct fsa_options {
-  /* Added to every frozen max (score units).  A large negative value makes
-   * every row fall back; 0 in normal use. */
+  /* Added to every frozen max, in binades of the probability (units of
+   * log2(e) * q.k / sqrt(D)).  A negative value of a few binades makes every
+   * row fall back; 0 in normal use. */
   float guess_bias;
   /* Optional device int32 [B][H][S]: receives each row's fallback offset in
    * binades (0 for rows whose scores stayed under the frozen max). */
   int32_t* row_kappa;
-  /* Optional device float [B][H][S]: receives each row's frozen max. */
+  /* Optional device float [B][H][S]: receives each row's frozen max, in
+   * the same binade units as guess_bias. */
   float* row_max_guess;
   /* Optional hipEvent_t (as void*) recorded on `stream` between the
    * quantisation kernels and the attention kernel, for kernel-only timing. */

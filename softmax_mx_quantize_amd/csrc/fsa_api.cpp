@@ -20,7 +20,6 @@ namespace {
 constexpr int kKeyTile = 128;
 
 int fmt_bits(int fmt) { return fmt == FSA_MXFP8_E4M3 ? 8 : (fmt == FSA_MXFP6_E2M3 ? 6 : 4); }
-int fmt_mbits(int fmt) { return fmt == FSA_MXFP4_E2M1 ? 1 : 3; }
 bool fmt_ok(int fmt) { return fmt == FSA_MXFP8_E4M3 || fmt == FSA_MXFP6_E2M3 || fmt == FSA_MXFP4_E2M1; }
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -95,7 +94,7 @@ int validate_attn(const void* q, const void* k, const void* v, void* out, int B,
 
 int quantize(const uint16_t* x, uint8_t* codes, uint8_t* scales, int64_t batch, int64_t rows,
              int64_t cols, int64_t out_rows, int64_t nb_out, int64_t code_stride,
-             int64_t scale_stride, int fmt, int mode, hipStream_t stream) {
+             int64_t scale_stride, int fmt, int mode, hipStream_t stream, float mult = 1.0f) {
   fsa::QuantArgs a;
   a.x = x;
   a.codes = codes;
@@ -107,6 +106,7 @@ int quantize(const uint16_t* x, uint8_t* codes, uint8_t* scales, int64_t batch, 
   a.nb_out = nb_out;
   a.code_stride = code_stride;
   a.scale_stride = scale_stride;
+  a.mult = mult;
   return fsa::launch_mx_quant(a, fmt, mode, stream) == hipSuccess ? FSA_OK : FSA_ERR_HIP;
 }
 
@@ -186,16 +186,28 @@ int fsa_attention_fwd_ex(const void* q, const void* k, const void* v, void* out,
     rl.vc = cv.take((size_t)(nbh * D * sk_alloc * bits / 8));
     rl.vs = cv.take((size_t)(nbh * D * (sk_alloc / 32)));
   }
+  // per-row frozen max and fallback offset, which the fallback kernel reads
+  // back; the caller's arrays when given
+  const int64_t n_rows = (int64_t)B * H * S;
+  const bool own_kappa = !(opt && opt->row_kappa);
+  const bool own_mguess = !(opt && opt->row_max_guess);
+  const size_t rk_off = own_kappa ? cv.take((size_t)n_rows * 4) : 0;
+  const size_t rm_off = own_mguess ? cv.take((size_t)n_rows * 4) : 0;
   uint8_t* ws = nullptr;
   st = workspace(cv.off, &ws);
   if (st != FSA_OK) return st;
+  int32_t* row_kappa = own_kappa ? reinterpret_cast<int32_t*>(ws + rk_off) : opt->row_kappa;
+  float* row_mguess = own_mguess ? reinterpret_cast<float*>(ws + rm_off) : opt->row_max_guess;
 
   const uint16_t* qb = static_cast<const uint16_t*>(q);
   const uint16_t* kb = static_cast<const uint16_t*>(k);
   const uint16_t* vb = static_cast<const uint16_t*>(v);
 
   // MX-quantise Q, K (blocks along D) and V (blocks along the keys, stored
-  // transposed) for every run; padding rows and blocks get zero codes.
+  // transposed) for every run; padding rows and blocks get zero codes.  Q
+  // carries the softmax scale in binades, c = fp32(log2(e) / sqrt(D)), so
+  // that the score product comes out in binades of the probability.
+  const float score_scale = (float)((1.0 / std::log(2.0)) / std::sqrt((double)D));
   for (const RunLayout& rl : runs) {
     const int bits = fmt_bits(rl.fmt);
     const int64_t rb = (int64_t)D * bits / 8;
@@ -204,7 +216,7 @@ int fsa_attention_fwd_ex(const void* q, const void* k, const void* v, void* out,
       const int64_t src = ((int64_t)b * H + rl.h0) * S * D;
       const int64_t w0 = (int64_t)b * rl.hrun;
       st = quantize(qb + src, ws + rl.qc + w0 * sq_alloc * rb, ws + rl.qs + w0 * sq_alloc * (D / 32),
-                    rl.hrun, S, D, sq_alloc, D / 32, rb, D / 32, rl.fmt, 0, stream);
+                    rl.hrun, S, D, sq_alloc, D / 32, rb, D / 32, rl.fmt, 0, stream, score_scale);
       if (st != FSA_OK) return st;
       st = quantize(kb + src, ws + rl.kc + w0 * sk_alloc * rb, ws + rl.ks + w0 * sk_alloc * (D / 32),
                     rl.hrun, S, D, sk_alloc, D / 32, rb, D / 32, rl.fmt, 0, stream);
@@ -226,16 +238,11 @@ int fsa_attention_fwd_ex(const void* q, const void* k, const void* v, void* out,
     a.kc = ws + rl.kc; a.ks = ws + rl.ks;
     a.vc = ws + rl.vc; a.vs = ws + rl.vs;
     a.out = static_cast<uint16_t*>(out);
-    a.row_kappa = opt ? opt->row_kappa : nullptr;
-    a.row_mguess = opt ? opt->row_max_guess : nullptr;
+    a.row_kappa = row_kappa;
+    a.row_mguess = row_mguess;
     a.B = B; a.H = H; a.S = S;
     a.h0 = rl.h0; a.hrun = rl.hrun;
     a.sq_alloc = (int)rl.sq_alloc; a.sk_alloc = (int)sk_alloc;
-    // beta = fp32(2^23 log2(e) / sqrt(D)); alpha = beta / 2^(23-M) exactly
-    const double log2e = 1.0 / std::log(2.0);
-    const float beta = (float)((8388608.0 * log2e) / std::sqrt((double)D));
-    a.beta = beta;
-    a.alpha = std::ldexp(beta, -(23 - fmt_mbits(rl.fmt)));
     a.bias = opt ? opt->guess_bias : 0.0f;
     if (fsa::launch_fsa_fwd(a, kern_fmt(rl.fmt), D, causal, stream) != hipSuccess)
       return FSA_ERR_HIP;

@@ -59,6 +59,23 @@ template <> struct Fmt<FMT_E2M1> {
   static constexpr uint32_t one_code = 0x2;
 };
 
+// Matrix-core operand of 32 elements in the format's packing: FP8 8 dwords,
+// FP6 6 dwords, FP4 4 dwords.  The narrow FP6/FP4 vectors keep registers
+// free that 8-dword operands would fill with zeros.
+template <int F> struct Operand;
+template <> struct Operand<FMT_E4M3> { typedef v8i type; static constexpr int words = 8; };
+template <> struct Operand<FMT_E2M3> { typedef v6i type; static constexpr int words = 6; };
+template <> struct Operand<FMT_E2M1> { typedef v4i type; static constexpr int words = 4; };
+template <int F> using opv = typename Operand<F>::type;
+
+template <int F>
+__device__ __forceinline__ opv<F> zero_operand() {
+  opv<F> o;
+#pragma unroll
+  for (int i = 0; i < Operand<F>::words; ++i) o[i] = 0;
+  return o;
+}
+
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t b) {
   return __uint_as_float(b << 16);
 }
@@ -76,23 +93,27 @@ __device__ __forceinline__ float exp2i(int n) {
   return __uint_as_float((uint32_t)(n + 127) << 23);
 }
 
-// Convert 32 fp32 values (already divided by the block scale) to packed
-// element codes with round-to-nearest-even and saturation.  Output words
-// follow the operand packing: FP8 8 words, FP6 6 words, FP4 4 words.  FP8
-// saturation needs an explicit clamp (the conversion overflows to NaN);
-// callers whose values provably stay in range pass CLAMP = false.
+// Convert 32 fp32 values to packed element codes: each value is divided by
+// a power-of-two scale (exact) and rounded to nearest even, saturating.
+// Elements 0-15 use s_lo and 16-31 use s_hi (one FP8 lane holds two half
+// blocks); FP6/FP4 lanes hold one block and use s_lo for all 32.  Output
+// words follow the operand packing: FP8 8 words, FP6 6 words, FP4 4 words.
+// FP8 saturation needs an explicit clamp (the conversion overflows to NaN);
+// callers whose scaled values provably stay in range pass CLAMP = false.
 template <int F, bool CLAMP> struct Pack32;
 
 template <bool CLAMP> struct Pack32<FMT_E4M3, CLAMP> {
   static __device__ __forceinline__ float sat(float v) {
     return CLAMP ? __builtin_fminf(__builtin_fmaxf(v, -448.0f), 448.0f) : v;
   }
-  static __device__ __forceinline__ void run(const float* y, uint32_t* w) {
+  static __device__ __forceinline__ void run(const float* y, uint32_t* w, float s_lo = 1.0f,
+                                             float s_hi = 1.0f) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+      const float sc = i < 4 ? s_lo : s_hi;
       v2s lo = {0, 0};
-      lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, sat(y[4 * i + 0]), sat(y[4 * i + 1]), 1.0f, false);
-      lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, sat(y[4 * i + 2]), sat(y[4 * i + 3]), 1.0f, true);
+      lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, sat(y[4 * i + 0]), sat(y[4 * i + 1]), sc, false);
+      lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, sat(y[4 * i + 2]), sat(y[4 * i + 3]), sc, true);
       w[i] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
     }
   }
@@ -104,31 +125,33 @@ template <bool CLAMP> struct Pack32<FMT_E4M3, CLAMP> {
 // which corrupts the result.  Issue it with an early-clobber destination and
 // wait states before anything can overwrite its sources.
 template <bool CLAMP> struct Pack32<FMT_E2M3, CLAMP> {
-  static __device__ __forceinline__ void run(const float* y, uint32_t* w) {
+  static __device__ __forceinline__ void run(const float* y, uint32_t* w, float s_lo = 1.0f,
+                                             float = 1.0f) {
     v16f ev, od;
 #pragma unroll
     for (int i = 0; i < 16; ++i) { ev[i] = y[2 * i]; od[i] = y[2 * i + 1]; }
     v6i r;
     asm volatile(
-        "v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, 1.0\n\t"
+        "v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3\n\t"
         "s_nop 7\n\t"
         "s_nop 7"
         : "=&v"(r)
-        : "v"(ev), "v"(od));
+        : "v"(ev), "v"(od), "v"(s_lo));
 #pragma unroll
     for (int i = 0; i < 6; ++i) w[i] = (uint32_t)r[i];
   }
 };
 
 template <bool CLAMP> struct Pack32<FMT_E2M1, CLAMP> {
-  static __device__ __forceinline__ void run(const float* y, uint32_t* w) {
+  static __device__ __forceinline__ void run(const float* y, uint32_t* w, float s_lo = 1.0f,
+                                             float = 1.0f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       uint32_t r = 0;
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * i + 0], y[8 * i + 1], 1.0f, 0);
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * i + 2], y[8 * i + 3], 1.0f, 1);
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * i + 4], y[8 * i + 5], 1.0f, 2);
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * i + 6], y[8 * i + 7], 1.0f, 3);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * i + 0], y[8 * i + 1], s_lo, 0);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * i + 2], y[8 * i + 3], s_lo, 1);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * i + 4], y[8 * i + 5], s_lo, 2);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * i + 6], y[8 * i + 7], s_lo, 3);
       w[i] = r;
     }
   }

@@ -59,18 +59,65 @@
 
 namespace fsa {
 
+// The builtin of the scaled MFMA only takes 8-dword operands; the narrow
+// FP6/FP4 forms of the same intrinsic are reached through its overloaded
+// LLVM name.  (Compiler instructions: the hazard handling is the same.)
+__device__ v4f mfma_scale_v6(v6i a, v6i b, v4f c, int cbsz, int blgp, int opsel_a, int sa,
+                             int opsel_b, int sb)
+    __asm("llvm.amdgcn.mfma.scale.f32.16x16x128.f8f6f4.v6i32.v6i32");
+__device__ v4f mfma_scale_v4(v4i a, v4i b, v4f c, int cbsz, int blgp, int opsel_a, int sa,
+                             int opsel_b, int sb)
+    __asm("llvm.amdgcn.mfma.scale.f32.16x16x128.f8f6f4.v4i32.v4i32");
+
 namespace {
 
 constexpr int KT = 128;          // keys per tile
 constexpr float MAGIC = 12582912.0f;   // 1.5 * 2^23: float + MAGIC rounds to an integer
+// A score equal to the reference gives the fp32 pattern of 2^REF, so scores
+// from 188 binades below it to 66 above map to normal fp32 numbers.
+constexpr int REF = 62;
+
+// Binade of a block relative to the reference, in element codes:
+// floor(RNE(2^M (y / 2^23 - 127 - REF)) / 2^M) for the block's largest
+// exponent-field value y.  y * 2^(M-23) is exact, and adding the integer
+// constant plus MAGIC rounds once, to nearest even.  Blocks whose largest
+// value lies below 2^-(127+REF) (or that are fully masked, y = -inf) count as
+// y = 0, which already puts them beyond the largest block shift.  Values
+// more than HI_BINADE binades above the reference count as exactly that
+// many (the MAGIC window holds 2^22 codes); the row then falls back with
+// kappa = HI_BINADE, which is exact for every score within 2^18 binades of
+// its frozen max.
+constexpr int HI_BINADE = 1 << 18;
+// Largest guess-relative block binade the main sweep absorbs by block shifts
+// alone; rows above it go to the fallback kernel.
+constexpr int EXT = 64;
+static_assert(HI_BINADE > EXT, "clamped binades must reach the fallback kernel");
+template <int M>
+__device__ __forceinline__ int block_binade(float y) {
+  const float yc = __builtin_amdgcn_fmed3f(y, 0.0f, 8388608.0f * (float)(127 + REF + HI_BINADE));
+  const float t = __builtin_fmaf(yc, (float)(1 << M) * 0x1p-23f,
+                                 MAGIC - (float)((1 << M) * (127 + REF)));
+  return (int)(__float_as_uint(t) - __float_as_uint(MAGIC)) >> M;
+}
+
+// Divisor of the scaled conversions for a block whose P~ scale byte is sb:
+// 2^(sb + REF - 127), taking the bit-pattern value 2^(t + REF) to
+// 2^(t + pl + Delta).
+__device__ __forceinline__ float conv_scale(int sb) {
+  return __uint_as_float((uint32_t)(sb + REF) << 23);
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Truncation toward zero to u32 (v_cvt_u32_f32, which saturates and maps NaN
+// and negatives to 0; the exponential relies on that).  It must stay a
+// compiler-visible conversion: the epilogue feeds it straight from MFMA
+// results, and only instructions the compiler sees get the wait states that
+// reading an MFMA result requires.  Its input must come straight from the
+// product (never a select with constants), so that no out-of-range case can
+// be folded away at compile time; masking happens on the integer result.
 __device__ __forceinline__ uint32_t cvt_u32_trunc(float y) {
-  // Truncation toward zero with saturation; negative and NaN give 0.
-  uint32_t u;
-  asm("v_cvt_u32_f32 %0, %1" : "=v"(u) : "v"(y));
-  return u;
+  return (uint32_t)y;
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
@@ -99,9 +146,9 @@ __device__ __forceinline__ int swz_v(int row) { return row & 7; }
 // A lane's 32 operand elements along a 128-byte swizzled LDS row.  `len` is
 // the number of valid K elements of the row (elements past it are zero).
 template <int F>
-__device__ __forceinline__ v8i lds_operand(const uint8_t* row, int sw, int g, int len) {
-  v8i o = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (Fmt<F>::bits == 8) {
+__device__ __forceinline__ opv<F> lds_operand(const uint8_t* row, int sw, int g, int len) {
+  opv<F> o = zero_operand<F>();
+  if constexpr (Fmt<F>::bits == 8) {
     if (16 * g < len) {
       uint4 a = *reinterpret_cast<const uint4*>(row + 16 * (g ^ sw));
       o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
@@ -110,7 +157,7 @@ __device__ __forceinline__ v8i lds_operand(const uint8_t* row, int sw, int g, in
       uint4 b = *reinterpret_cast<const uint4*>(row + 16 * ((4 + g) ^ sw));
       o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
     }
-  } else if (Fmt<F>::bits == 6) {
+  } else if constexpr (Fmt<F>::bits == 6) {
     if (32 * g < len) {
 #pragma unroll
       for (int i = 0; i < 3; ++i) {
@@ -130,9 +177,9 @@ __device__ __forceinline__ v8i lds_operand(const uint8_t* row, int sw, int g, in
 
 // The same 32 elements straight from global memory (unswizzled row).
 template <int F>
-__device__ __forceinline__ v8i global_operand(const uint8_t* row, int g, int len) {
-  v8i o = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (Fmt<F>::bits == 8) {
+__device__ __forceinline__ opv<F> global_operand(const uint8_t* row, int g, int len) {
+  opv<F> o = zero_operand<F>();
+  if constexpr (Fmt<F>::bits == 8) {
     if (16 * g < len) {
       uint4 a = *reinterpret_cast<const uint4*>(row + 16 * g);
       o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
@@ -141,7 +188,7 @@ __device__ __forceinline__ v8i global_operand(const uint8_t* row, int g, int len
       uint4 b = *reinterpret_cast<const uint4*>(row + 64 + 16 * g);
       o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
     }
-  } else if (Fmt<F>::bits == 6) {
+  } else if constexpr (Fmt<F>::bits == 6) {
     if (32 * g < len) {
       const uint2* p = reinterpret_cast<const uint2*>(row + 24 * g);
       uint2 a = p[0], b = p[1], c = p[2];
@@ -156,20 +203,28 @@ __device__ __forceinline__ v8i global_operand(const uint8_t* row, int g, int len
   return o;
 }
 
+// The scaled MFMA with operands of the format's own width (declared above,
+// outside this namespace).
+
 template <int F>
-__device__ __forceinline__ v4f mfma(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, Fmt<F>::mfma, Fmt<F>::mfma,
-                                                          0, sa, 0, sb);
+__device__ __forceinline__ v4f mfma(const opv<F>& a, const opv<F>& b, const v4f& c, int sa, int sb) {
+  if constexpr (Fmt<F>::bits == 8)
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, Fmt<F>::mfma, Fmt<F>::mfma,
+                                                            0, sa, 0, sb);
+  else if constexpr (Fmt<F>::bits == 6)
+    return mfma_scale_v6(a, b, c, Fmt<F>::mfma, Fmt<F>::mfma, 0, sa, 0, sb);
+  else
+    return mfma_scale_v4(a, b, c, Fmt<F>::mfma, Fmt<F>::mfma, 0, sa, 0, sb);
 }
 
 template <int F>
-__device__ __forceinline__ v8i ones_operand() {
+__device__ __forceinline__ opv<F> ones_operand() {
   constexpr int BITS = Fmt<F>::bits;
   constexpr uint32_t c = Fmt<F>::one_code;
-  v8i o = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (BITS == 8) {
+  opv<F> o = zero_operand<F>();
+  if constexpr (BITS == 8) {
     for (int i = 0; i < 8; ++i) o[i] = (int)(c * 0x01010101u);
-  } else if (BITS == 4) {
+  } else if constexpr (BITS == 4) {
     for (int i = 0; i < 4; ++i) o[i] = (int)(c * 0x11111111u);
   } else {
     // 32 six-bit fields: 4 fields make 3 bytes, repeated.
@@ -337,7 +392,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   if (n_tiles > 0) issue_tile(0, 0);
 
   // ---- Q^ fragments (B operand of the score product), one per subtile
-  v8i qf[NSUB];
+  opv<F> qf[NSUB];
   int qsc[NSUB];
   {
     const uint8_t* qc = a.qc + wi * (int64_t)a.sq_alloc * RB;
@@ -346,14 +401,17 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
     for (int s = 0; s < NSUB; ++s) {
       const int q = q_wave + 16 * s + r;
       qf[s] = global_operand<F>(qc + (int64_t)q * RB, g, D);
-      qsc[s] = g < NDB ? (int)qs[(int64_t)q * NDB + g] : 127;
+      // 2^23 rides on Q's E8M0 scale, so the product is 2^23 s: the
+      // exponent-field units of the bit-pattern exponential (255 stays NaN)
+      const int qb = g < NDB ? (int)qs[(int64_t)q * NDB + g] : 127;
+      qsc[s] = qb == 255 ? 255 : min(qb + 23, 254);
     }
   }
 
   // A operand of the score product for 16-key slice j of the tile in stage
   // st: row R of the slice is key kpos(R/4, 4j + R%4), so that output row
   // 4g+i lands on the lane's operand position 4j+i.
-  auto k_frag = [&](int st, int j, int& sc) -> v8i {
+  auto k_frag = [&](int st, int j, int& sc) -> opv<F> {
     const int kk = kpos<F>(r >> 2, 4 * j + (r & 3));
     const uint8_t* base = lds + st * STAGE;
     sc = g < NDB ? (int)base[K_BYTES + V_BYTES + kk * NDB + g] : 127;
@@ -373,7 +431,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       int sc;
-      const v8i kf = k_frag(0, j, sc);
+      const opv<F> kf = k_frag(0, j, sc);
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) acc[s][j] = mfma<F>(kf, qf[s], zero4, sc, qsc[s]);
     }
@@ -407,7 +465,8 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
       const float sd = __builtin_sqrtf(ss / (float)(cnt > 0 ? cnt : 1));
       const int nvis = CAUSAL ? (q + 1 < S ? q + 1 : S) : S;
       const float z = __builtin_sqrtf(2.0f * __builtin_logf((float)nvis)) + 1.0f;
-      mg[s] = __builtin_fmaxf(mx, mean + z * sd) + a.bias;
+      // statistics of 2^23 s, back to binades (exact power-of-two scaling)
+      mg[s] = __builtin_fmaxf(mx, mean + z * sd) * 0x1p-23f + a.bias;
     }
   }
 
@@ -416,8 +475,8 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   // its codes and takes an E8M0 scale 2^e_b above the guess's: exactly the
   // row the oracle re-bases by kappa = max e_b, scaled by 2^kappa in both
   // O and l.  Only a row beyond EXT binades (scale bytes or fp32 sums could
-  // overflow) is recomputed after the sweep with the re-basing made explicit.
-  constexpr int EXT = 64;
+  // overflow) is recomputed by the fallback kernel with the re-basing made
+  // explicit.
   v4f O[NSUB][NDT];
   v4f L[NSUB];
   int kmax[NSUB];
@@ -426,13 +485,13 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   for (int s = 0; s < NSUB; ++s) {
     L[s] = zero4;
     kmax[s] = -1000000;
-    minit[s] = v4f{-mg[s], -mg[s], -mg[s], -mg[s]};
+    // accumulator start: fp32(2^23 (127 + R) - 2^23 m~), one rounding
+    const float c0 = __builtin_fmaf(-8388608.0f, mg[s], 8388608.0f * (127 + REF));
+    minit[s] = v4f{c0, c0, c0, c0};
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) O[s][dt] = zero4;
   }
-  const v8i ones = ones_operand<F>();
-  const float alpha = a.alpha, beta = a.beta;
-  const float gmin = -2097152.0f / alpha;    // keeps alpha*g inside the MAGIC window
+  const opv<F> ones = ones_operand<F>();
 
   // Lane-constant LDS byte offsets.  For slice j of the score product the
   // lane's K^ row is kk0 + 4j (+48 for the FP8 high half), and its swizzle
@@ -456,9 +515,9 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   const bool k_live = 32 * g < D;               // FP6/FP4 lane groups past D
   const bool k_hi = 64 + 16 * g < D;            // FP8 high half present
 
-  auto frag = [&](const uint8_t* base, const int* off, int imm, bool live, bool hi) -> v8i {
-    v8i o = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (BITS == 8) {
+  auto frag = [&](const uint8_t* base, const int* off, int imm, bool live, bool hi) -> opv<F> {
+    opv<F> o = zero_operand<F>();
+    if constexpr (BITS == 8) {
       if (live) {
         const uint4 a0 = *reinterpret_cast<const uint4*>(base + off[0] + imm);
         o[0] = a0.x; o[1] = a0.y; o[2] = a0.z; o[3] = a0.w;
@@ -467,7 +526,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
         const uint4 a1 = *reinterpret_cast<const uint4*>(base + off[1] + imm);
         o[4] = a1.x; o[5] = a1.y; o[6] = a1.z; o[7] = a1.w;
       }
-    } else if (BITS == 6) {
+    } else if constexpr (BITS == 6) {
       if (live) {
 #pragma unroll
         for (int i = 0; i < 3; ++i) {
@@ -490,73 +549,68 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
     for (int j = 0; j < 8; ++j) {
       const int jrow = 4 * j + ((BITS == 8 && j >= 4) ? 48 : 0);
       const int sc = g < NDB ? (int)base[ks_off + jrow * NDB] : 127;
-      const v8i kf = frag(base, k_off, jrow * RS, BITS == 8 ? 16 * g < D : k_live,
+      const opv<F> kf = frag(base, k_off, jrow * RS, BITS == 8 ? 16 * g < D : k_live,
                           BITS == 8 ? k_hi : false);
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) acc[s][j] = mfma<F>(kf, qf[s], minit[s], sc, qsc[s]);
     }
-    v8i pw[NSUB];
+    opv<F> pw[NSUB];
     int psc[NSUB];
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
-      float x[32];
+      // The bit-pattern exponential: y's integer part is the fp32 pattern of
+      // 2^(t + R).  It is monotone in y, and exact wherever y >= 2^24 (below,
+      // the block sits beyond the largest shift anyway), so the block maxima
+      // are taken on the integers and y is dead from here on.  Masked keys
+      // get pattern 0 (value 0) after the conversion.
+      uint32_t pu[32];
 #pragma unroll
-      for (int p = 0; p < 32; ++p) x[p] = acc[s][p >> 2][p & 3];
+      for (int p = 0; p < 32; ++p) pu[p] = cvt_u32_trunc(acc[s][p >> 2][p & 3]);
       if (MASKED) {
         const int q = q_wave + 16 * s + r;
 #pragma unroll
         for (int p = 0; p < 32; ++p) {
           const int key = key0 + kpos<F>(g, p);
           const bool vis = key < S && (!CAUSAL || key <= q);
-          x[p] = vis ? x[p] : -INFINITY;
+          pu[p] = vis ? pu[p] : 0u;
         }
       }
       // block maxima: one block per lane (FP6/FP4) or two half blocks (FP8)
-      float m0 = __builtin_fmaxf(__builtin_fmaxf(x[0], x[1]), x[2]);
-      float m1 = __builtin_fmaxf(__builtin_fmaxf(x[16], x[17]), x[18]);
+      uint32_t m0 = max(max(pu[0], pu[1]), pu[2]);
+      uint32_t m1 = max(max(pu[16], pu[17]), pu[18]);
 #pragma unroll
       for (int p = 3; p < 15; p += 2) {
-        m0 = __builtin_fmaxf(__builtin_fmaxf(m0, x[p]), x[p + 1]);
-        m1 = __builtin_fmaxf(__builtin_fmaxf(m1, x[16 + p]), x[17 + p]);
+        m0 = max(max(m0, pu[p]), pu[p + 1]);
+        m1 = max(max(m1, pu[16 + p]), pu[17 + p]);
       }
-      m0 = __builtin_fmaxf(m0, x[15]);
-      m1 = __builtin_fmaxf(m1, x[31]);
+      m0 = max(m0, pu[15]);
+      m1 = max(m1, pu[31]);
       if (BITS == 8) {
-        m0 = __builtin_fmaxf(m0, __shfl_xor(m0, 16));
-        m1 = __builtin_fmaxf(m1, __shfl_xor(m1, 16));
+        m0 = max(m0, (uint32_t)__shfl_xor((int)m0, 16));
+        m1 = max(m1, (uint32_t)__shfl_xor((int)m1, 16));
       } else {
-        m0 = __builtin_fmaxf(m0, m1);
+        m0 = max(m0, m1);
         m1 = m0;
       }
-      // block binade relative to the guess: floor(round(alpha * max) / 2^M)
-      auto binade = [&](float m) -> int {
-        const float mc = __builtin_fmaxf(m, gmin);
-        const float tt = __builtin_fmaf(alpha, mc, MAGIC);
-        const int c = (int)(__float_as_uint(tt) - __float_as_uint(MAGIC));
-        return c >> MB;
-      };
-      const int e0 = binade(m0), e1 = binade(m1);
+      const int e0 = block_binade<MB>((float)m0), e1 = block_binade<MB>((float)m1);
       kmax[s] = max(kmax[s], max(e0, e1));
-      const int d0 = min(-min(e0, EXT), CAP);
-      const int d1 = min(-min(e1, EXT), CAP);
-      const float base0 = (float)(127 + PL + d0) * 8388608.0f;
-      const float base1 = (float)(127 + PL + d1) * 8388608.0f;
+      // block shifts relative to the guess; P~ scale bytes 127 - pl - d.  The
+      // conversion divides by 2^(sb + R - 127) = 2^(R - pl - d).
+      const int sb0 = 127 - PL - min(-min(e0, EXT), CAP);
+      const int sb1 = 127 - PL - min(-min(e1, EXT), CAP);
       float pv[32];
 #pragma unroll
-      for (int p = 0; p < 32; ++p) {
-        const float y = __builtin_fmaf(beta, x[p], p < 16 ? base0 : base1);
-        pv[p] = __uint_as_float(cvt_u32_trunc(y));
-      }
+      for (int p = 0; p < 32; ++p) pv[p] = __uint_as_float(pu[p]);
       uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      Pack32<F, false>::run(pv, w);
+      Pack32<F, false>::run(pv, w, conv_scale(sb0), conv_scale(sb1));
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pw[s][i] = (int)w[i];
-      psc[s] = p_scale<BITS>(127 - PL - d0, 127 - PL - d1, g);
+      for (int i = 0; i < Operand<F>::words; ++i) pw[s][i] = (int)w[i];
+      psc[s] = p_scale<BITS>(sb0, sb1, g);
     }
     // P V and the row sums on the matrix cores
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const v8i vf = frag(base, v_off, 16 * dt * RS, true, true);
+      const opv<F> vf = frag(base, v_off, 16 * dt * RS, true, true);
       const int vsc = (int)base[vs_off + 64 * dt];
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) O[s][dt] = mfma<F>(vf, pw[s], O[s][dt], vsc, psc[s]);
@@ -593,90 +647,15 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
     st = st == NSTAGE - 1 ? 0 : st + 1;
   }
 
-  // row offsets in binades (the oracle's kappa)
+  // row offsets in binades (the oracle's kappa); rows beyond EXT come out
+  // wrong here and are recomputed by the fallback kernel
   int kap[NSUB];
-  bool extreme = false;
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
     int k = kmax[s];
     k = max(k, __shfl_xor(k, 16));
     k = max(k, __shfl_xor(k, 32));
     kap[s] = k > 0 ? k : 0;
-    extreme |= kap[s] > EXT;
-  }
-  if (__builtin_amdgcn_ballot_w64(extreme) != 0) {
-    // Cold path: rows whose scores exceed the guess by more than EXT
-    // binades.  Recompute this wave's rows with the re-based reference
-    // (Delta_b = min(kappa - e_b, CAP)), reading K^ and V^T from global memory.
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      L[s] = zero4;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) O[s][dt] = zero4;
-    }
-    for (int t = 0; t < n_tiles; ++t) {
-      const int key0 = t * KT;
-      v4f acc[NSUB][8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int kk = kpos<F>(r >> 2, 4 * j + (r & 3));
-        const int sc = g < NDB ? (int)ks[(int64_t)(key0 + kk) * NDB + g] : 127;
-        const v8i kf = global_operand<F>(kc + (int64_t)(key0 + kk) * RB, g, D);
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) acc[s][j] = mfma<F>(kf, qf[s], minit[s], sc, qsc[s]);
-      }
-      v8i pw[NSUB];
-      int psc[NSUB];
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) {
-        const int q = q_wave + 16 * s + r;
-        float x[32];
-#pragma unroll
-        for (int p = 0; p < 32; ++p) {
-          const int key = key0 + kpos<F>(g, p);
-          const bool vis = key < S && (!CAUSAL || key <= q);
-          x[p] = vis ? acc[s][p >> 2][p & 3] : -INFINITY;
-        }
-        float m0 = x[0], m1 = x[16];
-#pragma unroll
-        for (int p = 1; p < 16; ++p) { m0 = __builtin_fmaxf(m0, x[p]); m1 = __builtin_fmaxf(m1, x[16 + p]); }
-        if (BITS == 8) {
-          m0 = __builtin_fmaxf(m0, __shfl_xor(m0, 16));
-          m1 = __builtin_fmaxf(m1, __shfl_xor(m1, 16));
-        } else {
-          m0 = __builtin_fmaxf(m0, m1);
-          m1 = m0;
-        }
-        auto binade = [&](float m) -> int {
-          const float mc = __builtin_fmaxf(m, gmin);
-          const float tt = __builtin_fmaf(alpha, mc, MAGIC);
-          return (int)(__float_as_uint(tt) - __float_as_uint(MAGIC)) >> MB;
-        };
-        const int e0 = binade(m0), e1 = binade(m1);
-        const int d0 = min(kap[s] - e0, CAP), d1 = min(kap[s] - e1, CAP);
-        const float base0 = (float)(127 + PL + d0 - kap[s]) * 8388608.0f;
-        const float base1 = (float)(127 + PL + d1 - kap[s]) * 8388608.0f;
-        float pv[32];
-#pragma unroll
-        for (int p = 0; p < 32; ++p)
-          pv[p] = __uint_as_float(cvt_u32_trunc(__builtin_fmaf(beta, x[p], p < 16 ? base0 : base1)));
-        uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        Pack32<F, false>::run(pv, w);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pw[s][i] = (int)w[i];
-        psc[s] = p_scale<BITS>(127 - PL - d0, 127 - PL - d1, g);
-      }
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const int d = 16 * dt + r;
-        const v8i vf = global_operand<F>(vc + d * v_row + (int64_t)t * VRB, g, KT);
-        const int vsc = (int)vs[(int64_t)d * vs_row + t * (KT / 32) + g];
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) O[s][dt] = mfma<F>(vf, pw[s], O[s][dt], vsc, psc[s]);
-      }
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) L[s] = mfma<F>(ones, pw[s], L[s], 127, psc[s]);
-    }
   }
 
   // ---- normalise and store: lane (g, r) holds O[q][16dt + 4g + i]
@@ -693,8 +672,206 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
         *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = make_uint2(lo, hi);
       }
       if (g == 0) {
-        if (a.row_kappa) a.row_kappa[bh * S + q] = kap[s];
-        if (a.row_mguess) a.row_mguess[bh * S + q] = mg[s];
+        a.row_kappa[bh * S + q] = kap[s];
+        a.row_mguess[bh * S + q] = mg[s];
+      }
+    }
+  }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+// Fallback for rows whose scores exceed the frozen max by more than EXT
+// binades: one wave per 32 query rows (two subtiles of 16).  A wave whose
+// rows all stayed within EXT exits at once; otherwise it recomputes its rows
+// from global memory with each row's reference raised by its kappa
+// (accumulator start and block shifts re-based, no in-loop clamp), reading
+// the frozen max and kappa the main kernel stored, and overwrites their
+// outputs.  Rows within EXT come out as the main kernel left them (the
+// re-based sums are the same up to the common power-of-two factor).
+template <int F, int D, bool CAUSAL>
+__global__ void __launch_bounds__(64) fsa_fallback_kernel(AttnArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NSUB = 2;
+  constexpr int BITS = Fmt<F>::bits;
+  constexpr int MB = Fmt<F>::mbits;
+  constexpr int PL = F == FMT_E4M3 ? Fmt<F>::emax - 1 : Fmt<F>::emax;
+  constexpr int CAP = 127 - PL;
+  constexpr int RB = D * BITS / 8;
+  constexpr int NDB = D / 32;
+  constexpr int NDT = D / 16;
+  constexpr int VRB = KT * BITS / 8;
+  const int lane = threadIdx.x;
+  const int g = lane >> 4;
+  const int r = lane & 15;
+  const int S = a.S;
+  const int ng = (S + 16 * NSUB - 1) / (16 * NSUB);
+  const int64_t wi = blockIdx.x / ng;
+  if (wi >= (int64_t)a.B * a.hrun) return;
+  const int b = (int)wi / a.hrun;
+  const int h = a.h0 + ((int)wi - b * a.hrun);
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int q0 = (int)(blockIdx.x - wi * ng) * 16 * NSUB;
+
+  int kap[NSUB];
+  float mg[NSUB];
+  bool extreme = false;
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    const int q = q0 + 16 * s + r;
+    kap[s] = q < S ? a.row_kappa[bh * S + q] : 0;
+    mg[s] = q < S ? a.row_mguess[bh * S + q] : 0.0f;
+    extreme |= kap[s] > EXT;
+  }
+  if (__builtin_amdgcn_ballot_w64(extreme) == 0) return;
+
+  const uint8_t* kc = a.kc + wi * (int64_t)a.sk_alloc * RB;
+  const uint8_t* ks = a.ks + wi * (int64_t)a.sk_alloc * NDB;
+  const int64_t v_row = (int64_t)a.sk_alloc * BITS / 8;
+  const uint8_t* vc = a.vc + wi * (int64_t)D * v_row;
+  const int vs_row = a.sk_alloc / 32;
+  const uint8_t* vs = a.vs + wi * (int64_t)D * vs_row;
+  const uint8_t* qc = a.qc + wi * (int64_t)a.sq_alloc * RB;
+  const uint8_t* qs = a.qs + wi * (int64_t)a.sq_alloc * NDB;
+
+  opv<F> qf[NSUB];
+  int qsc[NSUB];
+  v4f mk[NSUB], O[NSUB][NDT], L[NSUB];
+  const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    const int q = q0 + 16 * s + r;      // < sq_alloc: the query padding covers whole groups
+    qf[s] = global_operand<F>(qc + (int64_t)q * RB, g, D);
+    const int qb = g < NDB ? (int)qs[(int64_t)q * NDB + g] : 127;
+    qsc[s] = qb == 255 ? 255 : min(qb + 23, 254);
+    L[s] = zero4;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) O[s][dt] = zero4;
+  }
+  const opv<F> ones = ones_operand<F>();
+
+  int n_tiles = (S + KT - 1) / KT;
+  if (CAUSAL) {
+    const int last_q = q0 + 16 * NSUB - 1 < S - 1 ? q0 + 16 * NSUB - 1 : S - 1;
+    n_tiles = min(n_tiles, last_q / KT + 1);
+  }
+  // The main sweep measures binades on the integer patterns, which saturate
+  // some 320 binades above the guess; take kappa again from the fp32 values
+  // (exact to HI_BINADE).
+  {
+    v4f m0init[NSUB];
+    int km[NSUB];
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      const float c0 = __builtin_fmaf(-8388608.0f, mg[s], 8388608.0f * (float)(127 + REF));
+      m0init[s] = v4f{c0, c0, c0, c0};
+      km[s] = -(1 << 30);
+    }
+    for (int t = 0; t < n_tiles; ++t) {
+      const int key0 = t * KT;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int kk = kpos<F>(r >> 2, 4 * j + (r & 3));
+        const int sc = g < NDB ? (int)ks[(int64_t)(key0 + kk) * NDB + g] : 127;
+        const opv<F> kf = global_operand<F>(kc + (int64_t)(key0 + kk) * RB, g, D);
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+          const v4f y = mfma<F>(kf, qf[s], m0init[s], sc, qsc[s]);
+          const int q = q0 + 16 * s + r;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = key0 + kpos<F>(g, 4 * j + i);
+            const bool vis = key < S && (!CAUSAL || key <= q);
+            // the binade of each element bounds that of its block's maximum
+            if (vis) km[s] = max(km[s], block_binade<MB>(y[i]));
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      int k = km[s];
+      k = max(k, __shfl_xor(k, 16));
+      k = max(k, __shfl_xor(k, 32));
+      kap[s] = k > 0 ? k : 0;
+      const float c0 = __builtin_fmaf(-8388608.0f, mg[s], 8388608.0f * (float)(127 + REF - kap[s]));
+      mk[s] = v4f{c0, c0, c0, c0};
+      const int q = q0 + 16 * s + r;
+      if (g == 0 && q < S) a.row_kappa[bh * S + q] = kap[s];
+    }
+  }
+  for (int t = 0; t < n_tiles; ++t) {
+    const int key0 = t * KT;
+    v4f acc[NSUB][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int kk = kpos<F>(r >> 2, 4 * j + (r & 3));
+      const int sc = g < NDB ? (int)ks[(int64_t)(key0 + kk) * NDB + g] : 127;
+      const opv<F> kf = global_operand<F>(kc + (int64_t)(key0 + kk) * RB, g, D);
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) acc[s][j] = mfma<F>(kf, qf[s], mk[s], sc, qsc[s]);
+    }
+    opv<F> pw[NSUB];
+    int psc[NSUB];
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      const int q = q0 + 16 * s + r;
+      float x[32];
+#pragma unroll
+      for (int p = 0; p < 32; ++p) {
+        const int key = key0 + kpos<F>(g, p);
+        const bool vis = key < S && (!CAUSAL || key <= q);
+        x[p] = vis ? acc[s][p >> 2][p & 3] : -INFINITY;
+      }
+      float m0 = x[0], m1 = x[16];
+#pragma unroll
+      for (int p = 1; p < 16; ++p) { m0 = __builtin_fmaxf(m0, x[p]); m1 = __builtin_fmaxf(m1, x[16 + p]); }
+      if (BITS == 8) {
+        m0 = __builtin_fmaxf(m0, __shfl_xor(m0, 16));
+        m1 = __builtin_fmaxf(m1, __shfl_xor(m1, 16));
+      } else {
+        m0 = __builtin_fmaxf(m0, m1);
+        m1 = m0;
+      }
+      // binades relative to the raised reference: shifts need no EXT clamp
+      const int sb0 = 127 - PL - min(-block_binade<MB>(m0), CAP);
+      const int sb1 = 127 - PL - min(-block_binade<MB>(m1), CAP);
+      float pv[32];
+#pragma unroll
+      for (int p = 0; p < 32; ++p) {
+        const int key = key0 + kpos<F>(g, p);
+        const bool vis = key < S && (!CAUSAL || key <= q);
+        const uint32_t u = cvt_u32_trunc(acc[s][p >> 2][p & 3]);
+        pv[p] = __uint_as_float(vis ? u : 0u);
+      }
+      uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      Pack32<F, false>::run(pv, w, conv_scale(sb0), conv_scale(sb1));
+#pragma unroll
+      for (int i = 0; i < Operand<F>::words; ++i) pw[s][i] = (int)w[i];
+      psc[s] = p_scale<BITS>(sb0, sb1, g);
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int d = 16 * dt + r;
+      const opv<F> vf = global_operand<F>(vc + d * v_row + (int64_t)t * VRB, g, KT);
+      const int vsc = (int)vs[(int64_t)d * vs_row + t * (KT / 32) + g];
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) O[s][dt] = mfma<F>(vf, pw[s], O[s][dt], vsc, psc[s]);
+    }
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) L[s] = mfma<F>(ones, pw[s], L[s], 127, psc[s]);
+  }
+
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    const int q = q0 + 16 * s + r;
+    if (q < S) {
+      const float inv = 1.0f / L[s][0];
+      uint16_t* orow = a.out + (bh * S + q) * (int64_t)D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const uint32_t lo = f32_to_bf16_rne(O[s][dt][0] * inv) | ((uint32_t)f32_to_bf16_rne(O[s][dt][1] * inv) << 16);
+        const uint32_t hi = f32_to_bf16_rne(O[s][dt][2] * inv) | ((uint32_t)f32_to_bf16_rne(O[s][dt][3] * inv) << 16);
+        *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = make_uint2(lo, hi);
       }
     }
   }
@@ -724,6 +901,8 @@ static hipError_t launch3(const AttnArgs& a, hipStream_t stream) {
   const int n_items = (a.S + QW - 1) / QW * a.B * a.hrun;
   dim3 grid((n_items + 7) / 8 * 8);
   hipLaunchKernelGGL((fsa_fwd_kernel<F, D, CAUSAL, NSUB, NWAVES>), grid, dim3(NWAVES * 64), 0, stream, a);
+  const int n_groups = (a.S + 31) / 32 * a.B * a.hrun;
+  hipLaunchKernelGGL((fsa_fallback_kernel<F, D, CAUSAL>), dim3(n_groups), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -21,6 +21,7 @@ struct QuantArgs {
   int64_t nb_out;        // blocks per output row
   int64_t code_stride;   // bytes between output code rows
   int64_t scale_stride;  // bytes between output scale rows
+  float mult;            // every input value is multiplied by this (fp32) first
 };
 
 hipError_t launch_mx_quant(const QuantArgs& a, int fmt, int mode, hipStream_t stream);
@@ -38,12 +39,12 @@ struct AttnArgs {
   const uint8_t* kc; const uint8_t* ks;
   const uint8_t* vc; const uint8_t* vs;
   uint16_t* out;                 // bf16 [B][H][S][D]
-  int32_t* row_kappa;            // optional [B][H][S]
-  float* row_mguess;             // optional [B][H][S]
+  int32_t* row_kappa;            // [B][H][S], written by the main kernel, read by the fallback
+  float* row_mguess;             // [B][H][S], likewise (frozen max, binades)
   int B, H, S;
   int h0, hrun;                  // heads [h0, h0+hrun) of each batch entry
   int sq_alloc, sk_alloc;
-  float alpha, beta, bias;
+  float bias;                    // added to every frozen max, binades
 };
 
 hipError_t launch_fsa_fwd(const AttnArgs& a, int fmt, int D, int causal, hipStream_t stream);

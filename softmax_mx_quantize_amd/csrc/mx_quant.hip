@@ -9,6 +9,9 @@
 // ldexp; the rounding and packing use gfx950's scaled conversions with a
 // unit scale.
 //
+// The fused attention path quantises Q multiplied by the softmax scale in
+// binades (`mult`, one fp32 rounding per element); everything else uses 1.
+//
 // One thread owns one 32-element block.  Rows mode: the block runs along the
 // contiguous axis and consecutive threads take consecutive blocks of a row
 // (64-byte loads per thread, contiguous across the wave).  Columns mode: the
@@ -49,8 +52,8 @@ __global__ void __launch_bounds__(256) mx_quant_kernel(QuantArgs a) {
         for (int k = 0; k < 4; ++k) {
           uint32_t lo = w[k] & 0xFFFF, hi = w[k] >> 16;
           bad |= ((lo & 0x7F80) == 0x7F80) | ((hi & 0x7F80) == 0x7F80);
-          v[8 * i + 2 * k] = bf16_bits_to_float(lo);
-          v[8 * i + 2 * k + 1] = bf16_bits_to_float(hi);
+          v[8 * i + 2 * k] = bf16_bits_to_float(lo) * a.mult;
+          v[8 * i + 2 * k + 1] = bf16_bits_to_float(hi) * a.mult;
         }
       }
     } else {
@@ -59,7 +62,7 @@ __global__ void __launch_bounds__(256) mx_quant_kernel(QuantArgs a) {
         uint32_t bits = 0;
         if (row_ok && c0 + j < a.cols) bits = src[j];
         bad |= (bits & 0x7F80) == 0x7F80;
-        v[j] = bf16_bits_to_float(bits);
+        v[j] = bf16_bits_to_float(bits) * a.mult;
       }
     }
   } else {
@@ -73,7 +76,7 @@ __global__ void __launch_bounds__(256) mx_quant_kernel(QuantArgs a) {
       uint32_t bits = 0;
       if (r0 + j < a.rows) bits = src[(r0 + j) * a.cols];
       bad |= (bits & 0x7F80) == 0x7F80;
-      v[j] = bf16_bits_to_float(bits);
+      v[j] = bf16_bits_to_float(bits) * a.mult;
     }
   }
 
