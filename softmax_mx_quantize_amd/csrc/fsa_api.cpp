@@ -94,7 +94,8 @@ int validate_attn(const void* q, const void* k, const void* v, void* out, int B,
 
 int quantize(const uint16_t* x, uint8_t* codes, uint8_t* scales, int64_t batch, int64_t rows,
              int64_t cols, int64_t out_rows, int64_t nb_out, int64_t code_stride,
-             int64_t scale_stride, int fmt, int mode, hipStream_t stream, float mult = 1.0f) {
+             int64_t scale_stride, int fmt, int mode, hipStream_t stream, float mult = 1.0f,
+             int scale_layout = fsa::SCALES_ROWS) {
   fsa::QuantArgs a;
   a.x = x;
   a.codes = codes;
@@ -107,6 +108,7 @@ int quantize(const uint16_t* x, uint8_t* codes, uint8_t* scales, int64_t batch, 
   a.code_stride = code_stride;
   a.scale_stride = scale_stride;
   a.mult = mult;
+  a.scale_layout = scale_layout;
   return fsa::launch_mx_quant(a, fmt, mode, stream) == hipSuccess ? FSA_OK : FSA_ERR_HIP;
 }
 
@@ -219,11 +221,13 @@ int fsa_attention_fwd_ex(const void* q, const void* k, const void* v, void* out,
                     rl.hrun, S, D, sq_alloc, D / 32, rb, D / 32, rl.fmt, 0, stream, score_scale);
       if (st != FSA_OK) return st;
       st = quantize(kb + src, ws + rl.kc + w0 * sk_alloc * rb, ws + rl.ks + w0 * sk_alloc * (D / 32),
-                    rl.hrun, S, D, sk_alloc, D / 32, rb, D / 32, rl.fmt, 0, stream);
+                    rl.hrun, S, D, sk_alloc, D / 32, rb, D / 32, rl.fmt, 0, stream, 1.0f,
+                    fsa::SCALES_KEY_TILES);
       if (st != FSA_OK) return st;
       st = quantize(vb + src, ws + rl.vc + w0 * D * (sk_alloc * bits / 8),
                     ws + rl.vs + w0 * D * (sk_alloc / 32), rl.hrun, S, D, D, sk_alloc / 32,
-                    sk_alloc * bits / 8, sk_alloc / 32, rl.fmt, 1, stream);
+                    sk_alloc * bits / 8, sk_alloc / 32, rl.fmt, 1, stream, 1.0f,
+                    fsa::SCALES_DIM_TILES);
       if (st != FSA_OK) return st;
     }
   }

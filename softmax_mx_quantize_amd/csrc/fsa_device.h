@@ -142,6 +142,24 @@ template <bool CLAMP> struct Pack32<FMT_E2M3, CLAMP> {
   }
 };
 
+// FP6 pack of 32 values held as even elements (v[0..15]) then odd elements
+// (v[16..31]): the two sources of the 32-element conversion, so that callers
+// can produce them in place.  Same conversion and wait states as above.
+__device__ __forceinline__ void pack_fp6_split(const float* v, uint32_t* w, float scale) {
+  v16f ev, od;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) { ev[i] = v[i]; od[i] = v[16 + i]; }
+  v6i r;
+  asm volatile(
+      "v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3\n\t"
+      "s_nop 7\n\t"
+      "s_nop 7"
+      : "=&v"(r)
+      : "v"(ev), "v"(od), "v"(scale));
+#pragma unroll
+  for (int i = 0; i < 6; ++i) w[i] = (uint32_t)r[i];
+}
+
 template <bool CLAMP> struct Pack32<FMT_E2M1, CLAMP> {
   static __device__ __forceinline__ void run(const float* y, uint32_t* w, float s_lo = 1.0f,
                                              float = 1.0f) {

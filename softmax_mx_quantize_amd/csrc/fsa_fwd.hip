@@ -56,6 +56,11 @@
 #ifndef FSA_NW4
 #define FSA_NW4 8
 #endif
+// 8-wave kernels: two wave groups in alternating matrix / vector phases (1)
+// or every wave tile after tile (0).
+#ifndef FSA_PINGPONG
+#define FSA_PINGPONG 0
+#endif
 
 namespace fsa {
 
@@ -206,15 +211,28 @@ __device__ __forceinline__ opv<F> global_operand(const uint8_t* row, int g, int 
 // The scaled MFMA with operands of the format's own width (declared above,
 // outside this namespace).
 
-template <int F>
+// OA selects the byte of `sa` that scales A (op_sel); B's scale is byte 0.
+template <int F, int OA = 0>
 __device__ __forceinline__ v4f mfma(const opv<F>& a, const opv<F>& b, const v4f& c, int sa, int sb) {
   if constexpr (Fmt<F>::bits == 8)
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, Fmt<F>::mfma, Fmt<F>::mfma,
-                                                            0, sa, 0, sb);
+                                                            OA, sa, 0, sb);
   else if constexpr (Fmt<F>::bits == 6)
-    return mfma_scale_v6(a, b, c, Fmt<F>::mfma, Fmt<F>::mfma, 0, sa, 0, sb);
+    return mfma_scale_v6(a, b, c, Fmt<F>::mfma, Fmt<F>::mfma, OA, sa, 0, sb);
   else
-    return mfma_scale_v4(a, b, c, Fmt<F>::mfma, Fmt<F>::mfma, 0, sa, 0, sb);
+    return mfma_scale_v4(a, b, c, Fmt<F>::mfma, Fmt<F>::mfma, OA, sa, 0, sb);
+}
+// The same with A's scale byte chosen by a value that is a constant after
+// unrolling.
+template <int F>
+__device__ __forceinline__ v4f mfma_sel(const opv<F>& a, const opv<F>& b, const v4f& c, int sa,
+                                        int byte, int sb) {
+  switch (byte & 3) {
+    case 0: return mfma<F, 0>(a, b, c, sa, sb);
+    case 1: return mfma<F, 1>(a, b, c, sa, sb);
+    case 2: return mfma<F, 2>(a, b, c, sa, sb);
+    default: return mfma<F, 3>(a, b, c, sa, sb);
+  }
 }
 
 template <int F>
@@ -264,6 +282,15 @@ __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" :
 // (loads complete in issue order for the counter).
 template <int N>
 __device__ __forceinline__ void wait_dma_keep() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+// Workgroup barrier for the LDS ring.  __syncthreads() releases at
+// workgroup scope, which makes the compiler wait for every LDS DMA still in
+// flight (vmcnt(0)) and so drains the prefetch ring at each tile.  Here the
+// waits are explicit instead: each wave has waited for the DMA of the tile
+// the next phase reads (vmcnt before the call), and its own LDS reads
+// complete before the barrier, so nobody refills a stage still being read.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 }  // namespace
 
@@ -289,8 +316,23 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   constexpr int VS_BYTES = D * 4;
   constexpr int STAGE = K_BYTES + V_BYTES + KS_BYTES + VS_BYTES;
 
-  constexpr int NSTAGE = 3;                 // LDS ring depth (tiles in flight + 1)
-  __shared__ __align__(16) uint8_t lds[NSTAGE * STAGE];
+  // Ping-pong of two wave groups (8 waves) or one wave per SIMD (4 waves).
+  constexpr bool PP = NWAVES == 8 && FSA_PINGPONG;
+  constexpr int NSTAGE = PP ? 4 : 3;        // LDS ring depth
+  // One LDS object per stage, always addressed through a compile-time stage
+  // index: the compiler then sees that reads of one stage cannot alias the
+  // DMA in flight into another, and does not wait for that DMA first.
+  __shared__ __align__(16) uint8_t lds0[STAGE];
+  __shared__ __align__(16) uint8_t lds1[STAGE];
+  __shared__ __align__(16) uint8_t lds2[STAGE];
+  __shared__ __align__(16) uint8_t lds3[NSTAGE > 3 ? STAGE : 16];
+  auto stage = [&](auto st_tag) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int ST = decltype(st_tag)::value;
+    if constexpr (ST == 0) return lds0;
+    else if constexpr (ST == 1) return lds1;
+    else if constexpr (ST == 2) return lds2;
+    else return lds3;
+  };
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -362,15 +404,15 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
     v_voff[k] = row * (int)v_row + (c < VCH_VALID ? c : 0) * 16;
   }
   // scales: NKS K-scale dwords and D/64 V-scale dwords, one per wave (waves
-  // past them re-load the first K-scale dword to keep the count uniform)
+  // past them re-load the first K-scale dword to keep the count uniform);
+  // both are tile-ordered, 128 * D/32 and 4 * D contiguous bytes per tile
   const bool s_is_v = wave >= NKS && wave < NKS + D / 64;
   const int s_voff = wave < NKS ? wave * 256 + lane * 4
-                                : (s_is_v ? ((wave - NKS) * 64 + lane) * vs_row : lane * 4);
+                                : (s_is_v ? ((wave - NKS) * 64 + lane) * 4 : lane * 4);
   const int s_lds = wave < NKS ? K_BYTES + V_BYTES + wave * 256
                                : (s_is_v ? K_BYTES + V_BYTES + KS_BYTES + (wave - NKS) * 256
                                          : K_BYTES + V_BYTES);
-  auto issue_tile = [&](int t, int st) {
-    uint8_t* base = lds + st * STAGE;
+  auto issue_tile = [&](int t, uint8_t* base) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < NK_DMA; ++k)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (lds_void*)(base + (wave + NWAVES * k) * 1024),
@@ -381,7 +423,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
                                                16, v_voff[k], t * VRB, 0, 0);
     if (s_is_v)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vs_rsrc, (lds_void*)(base + s_lds), 4, s_voff,
-                                               t * (KT / 32), 0, 0);
+                                               t * VS_BYTES, 0, 0);
     else
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ks_rsrc, (lds_void*)(base + s_lds), 4, s_voff,
                                                t * KT * NDB, 0, 0);
@@ -389,7 +431,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   // DMA instructions each wave issues per tile
   constexpr int DMA_PER_TILE = NK_DMA + NV_DMA + 1;
 
-  if (n_tiles > 0) issue_tile(0, 0);
+  if (n_tiles > 0) issue_tile(0, lds0);
 
   // ---- Q^ fragments (B operand of the score product), one per subtile
   opv<F> qf[NSUB];
@@ -411,10 +453,10 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   // A operand of the score product for 16-key slice j of the tile in stage
   // st: row R of the slice is key kpos(R/4, 4j + R%4), so that output row
   // 4g+i lands on the lane's operand position 4j+i.
-  auto k_frag = [&](int st, int j, int& sc) -> opv<F> {
+  auto k_frag = [&](int j, int& sc) __attribute__((always_inline)) -> opv<F> {
     const int kk = kpos<F>(r >> 2, 4 * j + (r & 3));
-    const uint8_t* base = lds + st * STAGE;
-    sc = g < NDB ? (int)base[K_BYTES + V_BYTES + kk * NDB + g] : 127;
+    const uint8_t* base = lds0;
+    sc = g < NDB ? (int)base[K_BYTES + V_BYTES + (r * NDB + g) * 8 + j] : 127;
     return lds_operand<F>(base + kk * RS, swz_k<F, D>(kk), g, D);
   };
 
@@ -424,14 +466,14 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   float mg[NSUB];
   wait_dma();
   __syncthreads();
-  if (n_tiles > 1) issue_tile(1, 1);
-  if (n_tiles > 2) issue_tile(2, 2);
+  if (n_tiles > 1) issue_tile(1, lds1);
+  if (!PP && n_tiles > 2) issue_tile(2, lds2);
   {
     v4f acc[NSUB][8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       int sc;
-      const opv<F> kf = k_frag(0, j, sc);
+      const opv<F> kf = k_frag(j, sc);
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) acc[s][j] = mfma<F>(kf, qf[s], zero4, sc, qsc[s]);
     }
@@ -510,12 +552,24 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
     k_off[i] = kk0 * RS + 16 * ((lo >> 4) ^ ksw) + (lo & 15);
     v_off[i] = K_BYTES + r * RS + 16 * ((lo >> 4) ^ vsw) + (lo & 15);
   }
-  const int ks_off = K_BYTES + V_BYTES + kk0 * NDB + (g < NDB ? g : 0);
-  const int vs_off = K_BYTES + V_BYTES + KS_BYTES + r * 4 + g;
+  // Scale bytes of the lane's 8 score products (slice j) and 8 P V products
+  // (output tile dt), tile-ordered so that one read fetches all of them; the
+  // MFMA selects byte j & 3 / dt & 3 of a dword.  Lanes past D (D = 64)
+  // multiply zeros and take scale 1.
+  const int ks_off = K_BYTES + V_BYTES + (r * NDB + (g < NDB ? g : 0)) * 8;
+  const int vs_off = K_BYTES + V_BYTES + KS_BYTES + (r * 4 + g) * NDT;
+  auto k_scales = [&](const uint8_t* base) __attribute__((always_inline)) -> uint2 {
+    const uint2 v = *reinterpret_cast<const uint2*>(base + ks_off);
+    return g < NDB ? v : make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+  };
+  auto v_scales = [&](const uint8_t* base) __attribute__((always_inline)) -> uint2 {
+    if constexpr (NDT == 8) return *reinterpret_cast<const uint2*>(base + vs_off);
+    else return make_uint2(*reinterpret_cast<const uint32_t*>(base + vs_off), 0u);
+  };
   const bool k_live = 32 * g < D;               // FP6/FP4 lane groups past D
   const bool k_hi = 64 + 16 * g < D;            // FP8 high half present
 
-  auto frag = [&](const uint8_t* base, const int* off, int imm, bool live, bool hi) -> opv<F> {
+  auto frag = [&](const uint8_t* base, const int* off, int imm, bool live, bool hi) __attribute__((always_inline)) -> opv<F> {
     opv<F> o = zero_operand<F>();
     if constexpr (BITS == 8) {
       if (live) {
@@ -541,50 +595,67 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
     return o;
   };
 
-  // One key tile: scores, fused exponential + MX quantisation of P, P V.
-  auto tile = [&](const uint8_t* base, int key0, auto masked_tag) {
+  // The three steps of one key tile, on state shared across phases.
+  v4f acc[NSUB][8];
+  opv<F> pw[NSUB];
+  int psc[NSUB];
+
+  // Scores of the tile in stage `base`: y = 2^23 s + accumulator start.  In
+  // a masked tile the accumulator of an invisible key starts at -inf, so its
+  // y is -inf and its pattern 0: the epilogue carries no masking at all.
+  auto qk = [&](const uint8_t* base, int key0, auto masked_tag) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    v4f acc[NSUB][8];
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) {
+        const int q = q_wave + 16 * s + r;
+        const int lim = CAUSAL ? min(S, q + 1) : S;     // keys [0, lim) visible
+#pragma unroll
+        for (int p = 0; p < 32; ++p)
+          acc[s][p >> 2][p & 3] = key0 + kpos<F>(g, p) < lim ? minit[s][0] : -INFINITY;
+      }
+    }
+    const uint2 ksc = k_scales(base);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int jrow = 4 * j + ((BITS == 8 && j >= 4) ? 48 : 0);
-      const int sc = g < NDB ? (int)base[ks_off + jrow * NDB] : 127;
       const opv<F> kf = frag(base, k_off, jrow * RS, BITS == 8 ? 16 * g < D : k_live,
-                          BITS == 8 ? k_hi : false);
+                             BITS == 8 ? k_hi : false);
 #pragma unroll
-      for (int s = 0; s < NSUB; ++s) acc[s][j] = mfma<F>(kf, qf[s], minit[s], sc, qsc[s]);
+      for (int s = 0; s < NSUB; ++s)
+        acc[s][j] = mfma_sel<F>(kf, qf[s], MASKED ? acc[s][j] : minit[s],
+                                (int)(j < 4 ? ksc.x : ksc.y), j, qsc[s]);
     }
-    opv<F> pw[NSUB];
-    int psc[NSUB];
+  };
+
+  // Fused exponential + MX quantisation of P for the scores in acc.
+  //
+  // The bit-pattern exponential: y's integer part is the fp32 pattern of
+  // 2^(t + R).  It is monotone in y, and exact wherever y >= 2^24 (below, the
+  // block sits beyond the largest shift anyway), so the block maxima are
+  // taken on the integers, and y is dead once converted.
+  auto epi = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
-      // The bit-pattern exponential: y's integer part is the fp32 pattern of
-      // 2^(t + R).  It is monotone in y, and exact wherever y >= 2^24 (below,
-      // the block sits beyond the largest shift anyway), so the block maxima
-      // are taken on the integers and y is dead from here on.  Masked keys
-      // get pattern 0 (value 0) after the conversion.
-      uint32_t pu[32];
+      // patterns in the operand order of the pack conversion: FP6 takes
+      // even and odd elements as two 16-register sources
+      float pv[32];
 #pragma unroll
-      for (int p = 0; p < 32; ++p) pu[p] = cvt_u32_trunc(acc[s][p >> 2][p & 3]);
-      if (MASKED) {
-        const int q = q_wave + 16 * s + r;
-#pragma unroll
-        for (int p = 0; p < 32; ++p) {
-          const int key = key0 + kpos<F>(g, p);
-          const bool vis = key < S && (!CAUSAL || key <= q);
-          pu[p] = vis ? pu[p] : 0u;
-        }
+      for (int p = 0; p < 32; ++p) {
+        const int o = BITS == 6 ? (p & 1) * 16 + (p >> 1) : p;
+        pv[o] = __uint_as_float(cvt_u32_trunc(acc[s][p >> 2][p & 3]));
       }
+      auto u = [&](int o) __attribute__((always_inline)) { return __float_as_uint(pv[o]); };
       // block maxima: one block per lane (FP6/FP4) or two half blocks (FP8)
-      uint32_t m0 = max(max(pu[0], pu[1]), pu[2]);
-      uint32_t m1 = max(max(pu[16], pu[17]), pu[18]);
+      uint32_t m0 = max(max(u(0), u(1)), u(2));
+      uint32_t m1 = max(max(u(16), u(17)), u(18));
 #pragma unroll
       for (int p = 3; p < 15; p += 2) {
-        m0 = max(max(m0, pu[p]), pu[p + 1]);
-        m1 = max(max(m1, pu[16 + p]), pu[17 + p]);
+        m0 = max(max(m0, u(p)), u(p + 1));
+        m1 = max(max(m1, u(16 + p)), u(17 + p));
       }
-      m0 = max(m0, pu[15]);
-      m1 = max(m1, pu[31]);
+      m0 = max(m0, u(15));
+      m1 = max(m1, u(31));
       if (BITS == 8) {
         m0 = max(m0, (uint32_t)__shfl_xor((int)m0, 16));
         m1 = max(m1, (uint32_t)__shfl_xor((int)m1, 16));
@@ -598,22 +669,26 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
       // conversion divides by 2^(sb + R - 127) = 2^(R - pl - d).
       const int sb0 = 127 - PL - min(-min(e0, EXT), CAP);
       const int sb1 = 127 - PL - min(-min(e1, EXT), CAP);
-      float pv[32];
-#pragma unroll
-      for (int p = 0; p < 32; ++p) pv[p] = __uint_as_float(pu[p]);
       uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      Pack32<F, false>::run(pv, w, conv_scale(sb0), conv_scale(sb1));
+      if constexpr (BITS == 6)
+        pack_fp6_split(pv, w, conv_scale(sb0));
+      else
+        Pack32<F, false>::run(pv, w, conv_scale(sb0), conv_scale(sb1));
 #pragma unroll
       for (int i = 0; i < Operand<F>::words; ++i) pw[s][i] = (int)w[i];
       psc[s] = p_scale<BITS>(sb0, sb1, g);
     }
-    // P V and the row sums on the matrix cores
+  };
+
+  // P V and the row sums on the matrix cores, V^T tile in stage `base`.
+  auto pv_step = [&](const uint8_t* base) __attribute__((always_inline)) {
+    const uint2 vsc = v_scales(base);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       const opv<F> vf = frag(base, v_off, 16 * dt * RS, true, true);
-      const int vsc = (int)base[vs_off + 64 * dt];
 #pragma unroll
-      for (int s = 0; s < NSUB; ++s) O[s][dt] = mfma<F>(vf, pw[s], O[s][dt], vsc, psc[s]);
+      for (int s = 0; s < NSUB; ++s)
+        O[s][dt] = mfma_sel<F>(vf, pw[s], O[s][dt], (int)(dt < 4 ? vsc.x : vsc.y), dt, psc[s]);
     }
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) L[s] = mfma<F>(ones, pw[s], L[s], 127, psc[s]);
@@ -626,25 +701,82 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
     n_clean = c2 < n_clean ? c2 : n_clean;
   }
   n_clean = n_clean < n_tiles ? n_clean : n_tiles;
-  // Two loops so that the clean tiles' code carries no masking at all.
-  auto advance = [&](int t, int st) {
-    // tile t+1 must have landed (tile t+2 may still be in flight); after the
-    // barrier every wave is done with stage st, which takes tile t+3
-    if (t + 2 < n_tiles) wait_dma_keep<DMA_PER_TILE>();
-    else wait_dma();
-    __syncthreads();
-    if (t + 3 < n_tiles) issue_tile(t + 3, st);
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  auto qk_any = [&](const uint8_t* base, int t) __attribute__((always_inline)) {
+    if (t < n_clean) qk(base, t * KT, std::false_type{});
+    else qk(base, t * KT, std::true_type{});
   };
-  int t = 0, st = 0;
-  for (; t < n_clean; ++t) {
-    tile(lds + st * STAGE, t * KT, std::false_type{});
-    advance(t, st);
-    st = st == NSTAGE - 1 ? 0 : st + 1;
-  }
-  for (; t < n_tiles; ++t) {
-    tile(lds + st * STAGE, t * KT, std::true_type{});
-    advance(t, st);
-    st = st == NSTAGE - 1 ? 0 : st + 1;
+
+  if constexpr (!PP) {
+    // Tile after tile, one barrier per tile.  Tile t+1 must have landed
+    // (t+2 may still be in flight); after the barrier every wave is done
+    // with the stage of tile t, which then takes tile t+3.
+    auto step = [&](int t, auto st_tag) __attribute__((always_inline)) {
+      uint8_t* base = stage(st_tag);
+      qk_any(base, t);
+      epi();
+      pv_step(base);
+      if (t + 2 < n_tiles) wait_dma_keep<DMA_PER_TILE>();
+      else wait_dma();
+      ring_barrier();
+      if (t + 3 < n_tiles) issue_tile(t + 3, base);
+    };
+    for (int t = 0; t < n_tiles; t += 3) {
+      step(t, I0{});
+      if (t + 1 < n_tiles) step(t + 1, I1{});
+      if (t + 2 < n_tiles) step(t + 2, I2{});
+    }
+  } else {
+    // Two waves per SIMD in two groups (waves 0-3 and 4-7, one of each per
+    // SIMD) that alternate between a matrix phase (P V of the previous tile,
+    // scores of this one) and a vector phase (the epilogue), offset by one
+    // phase: while one group's MFMAs run, the other's vector work fills the
+    // SIMD.  Every phase ends at a workgroup barrier; group 1 starts with an
+    // extra barrier and group 0 ends with one, so the counts match.
+    // Ring of 4 stages: tile t+2 is issued at the start of the matrix phase
+    // of tile t into the stage of tile t-2, which both groups have finished
+    // (its P V ran in the matrix phases one and two phases earlier).  Tile
+    // t+1 must have landed before the barrier that ends global phase 2t+1,
+    // which for group 0 is its vector phase and for group 1 its matrix phase.
+    const int grp = wave >> 2;
+    auto sync = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+      ring_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto wait_next = [&](int t) __attribute__((always_inline)) {
+      if (t + 2 < n_tiles) wait_dma_keep<DMA_PER_TILE>();
+      else wait_dma();
+    };
+    auto pstep = [&](int t, auto st_tag) __attribute__((always_inline)) {
+      constexpr int ST = decltype(st_tag)::value;
+      if (t + 2 < n_tiles) issue_tile(t + 2, stage(std::integral_constant<int, (ST + 2) & 3>{}));
+      if (t > 0) pv_step(stage(std::integral_constant<int, (ST + 3) & 3>{}));
+      qk_any(stage(st_tag), t);
+      if (grp == 1) wait_next(t);
+      sync();
+      epi();
+      if (grp == 0) wait_next(t);
+      sync();
+    };
+    if (grp == 1) sync();
+    for (int t = 0; t < n_tiles; t += 4) {
+      pstep(t, I0{});
+      if (t + 1 < n_tiles) pstep(t + 1, I1{});
+      if (t + 2 < n_tiles) pstep(t + 2, I2{});
+      if (t + 3 < n_tiles) pstep(t + 3, I3{});
+    }
+    switch ((n_tiles - 1) & 3) {
+      case 0: pv_step(stage(I0{})); break;
+      case 1: pv_step(stage(I1{})); break;
+      case 2: pv_step(stage(I2{})); break;
+      default: pv_step(stage(I3{})); break;
+    }
+    if (grp == 0) sync();
   }
 
   // row offsets in binades (the oracle's kappa); rows beyond EXT come out
@@ -771,7 +903,7 @@ __global__ void __launch_bounds__(64) fsa_fallback_kernel(AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int kk = kpos<F>(r >> 2, 4 * j + (r & 3));
-        const int sc = g < NDB ? (int)ks[(int64_t)(key0 + kk) * NDB + g] : 127;
+        const int sc = g < NDB ? (int)ks[(int64_t)t * KT * NDB + (r * NDB + g) * 8 + j] : 127;
         const opv<F> kf = global_operand<F>(kc + (int64_t)(key0 + kk) * RB, g, D);
 #pragma unroll
         for (int s = 0; s < NSUB; ++s) {
@@ -805,7 +937,7 @@ __global__ void __launch_bounds__(64) fsa_fallback_kernel(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int kk = kpos<F>(r >> 2, 4 * j + (r & 3));
-      const int sc = g < NDB ? (int)ks[(int64_t)(key0 + kk) * NDB + g] : 127;
+      const int sc = g < NDB ? (int)ks[(int64_t)t * KT * NDB + (r * NDB + g) * 8 + j] : 127;
       const opv<F> kf = global_operand<F>(kc + (int64_t)(key0 + kk) * RB, g, D);
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) acc[s][j] = mfma<F>(kf, qf[s], mk[s], sc, qsc[s]);
@@ -853,7 +985,7 @@ __global__ void __launch_bounds__(64) fsa_fallback_kernel(AttnArgs a) {
     for (int dt = 0; dt < NDT; ++dt) {
       const int d = 16 * dt + r;
       const opv<F> vf = global_operand<F>(vc + d * v_row + (int64_t)t * VRB, g, KT);
-      const int vsc = (int)vs[(int64_t)d * vs_row + t * (KT / 32) + g];
+      const int vsc = (int)vs[(int64_t)t * 4 * D + (r * 4 + g) * NDT + dt];
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) O[s][dt] = mfma<F>(vf, pw[s], O[s][dt], vsc, psc[s]);
     }

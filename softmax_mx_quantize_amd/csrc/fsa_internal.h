@@ -22,7 +22,22 @@ struct QuantArgs {
   int64_t code_stride;   // bytes between output code rows
   int64_t scale_stride;  // bytes between output scale rows
   float mult;            // every input value is multiplied by this (fp32) first
+  int scale_layout;      // SCALES_* below
 };
+
+// Scale byte layouts.  ROWS: scales[row][block] (the public layout).  The two
+// tile layouts feed the attention kernel: per 128-key tile the bytes a lane
+// needs for its 8 products sit next to each other, so one 8-byte LDS read
+// fetches them and the scaled MFMA picks its byte with op_sel.
+//   KEY_TILES (K^, blocks along D): within tile T of a batch entry, key row
+//     R = 128 T + Rl and block b go to byte (r * (D/32) + b) * 8 + j of the
+//     tile's 128 * D/32 bytes, where (r, j) is the lane row and slice that
+//     read key Rl: FP8 r = 4 ((Rl>>4)&3) + (Rl&3), j = ((Rl>>2)&3) + 4 (Rl>>6);
+//     FP6/FP4 r = 4 (Rl>>5) + (Rl&3), j = (Rl>>2)&7.
+//   DIM_TILES (V^ transposed, blocks along keys): block kb = 4 T + g of
+//     output row d = 16 dt + r goes to byte (r * 4 + g) * (D/16) + dt of tile
+//     T's 4 D bytes.
+enum { SCALES_ROWS = 0, SCALES_KEY_TILES = 1, SCALES_DIM_TILES = 2 };
 
 hipError_t launch_mx_quant(const QuantArgs& a, int fmt, int mode, hipStream_t stream);
 

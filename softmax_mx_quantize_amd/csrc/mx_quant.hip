@@ -109,7 +109,27 @@ __global__ void __launch_bounds__(256) mx_quant_kernel(QuantArgs a) {
   } else {
     *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
   }
-  a.scales[o * a.scale_stride + b] = sbyte;
+  int64_t so = o * a.scale_stride + b;
+  if (a.scale_layout == SCALES_KEY_TILES) {
+    // o = (batch, key row), b = block along D; rows per batch entry are a
+    // whole number of 128-key tiles
+    const int nb = (int)a.nb_out;
+    const int64_t bt = o / a.out_rows;
+    const int64_t row = o - bt * a.out_rows;
+    const int rl = (int)(row & 127);
+    const int r = BITS == 8 ? 4 * ((rl >> 4) & 3) + (rl & 3) : 4 * (rl >> 5) + (rl & 3);
+    const int j = BITS == 8 ? ((rl >> 2) & 3) + 4 * (rl >> 6) : (rl >> 2) & 7;
+    so = bt * a.out_rows * nb + (row >> 7) * 128 * nb + (r * nb + b) * 8 + j;
+  } else if (a.scale_layout == SCALES_DIM_TILES) {
+    // o = (batch, d), b = key block; blocks per row are a whole number of
+    // 4-block tiles
+    const int64_t bt = o / a.out_rows;
+    const int d = (int)(o - bt * a.out_rows);
+    const int ndt = (int)(a.out_rows / 16);
+    so = bt * a.out_rows * a.nb_out + (b >> 2) * 4 * a.out_rows +
+         ((d & 15) * 4 + (int)(b & 3)) * ndt + (d >> 4);
+  }
+  a.scales[so] = sbyte;
 }
 
 template <int F, int MODE>
