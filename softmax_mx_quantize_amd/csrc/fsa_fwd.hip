@@ -1,1048 +1,10 @@
-// Fused-Softmax attention forward on gfx950 scaled MFMA (MXFP8/6/4).
-//
-// What is computed (Fused-Softmax for efficient quantized attention, summary;
-// Moving softmax to matrix operations speeds up AI inference by over 2x,
-// "Read it as" and the "How it works" figure), with the readings fixed in the
-// oracle's module documentation:
-//   1. frozen max per query row from the first 128 keys: max(window max,
-//      mean + (sqrt(2 ln n) + 1) * std) + bias;
-//   2. S^T = K^ Q^T on the matrix cores with the accumulator initialised to
-//      -m~: the max subtraction is folded into the product;
-//   3. epilogue per 32-key MX block: block binade from the block's largest
-//      score, then per element one FMA + one truncating conversion gives the
-//      fp32 bit-pattern exponential 2^(t + shift), and the scaled conversion
-//      rounds it onto the element grid: the exponential and the MX
-//      quantisation of P in one pass, with no exp instruction;
-//   4. O^T += V^T P~^T and l += 1 P~^T on the matrix cores (same P~ in
-//      numerator and denominator, as EFQ-Softmax: Exp-Free Quantization for
-//      Softmax, abstract, uses it);
-//   5. a row whose block overflows the placement binade is re-based by whole
-//      binades: its running O and l are scaled by an exact power of two and
-//      the remaining blocks use the raised reference (the fallback);
-//   6. out = bf16(O / l).
-//
-// Work decomposition.  One workgroup = 4 waves = 4*16*NSUB query rows of one
-// (batch, head).  Key tiles of 128 keys (K^ rows and the matching V^T
-// columns, with their E8M0 scales) stream through a two-stage LDS ring filled
-// by direct global->LDS loads: tile t+2 is in flight while tile t+1 waits and
-// tile t is computed.  Each wave keeps its queries' Q^ fragments, O^T
-// accumulators and row sums in registers; there is no online max and no
-// rescaling except on fallback.
-//
-// Register layout (16x16x128 scaled MFMA).  Lane (g, r) = 16g + r.  The score
-// tile is computed transposed (keys as rows, queries as columns) so that a
-// lane ends up with 32 keys of one query: the K^ rows are gathered from LDS
-// in the order that makes those 32 keys exactly the keys this lane must
-// supply as the B operand of the P V product.  For FP6/FP4 that is one whole
-// MX block of P; for FP8 it is two half blocks, completed with the lane
-// 16 apart.
-//
-// LDS layout.  Every K^ row and V^T row occupies 128 bytes (8 chunks of 16
-// bytes; FP6/FP4 rows leave chunks unused).  Chunk c of row R is stored at
-// chunk c ^ f(R): the XOR swizzle makes the 8 lanes that read the same
-// logical chunk of 8 different rows hit 8 different bank groups.
-#include <type_traits>
-
-#include "fsa_device.h"
-#include "fsa_internal.h"
-
-// Waves per workgroup for each element format (overridable at build time).
-#ifndef FSA_NW8
-#define FSA_NW8 4
-#endif
-#ifndef FSA_NW6
-#define FSA_NW6 8
-#endif
-#ifndef FSA_NW4
-#define FSA_NW4 8
-#endif
-// 8-wave kernels: two wave groups in alternating matrix / vector phases (1)
-// or every wave tile after tile (0).
-#ifndef FSA_PINGPONG
-#define FSA_PINGPONG 0
-#endif
+// Fused-Softmax attention forward: E2M3 and E2M1 kernels and the dispatch.
+// Built with the VGPR form of every MFMA: with two waves per SIMD the
+// epilogue reads the score accumulators on the vector units, which cannot
+// read AGPRs directly.
+#include "fsa_fwd_impl.h"
 
 namespace fsa {
-
-// The builtin of the scaled MFMA only takes 8-dword operands; the narrow
-// FP6/FP4 forms of the same intrinsic are reached through its overloaded
-// LLVM name.  (Compiler instructions: the hazard handling is the same.)
-__device__ v4f mfma_scale_v6(v6i a, v6i b, v4f c, int cbsz, int blgp, int opsel_a, int sa,
-                             int opsel_b, int sb)
-    __asm("llvm.amdgcn.mfma.scale.f32.16x16x128.f8f6f4.v6i32.v6i32");
-__device__ v4f mfma_scale_v4(v4i a, v4i b, v4f c, int cbsz, int blgp, int opsel_a, int sa,
-                             int opsel_b, int sb)
-    __asm("llvm.amdgcn.mfma.scale.f32.16x16x128.f8f6f4.v4i32.v4i32");
-
-namespace {
-
-constexpr int KT = 128;          // keys per tile
-constexpr float MAGIC = 12582912.0f;   // 1.5 * 2^23: float + MAGIC rounds to an integer
-// A score equal to the reference gives the fp32 pattern of 2^REF, so scores
-// from 188 binades below it to 66 above map to normal fp32 numbers.
-constexpr int REF = 62;
-
-// Binade of a block relative to the reference, in element codes:
-// floor(RNE(2^M (y / 2^23 - 127 - REF)) / 2^M) for the block's largest
-// exponent-field value y.  y * 2^(M-23) is exact, and adding the integer
-// constant plus MAGIC rounds once, to nearest even.  Blocks whose largest
-// value lies below 2^-(127+REF) (or that are fully masked, y = -inf) count as
-// y = 0, which already puts them beyond the largest block shift.  Values
-// more than HI_BINADE binades above the reference count as exactly that
-// many (the MAGIC window holds 2^22 codes); the row then falls back with
-// kappa = HI_BINADE, which is exact for every score within 2^18 binades of
-// its frozen max.
-constexpr int HI_BINADE = 1 << 18;
-// Largest guess-relative block binade the main sweep absorbs by block shifts
-// alone; rows above it go to the fallback kernel.
-constexpr int EXT = 64;
-static_assert(HI_BINADE > EXT, "clamped binades must reach the fallback kernel");
-template <int M>
-__device__ __forceinline__ int block_binade(float y) {
-  const float yc = __builtin_amdgcn_fmed3f(y, 0.0f, 8388608.0f * (float)(127 + REF + HI_BINADE));
-  const float t = __builtin_fmaf(yc, (float)(1 << M) * 0x1p-23f,
-                                 MAGIC - (float)((1 << M) * (127 + REF)));
-  return (int)(__float_as_uint(t) - __float_as_uint(MAGIC)) >> M;
-}
-
-// Divisor of the scaled conversions for a block whose P~ scale byte is sb:
-// 2^(sb + REF - 127), taking the bit-pattern value 2^(t + REF) to
-// 2^(t + pl + Delta).
-__device__ __forceinline__ float conv_scale(int sb) {
-  return __uint_as_float((uint32_t)(sb + REF) << 23);
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Truncation toward zero to u32 (v_cvt_u32_f32, which saturates and maps NaN
-// and negatives to 0; the exponential relies on that).  It must stay a
-// compiler-visible conversion: the epilogue feeds it straight from MFMA
-// results, and only instructions the compiler sees get the wait states that
-// reading an MFMA result requires.  Its input must come straight from the
-// product (never a select with constants), so that no out-of-range case can
-// be folded away at compile time; masking happens on the integer result.
-__device__ __forceinline__ uint32_t cvt_u32_trunc(float y) {
-  return (uint32_t)y;
-}
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7FFF + ((u >> 16) & 1);
-  return (uint16_t)(u >> 16);
-}
-
-// Position p (0..31) of a lane's operand list -> index along the 128-wide K
-// dimension for lane group g.
-template <int F>
-__device__ __forceinline__ int kpos(int g, int p) {
-  if (Fmt<F>::bits == 8) return p < 16 ? 16 * g + p : 64 + 16 * g + (p - 16);
-  return 32 * g + p;
-}
-
-// XOR swizzles (16-byte chunk index within a 128-byte LDS row).
-template <int F, int D>
-__device__ __forceinline__ int swz_k(int row) {
-  if (D != 128) return 0;
-  const int hi = Fmt<F>::bits == 8 ? (row >> 4) & 1 : (row >> 5) & 1;
-  return (row & 3) | (hi << 2);
-}
-__device__ __forceinline__ int swz_v(int row) { return row & 7; }
-
-// A lane's 32 operand elements along a 128-byte swizzled LDS row.  `len` is
-// the number of valid K elements of the row (elements past it are zero).
-template <int F>
-__device__ __forceinline__ opv<F> lds_operand(const uint8_t* row, int sw, int g, int len) {
-  opv<F> o = zero_operand<F>();
-  if constexpr (Fmt<F>::bits == 8) {
-    if (16 * g < len) {
-      uint4 a = *reinterpret_cast<const uint4*>(row + 16 * (g ^ sw));
-      o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
-    }
-    if (64 + 16 * g < len) {
-      uint4 b = *reinterpret_cast<const uint4*>(row + 16 * ((4 + g) ^ sw));
-      o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
-    }
-  } else if constexpr (Fmt<F>::bits == 6) {
-    if (32 * g < len) {
-#pragma unroll
-      for (int i = 0; i < 3; ++i) {
-        const int off = 24 * g + 8 * i;
-        uint2 a = *reinterpret_cast<const uint2*>(row + 16 * ((off >> 4) ^ sw) + (off & 15));
-        o[2 * i] = a.x; o[2 * i + 1] = a.y;
-      }
-    }
-  } else {
-    if (32 * g < len) {
-      uint4 a = *reinterpret_cast<const uint4*>(row + 16 * (g ^ sw));
-      o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
-    }
-  }
-  return o;
-}
-
-// The same 32 elements straight from global memory (unswizzled row).
-template <int F>
-__device__ __forceinline__ opv<F> global_operand(const uint8_t* row, int g, int len) {
-  opv<F> o = zero_operand<F>();
-  if constexpr (Fmt<F>::bits == 8) {
-    if (16 * g < len) {
-      uint4 a = *reinterpret_cast<const uint4*>(row + 16 * g);
-      o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
-    }
-    if (64 + 16 * g < len) {
-      uint4 b = *reinterpret_cast<const uint4*>(row + 64 + 16 * g);
-      o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
-    }
-  } else if constexpr (Fmt<F>::bits == 6) {
-    if (32 * g < len) {
-      const uint2* p = reinterpret_cast<const uint2*>(row + 24 * g);
-      uint2 a = p[0], b = p[1], c = p[2];
-      o[0] = a.x; o[1] = a.y; o[2] = b.x; o[3] = b.y; o[4] = c.x; o[5] = c.y;
-    }
-  } else {
-    if (32 * g < len) {
-      uint4 a = *reinterpret_cast<const uint4*>(row + 16 * g);
-      o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
-    }
-  }
-  return o;
-}
-
-// The scaled MFMA with operands of the format's own width (declared above,
-// outside this namespace).
-
-// OA selects the byte of `sa` that scales A (op_sel); B's scale is byte 0.
-template <int F, int OA = 0>
-__device__ __forceinline__ v4f mfma(const opv<F>& a, const opv<F>& b, const v4f& c, int sa, int sb) {
-  if constexpr (Fmt<F>::bits == 8)
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, Fmt<F>::mfma, Fmt<F>::mfma,
-                                                            OA, sa, 0, sb);
-  else if constexpr (Fmt<F>::bits == 6)
-    return mfma_scale_v6(a, b, c, Fmt<F>::mfma, Fmt<F>::mfma, OA, sa, 0, sb);
-  else
-    return mfma_scale_v4(a, b, c, Fmt<F>::mfma, Fmt<F>::mfma, OA, sa, 0, sb);
-}
-// The same with A's scale byte chosen by a value that is a constant after
-// unrolling.
-template <int F>
-__device__ __forceinline__ v4f mfma_sel(const opv<F>& a, const opv<F>& b, const v4f& c, int sa,
-                                        int byte, int sb) {
-  switch (byte & 3) {
-    case 0: return mfma<F, 0>(a, b, c, sa, sb);
-    case 1: return mfma<F, 1>(a, b, c, sa, sb);
-    case 2: return mfma<F, 2>(a, b, c, sa, sb);
-    default: return mfma<F, 3>(a, b, c, sa, sb);
-  }
-}
-
-template <int F>
-__device__ __forceinline__ opv<F> ones_operand() {
-  constexpr int BITS = Fmt<F>::bits;
-  constexpr uint32_t c = Fmt<F>::one_code;
-  opv<F> o = zero_operand<F>();
-  if constexpr (BITS == 8) {
-    for (int i = 0; i < 8; ++i) o[i] = (int)(c * 0x01010101u);
-  } else if constexpr (BITS == 4) {
-    for (int i = 0; i < 4; ++i) o[i] = (int)(c * 0x11111111u);
-  } else {
-    // 32 six-bit fields: 4 fields make 3 bytes, repeated.
-    const uint32_t w24 = c | (c << 6) | (c << 12) | (c << 18);
-    const uint8_t b0 = w24 & 0xFF, b1 = (w24 >> 8) & 0xFF, b2 = (w24 >> 16) & 0xFF;
-    uint8_t bytes[24];
-    for (int i = 0; i < 8; ++i) { bytes[3 * i] = b0; bytes[3 * i + 1] = b1; bytes[3 * i + 2] = b2; }
-    for (int i = 0; i < 6; ++i)
-      o[i] = (int)(bytes[4 * i] | (bytes[4 * i + 1] << 8) | (bytes[4 * i + 2] << 16) |
-                   ((uint32_t)bytes[4 * i + 3] << 24));
-  }
-  return o;
-}
-
-// Scale operand of the P~ B operand.  FP6/FP4: the lane's own block.  FP8:
-// lane group c supplies the scale of key block c; blocks 0/2 are the low/high
-// halves held by groups 0-1, blocks 1/3 those held by groups 2-3, so groups
-// 1 and 2 take the value from the lane 48 apart (a branch-free exchange).
-template <int BITS>
-__device__ __forceinline__ int p_scale(int s_lo, int s_hi, int g) {
-  if (BITS != 8) return s_lo;
-  const int give = g >= 2 ? s_lo : s_hi;            // what the partner needs
-  const int got = __shfl_xor(give, 48);
-  const int own = g < 2 ? s_lo : s_hi;
-  const bool cross = (g == 1) | (g == 2);
-  return cross ? got : own;
-}
-
-__device__ __forceinline__ void dma16(const void* g, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* g, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 4, 0, 0);
-}
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// Wait until at most N of this wave's memory loads are still outstanding
-// (loads complete in issue order for the counter).
-template <int N>
-__device__ __forceinline__ void wait_dma_keep() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
-// Workgroup barrier for the LDS ring.  __syncthreads() releases at
-// workgroup scope, which makes the compiler wait for every LDS DMA still in
-// flight (vmcnt(0)) and so drains the prefetch ring at each tile.  Here the
-// waits are explicit instead: each wave has waited for the DMA of the tile
-// the next phase reads (vmcnt before the call), and its own LDS reads
-// complete before the barrier, so nobody refills a stage still being read.
-__device__ __forceinline__ void ring_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-}  // namespace
-
-template <int F, int D, bool CAUSAL, int NSUB, int NWAVES>
-__global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES * 64))) fsa_fwd_kernel(AttnArgs a) {
-#if defined(__HIP_DEVICE_COMPILE__)  // buffer-resource types exist only in the device pass
-  constexpr int BITS = Fmt<F>::bits;
-  constexpr int MB = Fmt<F>::mbits;
-  constexpr int PL = F == FMT_E4M3 ? Fmt<F>::emax - 1 : Fmt<F>::emax;   // placement binade
-  constexpr int CAP = 127 - PL;
-  constexpr int RB = D * BITS / 8;          // bytes per Q^/K^ row (global)
-  constexpr int RS = 128;                   // bytes per K^/V^T row (LDS)
-  constexpr int NCH = RS / 16;              // 16-byte chunks per LDS row
-  constexpr int KCH_VALID = RB / 16 > 0 ? RB / 16 : 1;
-  constexpr int VCH_VALID = KT * BITS / 8 / 16;
-  constexpr int VRB = KT * BITS / 8;        // bytes per V^T tile row (global)
-  constexpr int NDB = D / 32;               // MX blocks per Q^/K^ row
-  constexpr int NDT = D / 16;               // 16-wide output tiles along D
-  constexpr int QW = NWAVES * 16 * NSUB;    // queries per workgroup
-  constexpr int K_BYTES = KT * RS;
-  constexpr int V_BYTES = D * RS;
-  constexpr int KS_BYTES = KT * NDB;
-  constexpr int VS_BYTES = D * 4;
-  constexpr int STAGE = K_BYTES + V_BYTES + KS_BYTES + VS_BYTES;
-
-  // Ping-pong of two wave groups (8 waves) or one wave per SIMD (4 waves).
-  constexpr bool PP = NWAVES == 8 && FSA_PINGPONG;
-  constexpr int NSTAGE = PP ? 4 : 3;        // LDS ring depth
-  // One LDS object per stage, always addressed through a compile-time stage
-  // index: the compiler then sees that reads of one stage cannot alias the
-  // DMA in flight into another, and does not wait for that DMA first.
-  __shared__ __align__(16) uint8_t lds0[STAGE];
-  __shared__ __align__(16) uint8_t lds1[STAGE];
-  __shared__ __align__(16) uint8_t lds2[STAGE];
-  __shared__ __align__(16) uint8_t lds3[NSTAGE > 3 ? STAGE : 16];
-  auto stage = [&](auto st_tag) __attribute__((always_inline)) -> uint8_t* {
-    constexpr int ST = decltype(st_tag)::value;
-    if constexpr (ST == 0) return lds0;
-    else if constexpr (ST == 1) return lds1;
-    else if constexpr (ST == 2) return lds2;
-    else return lds3;
-  };
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int g = lane >> 4;
-  const int r = lane & 15;
-
-  // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
-  // contiguous run of (head, query tile) work items so that the workgroups
-  // sharing one XCD's L2 work on the same head's K^ and V^.
-  const int nq = (a.S + QW - 1) / QW;
-  const int n_items = nq * a.B * a.hrun;
-  const int per_xcd = (n_items + 7) / 8;
-  const int item = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-  if (item >= n_items) return;
-  // workspace slabs are indexed by the launch's own (batch, head) order;
-  // outputs by the global head index
-  const int64_t wi = item / nq;
-  const int b = (int)wi / a.hrun;
-  const int h = a.h0 + ((int)wi - b * a.hrun);
-  const int64_t bh = (int64_t)b * a.H + h;
-  const int S = a.S;
-  const int q_wg = (item - (int)wi * nq) * QW;
-  const int q_wave = q_wg + wave * 16 * NSUB;
-
-  const uint8_t* kc = a.kc + wi * (int64_t)a.sk_alloc * RB;
-  const uint8_t* ks = a.ks + wi * (int64_t)a.sk_alloc * NDB;
-  const int64_t v_row = (int64_t)a.sk_alloc * BITS / 8;
-  const uint8_t* vc = a.vc + wi * (int64_t)D * v_row;
-  const int vs_row = a.sk_alloc / 32;
-  const uint8_t* vs = a.vs + wi * (int64_t)D * vs_row;
-
-  int n_tiles = (S + KT - 1) / KT;
-  if (CAUSAL) {
-    const int last_q = q_wg + QW - 1 < S - 1 ? q_wg + QW - 1 : S - 1;
-    const int t_need = last_q / KT + 1;
-    n_tiles = t_need < n_tiles ? t_need : n_tiles;
-  }
-
-  // Direct global->LDS copy of key tile t into stage st with buffer loads:
-  // each wave moves 1 KB per instruction (8 LDS rows of 8 chunks); lane i
-  // fills physical chunk i%8 of row i/8 with the logical chunk the swizzle
-  // maps there (unused chunks of FP6/FP4 rows re-read chunk 0 of their row).
-  // The lane's byte offset inside the head's slab is fixed for the whole
-  // sweep; the tile's offset goes in the scalar offset, so issuing a tile
-  // costs no vector instructions.
-  constexpr int NK_DMA = KT * NCH / 64 / NWAVES;      // per wave, per tile
-  constexpr int NV_DMA = D * NCH / 64 / NWAVES;
-  constexpr int NKS = KS_BYTES / 256;
-  const __amdgpu_buffer_rsrc_t k_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)kc, (short)0, a.sk_alloc * RB, 0x00020000);
-  const __amdgpu_buffer_rsrc_t v_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)vc, (short)0, (int)(D * v_row), 0x00020000);
-  const __amdgpu_buffer_rsrc_t ks_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)ks, (short)0, a.sk_alloc * NDB, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vs_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)vs, (short)0, D * vs_row, 0x00020000);
-  int k_voff[NK_DMA], v_voff[NV_DMA];
-#pragma unroll
-  for (int k = 0; k < NK_DMA; ++k) {
-    const int row = (wave + NWAVES * k) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz_k<F, D>(row);
-    k_voff[k] = row * RB + (c < KCH_VALID ? c : 0) * 16;
-  }
-#pragma unroll
-  for (int k = 0; k < NV_DMA; ++k) {
-    const int row = (wave + NWAVES * k) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz_v(row);
-    v_voff[k] = row * (int)v_row + (c < VCH_VALID ? c : 0) * 16;
-  }
-  // scales: NKS K-scale dwords and D/64 V-scale dwords, one per wave (waves
-  // past them re-load the first K-scale dword to keep the count uniform);
-  // both are tile-ordered, 128 * D/32 and 4 * D contiguous bytes per tile
-  const bool s_is_v = wave >= NKS && wave < NKS + D / 64;
-  const int s_voff = wave < NKS ? wave * 256 + lane * 4
-                                : (s_is_v ? ((wave - NKS) * 64 + lane) * 4 : lane * 4);
-  const int s_lds = wave < NKS ? K_BYTES + V_BYTES + wave * 256
-                               : (s_is_v ? K_BYTES + V_BYTES + KS_BYTES + (wave - NKS) * 256
-                                         : K_BYTES + V_BYTES);
-  auto issue_tile = [&](int t, uint8_t* base) __attribute__((always_inline)) {
-#pragma unroll
-    for (int k = 0; k < NK_DMA; ++k)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (lds_void*)(base + (wave + NWAVES * k) * 1024),
-                                               16, k_voff[k], t * KT * RB, 0, 0);
-#pragma unroll
-    for (int k = 0; k < NV_DMA; ++k)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc, (lds_void*)(base + K_BYTES + (wave + NWAVES * k) * 1024),
-                                               16, v_voff[k], t * VRB, 0, 0);
-    if (s_is_v)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vs_rsrc, (lds_void*)(base + s_lds), 4, s_voff,
-                                               t * VS_BYTES, 0, 0);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ks_rsrc, (lds_void*)(base + s_lds), 4, s_voff,
-                                               t * KT * NDB, 0, 0);
-  };
-  // DMA instructions each wave issues per tile
-  constexpr int DMA_PER_TILE = NK_DMA + NV_DMA + 1;
-
-  if (n_tiles > 0) issue_tile(0, lds0);
-
-  // ---- Q^ fragments (B operand of the score product), one per subtile
-  opv<F> qf[NSUB];
-  int qsc[NSUB];
-  {
-    const uint8_t* qc = a.qc + wi * (int64_t)a.sq_alloc * RB;
-    const uint8_t* qs = a.qs + wi * (int64_t)a.sq_alloc * NDB;
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      const int q = q_wave + 16 * s + r;
-      qf[s] = global_operand<F>(qc + (int64_t)q * RB, g, D);
-      // 2^23 rides on Q's E8M0 scale, so the product is 2^23 s: the
-      // exponent-field units of the bit-pattern exponential (255 stays NaN)
-      const int qb = g < NDB ? (int)qs[(int64_t)q * NDB + g] : 127;
-      qsc[s] = qb == 255 ? 255 : min(qb + 23, 254);
-    }
-  }
-
-  // A operand of the score product for 16-key slice j of the tile in stage
-  // st: row R of the slice is key kpos(R/4, 4j + R%4), so that output row
-  // 4g+i lands on the lane's operand position 4j+i.
-  auto k_frag = [&](int j, int& sc) __attribute__((always_inline)) -> opv<F> {
-    const int kk = kpos<F>(r >> 2, 4 * j + (r & 3));
-    const uint8_t* base = lds0;
-    sc = g < NDB ? (int)base[K_BYTES + V_BYTES + (r * NDB + g) * 8 + j] : 127;
-    return lds_operand<F>(base + kk * RS, swz_k<F, D>(kk), g, D);
-  };
-
-  const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
-
-  // ---- frozen max from the first tile (keys [0, 128))
-  float mg[NSUB];
-  wait_dma();
-  __syncthreads();
-  if (n_tiles > 1) issue_tile(1, lds1);
-  if (!PP && n_tiles > 2) issue_tile(2, lds2);
-  {
-    v4f acc[NSUB][8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      int sc;
-      const opv<F> kf = k_frag(j, sc);
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) acc[s][j] = mfma<F>(kf, qf[s], zero4, sc, qsc[s]);
-    }
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      const int q = q_wave + 16 * s + r;
-      float sum = 0.f, mx = -INFINITY;
-      int cnt = 0;
-#pragma unroll
-      for (int p = 0; p < 32; ++p) {
-        const int key = kpos<F>(g, p);
-        const bool vis = key < S && (!CAUSAL || key <= q);
-        const float x = acc[s][p >> 2][p & 3];
-        sum += vis ? x : 0.f;
-        mx = vis ? __builtin_fmaxf(mx, x) : mx;
-        cnt += vis ? 1 : 0;
-      }
-      sum += __shfl_xor(sum, 16); sum += __shfl_xor(sum, 32);
-      cnt += __shfl_xor(cnt, 16); cnt += __shfl_xor(cnt, 32);
-      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16)); mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
-      const float mean = sum / (float)(cnt > 0 ? cnt : 1);
-      float ss = 0.f;
-#pragma unroll
-      for (int p = 0; p < 32; ++p) {
-        const int key = kpos<F>(g, p);
-        const bool vis = key < S && (!CAUSAL || key <= q);
-        const float dlt = acc[s][p >> 2][p & 3] - mean;
-        ss += vis ? dlt * dlt : 0.f;
-      }
-      ss += __shfl_xor(ss, 16); ss += __shfl_xor(ss, 32);
-      const float sd = __builtin_sqrtf(ss / (float)(cnt > 0 ? cnt : 1));
-      const int nvis = CAUSAL ? (q + 1 < S ? q + 1 : S) : S;
-      const float z = __builtin_sqrtf(2.0f * __builtin_logf((float)nvis)) + 1.0f;
-      // statistics of 2^23 s, back to binades (exact power-of-two scaling)
-      mg[s] = __builtin_fmaxf(mx, mean + z * sd) * 0x1p-23f + a.bias;
-    }
-  }
-
-  // ---- main sweep
-  // A block whose largest score exceeds the guess by e_b > 0 binades keeps
-  // its codes and takes an E8M0 scale 2^e_b above the guess's: exactly the
-  // row the oracle re-bases by kappa = max e_b, scaled by 2^kappa in both
-  // O and l.  Only a row beyond EXT binades (scale bytes or fp32 sums could
-  // overflow) is recomputed by the fallback kernel with the re-basing made
-  // explicit.
-  v4f O[NSUB][NDT];
-  v4f L[NSUB];
-  int kmax[NSUB];
-  v4f minit[NSUB];
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    L[s] = zero4;
-    kmax[s] = -1000000;
-    // accumulator start: fp32(2^23 (127 + R) - 2^23 m~), one rounding
-    const float c0 = __builtin_fmaf(-8388608.0f, mg[s], 8388608.0f * (127 + REF));
-    minit[s] = v4f{c0, c0, c0, c0};
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) O[s][dt] = zero4;
-  }
-  const opv<F> ones = ones_operand<F>();
-
-  // Lane-constant LDS byte offsets.  For slice j of the score product the
-  // lane's K^ row is kk0 + 4j (+48 for the FP8 high half), and its swizzle
-  // does not depend on j; V^T row 16dt + r likewise.  Every fragment read is
-  // a base register plus a compile-time offset.
-  const int kk0 = BITS == 8 ? 16 * (r >> 2) + (r & 3) : 32 * (r >> 2) + (r & 3);
-  const int ksw = swz_k<F, D>(kk0);
-  const int vsw = swz_v(r);
-  int k_off[3], v_off[3];
-#pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    int lo;
-    if (BITS == 8) lo = i == 0 ? 16 * g : 64 + 16 * g;
-    else if (BITS == 6) lo = 24 * g + 8 * i;
-    else lo = 16 * g;
-    k_off[i] = kk0 * RS + 16 * ((lo >> 4) ^ ksw) + (lo & 15);
-    v_off[i] = K_BYTES + r * RS + 16 * ((lo >> 4) ^ vsw) + (lo & 15);
-  }
-  // Scale bytes of the lane's 8 score products (slice j) and 8 P V products
-  // (output tile dt), tile-ordered so that one read fetches all of them; the
-  // MFMA selects byte j & 3 / dt & 3 of a dword.  Lanes past D (D = 64)
-  // multiply zeros and take scale 1.
-  const int ks_off = K_BYTES + V_BYTES + (r * NDB + (g < NDB ? g : 0)) * 8;
-  const int vs_off = K_BYTES + V_BYTES + KS_BYTES + (r * 4 + g) * NDT;
-  auto k_scales = [&](const uint8_t* base) __attribute__((always_inline)) -> uint2 {
-    const uint2 v = *reinterpret_cast<const uint2*>(base + ks_off);
-    return g < NDB ? v : make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
-  };
-  auto v_scales = [&](const uint8_t* base) __attribute__((always_inline)) -> uint2 {
-    if constexpr (NDT == 8) return *reinterpret_cast<const uint2*>(base + vs_off);
-    else return make_uint2(*reinterpret_cast<const uint32_t*>(base + vs_off), 0u);
-  };
-  const bool k_live = 32 * g < D;               // FP6/FP4 lane groups past D
-  const bool k_hi = 64 + 16 * g < D;            // FP8 high half present
-
-  auto frag = [&](const uint8_t* base, const int* off, int imm, bool live, bool hi) __attribute__((always_inline)) -> opv<F> {
-    opv<F> o = zero_operand<F>();
-    if constexpr (BITS == 8) {
-      if (live) {
-        const uint4 a0 = *reinterpret_cast<const uint4*>(base + off[0] + imm);
-        o[0] = a0.x; o[1] = a0.y; o[2] = a0.z; o[3] = a0.w;
-      }
-      if (hi) {
-        const uint4 a1 = *reinterpret_cast<const uint4*>(base + off[1] + imm);
-        o[4] = a1.x; o[5] = a1.y; o[6] = a1.z; o[7] = a1.w;
-      }
-    } else if constexpr (BITS == 6) {
-      if (live) {
-#pragma unroll
-        for (int i = 0; i < 3; ++i) {
-          const uint2 a = *reinterpret_cast<const uint2*>(base + off[i] + imm);
-          o[2 * i] = a.x; o[2 * i + 1] = a.y;
-        }
-      }
-    } else if (live) {
-      const uint4 a0 = *reinterpret_cast<const uint4*>(base + off[0] + imm);
-      o[0] = a0.x; o[1] = a0.y; o[2] = a0.z; o[3] = a0.w;
-    }
-    return o;
-  };
-
-  // The three steps of one key tile, on state shared across phases.
-  v4f acc[NSUB][8];
-  opv<F> pw[NSUB];
-  int psc[NSUB];
-
-  // Scores of the tile in stage `base`: y = 2^23 s + accumulator start.  In
-  // a masked tile the accumulator of an invisible key starts at -inf, so its
-  // y is -inf and its pattern 0: the epilogue carries no masking at all.
-  auto qk = [&](const uint8_t* base, int key0, auto masked_tag) __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    if constexpr (MASKED) {
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) {
-        const int q = q_wave + 16 * s + r;
-        const int lim = CAUSAL ? min(S, q + 1) : S;     // keys [0, lim) visible
-#pragma unroll
-        for (int p = 0; p < 32; ++p)
-          acc[s][p >> 2][p & 3] = key0 + kpos<F>(g, p) < lim ? minit[s][0] : -INFINITY;
-      }
-    }
-    const uint2 ksc = k_scales(base);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int jrow = 4 * j + ((BITS == 8 && j >= 4) ? 48 : 0);
-      const opv<F> kf = frag(base, k_off, jrow * RS, BITS == 8 ? 16 * g < D : k_live,
-                             BITS == 8 ? k_hi : false);
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s)
-        acc[s][j] = mfma_sel<F>(kf, qf[s], MASKED ? acc[s][j] : minit[s],
-                                (int)(j < 4 ? ksc.x : ksc.y), j, qsc[s]);
-    }
-  };
-
-  // Fused exponential + MX quantisation of P for the scores in acc.
-  //
-  // The bit-pattern exponential: y's integer part is the fp32 pattern of
-  // 2^(t + R).  It is monotone in y, and exact wherever y >= 2^24 (below, the
-  // block sits beyond the largest shift anyway), so the block maxima are
-  // taken on the integers, and y is dead once converted.
-  auto epi = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      // patterns in the operand order of the pack conversion: FP6 takes
-      // even and odd elements as two 16-register sources
-      float pv[32];
-#pragma unroll
-      for (int p = 0; p < 32; ++p) {
-        const int o = BITS == 6 ? (p & 1) * 16 + (p >> 1) : p;
-        pv[o] = __uint_as_float(cvt_u32_trunc(acc[s][p >> 2][p & 3]));
-      }
-      auto u = [&](int o) __attribute__((always_inline)) { return __float_as_uint(pv[o]); };
-      // block maxima: one block per lane (FP6/FP4) or two half blocks (FP8)
-      uint32_t m0 = max(max(u(0), u(1)), u(2));
-      uint32_t m1 = max(max(u(16), u(17)), u(18));
-#pragma unroll
-      for (int p = 3; p < 15; p += 2) {
-        m0 = max(max(m0, u(p)), u(p + 1));
-        m1 = max(max(m1, u(16 + p)), u(17 + p));
-      }
-      m0 = max(m0, u(15));
-      m1 = max(m1, u(31));
-      if (BITS == 8) {
-        m0 = max(m0, (uint32_t)__shfl_xor((int)m0, 16));
-        m1 = max(m1, (uint32_t)__shfl_xor((int)m1, 16));
-      } else {
-        m0 = max(m0, m1);
-        m1 = m0;
-      }
-      const int e0 = block_binade<MB>((float)m0), e1 = block_binade<MB>((float)m1);
-      kmax[s] = max(kmax[s], max(e0, e1));
-      // block shifts relative to the guess; P~ scale bytes 127 - pl - d.  The
-      // conversion divides by 2^(sb + R - 127) = 2^(R - pl - d).
-      const int sb0 = 127 - PL - min(-min(e0, EXT), CAP);
-      const int sb1 = 127 - PL - min(-min(e1, EXT), CAP);
-      uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if constexpr (BITS == 6)
-        pack_fp6_split(pv, w, conv_scale(sb0));
-      else
-        Pack32<F, false>::run(pv, w, conv_scale(sb0), conv_scale(sb1));
-#pragma unroll
-      for (int i = 0; i < Operand<F>::words; ++i) pw[s][i] = (int)w[i];
-      psc[s] = p_scale<BITS>(sb0, sb1, g);
-    }
-  };
-
-  // P V and the row sums on the matrix cores, V^T tile in stage `base`.
-  auto pv_step = [&](const uint8_t* base) __attribute__((always_inline)) {
-    const uint2 vsc = v_scales(base);
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const opv<F> vf = frag(base, v_off, 16 * dt * RS, true, true);
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s)
-        O[s][dt] = mfma_sel<F>(vf, pw[s], O[s][dt], (int)(dt < 4 ? vsc.x : vsc.y), dt, psc[s]);
-    }
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) L[s] = mfma<F>(ones, pw[s], L[s], 127, psc[s]);
-  };
-
-  // tiles [0, n_clean) need no masking for any row of this wave
-  int n_clean = S / KT;
-  if (CAUSAL) {
-    const int c2 = (q_wave + 1) / KT;          // key0 + KT - 1 <= q_wave
-    n_clean = c2 < n_clean ? c2 : n_clean;
-  }
-  n_clean = n_clean < n_tiles ? n_clean : n_tiles;
-
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
-  auto qk_any = [&](const uint8_t* base, int t) __attribute__((always_inline)) {
-    if (t < n_clean) qk(base, t * KT, std::false_type{});
-    else qk(base, t * KT, std::true_type{});
-  };
-
-  if constexpr (!PP) {
-    // Tile after tile, one barrier per tile.  Tile t+1 must have landed
-    // (t+2 may still be in flight); after the barrier every wave is done
-    // with the stage of tile t, which then takes tile t+3.
-    auto step = [&](int t, auto st_tag) __attribute__((always_inline)) {
-      uint8_t* base = stage(st_tag);
-      qk_any(base, t);
-      epi();
-      pv_step(base);
-      if (t + 2 < n_tiles) wait_dma_keep<DMA_PER_TILE>();
-      else wait_dma();
-      ring_barrier();
-      if (t + 3 < n_tiles) issue_tile(t + 3, base);
-    };
-    for (int t = 0; t < n_tiles; t += 3) {
-      step(t, I0{});
-      if (t + 1 < n_tiles) step(t + 1, I1{});
-      if (t + 2 < n_tiles) step(t + 2, I2{});
-    }
-  } else {
-    // Two waves per SIMD in two groups (waves 0-3 and 4-7, one of each per
-    // SIMD) that alternate between a matrix phase (P V of the previous tile,
-    // scores of this one) and a vector phase (the epilogue), offset by one
-    // phase: while one group's MFMAs run, the other's vector work fills the
-    // SIMD.  Every phase ends at a workgroup barrier; group 1 starts with an
-    // extra barrier and group 0 ends with one, so the counts match.
-    // Ring of 4 stages: tile t+2 is issued at the start of the matrix phase
-    // of tile t into the stage of tile t-2, which both groups have finished
-    // (its P V ran in the matrix phases one and two phases earlier).  Tile
-    // t+1 must have landed before the barrier that ends global phase 2t+1,
-    // which for group 0 is its vector phase and for group 1 its matrix phase.
-    const int grp = wave >> 2;
-    auto sync = [&]() __attribute__((always_inline)) {
-      __builtin_amdgcn_sched_barrier(0);
-      ring_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    auto wait_next = [&](int t) __attribute__((always_inline)) {
-      if (t + 2 < n_tiles) wait_dma_keep<DMA_PER_TILE>();
-      else wait_dma();
-    };
-    auto pstep = [&](int t, auto st_tag) __attribute__((always_inline)) {
-      constexpr int ST = decltype(st_tag)::value;
-      if (t + 2 < n_tiles) issue_tile(t + 2, stage(std::integral_constant<int, (ST + 2) & 3>{}));
-      if (t > 0) pv_step(stage(std::integral_constant<int, (ST + 3) & 3>{}));
-      qk_any(stage(st_tag), t);
-      if (grp == 1) wait_next(t);
-      sync();
-      epi();
-      if (grp == 0) wait_next(t);
-      sync();
-    };
-    if (grp == 1) sync();
-    for (int t = 0; t < n_tiles; t += 4) {
-      pstep(t, I0{});
-      if (t + 1 < n_tiles) pstep(t + 1, I1{});
-      if (t + 2 < n_tiles) pstep(t + 2, I2{});
-      if (t + 3 < n_tiles) pstep(t + 3, I3{});
-    }
-    switch ((n_tiles - 1) & 3) {
-      case 0: pv_step(stage(I0{})); break;
-      case 1: pv_step(stage(I1{})); break;
-      case 2: pv_step(stage(I2{})); break;
-      default: pv_step(stage(I3{})); break;
-    }
-    if (grp == 0) sync();
-  }
-
-  // row offsets in binades (the oracle's kappa); rows beyond EXT come out
-  // wrong here and are recomputed by the fallback kernel
-  int kap[NSUB];
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    int k = kmax[s];
-    k = max(k, __shfl_xor(k, 16));
-    k = max(k, __shfl_xor(k, 32));
-    kap[s] = k > 0 ? k : 0;
-  }
-
-  // ---- normalise and store: lane (g, r) holds O[q][16dt + 4g + i]
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    const int q = q_wave + 16 * s + r;
-    if (q < S) {
-      const float inv = 1.0f / L[s][0];
-      uint16_t* orow = a.out + (bh * S + q) * (int64_t)D;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const uint32_t lo = f32_to_bf16_rne(O[s][dt][0] * inv) | ((uint32_t)f32_to_bf16_rne(O[s][dt][1] * inv) << 16);
-        const uint32_t hi = f32_to_bf16_rne(O[s][dt][2] * inv) | ((uint32_t)f32_to_bf16_rne(O[s][dt][3] * inv) << 16);
-        *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = make_uint2(lo, hi);
-      }
-      if (g == 0) {
-        a.row_kappa[bh * S + q] = kap[s];
-        a.row_mguess[bh * S + q] = mg[s];
-      }
-    }
-  }
-#endif  // __HIP_DEVICE_COMPILE__
-}
-
-// Fallback for rows whose scores exceed the frozen max by more than EXT
-// binades: one wave per 32 query rows (two subtiles of 16).  A wave whose
-// rows all stayed within EXT exits at once; otherwise it recomputes its rows
-// from global memory with each row's reference raised by its kappa
-// (accumulator start and block shifts re-based, no in-loop clamp), reading
-// the frozen max and kappa the main kernel stored, and overwrites their
-// outputs.  Rows within EXT come out as the main kernel left them (the
-// re-based sums are the same up to the common power-of-two factor).
-template <int F, int D, bool CAUSAL>
-__global__ void __launch_bounds__(64) fsa_fallback_kernel(AttnArgs a) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int NSUB = 2;
-  constexpr int BITS = Fmt<F>::bits;
-  constexpr int MB = Fmt<F>::mbits;
-  constexpr int PL = F == FMT_E4M3 ? Fmt<F>::emax - 1 : Fmt<F>::emax;
-  constexpr int CAP = 127 - PL;
-  constexpr int RB = D * BITS / 8;
-  constexpr int NDB = D / 32;
-  constexpr int NDT = D / 16;
-  constexpr int VRB = KT * BITS / 8;
-  const int lane = threadIdx.x;
-  const int g = lane >> 4;
-  const int r = lane & 15;
-  const int S = a.S;
-  const int ng = (S + 16 * NSUB - 1) / (16 * NSUB);
-  const int64_t wi = blockIdx.x / ng;
-  if (wi >= (int64_t)a.B * a.hrun) return;
-  const int b = (int)wi / a.hrun;
-  const int h = a.h0 + ((int)wi - b * a.hrun);
-  const int64_t bh = (int64_t)b * a.H + h;
-  const int q0 = (int)(blockIdx.x - wi * ng) * 16 * NSUB;
-
-  int kap[NSUB];
-  float mg[NSUB];
-  bool extreme = false;
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    const int q = q0 + 16 * s + r;
-    kap[s] = q < S ? a.row_kappa[bh * S + q] : 0;
-    mg[s] = q < S ? a.row_mguess[bh * S + q] : 0.0f;
-    extreme |= kap[s] > EXT;
-  }
-  if (__builtin_amdgcn_ballot_w64(extreme) == 0) return;
-
-  const uint8_t* kc = a.kc + wi * (int64_t)a.sk_alloc * RB;
-  const uint8_t* ks = a.ks + wi * (int64_t)a.sk_alloc * NDB;
-  const int64_t v_row = (int64_t)a.sk_alloc * BITS / 8;
-  const uint8_t* vc = a.vc + wi * (int64_t)D * v_row;
-  const int vs_row = a.sk_alloc / 32;
-  const uint8_t* vs = a.vs + wi * (int64_t)D * vs_row;
-  const uint8_t* qc = a.qc + wi * (int64_t)a.sq_alloc * RB;
-  const uint8_t* qs = a.qs + wi * (int64_t)a.sq_alloc * NDB;
-
-  opv<F> qf[NSUB];
-  int qsc[NSUB];
-  v4f mk[NSUB], O[NSUB][NDT], L[NSUB];
-  const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    const int q = q0 + 16 * s + r;      // < sq_alloc: the query padding covers whole groups
-    qf[s] = global_operand<F>(qc + (int64_t)q * RB, g, D);
-    const int qb = g < NDB ? (int)qs[(int64_t)q * NDB + g] : 127;
-    qsc[s] = qb == 255 ? 255 : min(qb + 23, 254);
-    L[s] = zero4;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) O[s][dt] = zero4;
-  }
-  const opv<F> ones = ones_operand<F>();
-
-  int n_tiles = (S + KT - 1) / KT;
-  if (CAUSAL) {
-    const int last_q = q0 + 16 * NSUB - 1 < S - 1 ? q0 + 16 * NSUB - 1 : S - 1;
-    n_tiles = min(n_tiles, last_q / KT + 1);
-  }
-  // The main sweep measures binades on the integer patterns, which saturate
-  // some 320 binades above the guess; take kappa again from the fp32 values
-  // (exact to HI_BINADE).
-  {
-    v4f m0init[NSUB];
-    int km[NSUB];
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      const float c0 = __builtin_fmaf(-8388608.0f, mg[s], 8388608.0f * (float)(127 + REF));
-      m0init[s] = v4f{c0, c0, c0, c0};
-      km[s] = -(1 << 30);
-    }
-    for (int t = 0; t < n_tiles; ++t) {
-      const int key0 = t * KT;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int kk = kpos<F>(r >> 2, 4 * j + (r & 3));
-        const int sc = g < NDB ? (int)ks[(int64_t)t * KT * NDB + (r * NDB + g) * 8 + j] : 127;
-        const opv<F> kf = global_operand<F>(kc + (int64_t)(key0 + kk) * RB, g, D);
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) {
-          const v4f y = mfma<F>(kf, qf[s], m0init[s], sc, qsc[s]);
-          const int q = q0 + 16 * s + r;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = key0 + kpos<F>(g, 4 * j + i);
-            const bool vis = key < S && (!CAUSAL || key <= q);
-            // the binade of each element bounds that of its block's maximum
-            if (vis) km[s] = max(km[s], block_binade<MB>(y[i]));
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      int k = km[s];
-      k = max(k, __shfl_xor(k, 16));
-      k = max(k, __shfl_xor(k, 32));
-      kap[s] = k > 0 ? k : 0;
-      const float c0 = __builtin_fmaf(-8388608.0f, mg[s], 8388608.0f * (float)(127 + REF - kap[s]));
-      mk[s] = v4f{c0, c0, c0, c0};
-      const int q = q0 + 16 * s + r;
-      if (g == 0 && q < S) a.row_kappa[bh * S + q] = kap[s];
-    }
-  }
-  for (int t = 0; t < n_tiles; ++t) {
-    const int key0 = t * KT;
-    v4f acc[NSUB][8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int kk = kpos<F>(r >> 2, 4 * j + (r & 3));
-      const int sc = g < NDB ? (int)ks[(int64_t)t * KT * NDB + (r * NDB + g) * 8 + j] : 127;
-      const opv<F> kf = global_operand<F>(kc + (int64_t)(key0 + kk) * RB, g, D);
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) acc[s][j] = mfma<F>(kf, qf[s], mk[s], sc, qsc[s]);
-    }
-    opv<F> pw[NSUB];
-    int psc[NSUB];
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      const int q = q0 + 16 * s + r;
-      float x[32];
-#pragma unroll
-      for (int p = 0; p < 32; ++p) {
-        const int key = key0 + kpos<F>(g, p);
-        const bool vis = key < S && (!CAUSAL || key <= q);
-        x[p] = vis ? acc[s][p >> 2][p & 3] : -INFINITY;
-      }
-      float m0 = x[0], m1 = x[16];
-#pragma unroll
-      for (int p = 1; p < 16; ++p) { m0 = __builtin_fmaxf(m0, x[p]); m1 = __builtin_fmaxf(m1, x[16 + p]); }
-      if (BITS == 8) {
-        m0 = __builtin_fmaxf(m0, __shfl_xor(m0, 16));
-        m1 = __builtin_fmaxf(m1, __shfl_xor(m1, 16));
-      } else {
-        m0 = __builtin_fmaxf(m0, m1);
-        m1 = m0;
-      }
-      // binades relative to the raised reference: shifts need no EXT clamp
-      const int sb0 = 127 - PL - min(-block_binade<MB>(m0), CAP);
-      const int sb1 = 127 - PL - min(-block_binade<MB>(m1), CAP);
-      float pv[32];
-#pragma unroll
-      for (int p = 0; p < 32; ++p) {
-        const int key = key0 + kpos<F>(g, p);
-        const bool vis = key < S && (!CAUSAL || key <= q);
-        const uint32_t u = cvt_u32_trunc(acc[s][p >> 2][p & 3]);
-        pv[p] = __uint_as_float(vis ? u : 0u);
-      }
-      uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      Pack32<F, false>::run(pv, w, conv_scale(sb0), conv_scale(sb1));
-#pragma unroll
-      for (int i = 0; i < Operand<F>::words; ++i) pw[s][i] = (int)w[i];
-      psc[s] = p_scale<BITS>(sb0, sb1, g);
-    }
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const int d = 16 * dt + r;
-      const opv<F> vf = global_operand<F>(vc + d * v_row + (int64_t)t * VRB, g, KT);
-      const int vsc = (int)vs[(int64_t)t * 4 * D + (r * 4 + g) * NDT + dt];
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) O[s][dt] = mfma<F>(vf, pw[s], O[s][dt], vsc, psc[s]);
-    }
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) L[s] = mfma<F>(ones, pw[s], L[s], 127, psc[s]);
-  }
-
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    const int q = q0 + 16 * s + r;
-    if (q < S) {
-      const float inv = 1.0f / L[s][0];
-      uint16_t* orow = a.out + (bh * S + q) * (int64_t)D;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const uint32_t lo = f32_to_bf16_rne(O[s][dt][0] * inv) | ((uint32_t)f32_to_bf16_rne(O[s][dt][1] * inv) << 16);
-        const uint32_t hi = f32_to_bf16_rne(O[s][dt][2] * inv) | ((uint32_t)f32_to_bf16_rne(O[s][dt][3] * inv) << 16);
-        *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = make_uint2(lo, hi);
-      }
-    }
-  }
-#endif  // __HIP_DEVICE_COMPILE__
-}
-
-// Query subtiles (16 rows each) per wave.  More subtiles reuse every K^/V^T
-// fragment read from LDS for more rows; the count is capped by the 256
-// architectural VGPRs the score accumulators and the epilogue need.
-template <int F> struct Nsub;
-template <> struct Nsub<FMT_E4M3> { static constexpr int value = 2; };
-template <> struct Nsub<FMT_E2M3> { static constexpr int value = 2; };
-template <> struct Nsub<FMT_E2M1> { static constexpr int value = 2; };
-// Waves per workgroup: 8 puts two waves on each SIMD, so one wave's vector
-// epilogue runs while the other's MFMAs occupy the matrix core; FP8's larger
-// operands leave room for only one wave per SIMD.
-template <int F> struct Nwaves;
-template <> struct Nwaves<FMT_E4M3> { static constexpr int value = FSA_NW8; };
-template <> struct Nwaves<FMT_E2M3> { static constexpr int value = FSA_NW6; };
-template <> struct Nwaves<FMT_E2M1> { static constexpr int value = FSA_NW4; };
-
-template <int F, int D, bool CAUSAL>
-static hipError_t launch3(const AttnArgs& a, hipStream_t stream) {
-  constexpr int NSUB = Nsub<F>::value;
-  constexpr int NWAVES = Nwaves<F>::value;
-  constexpr int QW = NWAVES * 16 * NSUB;
-  const int n_items = (a.S + QW - 1) / QW * a.B * a.hrun;
-  dim3 grid((n_items + 7) / 8 * 8);
-  hipLaunchKernelGGL((fsa_fwd_kernel<F, D, CAUSAL, NSUB, NWAVES>), grid, dim3(NWAVES * 64), 0, stream, a);
-  const int n_groups = (a.S + 31) / 32 * a.B * a.hrun;
-  hipLaunchKernelGGL((fsa_fallback_kernel<F, D, CAUSAL>), dim3(n_groups), dim3(64), 0, stream, a);
-  return hipGetLastError();
-}
-
-template <int F>
-static hipError_t launch2(const AttnArgs& a, int D, int causal, hipStream_t stream) {
-  if (D == 128) return causal ? launch3<F, 128, true>(a, stream) : launch3<F, 128, false>(a, stream);
-  return causal ? launch3<F, 64, true>(a, stream) : launch3<F, 64, false>(a, stream);
-}
 
 int fsa_queries_per_workgroup(int fmt) {
   if (fmt == FMT_E4M3) return Nwaves<FMT_E4M3>::value * 16 * Nsub<FMT_E4M3>::value;
@@ -1051,7 +13,7 @@ int fsa_queries_per_workgroup(int fmt) {
 }
 
 hipError_t launch_fsa_fwd(const AttnArgs& a, int fmt, int D, int causal, hipStream_t stream) {
-  if (fmt == FMT_E4M3) return launch2<FMT_E4M3>(a, D, causal, stream);
+  if (fmt == FMT_E4M3) return launch_fsa_fwd_e4m3(a, D, causal, stream);
   if (fmt == FMT_E2M3) return launch2<FMT_E2M3>(a, D, causal, stream);
   return launch2<FMT_E2M1>(a, D, causal, stream);
 }

@@ -63,6 +63,7 @@ struct AttnArgs {
 };
 
 hipError_t launch_fsa_fwd(const AttnArgs& a, int fmt, int D, int causal, hipStream_t stream);
+hipError_t launch_fsa_fwd_e4m3(const AttnArgs& a, int D, int causal, hipStream_t stream);
 int fsa_queries_per_workgroup(int fmt);   // query rows one workgroup covers
 
 // Plain BF16 flash attention.
