@@ -192,3 +192,47 @@ def test_full_size_outliers_e2m1_sampled():
 
 def test_full_size_hybrid_long_sampled():
     g, kap = _full_size("hybrid_long", heads=(0, 19, 20, 39), n_rows=8)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_causal_many_tiles_sampled(fmt):
+    """Causal rows across 16 key tiles: masked tiles at every ring phase and
+    rows whose clean-tile count ranges over the whole sweep."""
+    announce("fsa causal many tiles", fmt)
+    S, D = 2000, 128
+    q, k, v = (W.random_bf16((1, 2, S, D), seed, 1.2) for seed in (21, 22, 23))
+    g, kap, _ = _run(q, k, v, fmt, True)
+    rows = np.array([0, 1, 31, 127, 128, 129, 255, 256, 511, 640, 1023, 1024, 1151, 1500, 1919, 1999])
+    for h in range(2):
+        qh, kh, vh = (W.bf16_bits_to_f64(x[0, h]) for x in (q, k, v))
+        ref, info = O.fused_attention(qh, kh, vh, fmt, True, rows=rows, return_info=True)
+        assert rel_l2(g[0, h, rows], ref) <= TOL
+        assert np.mean(kap[0, h, rows] == info["kappa"]) >= 0.9
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_rows_far_above_the_guess_causal(fmt):
+    """The fallback kernel with causal masking (planted rows past the window)."""
+    announce("fsa far fallback causal", fmt)
+    S, D = 400, 128
+    q, k, v = (W.bf16_bits_to_f64(W.random_bf16((1, 1, S, D), seed, 1.0)) for seed in (31, 32, 33))
+    c = O.attention.score_scale(D)
+    for i, j in ((150, 140), (300, 290), (399, 131)):
+        q[0, 0, i] = k[0, 0, j] * (300.0 / (c * float(k[0, 0, j] @ k[0, 0, j])))
+    q, k, v = (W.f32_to_bf16_bits(x.astype(np.float32)) for x in (q, k, v))
+    g, kap, _ = _run(q, k, v, fmt, True)
+    ref, rk = _oracle_heads(q, k, v, [fmt], True)
+    assert np.all(rk[0, [150, 300, 399]] > 64)
+    _check(g, kap, ref, rk)
+
+
+def test_hybrid_heads_two_batches():
+    """Per-head formats in one call with B = 2: each run of equal formats is
+    quantised and launched per batch entry."""
+    announce("fsa hybrid B=2")
+    S, D = 300, 128
+    fmts = ["e2m3", "e2m3", "e2m1", "e4m3"]
+    q, k, v = (W.random_bf16((2, 4, S, D), seed, 1.1) for seed in (41, 42, 43))
+    g, kap, _ = _run(q, k, v, "e2m3", False, head_fmt=fmts)
+    ref, rk = _oracle_heads(q, k, v, fmts, False)
+    _check(g, kap, ref, rk)
