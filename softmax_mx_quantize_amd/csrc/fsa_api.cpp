@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
@@ -62,6 +63,13 @@ int workspace(size_t need, uint8_t** out) {
   return FSA_OK;
 }
 
+// Ids that tell a fallback kernel whether its own call's main kernel asked
+// for it (the flag word keeps the last id that did).
+uint64_t next_call_id() {
+  static std::atomic<uint64_t> counter{0};
+  return ++counter;
+}
+
 // Sub-allocation inside the workspace, 256-byte aligned.
 struct Carver {
   size_t off = 0;
@@ -107,6 +115,7 @@ int quantize(const uint16_t* x, uint8_t* codes, uint8_t* scales, int64_t batch, 
   a.nb_out = nb_out;
   a.code_stride = code_stride;
   a.scale_stride = scale_stride;
+  a.batch0 = 0;
   a.mult = mult;
   a.scale_layout = scale_layout;
   return fsa::launch_mx_quant(a, fmt, mode, stream) == hipSuccess ? FSA_OK : FSA_ERR_HIP;
@@ -195,6 +204,7 @@ int fsa_attention_fwd_ex(const void* q, const void* k, const void* v, void* out,
   const bool own_mguess = !(opt && opt->row_max_guess);
   const size_t rk_off = own_kappa ? cv.take((size_t)n_rows * 4) : 0;
   const size_t rm_off = own_mguess ? cv.take((size_t)n_rows * 4) : 0;
+  const size_t flag_off = cv.take(8);
   uint8_t* ws = nullptr;
   st = workspace(cv.off, &ws);
   if (st != FSA_OK) return st;
@@ -248,6 +258,8 @@ int fsa_attention_fwd_ex(const void* q, const void* k, const void* v, void* out,
     a.h0 = rl.h0; a.hrun = rl.hrun;
     a.sq_alloc = (int)rl.sq_alloc; a.sk_alloc = (int)sk_alloc;
     a.bias = opt ? opt->guess_bias : 0.0f;
+    a.fb_flag = reinterpret_cast<uint64_t*>(ws + flag_off);
+    a.call_id = next_call_id();
     if (fsa::launch_fsa_fwd(a, kern_fmt(rl.fmt), D, causal, stream) != hipSuccess)
       return FSA_ERR_HIP;
   }

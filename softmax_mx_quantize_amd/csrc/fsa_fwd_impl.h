@@ -852,6 +852,11 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
       }
     }
   }
+  // tell the fallback kernel of this call that it has work (one vector store)
+  bool beyond = false;
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) beyond |= kap[s] > EXT;
+  if (__builtin_amdgcn_ballot_w64(beyond) != 0 && lane == 0) *a.fb_flag = a.call_id;
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -864,8 +869,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
 // outputs.  Rows within EXT come out as the main kernel left them (the
 // re-based sums are the same up to the common power-of-two factor).
 template <int F, int D, bool CAUSAL>
-__global__ void __launch_bounds__(64) fsa_fallback_kernel(AttnArgs a) {
-#if defined(__HIP_DEVICE_COMPILE__)
+__device__ __forceinline__ void fallback_group(const AttnArgs& a, int64_t grp) {
   constexpr int NSUB = 2;
   constexpr int BITS = Fmt<F>::bits;
   constexpr int MB = Fmt<F>::mbits;
@@ -880,12 +884,12 @@ __global__ void __launch_bounds__(64) fsa_fallback_kernel(AttnArgs a) {
   const int r = lane & 15;
   const int S = a.S;
   const int ng = (S + 16 * NSUB - 1) / (16 * NSUB);
-  const int64_t wi = blockIdx.x / ng;
+  const int64_t wi = grp / ng;
   if (wi >= (int64_t)a.B * a.hrun) return;
   const int b = (int)wi / a.hrun;
   const int h = a.h0 + ((int)wi - b * a.hrun);
   const int64_t bh = (int64_t)b * a.H + h;
-  const int q0 = (int)(blockIdx.x - wi * ng) * 16 * NSUB;
+  const int q0 = (int)(grp - wi * ng) * 16 * NSUB;
 
   int kap[NSUB];
   float mg[NSUB];
@@ -1050,6 +1054,17 @@ __global__ void __launch_bounds__(64) fsa_fallback_kernel(AttnArgs a) {
       }
     }
   }
+}
+
+// Grid-stride over groups of 32 query rows; a call whose main kernel found
+// no row beyond EXT binades (flag not stamped with this call's id) exits
+// after one load.
+template <int F, int D, bool CAUSAL>
+__global__ void __launch_bounds__(64) fsa_fallback_kernel(AttnArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  if (*a.fb_flag != a.call_id) return;
+  const int64_t n_groups = (int64_t)(a.S + 31) / 32 * a.B * a.hrun;
+  for (int64_t grp = blockIdx.x; grp < n_groups; grp += gridDim.x) fallback_group<F, D, CAUSAL>(a, grp);
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -1077,7 +1092,8 @@ hipError_t launch3(const AttnArgs& a, hipStream_t stream) {
   dim3 grid((n_items + 7) / 8 * 8);
   hipLaunchKernelGGL((fsa_fwd_kernel<F, D, CAUSAL, NSUB, NWAVES>), grid, dim3(NWAVES * 64), 0, stream, a);
   const int n_groups = (a.S + 31) / 32 * a.B * a.hrun;
-  hipLaunchKernelGGL((fsa_fallback_kernel<F, D, CAUSAL>), dim3(n_groups), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL((fsa_fallback_kernel<F, D, CAUSAL>), dim3(n_groups < 1024 ? n_groups : 1024),
+                     dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

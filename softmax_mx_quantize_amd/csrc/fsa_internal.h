@@ -21,6 +21,7 @@ struct QuantArgs {
   int64_t nb_out;        // blocks per output row
   int64_t code_stride;   // bytes between output code rows
   int64_t scale_stride;  // bytes between output scale rows
+  int64_t batch0;        // first batch entry of this launch (columns mode)
   float mult;            // every input value is multiplied by this (fp32) first
   int scale_layout;      // SCALES_* below
 };
@@ -60,6 +61,8 @@ struct AttnArgs {
   int h0, hrun;                  // heads [h0, h0+hrun) of each batch entry
   int sq_alloc, sk_alloc;
   float bias;                    // added to every frozen max, binades
+  uint64_t* fb_flag;             // stamped with call_id when a row needs the fallback
+  uint64_t call_id;              // unique per call (never 0)
 };
 
 hipError_t launch_fsa_fwd(const AttnArgs& a, int fmt, int D, int causal, hipStream_t stream);

@@ -15,71 +15,20 @@
 // One thread owns one 32-element block.  Rows mode: the block runs along the
 // contiguous axis and consecutive threads take consecutive blocks of a row
 // (64-byte loads per thread, contiguous across the wave).  Columns mode: the
-// block runs along the row axis and the output is transposed; consecutive
-// threads take consecutive columns so each of the 32 loads is contiguous
-// across the wave.
+// block runs along the row axis and the output is transposed; a workgroup
+// stages a 128-row x 32-column tile in LDS with 16-byte loads first.
 #include "fsa_device.h"
 #include "fsa_internal.h"
 
 namespace fsa {
 
-template <int F, int MODE, bool VEC>
-__global__ void __launch_bounds__(256) mx_quant_kernel(QuantArgs a) {
+// Quantise one block of 32 values (already multiplied by a.mult) and write
+// its codes and scale byte: output row o (over all batch entries), block b.
+template <int F>
+__device__ __forceinline__ void quantize_block(const QuantArgs& a, float (&v)[32], bool bad,
+                                               int64_t o, int64_t b) {
   constexpr int BITS = Fmt<F>::bits;
   constexpr int OUT_BYTES = 4 * BITS;   // 32 elements
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t n_out_rows = a.batch * a.out_rows;
-  if (t >= n_out_rows * a.nb_out) return;
-  int64_t o, b;
-  if (MODE == 0) { o = t / a.nb_out; b = t - o * a.nb_out; }
-  else           { o = t % n_out_rows; b = t / n_out_rows; }
-
-  float v[32];
-  bool bad = false;
-  if (MODE == 0) {
-    const int64_t bt = o / a.out_rows;
-    const int64_t r = o - bt * a.out_rows;
-    const int64_t c0 = b * 32;
-    const bool row_ok = r < a.rows;
-    const uint16_t* src = a.x + (bt * a.rows + r) * a.cols + c0;
-    if (VEC && row_ok && c0 + 32 <= a.cols) {
-      const uint4* s4 = reinterpret_cast<const uint4*>(src);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint4 q = s4[i];
-        uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          uint32_t lo = w[k] & 0xFFFF, hi = w[k] >> 16;
-          bad |= ((lo & 0x7F80) == 0x7F80) | ((hi & 0x7F80) == 0x7F80);
-          v[8 * i + 2 * k] = bf16_bits_to_float(lo) * a.mult;
-          v[8 * i + 2 * k + 1] = bf16_bits_to_float(hi) * a.mult;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        uint32_t bits = 0;
-        if (row_ok && c0 + j < a.cols) bits = src[j];
-        bad |= (bits & 0x7F80) == 0x7F80;
-        v[j] = bf16_bits_to_float(bits) * a.mult;
-      }
-    }
-  } else {
-    // o = (batch, column); the block covers rows [32b, 32b+32)
-    const int64_t bt = o / a.cols;
-    const int64_t c = o - bt * a.cols;
-    const int64_t r0 = b * 32;
-    const uint16_t* src = a.x + (bt * a.rows) * a.cols + c;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      uint32_t bits = 0;
-      if (r0 + j < a.rows) bits = src[(r0 + j) * a.cols];
-      bad |= (bits & 0x7F80) == 0x7F80;
-      v[j] = bf16_bits_to_float(bits) * a.mult;
-    }
-  }
-
   float amax = 0.0f;
 #pragma unroll
   for (int j = 0; j < 32; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j]));
@@ -132,28 +81,127 @@ __global__ void __launch_bounds__(256) mx_quant_kernel(QuantArgs a) {
   a.scales[so] = sbyte;
 }
 
-template <int F, int MODE>
-static hipError_t launch_quant_fmt(const QuantArgs& a, hipStream_t stream) {
-  const int64_t total = a.batch * a.out_rows * a.nb_out;
-  const int64_t grid = (total + 255) / 256;
-  const bool vec = MODE == 0 && (a.cols % 32 == 0) &&
-                   ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0);
-  if (vec)
-    hipLaunchKernelGGL((mx_quant_kernel<F, MODE, true>), dim3((unsigned)grid), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((mx_quant_kernel<F, MODE, false>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+// Rows mode: blocks along the contiguous axis; one thread per block,
+// consecutive threads take consecutive blocks of a row (64-byte loads per
+// thread, contiguous across the wave).
+template <int F, bool VEC>
+__global__ void __launch_bounds__(256) mx_quant_rows_kernel(QuantArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n_out_rows = a.batch * a.out_rows;
+  if (t >= n_out_rows * a.nb_out) return;
+  const int64_t o = t / a.nb_out;
+  const int64_t b = t - o * a.nb_out;
+  float v[32];
+  bool bad = false;
+  const int64_t bt = o / a.out_rows;
+  const int64_t r = o - bt * a.out_rows;
+  const int64_t c0 = b * 32;
+  const bool row_ok = r < a.rows;
+  const uint16_t* src = a.x + (bt * a.rows + r) * a.cols + c0;
+  if (VEC && row_ok && c0 + 32 <= a.cols) {
+    const uint4* s4 = reinterpret_cast<const uint4*>(src);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint4 q = s4[i];
+      uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint32_t lo = w[k] & 0xFFFF, hi = w[k] >> 16;
+        bad |= ((lo & 0x7F80) == 0x7F80) | ((hi & 0x7F80) == 0x7F80);
+        v[8 * i + 2 * k] = bf16_bits_to_float(lo) * a.mult;
+        v[8 * i + 2 * k + 1] = bf16_bits_to_float(hi) * a.mult;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      uint32_t bits = 0;
+      if (row_ok && c0 + j < a.cols) bits = src[j];
+      bad |= (bits & 0x7F80) == 0x7F80;
+      v[j] = bf16_bits_to_float(bits) * a.mult;
+    }
+  }
+  quantize_block<F>(a, v, bad, o, b);
+}
+
+// Columns mode: blocks run along the row axis and the output is transposed.
+// A workgroup of 128 threads stages a tile of 128 input rows x 32 columns in
+// LDS with 16-byte loads (a row segment of 64 bytes per input row), then
+// thread (column c = t % 32, block kb = t / 32) quantises the 32 rows of
+// block kb in its column.
+constexpr int QC_ROWS = 128, QC_COLS = 32;
+template <int F, bool VEC>
+__global__ void __launch_bounds__(128) mx_quant_cols_kernel(QuantArgs a) {
+  __shared__ __align__(16) uint16_t tile[QC_ROWS][QC_COLS];
+  const int t = threadIdx.x;
+  const int64_t bt = a.batch0 + blockIdx.z;
+  const int64_t col0 = (int64_t)blockIdx.y * QC_COLS;
+  const int64_t row0 = (int64_t)blockIdx.x * QC_ROWS;
+  const uint16_t* src = a.x + bt * a.rows * a.cols;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = t + 128 * i;               // 16-byte chunk: row c/4, part c%4
+    const int row = c >> 2, part = c & 3;
+    const int64_t gr = row0 + row, gc = col0 + part * 8;
+    uint4 q = make_uint4(0, 0, 0, 0);
+    if (VEC) {
+      if (gr < a.rows && gc + 8 <= a.cols)
+        q = *reinterpret_cast<const uint4*>(src + gr * a.cols + gc);
+    } else if (gr < a.rows) {
+      uint32_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[e] = gc + e < a.cols ? src[gr * a.cols + gc + e] : 0u;
+      q = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+    }
+    *reinterpret_cast<uint4*>(&tile[row][part * 8]) = q;
+  }
+  __syncthreads();
+  const int cc = t & 31, kb = t >> 5;
+  const int64_t col = col0 + cc;
+  const int64_t b = (int64_t)blockIdx.x * (QC_ROWS / 32) + kb;
+  if (col >= a.cols || b >= a.nb_out) return;
+  float v[32];
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const uint32_t bits = tile[32 * kb + j][cc];
+    bad |= (bits & 0x7F80) == 0x7F80;
+    v[j] = bf16_bits_to_float(bits) * a.mult;
+  }
+  quantize_block<F>(a, v, bad, bt * a.out_rows + col, b);
+}
+
+template <int F>
+static hipError_t launch_quant_fmt(const QuantArgs& a, int mode, hipStream_t stream) {
+  const bool aligned = (reinterpret_cast<uintptr_t>(a.x) & 15) == 0;
+  if (mode == 0) {
+    const int64_t total = a.batch * a.out_rows * a.nb_out;
+    const int64_t grid = (total + 255) / 256;
+    if (a.cols % 32 == 0 && aligned)
+      hipLaunchKernelGGL((mx_quant_rows_kernel<F, true>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((mx_quant_rows_kernel<F, false>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+  } else {
+    // batch entries go in grid.z, in launches of at most 65535
+    for (int64_t b0 = 0; b0 < a.batch; b0 += 65535) {
+      QuantArgs c = a;
+      c.batch0 = b0;
+      const int64_t nb = a.batch - b0 < 65535 ? a.batch - b0 : 65535;
+      const dim3 grid((unsigned)((a.nb_out + QC_ROWS / 32 - 1) / (QC_ROWS / 32)),
+                      (unsigned)((a.cols + QC_COLS - 1) / QC_COLS), (unsigned)nb);
+      if (a.cols % 8 == 0 && aligned)
+        hipLaunchKernelGGL((mx_quant_cols_kernel<F, true>), grid, dim3(128), 0, stream, c);
+      else
+        hipLaunchKernelGGL((mx_quant_cols_kernel<F, false>), grid, dim3(128), 0, stream, c);
+    }
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_mx_quant(const QuantArgs& a, int fmt, int mode, hipStream_t stream) {
-  if (mode == 0) {
-    if (fmt == FMT_E4M3) return launch_quant_fmt<FMT_E4M3, 0>(a, stream);
-    if (fmt == FMT_E2M3) return launch_quant_fmt<FMT_E2M3, 0>(a, stream);
-    return launch_quant_fmt<FMT_E2M1, 0>(a, stream);
-  }
-  if (fmt == FMT_E4M3) return launch_quant_fmt<FMT_E4M3, 1>(a, stream);
-  if (fmt == FMT_E2M3) return launch_quant_fmt<FMT_E2M3, 1>(a, stream);
-  return launch_quant_fmt<FMT_E2M1, 1>(a, stream);
+  if (fmt == FMT_E4M3) return launch_quant_fmt<FMT_E4M3>(a, mode, stream);
+  if (fmt == FMT_E2M3) return launch_quant_fmt<FMT_E2M3>(a, mode, stream);
+  return launch_quant_fmt<FMT_E2M1>(a, mode, stream);
 }
 
 }  // namespace fsa
