@@ -601,6 +601,14 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
     return o;
   };
 
+  // FP6 fragments arrive in three 8-byte pieces per lane; left free, the
+  // scheduler hoists them for many slices at once and pays in register
+  // copies.  A scheduling fence after each slice's MFMAs keeps FP6 loads
+  // next to their use (measured: about +20 % for E2M3, a loss for the others).
+  auto slice_fence = [&]() __attribute__((always_inline)) {
+    if constexpr (BITS == 6) __builtin_amdgcn_sched_barrier(0);
+  };
+
   // The three steps of one key tile, on state shared across phases.  The
   // pipelined schedule keeps two score buffers (tiles of even and odd index).
   v4f acc[NSUB][8];
@@ -634,6 +642,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
       for (int s = 0; s < NSUB; ++s)
         acc[s][j] = mfma_sel<F>(kf, qf[s], MASKED ? acc[s][j] : minit[s],
                                 (int)(j < 4 ? ksc.x : ksc.y), j, qsc[s]);
+      slice_fence();
     }
   };
 
@@ -700,6 +709,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
     for (int dt = 0; dt < NDT; ++dt) {
       const opv<F> vf = frag(base, v_off, 16 * dt * RS, true, true);
       O[s][dt] = mfma_sel<F>(vf, pw[s], O[s][dt], (int)(dt < 4 ? vsc.x : vsc.y), dt, psc[s]);
+      slice_fence();
     }
     L[s] = mfma<F>(ones, pw[s], L[s], 127, psc[s]);
   };
@@ -713,6 +723,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
 #pragma unroll
       for (int s = 0; s < NSUB; ++s)
         O[s][dt] = mfma_sel<F>(vf, pw[s], O[s][dt], (int)(dt < 4 ? vsc.x : vsc.y), dt, psc[s]);
+      slice_fence();
     }
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) L[s] = mfma<F>(ones, pw[s], L[s], 127, psc[s]);
