@@ -88,13 +88,15 @@ int fsa_quantize_mx(const void* x_bf16, void* codes, void* scales_e8m0,
 /*
  * fsa_attention_fwd -- fused-softmax attention forward with MX operands.
  *
- * q, k, v : device, bf16 [B][H][S][D]; out : device, bf16 [B][H][S][D].
+ * q, k, v : device, bf16 [B][H][S][D]; out : device, bf16 [B][H][S][D];
+ *     all four 16-byte aligned (else FSA_ERR_INVALID_ARG).
  * Softmax scale 1/sqrt(D).  D must be 64 or 128 (else FSA_ERR_UNSUPPORTED).
  * fmt : element format of Q, K, V and P (fsa_fmt).  causal : 0 or 1 (key j
  * visible to query i iff j <= i).
- * The call MX-quantises Q times log2(e)/sqrt(D), K (blocks along D) and V
- * (blocks along the keys) into the library workspace, then runs one fused
- * kernel: frozen max from the first 128 keys, a score product whose fp32
+ * The call MX-quantises K (blocks along D) and V (blocks along the keys)
+ * into the library workspace, then runs one fused kernel that MX-quantises
+ * Q times log2(e)/sqrt(D) in its prologue: frozen max from the first 128
+ * keys, a score product whose fp32
  * output already is the bit-pattern exponential's exponent field (softmax
  * scale in Q, 2^23 in Q's block scale, max subtraction in the accumulator
  * start), MX quantisation of P in the accumulator epilogue (block shifts

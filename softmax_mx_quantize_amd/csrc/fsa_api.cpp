@@ -82,8 +82,7 @@ struct Carver {
 
 struct RunLayout {
   int h0, hrun, fmt;
-  int64_t sq_alloc;
-  size_t qc, qs, kc, ks, vc, vs;
+  size_t kc, ks, vc, vs;
 };
 
 int validate_attn(const void* q, const void* k, const void* v, void* out, int B, int H, int S,
@@ -96,6 +95,8 @@ int validate_attn(const void* q, const void* k, const void* v, void* out, int B,
   if ((int64_t)B * H > 65535) return FSA_ERR_INVALID_ARG;    // grid.y limit
   if (S > (1 << 30)) return FSA_ERR_INVALID_ARG;
   if (out == q || out == k || out == v) return FSA_ERR_INVALID_ARG;
+  for (const void* p : {q, k, v, static_cast<const void*>(out)})
+    if (reinterpret_cast<uintptr_t>(p) & 15) return FSA_ERR_INVALID_ARG;   // 16-byte vector loads
   if (D != 64 && D != 128) return FSA_ERR_UNSUPPORTED;
   return FSA_OK;
 }
@@ -187,11 +188,6 @@ int fsa_attention_fwd_ex(const void* q, const void* k, const void* v, void* out,
   for (RunLayout& rl : runs) {
     const int bits = fmt_bits(rl.fmt);
     const int64_t nbh = (int64_t)B * rl.hrun;
-    // Q^ rows cover every query row the run's grid touches
-    rl.sq_alloc = round_up(S, fsa::fsa_queries_per_workgroup(kern_fmt(rl.fmt)));
-    const int64_t sq_alloc = rl.sq_alloc;
-    rl.qc = cv.take((size_t)(nbh * sq_alloc * D * bits / 8));
-    rl.qs = cv.take((size_t)(nbh * sq_alloc * (D / 32)));
     rl.kc = cv.take((size_t)(nbh * sk_alloc * D * bits / 8));
     rl.ks = cv.take((size_t)(nbh * sk_alloc * (D / 32)));
     rl.vc = cv.take((size_t)(nbh * D * sk_alloc * bits / 8));
@@ -215,21 +211,18 @@ int fsa_attention_fwd_ex(const void* q, const void* k, const void* v, void* out,
   const uint16_t* kb = static_cast<const uint16_t*>(k);
   const uint16_t* vb = static_cast<const uint16_t*>(v);
 
-  // MX-quantise Q, K (blocks along D) and V (blocks along the keys, stored
-  // transposed) for every run; padding rows and blocks get zero codes.  Q
-  // carries the softmax scale in binades, c = fp32(log2(e) / sqrt(D)), so
-  // that the score product comes out in binades of the probability.
+  // MX-quantise K (blocks along D) and V (blocks along the keys, stored
+  // transposed) for every run; padding rows and blocks get zero codes.  Q is
+  // quantised inside the attention kernel, after scaling by the softmax scale
+  // in binades, c = fp32(log2(e) / sqrt(D)), so that the score product comes
+  // out in binades of the probability.
   const float score_scale = (float)((1.0 / std::log(2.0)) / std::sqrt((double)D));
   for (const RunLayout& rl : runs) {
     const int bits = fmt_bits(rl.fmt);
     const int64_t rb = (int64_t)D * bits / 8;
-    const int64_t sq_alloc = rl.sq_alloc;
     for (int b = 0; b < B; ++b) {
       const int64_t src = ((int64_t)b * H + rl.h0) * S * D;
       const int64_t w0 = (int64_t)b * rl.hrun;
-      st = quantize(qb + src, ws + rl.qc + w0 * sq_alloc * rb, ws + rl.qs + w0 * sq_alloc * (D / 32),
-                    rl.hrun, S, D, sq_alloc, D / 32, rb, D / 32, rl.fmt, 0, stream, score_scale);
-      if (st != FSA_OK) return st;
       st = quantize(kb + src, ws + rl.kc + w0 * sk_alloc * rb, ws + rl.ks + w0 * sk_alloc * (D / 32),
                     rl.hrun, S, D, sk_alloc, D / 32, rb, D / 32, rl.fmt, 0, stream, 1.0f,
                     fsa::SCALES_KEY_TILES);
@@ -248,7 +241,8 @@ int fsa_attention_fwd_ex(const void* q, const void* k, const void* v, void* out,
 
   for (const RunLayout& rl : runs) {
     fsa::AttnArgs a;
-    a.qc = ws + rl.qc; a.qs = ws + rl.qs;
+    a.q = qb;
+    a.qmul = score_scale;
     a.kc = ws + rl.kc; a.ks = ws + rl.ks;
     a.vc = ws + rl.vc; a.vs = ws + rl.vs;
     a.out = static_cast<uint16_t*>(out);
@@ -256,7 +250,7 @@ int fsa_attention_fwd_ex(const void* q, const void* k, const void* v, void* out,
     a.row_mguess = row_mguess;
     a.B = B; a.H = H; a.S = S;
     a.h0 = rl.h0; a.hrun = rl.hrun;
-    a.sq_alloc = (int)rl.sq_alloc; a.sk_alloc = (int)sk_alloc;
+    a.sk_alloc = (int)sk_alloc;
     a.bias = opt ? opt->guess_bias : 0.0f;
     a.fb_flag = reinterpret_cast<uint64_t*>(ws + flag_off);
     a.call_id = next_call_id();

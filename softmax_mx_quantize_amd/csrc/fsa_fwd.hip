@@ -6,12 +6,6 @@
 
 namespace fsa {
 
-int fsa_queries_per_workgroup(int fmt) {
-  if (fmt == FMT_E4M3) return Nwaves<FMT_E4M3>::value * 16 * Nsub<FMT_E4M3>::value;
-  if (fmt == FMT_E2M3) return Nwaves<FMT_E2M3>::value * 16 * Nsub<FMT_E2M3>::value;
-  return Nwaves<FMT_E2M1>::value * 16 * Nsub<FMT_E2M1>::value;
-}
-
 hipError_t launch_fsa_fwd(const AttnArgs& a, int fmt, int D, int causal, hipStream_t stream) {
   if (fmt == FMT_E4M3) return launch_fsa_fwd_e4m3(a, D, causal, stream);
   if (fmt == FMT_E2M3) return launch2<FMT_E2M3>(a, D, causal, stream);

@@ -276,6 +276,75 @@ __device__ __forceinline__ int p_scale(int s_lo, int s_hi, int g) {
   return cross ? got : own;
 }
 
+// The lane's Q' operand of the score product, MX-quantised here from the
+// bf16 row (the same rule as the quantiser: OCP floor scale, RNE, saturation,
+// NaN/Inf blocks get scale 0xFF and zero codes) with Q' = fp32(q * mult).
+// `row` is null for padding rows.  Returns the codes in operand order and
+// sets `sc` to the E8M0 byte of the block this lane group scales, raised by
+// 23 (2^23 rides on Q's scale; 255 stays NaN).
+template <int F, int D>
+__device__ __forceinline__ opv<F> q_operand(const uint16_t* row, float mult, int g, int& sc) {
+  constexpr int BITS = Fmt<F>::bits;
+  float v[32];
+  bool bad_lo = false, bad_hi = false;
+  // element k of the operand: FP6/FP4 column 32g + k; FP8 column 16g + k
+  // (k < 16) and 64 + 16g + (k - 16)
+  auto column = [&](int k) { return BITS == 8 ? (k < 16 ? 16 * g + k : 64 + 16 * g + k - 16) : 32 * g + k; };
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {                      // four 8-element chunks
+    const int col = column(8 * c);
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (row != nullptr && col < D) w = *reinterpret_cast<const uint4*>(row + col);
+    const uint32_t h[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = h[e] & 0xFFFF, hi = h[e] >> 16;
+      const bool nan_inf = ((lo & 0x7F80) == 0x7F80) | ((hi & 0x7F80) == 0x7F80);
+      if (c < 2) bad_lo |= nan_inf; else bad_hi |= nan_inf;
+      v[8 * c + 2 * e] = bf16_bits_to_float(lo) * mult;
+      v[8 * c + 2 * e + 1] = bf16_bits_to_float(hi) * mult;
+    }
+  }
+  float a_lo = 0.0f, a_hi = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    a_lo = __builtin_fmaxf(a_lo, __builtin_fabsf(v[k]));
+    a_hi = __builtin_fmaxf(a_hi, __builtin_fabsf(v[16 + k]));
+  }
+  if (BITS == 8) {
+    // each MX block is two half blocks held by lanes 16 apart
+    a_lo = __builtin_fmaxf(a_lo, __shfl_xor(a_lo, 16));
+    a_hi = __builtin_fmaxf(a_hi, __shfl_xor(a_hi, 16));
+    bad_lo |= __shfl_xor((int)bad_lo, 16) != 0;
+    bad_hi |= __shfl_xor((int)bad_hi, 16) != 0;
+  } else {
+    a_lo = a_hi = __builtin_fmaxf(a_lo, a_hi);
+    bad_lo = bad_hi = bad_lo | bad_hi;
+  }
+  auto scale_exp = [](float amax) {
+    int X = amax > 0.0f ? floor_log2(amax) - Fmt<F>::emax : -127;
+    return X < -127 ? -127 : (X > 127 ? 127 : X);
+  };
+  const int x_lo = scale_exp(a_lo), x_hi = scale_exp(a_hi);
+  float y[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) y[k] = __builtin_ldexpf(v[k], -(k < 16 ? x_lo : x_hi));
+  uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  Pack32<F, true>::run(y, w);
+  if (bad_lo) { for (int i = 0; i < 4; ++i) w[i] = 0; }
+  if (bad_hi) { for (int i = 4; i < 8; ++i) w[i] = 0; }
+  if (BITS != 8 && bad_lo) { for (int i = 0; i < 8; ++i) w[i] = 0; }
+  auto raised = [](int x, bool bad) { return bad ? 255 : min(x + 127 + 23, 254); };
+  int s_lo = raised(x_lo, bad_lo), s_hi = raised(x_hi, bad_hi);
+  if (BITS == 8 && D < 128) s_hi = 127;                // blocks past D: zeros
+  if (BITS != 8 && 32 * g >= D) s_lo = s_hi = 127;
+  sc = p_scale<BITS>(s_lo, s_hi, g);
+  opv<F> o;
+#pragma unroll
+  for (int i = 0; i < Operand<F>::words; ++i) o[i] = (int)w[i];
+  return o;
+}
+
 __device__ __forceinline__ void dma16(const void* g, uint8_t* lds_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);
 }
@@ -442,18 +511,12 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   // ---- Q^ fragments (B operand of the score product), one per subtile
   opv<F> qf[NSUB];
   int qsc[NSUB];
-  {
-    const uint8_t* qc = a.qc + wi * (int64_t)a.sq_alloc * RB;
-    const uint8_t* qs = a.qs + wi * (int64_t)a.sq_alloc * NDB;
+  // quantised here from the bf16 rows; 2^23 rides on Q's E8M0 scale, so the
+  // product is 2^23 s: the exponent-field units of the exponential
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      const int q = q_wave + 16 * s + r;
-      qf[s] = global_operand<F>(qc + (int64_t)q * RB, g, D);
-      // 2^23 rides on Q's E8M0 scale, so the product is 2^23 s: the
-      // exponent-field units of the bit-pattern exponential (255 stays NaN)
-      const int qb = g < NDB ? (int)qs[(int64_t)q * NDB + g] : 127;
-      qsc[s] = qb == 255 ? 255 : min(qb + 23, 254);
-    }
+  for (int s = 0; s < NSUB; ++s) {
+    const int q = q_wave + 16 * s + r;
+    qf[s] = q_operand<F, D>(q < S ? a.q + (bh * S + q) * (int64_t)D : nullptr, a.qmul, g, qsc[s]);
   }
 
   // A operand of the score product for 16-key slice j of the tile in stage
@@ -920,8 +983,6 @@ __device__ __forceinline__ void fallback_group(const AttnArgs& a, int64_t grp) {
   const uint8_t* vc = a.vc + wi * (int64_t)D * v_row;
   const int vs_row = a.sk_alloc / 32;
   const uint8_t* vs = a.vs + wi * (int64_t)D * vs_row;
-  const uint8_t* qc = a.qc + wi * (int64_t)a.sq_alloc * RB;
-  const uint8_t* qs = a.qs + wi * (int64_t)a.sq_alloc * NDB;
 
   opv<F> qf[NSUB];
   int qsc[NSUB];
@@ -929,10 +990,8 @@ __device__ __forceinline__ void fallback_group(const AttnArgs& a, int64_t grp) {
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
-    const int q = q0 + 16 * s + r;      // < sq_alloc: the query padding covers whole groups
-    qf[s] = global_operand<F>(qc + (int64_t)q * RB, g, D);
-    const int qb = g < NDB ? (int)qs[(int64_t)q * NDB + g] : 127;
-    qsc[s] = qb == 255 ? 255 : min(qb + 23, 254);
+    const int q = q0 + 16 * s + r;
+    qf[s] = q_operand<F, D>(q < S ? a.q + (bh * S + q) * (int64_t)D : nullptr, a.qmul, g, qsc[s]);
     L[s] = zero4;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) O[s][dt] = zero4;

@@ -42,16 +42,14 @@ enum { SCALES_ROWS = 0, SCALES_KEY_TILES = 1, SCALES_DIM_TILES = 2 };
 
 hipError_t launch_mx_quant(const QuantArgs& a, int fmt, int mode, hipStream_t stream);
 
-// Fused attention over MX operands prepared by the quantiser, for the heads
-// [h0, h0+hrun) of every batch entry.  Workspace slabs are indexed by
-// w = b*hrun + (h - h0):
-//   Q^ codes [BH][sq_alloc][D*bits/8], scales [BH][sq_alloc][D/32]
-//   K^ codes [BH][sk_alloc][D*bits/8], scales [BH][sk_alloc][D/32]
-//   V^ (transposed) codes [BH][D][sk_alloc*bits/8], scales [BH][D][sk_alloc/32]
-// sq_alloc covers every query tile of the grid, sk_alloc every key tile; the
-// padding holds zero codes.
+// Fused attention for the heads [h0, h0+hrun) of every batch entry.  Q is
+// read as bf16 and MX-quantised in the kernel (times qmul); K^ and V^ come
+// from the quantiser.  Workspace slabs are indexed by w = b*hrun + (h - h0):
+//   K^ codes [BH][sk_alloc][D*bits/8], scales key-tile ordered
+//   V^ (transposed) codes [BH][D][sk_alloc*bits/8], scales dim-tile ordered
+// sk_alloc covers every key tile; the padding holds zero codes.
 struct AttnArgs {
-  const uint8_t* qc; const uint8_t* qs;
+  const uint16_t* q;             // bf16 [B][H][S][D]
   const uint8_t* kc; const uint8_t* ks;
   const uint8_t* vc; const uint8_t* vs;
   uint16_t* out;                 // bf16 [B][H][S][D]
@@ -59,7 +57,8 @@ struct AttnArgs {
   float* row_mguess;             // [B][H][S], likewise (frozen max, binades)
   int B, H, S;
   int h0, hrun;                  // heads [h0, h0+hrun) of each batch entry
-  int sq_alloc, sk_alloc;
+  int sk_alloc;
+  float qmul;                    // log2(e) / sqrt(D), applied to Q before quantisation
   float bias;                    // added to every frozen max, binades
   uint64_t* fb_flag;             // stamped with call_id when a row needs the fallback
   uint64_t call_id;              // unique per call (never 0)
@@ -67,7 +66,6 @@ struct AttnArgs {
 
 hipError_t launch_fsa_fwd(const AttnArgs& a, int fmt, int D, int causal, hipStream_t stream);
 hipError_t launch_fsa_fwd_e4m3(const AttnArgs& a, int D, int causal, hipStream_t stream);
-int fsa_queries_per_workgroup(int fmt);   // query rows one workgroup covers
 
 // Plain BF16 flash attention.
 struct Bf16Args {

@@ -39,27 +39,31 @@ def test_strerror_and_argument_validation_without_gpu():
     assert fsa.strerror(12345) == "unknown status"
     fake = 4096          # never dereferenced: validation fails first
     # null pointers
-    assert lib.fsa_attention_fwd(None, fake, fake, fake + 8, 1, 1, 8, 64, 0, 0, None) == -1
-    assert lib.fsa_attention_bf16_ref(fake, None, fake, fake + 8, 1, 1, 8, 64, 0, None) == -1
+    assert lib.fsa_attention_fwd(None, fake, fake, fake + 4096, 1, 1, 8, 64, 0, 0, None) == -1
+    assert lib.fsa_attention_bf16_ref(fake, None, fake, fake + 4096, 1, 1, 8, 64, 0, None) == -1
     assert lib.fsa_quantize_mx(None, fake, fake, 1, 1, 32, 0, 0, None) == -1
     # sizes, enums, aliasing
-    assert lib.fsa_attention_fwd(fake, fake, fake, fake + 8, 0, 1, 8, 64, 0, 0, None) == -1
-    assert lib.fsa_attention_fwd(fake, fake, fake, fake + 8, 1, 1, -3, 64, 0, 0, None) == -1
-    assert lib.fsa_attention_fwd(fake, fake, fake, fake + 8, 1, 1, 8, 64, 7, 0, None) == -1
-    assert lib.fsa_attention_fwd(fake, fake, fake, fake + 8, 1, 1, 8, 64, 0, 2, None) == -1
-    assert lib.fsa_attention_fwd(fake, fake + 8, fake + 16, fake, 1, 1, 8, 64, 0, 0, None) == -1
-    assert lib.fsa_attention_fwd(fake, fake, fake, fake + 8, 1 << 20, 1 << 10, 1 << 20, 128, 0, 0, None) == -1
+    assert lib.fsa_attention_fwd(fake, fake, fake, fake + 4096, 0, 1, 8, 64, 0, 0, None) == -1
+    assert lib.fsa_attention_fwd(fake, fake, fake, fake + 4096, 1, 1, -3, 64, 0, 0, None) == -1
+    assert lib.fsa_attention_fwd(fake, fake, fake, fake + 4096, 1, 1, 8, 64, 7, 0, None) == -1
+    assert lib.fsa_attention_fwd(fake, fake, fake, fake + 4096, 1, 1, 8, 64, 0, 2, None) == -1
+    assert lib.fsa_attention_fwd(fake, fake + 4096, fake + 8192, fake, 1, 1, 8, 64, 0, 0, None) == -1
+    assert lib.fsa_attention_fwd(fake, fake, fake, fake + 4096, 1 << 20, 1 << 10, 1 << 20, 128, 0, 0, None) == -1
     assert lib.fsa_quantize_mx(fake, fake, fake, 1, 0, 32, 0, 0, None) == -1
     assert lib.fsa_quantize_mx(fake, fake, fake, 1, 1, 32, 3, 0, None) == -1
     assert lib.fsa_quantize_mx(fake, fake, fake, 1, 1, 32, 0, 2, None) == -1
+    # misaligned tensors (16-byte vector loads), checked before the head dim
+    assert lib.fsa_attention_fwd(fake, fake + 4096, fake + 8192, fake + 8, 1, 1, 8, 96, 0, 0, None) == -1
+    assert lib.fsa_attention_fwd(fake + 2, fake + 4096, fake + 8192, fake + 12288, 1, 1, 8, 96, 0, 0,
+                                 None) == -1
     # unsupported head dim
-    assert lib.fsa_attention_fwd(fake, fake, fake, fake + 8, 1, 1, 8, 96, 0, 0, None) == -2
-    assert lib.fsa_attention_bf16_ref(fake, fake, fake, fake + 8, 1, 1, 8, 80, 0, None) == -2
+    assert lib.fsa_attention_fwd(fake, fake, fake, fake + 4096, 1, 1, 8, 96, 0, 0, None) == -2
+    assert lib.fsa_attention_bf16_ref(fake, fake, fake, fake + 4096, 1, 1, 8, 80, 0, None) == -2
     # bad per-head format in the options
     opt = fsa.Options()
     hf = (ctypes.c_int * 2)(0, 9)
     opt.head_fmt = hf
-    assert lib.fsa_attention_fwd_ex(fake, fake, fake, fake + 8, 1, 2, 8, 64, 0, 0,
+    assert lib.fsa_attention_fwd_ex(fake, fake, fake, fake + 4096, 1, 2, 8, 64, 0, 0,
                                     ctypes.byref(opt), None) == -1
 
 
