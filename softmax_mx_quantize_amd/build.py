@@ -22,11 +22,11 @@ LIB = os.environ.get("FSA_LIB_OUT") or os.path.join(PKG, "libfsa.so")
 
 SOURCES = ["fsa_api.cpp", "mx_quant.hip", "fsa_fwd.hip", "fsa_fwd_e4m3.hip", "bf16_fa.hip"]
 
-# Per-source options.  The E2M3/E2M1 kernels run two waves per SIMD and
-# consume the score MFMA results on the vector units; asking for the VGPR
-# form of every MFMA keeps them out of AGPRs (no accvgpr moves in the loop).
-# The E4M3 kernel runs one wave per SIMD and gains from AGPR accumulators.
-SOURCE_FLAGS = {"fsa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source options.  The fused kernels run two waves per SIMD and consume
+# the score MFMA results on the vector units; asking for the VGPR form of
+# every MFMA keeps them out of AGPRs (no accvgpr moves in the loop).
+SOURCE_FLAGS = {"fsa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "fsa_fwd_e4m3.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 # Packed fp32 VALU instructions are disabled on purpose (the target feature is
 # switched off for the device pass; the host pass ignores it with a warning).

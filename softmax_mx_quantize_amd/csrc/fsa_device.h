@@ -111,10 +111,13 @@ template <bool CLAMP> struct Pack32<FMT_E4M3, CLAMP> {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float sc = i < 4 ? s_lo : s_hi;
-      v2s lo = {0, 0};
+      // each conversion writes one 16-bit half and keeps the other; the
+      // starting value is overwritten in full, so any register will do (one
+      // whose value dies here costs no copy)
+      v2s lo = __builtin_bit_cast(v2s, y[4 * i + 1]);
       lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, sat(y[4 * i + 0]), sat(y[4 * i + 1]), sc, false);
       lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, sat(y[4 * i + 2]), sat(y[4 * i + 3]), sc, true);
-      w[i] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+      w[i] = __builtin_bit_cast(uint32_t, lo);
     }
   }
 };

@@ -57,8 +57,35 @@
 #include "fsa_internal.h"
 
 // Waves per workgroup for each element format (overridable at build time).
+#ifndef FSA_PIPE
+#define FSA_PIPE -1
+#endif
+#ifndef FSA_PREFETCH
+#define FSA_PREFETCH -1
+#endif
+#ifndef FSA_PPSPLIT
+#define FSA_PPSPLIT 0
+#endif
+#ifndef FSA_XB
+#define FSA_XB 1
+#endif
+#ifndef FSA_PP
+#define FSA_PP 1
+#endif
+#ifndef FSA_HINT
+#define FSA_HINT 1
+#endif
+#ifndef FSA_NSUB6
+#define FSA_NSUB6 2
+#endif
+#ifndef FSA_NSUB4
+#define FSA_NSUB4 2
+#endif
+#ifndef FSA_NSUB8
+#define FSA_NSUB8 2
+#endif
 #ifndef FSA_NW8
-#define FSA_NW8 4
+#define FSA_NW8 8
 #endif
 #ifndef FSA_NW6
 #define FSA_NW6 8
@@ -78,6 +105,13 @@ __device__ v4f mfma_scale_v6(v6i a, v6i b, v4f c, int cbsz, int blgp, int opsel_
 __device__ v4f mfma_scale_v4(v4i a, v4i b, v4f c, int cbsz, int blgp, int opsel_a, int sa,
                              int opsel_b, int sb)
     __asm("llvm.amdgcn.mfma.scale.f32.16x16x128.f8f6f4.v4i32.v4i32");
+// Mixed widths: an FP4 A operand with an FP8 or FP6 B operand.
+__device__ v4f mfma_scale_v4_v8(v4i a, v8i b, v4f c, int cbsz, int blgp, int opsel_a, int sa,
+                                int opsel_b, int sb)
+    __asm("llvm.amdgcn.mfma.scale.f32.16x16x128.f8f6f4.v4i32.v8i32");
+__device__ v4f mfma_scale_v4_v6(v4i a, v6i b, v4f c, int cbsz, int blgp, int opsel_a, int sa,
+                                int opsel_b, int sb)
+    __asm("llvm.amdgcn.mfma.scale.f32.16x16x128.f8f6f4.v4i32.v6i32");
 
 namespace {
 
@@ -240,6 +274,25 @@ __device__ __forceinline__ v4f mfma_sel(const opv<F>& a, const opv<F>& b, const 
   }
 }
 
+// Row sums l += 1 P~^T on the matrix core: the all-ones A operand is held
+// in FP4 (E2M1 1.0 = 0x2 in every nibble, 4 registers) whatever the format
+// of P~; FP4 ones times P~ in its own format is the same exact sum.
+__device__ __forceinline__ v4i ones_fp4() {
+  v4i o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = 0x22222222;
+  return o;
+}
+template <int F>
+__device__ __forceinline__ v4f row_sum(const v4i& ones, const opv<F>& p, const v4f& c, int sp) {
+  if constexpr (Fmt<F>::bits == 8)
+    return mfma_scale_v4_v8(ones, p, c, Fmt<FMT_E2M1>::mfma, Fmt<F>::mfma, 0, 127, 0, sp);
+  else if constexpr (Fmt<F>::bits == 6)
+    return mfma_scale_v4_v6(ones, p, c, Fmt<FMT_E2M1>::mfma, Fmt<F>::mfma, 0, 127, 0, sp);
+  else
+    return mfma_scale_v4(ones, p, c, Fmt<FMT_E2M1>::mfma, Fmt<F>::mfma, 0, 127, 0, sp);
+}
+
 template <int F>
 __device__ __forceinline__ opv<F> ones_operand() {
   constexpr int BITS = Fmt<F>::bits;
@@ -262,6 +315,25 @@ __device__ __forceinline__ opv<F> ones_operand() {
   return o;
 }
 
+// Cross-lane exchanges on the vector unit (v_permlane16/32_swap; the swap
+// trades the odd 16-lane rows of its first operand with the even rows of its
+// second, resp. the upper 32 lanes of the first with the lower 32 of the
+// second), so that the epilogue waits on no LDS round trip.
+// max(x, x of lane ^ 16):
+__device__ __forceinline__ uint32_t max_xor16(uint32_t x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return max((uint32_t)p[0], (uint32_t)p[1]);
+}
+// x of lane ^ 48 for lane groups 1 and 2 (rows 1 and 2 trade places); the
+// result is unspecified in groups 0 and 3.
+__device__ __forceinline__ int swap_rows12(int x, int g) {
+  const auto h = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  // h[0] rows: x0 x1 x0 x1; h[1] rows: x2 x3 x2 x3
+  const auto q = __builtin_amdgcn_permlane16_swap((uint32_t)h[0], (uint32_t)h[1], false, false);
+  // q[0] rows: x0 x2 x0 x2; q[1] rows: x1 x3 x1 x3
+  return (int)(g == 1 ? q[0] : q[1]);
+}
+
 // Scale operand of the P~ B operand.  FP6/FP4: the lane's own block.  FP8:
 // lane group c supplies the scale of key block c; blocks 0/2 are the low/high
 // halves held by groups 0-1, blocks 1/3 those held by groups 2-3, so groups
@@ -270,7 +342,7 @@ template <int BITS>
 __device__ __forceinline__ int p_scale(int s_lo, int s_hi, int g) {
   if (BITS != 8) return s_lo;
   const int give = g >= 2 ? s_lo : s_hi;            // what the partner needs
-  const int got = __shfl_xor(give, 48);
+  const int got = swap_rows12(give, g);
   const int own = g < 2 ? s_lo : s_hi;
   const bool cross = (g == 1) | (g == 2);
   return cross ? got : own;
@@ -345,6 +417,19 @@ __device__ __forceinline__ opv<F> q_operand(const uint16_t* row, float mult, int
   return o;
 }
 
+// Scheduling hint for one straight-line phase of the pipelined loop: NM
+// times {one MFMA, up to ND LDS reads, up to NV vector instructions}, so that
+// the vector work of one wave issues in the shadow of its own MFMAs.
+template <int NM, int ND, int NV>
+__device__ __forceinline__ void interleave_hint() {
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, ND, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+  }
+}
+
 __device__ __forceinline__ void dma16(const void* g, uint8_t* lds_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);
 }
@@ -388,29 +473,48 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   constexpr int V_BYTES = D * RS;
   constexpr int KS_BYTES = KT * NDB;
   constexpr int VS_BYTES = D * 4;
-  constexpr int STAGE = K_BYTES + V_BYTES + KS_BYTES + VS_BYTES;
+  constexpr int KSTAGE = K_BYTES + KS_BYTES;   // K^ tile and its scales
+  constexpr int VSTAGE = V_BYTES + VS_BYTES;   // V^T tile and its scales
 
-  // One wave per SIMD (4 waves): software-pipelined tile loop on a 4-stage
-  // ring; two waves per SIMD (8 waves): tile after tile on a 3-stage ring.
+  // One wave per SIMD (4 waves): software-pipelined tile loop on 4-stage
+  // rings; two waves per SIMD (8 waves): tile after tile on 3-stage rings.
   constexpr bool SWP = NWAVES == 4;
+  // Eight waves of one subtile each: ping-pong between the two halves of
+  // the workgroup (two subtiles per wave leave too few registers for it).
+  constexpr bool PP = NWAVES == 8 && NSUB == 1 && FSA_PP;
   constexpr int NSTAGE = SWP ? 4 : 3;       // LDS ring depth
-  // One LDS object per stage, always addressed through a compile-time stage
-  // index: the compiler then sees that reads of one stage cannot alias the
-  // DMA in flight into another, and does not wait for that DMA first.
-  __shared__ __align__(16) uint8_t lds0[STAGE];
-  __shared__ __align__(16) uint8_t lds1[STAGE];
-  __shared__ __align__(16) uint8_t lds2[STAGE];
-  __shared__ __align__(16) uint8_t lds3[NSTAGE > 3 ? STAGE : 16];
-  auto stage = [&](auto st_tag) __attribute__((always_inline)) -> uint8_t* {
-    constexpr int ST = decltype(st_tag)::value;
-    if constexpr (ST == 0) return lds0;
-    else if constexpr (ST == 1) return lds1;
-    else if constexpr (ST == 2) return lds2;
-    else return lds3;
+  // K^ and V^T have rings of their own (the pipelined loop reads K^ one
+  // tile ahead of V^T).  One LDS object per stage, always addressed through
+  // a compile-time stage index: the compiler then sees that reads of one
+  // stage cannot alias the DMA in flight into another, and does not wait
+  // for that DMA first.
+  __shared__ __align__(16) uint8_t kl0[KSTAGE];
+  __shared__ __align__(16) uint8_t kl1[KSTAGE];
+  __shared__ __align__(16) uint8_t kl2[KSTAGE];
+  __shared__ __align__(16) uint8_t kl3[NSTAGE > 3 ? KSTAGE : 16];
+  __shared__ __align__(16) uint8_t vl0[VSTAGE];
+  __shared__ __align__(16) uint8_t vl1[VSTAGE];
+  __shared__ __align__(16) uint8_t vl2[VSTAGE];
+  __shared__ __align__(16) uint8_t vl3[NSTAGE > 3 ? VSTAGE : 16];
+  auto kstage = [&](auto st_tag) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int ST = decltype(st_tag)::value % NSTAGE;
+    if constexpr (ST == 0) return kl0;
+    else if constexpr (ST == 1) return kl1;
+    else if constexpr (ST == 2) return kl2;
+    else return kl3;
+  };
+  auto vstage = [&](auto st_tag) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int ST = decltype(st_tag)::value % NSTAGE;
+    if constexpr (ST == 0) return vl0;
+    else if constexpr (ST == 1) return vl1;
+    else if constexpr (ST == 2) return vl2;
+    else return vl3;
   };
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // wave-uniform by construction; made scalar so that everything derived
+  // from it (LDS DMA targets in particular) stays in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 4;
   const int r = lane & 15;
@@ -456,7 +560,9 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   // costs no vector instructions.
   constexpr int NK_DMA = KT * NCH / 64 / NWAVES;      // per wave, per tile
   constexpr int NV_DMA = D * NCH / 64 / NWAVES;
-  constexpr int NKS = KS_BYTES / 256;
+  constexpr int NKS = KS_BYTES / 256;                 // scale dwords per lane and tile
+  constexpr int NVS = VS_BYTES / 256;
+  static_assert(NKS <= NWAVES && NVS <= NWAVES, "one scale dword per wave");
   const __amdgpu_buffer_rsrc_t k_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)kc, (short)0, a.sk_alloc * RB, 0x00020000);
   const __amdgpu_buffer_rsrc_t v_rsrc =
@@ -465,48 +571,77 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
       __builtin_amdgcn_make_buffer_rsrc((void*)ks, (short)0, a.sk_alloc * NDB, 0x00020000);
   const __amdgpu_buffer_rsrc_t vs_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)vs, (short)0, D * vs_row, 0x00020000);
-  int k_voff[NK_DMA], v_voff[NV_DMA];
+  // The rows a wave fills are 8 * NWAVES apart; when that is a multiple of
+  // 64 their swizzles agree, so one lane offset serves them all and the row
+  // step goes into the scalar offset (fewer vector registers held across the
+  // sweep).  Otherwise each row keeps its own lane offset.
+  constexpr bool ONE_VOFF = (8 * NWAVES) % 64 == 0;
+  constexpr int NKV = ONE_VOFF ? 1 : NK_DMA;
+  constexpr int NVV = ONE_VOFF ? 1 : NV_DMA;
+  // With one lane offset per operand the offsets are recomputed at every
+  // issue from an opaque lane index (a few vector instructions) instead of
+  // being held across the sweep, where the register allocator would rather
+  // spill them, and reloading a spill would wait for the DMA in flight.
+  auto k_lane_off = [&](int k, int ln) __attribute__((always_inline)) {
+    const int row = (wave + NWAVES * k) * 8 + (ln >> 3);
+    const int c = (ln & 7) ^ swz_k<F, D>(row);
+    return row * RB + (c < KCH_VALID ? c : 0) * 16;
+  };
+  auto v_lane_off = [&](int k, int ln) __attribute__((always_inline)) {
+    const int row = (wave + NWAVES * k) * 8 + (ln >> 3);
+    const int c = (ln & 7) ^ swz_v(row);
+    return row * (int)v_row + (c < VCH_VALID ? c : 0) * 16;
+  };
+  auto opaque_lane = [&]() __attribute__((always_inline)) {
+    int l = lane;
+    if constexpr (ONE_VOFF) asm volatile("" : "+v"(l));
+    return l;
+  };
+  int k_voff[NKV], v_voff[NVV];
 #pragma unroll
-  for (int k = 0; k < NK_DMA; ++k) {
-    const int row = (wave + NWAVES * k) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz_k<F, D>(row);
-    k_voff[k] = row * RB + (c < KCH_VALID ? c : 0) * 16;
-  }
+  for (int k = 0; k < NKV; ++k) k_voff[k] = k_lane_off(k, lane);
 #pragma unroll
-  for (int k = 0; k < NV_DMA; ++k) {
-    const int row = (wave + NWAVES * k) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz_v(row);
-    v_voff[k] = row * (int)v_row + (c < VCH_VALID ? c : 0) * 16;
-  }
-  // scales: NKS K-scale dwords and D/64 V-scale dwords, one per wave (waves
-  // past them re-load the first K-scale dword to keep the count uniform);
-  // both are tile-ordered, 128 * D/32 and 4 * D contiguous bytes per tile
-  const bool s_is_v = wave >= NKS && wave < NKS + D / 64;
-  const int s_voff = wave < NKS ? wave * 256 + lane * 4
-                                : (s_is_v ? ((wave - NKS) * 64 + lane) * 4 : lane * 4);
-  const int s_lds = wave < NKS ? K_BYTES + V_BYTES + wave * 256
-                               : (s_is_v ? K_BYTES + V_BYTES + KS_BYTES + (wave - NKS) * 256
-                                         : K_BYTES + V_BYTES);
-  auto issue_tile = [&](int t, uint8_t* base) __attribute__((always_inline)) {
+  for (int k = 0; k < NVV; ++k) v_voff[k] = v_lane_off(k, lane);
+  // Scales are tile-ordered, 128 * D/32 (K^) and 4 * D (V^T) contiguous
+  // bytes per tile: NKS resp. NVS dwords per lane, one per wave; the other
+  // waves re-load the first dword (the same bytes to the same place) so that
+  // every wave issues the same number of loads.  The wave's part goes in
+  // the scalar offset.
+  const int s_voff = lane * 4;
+  const int ks_soff = wave < NKS ? wave * 256 : 0;
+  const int vs_soff = wave < NVS ? wave * 256 : 0;
+  const int ks_lds = K_BYTES + ks_soff;
+  const int vs_lds = V_BYTES + vs_soff;
+  auto issue_k = [&](int t, uint8_t* base) __attribute__((always_inline)) {
+    const int ln = opaque_lane();
+    const int kv0 = ONE_VOFF ? k_lane_off(0, ln) : 0;
 #pragma unroll
     for (int k = 0; k < NK_DMA; ++k)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (lds_void*)(base + (wave + NWAVES * k) * 1024),
-                                               16, k_voff[k], t * KT * RB, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          k_rsrc, (lds_void*)(base + (wave + NWAVES * k) * 1024), 16, ONE_VOFF ? kv0 : k_voff[k],
+          t * KT * RB + (ONE_VOFF ? k * NWAVES * 8 * RB : 0), 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ks_rsrc, (lds_void*)(base + ks_lds), 4,
+                                             ONE_VOFF ? ln * 4 : s_voff, t * KS_BYTES + ks_soff, 0, 0);
+  };
+  auto issue_v = [&](int t, uint8_t* base) __attribute__((always_inline)) {
+    const int ln = opaque_lane();
+    const int vv0 = ONE_VOFF ? v_lane_off(0, ln) : 0;
 #pragma unroll
     for (int k = 0; k < NV_DMA; ++k)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc, (lds_void*)(base + K_BYTES + (wave + NWAVES * k) * 1024),
-                                               16, v_voff[k], t * VRB, 0, 0);
-    if (s_is_v)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vs_rsrc, (lds_void*)(base + s_lds), 4, s_voff,
-                                               t * VS_BYTES, 0, 0);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ks_rsrc, (lds_void*)(base + s_lds), 4, s_voff,
-                                               t * KT * NDB, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          v_rsrc, (lds_void*)(base + (wave + NWAVES * k) * 1024), 16, ONE_VOFF ? vv0 : v_voff[k],
+          t * VRB + (ONE_VOFF ? k * NWAVES * 8 * (int)v_row : 0), 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vs_rsrc, (lds_void*)(base + vs_lds), 4,
+                                             ONE_VOFF ? ln * 4 : s_voff, t * VS_BYTES + vs_soff, 0, 0);
   };
-  // DMA instructions each wave issues per tile
-  constexpr int DMA_PER_TILE = NK_DMA + NV_DMA + 1;
+  // DMA instructions each wave issues per K^ tile and per V^T tile
+  constexpr int DMA_K = NK_DMA + 1;
+  constexpr int DMA_V = NV_DMA + 1;
 
-  if (n_tiles > 0) issue_tile(0, lds0);
+  if (n_tiles > 0) {
+    issue_k(0, kl0);
+    issue_v(0, vl0);
+  }
 
   // ---- Q^ fragments (B operand of the score product), one per subtile
   opv<F> qf[NSUB];
@@ -524,8 +659,8 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   // 4g+i lands on the lane's operand position 4j+i.
   auto k_frag = [&](int j, int& sc) __attribute__((always_inline)) -> opv<F> {
     const int kk = kpos<F>(r >> 2, 4 * j + (r & 3));
-    const uint8_t* base = lds0;
-    sc = g < NDB ? (int)base[K_BYTES + V_BYTES + (r * NDB + g) * 8 + j] : 127;
+    const uint8_t* base = kl0;
+    sc = g < NDB ? (int)base[K_BYTES + (r * NDB + g) * 8 + j] : 127;
     return lds_operand<F>(base + kk * RS, swz_k<F, D>(kk), g, D);
   };
 
@@ -535,8 +670,20 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   float mg[NSUB];
   wait_dma();
   __syncthreads();
-  if (n_tiles > 1) issue_tile(1, lds1);
-  if (!SWP && n_tiles > 2) issue_tile(2, lds2);
+  // The rings fill ahead of the sweep.  The pipelined loop reads K^ one
+  // tile ahead: K^ tiles 1 and 2 and V^T tile 1 are issued here (clamped to
+  // the last tile, which then lands again in a stage nobody reads, so the
+  // load count stays uniform); the tile-after-tile loop takes tiles 1 and 2.
+  if constexpr (SWP) {
+    issue_k(min(1, n_tiles - 1), kl1);
+    issue_k(min(2, n_tiles - 1), kl2);
+    issue_v(min(1, n_tiles - 1), vl1);
+  } else if constexpr (PP) {
+    issue_k(min(1, n_tiles - 1), kl1);
+  } else {
+    if (n_tiles > 1) { issue_k(1, kl1); issue_v(1, vl1); }
+    if (n_tiles > 2) { issue_k(2, kl2); issue_v(2, vl2); }
+  }
   {
     v4f acc[NSUB][8];
 #pragma unroll
@@ -591,18 +738,31 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   v4f O[NSUB][NDT];
   v4f L[NSUB];
   int kmax[NSUB];
-  v4f minit[NSUB];
+  float c0s[NSUB];
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
     L[s] = zero4;
     kmax[s] = -1000000;
     // accumulator start: fp32(2^23 (127 + R) - 2^23 m~), one rounding
-    const float c0 = __builtin_fmaf(-8388608.0f, mg[s], 8388608.0f * (127 + REF));
-    minit[s] = v4f{c0, c0, c0, c0};
+    c0s[s] = __builtin_fmaf(-8388608.0f, mg[s], 8388608.0f * (127 + REF));
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) O[s][dt] = zero4;
   }
-  const opv<F> ones = ones_operand<F>();
+  // The score products start from the 4-register quad {c0, c0, c0, c0}.
+  // Where registers are tightest (FP8, two subtiles) the quads are rebuilt
+  // at every tile (4 moves each) from the one value kept across the sweep.
+  constexpr bool QUAD_PER_TILE = BITS == 8 && NSUB >= 2;
+  v4f minit[NSUB];
+  auto refresh_start = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      float c = c0s[s];
+      if constexpr (QUAD_PER_TILE) asm volatile("" : "+v"(c));
+      minit[s] = v4f{c, c, c, c};
+    }
+  };
+  refresh_start();
+  const v4i ones = ones_fp4();
 
   // Lane-constant LDS byte offsets.  For slice j of the score product the
   // lane's K^ row is kk0 + 4j (+48 for the FP8 high half), and its swizzle
@@ -618,15 +778,15 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
     if (BITS == 8) lo = i == 0 ? 16 * g : 64 + 16 * g;
     else if (BITS == 6) lo = 24 * g + 8 * i;
     else lo = 16 * g;
-    k_off[i] = kk0 * RS + 16 * ((lo >> 4) ^ ksw) + (lo & 15);
-    v_off[i] = K_BYTES + r * RS + 16 * ((lo >> 4) ^ vsw) + (lo & 15);
+    k_off[i] = kk0 * RS + 16 * ((lo >> 4) ^ ksw) + (lo & 15);      // in a K^ stage
+    v_off[i] = r * RS + 16 * ((lo >> 4) ^ vsw) + (lo & 15);         // in a V^T stage
   }
   // Scale bytes of the lane's 8 score products (slice j) and 8 P V products
   // (output tile dt), tile-ordered so that one read fetches all of them; the
   // MFMA selects byte j & 3 / dt & 3 of a dword.  Lanes past D (D = 64)
   // multiply zeros and take scale 1.
-  const int ks_off = K_BYTES + V_BYTES + (r * NDB + (g < NDB ? g : 0)) * 8;
-  const int vs_off = K_BYTES + V_BYTES + KS_BYTES + (r * 4 + g) * NDT;
+  const int ks_off = K_BYTES + (r * NDB + (g < NDB ? g : 0)) * 8;
+  const int vs_off = V_BYTES + (r * 4 + g) * NDT;
   auto k_scales = [&](const uint8_t* base) __attribute__((always_inline)) -> uint2 {
     const uint2 v = *reinterpret_cast<const uint2*>(base + ks_off);
     return g < NDB ? v : make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
@@ -635,6 +795,14 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
     if constexpr (NDT == 8) return *reinterpret_cast<const uint2*>(base + vs_off);
     else return make_uint2(*reinterpret_cast<const uint32_t*>(base + vs_off), 0u);
   };
+  // Read every fragment of a phase before its first product (one subtile
+  // per wave leaves the registers for it); otherwise one slice at a time.
+  constexpr bool PREFETCH = FSA_PREFETCH >= 0 ? FSA_PREFETCH != 0 : NSUB == 1;
+  // Otherwise, fragments in flight per operand stream (0: the compiler's
+  // choice, with the FP6 slice fence).  FP8 reads three ahead in a fixed
+  // order (measured best; left free, the compiler hoists every read of a
+  // phase and runs out of registers).
+  constexpr int PIPE = FSA_PIPE >= 0 ? FSA_PIPE : (BITS == 8 ? 3 : 0);
   const bool k_live = 32 * g < D;               // FP6/FP4 lane groups past D
   const bool k_hi = 64 + 16 * g < D;            // FP8 high half present
 
@@ -663,6 +831,12 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
     }
     return o;
   };
+  // K^ fragment of 16-key slice j of the tile in stage `base`
+  auto kfrag = [&](const uint8_t* base, int j) __attribute__((always_inline)) -> opv<F> {
+    const int jrow = 4 * j + ((BITS == 8 && j >= 4) ? 48 : 0);
+    return frag(base, k_off, jrow * RS, BITS == 8 ? 16 * g < D : k_live, BITS == 8 ? k_hi : false);
+  };
+
 
   // FP6 fragments arrive in three 8-byte pieces per lane; left free, the
   // scheduler hoists them for many slices at once and pays in register
@@ -672,10 +846,9 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
     if constexpr (BITS == 6) __builtin_amdgcn_sched_barrier(0);
   };
 
-  // The three steps of one key tile, on state shared across phases.  The
-  // pipelined schedule keeps two score buffers (tiles of even and odd index).
+  // The steps of one key tile, on state shared across phases: the score
+  // accumulators of each subtile, and P~ of each subtile in operand form.
   v4f acc[NSUB][8];
-  v4f acc2[NSUB][8];
   opv<F> pw[NSUB];
   int psc[NSUB];
 
@@ -685,6 +858,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   auto qk_into = [&](v4f (&acc)[NSUB][8], const uint8_t* base, int key0, auto masked_tag)
                      __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
+    if constexpr (QUAD_PER_TILE) refresh_start();
     if constexpr (MASKED) {
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) {
@@ -692,8 +866,67 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
         const int lim = CAUSAL ? min(S, q + 1) : S;     // keys [0, lim) visible
 #pragma unroll
         for (int p = 0; p < 32; ++p)
-          acc[s][p >> 2][p & 3] = key0 + kpos<F>(g, p) < lim ? minit[s][0] : -INFINITY;
+          acc[s][p >> 2][p & 3] = key0 + kpos<F>(g, p) < lim ? c0s[s] : -INFINITY;
       }
+    }
+    const uint2 ksc = k_scales(base);
+    if constexpr (PREFETCH) {
+      // all eight K^ fragments in flight before the first product
+      opv<F> kfs[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int jrow = 4 * j + ((BITS == 8 && j >= 4) ? 48 : 0);
+        kfs[j] = frag(base, k_off, jrow * RS, BITS == 8 ? 16 * g < D : k_live, BITS == 8 ? k_hi : false);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s)
+          acc[s][j] = mfma_sel<F>(kfs[j], qf[s], MASKED ? acc[s][j] : minit[s],
+                                  (int)(j < 4 ? ksc.x : ksc.y), j, qsc[s]);
+    } else if constexpr (PIPE > 0) {
+      // PIPE fragments in flight: the read of slice j+PIPE issues right
+      // after the products of slice j, in a fixed order
+      opv<F> kfs[PIPE > 0 ? PIPE : 1];
+#pragma unroll
+      for (int j = 0; j < PIPE; ++j) kfs[j] = kfrag(base, j);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s)
+          acc[s][j] = mfma_sel<F>(kfs[j % PIPE], qf[s], MASKED ? acc[s][j] : minit[s],
+                                  (int)(j < 4 ? ksc.x : ksc.y), j, qsc[s]);
+        if (j + PIPE < 8) kfs[j % PIPE] = kfrag(base, j + PIPE);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int jrow = 4 * j + ((BITS == 8 && j >= 4) ? 48 : 0);
+        const opv<F> kf = frag(base, k_off, jrow * RS, BITS == 8 ? 16 * g < D : k_live,
+                               BITS == 8 ? k_hi : false);
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s)
+          acc[s][j] = mfma_sel<F>(kf, qf[s], MASKED ? acc[s][j] : minit[s],
+                                  (int)(j < 4 ? ksc.x : ksc.y), j, qsc[s]);
+        slice_fence();
+      }
+    }
+  };
+
+  // The same for subtile S alone (the pipelined loop computes the two
+  // subtiles in different phases).
+  auto qk_sub = [&](v4f (&A)[8], const uint8_t* base, int key0, auto s_tag, auto masked_tag)
+                    __attribute__((always_inline)) {
+    constexpr int SS = decltype(s_tag)::value;
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    if constexpr (MASKED) {
+      const int q = q_wave + 16 * SS + r;
+      const int lim = CAUSAL ? min(S, q + 1) : S;
+#pragma unroll
+      for (int p = 0; p < 32; ++p)
+        A[p >> 2][p & 3] = key0 + kpos<F>(g, p) < lim ? c0s[SS] : -INFINITY;
     }
     const uint2 ksc = k_scales(base);
 #pragma unroll
@@ -701,10 +934,8 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
       const int jrow = 4 * j + ((BITS == 8 && j >= 4) ? 48 : 0);
       const opv<F> kf = frag(base, k_off, jrow * RS, BITS == 8 ? 16 * g < D : k_live,
                              BITS == 8 ? k_hi : false);
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s)
-        acc[s][j] = mfma_sel<F>(kf, qf[s], MASKED ? acc[s][j] : minit[s],
-                                (int)(j < 4 ? ksc.x : ksc.y), j, qsc[s]);
+      A[j] = mfma_sel<F>(kf, qf[SS], MASKED ? A[j] : minit[SS], (int)(j < 4 ? ksc.x : ksc.y), j,
+                         qsc[SS]);
       slice_fence();
     }
   };
@@ -737,8 +968,8 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
       m0 = max(m0, u(15));
       m1 = max(m1, u(31));
       if (BITS == 8) {
-        m0 = max(m0, (uint32_t)__shfl_xor((int)m0, 16));
-        m1 = max(m1, (uint32_t)__shfl_xor((int)m1, 16));
+        m0 = max_xor16(m0);
+        m1 = max_xor16(m1);
       } else {
         m0 = max(m0, m1);
         m1 = m0;
@@ -774,22 +1005,58 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
       O[s][dt] = mfma_sel<F>(vf, pw[s], O[s][dt], (int)(dt < 4 ? vsc.x : vsc.y), dt, psc[s]);
       slice_fence();
     }
-    L[s] = mfma<F>(ones, pw[s], L[s], 127, psc[s]);
+    L[s] = row_sum<F>(ones, pw[s], L[s], psc[s]);
   };
 
+  // V^T fragments of the tile in stage `base`, read ahead of the epilogue
+  // so that their LDS latency hides under it.
+  opv<F> vfs[PREFETCH ? NDT : 1];
+  uint2 vsc_pf;
+  auto pv_load = [&](const uint8_t* base) __attribute__((always_inline)) {
+    if constexpr (PREFETCH) {
+      vsc_pf = v_scales(base);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) vfs[dt] = frag(base, v_off, 16 * dt * RS, true, true);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   // P V and the row sums on the matrix cores, V^T tile in stage `base`.
   auto pv_step = [&](const uint8_t* base) __attribute__((always_inline)) {
+    if constexpr (PREFETCH) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s)
+          O[s][dt] = mfma_sel<F>(vfs[dt], pw[s], O[s][dt], (int)(dt < 4 ? vsc_pf.x : vsc_pf.y), dt, psc[s]);
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) L[s] = row_sum<F>(ones, pw[s], L[s], psc[s]);
+      return;
+    }
     const uint2 vsc = v_scales(base);
+    if constexpr (PIPE > 0) {
+      opv<F> vfp[PIPE > 0 ? PIPE : 1];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const opv<F> vf = frag(base, v_off, 16 * dt * RS, true, true);
+      for (int dt = 0; dt < PIPE && dt < NDT; ++dt) vfp[dt] = frag(base, v_off, 16 * dt * RS, true, true);
 #pragma unroll
-      for (int s = 0; s < NSUB; ++s)
-        O[s][dt] = mfma_sel<F>(vf, pw[s], O[s][dt], (int)(dt < 4 ? vsc.x : vsc.y), dt, psc[s]);
-      slice_fence();
+      for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s)
+          O[s][dt] = mfma_sel<F>(vfp[dt % PIPE], pw[s], O[s][dt], (int)(dt < 4 ? vsc.x : vsc.y), dt, psc[s]);
+        if (dt + PIPE < NDT) vfp[dt % PIPE] = frag(base, v_off, 16 * (dt + PIPE) * RS, true, true);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const opv<F> vf = frag(base, v_off, 16 * dt * RS, true, true);
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s)
+          O[s][dt] = mfma_sel<F>(vf, pw[s], O[s][dt], (int)(dt < 4 ? vsc.x : vsc.y), dt, psc[s]);
+        slice_fence();
+      }
     }
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) L[s] = mfma<F>(ones, pw[s], L[s], 127, psc[s]);
+    for (int s = 0; s < NSUB; ++s) L[s] = row_sum<F>(ones, pw[s], L[s], psc[s]);
   };
 
   // tiles [0, n_clean) need no masking for any row of this wave
@@ -815,79 +1082,185 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
 
   if constexpr (SWP) {
     // One wave per SIMD, software-pipelined so that every stretch of matrix
-    // work has independent vector work beside it (one wave cannot overlap
-    // them otherwise: an MFMA blocks issue until the matrix core takes it):
-    //   G1  scores of tile t            | epilogue of tile t-1, subtile 1
-    //   G2  P V of tile t-1, subtile 1  | epilogue of tile t, subtile 0
-    //   G3  P V of tile t, subtile 0
-    // Score buffers alternate by tile parity.  Ring of 4 stages: tile t+2 is
-    // issued at the start of step t into the stage of tile t-2, whose last
-    // reader (G2 of step t-1) finished before the barrier that ended step
-    // t-1; tile t+1 must have landed by the barrier that ends step t.
-    // Steps after the first, clean or masked; each of G1 and G2 is one basic
-    // block so that the scheduler can interleave its two halves.  The DMA of
-    // step t fetches tile min(t+2, n-1): past the end it re-fetches the last
-    // tile into a stage nobody reads any more, which keeps the step
-    // branch-free; everything in flight is drained before the kernel ends.
-    auto swp_step = [&](int t, auto st_tag, auto masked_tag) __attribute__((always_inline)) {
-      constexpr int ST = decltype(st_tag)::value;
-      v4f (&X)[NSUB][8] = (ST & 1) ? acc2 : acc;       // tile t
-      v4f (&Y)[NSUB][8] = (ST & 1) ? acc : acc2;       // tile t-1
-      issue_tile(min(t + 2, n_tiles - 1), stage(std::integral_constant<int, (ST + 2) & 3>{}));
-      qk_into(X, stage(st_tag), t * KT, masked_tag);
-      epi_sub(Y, 1);
+    // work has independent vector work beside it (one wave overlaps them only
+    // within its own instruction stream), with the score accumulators of one
+    // subtile written while those of the other are read:
+    //   phase 1: scores of tile t, subtile 1 + P V of tile t-1, subtile 1
+    //            | epilogue of tile t, subtile 0
+    //   phase 2: scores of tile t+1, subtile 0 + P V of tile t, subtile 0
+    //            | epilogue of tile t, subtile 1
+    // K^ is read one tile ahead of V^T.  Step t issues K^ tile t+3 into the
+    // stage of tile t-1 and V^T tile t+2 into that of tile t-2, both last
+    // read in step t-1, before the barrier that ended it; the loads of step
+    // t-1 (K^ t+2, V^T t+1) must have landed by the barrier that ends step t.
+    // Past the end the loads re-fetch the last tile into a stage nobody reads
+    // any more, which keeps the count uniform; everything in flight is
+    // drained before the kernel ends.
+    //
+    // A clean step (every key of both tiles visible to every row of the
+    // wave, a previous and a next tile present) is one straight-line block
+    // per phase with an interleaving hint; the generic step masks both score
+    // products and branches on the neighbours.
+    auto step = [&](int t, auto ph, auto clean_tag, bool has_prev, bool has_next)
+                    __attribute__((always_inline)) {
+      constexpr int P = decltype(ph)::value;
+      constexpr bool CLEAN = decltype(clean_tag)::value;
+      using IP = std::integral_constant<int, P>;
+      using IP1 = std::integral_constant<int, (P + 1) & 3>;
+      using IP2 = std::integral_constant<int, (P + 2) & 3>;
+      using IP3 = std::integral_constant<int, (P + 3) & 3>;
+      using MT = std::integral_constant<bool, !CLEAN>;
+      issue_k(min(t + 3, n_tiles - 1), kstage(IP3{}));
+      issue_v(min(t + 2, n_tiles - 1), vstage(IP2{}));
+      qk_sub(acc[1], kstage(IP{}), t * KT, I1{}, MT{});
+      if (CLEAN || has_prev) pv_sub(vstage(IP3{}), 1);
+      epi_sub(acc, 0);
+      if constexpr (CLEAN && FSA_HINT) interleave_hint<17, 2, 6>();
       __builtin_amdgcn_sched_barrier(0);
-      pv_sub(stage(std::integral_constant<int, (ST + 3) & 3>{}), 1);
-      epi_sub(X, 0);
+      if (CLEAN || has_next) qk_sub(acc[0], kstage(IP1{}), (t + 1) * KT, I0{}, MT{});
+      pv_sub(vstage(IP{}), 0);
+      epi_sub(acc, 1);
+      if constexpr (CLEAN && FSA_HINT) interleave_hint<17, 2, 6>();
       __builtin_amdgcn_sched_barrier(0);
-      pv_sub(stage(st_tag), 0);
-      wait_dma_keep<DMA_PER_TILE>();
+      wait_dma_keep<DMA_K + DMA_V>();
       ring_barrier();
     };
-    // step 0: no previous tile
-    issue_tile(min(2, n_tiles - 1), stage(I2{}));
-    qk_any_into(acc, stage(I0{}), 0);
-    epi_sub(acc, 0);
-    pv_sub(stage(I0{}), 0);
-    wait_dma_keep<DMA_PER_TILE>();
-    ring_barrier();
-    int t = 1;
-    for (; t + 3 < n_clean; t += 4) {
-      swp_step(t, I1{}, std::false_type{});
-      swp_step(t + 1, I2{}, std::false_type{});
-      swp_step(t + 2, I3{}, std::false_type{});
-      swp_step(t + 3, I0{}, std::false_type{});
-    }
-    for (; t < n_tiles; ++t) {
-      const bool clean = t < n_clean;
+    auto step_any = [&](int t) __attribute__((always_inline)) {
+      const bool has_prev = t > 0, has_next = t + 1 < n_tiles;
       switch (t & 3) {
-        case 0: if (clean) swp_step(t, I0{}, std::false_type{}); else swp_step(t, I0{}, std::true_type{}); break;
-        case 1: if (clean) swp_step(t, I1{}, std::false_type{}); else swp_step(t, I1{}, std::true_type{}); break;
-        case 2: if (clean) swp_step(t, I2{}, std::false_type{}); else swp_step(t, I2{}, std::true_type{}); break;
-        default: if (clean) swp_step(t, I3{}, std::false_type{}); else swp_step(t, I3{}, std::true_type{}); break;
+        case 0: step(t, I0{}, std::false_type{}, has_prev, has_next); break;
+        case 1: step(t, I1{}, std::false_type{}, has_prev, has_next); break;
+        case 2: step(t, I2{}, std::false_type{}, has_prev, has_next); break;
+        default: step(t, I3{}, std::false_type{}, has_prev, has_next); break;
       }
+    };
+    // scores of tile 0, subtile 0; K^ tile 1 must land before step 0 reads it
+    qk_sub(acc[0], kl0, 0, I0{}, std::true_type{});
+    wait_dma_keep<DMA_K + DMA_V>();
+    ring_barrier();
+    step_any(0);
+    int t = 1;
+    // steps t..t+3 clean: tiles up to t+4 unmasked for every row of the wave
+    for (; t + 4 < n_clean; t += 4) {
+      step(t, I1{}, std::true_type{}, true, true);
+      step(t + 1, I2{}, std::true_type{}, true, true);
+      step(t + 2, I3{}, std::true_type{}, true, true);
+      step(t + 3, I0{}, std::true_type{}, true, true);
     }
-    // drain: subtile 1 of the last tile
+    for (; t < n_tiles; ++t) step_any(t);
+    // drain: P V of the last tile, subtile 1
     switch ((n_tiles - 1) & 3) {
-      case 0: epi_sub(acc, 1); pv_sub(stage(I0{}), 1); break;
-      case 1: epi_sub(acc2, 1); pv_sub(stage(I1{}), 1); break;
-      case 2: epi_sub(acc, 1); pv_sub(stage(I2{}), 1); break;
-      default: epi_sub(acc2, 1); pv_sub(stage(I3{}), 1); break;
+      case 0: pv_sub(vstage(I0{}), 1); break;
+      case 1: pv_sub(vstage(I1{}), 1); break;
+      case 2: pv_sub(vstage(I2{}), 1); break;
+      default: pv_sub(vstage(I3{}), 1); break;
     }
     wait_dma();
+  } else if constexpr (PP) {
+    // Ping-pong.  Waves w and w+4 share a SIMD.  Every wave runs the same
+    // sequence of phases, a workgroup barrier after each,
+    //   matrix phase t: scores of tile t and P V of tile t-1 (MFMA),
+    //   vector phase t: epilogue of tile t (VALU),
+    // but waves 4-7 start one phase late (one extra barrier before their
+    // first phase, none after their last), so that the matrix core runs one
+    // half's products while the vector unit runs the other half's epilogue.
+    // K^ tile t sits in stage t % 3, V^T tile t-1 in stage (t-1) % 3.  A
+    // wave's matrix phase t issues its share of K^ tile t+2 (into the stage
+    // of tile t-1) and V^T tile t+1 (into that of tile t-2); every wave has
+    // finished reading those by then: the first half reads tile t-1 up to
+    // its phase 2t-1, the second half one phase later, which ends at the
+    // barrier before the first half's matrix phase t.  The first read of K^
+    // tile t+2 follows the first half's vector phase t+1, which the second
+    // half meets at the end of its matrix phase t+1: each half waits for its
+    // own loads there.
+    const bool second = FSA_PPSPLIT ? (wave & 1) != 0 : wave >= NWAVES / 2;
+    // matrix phase, clean: one stream of score and P V products; each V^T
+    // fragment is read into the registers of the K^ fragment whose product
+    // has just issued, so the reads of the P V products hide under the
+    // score products
+    auto mphase_clean = [&](const uint8_t* kb, const uint8_t* vb) __attribute__((always_inline)) {
+      const uint2 ksc = k_scales(kb);
+      const uint2 vsc = v_scales(vb);
+      opv<F> fr[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int jrow = 4 * j + ((BITS == 8 && j >= 4) ? 48 : 0);
+        fr[j] = frag(kb, k_off, jrow * RS, BITS == 8 ? 16 * g < D : k_live, BITS == 8 ? k_hi : false);
+      }
+      if (FSA_XB) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s)
+          acc[s][j] = mfma_sel<F>(fr[j], qf[s], minit[s], (int)(j < 4 ? ksc.x : ksc.y), j, qsc[s]);
+        if (j < NDT) fr[j] = frag(vb, v_off, 16 * j * RS, true, true);
+        if (FSA_XB) __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s)
+          O[s][dt] = mfma_sel<F>(fr[dt], pw[s], O[s][dt], (int)(dt < 4 ? vsc.x : vsc.y), dt, psc[s]);
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) L[s] = row_sum<F>(ones, pw[s], L[s], psc[s]);
+    };
+    auto iter = [&](int t, auto st_tag) __attribute__((always_inline)) {
+      constexpr int P = decltype(st_tag)::value;
+      const uint8_t* kb = kstage(st_tag);
+      const uint8_t* vb = vstage(std::integral_constant<int, (P + 2) % 3>{});
+      const bool more = t < n_tiles;
+      if (more) {
+        issue_k(min(t + 2, n_tiles - 1), kstage(std::integral_constant<int, (P + 2) % 3>{}));
+        issue_v(min(t + 1, n_tiles - 1), vstage(std::integral_constant<int, (P + 1) % 3>{}));
+      }
+      if (t > 0 && t < n_clean) {
+        mphase_clean(kb, vb);
+      } else {
+        if (more) qk_any(kb, t);
+        if (t > 0) {
+          pv_load(vb);
+          pv_step(vb);
+        }
+      }
+      if (second) {
+        if (more) wait_dma_keep<DMA_K + DMA_V>();
+        else wait_dma();
+      }
+      ring_barrier();
+      if (more) epi();
+      if (!second) {
+        if (more) wait_dma_keep<DMA_K + DMA_V>();
+        else wait_dma();
+      }
+      if (more || !second) ring_barrier();
+    };
+    if (second) ring_barrier();
+    for (int t = 0; t <= n_tiles; t += 3) {
+      iter(t, I0{});
+      if (t + 1 <= n_tiles) iter(t + 1, I1{});
+      if (t + 2 <= n_tiles) iter(t + 2, I2{});
+    }
   } else {
     // Tile after tile, one barrier per tile.  Tile t+1 must have landed
     // (t+2 may still be in flight); after the barrier every wave is done
-    // with the stage of tile t, which then takes tile t+3.
+    // with the stages of tile t, which then take tile t+3.
     auto step = [&](int t, auto st_tag) __attribute__((always_inline)) {
-      uint8_t* base = stage(st_tag);
-      qk_any(base, t);
+      uint8_t* kb = kstage(st_tag);
+      uint8_t* vb = vstage(st_tag);
+      qk_any(kb, t);
+      pv_load(vb);
       epi();
-      pv_step(base);
-      if (t + 2 < n_tiles) wait_dma_keep<DMA_PER_TILE>();
+      // keep the P V fragment reads below the epilogue: hoisted above it
+      // they would hold registers through it
+      if constexpr (PIPE > 0) __builtin_amdgcn_sched_barrier(0);
+      pv_step(vb);
+      if (t + 2 < n_tiles) wait_dma_keep<DMA_K + DMA_V>();
       else wait_dma();
       ring_barrier();
-      if (t + 3 < n_tiles) issue_tile(t + 3, base);
+      if (t + 3 < n_tiles) {
+        issue_k(t + 3, kb);
+        issue_v(t + 3, vb);
+      }
     };
     for (int t = 0; t < n_tiles; t += 3) {
       step(t, I0{});
@@ -996,7 +1369,7 @@ __device__ __forceinline__ void fallback_group(const AttnArgs& a, int64_t grp) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) O[s][dt] = zero4;
   }
-  const opv<F> ones = ones_operand<F>();
+  const v4i ones = ones_fp4();
 
   int n_tiles = (S + KT - 1) / KT;
   if (CAUSAL) {
@@ -1107,7 +1480,7 @@ __device__ __forceinline__ void fallback_group(const AttnArgs& a, int64_t grp) {
       for (int s = 0; s < NSUB; ++s) O[s][dt] = mfma<F>(vf, pw[s], O[s][dt], vsc, psc[s]);
     }
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) L[s] = mfma<F>(ones, pw[s], L[s], 127, psc[s]);
+    for (int s = 0; s < NSUB; ++s) L[s] = row_sum<F>(ones, pw[s], L[s], psc[s]);
   }
 
 #pragma unroll
@@ -1142,9 +1515,9 @@ __global__ void __launch_bounds__(64) fsa_fallback_kernel(AttnArgs a) {
 // fragment read from LDS for more rows; the count is capped by the 256
 // architectural VGPRs the score accumulators and the epilogue need.
 template <int F> struct Nsub;
-template <> struct Nsub<FMT_E4M3> { static constexpr int value = 2; };
-template <> struct Nsub<FMT_E2M3> { static constexpr int value = 2; };
-template <> struct Nsub<FMT_E2M1> { static constexpr int value = 2; };
+template <> struct Nsub<FMT_E4M3> { static constexpr int value = FSA_NSUB8; };
+template <> struct Nsub<FMT_E2M3> { static constexpr int value = FSA_NSUB6; };
+template <> struct Nsub<FMT_E2M1> { static constexpr int value = FSA_NSUB4; };
 // Waves per workgroup: 8 puts two waves on each SIMD, so one wave's vector
 // epilogue runs while the other's MFMAs occupy the matrix core; FP8's larger
 // operands leave room for only one wave per SIMD.
