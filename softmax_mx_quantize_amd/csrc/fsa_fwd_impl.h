@@ -60,21 +60,6 @@
 #ifndef FSA_PIPE
 #define FSA_PIPE -1
 #endif
-#ifndef FSA_PREFETCH
-#define FSA_PREFETCH -1
-#endif
-#ifndef FSA_PPSPLIT
-#define FSA_PPSPLIT 0
-#endif
-#ifndef FSA_XB
-#define FSA_XB 1
-#endif
-#ifndef FSA_PP
-#define FSA_PP 1
-#endif
-#ifndef FSA_HINT
-#define FSA_HINT 1
-#endif
 #ifndef FSA_NSUB6
 #define FSA_NSUB6 2
 #endif
@@ -151,7 +136,24 @@ __device__ __forceinline__ float conv_scale(int sb) {
   return __uint_as_float((uint32_t)(sb + REF) << 23);
 }
 
+// Level of a block whose largest pattern is m: the binade plus 127 + REF,
+// i.e. the exponent field of m after rounding its mantissa to M bits
+// (nearest, ties to even): floor(RNE(2^M m / 2^23) / 2^M).  For a pattern
+// from y >= 2^23 this is the binade of block_binade below; smaller patterns
+// lie below every level the shifts distinguish.  m is clamped first so that
+// the rounding cannot carry out of 32 bits; the clamp sits one level above
+// the largest shift (127 + REF + EXT), so the row still reaches the
+// fallback.
+template <int M>
+__device__ __forceinline__ int block_level(uint32_t m) {
+  constexpr uint32_t LIM = (uint32_t)(127 + REF + EXT + 1) << 23;
+  const uint32_t mc = min(m, LIM);
+  const uint32_t lsb = (mc >> (23 - M)) & 1u;
+  return (int)((mc + (1u << (22 - M)) - 1u + lsb) >> 23);
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
+
 
 // Truncation toward zero to u32 (v_cvt_u32_f32, which saturates and maps NaN
 // and negatives to 0; the exponential relies on that).  It must stay a
@@ -319,11 +321,6 @@ __device__ __forceinline__ opv<F> ones_operand() {
 // trades the odd 16-lane rows of its first operand with the even rows of its
 // second, resp. the upper 32 lanes of the first with the lower 32 of the
 // second), so that the epilogue waits on no LDS round trip.
-// max(x, x of lane ^ 16):
-__device__ __forceinline__ uint32_t max_xor16(uint32_t x) {
-  const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-  return max((uint32_t)p[0], (uint32_t)p[1]);
-}
 // x of lane ^ 48 for lane groups 1 and 2 (rows 1 and 2 trade places); the
 // result is unspecified in groups 0 and 3.
 __device__ __forceinline__ int swap_rows12(int x, int g) {
@@ -417,25 +414,30 @@ __device__ __forceinline__ opv<F> q_operand(const uint16_t* row, float mult, int
   return o;
 }
 
-// Scheduling hint for one straight-line phase of the pipelined loop: NM
-// times {one MFMA, up to ND LDS reads, up to NV vector instructions}, so that
-// the vector work of one wave issues in the shadow of its own MFMAs.
-template <int NM, int ND, int NV>
-__device__ __forceinline__ void interleave_hint() {
-#pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, ND, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
-  }
+// Direct buffer -> LDS loads (lane i of the wave writes the 16 (4) bytes it
+// loads at lds + 16 i (4 i)), issued as inline assembly: the compiler then
+// adds no waits of its own for them.  Its own tracking of such loads loses
+// precision across the unrolled sweep and made each tile wait for the loads
+// issued just before it; the sweep orders them explicitly instead (a vmcnt
+// wait before each workgroup barrier).  M0 carries the LDS address.  The
+// compiler inserts no wait states ahead of inline assembly, so the load
+// brings its own: 5, the most any of its operands needs (a buffer resource
+// or offset in scalar registers the vector unit has just written, as when
+// the compiler refills spilled scalar registers with v_readlane; 1 after an
+// M0 write).
+__device__ __forceinline__ void dma_lds16(__amdgpu_buffer_rsrc_t rs, uint32_t lds, int voff, int soff) {
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rs), "s"(soff), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma_lds4(__amdgpu_buffer_rsrc_t rs, uint32_t lds, int voff, int soff) {
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rs), "s"(soff), "{m0}"(lds) : "memory");
+}
+// 32-bit LDS address of a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
 
-__device__ __forceinline__ void dma16(const void* g, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* g, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 4, 0, 0);
-}
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Wait until at most N of this wave's memory loads are still outstanding
 // (loads complete in issue order for the counter).
@@ -476,39 +478,31 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   constexpr int KSTAGE = K_BYTES + KS_BYTES;   // K^ tile and its scales
   constexpr int VSTAGE = V_BYTES + VS_BYTES;   // V^T tile and its scales
 
-  // One wave per SIMD (4 waves): software-pipelined tile loop on 4-stage
-  // rings; two waves per SIMD (8 waves): tile after tile on 3-stage rings.
-  constexpr bool SWP = NWAVES == 4;
-  // Eight waves of one subtile each: ping-pong between the two halves of
-  // the workgroup (two subtiles per wave leave too few registers for it).
-  constexpr bool PP = NWAVES == 8 && NSUB == 1 && FSA_PP;
-  constexpr int NSTAGE = SWP ? 4 : 3;       // LDS ring depth
-  // K^ and V^T have rings of their own (the pipelined loop reads K^ one
-  // tile ahead of V^T).  One LDS object per stage, always addressed through
-  // a compile-time stage index: the compiler then sees that reads of one
-  // stage cannot alias the DMA in flight into another, and does not wait
-  // for that DMA first.
+  // Block levels (a block's binade plus 127 + REF) between which the block
+  // shifts are linear: at XLO and below the shift is CAP, at XHI and above
+  // it is -EXT.
+  constexpr int XLO = 127 + REF - CAP, XHI = 127 + REF + EXT;
+  // Three-stage LDS rings, K^ and V^T each.  One LDS object per stage,
+  // always addressed through a compile-time stage index: the compiler then
+  // sees that reads of one stage cannot alias the DMA in flight into
+  // another, and does not wait for that DMA first.
   __shared__ __align__(16) uint8_t kl0[KSTAGE];
   __shared__ __align__(16) uint8_t kl1[KSTAGE];
   __shared__ __align__(16) uint8_t kl2[KSTAGE];
-  __shared__ __align__(16) uint8_t kl3[NSTAGE > 3 ? KSTAGE : 16];
   __shared__ __align__(16) uint8_t vl0[VSTAGE];
   __shared__ __align__(16) uint8_t vl1[VSTAGE];
   __shared__ __align__(16) uint8_t vl2[VSTAGE];
-  __shared__ __align__(16) uint8_t vl3[NSTAGE > 3 ? VSTAGE : 16];
   auto kstage = [&](auto st_tag) __attribute__((always_inline)) -> uint8_t* {
-    constexpr int ST = decltype(st_tag)::value % NSTAGE;
+    constexpr int ST = decltype(st_tag)::value;
     if constexpr (ST == 0) return kl0;
     else if constexpr (ST == 1) return kl1;
-    else if constexpr (ST == 2) return kl2;
-    else return kl3;
+    else return kl2;
   };
   auto vstage = [&](auto st_tag) __attribute__((always_inline)) -> uint8_t* {
-    constexpr int ST = decltype(st_tag)::value % NSTAGE;
+    constexpr int ST = decltype(st_tag)::value;
     if constexpr (ST == 0) return vl0;
     else if constexpr (ST == 1) return vl1;
-    else if constexpr (ST == 2) return vl2;
-    else return vl3;
+    else return vl2;
   };
 
   const int tid = threadIdx.x;
@@ -615,24 +609,22 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   auto issue_k = [&](int t, uint8_t* base) __attribute__((always_inline)) {
     const int ln = opaque_lane();
     const int kv0 = ONE_VOFF ? k_lane_off(0, ln) : 0;
+    const uint32_t lb = lds_addr(base);
 #pragma unroll
     for (int k = 0; k < NK_DMA; ++k)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          k_rsrc, (lds_void*)(base + (wave + NWAVES * k) * 1024), 16, ONE_VOFF ? kv0 : k_voff[k],
-          t * KT * RB + (ONE_VOFF ? k * NWAVES * 8 * RB : 0), 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ks_rsrc, (lds_void*)(base + ks_lds), 4,
-                                             ONE_VOFF ? ln * 4 : s_voff, t * KS_BYTES + ks_soff, 0, 0);
+      dma_lds16(k_rsrc, lb + (wave + NWAVES * k) * 1024, ONE_VOFF ? kv0 : k_voff[k],
+                t * KT * RB + (ONE_VOFF ? k * NWAVES * 8 * RB : 0));
+    dma_lds4(ks_rsrc, lb + ks_lds, ONE_VOFF ? ln * 4 : s_voff, t * KS_BYTES + ks_soff);
   };
   auto issue_v = [&](int t, uint8_t* base) __attribute__((always_inline)) {
     const int ln = opaque_lane();
     const int vv0 = ONE_VOFF ? v_lane_off(0, ln) : 0;
+    const uint32_t lb = lds_addr(base);
 #pragma unroll
     for (int k = 0; k < NV_DMA; ++k)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          v_rsrc, (lds_void*)(base + (wave + NWAVES * k) * 1024), 16, ONE_VOFF ? vv0 : v_voff[k],
-          t * VRB + (ONE_VOFF ? k * NWAVES * 8 * (int)v_row : 0), 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vs_rsrc, (lds_void*)(base + vs_lds), 4,
-                                             ONE_VOFF ? ln * 4 : s_voff, t * VS_BYTES + vs_soff, 0, 0);
+      dma_lds16(v_rsrc, lb + (wave + NWAVES * k) * 1024, ONE_VOFF ? vv0 : v_voff[k],
+                t * VRB + (ONE_VOFF ? k * NWAVES * 8 * (int)v_row : 0));
+    dma_lds4(vs_rsrc, lb + vs_lds, ONE_VOFF ? ln * 4 : s_voff, t * VS_BYTES + vs_soff);
   };
   // DMA instructions each wave issues per K^ tile and per V^T tile
   constexpr int DMA_K = NK_DMA + 1;
@@ -670,20 +662,9 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   float mg[NSUB];
   wait_dma();
   __syncthreads();
-  // The rings fill ahead of the sweep.  The pipelined loop reads K^ one
-  // tile ahead: K^ tiles 1 and 2 and V^T tile 1 are issued here (clamped to
-  // the last tile, which then lands again in a stage nobody reads, so the
-  // load count stays uniform); the tile-after-tile loop takes tiles 1 and 2.
-  if constexpr (SWP) {
-    issue_k(min(1, n_tiles - 1), kl1);
-    issue_k(min(2, n_tiles - 1), kl2);
-    issue_v(min(1, n_tiles - 1), vl1);
-  } else if constexpr (PP) {
-    issue_k(min(1, n_tiles - 1), kl1);
-  } else {
-    if (n_tiles > 1) { issue_k(1, kl1); issue_v(1, vl1); }
-    if (n_tiles > 2) { issue_k(2, kl2); issue_v(2, vl2); }
-  }
+  // the rings fill ahead of the sweep
+  if (n_tiles > 1) { issue_k(1, kl1); issue_v(1, vl1); }
+  if (n_tiles > 2) { issue_k(2, kl2); issue_v(2, vl2); }
   {
     v4f acc[NSUB][8];
 #pragma unroll
@@ -766,14 +747,14 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
 
   // Lane-constant LDS byte offsets.  For slice j of the score product the
   // lane's K^ row is kk0 + 4j (+48 for the FP8 high half), and its swizzle
-  // does not depend on j; V^T row 16dt + r likewise.  Every fragment read is
-  // a base register plus a compile-time offset.
+  // does not depend on j; V^T row 16dt + r likewise.
   const int kk0 = BITS == 8 ? 16 * (r >> 2) + (r & 3) : 32 * (r >> 2) + (r & 3);
   const int ksw = swz_k<F, D>(kk0);
   const int vsw = swz_v(r);
-  int k_off[3], v_off[3];
+  constexpr int NOFF = BITS == 8 ? 2 : (BITS == 6 ? 3 : 1);   // row pieces per operand
+  int k_off[NOFF], v_off[NOFF];
 #pragma unroll
-  for (int i = 0; i < 3; ++i) {
+  for (int i = 0; i < NOFF; ++i) {
     int lo;
     if (BITS == 8) lo = i == 0 ? 16 * g : 64 + 16 * g;
     else if (BITS == 6) lo = 24 * g + 8 * i;
@@ -795,19 +776,25 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
     if constexpr (NDT == 8) return *reinterpret_cast<const uint2*>(base + vs_off);
     else return make_uint2(*reinterpret_cast<const uint32_t*>(base + vs_off), 0u);
   };
-  // Read every fragment of a phase before its first product (one subtile
-  // per wave leaves the registers for it); otherwise one slice at a time.
-  constexpr bool PREFETCH = FSA_PREFETCH >= 0 ? FSA_PREFETCH != 0 : NSUB == 1;
-  // Otherwise, fragments in flight per operand stream (0: the compiler's
-  // choice, with the FP6 slice fence).  FP8 reads three ahead in a fixed
+  // Fragments in flight per operand stream: 0 leaves the order to the
+  // compiler (with the FP6 slice fence); FP8 reads three ahead in a fixed
   // order (measured best; left free, the compiler hoists every read of a
   // phase and runs out of registers).
   constexpr int PIPE = FSA_PIPE >= 0 ? FSA_PIPE : (BITS == 8 ? 3 : 0);
   const bool k_live = 32 * g < D;               // FP6/FP4 lane groups past D
   const bool k_hi = 64 + 16 * g < D;            // FP8 high half present
 
-  auto frag = [&](const uint8_t* base, const int* off, int imm, bool live, bool hi) __attribute__((always_inline)) -> opv<F> {
+  // Fragment reads go through the stage object itself (never an opaque
+  // address): the compiler then knows which stage a read touches and does
+  // not make it wait for the DMA in flight into the others.
+  struct Rows { const uint8_t* base; const int* off; };
+  auto rows = [&](const uint8_t* stage, const int* off) __attribute__((always_inline)) -> Rows {
+    return Rows{stage, off};
+  };
+  auto frag = [&](const Rows& rw, int imm, bool live, bool hi) __attribute__((always_inline)) -> opv<F> {
     opv<F> o = zero_operand<F>();
+    const uint8_t* base = rw.base;
+    const int* off = rw.off;
     if constexpr (BITS == 8) {
       if (live) {
         const uint4 a0 = *reinterpret_cast<const uint4*>(base + off[0] + imm);
@@ -831,12 +818,14 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
     }
     return o;
   };
-  // K^ fragment of 16-key slice j of the tile in stage `base`
-  auto kfrag = [&](const uint8_t* base, int j) __attribute__((always_inline)) -> opv<F> {
+  // K^ fragment of 16-key slice j; V^T fragment of output tile dt
+  auto kfrag = [&](const Rows& rw, int j) __attribute__((always_inline)) -> opv<F> {
     const int jrow = 4 * j + ((BITS == 8 && j >= 4) ? 48 : 0);
-    return frag(base, k_off, jrow * RS, BITS == 8 ? 16 * g < D : k_live, BITS == 8 ? k_hi : false);
+    return frag(rw, jrow * RS, BITS == 8 ? 16 * g < D : k_live, BITS == 8 ? k_hi : false);
   };
-
+  auto vfrag = [&](const Rows& rw, int dt) __attribute__((always_inline)) -> opv<F> {
+    return frag(rw, 16 * dt * RS, true, true);
+  };
 
   // FP6 fragments arrive in three 8-byte pieces per lane; left free, the
   // scheduler hoists them for many slices at once and pays in register
@@ -846,8 +835,8 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
     if constexpr (BITS == 6) __builtin_amdgcn_sched_barrier(0);
   };
 
-  // The steps of one key tile, on state shared across phases: the score
-  // accumulators of each subtile, and P~ of each subtile in operand form.
+  // State of one key tile: the score accumulators of each subtile, and P~ of
+  // each subtile in operand form with its scale byte.
   v4f acc[NSUB][8];
   opv<F> pw[NSUB];
   int psc[NSUB];
@@ -855,8 +844,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   // Scores of the tile in stage `base`: y = 2^23 s + accumulator start.  In
   // a masked tile the accumulator of an invisible key starts at -inf, so its
   // y is -inf and its pattern 0: the epilogue carries no masking at all.
-  auto qk_into = [&](v4f (&acc)[NSUB][8], const uint8_t* base, int key0, auto masked_tag)
-                     __attribute__((always_inline)) {
+  auto qk_into = [&](const uint8_t* base, int key0, auto masked_tag) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     if constexpr (QUAD_PER_TILE) refresh_start();
     if constexpr (MASKED) {
@@ -870,42 +858,26 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
       }
     }
     const uint2 ksc = k_scales(base);
-    if constexpr (PREFETCH) {
-      // all eight K^ fragments in flight before the first product
-      opv<F> kfs[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int jrow = 4 * j + ((BITS == 8 && j >= 4) ? 48 : 0);
-        kfs[j] = frag(base, k_off, jrow * RS, BITS == 8 ? 16 * g < D : k_live, BITS == 8 ? k_hi : false);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s)
-          acc[s][j] = mfma_sel<F>(kfs[j], qf[s], MASKED ? acc[s][j] : minit[s],
-                                  (int)(j < 4 ? ksc.x : ksc.y), j, qsc[s]);
-    } else if constexpr (PIPE > 0) {
+    const Rows rw = rows(base, k_off);
+    if constexpr (PIPE > 0) {
       // PIPE fragments in flight: the read of slice j+PIPE issues right
       // after the products of slice j, in a fixed order
       opv<F> kfs[PIPE > 0 ? PIPE : 1];
 #pragma unroll
-      for (int j = 0; j < PIPE; ++j) kfs[j] = kfrag(base, j);
+      for (int j = 0; j < PIPE; ++j) kfs[j] = kfrag(rw, j);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
 #pragma unroll
         for (int s = 0; s < NSUB; ++s)
           acc[s][j] = mfma_sel<F>(kfs[j % PIPE], qf[s], MASKED ? acc[s][j] : minit[s],
                                   (int)(j < 4 ? ksc.x : ksc.y), j, qsc[s]);
-        if (j + PIPE < 8) kfs[j % PIPE] = kfrag(base, j + PIPE);
+        if (j + PIPE < 8) kfs[j % PIPE] = kfrag(rw, j + PIPE);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int jrow = 4 * j + ((BITS == 8 && j >= 4) ? 48 : 0);
-        const opv<F> kf = frag(base, k_off, jrow * RS, BITS == 8 ? 16 * g < D : k_live,
-                               BITS == 8 ? k_hi : false);
+        const opv<F> kf = kfrag(rw, j);
 #pragma unroll
         for (int s = 0; s < NSUB; ++s)
           acc[s][j] = mfma_sel<F>(kf, qf[s], MASKED ? acc[s][j] : minit[s],
@@ -915,140 +887,85 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
     }
   };
 
-  // The same for subtile S alone (the pipelined loop computes the two
-  // subtiles in different phases).
-  auto qk_sub = [&](v4f (&A)[8], const uint8_t* base, int key0, auto s_tag, auto masked_tag)
-                    __attribute__((always_inline)) {
-    constexpr int SS = decltype(s_tag)::value;
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    if constexpr (MASKED) {
-      const int q = q_wave + 16 * SS + r;
-      const int lim = CAUSAL ? min(S, q + 1) : S;
-#pragma unroll
-      for (int p = 0; p < 32; ++p)
-        A[p >> 2][p & 3] = key0 + kpos<F>(g, p) < lim ? c0s[SS] : -INFINITY;
-    }
-    const uint2 ksc = k_scales(base);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int jrow = 4 * j + ((BITS == 8 && j >= 4) ? 48 : 0);
-      const opv<F> kf = frag(base, k_off, jrow * RS, BITS == 8 ? 16 * g < D : k_live,
-                             BITS == 8 ? k_hi : false);
-      A[j] = mfma_sel<F>(kf, qf[SS], MASKED ? A[j] : minit[SS], (int)(j < 4 ? ksc.x : ksc.y), j,
-                         qsc[SS]);
-      slice_fence();
-    }
-  };
-
-  // Fused exponential + MX quantisation of P for the scores in acc.
+  // Fused exponential + MX quantisation of P for the scores of subtile s.
   //
   // The bit-pattern exponential: y's integer part is the fp32 pattern of
   // 2^(t + R).  It is monotone in y, and exact wherever y >= 2^24 (below, the
   // block sits beyond the largest shift anyway), so the block maxima are
   // taken on the integers, and y is dead once converted.
-  auto epi_sub = [&](v4f (&acc)[NSUB][8], int s) __attribute__((always_inline)) {
-    {
-      // patterns in the operand order of the pack conversion: FP6 takes
-      // even and odd elements as two 16-register sources
-      float pv[32];
+  auto epi_sub = [&](int s) __attribute__((always_inline)) {
+    // patterns in the operand order of the pack conversion: FP6 takes even
+    // and odd elements as two 16-register sources
+    float pv[32];
 #pragma unroll
-      for (int p = 0; p < 32; ++p) {
-        const int o = BITS == 6 ? (p & 1) * 16 + (p >> 1) : p;
-        pv[o] = __uint_as_float(cvt_u32_trunc(acc[s][p >> 2][p & 3]));
-      }
-      auto u = [&](int o) __attribute__((always_inline)) { return __float_as_uint(pv[o]); };
-      // block maxima: one block per lane (FP6/FP4) or two half blocks (FP8)
-      uint32_t m0 = max(max(u(0), u(1)), u(2));
-      uint32_t m1 = max(max(u(16), u(17)), u(18));
-#pragma unroll
-      for (int p = 3; p < 15; p += 2) {
-        m0 = max(max(m0, u(p)), u(p + 1));
-        m1 = max(max(m1, u(16 + p)), u(17 + p));
-      }
-      m0 = max(m0, u(15));
-      m1 = max(m1, u(31));
-      if (BITS == 8) {
-        m0 = max_xor16(m0);
-        m1 = max_xor16(m1);
-      } else {
-        m0 = max(m0, m1);
-        m1 = m0;
-      }
-      const int e0 = block_binade<MB>((float)m0), e1 = block_binade<MB>((float)m1);
-      kmax[s] = max(kmax[s], max(e0, e1));
-      // block shifts relative to the guess; P~ scale bytes 127 - pl - d.  The
-      // conversion divides by 2^(sb + R - 127) = 2^(R - pl - d).
-      const int sb0 = 127 - PL - min(-min(e0, EXT), CAP);
-      const int sb1 = 127 - PL - min(-min(e1, EXT), CAP);
-      uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if constexpr (BITS == 6)
-        pack_fp6_split(pv, w, conv_scale(sb0));
-      else
-        Pack32<F, false>::run(pv, w, conv_scale(sb0), conv_scale(sb1));
-#pragma unroll
-      for (int i = 0; i < Operand<F>::words; ++i) pw[s][i] = (int)w[i];
-      psc[s] = p_scale<BITS>(sb0, sb1, g);
+    for (int p = 0; p < 32; ++p) {
+      const int o = BITS == 6 ? (p & 1) * 16 + (p >> 1) : p;
+      pv[o] = __uint_as_float(cvt_u32_trunc(acc[s][p >> 2][p & 3]));
     }
+    auto u = [&](int o) __attribute__((always_inline)) { return __float_as_uint(pv[o]); };
+    // maxima of the two halves of the lane's 32 values
+    uint32_t m0 = max(max(u(0), u(1)), u(2));
+    uint32_t m1 = max(max(u(16), u(17)), u(18));
+#pragma unroll
+    for (int p = 3; p < 15; p += 2) {
+      m0 = max(max(m0, u(p)), u(p + 1));
+      m1 = max(max(m1, u(16 + p)), u(17 + p));
+    }
+    m0 = max(m0, u(15));
+    m1 = max(m1, u(31));
+    // One block maximum per lane.  FP6/FP4: the lane's own block.  FP8: a
+    // lane holds half blocks; one swap of the two half maxima across the
+    // 16-lane rows completes one whole block per lane group, group g ending
+    // up with block (0, 2, 1, 3)[g].
+    uint32_t mb;
+    if constexpr (BITS == 8) {
+      const auto h = __builtin_amdgcn_permlane16_swap(m0, m1, false, false);
+      mb = max((uint32_t)h[0], (uint32_t)h[1]);
+    } else {
+      mb = max(m0, m1);
+    }
+    const int x = block_level<MB>(mb);
+    kmax[s] = max(kmax[s], x);
+    // scale byte 127 - pl - d of that block (d = the block shift); the
+    // conversion divides by 2^(sb + R - 127) = 2^(R - pl - d)
+    const int sb = min(max(x, XLO), XHI) - REF - PL;
+    uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if constexpr (BITS == 8) {
+      // the lane's low and high half blocks, then block g for the B scale
+      const auto hl = __builtin_amdgcn_permlane16_swap((uint32_t)sb, (uint32_t)sb, false, false);
+      const int sb_lo = (int)hl[0], sb_hi = (int)hl[1];
+      Pack32<F, false>::run(pv, w, conv_scale(sb_lo), conv_scale(sb_hi));
+      const auto hd = __builtin_amdgcn_permlane32_swap((uint32_t)sb_lo, (uint32_t)sb_hi, false, false);
+      psc[s] = (int)((g & 1) ? hd[1] : hd[0]);
+    } else {
+      if constexpr (BITS == 6) pack_fp6_split(pv, w, conv_scale(sb));
+      else Pack32<F, false>::run(pv, w, conv_scale(sb), conv_scale(sb));
+      psc[s] = sb;
+    }
+#pragma unroll
+    for (int i = 0; i < Operand<F>::words; ++i) pw[s][i] = (int)w[i];
   };
 
-  auto epi = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) epi_sub(acc, s);
-  };
-
-  // P V and the row sums of subtile s on the matrix cores.
-  auto pv_sub = [&](const uint8_t* base, int s) __attribute__((always_inline)) {
-    const uint2 vsc = v_scales(base);
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const opv<F> vf = frag(base, v_off, 16 * dt * RS, true, true);
-      O[s][dt] = mfma_sel<F>(vf, pw[s], O[s][dt], (int)(dt < 4 ? vsc.x : vsc.y), dt, psc[s]);
-      slice_fence();
-    }
-    L[s] = row_sum<F>(ones, pw[s], L[s], psc[s]);
-  };
-
-  // V^T fragments of the tile in stage `base`, read ahead of the epilogue
-  // so that their LDS latency hides under it.
-  opv<F> vfs[PREFETCH ? NDT : 1];
-  uint2 vsc_pf;
-  auto pv_load = [&](const uint8_t* base) __attribute__((always_inline)) {
-    if constexpr (PREFETCH) {
-      vsc_pf = v_scales(base);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) vfs[dt] = frag(base, v_off, 16 * dt * RS, true, true);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
   // P V and the row sums on the matrix cores, V^T tile in stage `base`.
   auto pv_step = [&](const uint8_t* base) __attribute__((always_inline)) {
-    if constexpr (PREFETCH) {
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s)
-          O[s][dt] = mfma_sel<F>(vfs[dt], pw[s], O[s][dt], (int)(dt < 4 ? vsc_pf.x : vsc_pf.y), dt, psc[s]);
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) L[s] = row_sum<F>(ones, pw[s], L[s], psc[s]);
-      return;
-    }
     const uint2 vsc = v_scales(base);
+    const Rows rw = rows(base, v_off);
     if constexpr (PIPE > 0) {
       opv<F> vfp[PIPE > 0 ? PIPE : 1];
 #pragma unroll
-      for (int dt = 0; dt < PIPE && dt < NDT; ++dt) vfp[dt] = frag(base, v_off, 16 * dt * RS, true, true);
+      for (int dt = 0; dt < PIPE && dt < NDT; ++dt) vfp[dt] = vfrag(rw, dt);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
         for (int s = 0; s < NSUB; ++s)
           O[s][dt] = mfma_sel<F>(vfp[dt % PIPE], pw[s], O[s][dt], (int)(dt < 4 ? vsc.x : vsc.y), dt, psc[s]);
-        if (dt + PIPE < NDT) vfp[dt % PIPE] = frag(base, v_off, 16 * (dt + PIPE) * RS, true, true);
+        if (dt + PIPE < NDT) vfp[dt % PIPE] = vfrag(rw, dt + PIPE);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const opv<F> vf = frag(base, v_off, 16 * dt * RS, true, true);
+        const opv<F> vf = vfrag(rw, dt);
 #pragma unroll
         for (int s = 0; s < NSUB; ++s)
           O[s][dt] = mfma_sel<F>(vf, pw[s], O[s][dt], (int)(dt < 4 ? vsc.x : vsc.y), dt, psc[s]);
@@ -1070,203 +987,34 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
-  auto qk_any_into = [&](v4f (&A)[NSUB][8], const uint8_t* base, int t)
-                         __attribute__((always_inline)) {
-    if (t < n_clean) qk_into(A, base, t * KT, std::false_type{});
-    else qk_into(A, base, t * KT, std::true_type{});
-  };
-  auto qk_any = [&](const uint8_t* base, int t) __attribute__((always_inline)) {
-    qk_any_into(acc, base, t);
-  };
 
-  if constexpr (SWP) {
-    // One wave per SIMD, software-pipelined so that every stretch of matrix
-    // work has independent vector work beside it (one wave overlaps them only
-    // within its own instruction stream), with the score accumulators of one
-    // subtile written while those of the other are read:
-    //   phase 1: scores of tile t, subtile 1 + P V of tile t-1, subtile 1
-    //            | epilogue of tile t, subtile 0
-    //   phase 2: scores of tile t+1, subtile 0 + P V of tile t, subtile 0
-    //            | epilogue of tile t, subtile 1
-    // K^ is read one tile ahead of V^T.  Step t issues K^ tile t+3 into the
-    // stage of tile t-1 and V^T tile t+2 into that of tile t-2, both last
-    // read in step t-1, before the barrier that ended it; the loads of step
-    // t-1 (K^ t+2, V^T t+1) must have landed by the barrier that ends step t.
-    // Past the end the loads re-fetch the last tile into a stage nobody reads
-    // any more, which keeps the count uniform; everything in flight is
-    // drained before the kernel ends.
-    //
-    // A clean step (every key of both tiles visible to every row of the
-    // wave, a previous and a next tile present) is one straight-line block
-    // per phase with an interleaving hint; the generic step masks both score
-    // products and branches on the neighbours.
-    auto step = [&](int t, auto ph, auto clean_tag, bool has_prev, bool has_next)
-                    __attribute__((always_inline)) {
-      constexpr int P = decltype(ph)::value;
-      constexpr bool CLEAN = decltype(clean_tag)::value;
-      using IP = std::integral_constant<int, P>;
-      using IP1 = std::integral_constant<int, (P + 1) & 3>;
-      using IP2 = std::integral_constant<int, (P + 2) & 3>;
-      using IP3 = std::integral_constant<int, (P + 3) & 3>;
-      using MT = std::integral_constant<bool, !CLEAN>;
-      issue_k(min(t + 3, n_tiles - 1), kstage(IP3{}));
-      issue_v(min(t + 2, n_tiles - 1), vstage(IP2{}));
-      qk_sub(acc[1], kstage(IP{}), t * KT, I1{}, MT{});
-      if (CLEAN || has_prev) pv_sub(vstage(IP3{}), 1);
-      epi_sub(acc, 0);
-      if constexpr (CLEAN && FSA_HINT) interleave_hint<17, 2, 6>();
-      __builtin_amdgcn_sched_barrier(0);
-      if (CLEAN || has_next) qk_sub(acc[0], kstage(IP1{}), (t + 1) * KT, I0{}, MT{});
-      pv_sub(vstage(IP{}), 0);
-      epi_sub(acc, 1);
-      if constexpr (CLEAN && FSA_HINT) interleave_hint<17, 2, 6>();
-      __builtin_amdgcn_sched_barrier(0);
-      wait_dma_keep<DMA_K + DMA_V>();
-      ring_barrier();
-    };
-    auto step_any = [&](int t) __attribute__((always_inline)) {
-      const bool has_prev = t > 0, has_next = t + 1 < n_tiles;
-      switch (t & 3) {
-        case 0: step(t, I0{}, std::false_type{}, has_prev, has_next); break;
-        case 1: step(t, I1{}, std::false_type{}, has_prev, has_next); break;
-        case 2: step(t, I2{}, std::false_type{}, has_prev, has_next); break;
-        default: step(t, I3{}, std::false_type{}, has_prev, has_next); break;
-      }
-    };
-    // scores of tile 0, subtile 0; K^ tile 1 must land before step 0 reads it
-    qk_sub(acc[0], kl0, 0, I0{}, std::true_type{});
-    wait_dma_keep<DMA_K + DMA_V>();
+  // Tile after tile, one barrier per tile; two waves per SIMD overlap one's
+  // vector epilogue with the other's products.  Tile t+1 must have landed
+  // (t+2 may still be in flight); after the barrier every wave is done with
+  // the stages of tile t, which then take tile t+3.
+  auto step = [&](int t, auto st_tag) __attribute__((always_inline)) {
+    uint8_t* kb = kstage(st_tag);
+    uint8_t* vb = vstage(st_tag);
+    if (t < n_clean) qk_into(kb, t * KT, std::false_type{});
+    else qk_into(kb, t * KT, std::true_type{});
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) epi_sub(s);
+    // keep the P V fragment reads below the epilogue: hoisted above it they
+    // would hold registers through it
+    if constexpr (PIPE > 0) __builtin_amdgcn_sched_barrier(0);
+    pv_step(vb);
+    if (t + 2 < n_tiles) wait_dma_keep<DMA_K + DMA_V>();
+    else wait_dma();
     ring_barrier();
-    step_any(0);
-    int t = 1;
-    // steps t..t+3 clean: tiles up to t+4 unmasked for every row of the wave
-    for (; t + 4 < n_clean; t += 4) {
-      step(t, I1{}, std::true_type{}, true, true);
-      step(t + 1, I2{}, std::true_type{}, true, true);
-      step(t + 2, I3{}, std::true_type{}, true, true);
-      step(t + 3, I0{}, std::true_type{}, true, true);
+    if (t + 3 < n_tiles) {
+      issue_k(t + 3, kb);
+      issue_v(t + 3, vb);
     }
-    for (; t < n_tiles; ++t) step_any(t);
-    // drain: P V of the last tile, subtile 1
-    switch ((n_tiles - 1) & 3) {
-      case 0: pv_sub(vstage(I0{}), 1); break;
-      case 1: pv_sub(vstage(I1{}), 1); break;
-      case 2: pv_sub(vstage(I2{}), 1); break;
-      default: pv_sub(vstage(I3{}), 1); break;
-    }
-    wait_dma();
-  } else if constexpr (PP) {
-    // Ping-pong.  Waves w and w+4 share a SIMD.  Every wave runs the same
-    // sequence of phases, a workgroup barrier after each,
-    //   matrix phase t: scores of tile t and P V of tile t-1 (MFMA),
-    //   vector phase t: epilogue of tile t (VALU),
-    // but waves 4-7 start one phase late (one extra barrier before their
-    // first phase, none after their last), so that the matrix core runs one
-    // half's products while the vector unit runs the other half's epilogue.
-    // K^ tile t sits in stage t % 3, V^T tile t-1 in stage (t-1) % 3.  A
-    // wave's matrix phase t issues its share of K^ tile t+2 (into the stage
-    // of tile t-1) and V^T tile t+1 (into that of tile t-2); every wave has
-    // finished reading those by then: the first half reads tile t-1 up to
-    // its phase 2t-1, the second half one phase later, which ends at the
-    // barrier before the first half's matrix phase t.  The first read of K^
-    // tile t+2 follows the first half's vector phase t+1, which the second
-    // half meets at the end of its matrix phase t+1: each half waits for its
-    // own loads there.
-    const bool second = FSA_PPSPLIT ? (wave & 1) != 0 : wave >= NWAVES / 2;
-    // matrix phase, clean: one stream of score and P V products; each V^T
-    // fragment is read into the registers of the K^ fragment whose product
-    // has just issued, so the reads of the P V products hide under the
-    // score products
-    auto mphase_clean = [&](const uint8_t* kb, const uint8_t* vb) __attribute__((always_inline)) {
-      const uint2 ksc = k_scales(kb);
-      const uint2 vsc = v_scales(vb);
-      opv<F> fr[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int jrow = 4 * j + ((BITS == 8 && j >= 4) ? 48 : 0);
-        fr[j] = frag(kb, k_off, jrow * RS, BITS == 8 ? 16 * g < D : k_live, BITS == 8 ? k_hi : false);
-      }
-      if (FSA_XB) __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s)
-          acc[s][j] = mfma_sel<F>(fr[j], qf[s], minit[s], (int)(j < 4 ? ksc.x : ksc.y), j, qsc[s]);
-        if (j < NDT) fr[j] = frag(vb, v_off, 16 * j * RS, true, true);
-        if (FSA_XB) __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s)
-          O[s][dt] = mfma_sel<F>(fr[dt], pw[s], O[s][dt], (int)(dt < 4 ? vsc.x : vsc.y), dt, psc[s]);
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) L[s] = row_sum<F>(ones, pw[s], L[s], psc[s]);
-    };
-    auto iter = [&](int t, auto st_tag) __attribute__((always_inline)) {
-      constexpr int P = decltype(st_tag)::value;
-      const uint8_t* kb = kstage(st_tag);
-      const uint8_t* vb = vstage(std::integral_constant<int, (P + 2) % 3>{});
-      const bool more = t < n_tiles;
-      if (more) {
-        issue_k(min(t + 2, n_tiles - 1), kstage(std::integral_constant<int, (P + 2) % 3>{}));
-        issue_v(min(t + 1, n_tiles - 1), vstage(std::integral_constant<int, (P + 1) % 3>{}));
-      }
-      if (t > 0 && t < n_clean) {
-        mphase_clean(kb, vb);
-      } else {
-        if (more) qk_any(kb, t);
-        if (t > 0) {
-          pv_load(vb);
-          pv_step(vb);
-        }
-      }
-      if (second) {
-        if (more) wait_dma_keep<DMA_K + DMA_V>();
-        else wait_dma();
-      }
-      ring_barrier();
-      if (more) epi();
-      if (!second) {
-        if (more) wait_dma_keep<DMA_K + DMA_V>();
-        else wait_dma();
-      }
-      if (more || !second) ring_barrier();
-    };
-    if (second) ring_barrier();
-    for (int t = 0; t <= n_tiles; t += 3) {
-      iter(t, I0{});
-      if (t + 1 <= n_tiles) iter(t + 1, I1{});
-      if (t + 2 <= n_tiles) iter(t + 2, I2{});
-    }
-  } else {
-    // Tile after tile, one barrier per tile.  Tile t+1 must have landed
-    // (t+2 may still be in flight); after the barrier every wave is done
-    // with the stages of tile t, which then take tile t+3.
-    auto step = [&](int t, auto st_tag) __attribute__((always_inline)) {
-      uint8_t* kb = kstage(st_tag);
-      uint8_t* vb = vstage(st_tag);
-      qk_any(kb, t);
-      pv_load(vb);
-      epi();
-      // keep the P V fragment reads below the epilogue: hoisted above it
-      // they would hold registers through it
-      if constexpr (PIPE > 0) __builtin_amdgcn_sched_barrier(0);
-      pv_step(vb);
-      if (t + 2 < n_tiles) wait_dma_keep<DMA_K + DMA_V>();
-      else wait_dma();
-      ring_barrier();
-      if (t + 3 < n_tiles) {
-        issue_k(t + 3, kb);
-        issue_v(t + 3, vb);
-      }
-    };
-    for (int t = 0; t < n_tiles; t += 3) {
-      step(t, I0{});
-      if (t + 1 < n_tiles) step(t + 1, I1{});
-      if (t + 2 < n_tiles) step(t + 2, I2{});
-    }
+  };
+  for (int t = 0; t < n_tiles; t += 3) {
+    step(t, I0{});
+    if (t + 1 < n_tiles) step(t + 1, I1{});
+    if (t + 2 < n_tiles) step(t + 2, I2{});
   }
 
   // row offsets in binades (the oracle's kappa); rows beyond EXT come out
@@ -1274,7 +1022,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   int kap[NSUB];
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
-    int k = kmax[s];
+    int k = kmax[s] - (127 + REF);            // block level -> binade
     k = max(k, __shfl_xor(k, 16));
     k = max(k, __shfl_xor(k, 32));
     kap[s] = k > 0 ? k : 0;
