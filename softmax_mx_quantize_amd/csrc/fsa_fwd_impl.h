@@ -602,29 +602,37 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   // every wave issues the same number of loads.  The wave's part goes in
   // the scalar offset.
   const int s_voff = lane * 4;
-  const int ks_soff = wave < NKS ? wave * 256 : 0;
-  const int vs_soff = wave < NVS ? wave * 256 : 0;
-  const int ks_lds = K_BYTES + ks_soff;
-  const int vs_lds = V_BYTES + vs_soff;
+  // The wave index is made opaque at every issue so that the LDS targets
+  // (one per stage and row group) are recomputed with a scalar add rather
+  // than held in scalar registers across the sweep, where they would spill.
+  auto opaque_wave = [&]() __attribute__((always_inline)) {
+    int w = wave;
+    asm volatile("" : "+s"(w));
+    return w;
+  };
   auto issue_k = [&](int t, uint8_t* base) __attribute__((always_inline)) {
     const int ln = opaque_lane();
+    const int wv = opaque_wave();
     const int kv0 = ONE_VOFF ? k_lane_off(0, ln) : 0;
     const uint32_t lb = lds_addr(base);
+    const int ks_soff = wv < NKS ? wv * 256 : 0;
 #pragma unroll
     for (int k = 0; k < NK_DMA; ++k)
-      dma_lds16(k_rsrc, lb + (wave + NWAVES * k) * 1024, ONE_VOFF ? kv0 : k_voff[k],
+      dma_lds16(k_rsrc, lb + (wv + NWAVES * k) * 1024, ONE_VOFF ? kv0 : k_voff[k],
                 t * KT * RB + (ONE_VOFF ? k * NWAVES * 8 * RB : 0));
-    dma_lds4(ks_rsrc, lb + ks_lds, ONE_VOFF ? ln * 4 : s_voff, t * KS_BYTES + ks_soff);
+    dma_lds4(ks_rsrc, lb + K_BYTES + ks_soff, ONE_VOFF ? ln * 4 : s_voff, t * KS_BYTES + ks_soff);
   };
   auto issue_v = [&](int t, uint8_t* base) __attribute__((always_inline)) {
     const int ln = opaque_lane();
+    const int wv = opaque_wave();
     const int vv0 = ONE_VOFF ? v_lane_off(0, ln) : 0;
     const uint32_t lb = lds_addr(base);
+    const int vs_soff = wv < NVS ? wv * 256 : 0;
 #pragma unroll
     for (int k = 0; k < NV_DMA; ++k)
-      dma_lds16(v_rsrc, lb + (wave + NWAVES * k) * 1024, ONE_VOFF ? vv0 : v_voff[k],
+      dma_lds16(v_rsrc, lb + (wv + NWAVES * k) * 1024, ONE_VOFF ? vv0 : v_voff[k],
                 t * VRB + (ONE_VOFF ? k * NWAVES * 8 * (int)v_row : 0));
-    dma_lds4(vs_rsrc, lb + vs_lds, ONE_VOFF ? ln * 4 : s_voff, t * VS_BYTES + vs_soff);
+    dma_lds4(vs_rsrc, lb + V_BYTES + vs_soff, ONE_VOFF ? ln * 4 : s_voff, t * VS_BYTES + vs_soff);
   };
   // DMA instructions each wave issues per K^ tile and per V^T tile
   constexpr int DMA_K = NK_DMA + 1;
@@ -990,13 +998,23 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
 
   // Tile after tile, one barrier per tile; two waves per SIMD overlap one's
   // vector epilogue with the other's products.  Tile t+1 must have landed
-  // (t+2 may still be in flight); after the barrier every wave is done with
-  // the stages of tile t, which then take tile t+3.
+  // by the end of step t (t+2 may still be in flight); after the barrier the
+  // stages of tile t take tile t+3.  FP8 issues the loads of a tile in two
+  // halves (measured a little faster; a little slower for FP6/FP4): K^ tile
+  // t+3 right after the barrier that ends step t, V^T tile t+2 after the
+  // score products of step t (into the stage of tile t-1, free since the
+  // barrier that ended step t-1).  Either way the loads of tile t+1 precede
+  // those of tile t+2 in issue order, so the count kept in flight stays one
+  // tile.
+  constexpr bool SPLIT = BITS == 8;
   auto step = [&](int t, auto st_tag) __attribute__((always_inline)) {
+    constexpr int P = decltype(st_tag)::value;
     uint8_t* kb = kstage(st_tag);
     uint8_t* vb = vstage(st_tag);
     if (t < n_clean) qk_into(kb, t * KT, std::false_type{});
     else qk_into(kb, t * KT, std::true_type{});
+    if (SPLIT && t >= 1 && t + 2 < n_tiles)
+      issue_v(t + 2, vstage(std::integral_constant<int, (P + 2) % 3>{}));
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) epi_sub(s);
     // keep the P V fragment reads below the epilogue: hoisted above it they
@@ -1008,7 +1026,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
     ring_barrier();
     if (t + 3 < n_tiles) {
       issue_k(t + 3, kb);
-      issue_v(t + 3, vb);
+      if (!SPLIT) issue_v(t + 3, vb);
     }
   };
   for (int t = 0; t < n_tiles; t += 3) {
