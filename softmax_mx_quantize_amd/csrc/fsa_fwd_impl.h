@@ -31,9 +31,9 @@
 // V^T columns, with their E8M0 scales) stream through an LDS ring filled by
 // direct global->LDS buffer loads.  Each wave keeps its queries' Q^
 // fragments, O^T accumulators and row sums in registers; there is no online
-// max and no rescaling.  With 8 waves (two per SIMD) the hardware overlaps
-// one wave's vector epilogue with the other's MFMAs; with 4 waves the tile
-// loop is software-pipelined instead.
+// max and no rescaling.  Two waves share each SIMD (two workgroups of four
+// waves per CU by default), and the hardware overlaps one wave's vector
+// epilogue with the other's MFMAs.
 //
 // Register layout (16x16x128 scaled MFMA).  Lane (g, r) = 16g + r.  The score
 // tile is computed transposed (keys as rows, queries as columns) so that a
@@ -56,7 +56,12 @@
 #include "fsa_device.h"
 #include "fsa_internal.h"
 
-// Waves per workgroup for each element format (overridable at build time).
+// Build-time knobs (the defaults are the measured best): waves per SIMD the
+// kernels are built for, fragment pipeline depth (-1: per format), query
+// subtiles per wave and waves per workgroup for each element format.
+#ifndef FSA_WPE
+#define FSA_WPE 2
+#endif
 #ifndef FSA_PIPE
 #define FSA_PIPE -1
 #endif
@@ -70,13 +75,13 @@
 #define FSA_NSUB8 2
 #endif
 #ifndef FSA_NW8
-#define FSA_NW8 8
+#define FSA_NW8 4
 #endif
 #ifndef FSA_NW6
-#define FSA_NW6 8
+#define FSA_NW6 4
 #endif
 #ifndef FSA_NW4
-#define FSA_NW4 8
+#define FSA_NW4 4
 #endif
 
 namespace fsa {
@@ -456,7 +461,7 @@ __device__ __forceinline__ void ring_barrier() {
 }  // namespace
 
 template <int F, int D, bool CAUSAL, int NSUB, int NWAVES>
-__global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES * 64))) fsa_fwd_kernel(AttnArgs a) {
+__global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES * 64), amdgpu_waves_per_eu(FSA_WPE))) fsa_fwd_kernel(AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer-resource types exist only in the device pass
   constexpr int BITS = Fmt<F>::bits;
   constexpr int MB = Fmt<F>::mbits;
@@ -486,12 +491,15 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   // always addressed through a compile-time stage index: the compiler then
   // sees that reads of one stage cannot alias the DMA in flight into
   // another, and does not wait for that DMA first.
+  // Ring depth: three stages for one workgroup per CU; two let two
+  // workgroups share a CU (their barriers are independent).
+  constexpr int NST = NWAVES == 8 ? 3 : 2;
   __shared__ __align__(16) uint8_t kl0[KSTAGE];
   __shared__ __align__(16) uint8_t kl1[KSTAGE];
-  __shared__ __align__(16) uint8_t kl2[KSTAGE];
+  __shared__ __align__(16) uint8_t kl2[NST > 2 ? KSTAGE : 16];
   __shared__ __align__(16) uint8_t vl0[VSTAGE];
   __shared__ __align__(16) uint8_t vl1[VSTAGE];
-  __shared__ __align__(16) uint8_t vl2[VSTAGE];
+  __shared__ __align__(16) uint8_t vl2[NST > 2 ? VSTAGE : 16];
   auto kstage = [&](auto st_tag) __attribute__((always_inline)) -> uint8_t* {
     constexpr int ST = decltype(st_tag)::value;
     if constexpr (ST == 0) return kl0;
@@ -569,7 +577,8 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   // 64 their swizzles agree, so one lane offset serves them all and the row
   // step goes into the scalar offset (fewer vector registers held across the
   // sweep).  Otherwise each row keeps its own lane offset.
-  constexpr bool ONE_VOFF = (8 * NWAVES) % 64 == 0;
+  constexpr int K_SWZ_PERIOD = D != 128 ? 1 : (BITS == 8 ? 32 : 64);   // rows (see swz_k)
+  constexpr bool ONE_VOFF = (8 * NWAVES) % K_SWZ_PERIOD == 0 && (8 * NWAVES) % 8 == 0;
   constexpr int NKV = ONE_VOFF ? 1 : NK_DMA;
   constexpr int NVV = ONE_VOFF ? 1 : NV_DMA;
   // With one lane offset per operand the offsets are recomputed at every
@@ -672,7 +681,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   __syncthreads();
   // the rings fill ahead of the sweep
   if (n_tiles > 1) { issue_k(1, kl1); issue_v(1, vl1); }
-  if (n_tiles > 2) { issue_k(2, kl2); issue_v(2, vl2); }
+  if (NST > 2 && n_tiles > 2) { issue_k(2, kl2); issue_v(2, vl2); }
   {
     v4f acc[NSUB][8];
 #pragma unroll
@@ -996,43 +1005,68 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
 
-  // Tile after tile, one barrier per tile; two waves per SIMD overlap one's
-  // vector epilogue with the other's products.  Tile t+1 must have landed
-  // by the end of step t (t+2 may still be in flight); after the barrier the
-  // stages of tile t take tile t+3.  FP8 issues the loads of a tile in two
-  // halves (measured a little faster; a little slower for FP6/FP4): K^ tile
-  // t+3 right after the barrier that ends step t, V^T tile t+2 after the
-  // score products of step t (into the stage of tile t-1, free since the
-  // barrier that ended step t-1).  Either way the loads of tile t+1 precede
-  // those of tile t+2 in issue order, so the count kept in flight stays one
-  // tile.
-  constexpr bool SPLIT = BITS == 8;
-  auto step = [&](int t, auto st_tag) __attribute__((always_inline)) {
-    constexpr int P = decltype(st_tag)::value;
-    uint8_t* kb = kstage(st_tag);
-    uint8_t* vb = vstage(st_tag);
-    if (t < n_clean) qk_into(kb, t * KT, std::false_type{});
-    else qk_into(kb, t * KT, std::true_type{});
-    if (SPLIT && t >= 1 && t + 2 < n_tiles)
-      issue_v(t + 2, vstage(std::integral_constant<int, (P + 2) % 3>{}));
+  if constexpr (NST == 2) {
+    // Two stages: tile t+1 lands while tile t is read; after the barrier
+    // that ends step t its stages take tile t+2.
+    auto step2 = [&](int t, auto st_tag) __attribute__((always_inline)) {
+      uint8_t* kb = kstage(st_tag);
+      uint8_t* vb = vstage(st_tag);
+      if (t < n_clean) qk_into(kb, t * KT, std::false_type{});
+      else qk_into(kb, t * KT, std::true_type{});
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) epi_sub(s);
-    // keep the P V fragment reads below the epilogue: hoisted above it they
-    // would hold registers through it
-    if constexpr (PIPE > 0) __builtin_amdgcn_sched_barrier(0);
-    pv_step(vb);
-    if (t + 2 < n_tiles) wait_dma_keep<DMA_K + DMA_V>();
-    else wait_dma();
-    ring_barrier();
-    if (t + 3 < n_tiles) {
-      issue_k(t + 3, kb);
-      if (!SPLIT) issue_v(t + 3, vb);
+      for (int s = 0; s < NSUB; ++s) epi_sub(s);
+      if constexpr (PIPE > 0) __builtin_amdgcn_sched_barrier(0);
+      pv_step(vb);
+      wait_dma();
+      ring_barrier();
+      if (t + 2 < n_tiles) {
+        issue_k(t + 2, kb);
+        issue_v(t + 2, vb);
+      }
+    };
+    for (int t = 0; t < n_tiles; t += 2) {
+      step2(t, I0{});
+      if (t + 1 < n_tiles) step2(t + 1, I1{});
     }
-  };
-  for (int t = 0; t < n_tiles; t += 3) {
-    step(t, I0{});
-    if (t + 1 < n_tiles) step(t + 1, I1{});
-    if (t + 2 < n_tiles) step(t + 2, I2{});
+  } else {
+  // Tile after tile, one barrier per tile; two waves per SIMD overlap one's
+    // vector epilogue with the other's products.  Tile t+1 must have landed
+    // by the end of step t (t+2 may still be in flight); after the barrier the
+    // stages of tile t take tile t+3.  FP8 issues the loads of a tile in two
+    // halves (measured a little faster; a little slower for FP6/FP4): K^ tile
+    // t+3 right after the barrier that ends step t, V^T tile t+2 after the
+    // score products of step t (into the stage of tile t-1, free since the
+    // barrier that ended step t-1).  Either way the loads of tile t+1 precede
+    // those of tile t+2 in issue order, so the count kept in flight stays one
+    // tile.
+    constexpr bool SPLIT = BITS == 8;
+    auto step = [&](int t, auto st_tag) __attribute__((always_inline)) {
+      constexpr int P = decltype(st_tag)::value;
+      uint8_t* kb = kstage(st_tag);
+      uint8_t* vb = vstage(st_tag);
+      if (t < n_clean) qk_into(kb, t * KT, std::false_type{});
+      else qk_into(kb, t * KT, std::true_type{});
+      if (SPLIT && t >= 1 && t + 2 < n_tiles)
+        issue_v(t + 2, vstage(std::integral_constant<int, (P + 2) % 3>{}));
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) epi_sub(s);
+      // keep the P V fragment reads below the epilogue: hoisted above it they
+      // would hold registers through it
+      if constexpr (PIPE > 0) __builtin_amdgcn_sched_barrier(0);
+      pv_step(vb);
+      if (t + 2 < n_tiles) wait_dma_keep<DMA_K + DMA_V>();
+      else wait_dma();
+      ring_barrier();
+      if (t + 3 < n_tiles) {
+        issue_k(t + 3, kb);
+        if (!SPLIT) issue_v(t + 3, vb);
+      }
+    };
+    for (int t = 0; t < n_tiles; t += 3) {
+      step(t, I0{});
+      if (t + 1 < n_tiles) step(t + 1, I1{});
+      if (t + 2 < n_tiles) step(t + 2, I2{});
+    }
   }
 
   // row offsets in binades (the oracle's kappa); rows beyond EXT come out
@@ -1284,9 +1318,11 @@ template <int F> struct Nsub;
 template <> struct Nsub<FMT_E4M3> { static constexpr int value = FSA_NSUB8; };
 template <> struct Nsub<FMT_E2M3> { static constexpr int value = FSA_NSUB6; };
 template <> struct Nsub<FMT_E2M1> { static constexpr int value = FSA_NSUB4; };
-// Waves per workgroup: 8 puts two waves on each SIMD, so one wave's vector
-// epilogue runs while the other's MFMAs occupy the matrix core; FP8's larger
-// operands leave room for only one wave per SIMD.
+// Waves per workgroup.  Four (one per SIMD) on two-stage rings lets two
+// workgroups share a CU, two waves per SIMD whose barriers are independent
+// (measured: +11 % for E2M1, +1-2 % for the others over eight waves of one
+// workgroup on three-stage rings, which the code keeps as an option).  Every
+// kernel is built for two waves per SIMD (at most 256 registers each).
 template <int F> struct Nwaves;
 template <> struct Nwaves<FMT_E4M3> { static constexpr int value = FSA_NW8; };
 template <> struct Nwaves<FMT_E2M3> { static constexpr int value = FSA_NW6; };
