@@ -98,6 +98,9 @@ int validate_attn(const void* q, const void* k, const void* v, void* out, int B,
   for (const void* p : {q, k, v, static_cast<const void*>(out)})
     if (reinterpret_cast<uintptr_t>(p) & 15) return FSA_ERR_INVALID_ARG;   // 16-byte vector loads
   if (D != 64 && D != 128) return FSA_ERR_UNSUPPORTED;
+  // one head's bf16 rows (and its quantised slabs) are addressed with
+  // 32-bit buffer offsets
+  if (round_up(S, 128) * D * 2 >= ((int64_t)1 << 31)) return FSA_ERR_UNSUPPORTED;
   return FSA_OK;
 }
 
@@ -276,6 +279,11 @@ int fsa_attention_bf16_ref(const void* q, const void* k, const void* v, void* ou
   a.out = static_cast<uint16_t*>(out);
   a.BH = B * H;
   a.S = S;
+  a.s_alloc = (int)round_up(S, fsa::BF16_KEY_TILE);
+  uint8_t* ws = nullptr;
+  const int wst = workspace((size_t)a.BH * D * a.s_alloc * 2, &ws);
+  if (wst != FSA_OK) return wst;
+  a.vt = reinterpret_cast<uint16_t*>(ws);
   a.scale_log2 = (float)(1.0 / std::log(2.0) / std::sqrt((double)D));
   return fsa::launch_bf16_fa(a, D, causal, static_cast<hipStream_t>(stream)) == hipSuccess
              ? FSA_OK

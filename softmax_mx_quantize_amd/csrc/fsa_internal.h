@@ -68,10 +68,13 @@ hipError_t launch_fsa_fwd(const AttnArgs& a, int fmt, int D, int causal, hipStre
 hipError_t launch_fsa_fwd_e4m3(const AttnArgs& a, int D, int causal, hipStream_t stream);
 
 // Plain BF16 flash attention.
+constexpr int BF16_KEY_TILE = 64;
 struct Bf16Args {
   const uint16_t* q; const uint16_t* k; const uint16_t* v;
   uint16_t* out;
+  uint16_t* vt;                  // workspace: V^T [BH][D][s_alloc]
   int BH, S;
+  int s_alloc;                   // S rounded up to BF16_KEY_TILE
   float scale_log2;              // log2(e) / sqrt(D)
 };
 
