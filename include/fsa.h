@@ -105,7 +105,9 @@ int fsa_quantize_mx(const void* x_bf16, void* codes, void* scales_e8m0,
  * scores exceed the frozen max, applied as an exact power-of-two rescale.
  * Errors: FSA_ERR_INVALID_ARG (null pointers, non-positive sizes, B*H*S*D
  * beyond 2^40, unknown fmt, causal not 0/1), FSA_ERR_UNSUPPORTED (D not
- * 64/128), FSA_ERR_NO_MEMORY (workspace), FSA_ERR_HIP (launch).
+ * 64/128, or one head's bf16 rows, S rounded up to 128 times 2*D bytes,
+ * reaching 2^31: the kernels address a head with 32-bit buffer offsets),
+ * FSA_ERR_NO_MEMORY (workspace), FSA_ERR_HIP (launch).
  */
 int fsa_attention_fwd(const void* q, const void* k, const void* v, void* out,
                       int B, int H, int S, int D, int fmt, int causal, void* stream);
@@ -117,6 +119,8 @@ int fsa_attention_fwd(const void* q, const void* k, const void* v, void* out,
  * efficient quantized attention, summary; the "Softmax (Vector)" path of the
  * "How it works" figure): bf16 matrix-core products with fp32 accumulation,
  * exact exponential, online row max and rescaling on the vector units.
+ * V is first transposed into the library workspace (B*H*D*S' bf16, S'
+ * being S rounded up to 64), which it shares with fsa_attention_fwd.
  * Same tensor layout and errors as fsa_attention_fwd (no fmt).
  */
 int fsa_attention_bf16_ref(const void* q, const void* k, const void* v, void* out,

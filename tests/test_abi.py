@@ -59,6 +59,11 @@ def test_strerror_and_argument_validation_without_gpu():
     # unsupported head dim
     assert lib.fsa_attention_fwd(fake, fake, fake, fake + 4096, 1, 1, 8, 96, 0, 0, None) == -2
     assert lib.fsa_attention_bf16_ref(fake, fake, fake, fake + 4096, 1, 1, 8, 80, 0, None) == -2
+    # a head beyond 32-bit buffer offsets: 2^23 keys of 256 bytes
+    assert lib.fsa_attention_fwd(fake, fake + 4096, fake + 8192, fake + 12288, 1, 1, 1 << 23, 128, 0, 0,
+                                 None) == -2
+    assert lib.fsa_attention_bf16_ref(fake, fake + 4096, fake + 8192, fake + 12288, 1, 1, 1 << 23, 128, 0,
+                                      None) == -2
     # bad per-head format in the options
     opt = fsa.Options()
     hf = (ctypes.c_int * 2)(0, 9)
