@@ -186,14 +186,24 @@ __device__ __forceinline__ int kpos(int g, int p) {
   return 32 * g + p;
 }
 
-// XOR swizzles (16-byte chunk index within a 128-byte LDS row).
+// XOR swizzles (16-byte chunk index within a 128-byte LDS row), so that
+// the lanes the LDS serves together read distinct banks (64 banks of 4
+// bytes: two rows per bank line, the row's parity picks the half).  FP8 and
+// FP4 fragments are 16-byte reads, served 8 lanes at a time: the 8 rows of
+// lanes r = 0..7 need distinct chunks within each parity.  FP6 fragments
+// are three 8-byte reads, served 16 or more lanes at a time: all 16 rows of
+// a lane group need distinct 8-byte slots, i.e. distinct chunks within each
+// parity over 8 rows (a lane's score-product rows are 32 (r/4) + r%4 + 4j,
+// its output-product rows r + 16 dt).
 template <int F, int D>
 __device__ __forceinline__ int swz_k(int row) {
   if (D != 128) return 0;
+  if (Fmt<F>::bits == 6) return ((row >> 1) & 1) | (((row >> 5) & 3) << 1);
   const int hi = Fmt<F>::bits == 8 ? (row >> 4) & 1 : (row >> 5) & 1;
   return (row & 3) | (hi << 2);
 }
-__device__ __forceinline__ int swz_v(int row) { return row & 7; }
+template <int F>
+__device__ __forceinline__ int swz_v(int row) { return Fmt<F>::bits == 6 ? (row >> 1) & 7 : row & 7; }
 
 // A lane's 32 operand elements along a 128-byte swizzled LDS row.  `len` is
 // the number of valid K elements of the row (elements past it are zero).
@@ -536,12 +546,15 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   const __amdgpu_buffer_rsrc_t vs_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)vs, (short)0, D * vs_row, 0x00020000);
   // The rows a wave fills are 8 * NWAVES apart; when that is a multiple of
-  // 64 their swizzles agree, so one lane offset serves them all and the row
-  // step goes into the scalar offset (fewer vector registers held across the
-  // sweep).  Otherwise each row keeps its own lane offset.
-  constexpr int K_SWZ_PERIOD = D != 128 ? 1 : (BITS == 8 ? 32 : 64);   // rows (see swz_k)
-  constexpr bool ONE_VOFF = (8 * NWAVES) % K_SWZ_PERIOD == 0 && (8 * NWAVES) % 8 == 0;
-  constexpr int NKV = ONE_VOFF ? 1 : NK_DMA;
+  // the swizzle's period their swizzles agree, so one lane offset serves
+  // them all and the row step goes into the scalar offset (fewer vector
+  // registers held across the sweep).  Otherwise each row keeps its own lane
+  // offset.
+  constexpr int K_SWZ_PERIOD = D != 128 ? 1 : (BITS == 8 ? 32 : (BITS == 6 ? 128 : 64));   // rows
+  constexpr int V_SWZ_PERIOD = BITS == 6 ? 16 : 8;
+  constexpr bool ONE_KOFF = (8 * NWAVES) % K_SWZ_PERIOD == 0;
+  constexpr bool ONE_VOFF = (8 * NWAVES) % V_SWZ_PERIOD == 0;
+  constexpr int NKV = ONE_KOFF ? 1 : NK_DMA;
   constexpr int NVV = ONE_VOFF ? 1 : NV_DMA;
   // With one lane offset per operand the offsets are recomputed at every
   // issue from an opaque lane index (a few vector instructions) instead of
@@ -554,12 +567,12 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   };
   auto v_lane_off = [&](int k, int ln) __attribute__((always_inline)) {
     const int row = (wave + NWAVES * k) * 8 + (ln >> 3);
-    const int c = (ln & 7) ^ swz_v(row);
+    const int c = (ln & 7) ^ swz_v<F>(row);
     return row * (int)v_row + (c < VCH_VALID ? c : 0) * 16;
   };
   auto opaque_lane = [&]() __attribute__((always_inline)) {
     int l = lane;
-    if constexpr (ONE_VOFF) asm volatile("" : "+v"(l));
+    if constexpr (ONE_KOFF || ONE_VOFF) asm volatile("" : "+v"(l));
     return l;
   };
   int k_voff[NKV], v_voff[NVV];
@@ -584,14 +597,14 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   auto issue_k = [&](int t, uint8_t* base) __attribute__((always_inline)) {
     const int ln = opaque_lane();
     const int wv = opaque_wave();
-    const int kv0 = ONE_VOFF ? k_lane_off(0, ln) : 0;
+    const int kv0 = ONE_KOFF ? k_lane_off(0, ln) : 0;
     const uint32_t lb = lds_addr(base);
     const int ks_soff = wv < NKS ? wv * 256 : 0;
 #pragma unroll
     for (int k = 0; k < NK_DMA; ++k)
-      dma_lds16(k_rsrc, lb + (wv + NWAVES * k) * 1024, ONE_VOFF ? kv0 : k_voff[k],
-                t * KT * RB + (ONE_VOFF ? k * NWAVES * 8 * RB : 0));
-    dma_lds4(ks_rsrc, lb + K_BYTES + ks_soff, ONE_VOFF ? ln * 4 : s_voff, t * KS_BYTES + ks_soff);
+      dma_lds16(k_rsrc, lb + (wv + NWAVES * k) * 1024, ONE_KOFF ? kv0 : k_voff[k],
+                t * KT * RB + (ONE_KOFF ? k * NWAVES * 8 * RB : 0));
+    dma_lds4(ks_rsrc, lb + K_BYTES + ks_soff, ONE_KOFF ? ln * 4 : s_voff, t * KS_BYTES + ks_soff);
   };
   auto issue_v = [&](int t, uint8_t* base) __attribute__((always_inline)) {
     const int ln = opaque_lane();
@@ -729,7 +742,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
   // does not depend on j; V^T row 16dt + r likewise.
   const int kk0 = BITS == 8 ? 16 * (r >> 2) + (r & 3) : 32 * (r >> 2) + (r & 3);
   const int ksw = swz_k<F, D>(kk0);
-  const int vsw = swz_v(r);
+  const int vsw = swz_v<F>(r);
   constexpr int NOFF = BITS == 8 ? 2 : (BITS == 6 ? 3 : 1);   // row pieces per operand
   int k_off[NOFF], v_off[NOFF];
 #pragma unroll
