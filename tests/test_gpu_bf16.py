@@ -45,3 +45,25 @@ def test_bf16_full_size_sampled():
         qh, kh, vh = (W.bf16_bits_to_f64(x[0, h]) for x in (q, k, v))
         ex = O.exact_attention(qh, kh, vh, False, rows)
         assert rel_l2(g[0, h, rows], ex) <= TOL
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_growing_scores(causal):
+    """Scores that climb by about 100 binades along the keys (about 6 per
+    64-key tile) move the kept row max past its 8-binade margin every tile
+    or two, which exercises the rescale of the output and the row sum."""
+    S, D = 1030, 128
+    announce("bf16 growing scores", causal)
+    rng = np.random.default_rng(31)
+    u = rng.standard_normal(D)
+    u /= np.linalg.norm(u)
+    q = np.tile(20.0 * u, (S, 1)) + 0.1 * rng.standard_normal((S, D))
+    ramp = 40.0 * np.arange(S) / S
+    k = ramp[:, None] * u[None, :] + 0.1 * rng.standard_normal((S, D))
+    v = rng.standard_normal((S, D))
+    q, k, v = (W.f32_to_bf16_bits(x.astype(np.float32))[None, None] for x in (q, k, v))
+    g = _run(q, k, v, causal)
+    qh, kh, vh = (W.bf16_bits_to_f64(x[0, 0]) for x in (q, k, v))
+    ex = O.exact_attention(qh, kh, vh, causal)
+    assert np.all(np.isfinite(g))
+    assert rel_l2(g[0, 0], ex) <= TOL
