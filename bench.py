@@ -40,6 +40,7 @@ METRIC = "attention fwd TFLOP/s and % of MX MFMA peak (MXFP8/6/4, S=16K, D=128)"
 KERNEL_SOURCES = ("softmax_mx_quantize_amd/csrc/fsa_fwd_impl.h",
                   "softmax_mx_quantize_amd/csrc/fsa_fwd.hip",
                   "softmax_mx_quantize_amd/csrc/fsa_fwd_e4m3.hip",
+                  "softmax_mx_quantize_amd/csrc/fsa_fwd32.hip",
                   "softmax_mx_quantize_amd/csrc/fsa_device.h",
                   "softmax_mx_quantize_amd/csrc/lds_dma.h")
 

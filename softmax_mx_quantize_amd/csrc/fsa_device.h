@@ -168,7 +168,9 @@ template <bool CLAMP> struct Pack32<FMT_E2M1, CLAMP> {
                                              float = 1.0f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint32_t r = 0;
+      // the four conversions write the four bytes of r, so its starting
+      // value does not matter (one that dies here costs no move)
+      uint32_t r = __float_as_uint(y[8 * i + 1]);
       r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * i + 0], y[8 * i + 1], s_lo, 0);
       r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * i + 2], y[8 * i + 3], s_lo, 1);
       r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * i + 4], y[8 * i + 5], s_lo, 2);

@@ -1089,8 +1089,9 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NWAVES * 64, NWAVES *
 // (accumulator start and block shifts re-based, no in-loop clamp), reading
 // the frozen max and kappa the main kernel stored, and overwrites their
 // outputs.  Rows within EXT come out as the main kernel left them (the
-// re-based sums are the same up to the common power-of-two factor).
-template <int F, int D, bool CAUSAL>
+// re-based sums are the same up to the common power-of-two factor).  L32:
+// the scales are in the *_TILES32 layouts of the 32x32x64 kernel.
+template <int F, int D, bool CAUSAL, bool L32>
 __device__ __forceinline__ void fallback_group(const AttnArgs& a, int64_t grp) {
   constexpr int NSUB = 2;
   constexpr int BITS = Fmt<F>::bits;
@@ -1131,6 +1132,10 @@ __device__ __forceinline__ void fallback_group(const AttnArgs& a, int64_t grp) {
   const uint8_t* vc = a.vc + wi * (int64_t)D * v_row;
   const int vs_row = a.sk_alloc / 32;
   const uint8_t* vs = a.vs + wi * (int64_t)D * vs_row;
+  // scale byte of tile key kk (read by lane (g, r) as slice j) and D block g
+  auto ks_byte = [&](int kk, int j) __attribute__((always_inline)) {
+    return L32 ? key_tile32_byte(kk, g, D) : (r * NDB + g) * 8 + j;
+  };
 
   opv<F> qf[NSUB];
   int qsc[NSUB];
@@ -1168,7 +1173,7 @@ __device__ __forceinline__ void fallback_group(const AttnArgs& a, int64_t grp) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int kk = kpos<F>(r >> 2, 4 * j + (r & 3));
-        const int sc = g < NDB ? (int)ks[(int64_t)t * KT * NDB + (r * NDB + g) * 8 + j] : 127;
+        const int sc = g < NDB ? (int)ks[(int64_t)t * KT * NDB + ks_byte(kk, j)] : 127;
         const opv<F> kf = global_operand<F>(kc + (int64_t)(key0 + kk) * RB, g, D);
 #pragma unroll
         for (int s = 0; s < NSUB; ++s) {
@@ -1202,7 +1207,7 @@ __device__ __forceinline__ void fallback_group(const AttnArgs& a, int64_t grp) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int kk = kpos<F>(r >> 2, 4 * j + (r & 3));
-      const int sc = g < NDB ? (int)ks[(int64_t)t * KT * NDB + (r * NDB + g) * 8 + j] : 127;
+      const int sc = g < NDB ? (int)ks[(int64_t)t * KT * NDB + ks_byte(kk, j)] : 127;
       const opv<F> kf = global_operand<F>(kc + (int64_t)(key0 + kk) * RB, g, D);
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) acc[s][j] = mfma<F>(kf, qf[s], mk[s], sc, qsc[s]);
@@ -1250,7 +1255,7 @@ __device__ __forceinline__ void fallback_group(const AttnArgs& a, int64_t grp) {
     for (int dt = 0; dt < NDT; ++dt) {
       const int d = 16 * dt + r;
       const opv<F> vf = global_operand<F>(vc + d * v_row + (int64_t)t * VRB, g, KT);
-      const int vsc = (int)vs[(int64_t)t * 4 * D + (r * 4 + g) * NDT + dt];
+      const int vsc = (int)vs[(int64_t)t * 4 * D + (L32 ? dim_tile32_byte(d, g, D) : (r * 4 + g) * NDT + dt)];
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) O[s][dt] = mfma<F>(vf, pw[s], O[s][dt], vsc, psc[s]);
     }
@@ -1277,12 +1282,13 @@ __device__ __forceinline__ void fallback_group(const AttnArgs& a, int64_t grp) {
 // Grid-stride over groups of 32 query rows; a call whose main kernel found
 // no row beyond EXT binades (flag not stamped with this call's id) exits
 // after one load.
-template <int F, int D, bool CAUSAL>
+template <int F, int D, bool CAUSAL, bool L32>
 __global__ void __launch_bounds__(64) fsa_fallback_kernel(AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   if (*a.fb_flag != a.call_id) return;
   const int64_t n_groups = (int64_t)(a.S + 31) / 32 * a.B * a.hrun;
-  for (int64_t grp = blockIdx.x; grp < n_groups; grp += gridDim.x) fallback_group<F, D, CAUSAL>(a, grp);
+  for (int64_t grp = blockIdx.x; grp < n_groups; grp += gridDim.x)
+    fallback_group<F, D, CAUSAL, L32>(a, grp);
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -1312,7 +1318,7 @@ hipError_t launch3(const AttnArgs& a, hipStream_t stream) {
   dim3 grid((n_items + 7) / 8 * 8);
   hipLaunchKernelGGL((fsa_fwd_kernel<F, D, CAUSAL, NSUB, NWAVES>), grid, dim3(NWAVES * 64), 0, stream, a);
   const int n_groups = (a.S + 31) / 32 * a.B * a.hrun;
-  hipLaunchKernelGGL((fsa_fallback_kernel<F, D, CAUSAL>), dim3(n_groups < 1024 ? n_groups : 1024),
+  hipLaunchKernelGGL((fsa_fallback_kernel<F, D, CAUSAL, false>), dim3(n_groups < 1024 ? n_groups : 1024),
                      dim3(64), 0, stream, a);
   return hipGetLastError();
 }

@@ -77,6 +77,16 @@ __device__ __forceinline__ void quantize_block(const QuantArgs& a, float (&v)[32
     const int ndt = (int)(a.out_rows / 16);
     so = bt * a.out_rows * a.nb_out + (b >> 2) * 4 * a.out_rows +
          ((d & 15) * 4 + (int)(b & 3)) * ndt + (d >> 4);
+  } else if (a.scale_layout == SCALES_KEY_TILES32) {
+    const int nb = (int)a.nb_out;
+    const int64_t bt = o / a.out_rows;
+    const int64_t row = o - bt * a.out_rows;
+    so = bt * a.out_rows * nb + (row >> 7) * 128 * nb + key_tile32_byte((int)(row & 127), (int)b, 32 * nb);
+  } else if (a.scale_layout == SCALES_DIM_TILES32) {
+    const int64_t bt = o / a.out_rows;
+    const int d = (int)(o - bt * a.out_rows);
+    so = bt * a.out_rows * a.nb_out + (b >> 2) * 4 * a.out_rows +
+         dim_tile32_byte(d, (int)(b & 3), (int)a.out_rows);
   }
   a.scales[so] = sbyte;
 }
