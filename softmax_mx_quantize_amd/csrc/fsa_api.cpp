@@ -29,15 +29,16 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 // fsa_fmt -> kernel format index
 int kern_fmt(int fmt) { return fmt == FSA_MXFP8_E4M3 ? 0 : (fmt == FSA_MXFP6_E2M3 ? 1 : 2); }
 
-// E2M3 and E2M1 run on the 32x32x64 kernel (scales in its tile layouts);
-// FSA_MMA16=1 in the environment selects the 16x16x128 kernel instead, for
+// Every format runs on the 32x32x64 kernel (scales in its tile layouts);
+// FSA_MMA16=1 in the environment selects the 16x16x128 kernels instead, for
 // comparisons.
 bool use_mma32(int fmt) {
   static const bool force16 = [] {
     const char* e = std::getenv("FSA_MMA16");
     return e && e[0] == '1';
   }();
-  return fmt != FSA_MXFP8_E4M3 && !force16;
+  (void)fmt;
+  return !force16;
 }
 
 struct Workspace {

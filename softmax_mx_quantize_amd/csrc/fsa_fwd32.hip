@@ -1,5 +1,5 @@
-// Fused-Softmax attention forward for MXFP6 (E2M3) and MXFP4 (E2M1) operands
-// on the 32x32x64 scaled MFMA of gfx950.
+// Fused-Softmax attention forward for MXFP8 (E4M3), MXFP6 (E2M3) and MXFP4
+// (E2M1) operands on the 32x32x64 scaled MFMA of gfx950.
 //
 // It computes what the kernels of fsa_fwd_impl.h compute (same frozen max,
 // same score product with the exponential's linear part folded in, same
@@ -53,13 +53,20 @@ __device__ v16f mfma32_v6(v6i a, v6i b, v16f c, int cbsz, int blgp, int opsel_a,
 __device__ v16f mfma32_v4(v4i a, v4i b, v16f c, int cbsz, int blgp, int opsel_a, int sa,
                           int opsel_b, int sb)
     __asm("llvm.amdgcn.mfma.scale.f32.32x32x64.f8f6f4.v4i32.v4i32");
+// FP4 A operand with an FP8 B operand (row sums of FP8 probabilities).
+__device__ v16f mfma32_v4_v8(v4i a, v8i b, v16f c, int cbsz, int blgp, int opsel_a, int sa,
+                             int opsel_b, int sb)
+    __asm("llvm.amdgcn.mfma.scale.f32.32x32x64.f8f6f4.v4i32.v8i32");
 
 namespace {
 
 template <int F, int OA>
 __device__ __forceinline__ v16f mma32(const opv<F>& a, const opv<F>& b, const v16f& c, int sa,
                                       int sb) {
-  if constexpr (Fmt<F>::bits == 6)
+  if constexpr (Fmt<F>::bits == 8)
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, Fmt<F>::mfma, Fmt<F>::mfma, OA,
+                                                           sa, 0, sb);
+  else if constexpr (Fmt<F>::bits == 6)
     return mfma32_v6(a, b, c, Fmt<F>::mfma, Fmt<F>::mfma, OA, sa, 0, sb);
   else
     return mfma32_v4(a, b, c, Fmt<F>::mfma, Fmt<F>::mfma, OA, sa, 0, sb);
@@ -83,7 +90,69 @@ __device__ __forceinline__ v16f mma32_sel(const opv<F>& a, const opv<F>& b, cons
 // each parity.  Score product: lanes n = 8j + 4x + k read key rows
 // 32x + 16b + 4j + k (+64u): rows differing in bits 0, 1, 2 and 5.  P V
 // product: lanes n read rows n (+32 db): bits 0-3.
-__device__ __forceinline__ int swz_k32(int row) { return ((row >> 1) & 3) | (((row >> 5) & 1) << 2); }
+// FP8 operands are two 16-byte reads per lane; its score rows are
+// 32b + 16x + 4j + k, differing in bits 0-4.
+template <int BITS>
+__device__ __forceinline__ int swz_k32(int row) {
+  if (BITS == 8) return ((row >> 1) & 1) | (((row >> 4) & 1) << 1) | (((row >> 2) & 1) << 2);
+  return ((row >> 1) & 3) | (((row >> 5) & 1) << 2);
+}
+
+// The lane's Q' operand for 64-wide D chunk c of the FP8 score product:
+// elements [64c + 16h, +16) and [64c + 32 + 16h, +16), i.e. half of D block
+// 2c and half of block 2c+1; the other halves are in the lane 32 apart.  Same
+// rule as the quantiser (OCP floor scale, RNE, saturation, NaN/Inf blocks
+// get scale 0xFF and zero codes), Q' = fp32(q * mult), 2^23 raised onto the
+// E8M0 byte.  `sc` is the byte of block 2c + h, which this lane supplies.
+template <int D>
+__device__ __forceinline__ v8i q_operand32_e4m3(const uint16_t* row, float mult, int c, int hh,
+                                               int& sc) {
+  float v[32];
+  bool bad_lo = false, bad_hi = false;
+#pragma unroll
+  for (int ch = 0; ch < 4; ++ch) {
+    const int col = 64 * c + 16 * hh + (ch < 2 ? 8 * ch : 32 + 8 * (ch - 2));
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (row != nullptr && col < D) w = *reinterpret_cast<const uint4*>(row + col);
+    const uint32_t hw[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = hw[e] & 0xFFFF, hi = hw[e] >> 16;
+      const bool nan_inf = ((lo & 0x7F80) == 0x7F80) | ((hi & 0x7F80) == 0x7F80);
+      if (ch < 2) bad_lo |= nan_inf; else bad_hi |= nan_inf;
+      v[8 * ch + 2 * e] = bf16_bits_to_float(lo) * mult;
+      v[8 * ch + 2 * e + 1] = bf16_bits_to_float(hi) * mult;
+    }
+  }
+  float a_lo = 0.0f, a_hi = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    a_lo = __builtin_fmaxf(a_lo, __builtin_fabsf(v[k]));
+    a_hi = __builtin_fmaxf(a_hi, __builtin_fabsf(v[16 + k]));
+  }
+  a_lo = __builtin_fmaxf(a_lo, __shfl_xor(a_lo, 32));
+  a_hi = __builtin_fmaxf(a_hi, __shfl_xor(a_hi, 32));
+  bad_lo |= __shfl_xor((int)bad_lo, 32) != 0;
+  bad_hi |= __shfl_xor((int)bad_hi, 32) != 0;
+  auto scale_exp = [](float amax) {
+    int X = amax > 0.0f ? floor_log2(amax) - Fmt<FMT_E4M3>::emax : -127;
+    return X < -127 ? -127 : (X > 127 ? 127 : X);
+  };
+  const int x_lo = scale_exp(a_lo), x_hi = scale_exp(a_hi);
+  float y[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) y[k] = __builtin_ldexpf(v[k], -(k < 16 ? x_lo : x_hi));
+  uint32_t w[8];
+  Pack32<FMT_E4M3, true>::run(y, w);
+  if (bad_lo) { for (int i = 0; i < 4; ++i) w[i] = 0; }
+  if (bad_hi) { for (int i = 4; i < 8; ++i) w[i] = 0; }
+  auto raised = [](int x, bool bad) { return bad ? 255 : min(x + 127 + 23, 254); };
+  sc = hh ? raised(x_hi, bad_hi) : raised(x_lo, bad_lo);
+  v8i o;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = (int)w[i];
+  return o;
+}
 template <int BITS>
 __device__ __forceinline__ int swz_v32(int row) { return BITS == 6 ? (row >> 1) & 7 : row & 7; }
 
@@ -95,10 +164,12 @@ fsa_fwd32_kernel(AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer-resource types exist only in the device pass
   constexpr int NWAVES = 4;
   constexpr int BITS = Fmt<F>::bits;
-  static_assert(BITS == 6 || BITS == 4, "FP6 / FP4 operands only");
+
   static_assert(D == 64 || D == 128, "D is 64 or 128");
   constexpr int MB = Fmt<F>::mbits;
-  constexpr int PL = Fmt<F>::emax;           // placement binade of P~ blocks
+  // placement binade of P~ blocks (E4M3: one below the top, whose largest
+  // code is NaN and whose values clip at 448)
+  constexpr int PL = F == FMT_E4M3 ? Fmt<F>::emax - 1 : Fmt<F>::emax;
   constexpr int CAP = 127 - PL;
   constexpr int RB = D * BITS / 8;           // bytes per K^ row (global)
   constexpr int RS = 128;                    // bytes per K^ / V^T row (LDS)
@@ -115,12 +186,13 @@ fsa_fwd32_kernel(AttnArgs a) {
   constexpr int NBK = KS_BYTES / 64;         // K^ scale bytes per lane and tile
   constexpr int NBV = VS_BYTES / 64;         // V^T scale bytes per lane and tile
   constexpr int XLO = 127 + REF - CAP, XHI = 127 + REF + EXT;
-  // LDS rows.  FP4: logical chunk c is bytes [16c, 16c+16) of the row
-  // (one MX block).  FP6: each 24-byte block b takes two chunks, 2b (its
-  // bytes 0-15) and 2b+1 (bytes 16-23, the upper half unused), so that a
-  // lane's operand is one 16-byte and one 8-byte read into consecutive
-  // registers.
-  constexpr int NPC = BITS == 6 ? 2 : 1;     // LDS reads per operand
+  // LDS rows.  FP8 and FP4: logical chunk c is bytes [16c, 16c+16) of the
+  // row.  FP6: each 24-byte block b takes two chunks, 2b (its bytes 0-15)
+  // and 2b+1 (bytes 16-23, the upper half unused), so that a lane's operand
+  // is one 16-byte and one 8-byte read into consecutive registers.
+  constexpr int NPC = BITS == 4 ? 1 : 2;     // LDS reads per operand
+  // Score rows: block b of a chunk steps KB rows, the A row's x bit KX rows.
+  constexpr int KB = BITS == 8 ? 32 : 16, KX = BITS == 8 ? 16 : 32;
 
   // Two-stage rings (two workgroups share a CU); one LDS object per stage,
   // always addressed through a compile-time stage index so that the
@@ -198,14 +270,14 @@ fsa_fwd32_kernel(AttnArgs a) {
   // (chunks past the row's data re-read its first bytes).
   auto chunk_src = [](int c, int nblk) __attribute__((always_inline)) {
     if constexpr (BITS == 6) return (c >> 1) < nblk ? 24 * (c >> 1) + 16 * (c & 1) : 0;
-    else return c < nblk ? 16 * c : 0;
+    else return c < nblk * BITS / 4 ? 16 * c : 0;
   };
   int koff_e, koff_o, voff;
   {
-    const int c_even = (lane & 7) ^ ((lane >> 4) & 3);
-    koff_e = (lane >> 3) * RB + chunk_src(c_even, NDB);
-    koff_o = (lane >> 3) * RB + chunk_src(c_even ^ 4, NDB);
-    const int c = (lane & 7) ^ swz_v32<BITS>(8 * wave + (lane >> 3));
+    const int r_e = 8 * wave + (lane >> 3), r_o = r_e + 8 * NWAVES;   // rows of even / odd k
+    koff_e = (lane >> 3) * RB + chunk_src((lane & 7) ^ swz_k32<BITS>(r_e), NDB);
+    koff_o = (lane >> 3) * RB + chunk_src((lane & 7) ^ swz_k32<BITS>(r_o), NDB);
+    const int c = (lane & 7) ^ swz_v32<BITS>(r_e);
     voff = (lane >> 3) * (int)v_row + chunk_src(c, 4);
   }
   const int s_voff = lane * 4;
@@ -239,34 +311,46 @@ fsa_fwd32_kernel(AttnArgs a) {
   opv<F> qf[ND];
   int qsc[ND];
 #pragma unroll
-  for (int c = 0; c < ND; ++c)
-    qf[c] = q_operand<F, D>(q < S ? a.q + (bh * S + q) * (int64_t)D : nullptr, a.qmul, 2 * c + hh,
-                            qsc[c]);
+  for (int c = 0; c < ND; ++c) {
+    const uint16_t* qrow = q < S ? a.q + (bh * S + q) * (int64_t)D : nullptr;
+    if constexpr (BITS == 8) qf[c] = q_operand32_e4m3<D>(qrow, a.qmul, c, hh, qsc[c]);
+    else qf[c] = q_operand<F, D>(qrow, a.qmul, 2 * c + hh, qsc[c]);
+  }
 
   // ---- lane-constant LDS offsets.  Score product, chunk u, block b, D chunk
   // c: A row n reads key row 64u + 16b + krow0 at logical byte
   // (64c + 32h) * BITS/8 (+8 per FP6 piece); the swizzle of those rows does
   // not depend on u or b.  P V product, chunk u, block db: A row n reads
   // V^T row 32 db + n at logical byte (64u + 32h) * BITS/8.
-  const int krow0 = 32 * ((n >> 2) & 1) + 4 * (n >> 3) + (n & 3);
-  const int ksw = swz_k32(krow0);
+  const int krow0 = KX * ((n >> 2) & 1) + 4 * (n >> 3) + (n & 3);
+  const int ksw = swz_k32<BITS>(krow0);
   const int vsw = swz_v32<BITS>(n);
-  // logical chunk of piece p of MX block m of a row
-  auto piece_chunk = [](int m, int p) __attribute__((always_inline)) { return BITS == 6 ? 2 * m + p : m; };
+  // logical chunk of piece p of the lane's part of 64-element chunk m of a
+  // row (FP8: elements [64m + 16h, +16) and [64m + 32 + 16h, +16); FP6/FP4:
+  // MX block 2m + h)
+  auto piece_chunk = [&](int m, int p) __attribute__((always_inline)) {
+    if constexpr (BITS == 8) return 4 * m + 2 * p + hh;
+    else if constexpr (BITS == 6) return 2 * (2 * m + hh) + p;
+    else return 2 * m + hh;
+  };
   int k_off[ND][NPC], v_off[2][NPC];
 #pragma unroll
   for (int c = 0; c < ND; ++c)
 #pragma unroll
     for (int p = 0; p < NPC; ++p)
-      k_off[c][p] = krow0 * RS + 16 * (piece_chunk(2 * c + hh, p) ^ ksw);
+      k_off[c][p] = krow0 * RS + 16 * (piece_chunk(c, p) ^ ksw);
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int p = 0; p < NPC; ++p)
-      v_off[u][p] = n * RS + 16 * (piece_chunk(2 * u + hh, p) ^ vsw);
+      v_off[u][p] = n * RS + 16 * (piece_chunk(u, p) ^ vsw);
   auto frag = [&](const uint8_t* base, const int* off, int imm) __attribute__((always_inline)) -> opv<F> {
     opv<F> o;
-    if constexpr (BITS == 6) {
+    if constexpr (BITS == 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(base + off[0] + imm);
+      const uint4 w = *reinterpret_cast<const uint4*>(base + off[1] + imm);
+      o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w; o[4] = w.x; o[5] = w.y; o[6] = w.z; o[7] = w.w;
+    } else if constexpr (BITS == 6) {
       const uint4 v = *reinterpret_cast<const uint4*>(base + off[0] + imm);
       const uint2 w = *reinterpret_cast<const uint2*>(base + off[1] + imm);
       o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w; o[4] = w.x; o[5] = w.y;
@@ -277,7 +361,7 @@ fsa_fwd32_kernel(AttnArgs a) {
     return o;
   };
   auto kfrag = [&](const uint8_t* base, int u, int bb, int c) __attribute__((always_inline)) {
-    return frag(base, k_off[c], (64 * u + 16 * bb) * RS);
+    return frag(base, k_off[c], (64 * u + KB * bb) * RS);
   };
   auto vfrag = [&](const uint8_t* base, int u, int db) __attribute__((always_inline)) {
     return frag(base, v_off[u], 32 * db * RS);
@@ -296,6 +380,11 @@ fsa_fwd32_kernel(AttnArgs a) {
   };
 
   const v16f zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  // Key (within the tile) of output register i of block b of chunk u in
+  // this lane: 64u + 32h + 16b + i (FP6/FP4), 64u + 32b + 16h + i (FP8).
+  auto ckey = [&](int u, int bb, int i) __attribute__((always_inline)) {
+    return 64 * u + (BITS == 8 ? 32 * bb + 16 * hh : 32 * hh + 16 * bb) + i;
+  };
 
   // ---- frozen max from the first tile (keys [0, 128)); register i of lane
   // (h, n) in block b of chunk u is key 64u + 32h + 16b + i
@@ -324,7 +413,7 @@ fsa_fwd32_kernel(AttnArgs a) {
       for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = 64 * u + 32 * hh + 16 * bb + i;
+          const int key = ckey(u, bb, i);
           const bool vis = key < S && (!CAUSAL || key <= q);
           const float x = s0[u][bb][i];
           sum += vis ? x : 0.f;
@@ -342,7 +431,7 @@ fsa_fwd32_kernel(AttnArgs a) {
       for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = 64 * u + 32 * hh + 16 * bb + i;
+          const int key = ckey(u, bb, i);
           const bool vis = key < S && (!CAUSAL || key <= q);
           const float dlt = s0[u][bb][i] - mean;
           ss += vis ? dlt * dlt : 0.f;
@@ -360,7 +449,14 @@ fsa_fwd32_kernel(AttnArgs a) {
   v16f O[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) O[db] = zero16;
-  v4f L = {0.f, 0.f, 0.f, 0.f};
+  // Row sums: FP6/FP4 in a 16x16 product (see the head of this file); FP8 in
+  // a 32x32x64 product with an all-ones FP4 A operand (every output row is
+  // the sum of column n), because the FP8 16x16x128 B operand shares one
+  // scale between the half blocks of two queries.
+  using LAcc = std::conditional_t<BITS == 8, v16f, v4f>;
+  LAcc L;
+#pragma unroll
+  for (int i = 0; i < (BITS == 8 ? 16 : 4); ++i) L[i] = 0.f;
   int kmax = -1000000;
   // accumulator start: fp32(2^23 (127 + R) - 2^23 m~), one rounding
   const float c0 = __builtin_fmaf(-8388608.0f, mg, 8388608.0f * (127 + REF));
@@ -370,7 +466,7 @@ fsa_fwd32_kernel(AttnArgs a) {
   // FP4 ones in A rows 0-7 for even lane groups and rows 8-15 for odd ones
   v4i ones;
   {
-    const int on = ((lane >> 4) & 1) == ((lane & 15) >> 3) ? 0x22222222 : 0;
+    const int on = BITS == 8 || ((lane >> 4) & 1) == ((lane & 15) >> 3) ? 0x22222222 : 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) ones[i] = on;
   }
@@ -394,7 +490,7 @@ fsa_fwd32_kernel(AttnArgs a) {
       for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          acc[u][bb][i] = key0 + 64 * u + 32 * hh + 16 * bb + i < lim ? c0 : -INFINITY;
+          acc[u][bb][i] = key0 + ckey(u, bb, i) < lim ? c0 : -INFINITY;
     }
     const uint2 ksc = k_scales(base);
 #pragma unroll
@@ -407,8 +503,12 @@ fsa_fwd32_kernel(AttnArgs a) {
                                   qsc[c]);
       }
   };
-  // Bit-pattern exponential + MX quantisation of P for chunk u: the lane's
-  // 32 values are one whole block (keys 32h .. 32h+31 of the chunk).
+  // Bit-pattern exponential + MX quantisation of P for chunk u.  FP6/FP4:
+  // the lane's 32 values are one whole block (keys 32h .. 32h+31 of the
+  // chunk).  FP8: they are half of each of the chunk's two blocks (keys
+  // 16h + i and 32 + 16h + i); one swap of the half maxima with the lane 32
+  // apart gives every lane the maximum of block h, which it scales in the
+  // P V product, and a second swap hands it the byte of the other block.
   auto epi = [&](int u) __attribute__((always_inline)) {
     float pv[32];
 #pragma unroll
@@ -424,13 +524,27 @@ fsa_fwd32_kernel(AttnArgs a) {
       m0 = max(max(m0, uv(p)), uv(p + 1));
       m1 = max(max(m1, uv(16 + p)), uv(17 + p));
     }
-    const uint32_t mb = max(max(m0, uv(15)), max(m1, uv(31)));
+    m0 = max(m0, uv(15));
+    m1 = max(m1, uv(31));
+    uint32_t mb;
+    if constexpr (BITS == 8) {
+      const auto hs = __builtin_amdgcn_permlane32_swap(m0, m1, false, false);
+      mb = max((uint32_t)hs[0], (uint32_t)hs[1]);
+    } else {
+      mb = max(m0, m1);
+    }
     const int x = block_level<MB>(mb);
     kmax = max(kmax, x);
     const int sb = min(max(x, XLO), XHI) - REF - PL;
-    uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if constexpr (BITS == 6) pack_fp6_split(pv, w, conv_scale(sb));
-    else Pack32<F, false>::run(pv, w, conv_scale(sb), conv_scale(sb));
+    uint32_t w[8];
+    if constexpr (BITS == 8) {
+      const auto sbs = __builtin_amdgcn_permlane32_swap((uint32_t)sb, (uint32_t)sb, false, false);
+      Pack32<F, false>::run(pv, w, conv_scale((int)sbs[0]), conv_scale((int)sbs[1]));
+    } else if constexpr (BITS == 6) {
+      pack_fp6_split(pv, w, conv_scale(sb));
+    } else {
+      Pack32<F, false>::run(pv, w, conv_scale(sb), conv_scale(sb));
+    }
 #pragma unroll
     for (int i = 0; i < Operand<F>::words; ++i) pw[u][i] = (int)w[i];
     psc[u] = sb;
@@ -443,7 +557,10 @@ fsa_fwd32_kernel(AttnArgs a) {
       const int byte = u * NDB + db;
       O[db] = mma32_sel<F>(vfrag(base, u, db), pw[u], O[db], pick(vsc, byte), byte, psc[u]);
     }
-    L = row_sum<F>(ones, pw[u], L, psc[u]);
+    if constexpr (BITS == 8)
+      L = mfma32_v4_v8(ones, pw[u], L, Fmt<FMT_E2M1>::mfma, Fmt<F>::mfma, 0, 127, 0, psc[u]);
+    else
+      L = row_sum<F>(ones, pw[u], L, psc[u]);
   };
 
   using I0 = std::integral_constant<int, 0>;
@@ -523,8 +640,11 @@ fsa_fwd32_kernel(AttnArgs a) {
   int kap = kmax - (127 + REF);
   kap = max(kap, __shfl_xor(kap, 32));
   kap = kap > 0 ? kap : 0;
-  // row sum of query n: output row 0 of lane n (n < 16) or row 8 of lane n + 16
-  const float lsum = __shfl(L[0], n < 16 ? n : n + 16);
+  // row sum of query n: FP8 in every register of the lane; FP6/FP4 output
+  // row 0 of lane n (n < 16) or row 8 of lane n + 16
+  float lsum;
+  if constexpr (BITS == 8) lsum = L[0];
+  else lsum = __shfl(L[0], n < 16 ? n : n + 16);
 
   // ---- normalise and store: register i of O[db] is d = 32 db + 8 (i/4) + 4h + i%4
   if (q < S) {
@@ -573,6 +693,7 @@ hipError_t launch32_2(const AttnArgs& a, int D, int causal, hipStream_t stream) 
 }  // namespace
 
 hipError_t launch_fsa_fwd32(const AttnArgs& a, int fmt, int D, int causal, hipStream_t stream) {
+  if (fmt == FMT_E4M3) return launch32_2<FMT_E4M3>(a, D, causal, stream);
   if (fmt == FMT_E2M3) return launch32_2<FMT_E2M3>(a, D, causal, stream);
   return launch32_2<FMT_E2M1>(a, D, causal, stream);
 }

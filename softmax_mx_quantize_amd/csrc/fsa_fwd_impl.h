@@ -1134,7 +1134,7 @@ __device__ __forceinline__ void fallback_group(const AttnArgs& a, int64_t grp) {
   const uint8_t* vs = a.vs + wi * (int64_t)D * vs_row;
   // scale byte of tile key kk (read by lane (g, r) as slice j) and D block g
   auto ks_byte = [&](int kk, int j) __attribute__((always_inline)) {
-    return L32 ? key_tile32_byte(kk, g, D) : (r * NDB + g) * 8 + j;
+    return L32 ? key_tile32_byte(kk, g, D, BITS) : (r * NDB + g) * 8 + j;
   };
 
   opv<F> qf[NSUB];

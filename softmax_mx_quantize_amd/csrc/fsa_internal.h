@@ -39,7 +39,7 @@ struct QuantArgs {
 //     output row d = 16 dt + r goes to byte (r * 4 + g) * (D/16) + dt of tile
 //     T's 4 D bytes.
 //   KEY_TILES32 / DIM_TILES32: the same idea for the kernel built on the
-//     32x32x64 scaled MFMA (FP6/FP4 operands, D a multiple of 64): lane
+//     32x32x64 scaled MFMA (D a multiple of 64): lane
 //     (h, rho) = 32 h + rho of that product reads the NBK = D/8 (K^) or
 //     D/16 (V^T) bytes at lane * NB of each tile; see the two functions below.
 enum { SCALES_ROWS = 0, SCALES_KEY_TILES = 1, SCALES_DIM_TILES = 2, SCALES_KEY_TILES32 = 3,
@@ -48,13 +48,15 @@ enum { SCALES_ROWS = 0, SCALES_KEY_TILES = 1, SCALES_DIM_TILES = 2, SCALES_KEY_T
 // Byte of key row Rl (0..127 within its tile) and D block blk in a
 // KEY_TILES32 tile of 128 * D/32 bytes.  The score product of the 32x32x64
 // kernel covers 64-key chunk u = Rl / 64 with two 32-row blocks b; its A row
-// rho = 8 j + 4 x + k holds key 32 x + 16 b + 4 j + k of the chunk, so that a
-// lane's 32 outputs are 32 consecutive keys.  Lane half h reads D block
-// 2 c + h of 64-wide D chunk c; its byte for (u, b, c) is u*2nd + b*nd + c.
-__host__ __device__ inline int key_tile32_byte(int rl, int blk, int d) {
+// rho = 8 j + 4 x + k holds key 32 x + 16 b + 4 j + k of the chunk (FP6/FP4)
+// or 32 b + 16 x + 4 j + k (FP8), so that a lane's 32 outputs are the keys it
+// supplies to the P V product.  Lane half h reads D block 2 c + h of 64-wide
+// D chunk c; its byte for (u, b, c) is u*2nd + b*nd + c.
+__host__ __device__ inline int key_tile32_byte(int rl, int blk, int d, int bits) {
   const int nd = d / 64;
   const int u = rl >> 6, kk = rl & 63;
-  const int x = kk >> 5, b = (kk >> 4) & 1, j = (kk >> 2) & 3, k = kk & 3;
+  const int hi = kk >> 5, mid = (kk >> 4) & 1, j = (kk >> 2) & 3, k = kk & 3;
+  const int x = bits == 8 ? mid : hi, b = bits == 8 ? hi : mid;
   const int rho = 8 * j + 4 * x + k;
   return (32 * (blk & 1) + rho) * 4 * nd + u * 2 * nd + b * nd + (blk >> 1);
 }
@@ -91,8 +93,7 @@ struct AttnArgs {
 
 hipError_t launch_fsa_fwd(const AttnArgs& a, int fmt, int D, int causal, hipStream_t stream);
 hipError_t launch_fsa_fwd_e4m3(const AttnArgs& a, int D, int causal, hipStream_t stream);
-// The E2M3/E2M1 kernel on the 32x32x64 scaled MFMA (scales in the *_TILES32
-// layouts).
+// The kernel on the 32x32x64 scaled MFMA (scales in the *_TILES32 layouts).
 hipError_t launch_fsa_fwd32(const AttnArgs& a, int fmt, int D, int causal, hipStream_t stream);
 
 // Plain BF16 flash attention.

@@ -81,7 +81,7 @@ __device__ __forceinline__ void quantize_block(const QuantArgs& a, float (&v)[32
     const int nb = (int)a.nb_out;
     const int64_t bt = o / a.out_rows;
     const int64_t row = o - bt * a.out_rows;
-    so = bt * a.out_rows * nb + (row >> 7) * 128 * nb + key_tile32_byte((int)(row & 127), (int)b, 32 * nb);
+    so = bt * a.out_rows * nb + (row >> 7) * 128 * nb + key_tile32_byte((int)(row & 127), (int)b, 32 * nb, BITS);
   } else if (a.scale_layout == SCALES_DIM_TILES32) {
     const int64_t bt = o / a.out_rows;
     const int d = (int)(o - bt * a.out_rows);
