@@ -37,10 +37,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"e4m3": 5000.0, "e2m3": 10100.0, "e2m1": 10100.0, "bf16": 2500.0}
 METRIC = "attention fwd TFLOP/s and % of MX MFMA peak (MXFP8/6/4, S=16K, D=128)"
-KERNEL_SOURCES = ("softmax_mx_quantize_amd/csrc/fsa_fwd_impl.h",
+KERNEL_SOURCES = ("softmax_mx_quantize_amd/csrc/fsa_common.h",
                   "softmax_mx_quantize_amd/csrc/fsa_fwd.hip",
-                  "softmax_mx_quantize_amd/csrc/fsa_fwd_e4m3.hip",
-                  "softmax_mx_quantize_amd/csrc/fsa_fwd32.hip",
                   "softmax_mx_quantize_amd/csrc/fsa_device.h",
                   "softmax_mx_quantize_amd/csrc/lds_dma.h")
 

@@ -20,15 +20,12 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.environ.get("FSA_BUILD_DIR") or os.path.join(PKG, "_build")
 LIB = os.environ.get("FSA_LIB_OUT") or os.path.join(PKG, "libfsa.so")
 
-SOURCES = ["fsa_api.cpp", "mx_quant.hip", "fsa_fwd.hip", "fsa_fwd_e4m3.hip", "fsa_fwd32.hip",
-           "bf16_fa.hip"]
+SOURCES = ["fsa_api.cpp", "mx_quant.hip", "fsa_fwd.hip", "bf16_fa.hip"]
 
-# Per-source options.  The fused kernels run two waves per SIMD and consume
+# Per-source options.  The fused kernel runs two waves per SIMD and consumes
 # the score MFMA results on the vector units; asking for the VGPR form of
 # every MFMA keeps them out of AGPRs (no accvgpr moves in the loop).
-SOURCE_FLAGS = {"fsa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-                "fsa_fwd_e4m3.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-                "fsa_fwd32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+SOURCE_FLAGS = {"fsa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 # Packed fp32 VALU instructions are disabled on purpose (the target feature is
 # switched off for the device pass; the host pass ignores it with a warning).

@@ -7,7 +7,6 @@
 
 #include <atomic>
 #include <cmath>
-#include <cstdlib>
 #include <cstddef>
 #include <cstdint>
 #include <mutex>
@@ -28,18 +27,6 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 // fsa_fmt -> kernel format index
 int kern_fmt(int fmt) { return fmt == FSA_MXFP8_E4M3 ? 0 : (fmt == FSA_MXFP6_E2M3 ? 1 : 2); }
-
-// Every format runs on the 32x32x64 kernel (scales in its tile layouts);
-// FSA_MMA16=1 in the environment selects the 16x16x128 kernels instead, for
-// comparisons.
-bool use_mma32(int fmt) {
-  static const bool force16 = [] {
-    const char* e = std::getenv("FSA_MMA16");
-    return e && e[0] == '1';
-  }();
-  (void)fmt;
-  return !force16;
-}
 
 struct Workspace {
   void* ptr = nullptr;
@@ -239,15 +226,14 @@ int fsa_attention_fwd_ex(const void* q, const void* k, const void* v, void* out,
     for (int b = 0; b < B; ++b) {
       const int64_t src = ((int64_t)b * H + rl.h0) * S * D;
       const int64_t w0 = (int64_t)b * rl.hrun;
-      const bool l32 = use_mma32(rl.fmt);
       st = quantize(kb + src, ws + rl.kc + w0 * sk_alloc * rb, ws + rl.ks + w0 * sk_alloc * (D / 32),
                     rl.hrun, S, D, sk_alloc, D / 32, rb, D / 32, rl.fmt, 0, stream, 1.0f,
-                    l32 ? fsa::SCALES_KEY_TILES32 : fsa::SCALES_KEY_TILES);
+                    fsa::SCALES_KEY_TILES);
       if (st != FSA_OK) return st;
       st = quantize(vb + src, ws + rl.vc + w0 * D * (sk_alloc * bits / 8),
                     ws + rl.vs + w0 * D * (sk_alloc / 32), rl.hrun, S, D, D, sk_alloc / 32,
                     sk_alloc * bits / 8, sk_alloc / 32, rl.fmt, 1, stream, 1.0f,
-                    l32 ? fsa::SCALES_DIM_TILES32 : fsa::SCALES_DIM_TILES);
+                    fsa::SCALES_DIM_TILES);
       if (st != FSA_OK) return st;
     }
   }
@@ -271,10 +257,8 @@ int fsa_attention_fwd_ex(const void* q, const void* k, const void* v, void* out,
     a.bias = opt ? opt->guess_bias : 0.0f;
     a.fb_flag = reinterpret_cast<uint64_t*>(ws + flag_off);
     a.call_id = next_call_id();
-    const hipError_t e = use_mma32(rl.fmt)
-                             ? fsa::launch_fsa_fwd32(a, kern_fmt(rl.fmt), D, causal, stream)
-                             : fsa::launch_fsa_fwd(a, kern_fmt(rl.fmt), D, causal, stream);
-    if (e != hipSuccess) return FSA_ERR_HIP;
+    if (fsa::launch_fsa_fwd(a, kern_fmt(rl.fmt), D, causal, stream) != hipSuccess)
+      return FSA_ERR_HIP;
   }
   return FSA_OK;
 }

@@ -1,0 +1,504 @@
+// Device helpers of the fused-softmax attention kernels (gfx950) and the
+// fallback kernel for rows far above their frozen max.
+//
+// What the path computes (Fused-Softmax for efficient quantized attention,
+// summary; Moving softmax to matrix operations speeds up AI inference by over
+// 2x, "Read it as" and the "How it works" figure; the exact readings are
+// fixed in the oracle's module documentation):
+//   1. frozen max per query row from the first 128 keys, in binades:
+//      max(window max, mean + (sqrt(2 ln n) + 1) * std) + bias;
+//   2. scores on the matrix cores with the exponential's linear part folded
+//      in: Q carries log2(e)/sqrt(D) (applied when it is quantised), 2^23
+//      rides on Q's E8M0 scale, and the accumulator starts at
+//      2^23 (127 + R) - 2^23 m~, so each fp32 output y already is the
+//      exponent-field value of the bit-pattern exponential;
+//   3. epilogue per 32-key MX block: one truncating conversion per element
+//      turns y into the fp32 pattern of 2^(t + R); the block's binade comes
+//      from the largest pattern, and the scaled pack conversion divides by the
+//      block's power-of-two shift and rounds onto the element grid: the
+//      exponential and the MX quantisation of P with no exp instruction;
+//   4. O^T += V^T P~^T and l += 1 P~^T on the matrix cores (same P~ in
+//      numerator and denominator, as EFQ-Softmax: Exp-Free Quantization for
+//      Softmax, abstract, uses it);
+//   5. a block above the guess takes a larger E8M0 scale, which is the
+//      whole-binade re-basing of the fallback up to a common power of two;
+//      rows beyond 64 binades are recomputed by the fallback kernel here;
+//   6. out = bf16(O / l).
+#pragma once
+
+#include <type_traits>
+
+#include "fsa_device.h"
+#include "fsa_internal.h"
+#include "lds_dma.h"
+
+namespace fsa {
+
+// The builtin of the scaled MFMA only takes 8-dword operands; the narrow
+// FP6/FP4 forms of the same intrinsic are reached through its overloaded
+// LLVM name.  (Compiler instructions: the hazard handling is the same.)
+__device__ v4f mfma_scale_v6(v6i a, v6i b, v4f c, int cbsz, int blgp, int opsel_a, int sa,
+                             int opsel_b, int sb)
+    __asm("llvm.amdgcn.mfma.scale.f32.16x16x128.f8f6f4.v6i32.v6i32");
+__device__ v4f mfma_scale_v4(v4i a, v4i b, v4f c, int cbsz, int blgp, int opsel_a, int sa,
+                             int opsel_b, int sb)
+    __asm("llvm.amdgcn.mfma.scale.f32.16x16x128.f8f6f4.v4i32.v4i32");
+// Mixed widths: an FP4 A operand with an FP8 or FP6 B operand.
+__device__ v4f mfma_scale_v4_v8(v4i a, v8i b, v4f c, int cbsz, int blgp, int opsel_a, int sa,
+                                int opsel_b, int sb)
+    __asm("llvm.amdgcn.mfma.scale.f32.16x16x128.f8f6f4.v4i32.v8i32");
+__device__ v4f mfma_scale_v4_v6(v4i a, v6i b, v4f c, int cbsz, int blgp, int opsel_a, int sa,
+                                int opsel_b, int sb)
+    __asm("llvm.amdgcn.mfma.scale.f32.16x16x128.f8f6f4.v4i32.v6i32");
+
+namespace {
+
+constexpr int KT = 128;          // keys per tile
+constexpr float MAGIC = 12582912.0f;   // 1.5 * 2^23: float + MAGIC rounds to an integer
+// A score equal to the reference gives the fp32 pattern of 2^REF, so scores
+// from 188 binades below it to 66 above map to normal fp32 numbers.
+constexpr int REF = 62;
+
+// Binade of a block relative to the reference, in element codes:
+// floor(RNE(2^M (y / 2^23 - 127 - REF)) / 2^M) for the block's largest
+// exponent-field value y.  y * 2^(M-23) is exact, and adding the integer
+// constant plus MAGIC rounds once, to nearest even.  Blocks whose largest
+// value lies below 2^-(127+REF) (or that are fully masked, y = -inf) count as
+// y = 0, which already puts them beyond the largest block shift.  Values
+// more than HI_BINADE binades above the reference count as exactly that
+// many (the MAGIC window holds 2^22 codes); the row then falls back with
+// kappa = HI_BINADE, which is exact for every score within 2^18 binades of
+// its frozen max.
+constexpr int HI_BINADE = 1 << 18;
+// Largest guess-relative block binade the main sweep absorbs by block shifts
+// alone; rows above it go to the fallback kernel.
+constexpr int EXT = 64;
+static_assert(HI_BINADE > EXT, "clamped binades must reach the fallback kernel");
+template <int M>
+__device__ __forceinline__ int block_binade(float y) {
+  const float yc = __builtin_amdgcn_fmed3f(y, 0.0f, 8388608.0f * (float)(127 + REF + HI_BINADE));
+  const float t = __builtin_fmaf(yc, (float)(1 << M) * 0x1p-23f,
+                                 MAGIC - (float)((1 << M) * (127 + REF)));
+  return (int)(__float_as_uint(t) - __float_as_uint(MAGIC)) >> M;
+}
+
+// Divisor of the scaled conversions for a block whose P~ scale byte is sb:
+// 2^(sb + REF - 127), taking the bit-pattern value 2^(t + REF) to
+// 2^(t + pl + Delta).
+__device__ __forceinline__ float conv_scale(int sb) {
+  return __uint_as_float((uint32_t)(sb + REF) << 23);
+}
+
+// Level of a block whose largest pattern is m: the binade plus 127 + REF,
+// i.e. the exponent field of m after rounding its mantissa to M bits
+// (nearest, ties to even): floor(RNE(2^M m / 2^23) / 2^M).  For a pattern
+// from y >= 2^23 this is the binade of block_binade below; smaller patterns
+// lie below every level the shifts distinguish.  m is clamped first so that
+// the rounding cannot carry out of 32 bits; the clamp sits one level above
+// the largest shift (127 + REF + EXT), so the row still reaches the
+// fallback.
+template <int M>
+__device__ __forceinline__ int block_level(uint32_t m) {
+  constexpr uint32_t LIM = (uint32_t)(127 + REF + EXT + 1) << 23;
+  const uint32_t mc = min(m, LIM);
+  const uint32_t lsb = (mc >> (23 - M)) & 1u;
+  return (int)((mc + (1u << (22 - M)) - 1u + lsb) >> 23);
+}
+
+// Truncation toward zero to u32 (v_cvt_u32_f32, which saturates and maps NaN
+// and negatives to 0; the exponential relies on that).  It must stay a
+// compiler-visible conversion: the epilogue feeds it straight from MFMA
+// results, and only instructions the compiler sees get the wait states that
+// reading an MFMA result requires.  Its input must come straight from the
+// product (never a select with constants), so that no out-of-range case can
+// be folded away at compile time; masking happens on the integer result.
+__device__ __forceinline__ uint32_t cvt_u32_trunc(float y) {
+  return (uint32_t)y;
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFF + ((u >> 16) & 1);
+  return (uint16_t)(u >> 16);
+}
+
+// Position p (0..31) of a lane's operand list -> index along the 128-wide K
+// dimension for lane group g.
+template <int F>
+__device__ __forceinline__ int kpos(int g, int p) {
+  if (Fmt<F>::bits == 8) return p < 16 ? 16 * g + p : 64 + 16 * g + (p - 16);
+  return 32 * g + p;
+}
+
+// A lane's 32 operand elements of the 16x16x128 product straight from a
+// global row (`len` valid K elements; past it, zeros).
+template <int F>
+__device__ __forceinline__ opv<F> global_operand(const uint8_t* row, int g, int len) {
+  opv<F> o = zero_operand<F>();
+  if constexpr (Fmt<F>::bits == 8) {
+    if (16 * g < len) {
+      uint4 a = *reinterpret_cast<const uint4*>(row + 16 * g);
+      o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+    }
+    if (64 + 16 * g < len) {
+      uint4 b = *reinterpret_cast<const uint4*>(row + 64 + 16 * g);
+      o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+    }
+  } else if constexpr (Fmt<F>::bits == 6) {
+    if (32 * g < len) {
+      const uint2* p = reinterpret_cast<const uint2*>(row + 24 * g);
+      uint2 a = p[0], b = p[1], c = p[2];
+      o[0] = a.x; o[1] = a.y; o[2] = b.x; o[3] = b.y; o[4] = c.x; o[5] = c.y;
+    }
+  } else {
+    if (32 * g < len) {
+      uint4 a = *reinterpret_cast<const uint4*>(row + 16 * g);
+      o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+    }
+  }
+  return o;
+}
+
+// The 16x16x128 scaled MFMA with operands of the format's own width.
+// OA selects the byte of `sa` that scales A (op_sel); B's scale is byte 0.
+template <int F, int OA = 0>
+__device__ __forceinline__ v4f mfma(const opv<F>& a, const opv<F>& b, const v4f& c, int sa, int sb) {
+  if constexpr (Fmt<F>::bits == 8)
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, Fmt<F>::mfma, Fmt<F>::mfma,
+                                                            OA, sa, 0, sb);
+  else if constexpr (Fmt<F>::bits == 6)
+    return mfma_scale_v6(a, b, c, Fmt<F>::mfma, Fmt<F>::mfma, OA, sa, 0, sb);
+  else
+    return mfma_scale_v4(a, b, c, Fmt<F>::mfma, Fmt<F>::mfma, OA, sa, 0, sb);
+}
+// Row sums l += 1 P~^T on the matrix core: the all-ones A operand is held
+// in FP4 (E2M1 1.0 = 0x2 in every nibble, 4 registers) whatever the format
+// of P~; FP4 ones times P~ in its own format is the same exact sum.
+__device__ __forceinline__ v4i ones_fp4() {
+  v4i o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = 0x22222222;
+  return o;
+}
+template <int F>
+__device__ __forceinline__ v4f row_sum(const v4i& ones, const opv<F>& p, const v4f& c, int sp) {
+  if constexpr (Fmt<F>::bits == 8)
+    return mfma_scale_v4_v8(ones, p, c, Fmt<FMT_E2M1>::mfma, Fmt<F>::mfma, 0, 127, 0, sp);
+  else if constexpr (Fmt<F>::bits == 6)
+    return mfma_scale_v4_v6(ones, p, c, Fmt<FMT_E2M1>::mfma, Fmt<F>::mfma, 0, 127, 0, sp);
+  else
+    return mfma_scale_v4(ones, p, c, Fmt<FMT_E2M1>::mfma, Fmt<F>::mfma, 0, 127, 0, sp);
+}
+
+// Cross-lane exchanges on the vector unit (v_permlane16/32_swap; the swap
+// trades the odd 16-lane rows of its first operand with the even rows of its
+// second, resp. the upper 32 lanes of the first with the lower 32 of the
+// second), so that the epilogue waits on no LDS round trip.
+// x of lane ^ 48 for lane groups 1 and 2 (rows 1 and 2 trade places); the
+// result is unspecified in groups 0 and 3.
+__device__ __forceinline__ int swap_rows12(int x, int g) {
+  const auto h = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  // h[0] rows: x0 x1 x0 x1; h[1] rows: x2 x3 x2 x3
+  const auto q = __builtin_amdgcn_permlane16_swap((uint32_t)h[0], (uint32_t)h[1], false, false);
+  // q[0] rows: x0 x2 x0 x2; q[1] rows: x1 x3 x1 x3
+  return (int)(g == 1 ? q[0] : q[1]);
+}
+
+// Scale operand of the P~ B operand.  FP6/FP4: the lane's own block.  FP8:
+// lane group c supplies the scale of key block c; blocks 0/2 are the low/high
+// halves held by groups 0-1, blocks 1/3 those held by groups 2-3, so groups
+// 1 and 2 take the value from the lane 48 apart (a branch-free exchange).
+template <int BITS>
+__device__ __forceinline__ int p_scale(int s_lo, int s_hi, int g) {
+  if (BITS != 8) return s_lo;
+  const int give = g >= 2 ? s_lo : s_hi;            // what the partner needs
+  const int got = swap_rows12(give, g);
+  const int own = g < 2 ? s_lo : s_hi;
+  const bool cross = (g == 1) | (g == 2);
+  return cross ? got : own;
+}
+
+// The lane's Q' operand of the score product, MX-quantised here from the
+// bf16 row (the same rule as the quantiser: OCP floor scale, RNE, saturation,
+// NaN/Inf blocks get scale 0xFF and zero codes) with Q' = fp32(q * mult).
+// `row` is null for padding rows.  Returns the codes in operand order and
+// sets `sc` to the E8M0 byte of the block this lane group scales, raised by
+// 23 (2^23 rides on Q's scale; 255 stays NaN).
+template <int F, int D>
+__device__ __forceinline__ opv<F> q_operand(const uint16_t* row, float mult, int g, int& sc) {
+  constexpr int BITS = Fmt<F>::bits;
+  float v[32];
+  bool bad_lo = false, bad_hi = false;
+  // element k of the operand: FP6/FP4 column 32g + k; FP8 column 16g + k
+  // (k < 16) and 64 + 16g + (k - 16)
+  auto column = [&](int k) { return BITS == 8 ? (k < 16 ? 16 * g + k : 64 + 16 * g + k - 16) : 32 * g + k; };
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {                      // four 8-element chunks
+    const int col = column(8 * c);
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (row != nullptr && col < D) w = *reinterpret_cast<const uint4*>(row + col);
+    const uint32_t h[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = h[e] & 0xFFFF, hi = h[e] >> 16;
+      const bool nan_inf = ((lo & 0x7F80) == 0x7F80) | ((hi & 0x7F80) == 0x7F80);
+      if (c < 2) bad_lo |= nan_inf; else bad_hi |= nan_inf;
+      v[8 * c + 2 * e] = bf16_bits_to_float(lo) * mult;
+      v[8 * c + 2 * e + 1] = bf16_bits_to_float(hi) * mult;
+    }
+  }
+  float a_lo = 0.0f, a_hi = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    a_lo = __builtin_fmaxf(a_lo, __builtin_fabsf(v[k]));
+    a_hi = __builtin_fmaxf(a_hi, __builtin_fabsf(v[16 + k]));
+  }
+  if (BITS == 8) {
+    // each MX block is two half blocks held by lanes 16 apart
+    a_lo = __builtin_fmaxf(a_lo, __shfl_xor(a_lo, 16));
+    a_hi = __builtin_fmaxf(a_hi, __shfl_xor(a_hi, 16));
+    bad_lo |= __shfl_xor((int)bad_lo, 16) != 0;
+    bad_hi |= __shfl_xor((int)bad_hi, 16) != 0;
+  } else {
+    a_lo = a_hi = __builtin_fmaxf(a_lo, a_hi);
+    bad_lo = bad_hi = bad_lo | bad_hi;
+  }
+  auto scale_exp = [](float amax) {
+    int X = amax > 0.0f ? floor_log2(amax) - Fmt<F>::emax : -127;
+    return X < -127 ? -127 : (X > 127 ? 127 : X);
+  };
+  const int x_lo = scale_exp(a_lo), x_hi = scale_exp(a_hi);
+  float y[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) y[k] = __builtin_ldexpf(v[k], -(k < 16 ? x_lo : x_hi));
+  uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  Pack32<F, true>::run(y, w);
+  if (bad_lo) { for (int i = 0; i < 4; ++i) w[i] = 0; }
+  if (bad_hi) { for (int i = 4; i < 8; ++i) w[i] = 0; }
+  if (BITS != 8 && bad_lo) { for (int i = 0; i < 8; ++i) w[i] = 0; }
+  auto raised = [](int x, bool bad) { return bad ? 255 : min(x + 127 + 23, 254); };
+  int s_lo = raised(x_lo, bad_lo), s_hi = raised(x_hi, bad_hi);
+  if (BITS == 8 && D < 128) s_hi = 127;                // blocks past D: zeros
+  if (BITS != 8 && 32 * g >= D) s_lo = s_hi = 127;
+  sc = p_scale<BITS>(s_lo, s_hi, g);
+  opv<F> o;
+#pragma unroll
+  for (int i = 0; i < Operand<F>::words; ++i) o[i] = (int)w[i];
+  return o;
+}
+
+}  // namespace
+
+// Fallback for rows whose scores exceed the frozen max by more than EXT
+// binades: one wave per 32 query rows (two subtiles of 16).  A wave whose
+// rows all stayed within EXT exits at once; otherwise it recomputes its rows
+// from global memory with each row's reference raised by its kappa
+// (accumulator start and block shifts re-based, no in-loop clamp), reading
+// the frozen max and kappa the main kernel stored, and overwrites their
+// outputs.  Rows within EXT come out as the main kernel left them (the
+// re-based sums are the same up to the common power-of-two factor).  It runs
+// on the 16x16x128 product (lane (g, r) = 16 g + r; FP8 operands hold K
+// elements [16g, +16) and [64+16g, +16), FP6/FP4 ones [32g, +32)) and reads
+// the tile-ordered scales through the layout functions.
+template <int F, int D, bool CAUSAL>
+__device__ __forceinline__ void fallback_group(const AttnArgs& a, int64_t grp) {
+  constexpr int NSUB = 2;
+  constexpr int BITS = Fmt<F>::bits;
+  constexpr int MB = Fmt<F>::mbits;
+  constexpr int PL = F == FMT_E4M3 ? Fmt<F>::emax - 1 : Fmt<F>::emax;
+  constexpr int CAP = 127 - PL;
+  constexpr int RB = D * BITS / 8;
+  constexpr int NDB = D / 32;
+  constexpr int NDT = D / 16;
+  constexpr int VRB = KT * BITS / 8;
+  const int lane = threadIdx.x;
+  const int g = lane >> 4;
+  const int r = lane & 15;
+  const int S = a.S;
+  const int ng = (S + 16 * NSUB - 1) / (16 * NSUB);
+  const int64_t wi = grp / ng;
+  if (wi >= (int64_t)a.B * a.hrun) return;
+  const int b = (int)wi / a.hrun;
+  const int h = a.h0 + ((int)wi - b * a.hrun);
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int q0 = (int)(grp - wi * ng) * 16 * NSUB;
+
+  int kap[NSUB];
+  float mg[NSUB];
+  bool extreme = false;
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    const int q = q0 + 16 * s + r;
+    kap[s] = q < S ? a.row_kappa[bh * S + q] : 0;
+    mg[s] = q < S ? a.row_mguess[bh * S + q] : 0.0f;
+    extreme |= kap[s] > EXT;
+  }
+  if (__builtin_amdgcn_ballot_w64(extreme) == 0) return;
+
+  const uint8_t* kc = a.kc + wi * (int64_t)a.sk_alloc * RB;
+  const uint8_t* ks = a.ks + wi * (int64_t)a.sk_alloc * NDB;
+  const int64_t v_row = (int64_t)a.sk_alloc * BITS / 8;
+  const uint8_t* vc = a.vc + wi * (int64_t)D * v_row;
+  const int vs_row = a.sk_alloc / 32;
+  const uint8_t* vs = a.vs + wi * (int64_t)D * vs_row;
+  // scale byte of tile key kk (read by lane (g, r) as slice j) and D block g
+  auto ks_byte = [&](int kk, int j) __attribute__((always_inline)) {
+    return key_tile_byte(kk, g, D, BITS);
+  };
+
+  opv<F> qf[NSUB];
+  int qsc[NSUB];
+  v4f mk[NSUB], O[NSUB][NDT], L[NSUB];
+  const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    const int q = q0 + 16 * s + r;
+    qf[s] = q_operand<F, D>(q < S ? a.q + (bh * S + q) * (int64_t)D : nullptr, a.qmul, g, qsc[s]);
+    L[s] = zero4;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) O[s][dt] = zero4;
+  }
+  const v4i ones = ones_fp4();
+
+  int n_tiles = (S + KT - 1) / KT;
+  if (CAUSAL) {
+    const int last_q = q0 + 16 * NSUB - 1 < S - 1 ? q0 + 16 * NSUB - 1 : S - 1;
+    n_tiles = min(n_tiles, last_q / KT + 1);
+  }
+  // The main sweep measures binades on the integer patterns, which saturate
+  // some 320 binades above the guess; take kappa again from the fp32 values
+  // (exact to HI_BINADE).
+  {
+    v4f m0init[NSUB];
+    int km[NSUB];
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      const float c0 = __builtin_fmaf(-8388608.0f, mg[s], 8388608.0f * (float)(127 + REF));
+      m0init[s] = v4f{c0, c0, c0, c0};
+      km[s] = -(1 << 30);
+    }
+    for (int t = 0; t < n_tiles; ++t) {
+      const int key0 = t * KT;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int kk = kpos<F>(r >> 2, 4 * j + (r & 3));
+        const int sc = g < NDB ? (int)ks[(int64_t)t * KT * NDB + ks_byte(kk, j)] : 127;
+        const opv<F> kf = global_operand<F>(kc + (int64_t)(key0 + kk) * RB, g, D);
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+          const v4f y = mfma<F>(kf, qf[s], m0init[s], sc, qsc[s]);
+          const int q = q0 + 16 * s + r;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = key0 + kpos<F>(g, 4 * j + i);
+            const bool vis = key < S && (!CAUSAL || key <= q);
+            // the binade of each element bounds that of its block's maximum
+            if (vis) km[s] = max(km[s], block_binade<MB>(y[i]));
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      int k = km[s];
+      k = max(k, __shfl_xor(k, 16));
+      k = max(k, __shfl_xor(k, 32));
+      kap[s] = k > 0 ? k : 0;
+      const float c0 = __builtin_fmaf(-8388608.0f, mg[s], 8388608.0f * (float)(127 + REF - kap[s]));
+      mk[s] = v4f{c0, c0, c0, c0};
+      const int q = q0 + 16 * s + r;
+      if (g == 0 && q < S) a.row_kappa[bh * S + q] = kap[s];
+    }
+  }
+  for (int t = 0; t < n_tiles; ++t) {
+    const int key0 = t * KT;
+    v4f acc[NSUB][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int kk = kpos<F>(r >> 2, 4 * j + (r & 3));
+      const int sc = g < NDB ? (int)ks[(int64_t)t * KT * NDB + ks_byte(kk, j)] : 127;
+      const opv<F> kf = global_operand<F>(kc + (int64_t)(key0 + kk) * RB, g, D);
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) acc[s][j] = mfma<F>(kf, qf[s], mk[s], sc, qsc[s]);
+    }
+    opv<F> pw[NSUB];
+    int psc[NSUB];
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      const int q = q0 + 16 * s + r;
+      float x[32];
+#pragma unroll
+      for (int p = 0; p < 32; ++p) {
+        const int key = key0 + kpos<F>(g, p);
+        const bool vis = key < S && (!CAUSAL || key <= q);
+        x[p] = vis ? acc[s][p >> 2][p & 3] : -INFINITY;
+      }
+      float m0 = x[0], m1 = x[16];
+#pragma unroll
+      for (int p = 1; p < 16; ++p) { m0 = __builtin_fmaxf(m0, x[p]); m1 = __builtin_fmaxf(m1, x[16 + p]); }
+      if (BITS == 8) {
+        m0 = __builtin_fmaxf(m0, __shfl_xor(m0, 16));
+        m1 = __builtin_fmaxf(m1, __shfl_xor(m1, 16));
+      } else {
+        m0 = __builtin_fmaxf(m0, m1);
+        m1 = m0;
+      }
+      // binades relative to the raised reference: shifts need no EXT clamp
+      const int sb0 = 127 - PL - min(-block_binade<MB>(m0), CAP);
+      const int sb1 = 127 - PL - min(-block_binade<MB>(m1), CAP);
+      float pv[32];
+#pragma unroll
+      for (int p = 0; p < 32; ++p) {
+        const int key = key0 + kpos<F>(g, p);
+        const bool vis = key < S && (!CAUSAL || key <= q);
+        const uint32_t u = cvt_u32_trunc(acc[s][p >> 2][p & 3]);
+        pv[p] = __uint_as_float(vis ? u : 0u);
+      }
+      uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      Pack32<F, false>::run(pv, w, conv_scale(sb0), conv_scale(sb1));
+#pragma unroll
+      for (int i = 0; i < Operand<F>::words; ++i) pw[s][i] = (int)w[i];
+      psc[s] = p_scale<BITS>(sb0, sb1, g);
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int d = 16 * dt + r;
+      const opv<F> vf = global_operand<F>(vc + d * v_row + (int64_t)t * VRB, g, KT);
+      const int vsc = (int)vs[(int64_t)t * 4 * D + dim_tile_byte(d, g, D)];
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) O[s][dt] = mfma<F>(vf, pw[s], O[s][dt], vsc, psc[s]);
+    }
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) L[s] = row_sum<F>(ones, pw[s], L[s], psc[s]);
+  }
+
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    const int q = q0 + 16 * s + r;
+    if (q < S) {
+      const float inv = 1.0f / L[s][0];
+      uint16_t* orow = a.out + (bh * S + q) * (int64_t)D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const uint32_t lo = f32_to_bf16_rne(O[s][dt][0] * inv) | ((uint32_t)f32_to_bf16_rne(O[s][dt][1] * inv) << 16);
+        const uint32_t hi = f32_to_bf16_rne(O[s][dt][2] * inv) | ((uint32_t)f32_to_bf16_rne(O[s][dt][3] * inv) << 16);
+        *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = make_uint2(lo, hi);
+      }
+    }
+  }
+}
+
+// Grid-stride over groups of 32 query rows; a call whose main kernel found
+// no row beyond EXT binades (flag not stamped with this call's id) exits
+// after one load.
+template <int F, int D, bool CAUSAL>
+__global__ void __launch_bounds__(64) fsa_fallback_kernel(AttnArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  if (*a.fb_flag != a.call_id) return;
+  const int64_t n_groups = (int64_t)(a.S + 31) / 32 * a.B * a.hrun;
+  for (int64_t grp = blockIdx.x; grp < n_groups; grp += gridDim.x)
+    fallback_group<F, D, CAUSAL>(a, grp);
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+}  // namespace fsa

@@ -27,32 +27,21 @@ struct QuantArgs {
 };
 
 // Scale byte layouts.  ROWS: scales[row][block] (the public layout).  The two
-// tile layouts feed the attention kernel: per 128-key tile the bytes a lane
-// needs for its 8 products sit next to each other, so one 8-byte LDS read
-// fetches them and the scaled MFMA picks its byte with op_sel.
-//   KEY_TILES (K^, blocks along D): within tile T of a batch entry, key row
-//     R = 128 T + Rl and block b go to byte (r * (D/32) + b) * 8 + j of the
-//     tile's 128 * D/32 bytes, where (r, j) is the lane row and slice that
-//     read key Rl: FP8 r = 4 ((Rl>>4)&3) + (Rl&3), j = ((Rl>>2)&3) + 4 (Rl>>6);
-//     FP6/FP4 r = 4 (Rl>>5) + (Rl&3), j = (Rl>>2)&7.
-//   DIM_TILES (V^ transposed, blocks along keys): block kb = 4 T + g of
-//     output row d = 16 dt + r goes to byte (r * 4 + g) * (D/16) + dt of tile
-//     T's 4 D bytes.
-//   KEY_TILES32 / DIM_TILES32: the same idea for the kernel built on the
-//     32x32x64 scaled MFMA (D a multiple of 64): lane
-//     (h, rho) = 32 h + rho of that product reads the NBK = D/8 (K^) or
-//     D/16 (V^T) bytes at lane * NB of each tile; see the two functions below.
-enum { SCALES_ROWS = 0, SCALES_KEY_TILES = 1, SCALES_DIM_TILES = 2, SCALES_KEY_TILES32 = 3,
-       SCALES_DIM_TILES32 = 4 };
+// tile layouts feed the attention kernel (32x32x64 scaled MFMA, D a multiple
+// of 64): per 128-key tile, lane (h, rho) = 32 h + rho of that product finds
+// the bytes of its products next to each other (NB = D/8 bytes for K^, D/16
+// for V^T, at lane * NB), so one LDS read fetches them and the MFMA picks its
+// byte with op_sel.
+enum { SCALES_ROWS = 0, SCALES_KEY_TILES = 1, SCALES_DIM_TILES = 2 };
 
-// Byte of key row Rl (0..127 within its tile) and D block blk in a
-// KEY_TILES32 tile of 128 * D/32 bytes.  The score product of the 32x32x64
-// kernel covers 64-key chunk u = Rl / 64 with two 32-row blocks b; its A row
-// rho = 8 j + 4 x + k holds key 32 x + 16 b + 4 j + k of the chunk (FP6/FP4)
-// or 32 b + 16 x + 4 j + k (FP8), so that a lane's 32 outputs are the keys it
-// supplies to the P V product.  Lane half h reads D block 2 c + h of 64-wide
-// D chunk c; its byte for (u, b, c) is u*2nd + b*nd + c.
-__host__ __device__ inline int key_tile32_byte(int rl, int blk, int d, int bits) {
+// Byte of key row Rl (0..127 within its tile) and D block blk in a KEY_TILES
+// tile of 128 * D/32 bytes.  The score product covers 64-key chunk u = Rl / 64
+// with two 32-row blocks b; its A row rho = 8 j + 4 x + k holds key
+// 32 x + 16 b + 4 j + k of the chunk (FP6/FP4) or 32 b + 16 x + 4 j + k (FP8),
+// so that a lane's 32 outputs are the keys it supplies to the P V product.
+// Lane half h reads D block 2 c + h of 64-wide D chunk c; its byte for
+// (u, b, c) is u*2nd + b*nd + c.
+__host__ __device__ inline int key_tile_byte(int rl, int blk, int d, int bits) {
   const int nd = d / 64;
   const int u = rl >> 6, kk = rl & 63;
   const int hi = kk >> 5, mid = (kk >> 4) & 1, j = (kk >> 2) & 3, k = kk & 3;
@@ -61,9 +50,9 @@ __host__ __device__ inline int key_tile32_byte(int rl, int blk, int d, int bits)
   return (32 * (blk & 1) + rho) * 4 * nd + u * 2 * nd + b * nd + (blk >> 1);
 }
 // Byte of output row dd (0..D-1) and key block kb (0..3 within its tile) in a
-// DIM_TILES32 tile of 4 D bytes: the P V product's A row rho = dd % 32 of
+// DIM_TILES tile of 4 D bytes: the P V product's A row rho = dd % 32 of
 // 32-row block db = dd / 32, lane half h = kb % 2 of 64-key chunk u = kb / 2.
-__host__ __device__ inline int dim_tile32_byte(int dd, int kb, int d) {
+__host__ __device__ inline int dim_tile_byte(int dd, int kb, int d) {
   return (32 * (kb & 1) + (dd & 31)) * (d / 16) + (kb >> 1) * (d / 32) + (dd >> 5);
 }
 
@@ -72,8 +61,8 @@ hipError_t launch_mx_quant(const QuantArgs& a, int fmt, int mode, hipStream_t st
 // Fused attention for the heads [h0, h0+hrun) of every batch entry.  Q is
 // read as bf16 and MX-quantised in the kernel (times qmul); K^ and V^ come
 // from the quantiser.  Workspace slabs are indexed by w = b*hrun + (h - h0):
-//   K^ codes [BH][sk_alloc][D*bits/8], scales key-tile ordered
-//   V^ (transposed) codes [BH][D][sk_alloc*bits/8], scales dim-tile ordered
+//   K^ codes [BH][sk_alloc][D*bits/8], scales in the KEY_TILES layout
+//   V^ (transposed) codes [BH][D][sk_alloc*bits/8], scales in DIM_TILES
 // sk_alloc covers every key tile; the padding holds zero codes.
 struct AttnArgs {
   const uint16_t* q;             // bf16 [B][H][S][D]
@@ -92,9 +81,6 @@ struct AttnArgs {
 };
 
 hipError_t launch_fsa_fwd(const AttnArgs& a, int fmt, int D, int causal, hipStream_t stream);
-hipError_t launch_fsa_fwd_e4m3(const AttnArgs& a, int D, int causal, hipStream_t stream);
-// The kernel on the 32x32x64 scaled MFMA (scales in the *_TILES32 layouts).
-hipError_t launch_fsa_fwd32(const AttnArgs& a, int fmt, int D, int causal, hipStream_t stream);
 
 // Plain BF16 flash attention.
 constexpr int BF16_KEY_TILE = 64;

@@ -65,28 +65,14 @@ __device__ __forceinline__ void quantize_block(const QuantArgs& a, float (&v)[32
     const int nb = (int)a.nb_out;
     const int64_t bt = o / a.out_rows;
     const int64_t row = o - bt * a.out_rows;
-    const int rl = (int)(row & 127);
-    const int r = BITS == 8 ? 4 * ((rl >> 4) & 3) + (rl & 3) : 4 * (rl >> 5) + (rl & 3);
-    const int j = BITS == 8 ? ((rl >> 2) & 3) + 4 * (rl >> 6) : (rl >> 2) & 7;
-    so = bt * a.out_rows * nb + (row >> 7) * 128 * nb + (r * nb + b) * 8 + j;
+    so = bt * a.out_rows * nb + (row >> 7) * 128 * nb + key_tile_byte((int)(row & 127), (int)b, 32 * nb, BITS);
   } else if (a.scale_layout == SCALES_DIM_TILES) {
     // o = (batch, d), b = key block; blocks per row are a whole number of
     // 4-block tiles
     const int64_t bt = o / a.out_rows;
     const int d = (int)(o - bt * a.out_rows);
-    const int ndt = (int)(a.out_rows / 16);
     so = bt * a.out_rows * a.nb_out + (b >> 2) * 4 * a.out_rows +
-         ((d & 15) * 4 + (int)(b & 3)) * ndt + (d >> 4);
-  } else if (a.scale_layout == SCALES_KEY_TILES32) {
-    const int nb = (int)a.nb_out;
-    const int64_t bt = o / a.out_rows;
-    const int64_t row = o - bt * a.out_rows;
-    so = bt * a.out_rows * nb + (row >> 7) * 128 * nb + key_tile32_byte((int)(row & 127), (int)b, 32 * nb, BITS);
-  } else if (a.scale_layout == SCALES_DIM_TILES32) {
-    const int64_t bt = o / a.out_rows;
-    const int d = (int)(o - bt * a.out_rows);
-    so = bt * a.out_rows * a.nb_out + (b >> 2) * 4 * a.out_rows +
-         dim_tile32_byte(d, (int)(b & 3), (int)a.out_rows);
+         dim_tile_byte(d, (int)(b & 3), (int)a.out_rows);
   }
   a.scales[so] = sbyte;
 }
