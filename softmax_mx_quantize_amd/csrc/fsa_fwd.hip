@@ -84,20 +84,21 @@ __device__ __forceinline__ v16f mma32_sel(const opv<F>& a, const opv<F>& b, cons
   }
 }
 
-// XOR swizzles of the 16-byte chunk of a 128-byte LDS row.  The LDS serves a
-// 16-byte read 8 lanes at a time and an 8-byte read 16 lanes at a time (64
-// banks of 4 bytes: two rows per bank line, the row's parity picks the
-// half), so the rows a lane group reads together need distinct chunks within
-// each parity.  Score product: lanes n = 8j + 4x + k read key rows
-// 32x + 16b + 4j + k (+64u): rows differing in bits 0, 1, 2 and 5.  P V
-// product: lanes n read rows n (+32 db): bits 0-3.
-// FP8 operands are two 16-byte reads per lane; its score rows are
-// 32b + 16x + 4j + k, differing in bits 0-4.
+// XOR swizzles of the 16-byte chunk of a 128-byte LDS row.  The LDS has 64
+// banks of 4 bytes (two rows per bank line, the row's parity picks the half)
+// and serves a 16-byte read 16 lanes at a time, so the 16 rows those lanes
+// read need distinct chunks within each parity (the bank-conflict counter
+// confirms it).  Score product: lanes n = 8j + 4x + k of one 16-lane group
+// read key rows 32x + 16b + 4j + k (FP6/FP4) or 32b + 16x + 4j + k (FP8)
+// (+64u): rows differing in bits 0, 1, 2 and 5 (FP8: 4).  P V product:
+// lanes n read rows n (+32 db): bits 0-3.  FP6's 8-byte second piece is
+// read 32 lanes at a time; its half of the chunk follows row bit 3 (K^) or 4
+// (V^T), the fifth bit those 32 rows differ in.
 template <int BITS>
 __device__ __forceinline__ int swz_k32(int row) {
-  if (BITS == 8) return ((row >> 1) & 1) | (((row >> 4) & 1) << 1) | (((row >> 2) & 1) << 2);
-  return ((row >> 1) & 3) | (((row >> 5) & 1) << 2);
+  return ((row >> 1) & 3) | (((row >> (BITS == 8 ? 4 : 5)) & 1) << 2);
 }
+__device__ __forceinline__ int swz_v32(int row) { return (row >> 1) & 7; }
 
 // The lane's Q' operand for 64-wide D chunk c of the FP8 score product:
 // elements [64c + 16h, +16) and [64c + 32 + 16h, +16), i.e. half of D block
@@ -154,8 +155,6 @@ __device__ __forceinline__ v8i q_operand32_e4m3(const uint16_t* row, float mult,
   for (int i = 0; i < 8; ++i) o[i] = (int)w[i];
   return o;
 }
-template <int BITS>
-__device__ __forceinline__ int swz_v32(int row) { return BITS == 6 ? (row >> 1) & 7 : row & 7; }
 
 }  // namespace
 
@@ -269,17 +268,22 @@ fsa_fwd_kernel(AttnArgs a) {
   // scarce at FP6/FP4): K^ rows of even and odd k, V^T rows.
   // Global byte of logical chunk c within a row of `nblk` MX blocks
   // (chunks past the row's data re-read its first bytes).
-  auto chunk_src = [](int c, int nblk) __attribute__((always_inline)) {
-    if constexpr (BITS == 6) return (c >> 1) < nblk ? 24 * (c >> 1) + 16 * (c & 1) : 0;
+  // FP6: `hs` = 1 puts block bytes 16-23 in the upper half of their chunk
+  // (rows with bit 3 set for K^, bit 4 for V^T), so that the 32 lanes reading
+  // those 8-byte pieces together spread over both halves of the bank line.
+  auto chunk_src = [](int c, int nblk, int hs) __attribute__((always_inline)) {
+    if constexpr (BITS == 6) return (c >> 1) < nblk ? 24 * (c >> 1) + (c & 1) * (16 - 8 * hs) : 0;
     else return c < nblk * BITS / 4 ? 16 * c : 0;
   };
+  auto k_hs = [](int row) __attribute__((always_inline)) { return (row >> 3) & 1; };
+  auto v_hs = [](int row) __attribute__((always_inline)) { return (row >> 4) & 1; };
   int koff_e, koff_o, voff;
   {
     const int r_e = 8 * wave + (lane >> 3), r_o = r_e + 8 * NWAVES;   // rows of even / odd k
-    koff_e = (lane >> 3) * RB + chunk_src((lane & 7) ^ swz_k32<BITS>(r_e), NDB);
-    koff_o = (lane >> 3) * RB + chunk_src((lane & 7) ^ swz_k32<BITS>(r_o), NDB);
-    const int c = (lane & 7) ^ swz_v32<BITS>(r_e);
-    voff = (lane >> 3) * (int)v_row + chunk_src(c, 4);
+    koff_e = (lane >> 3) * RB + chunk_src((lane & 7) ^ swz_k32<BITS>(r_e), NDB, k_hs(r_e));
+    koff_o = (lane >> 3) * RB + chunk_src((lane & 7) ^ swz_k32<BITS>(r_o), NDB, k_hs(r_o));
+    const int c = (lane & 7) ^ swz_v32(r_e);
+    voff = (lane >> 3) * (int)v_row + chunk_src(c, 4, v_hs(r_e));
   }
   const int s_voff = lane * 4;
   auto issue_k = [&](int t, uint8_t* base) __attribute__((always_inline)) {
@@ -325,7 +329,7 @@ fsa_fwd_kernel(AttnArgs a) {
   // V^T row 32 db + n at logical byte (64u + 32h) * BITS/8.
   const int krow0 = KX * ((n >> 2) & 1) + 4 * (n >> 3) + (n & 3);
   const int ksw = swz_k32<BITS>(krow0);
-  const int vsw = swz_v32<BITS>(n);
+  const int vsw = swz_v32(n);
   // logical chunk of piece p of the lane's part of 64-element chunk m of a
   // row (FP8: elements [64m + 16h, +16) and [64m + 32 + 16h, +16); FP6/FP4:
   // MX block 2m + h)
@@ -339,12 +343,12 @@ fsa_fwd_kernel(AttnArgs a) {
   for (int c = 0; c < ND; ++c)
 #pragma unroll
     for (int p = 0; p < NPC; ++p)
-      k_off[c][p] = krow0 * RS + 16 * (piece_chunk(c, p) ^ ksw);
+      k_off[c][p] = krow0 * RS + 16 * (piece_chunk(c, p) ^ ksw) + (BITS == 6 && p == 1 ? 8 * k_hs(krow0) : 0);
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int p = 0; p < NPC; ++p)
-      v_off[u][p] = n * RS + 16 * (piece_chunk(u, p) ^ vsw);
+      v_off[u][p] = n * RS + 16 * (piece_chunk(u, p) ^ vsw) + (BITS == 6 && p == 1 ? 8 * v_hs(n) : 0);
   auto frag = [&](const uint8_t* base, const int* off, int imm) __attribute__((always_inline)) -> opv<F> {
     opv<F> o;
     if constexpr (BITS == 8) {
@@ -353,7 +357,13 @@ fsa_fwd_kernel(AttnArgs a) {
       o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w; o[4] = w.x; o[5] = w.y; o[6] = w.z; o[7] = w.w;
     } else if constexpr (BITS == 6) {
       const uint4 v = *reinterpret_cast<const uint4*>(base + off[0] + imm);
-      const uint2 w = *reinterpret_cast<const uint2*>(base + off[1] + imm);
+      // the 8-byte piece's address is made opaque: left visible, the
+      // compiler pairs the pieces of blocks 16 or 32 rows apart into one
+      // ds_read2st64_b64, whose two addresses hit the same banks (measured:
+      // a third of the LDS cycles in bank conflicts, 3 % slower)
+      int a1 = off[1] + imm;
+      asm volatile("" : "+v"(a1));
+      const uint2 w = *reinterpret_cast<const uint2*>(base + a1);
       o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w; o[4] = w.x; o[5] = w.y;
     } else {
       const uint4 v = *reinterpret_cast<const uint4*>(base + off[0] + imm);
