@@ -10,7 +10,8 @@ flash-attention baseline.  FLOPs are 4*B*H*S^2*D (halved for causal).
 Prints ONE JSON line.  Options:
   --gpus N        only 1 is supported (the path is a single-GPU kernel)
   --steps K       timed steps (default 20)
-  --warmup W      untimed steps first (default 3)
+  --warmup W      untimed steps first (default 10: the first launches after
+                  idle run up to 30 % slower while the clock settles)
   --no-cpu        skip the CPU-oracle baseline
   --only FMT      time only one element format (e4m3, e2m3, e2m1)
   --copy-bytes N  also run one plain device copy of N bytes (counter calibration)
@@ -183,7 +184,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default=None)
     ap.add_argument("--copy-bytes", type=int, default=0)
