@@ -32,20 +32,6 @@
 // the sum of query c and in rows 8-15 that of query 16 + c.
 #include "fsa_common.h"
 
-// Schedule of a tile (build-time knob): 0 leaves the order to the compiler,
-// 1 fences the three phases, 2 also interleaves fragment reads, products and
-// vector instructions within the phases (FSA32_VB / FSA32_VC vector
-// instructions after each product).
-#ifndef FSA32_SCHED
-#define FSA32_SCHED 1
-#endif
-#ifndef FSA32_VB
-#define FSA32_VB 18
-#endif
-#ifndef FSA32_VC
-#define FSA32_VC 14
-#endif
-
 namespace fsa {
 
 __device__ v16f mfma32_v6(v6i a, v6i b, v16f c, int cbsz, int blgp, int opsel_a, int sa,
@@ -490,28 +476,18 @@ fsa_fwd_kernel(AttnArgs a) {
   if (CAUSAL) n_clean = min(n_clean, (q_wave + 1) / KT);
   n_clean = min(n_clean, n_tiles);
 
-  // Scores of chunk u of the tile in `base`: y = 2^23 s + start.  In a
-  // masked tile an invisible key starts at -inf, so its y is -inf and its
-  // pattern 0.
-  auto qk_chunk = [&](const uint8_t* base, int key0, int u, auto masked_tag) __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    if constexpr (MASKED) {
-      const int lim = CAUSAL ? min(S, q + 1) : S;
-#pragma unroll
-      for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          acc[u][bb][i] = key0 + ckey(u, bb, i) < lim ? c0 : -INFINITY;
-    }
+  // Scores of chunk u of the tile in `base`: y = 2^23 s + start.  Masking
+  // (keys past S, or above the diagonal) is applied by the epilogue on the
+  // integer patterns, so masked tiles need no registers of their own.
+  auto qk_chunk = [&](const uint8_t* base, int u) __attribute__((always_inline)) {
     const uint2 ksc = k_scales(base);
 #pragma unroll
     for (int c = 0; c < ND; ++c)
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb) {
         const int byte = u * 2 * ND + bb * ND + c;
-        acc[u][bb] = mma32_sel<F>(kfrag(base, u, bb, c), qf[c],
-                                  (c == 0 && !MASKED) ? minit : acc[u][bb], pick(ksc, byte), byte,
-                                  qsc[c]);
+        acc[u][bb] = mma32_sel<F>(kfrag(base, u, bb, c), qf[c], c == 0 ? minit : acc[u][bb],
+                                  pick(ksc, byte), byte, qsc[c]);
       }
   };
   // Bit-pattern exponential + MX quantisation of P for chunk u.  FP6/FP4:
@@ -520,12 +496,18 @@ fsa_fwd_kernel(AttnArgs a) {
   // 16h + i and 32 + 16h + i); one swap of the half maxima with the lane 32
   // apart gives every lane the maximum of block h, which it scales in the
   // P V product, and a second swap hands it the byte of the other block.
-  auto epi = [&](int u) __attribute__((always_inline)) {
+  // In a masked tile an invisible key's pattern is set to 0 (P~ = 0), on
+  // the integer after the conversion.
+  auto epi = [&](int u, int key0, auto masked_tag) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int lim = CAUSAL ? min(S, q + 1) : S;
     float pv[32];
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
       const int o = BITS == 6 ? (e & 1) * 16 + (e >> 1) : e;   // FP6: evens, then odds
-      pv[o] = __uint_as_float(cvt_u32_trunc(acc[u][e >> 4][e & 15]));
+      uint32_t pat = cvt_u32_trunc(acc[u][e >> 4][e & 15]);
+      if constexpr (MASKED) pat = key0 + ckey(u, e >> 4, e & 15) < lim ? pat : 0u;
+      pv[o] = __uint_as_float(pat);
     }
     auto uv = [&](int o) __attribute__((always_inline)) { return __float_as_uint(pv[o]); };
     uint32_t m0 = max(max(uv(0), uv(1)), uv(2));
@@ -578,51 +560,27 @@ fsa_fwd_kernel(AttnArgs a) {
   using I1 = std::integral_constant<int, 1>;
   // Tile t+1 lands while tile t is read; after the barrier that ends step t
   // its stages take tile t+2.
-  // Per tile: the score products of chunk 1 beside the epilogue of chunk 0,
-  // then the P V products of chunk 0 beside the epilogue of chunk 1, so that
-  // one wave's matrix and vector work overlap.  ALWAYS_ISSUE: the loads of
-  // tile t+2 are issued even past the last tile (their stage is never read
-  // again; past the slab the buffer loads return zeros), which keeps the
-  // sweep over full tiles free of branches.
+  // One tile in three fenced phases: the scores of chunk 0; those of chunk 1
+  // beside the epilogue of chunk 0; the P V products of chunk 0 beside the
+  // epilogue of chunk 1; then those of chunk 1.  Left unfenced, the
+  // scheduler interleaves further and lengthens live ranges until registers
+  // spill (measured: every D=128 kernel spills, the FP8 one 335 registers),
+  // and spill reloads do not mix safely with the LDS DMA in flight, whose
+  // completions the compiler cannot see.  ALWAYS_ISSUE: the loads of tile
+  // t+2 are issued even past the last tile (their stage is never read again;
+  // past the slab the buffer loads return zeros), which keeps the sweep over
+  // full tiles free of branches.
   auto step = [&](int t, auto st_tag, auto masked_tag, auto always_tag) __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
     uint8_t* kb = kstage(st_tag);
     uint8_t* vb = vstage(st_tag);
-    qk_chunk(kb, t * KT, 0, masked_tag);
-#if FSA32_SCHED >= 1
+    qk_chunk(kb, 0);
     __builtin_amdgcn_sched_barrier(0);
-#endif
-    qk_chunk(kb, t * KT, 1, masked_tag);
-    epi(0);
-#if FSA32_SCHED >= 2
-    if constexpr (!MASKED) {
-#pragma unroll
-      for (int i = 0; i < 2 * ND; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, NPC, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, FSA32_VB, 0);
-      }
-    }
-#endif
-#if FSA32_SCHED >= 1
+    qk_chunk(kb, 1);
+    epi(0, t * KT, masked_tag);
     __builtin_amdgcn_sched_barrier(0);
-#endif
     pv_chunk(vb, 0);
-    epi(1);
-#if FSA32_SCHED >= 2
-    if constexpr (!MASKED) {
-#pragma unroll
-      for (int i = 0; i < NDB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, NPC, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, FSA32_VC, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
-#endif
-#if FSA32_SCHED >= 1
+    epi(1, t * KT, masked_tag);
     __builtin_amdgcn_sched_barrier(0);
-#endif
     pv_chunk(vb, 1);
     wait_dma();
     ring_barrier();
