@@ -29,7 +29,7 @@ struct QuantArgs {
 // Scale byte layouts.  ROWS: scales[row][block] (the public layout).  The two
 // tile layouts feed the attention kernel (32x32x64 scaled MFMA, D a multiple
 // of 64): per 128-key tile, lane (h, rho) = 32 h + rho of that product finds
-// the bytes of its products next to each other (NB = D/8 bytes for K^, D/16
+// the bytes of its products next to each other (NB = D/16 bytes for K^ and
 // for V^T, at lane * NB), so one LDS read fetches them and the MFMA picks its
 // byte with op_sel.
 enum { SCALES_ROWS = 0, SCALES_KEY_TILES = 1, SCALES_DIM_TILES = 2 };
