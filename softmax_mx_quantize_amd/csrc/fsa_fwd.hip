@@ -439,6 +439,8 @@ fsa_fwd_kernel(AttnArgs a) {
     const float z = __builtin_sqrtf(2.0f * __builtin_logf((float)nvis)) + 1.0f;
     // statistics of 2^23 s, back to binades (exact power-of-two scaling)
     mg = __builtin_fmaxf(mx, mean + z * sd) * 0x1p-23f + a.bias;
+    // stored now, so that it need not stay live across the sweep
+    if (q < S && hh == 0) a.row_mguess[bh * S + q] = mg;
   }
 
   // ---- main sweep (no online max, no rescaling; a block above the guess
@@ -615,10 +617,17 @@ fsa_fwd_kernel(AttnArgs a) {
   if constexpr (BITS == 8) lsum = L[0];
   else lsum = __shfl(L[0], n < 16 ? n : n + 16);
 
-  // ---- normalise and store: register i of O[db] is d = 32 db + 8 (i/4) + 4h + i%4
-  if (q < S) {
+  // ---- normalise and store: register i of O[db] is d = 32 db + 8 (i/4) + 4h + i%4.
+  // The row index is recomputed from an opaque lane index, so that the
+  // prologue's copy (used to load Q) need not stay live across the sweep.
+  int lane_e = lane;
+  asm volatile("" : "+v"(lane_e));
+  const int qe = q_wave + (lane_e & 31);
+  const int he = lane_e >> 5;
+  if (qe < S) {
     const float inv = 1.0f / lsum;
-    uint16_t* orow = a.out + (bh * S + q) * (int64_t)D;
+    const int64_t row = bh * S + qe;
+    uint16_t* orow = a.out + row * (int64_t)D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -627,12 +636,9 @@ fsa_fwd_kernel(AttnArgs a) {
                             ((uint32_t)f32_to_bf16_rne(O[db][4 * gq + 1] * inv) << 16);
         const uint32_t hi = f32_to_bf16_rne(O[db][4 * gq + 2] * inv) |
                             ((uint32_t)f32_to_bf16_rne(O[db][4 * gq + 3] * inv) << 16);
-        *reinterpret_cast<uint2*>(orow + 32 * db + 8 * gq + 4 * hh) = make_uint2(lo, hi);
+        *reinterpret_cast<uint2*>(orow + 32 * db + 8 * gq + 4 * he) = make_uint2(lo, hi);
       }
-    if (hh == 0) {
-      a.row_kappa[bh * S + q] = kap;
-      a.row_mguess[bh * S + q] = mg;
-    }
+    if (he == 0) a.row_kappa[row] = kap;
   }
   // tell the fallback kernel of this call that it has work (one vector store)
   if (__builtin_amdgcn_ballot_w64(kap > EXT) != 0 && lane == 0) *a.fb_flag = a.call_id;
