@@ -25,11 +25,14 @@
 // over that chunk: for FP6/FP4 one whole MX block of P, whose maximum and
 // scale need no lane exchange; for FP8 half of each of the chunk's blocks.
 //
-// Row sums l += 1 P~^T use one 16x16x128 product per chunk with an FP4 ones
-// operand: in that product lane 16 g + c supplies K elements [32g, 32g+32) of
-// column c, i.e. chunk keys [32 (g/2), +32) of query 16 (g%2) + c, so ones in
-// the A rows 0-7 for even g and rows 8-15 for odd g give, in output rows 0-7,
-// the sum of query c and in rows 8-15 that of query 16 + c.
+// Row sums l += 1 P~^T.  FP6/FP4: one 16x16x128 product per chunk with an
+// FP4 ones operand: in that product lane 16 g + c supplies K elements
+// [32g, 32g+32) of column c, i.e. chunk keys [32 (g/2), +32) of query
+// 16 (g%2) + c, so ones in the A rows 0-7 for even g and rows 8-15 for odd g
+// give, in output rows 0-7, the sum of query c and in rows 8-15 that of query
+// 16 + c.  FP8: that product's B operand would share one scale between the
+// half blocks of two queries, so the sum takes a 32x32x64 product with an
+// all-ones FP4 operand instead (every output row is the column's sum).
 #include "fsa_common.h"
 
 namespace fsa {
@@ -174,8 +177,8 @@ fsa_fwd_kernel(AttnArgs a) {
   constexpr int XLO = 127 + REF - CAP, XHI = 127 + REF + EXT;
   // LDS rows.  FP8 and FP4: logical chunk c is bytes [16c, 16c+16) of the
   // row.  FP6: each 24-byte block b takes two chunks, 2b (its bytes 0-15)
-  // and 2b+1 (bytes 16-23, the upper half unused), so that a lane's operand
-  // is one 16-byte and one 8-byte read into consecutive registers.
+  // and 2b+1 (bytes 16-23 in one half), so that a lane's operand is one
+  // 16-byte and one 8-byte read into consecutive registers.
   constexpr int NPC = BITS == 4 ? 1 : 2;     // LDS reads per operand
   // Score rows: block b of a chunk steps KB rows, the A row's x bit KX rows.
   constexpr int KB = BITS == 8 ? 32 : 16, KX = BITS == 8 ? 16 : 32;
@@ -233,10 +236,10 @@ fsa_fwd_kernel(AttnArgs a) {
   // ---- direct global -> LDS copies (each instruction: 8 LDS rows of 8
   // chunks per wave; lane i fills physical chunk i%8 of row i/8 with the
   // logical chunk the swizzle maps there; chunks past a row's data re-read
-  // its chunk 0).  Row R = 8 (wave + 4k) + i/8 of a K^ tile has swizzle
-  // bits 1-2 from i/8 and bit 5 from k; a V^T row's swizzle depends on i/8
-  // (and, for FP6, on the wave's parity) only.  The tile and row offsets go
-  // in the scalar operand.
+  // its chunk 0).  Row R = 8 (wave + 4k) + i/8: its bits 1-2 come from i/8,
+  // bits 3-4 from the wave and bit 5 from k, so a lane needs one K^ offset
+  // for even and one for odd k, and one V^T offset.  The tile and row
+  // offsets go in the scalar operand.
   constexpr int NK_DMA = KT * 8 / 64 / NWAVES;
   constexpr int NV_DMA = D * 8 / 64 / NWAVES;
   constexpr int NKS = KS_BYTES / 256;
@@ -250,8 +253,6 @@ fsa_fwd_kernel(AttnArgs a) {
       __builtin_amdgcn_make_buffer_rsrc((void*)ks, (short)0, a.sk_alloc * NDB, 0x00020000);
   const __amdgpu_buffer_rsrc_t vs_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)vs, (short)0, D * vs_row, 0x00020000);
-  // Lane offsets of the copies, fixed for the sweep (registers are not
-  // scarce at FP6/FP4): K^ rows of even and odd k, V^T rows.
   // Global byte of logical chunk c within a row of `nblk` MX blocks
   // (chunks past the row's data re-read its first bytes).
   // FP6: `hs` = 1 puts block bytes 16-23 in the upper half of their chunk
