@@ -14,6 +14,9 @@ Prints ONE JSON line.  Options:
                   idle run up to 30 % slower while the clock settles)
   --no-cpu        skip the CPU-oracle baseline
   --only FMT      time only one element format (e4m3, e2m3, e2m1)
+  --workload NAME time another workload of workloads.py instead (its own
+                  formats, per head for the hybrid schedule) and print one
+                  JSON line for it; no BF16 or CPU legs
   --copy-bytes N  also run one plain device copy of N bytes (counter calibration)
   --write-traffic FETCH_DB WRITE_DB
                   no timing: read two rocprofv3 --pmc result databases (one
@@ -180,6 +183,46 @@ def cpu_baseline(w, budget_s: float = 15.0):
     }
 
 
+def bench_workload(name: str, steps: int, warmup: int) -> dict:
+    """Whole-call and kernel TFLOP/s of one workload in its own formats."""
+    import numpy as np
+    import torch
+    import softmax_mx_quantize_amd as fsa
+    import workloads as W
+    w = W.WORKLOADS[name]
+    print("[bench] generating %s inputs" % w.name, file=sys.stderr, flush=True)
+    qb, kb, vb = W.generate(w)
+    dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = dev(qb), dev(kb), dev(vb)
+    del qb, kb, vb
+    hf = list(w.head_fmts)
+    kw = {} if len(set(hf)) == 1 else {"head_fmt": hf}
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    call = lambda ev=None: fsa.attention_fwd(q, k, v, hf[0], w.causal, out=out, event_after_quantize=ev, **kw)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for m in mids:
+        m.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        call(mids[i])
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    kern_ms = sum(m.elapsed_time(e) for m, e in zip(mids, ends)) / steps
+    peak = max(PEAK_TFLOPS[f] for f in hf)
+    return {"workload": w.name, "B": w.B, "H": w.H, "S": w.S, "D": w.D, "causal": w.causal,
+            "head_fmts": sorted(set(hf)), "steps": steps, "warmup": warmup,
+            "ms_per_step": wall_ms, "tflops": w.flops / (wall_ms * 1e-3) / 1e12,
+            "kernel_ms": kern_ms, "kernel_tflops": w.flops / (kern_ms * 1e-3) / 1e12,
+            "kernel_frac_of_peak": w.flops / (kern_ms * 1e-3) / 1e12 / peak, "peak_tflops": peak}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -187,6 +230,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default=None)
+    ap.add_argument("--workload", default=None)
     ap.add_argument("--copy-bytes", type=int, default=0)
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"))
     args = ap.parse_args()
@@ -210,6 +254,9 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 2
+    if args.workload:
+        print(json.dumps(bench_workload(args.workload, args.steps, args.warmup)), flush=True)
+        return 0
     w = W.WORKLOADS["video_dit_e4m3"]
     print("[bench] generating %s inputs" % w.name, file=sys.stderr, flush=True)
     qb, kb, vb = W.generate(w)

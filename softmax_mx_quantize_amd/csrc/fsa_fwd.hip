@@ -655,7 +655,10 @@ hipError_t launch32_3(const AttnArgs& a, hipStream_t stream) {
   dim3 grid((n_items + 7) / 8 * 8);
   hipLaunchKernelGGL((fsa_fwd_kernel<F, D, CAUSAL>), grid, dim3(256), 0, stream, a);
   const int n_groups = (a.S + 31) / 32 * a.B * a.hrun;
-  hipLaunchKernelGGL((fsa_fallback_kernel<F, D, CAUSAL>), dim3(n_groups < 1024 ? n_groups : 1024),
+  // Up to 8192 one-wave workgroups: the groups of rows beyond EXT then run
+  // side by side (the sweep of one group is bound by load latency); an idle
+  // fallback still costs ~4 us.
+  hipLaunchKernelGGL((fsa_fallback_kernel<F, D, CAUSAL>), dim3(n_groups < 8192 ? n_groups : 8192),
                      dim3(64), 0, stream, a);
   return hipGetLastError();
 }
