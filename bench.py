@@ -103,15 +103,17 @@ def write_traffic(fetch_db: str, write_db: str, copy_bytes: int) -> dict:
     out = {"kernel_hash": kernel_hash(), "copy_bytes": copy_bytes,
            "fetch_bytes_per_count_byte": f_scale, "write_bytes_per_count_byte": w_scale,
            "bytes_per_launch": {}, "fetch_bytes": {}, "write_bytes": {}}
+    # a call launches the kernel twice (the sweep, then the re-based pass
+    # that exits at once unless a row is beyond its reach): both count
     for k in fetch:
         if "fsa_fwd_kernel<" not in k:
             continue
         fmt = FMT_OF_TEMPLATE[k.split("fsa_fwd_kernel<")[1].split(",")[0].strip()]
         fb = fetch[k] * 1024.0 * f_scale
         wb = write.get(k, 0.0) * 1024.0 * w_scale
-        out["fetch_bytes"][fmt] = fb
-        out["write_bytes"][fmt] = wb
-        out["bytes_per_launch"][fmt] = fb + wb
+        out["fetch_bytes"][fmt] = out["fetch_bytes"].get(fmt, 0.0) + fb
+        out["write_bytes"][fmt] = out["write_bytes"].get(fmt, 0.0) + wb
+        out["bytes_per_launch"][fmt] = out["bytes_per_launch"].get(fmt, 0.0) + fb + wb
     with open(os.path.join(ROOT, "profiles", "fsa_fwd_traffic.json"), "w") as f:
         json.dump(out, f, indent=1)
     return out

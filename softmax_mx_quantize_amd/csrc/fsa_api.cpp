@@ -63,7 +63,7 @@ int workspace(size_t need, uint8_t** out) {
   return FSA_OK;
 }
 
-// Ids that tell a fallback kernel whether its own call's main kernel asked
+// Ids that tell the fallback pass whether its own call's first pass asked
 // for it (the flag word keeps the last id that did).
 uint64_t next_call_id() {
   static std::atomic<uint64_t> counter{0};
@@ -196,7 +196,7 @@ int fsa_attention_fwd_ex(const void* q, const void* k, const void* v, void* out,
     rl.vc = cv.take((size_t)(nbh * D * sk_alloc * bits / 8));
     rl.vs = cv.take((size_t)(nbh * D * (sk_alloc / 32)));
   }
-  // per-row frozen max and fallback offset, which the fallback kernel reads
+  // per-row frozen max and fallback offset, which the fallback pass reads
   // back; the caller's arrays when given
   const int64_t n_rows = (int64_t)B * H * S;
   const bool own_kappa = !(opt && opt->row_kappa);

@@ -1,5 +1,4 @@
-// Device helpers of the fused-softmax attention kernels (gfx950) and the
-// fallback kernel for rows far above their frozen max.
+// Device helpers of the fused-softmax attention kernel (gfx950).
 //
 // What the path computes (Fused-Softmax for efficient quantized attention,
 // summary; Moving softmax to matrix operations speeds up AI inference by over
@@ -22,7 +21,8 @@
 //      Softmax, abstract, uses it);
 //   5. a block above the guess takes a larger E8M0 scale, which is the
 //      whole-binade re-basing of the fallback up to a common power of two;
-//      rows beyond 64 binades are recomputed by the fallback kernel here;
+//      rows beyond 64 binades are recomputed by a second, re-based pass
+//      of the same kernel;
 //   6. out = bf16(O / l).
 #pragma once
 
@@ -37,16 +37,10 @@ namespace fsa {
 // The builtin of the scaled MFMA only takes 8-dword operands; the narrow
 // FP6/FP4 forms of the same intrinsic are reached through its overloaded
 // LLVM name.  (Compiler instructions: the hazard handling is the same.)
-__device__ v4f mfma_scale_v6(v6i a, v6i b, v4f c, int cbsz, int blgp, int opsel_a, int sa,
-                             int opsel_b, int sb)
-    __asm("llvm.amdgcn.mfma.scale.f32.16x16x128.f8f6f4.v6i32.v6i32");
 __device__ v4f mfma_scale_v4(v4i a, v4i b, v4f c, int cbsz, int blgp, int opsel_a, int sa,
                              int opsel_b, int sb)
     __asm("llvm.amdgcn.mfma.scale.f32.16x16x128.f8f6f4.v4i32.v4i32");
 // Mixed widths: an FP4 A operand with an FP8 or FP6 B operand.
-__device__ v4f mfma_scale_v4_v8(v4i a, v8i b, v4f c, int cbsz, int blgp, int opsel_a, int sa,
-                                int opsel_b, int sb)
-    __asm("llvm.amdgcn.mfma.scale.f32.16x16x128.f8f6f4.v4i32.v8i32");
 __device__ v4f mfma_scale_v4_v6(v4i a, v6i b, v4f c, int cbsz, int blgp, int opsel_a, int sa,
                                 int opsel_b, int sb)
     __asm("llvm.amdgcn.mfma.scale.f32.16x16x128.f8f6f4.v4i32.v6i32");
@@ -71,9 +65,9 @@ constexpr int REF = 62;
 // its frozen max.
 constexpr int HI_BINADE = 1 << 18;
 // Largest guess-relative block binade the main sweep absorbs by block shifts
-// alone; rows above it go to the fallback kernel.
+// alone; rows above it go to the re-based fallback pass.
 constexpr int EXT = 64;
-static_assert(HI_BINADE > EXT, "clamped binades must reach the fallback kernel");
+static_assert(HI_BINADE > EXT, "clamped binades must reach the fallback pass");
 template <int M>
 __device__ __forceinline__ int block_binade(float y) {
   const float yc = __builtin_amdgcn_fmed3f(y, 0.0f, 8388608.0f * (float)(127 + REF + HI_BINADE));
@@ -122,69 +116,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   return (uint16_t)(u >> 16);
 }
 
-// Position p (0..31) of a lane's operand list -> index along the 128-wide K
-// dimension for lane group g.
-template <int F>
-__device__ __forceinline__ int kpos(int g, int p) {
-  if (Fmt<F>::bits == 8) return p < 16 ? 16 * g + p : 64 + 16 * g + (p - 16);
-  return 32 * g + p;
-}
-
-// A lane's 32 operand elements of the 16x16x128 product straight from a
-// global row (`len` valid K elements; past it, zeros).
-template <int F>
-__device__ __forceinline__ opv<F> global_operand(const uint8_t* row, int g, int len) {
-  opv<F> o = zero_operand<F>();
-  if constexpr (Fmt<F>::bits == 8) {
-    if (16 * g < len) {
-      uint4 a = *reinterpret_cast<const uint4*>(row + 16 * g);
-      o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
-    }
-    if (64 + 16 * g < len) {
-      uint4 b = *reinterpret_cast<const uint4*>(row + 64 + 16 * g);
-      o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
-    }
-  } else if constexpr (Fmt<F>::bits == 6) {
-    if (32 * g < len) {
-      const uint2* p = reinterpret_cast<const uint2*>(row + 24 * g);
-      uint2 a = p[0], b = p[1], c = p[2];
-      o[0] = a.x; o[1] = a.y; o[2] = b.x; o[3] = b.y; o[4] = c.x; o[5] = c.y;
-    }
-  } else {
-    if (32 * g < len) {
-      uint4 a = *reinterpret_cast<const uint4*>(row + 16 * g);
-      o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
-    }
-  }
-  return o;
-}
-
-// The 16x16x128 scaled MFMA with operands of the format's own width.
-// OA selects the byte of `sa` that scales A (op_sel); B's scale is byte 0.
-template <int F, int OA = 0>
-__device__ __forceinline__ v4f mfma(const opv<F>& a, const opv<F>& b, const v4f& c, int sa, int sb) {
-  if constexpr (Fmt<F>::bits == 8)
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, Fmt<F>::mfma, Fmt<F>::mfma,
-                                                            OA, sa, 0, sb);
-  else if constexpr (Fmt<F>::bits == 6)
-    return mfma_scale_v6(a, b, c, Fmt<F>::mfma, Fmt<F>::mfma, OA, sa, 0, sb);
-  else
-    return mfma_scale_v4(a, b, c, Fmt<F>::mfma, Fmt<F>::mfma, OA, sa, 0, sb);
-}
-// Row sums l += 1 P~^T on the matrix core: the all-ones A operand is held
-// in FP4 (E2M1 1.0 = 0x2 in every nibble, 4 registers) whatever the format
-// of P~; FP4 ones times P~ in its own format is the same exact sum.
-__device__ __forceinline__ v4i ones_fp4() {
-  v4i o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = 0x22222222;
-  return o;
-}
+// Row sums l += 1 P~^T on the matrix core with an FP4 ones operand (E2M1
+// 1.0 = 0x2 per nibble, 4 registers) against P~ in its own format: FP4 ones
+// times P~ is the same exact sum.
 template <int F>
 __device__ __forceinline__ v4f row_sum(const v4i& ones, const opv<F>& p, const v4f& c, int sp) {
-  if constexpr (Fmt<F>::bits == 8)
-    return mfma_scale_v4_v8(ones, p, c, Fmt<FMT_E2M1>::mfma, Fmt<F>::mfma, 0, 127, 0, sp);
-  else if constexpr (Fmt<F>::bits == 6)
+  static_assert(Fmt<F>::bits != 8, "FP8 row sums take the 32x32x64 product");
+  if constexpr (Fmt<F>::bits == 6)
     return mfma_scale_v4_v6(ones, p, c, Fmt<FMT_E2M1>::mfma, Fmt<F>::mfma, 0, 127, 0, sp);
   else
     return mfma_scale_v4(ones, p, c, Fmt<FMT_E2M1>::mfma, Fmt<F>::mfma, 0, 127, 0, sp);
@@ -288,217 +226,5 @@ __device__ __forceinline__ opv<F> q_operand(const uint16_t* row, float mult, int
 }
 
 }  // namespace
-
-// Fallback for rows whose scores exceed the frozen max by more than EXT
-// binades: one wave per 32 query rows (two subtiles of 16).  A wave whose
-// rows all stayed within EXT exits at once; otherwise it recomputes its rows
-// from global memory with each row's reference raised by its kappa
-// (accumulator start and block shifts re-based, no in-loop clamp), reading
-// the frozen max and kappa the main kernel stored, and overwrites their
-// outputs.  Rows within EXT come out as the main kernel left them (the
-// re-based sums are the same up to the common power-of-two factor).  It runs
-// on the 16x16x128 product (lane (g, r) = 16 g + r; FP8 operands hold K
-// elements [16g, +16) and [64+16g, +16), FP6/FP4 ones [32g, +32)) and reads
-// the tile-ordered scales through the layout functions.
-template <int F, int D, bool CAUSAL>
-__device__ __forceinline__ void fallback_group(const AttnArgs& a, int64_t grp) {
-  constexpr int NSUB = 2;
-  constexpr int BITS = Fmt<F>::bits;
-  constexpr int MB = Fmt<F>::mbits;
-  constexpr int PL = F == FMT_E4M3 ? Fmt<F>::emax - 1 : Fmt<F>::emax;
-  constexpr int CAP = 127 - PL;
-  constexpr int RB = D * BITS / 8;
-  constexpr int NDB = D / 32;
-  constexpr int NDT = D / 16;
-  constexpr int VRB = KT * BITS / 8;
-  const int lane = threadIdx.x;
-  const int g = lane >> 4;
-  const int r = lane & 15;
-  const int S = a.S;
-  const int ng = (S + 16 * NSUB - 1) / (16 * NSUB);
-  const int64_t wi = grp / ng;
-  if (wi >= (int64_t)a.B * a.hrun) return;
-  const int b = (int)wi / a.hrun;
-  const int h = a.h0 + ((int)wi - b * a.hrun);
-  const int64_t bh = (int64_t)b * a.H + h;
-  const int q0 = (int)(grp - wi * ng) * 16 * NSUB;
-
-  int kap[NSUB];
-  float mg[NSUB];
-  bool extreme = false;
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    const int q = q0 + 16 * s + r;
-    kap[s] = q < S ? a.row_kappa[bh * S + q] : 0;
-    mg[s] = q < S ? a.row_mguess[bh * S + q] : 0.0f;
-    extreme |= kap[s] > EXT;
-  }
-  if (__builtin_amdgcn_ballot_w64(extreme) == 0) return;
-
-  const uint8_t* kc = a.kc + wi * (int64_t)a.sk_alloc * RB;
-  const uint8_t* ks = a.ks + wi * (int64_t)a.sk_alloc * NDB;
-  const int64_t v_row = (int64_t)a.sk_alloc * BITS / 8;
-  const uint8_t* vc = a.vc + wi * (int64_t)D * v_row;
-  const int vs_row = a.sk_alloc / 32;
-  const uint8_t* vs = a.vs + wi * (int64_t)D * vs_row;
-  // scale byte of tile key kk (read by lane (g, r) as slice j) and D block g
-  auto ks_byte = [&](int kk, int j) __attribute__((always_inline)) {
-    return key_tile_byte(kk, g, D, BITS);
-  };
-
-  opv<F> qf[NSUB];
-  int qsc[NSUB];
-  v4f mk[NSUB], O[NSUB][NDT], L[NSUB];
-  const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    const int q = q0 + 16 * s + r;
-    qf[s] = q_operand<F, D>(q < S ? a.q + (bh * S + q) * (int64_t)D : nullptr, a.qmul, g, qsc[s]);
-    L[s] = zero4;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) O[s][dt] = zero4;
-  }
-  const v4i ones = ones_fp4();
-
-  int n_tiles = (S + KT - 1) / KT;
-  if (CAUSAL) {
-    const int last_q = q0 + 16 * NSUB - 1 < S - 1 ? q0 + 16 * NSUB - 1 : S - 1;
-    n_tiles = min(n_tiles, last_q / KT + 1);
-  }
-  // The main sweep measures binades on the integer patterns, which saturate
-  // some 320 binades above the guess; take kappa again from the fp32 values
-  // (exact to HI_BINADE).
-  {
-    v4f m0init[NSUB];
-    int km[NSUB];
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      const float c0 = __builtin_fmaf(-8388608.0f, mg[s], 8388608.0f * (float)(127 + REF));
-      m0init[s] = v4f{c0, c0, c0, c0};
-      km[s] = -(1 << 30);
-    }
-    for (int t = 0; t < n_tiles; ++t) {
-      const int key0 = t * KT;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int kk = kpos<F>(r >> 2, 4 * j + (r & 3));
-        const int sc = g < NDB ? (int)ks[(int64_t)t * KT * NDB + ks_byte(kk, j)] : 127;
-        const opv<F> kf = global_operand<F>(kc + (int64_t)(key0 + kk) * RB, g, D);
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) {
-          const v4f y = mfma<F>(kf, qf[s], m0init[s], sc, qsc[s]);
-          const int q = q0 + 16 * s + r;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = key0 + kpos<F>(g, 4 * j + i);
-            const bool vis = key < S && (!CAUSAL || key <= q);
-            // the binade of each element bounds that of its block's maximum
-            if (vis) km[s] = max(km[s], block_binade<MB>(y[i]));
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      int k = km[s];
-      k = max(k, __shfl_xor(k, 16));
-      k = max(k, __shfl_xor(k, 32));
-      kap[s] = k > 0 ? k : 0;
-      const float c0 = __builtin_fmaf(-8388608.0f, mg[s], 8388608.0f * (float)(127 + REF - kap[s]));
-      mk[s] = v4f{c0, c0, c0, c0};
-      const int q = q0 + 16 * s + r;
-      if (g == 0 && q < S) a.row_kappa[bh * S + q] = kap[s];
-    }
-  }
-  for (int t = 0; t < n_tiles; ++t) {
-    const int key0 = t * KT;
-    v4f acc[NSUB][8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int kk = kpos<F>(r >> 2, 4 * j + (r & 3));
-      const int sc = g < NDB ? (int)ks[(int64_t)t * KT * NDB + ks_byte(kk, j)] : 127;
-      const opv<F> kf = global_operand<F>(kc + (int64_t)(key0 + kk) * RB, g, D);
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) acc[s][j] = mfma<F>(kf, qf[s], mk[s], sc, qsc[s]);
-    }
-    opv<F> pw[NSUB];
-    int psc[NSUB];
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      const int q = q0 + 16 * s + r;
-      float x[32];
-#pragma unroll
-      for (int p = 0; p < 32; ++p) {
-        const int key = key0 + kpos<F>(g, p);
-        const bool vis = key < S && (!CAUSAL || key <= q);
-        x[p] = vis ? acc[s][p >> 2][p & 3] : -INFINITY;
-      }
-      float m0 = x[0], m1 = x[16];
-#pragma unroll
-      for (int p = 1; p < 16; ++p) { m0 = __builtin_fmaxf(m0, x[p]); m1 = __builtin_fmaxf(m1, x[16 + p]); }
-      if (BITS == 8) {
-        m0 = __builtin_fmaxf(m0, __shfl_xor(m0, 16));
-        m1 = __builtin_fmaxf(m1, __shfl_xor(m1, 16));
-      } else {
-        m0 = __builtin_fmaxf(m0, m1);
-        m1 = m0;
-      }
-      // binades relative to the raised reference: shifts need no EXT clamp
-      const int sb0 = 127 - PL - min(-block_binade<MB>(m0), CAP);
-      const int sb1 = 127 - PL - min(-block_binade<MB>(m1), CAP);
-      float pv[32];
-#pragma unroll
-      for (int p = 0; p < 32; ++p) {
-        const int key = key0 + kpos<F>(g, p);
-        const bool vis = key < S && (!CAUSAL || key <= q);
-        const uint32_t u = cvt_u32_trunc(acc[s][p >> 2][p & 3]);
-        pv[p] = __uint_as_float(vis ? u : 0u);
-      }
-      uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      Pack32<F, false>::run(pv, w, conv_scale(sb0), conv_scale(sb1));
-#pragma unroll
-      for (int i = 0; i < Operand<F>::words; ++i) pw[s][i] = (int)w[i];
-      psc[s] = p_scale<BITS>(sb0, sb1, g);
-    }
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const int d = 16 * dt + r;
-      const opv<F> vf = global_operand<F>(vc + d * v_row + (int64_t)t * VRB, g, KT);
-      const int vsc = (int)vs[(int64_t)t * 4 * D + dim_tile_byte(d, g, D)];
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) O[s][dt] = mfma<F>(vf, pw[s], O[s][dt], vsc, psc[s]);
-    }
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) L[s] = row_sum<F>(ones, pw[s], L[s], psc[s]);
-  }
-
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    const int q = q0 + 16 * s + r;
-    if (q < S) {
-      const float inv = 1.0f / L[s][0];
-      uint16_t* orow = a.out + (bh * S + q) * (int64_t)D;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const uint32_t lo = f32_to_bf16_rne(O[s][dt][0] * inv) | ((uint32_t)f32_to_bf16_rne(O[s][dt][1] * inv) << 16);
-        const uint32_t hi = f32_to_bf16_rne(O[s][dt][2] * inv) | ((uint32_t)f32_to_bf16_rne(O[s][dt][3] * inv) << 16);
-        *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = make_uint2(lo, hi);
-      }
-    }
-  }
-}
-
-// Grid-stride over groups of 32 query rows; a call whose main kernel found
-// no row beyond EXT binades (flag not stamped with this call's id) exits
-// after one load.
-template <int F, int D, bool CAUSAL>
-__global__ void __launch_bounds__(64) fsa_fallback_kernel(AttnArgs a) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  if (*a.fb_flag != a.call_id) return;
-  const int64_t n_groups = (int64_t)(a.S + 31) / 32 * a.B * a.hrun;
-  for (int64_t grp = blockIdx.x; grp < n_groups; grp += gridDim.x)
-    fallback_group<F, D, CAUSAL>(a, grp);
-#endif  // __HIP_DEVICE_COMPILE__
-}
 
 }  // namespace fsa

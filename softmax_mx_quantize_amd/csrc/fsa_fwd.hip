@@ -147,7 +147,13 @@ __device__ __forceinline__ v8i q_operand32_e4m3(const uint16_t* row, float mult,
 
 }  // namespace
 
-template <int F, int D, bool CAUSAL>
+// REBASE: the fallback pass of a call.  A workgroup does nothing unless
+// the first pass stamped the call's flag and left one of its rows more than
+// EXT binades above its frozen max; it then measures each row's offset kappa
+// exactly from the fp32 scores (a scores-only sweep), sweeps again from the
+// reference raised by kappa whole binades (no shift is then clamped), and
+// overwrites the rows the first pass left beyond EXT.
+template <int F, int D, bool CAUSAL, bool REBASE>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
 fsa_fwd_kernel(AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer-resource types exist only in the device pass
@@ -209,7 +215,9 @@ fsa_fwd_kernel(AttnArgs a) {
   const int nq = (a.S + QW - 1) / QW;
   const int n_items = nq * a.B * a.hrun;
   const int per_xcd = (n_items + 7) / 8;
-  const int item = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  // (The REBASE pass deals its items round-robin instead: its few busy
+  // workgroups, often all from one head, then spread over every XCD.)
+  const int item = REBASE ? (int)blockIdx.x : (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
   if (item >= n_items) return;
   const int64_t wi = item / nq;
   const int b = (int)wi / a.hrun;
@@ -291,6 +299,14 @@ fsa_fwd_kernel(AttnArgs a) {
                 t * VRB + (wave + NWAVES * k) * 8 * (int)v_row);
     dma_lds4(vs_rsrc, lb + V_BYTES + vs_soff, s_voff, t * VS_BYTES + vs_soff);
   };
+
+  // first pass's offset of this lane's row (REBASE)
+  [[maybe_unused]] int kap_in = 0;
+  if constexpr (REBASE) {
+    if (*a.fb_flag != a.call_id) return;                    // the same for every workgroup
+    kap_in = q < S ? a.row_kappa[bh * S + q] : 0;
+    if (!__syncthreads_or(kap_in > EXT)) return;            // the same for the whole workgroup
+  }
 
   if (n_tiles > 0) {
     issue_k(0, kl0);
@@ -390,7 +406,9 @@ fsa_fwd_kernel(AttnArgs a) {
   wait_dma();
   __syncthreads();
   if (n_tiles > 1) { issue_k(1, kl1); issue_v(1, vl1); }
-  {
+  if constexpr (REBASE) {
+    mg = q < S ? a.row_mguess[bh * S + q] : 0.0f;
+  } else {
     const uint2 ksc = k_scales(kl0);
     v16f s0[2][2];
 #pragma unroll
@@ -459,7 +477,7 @@ fsa_fwd_kernel(AttnArgs a) {
   for (int i = 0; i < (BITS == 8 ? 16 : 4); ++i) L[i] = 0.f;
   int kmax = -1000000;
   // accumulator start: fp32(2^23 (127 + R) - 2^23 m~), one rounding
-  const float c0 = __builtin_fmaf(-8388608.0f, mg, 8388608.0f * (127 + REF));
+  float c0 = __builtin_fmaf(-8388608.0f, mg, 8388608.0f * (127 + REF));
   v16f minit;
 #pragma unroll
   for (int i = 0; i < 16; ++i) minit[i] = c0;
@@ -594,6 +612,46 @@ fsa_fwd_kernel(AttnArgs a) {
   };
   using F0 = std::false_type;
   using T1 = std::true_type;
+  [[maybe_unused]] int kap_x = 0;
+  if constexpr (REBASE) {
+    // scores-only sweep: the largest binade of any visible score above the
+    // frozen max, exact to HI_BINADE (the bit patterns saturate far sooner)
+    int km = -(1 << 30);
+    const int lim = CAUSAL ? min(S, q + 1) : S;
+    auto pstep = [&](int tt, auto st_tag) __attribute__((always_inline)) {
+      uint8_t* kb = kstage(st_tag);
+      qk_chunk(kb, 0);
+      qk_chunk(kb, 1);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (tt * KT + ckey(u, bb, i) < lim) km = max(km, block_binade<MB>(acc[u][bb][i]));
+      wait_dma();
+      ring_barrier();
+      if (tt + 2 < n_tiles) {
+        issue_k(tt + 2, kb);
+        issue_v(tt + 2, vstage(st_tag));
+      }
+    };
+    for (int tt = 0; tt < n_tiles; tt += 2) {
+      pstep(tt, I0{});
+      if (tt + 1 < n_tiles) pstep(tt + 1, I1{});
+    }
+    km = max(km, __shfl_xor(km, 32));
+    kap_x = km > 0 ? km : 0;
+    // restart the ring for the sweep from the raised reference
+    issue_k(0, kl0);
+    issue_v(0, vl0);
+    wait_dma();
+    __syncthreads();
+    if (n_tiles > 1) { issue_k(1, kl1); issue_v(1, vl1); }
+    c0 = __builtin_fmaf(-8388608.0f, mg, 8388608.0f * (float)(127 + REF - kap_x));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) minit[i] = c0;
+  }
   int t = 0;
   // full tiles, two per iteration, branch-free
   for (; t + 1 < n_clean; t += 2) {
@@ -608,10 +666,11 @@ fsa_fwd_kernel(AttnArgs a) {
   }
 
   // row offset in binades (the oracle's kappa); rows beyond EXT come out
-  // wrong here and are recomputed by the fallback kernel
+  // wrong here and are recomputed by the REBASE pass
   int kap = kmax - (127 + REF);
   kap = max(kap, __shfl_xor(kap, 32));
   kap = kap > 0 ? kap : 0;
+  if constexpr (REBASE) kap = kap_x;
   // row sum of query n: FP8 in every register of the lane; FP6/FP4 output
   // row 0 of lane n (n < 16) or row 8 of lane n + 16
   float lsum;
@@ -625,7 +684,7 @@ fsa_fwd_kernel(AttnArgs a) {
   asm volatile("" : "+v"(lane_e));
   const int qe = q_wave + (lane_e & 31);
   const int he = lane_e >> 5;
-  if (qe < S) {
+  if (qe < S && (!REBASE || kap_in > EXT)) {
     const float inv = 1.0f / lsum;
     const int64_t row = bh * S + qe;
     uint16_t* orow = a.out + row * (int64_t)D;
@@ -641,8 +700,8 @@ fsa_fwd_kernel(AttnArgs a) {
       }
     if (he == 0) a.row_kappa[row] = kap;
   }
-  // tell the fallback kernel of this call that it has work (one vector store)
-  if (__builtin_amdgcn_ballot_w64(kap > EXT) != 0 && lane == 0) *a.fb_flag = a.call_id;
+  // tell the REBASE pass of this call that it has work (one vector store)
+  if (!REBASE && __builtin_amdgcn_ballot_w64(kap > EXT) != 0 && lane == 0) *a.fb_flag = a.call_id;
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -653,13 +712,9 @@ hipError_t launch32_3(const AttnArgs& a, hipStream_t stream) {
   constexpr int QW = 128;
   const int n_items = (a.S + QW - 1) / QW * a.B * a.hrun;
   dim3 grid((n_items + 7) / 8 * 8);
-  hipLaunchKernelGGL((fsa_fwd_kernel<F, D, CAUSAL>), grid, dim3(256), 0, stream, a);
-  const int n_groups = (a.S + 31) / 32 * a.B * a.hrun;
-  // Up to 8192 one-wave workgroups: the groups of rows beyond EXT then run
-  // side by side (the sweep of one group is bound by load latency); an idle
-  // fallback still costs ~4 us.
-  hipLaunchKernelGGL((fsa_fallback_kernel<F, D, CAUSAL>), dim3(n_groups < 8192 ? n_groups : 8192),
-                     dim3(64), 0, stream, a);
+  hipLaunchKernelGGL((fsa_fwd_kernel<F, D, CAUSAL, false>), grid, dim3(256), 0, stream, a);
+  // the fallback pass: ~4 us when the first pass left no row beyond EXT
+  hipLaunchKernelGGL((fsa_fwd_kernel<F, D, CAUSAL, true>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -69,7 +69,7 @@ struct AttnArgs {
   const uint8_t* kc; const uint8_t* ks;
   const uint8_t* vc; const uint8_t* vs;
   uint16_t* out;                 // bf16 [B][H][S][D]
-  int32_t* row_kappa;            // [B][H][S], written by the main kernel, read by the fallback
+  int32_t* row_kappa;            // [B][H][S], written by the first pass, read by the fallback pass
   float* row_mguess;             // [B][H][S], likewise (frozen max, binades)
   int B, H, S;
   int h0, hrun;                  // heads [h0, h0+hrun) of each batch entry

@@ -212,7 +212,7 @@ def test_causal_many_tiles_sampled(fmt):
 
 @pytest.mark.parametrize("fmt", FMTS)
 def test_rows_far_above_the_guess_causal(fmt):
-    """The fallback kernel with causal masking (planted rows past the window)."""
+    """The fallback pass with causal masking (planted rows past the window)."""
     announce("fsa far fallback causal", fmt)
     S, D = 400, 128
     q, k, v = (W.bf16_bits_to_f64(W.random_bf16((1, 1, S, D), seed, 1.0)) for seed in (31, 32, 33))
