@@ -672,6 +672,11 @@ fsa_fwd_kernel(AttnArgs a) {
     if (t + 1 < n_tiles) step(t + 1, I1{}, T1{}, F0{});
   }
 
+  // The full-tile sweep issues two tiles past the last one; their loads
+  // return zeros at once, but none may still be writing this workgroup's
+  // LDS when the workgroup ends and the LDS passes to the next one.
+  wait_dma();
+
   // row offset in binades (the oracle's kappa); rows beyond EXT come out
   // wrong here and are recomputed by the REBASE pass
   int kap = kmax - (127 + REF);
@@ -707,8 +712,10 @@ fsa_fwd_kernel(AttnArgs a) {
       }
     if (he == 0) a.row_kappa[row] = kap;
   }
-  // tell the REBASE pass of this call that it has work (one vector store)
-  if (!REBASE && __builtin_amdgcn_ballot_w64(kap > EXT) != 0 && lane == 0) *a.fb_flag = a.call_id;
+  // tell the REBASE pass of this call that it has work (one vector store);
+  // rows past S (a ragged last query tile) never ask for it
+  if (!REBASE && __builtin_amdgcn_ballot_w64(qe < S && kap > EXT) != 0 && lane == 0)
+    *a.fb_flag = a.call_id;
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
