@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests are skipped, not failed, when no GPU is visible; the marker
-    # still lets "-m gpu" select exactly them on a GPU machine.
+    # still lets "-m gpu" select exactly them on a machine with a GPU.
     try:
         import torch
         has_gpu = torch.cuda.is_available()

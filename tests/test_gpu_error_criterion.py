@@ -7,7 +7,7 @@ quantisation floor).
 Evaluated per workload over sampled query rows of 14 heads (6 for the hybrid
 schedule), pooled over those rows: relL2 = ||a - b|| / ||b|| over all sampled
 elements.  Per-head ratios are printed; with a few dozen rows per head they
-scatter around 1 (0.44-1.56 measured), so the bar is the pooled one.
+scatter about 1 (0.44-1.56 measured), so the bar is the pooled one.
 """
 
 import numpy as np
