@@ -5,11 +5,14 @@ arithmetic unless a step says otherwise:
 
 * ``exact_attention`` -- softmax(q k^T / sqrt(D)) v on the unquantised bf16
   inputs: the ground truth the error criterion is measured against.
-* ``plain_mx_attention`` -- the "exp-then-quantize" path: MX operands, exact
-  max and exact exp, then the probabilities MX-quantised before the PV
-  product.  Its error is the floor set by quantising the GEMM operands
-  (Fused-Softmax for efficient quantized attention, summary; EFQ-Softmax:
-  Exp-Free Quantization for Softmax, abstract).
+* ``plain_mx_attention`` -- the "exp-then-quantize" path on the very same MX
+  operands as the fused path (the pre-scaled q' of step 1, k, v): exact row
+  max, exact exponential, then the probabilities MX-quantised along the keys
+  before the PV product.  Its error is the floor set by quantising the GEMM
+  operands (Fused-Softmax for efficient quantized attention, summary;
+  EFQ-Softmax: Exp-Free Quantization for Softmax, abstract), so that the
+  fused/plain comparison isolates the approximated exponential and the
+  frozen max.
 * ``fused_attention`` -- Fused-Softmax attention as specified below.
 
 Fused-Softmax, as the pages outline it and as read here
@@ -37,44 +40,46 @@ no formulas, so each step below is a reading:
    no rule; the mean + z*std term is the expected Gaussian extreme over n_i
    keys plus one standard deviation of margin, so that a well-behaved row
    rarely exceeds it.  ``bias`` (binades) is a test hook, 0 in normal use.
-4. Exponential folded into the score product.  The float32 number whose bit
-   pattern is the integer 2**23 * (127 + x) has the value
-   2**floor(x) * (1 + frac(x)), i.e. 2**x linearly interpolated between
-   integer exponents (the bit-pattern exponential).  The score product itself
-   produces that integer: with 2**23 folded into q's power-of-two block scale
-   and the accumulator started at fp32(2**23 * (127 + R - kappa_i - m~_i)),
-       y_ij = fp32(2**23 * s_ij + fp32(2**23 * (127 + R - kappa_i) - 2**23 * m~_i)),
-   one rounding at the product's output (R = 62, below).  Truncation to an
-   unsigned integer (0 below zero) gives the bits of
-   p_ij = 2**(t_ij + R - kappa_i), t_ij = s_ij - m~_i, with 16 or more
-   fraction bits of t.  R only places the value inside fp32's range: scores
-   from 188 binades below the reference to 66 above give normal numbers.
+4. The fast exponential is the bit-pattern one (``mitchell_exp2``): read as
+   a float, the integer 2**23 * (127 + x) is 2**floor(x) * (1 + frac(x)),
+   i.e. 2**x linearly interpolated between integer exponents.  Because x is
+   linear in the score, the max subtraction and the scaling that produce it
+   fold into the score product (its accumulator start and Q's block scale);
+   that placement is the kernel's business, and here t_ij = s_ij - m~_i is
+   taken exactly.
 5. MX quantisation of P.  Per block b of 32 keys of a row (keys
-   [32b, 32b+32), visible keys only), with y0 the kappa = 0 values of step 4,
-   c_b = round_half_even(2**M * (max_j y0_ij / 2**23 - 127 - R)) and
-   e_b = floor(c_b / 2**M): the binade of the block's largest value relative
-   to the guess, counted in element codes.  The block is shifted up by
-   Delta_b = min(kappa_i - e_b, 127 - pl) whole binades so that its largest
-   value lands in the placement binade 2**pl: the top binade (pl = emax) for
-   E2M3 and E2M1; for E4M3 the binade below it (pl = emax - 1), which keeps
-   rounding away from E4M3's NaN pattern at no cost in precision (every
-   normal E4M3 binade has the same 3 mantissa bits).  Each element is
-   p_ij * 2**(pl + Delta_b - R) (an exact power-of-two rescale) rounded to
-   the nearest element (ties to even, saturating at the largest finite one),
-   which puts values below the normal range on the subnormal grid by value.
-   The block's E8M0 scale is 2**-(pl + Delta_b) and
+   [32b, 32b+32), visible keys only), the block's binade relative to the
+   guess, counted in element codes, is
+   e_b = floor(round_half_even(2**M * max_j t_ij) / 2**M): the binade its
+   largest value lands in once rounded to M mantissa bits.  The row's
+   offset is kappa_i = max(0, max_b e_b) (step 6) and the block is shifted
+   up by Delta_b = min(kappa_i - e_b, 127 - pl) whole binades (a fully
+   masked block takes the largest shift), so that its largest value lands
+   in the placement binade 2**pl: the top binade (pl = emax) for E2M3 and
+   E2M1; for E4M3 the binade below it (pl = emax - 1), which keeps rounding
+   away from E4M3's NaN pattern at no cost in precision (every normal E4M3
+   binade has the same 3 mantissa bits).  Each element is
+   mitchell_exp2(t_ij - kappa_i + pl + Delta_b) rounded to the nearest
+   element (ties to even, saturating at the largest finite one), which puts
+   values below the normal range on the subnormal grid by value.  The
+   block's E8M0 scale is 2**-(pl + Delta_b) and
    P~_ij = decode(code_ij) * 2**-(pl + Delta_b), about 2**(t_ij - kappa_i).
 6. Fallback: a row whose guess was too low has some block with e_b > 0
    (its scores exceed m~ by a whole binade in the code domain).  The row is
    recomputed with its reference raised by the whole number of binades
    kappa_i = max(0, max_b e_b).  Raising the reference by whole binades
-   leaves every code of the row unchanged (up to the fp32 rounding of y) and
-   lowers every block scale by 2**kappa_i (except where a block shift
-   reaches the E8M0 floor), so the kernel can realise the recomputation as
-   an exact power-of-two rescale of its running sums.
+   leaves every code of the row unchanged and lowers every block scale by
+   2**kappa_i (except where a block shift reaches the E8M0 floor), so the
+   recomputation is an exact power-of-two rescale of the row's sums.
 7. O_i = sum_j P~_ij v^_j, l_i = sum_j P~_ij (the same quantised P~ in both,
    as EFQ-Softmax does for its numerator and denominator), and
    out_i = bf16(O_i / l_i).
+
+Kernel tolerance.  A kernel that places x in fp32 (for instance as the
+exponent-field value 2**23 * (127 + R + t) of a score product) carries t to
+a fixed number of fraction bits; its codes and block binades then differ
+from these exact ones only where the exact value lies within that rounding
+of a rounding tie.  Parity tests absorb this in their tolerance.
 """
 
 from __future__ import annotations
@@ -89,7 +94,6 @@ from .mx import (FORMATS, BLOCK, Format, decode, encode_values, round_to_format,
 
 WINDOW = 128          # keys that feed the frozen-max guess
 Z_MARGIN = 1.0        # standard deviations above the expected Gaussian extreme
-REF_BINADE = 62       # R of step 4: where a score equal to the reference lands
 LOG2E = 1.0 / math.log(2.0)
 
 
@@ -126,14 +130,13 @@ def prescale_q(q: np.ndarray) -> np.ndarray:
     return (np.asarray(q, np.float64).astype(np.float32) * c).astype(np.float64)
 
 
-def quantized_operands(q, k, v, fmt, prescale: bool = False):
-    """Dequantised q^ (of q' when ``prescale``), k^ (blocks along D) and
-    v^ (blocks along keys)."""
+def quantized_operands(q, k, v, fmt):
+    """Dequantised q'^ (the pre-scaled q' of step 1), k^ (blocks along D) and
+    v^ (blocks along keys): the operands both MX paths multiply."""
     f = _fmt(fmt)
     S = k.shape[0]
-    if prescale:
-        q = prescale_q(q)
-    qh = mx_dequantize(*mx_quantize(q, f), f)[:, : q.shape[1]]
+    qp = prescale_q(q)
+    qh = mx_dequantize(*mx_quantize(qp, f), f)[:, : q.shape[1]]
     kh = mx_dequantize(*mx_quantize(k, f), f)[:, : k.shape[1]]
     vt = mx_dequantize(*mx_quantize(np.ascontiguousarray(v.T), f), f)[:, :S]
     return qh, kh, np.ascontiguousarray(vt.T)
@@ -177,41 +180,19 @@ def frozen_max(s: np.ndarray, vis: np.ndarray, bias: float = 0.0) -> np.ndarray:
     return guess.astype(np.float32).astype(np.float64)
 
 
-def fma_f32(a: np.ndarray, b: np.ndarray, c: np.ndarray) -> np.ndarray:
-    """fp32 fused multiply-add of fp32 operands, rounded once (nearest, ties even).
+def mitchell_exp2(x: np.ndarray) -> np.ndarray:
+    """2**floor(x) * (1 + frac(x)): the bit-pattern exponential (step 4).
 
-    a*b is exact in float64; a + c is resolved with an error-free two-sum so
-    that the single rounding to fp32 is exact even on float64 ties.
+    Exact at integer x, at most about 6.1 % above 2**x in between.
+    ``-inf`` gives 0.
     """
-    a = np.asarray(a, np.float64)
-    b = np.asarray(b, np.float64)
-    c = np.asarray(c, np.float64)
-    p = a * b
-    s = p + c
-    bb = s - p
-    err = (p - (s - bb)) + (c - bb)
-    with np.errstate(invalid="ignore", over="ignore"):
-        r = s.astype(np.float32).astype(np.float64)
-        up = r > s
-        other = np.where(up, np.nextafter(r.astype(np.float32), np.float32(-np.inf)),
-                         np.nextafter(r.astype(np.float32), np.float32(np.inf))).astype(np.float64)
-        lo = np.where(up, other, r)
-        hi = np.where(up, r, other)
-        tie = np.isfinite(s) & ((s - lo) == (hi - s))
-    r = np.where(tie & (err > 0), hi, np.where(tie & (err < 0), lo, r))
-    return r
-
-
-def bits_to_f32(u: np.ndarray) -> np.ndarray:
-    """float32 value (as float64) of unsigned 32-bit patterns."""
-    return np.asarray(u, np.uint64).astype(np.uint32).view(np.float32).astype(np.float64)
-
-
-def trunc_u32(y: np.ndarray) -> np.ndarray:
-    """Truncate toward zero to an unsigned 32-bit integer; below zero or NaN give 0."""
-    y = np.asarray(y, np.float64)
-    y = np.where(np.isnan(y), 0.0, y)
-    return np.clip(np.trunc(y), 0, 2.0 ** 32 - 1).astype(np.uint64)
+    x = np.asarray(x, np.float64)
+    fin = np.isfinite(x)
+    xs = np.where(fin, x, 0.0)
+    fl = np.floor(xs)
+    # floor(x) below the float64 exponent range underflows to 0, as it should
+    val = np.ldexp(1.0 + (xs - fl), np.clip(fl, -1100, 1100).astype(np.int64))
+    return np.where(fin, val, 0.0)
 
 
 def placement_exponent(fmt) -> int:
@@ -221,16 +202,19 @@ def placement_exponent(fmt) -> int:
     return f.emax - 1 if f.name == "e4m3" else f.emax
 
 
-def reference_addend(m_tilde: np.ndarray, kappa: np.ndarray) -> np.ndarray:
-    """fp32(2**23 * (127 + R - kappa) - 2**23 * m~): the accumulator start of
-    the score product (step 4), one rounding."""
-    a = (2.0 ** 23) * (127 + REF_BINADE - np.asarray(kappa, np.float64)) - (2.0 ** 23) * m_tilde
-    return a.astype(np.float32).astype(np.float64)
-
-
-def exponent_field_values(s: np.ndarray, addend: np.ndarray) -> np.ndarray:
-    """y = fp32(2**23 * s + addend) for rows of log2-domain scores (step 4)."""
-    return fma_f32(np.float64(2.0 ** 23), s, addend[:, None])
+def block_binades(t: np.ndarray, vis: np.ndarray, fmt) -> np.ndarray:
+    """e_b of step 5 for rows of guess-relative scores t [R, S]: the binade of
+    each 32-key block's largest visible value after rounding to M mantissa
+    bits (half to even).  Blocks with no visible key give -inf."""
+    f = _fmt(fmt)
+    R, S = t.shape
+    nb = (S + BLOCK - 1) // BLOCK
+    tp = np.full((R, nb * BLOCK), -np.inf)
+    tp[:, :S] = np.where(vis, t, -np.inf)
+    g = tp.reshape(R, nb, BLOCK).max(axis=2)
+    with np.errstate(invalid="ignore"):
+        c = np.rint((2 ** f.mbits) * g)            # np.rint: half to even
+    return np.floor(c / (2 ** f.mbits))
 
 
 def fused_probabilities(s: np.ndarray, m_tilde: np.ndarray, vis: np.ndarray,
@@ -238,31 +222,20 @@ def fused_probabilities(s: np.ndarray, m_tilde: np.ndarray, vis: np.ndarray,
     """Steps 4-6 of the module doc for rows of log2-domain scores ``s`` [R, S].
 
     Returns the P~ values (float64), the element codes, the per-block shifts
-    Delta, the E8M0 scale bytes of P~ and the per-row binade offset kappa
-    (> 0 for rows that fell back).
+    Delta, the E8M0 scale bytes of P~, the per-row binade offset kappa
+    (> 0 for rows that fell back) and the guess-relative block binades e_b.
     """
     f = _fmt(fmt)
-    M = f.mbits
     pl = placement_exponent(f)
     cap = 127 - pl
     R, S = s.shape
-    nb = (S + BLOCK - 1) // BLOCK
-    s0 = np.where(vis, s, 0.0)
-    # guess-relative block binades from the kappa = 0 values
-    y0 = exponent_field_values(s0, reference_addend(m_tilde, np.zeros(R)))
-    yp = np.full((R, nb * BLOCK), -np.inf)
-    yp[:, :S] = np.where(vis, y0, -np.inf)
-    g = yp.reshape(R, nb, BLOCK).max(axis=2)          # -inf for blocks with no visible key
-    c = np.rint((2 ** M) * (g / 2.0 ** 23 - 127 - REF_BINADE))   # exact in float64
-    e = np.floor(c / (2 ** M))
-    kappa = np.maximum(0.0, np.max(e, axis=1))
+    t = np.asarray(s, np.float64) - np.asarray(m_tilde, np.float64)[:, None]
+    e = block_binades(t, vis, f)
+    kappa = np.maximum(0.0, np.max(e, axis=1)) if e.size else np.zeros(R)
     delta = np.where(np.isfinite(e), np.minimum(kappa[:, None] - e, cap), cap)
     delta_full = np.repeat(delta, BLOCK, axis=1)[:, :S]
-    y = exponent_field_values(s0, reference_addend(m_tilde, kappa))
-    y = np.where(vis, y, -np.inf)
-    p = bits_to_f32(trunc_u32(y))
-    p = p * np.ldexp(1.0, (pl + delta_full - REF_BINADE).astype(np.int32))
-    vals = round_to_format(p, f)
+    x = np.where(vis, t - kappa[:, None] + pl + delta_full, -np.inf)
+    vals = round_to_format(mitchell_exp2(x), f)
     code = encode_values(vals, f).astype(np.int64)
     P = vals * np.ldexp(1.0, (-pl - delta_full).astype(np.int32))
     return {
@@ -271,6 +244,7 @@ def fused_probabilities(s: np.ndarray, m_tilde: np.ndarray, vis: np.ndarray,
         "delta": delta.astype(np.int64),
         "scale_bytes": (127 - pl - delta).astype(np.int64),
         "kappa": kappa.astype(np.int64),
+        "binades": e,
     }
 
 
@@ -289,7 +263,7 @@ def fused_attention(q, k, v, fmt, causal: bool = False, rows=None, bias: float =
     v = np.asarray(v, np.float64)
     S, D = k.shape
     rows = _rows(rows, S)
-    qh, kh, vh = quantized_operands(q[rows] if rows.size else q[:0], k, v, f, prescale=True)
+    qh, kh, vh = quantized_operands(q[rows] if rows.size else q[:0], k, v, f)
     s = qh @ kh.T
     vis = _visible(rows, S, causal)
     m_tilde = frozen_max(s, vis, bias)
@@ -305,12 +279,29 @@ def fused_attention(q, k, v, fmt, causal: bool = False, rows=None, bias: float =
     return out, info
 
 
-def plain_mx_attention(q, k, v, fmt, causal: bool = False, rows=None) -> np.ndarray:
+def plain_probabilities(s: np.ndarray, vis: np.ndarray, fmt) -> np.ndarray:
+    """Exp-then-quantize probabilities for rows of log2-domain scores [R, S]:
+    P = 2**(s - max_j s) with the exact row max, then MX-quantised along the
+    keys (blocks of 32 aligned at key 0, the OCP rule of ``mx_quantize``) in
+    the operand format.  Masked keys are 0.  Returns the dequantised values."""
+    f = _fmt(fmt)
+    S = s.shape[1]
+    sm = np.where(vis, s, -np.inf)
+    m = sm.max(axis=1, keepdims=True)
+    P = np.where(vis, np.exp2(sm - m), 0.0)
+    return mx_dequantize(*mx_quantize(P, f), f)[:, :S]
+
+
+def plain_mx_attention(q, k, v, fmt, causal: bool = False, rows=None,
+                       return_info: bool = False):
     """Exp-then-quantize attention (bf16 values as float64) for one head.
 
-    The same MX operands as ``fused_attention``; exact row max and exact exp
-    in float64; P MX-quantised along the keys (blocks of 32 aligned at key 0,
-    the same blocks as the fused path); out = bf16(sum P^ v^ / sum P^).
+    The same MX operands as ``fused_attention`` (q'^ of step 1, k^, v^), so
+    the same log2-domain scores s; exact row max and exact exponential in
+    float64, P = 2**(s - max s) = exp((q'.k - max) ...) in the softmax scale;
+    P MX-quantised along the keys (``plain_probabilities``);
+    out = bf16(sum P^ v^ / sum P^).  With ``return_info`` also returns the
+    dequantised P^ and the scores.
     """
     f = _fmt(fmt)
     q = np.asarray(q, np.float64)
@@ -321,10 +312,10 @@ def plain_mx_attention(q, k, v, fmt, causal: bool = False, rows=None) -> np.ndar
     qh, kh, vh = quantized_operands(q[rows], k, v, f)
     s = qh @ kh.T
     vis = _visible(rows, S, causal)
-    s = np.where(vis, s, -np.inf)
-    m = s.max(axis=1, keepdims=True)
-    P = np.where(vis, np.exp((s - m) / math.sqrt(D)), 0.0)
-    Pq = mx_dequantize(*mx_quantize(P, f), f)[:, :S]
+    Pq = plain_probabilities(s, vis, f)
     O = Pq @ vh
     l = Pq.sum(axis=1)
-    return bf16_round(O / l[:, None])
+    out = bf16_round(O / l[:, None])
+    if not return_info:
+        return out
+    return out, {"P": Pq, "scores": s}

@@ -2,56 +2,93 @@
 attention, the fused-softmax output's error stays within 1.1x that of plain
 exp-then-quantize MX attention on the same operands (Fused-Softmax for
 efficient quantized attention, summary: the added error stays below the
-quantisation floor).
+quantisation floor).  Both MX paths multiply the same pre-scaled q'^, k^ and
+v^, so the comparison isolates the approximated exponential and the frozen
+max.
 
-Evaluated per workload over sampled query rows of 14 heads (6 for the hybrid
-schedule), pooled over those rows: relL2 = ||a - b|| / ||b|| over all sampled
-elements.  Per-head ratios are printed; with a few dozen rows per head they
-scatter about 1 (0.44-1.56 measured), so the bar is the pooled one.
+Every head of every workload is evaluated on its own sample of query rows
+(relL2 = ||a - b|| / ||b|| over the sample); the GPU output comes from one
+call over the whole tensor.  Asserted:
+
+* per workload, the ratio pooled over all heads' rows is at most 1.1;
+* per head, the ratio is at most 1.1 unless its sampling spread explains the
+  excess: the per-row errors are heavy-tailed (a few rows whose weight sits
+  on a handful of keys dominate a few hundred rows), so the head must not be
+  above 1.1 by more than three bootstrap standard deviations over its rows.
+
+Every per-head ratio and its spread is printed.
 """
+
+import concurrent.futures
+import os
 
 import numpy as np
 import pytest
 
 import workloads as W
 import oracle as O
-from gpu_helpers import announce, to_dev, from_dev_bf16, rel_l2
+from gpu_helpers import announce, to_dev, from_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
-CASES = [("video_dit_e4m3", tuple(range(0, 40, 3)), 24),
-         ("video_dit_e2m3", tuple(range(0, 40, 3)), 24),
-         ("video_dit_e2m1", tuple(range(0, 40, 3)), 24),
-         ("outliers_e2m1", (0, 13, 27), 16),
-         ("hybrid_long", (0, 10, 19, 20, 30, 39), 8)]
+CASES = [("video_dit_e4m3", 512), ("video_dit_e2m3", 512), ("video_dit_e2m1", 512),
+         ("outliers_e2m1", 384), ("hybrid_long", 256)]
+BAR = 1.1
 
 
-@pytest.mark.parametrize("name,heads,n_rows", CASES, ids=[c[0] for c in CASES])
-def test_fused_error_within_1p1_of_plain_mx(name, heads, n_rows):
+def _threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except Exception:
+        n = os.cpu_count() or 4
+    return max(1, min(16, n))
+
+
+def _head_errors(w, h, rows, g_rows):
+    """Per-row squared errors of the GPU output and of the plain MX path
+    against exact attention for one head (oracle on the host)."""
+    qh, kh, vh = (W.bf16_bits_to_f64(x) for x in W.generate_head(w, 0, h))
+    ex = O.exact_attention(qh, kh, vh, w.causal, rows=rows)
+    pl = O.plain_mx_attention(qh, kh, vh, w.head_fmts[h], w.causal, rows=rows)
+    ef = np.sum((g_rows - ex) ** 2, axis=1)
+    ep = np.sum((pl - ex) ** 2, axis=1)
+    return ef, ep
+
+
+@pytest.mark.parametrize("name,n_rows", CASES, ids=[c[0] for c in CASES])
+def test_fused_error_within_1p1_of_plain_mx_per_head(name, n_rows):
     import torch
     import softmax_mx_quantize_amd as fsa
     w = W.WORKLOADS[name]
-    announce("error criterion", name)
+    announce("error criterion", name, "rows per head", n_rows)
     q, k, v = W.generate(w)
     hf = list(w.head_fmts)
     kw = {} if len(set(hf)) == 1 else {"head_fmt": hf}
     out = fsa.attention_fwd(to_dev(q), to_dev(k), to_dev(v), hf[0], w.causal, **kw)
     torch.cuda.synchronize()
     g = from_dev_bf16(out)
-    rng = np.random.default_rng(99)
-    rows = np.sort(rng.choice(w.S, size=n_rows, replace=False))
-    G, E, P = [], [], []
-    for h in heads:
-        qh, kh, vh = (W.bf16_bits_to_f64(x[0, h]) for x in (q, k, v))
-        ex = O.exact_attention(qh, kh, vh, w.causal, rows=rows)
-        pl = O.plain_mx_attention(qh, kh, vh, hf[h], w.causal, rows=rows)
-        gh = g[0, h, rows]
-        print("%s head %d (%s): fused %.3e, plain %.3e, ratio %.3f"
-              % (name, h, hf[h], rel_l2(gh, ex), rel_l2(pl, ex), rel_l2(gh, ex) / rel_l2(pl, ex)))
-        G.append(gh)
-        E.append(ex)
-        P.append(pl)
-    G, E, P = np.stack(G), np.stack(E), np.stack(P)
-    ratio = rel_l2(G, E) / rel_l2(P, E)
-    print("%s pooled ratio %.3f" % (name, ratio))
-    assert ratio <= 1.1, ratio
+    del out, q, k, v
+    samples = {h: np.sort(np.random.default_rng([77, h]).choice(w.S, n_rows, replace=False))
+               for h in range(w.H)}
+    with concurrent.futures.ThreadPoolExecutor(_threads()) as ex:
+        futs = {h: ex.submit(_head_errors, w, h, samples[h], g[0, h, samples[h]]) for h in range(w.H)}
+        res = {h: f.result() for h, f in futs.items()}
+    rng = np.random.default_rng(5)
+    worst, EF, EP = [], 0.0, 0.0
+    for h in range(w.H):
+        ef, ep = res[h]
+        EF += ef.sum()
+        EP += ep.sum()
+        ratio = float(np.sqrt(ef.sum() / ep.sum()))
+        idx = rng.integers(0, ef.size, size=(400, ef.size))
+        boot = np.sqrt(ef[idx].sum(axis=1) / ep[idx].sum(axis=1))
+        sd = float(boot.std())
+        print("%s head %2d (%s): ratio %.3f  bootstrap sd %.3f" % (name, h, hf[h], ratio, sd))
+        if ratio > BAR:
+            worst.append((h, ratio, sd))
+    pooled = float(np.sqrt(EF / EP))
+    print("%s pooled ratio %.3f over %d heads x %d rows; heads above %.1f: %s"
+          % (name, pooled, w.H, n_rows, BAR, worst))
+    assert pooled <= BAR, pooled
+    for h, ratio, sd in worst:
+        assert ratio <= BAR + 3.0 * sd, (h, ratio, sd)

@@ -19,8 +19,8 @@ import workloads as W
 import oracle as O
 from oracle import FORMATS, decode, mx_quantize, mx_dequantize, bf16_round, rel_l2
 from oracle.attention import (frozen_max, fused_probabilities, score_scale, prescale_q,
-                              reference_addend, quantized_operands, _visible, WINDOW,
-                              REF_BINADE)
+                              quantized_operands, _visible, WINDOW, mitchell_exp2,
+                              placement_exponent)
 
 FMTS = ["e4m3", "e2m3", "e2m1"]
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -116,25 +116,18 @@ def test_probability_map_against_independent_route(fmt):
     pl = f.emax - 1 if fmt == "e4m3" else f.emax
     M = f.mbits
     for i in range(R):
-        t = s[i] - m[i]                                 # exact
+        t = s[i] - m[i]
         # block binade from the largest score, in element codes (half to even)
-        x = (2 ** M) * t.max()
-        code = round(x)
+        x = (2 ** M) * max(t)
+        code = round(x)                                 # Python rounds half to even
         e = math.floor(code / 2 ** M)
         delta = min(-e, 127 - pl)
         assert fp["kappa"][i] == 0
-        near_tie = abs(x - math.floor(x) - 0.5) < 1e-4
-        if not near_tie:
-            assert fp["delta"][i, 0] == delta
-        delta = int(fp["delta"][i, 0])
+        assert fp["delta"][i, 0] == delta
         for j in range(32):
             p = _mitchell_value(pl + delta + t[j])
             want = _nearest(table, min(p, f.max_value * 2)) * 2.0 ** (-pl - delta)
-            got = fp["P"][i, j]
-            # y keeps >= 16 fraction bits of t; allow the rare element whose
-            # value sits within that rounding of a rounding tie
-            if got != want:
-                assert abs(p / 2 ** math.floor(math.log2(p)) * 2 ** M % 1 - 0.5) < 1e-3
+            assert fp["P"][i, j] == want, (i, j)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -220,8 +213,8 @@ def test_error_criterion_on_tiny_workload():
     assert e_f <= 1.1 * e_p
 
 
-def test_score_scale_prescale_and_addend():
-    """The fp32 constants of steps 1 and 4 against independent evaluations."""
+def test_score_scale_and_prescale():
+    """The fp32 constants of step 1 against independent evaluations."""
     from fractions import Fraction
     for D in (64, 128):
         c = score_scale(D)
@@ -232,12 +225,85 @@ def test_score_scale_prescale_and_addend():
         for a, b in zip(q.ravel()[:64], qp.ravel()[:64]):
             # one fp32 rounding of the exact product
             assert b == float(np.float32(Fraction(a) * Fraction(c)))
-    m = np.array([0.0, 3.25, -7.5, 1e-3, 41.0], np.float32).astype(np.float64)
-    for kap in (0, 1, 70):
-        got = reference_addend(m, np.full(m.shape, kap))
-        for gi, mi in zip(got, m):
-            exact = Fraction(2 ** 23) * (127 + REF_BINADE - kap) - Fraction(2 ** 23) * Fraction(mi)
-            assert gi == float(np.float32(float(exact)))
-    # a score equal to the reference gives the bit pattern of 2**REF_BINADE
-    y = O.attention.exponent_field_values(np.array([[3.25]]), reference_addend(np.array([3.25]), np.zeros(1)))
-    assert O.attention.bits_to_f32(O.attention.trunc_u32(y))[0, 0] == 2.0 ** REF_BINADE
+
+
+def test_mitchell_exp2_closed_forms():
+    """2**floor(x) * (1 + frac x): exact at integers, the chord of 2**x in between."""
+    xs = np.array([0.0, 1.0, -3.0, 0.5, -0.25, 2.75, -7.125, -np.inf])
+    want = [1.0, 2.0, 0.125, 1.5, 0.875, 7.0, 2.0 ** -8 * 1.875, 0.0]
+    assert np.array_equal(mitchell_exp2(xs), np.array(want))
+    x = np.random.default_rng(3).uniform(-30, 30, 10000)
+    r = mitchell_exp2(x) / np.exp2(x)
+    assert np.all(r >= 1.0 - 1e-15) and np.all(r <= 1.0615)
+
+
+def _loop_plain_rows(s, vis, fmt):
+    """Exp-then-quantize probabilities by explicit loops: exact exponential of
+    each score against its row's visible maximum, then each block of 32
+    consecutive keys of a row MX-quantised on its own (OCP floor scale,
+    brute-force nearest value, ties to the even code)."""
+    f = FORMATS[fmt]
+    mags = decode(np.arange(f.max_code + 1), f)
+    R, S = s.shape
+    out = np.zeros((R, S))
+    for i in range(R):
+        m = max(s[i, j] for j in range(S) if vis[i, j])
+        p = [math.pow(2.0, s[i, j] - m) if vis[i, j] else 0.0 for j in range(S)]
+        for b0 in range(0, S, 32):
+            blk = p[b0:b0 + 32]
+            amax = max(blk)
+            if amax == 0.0:
+                continue
+            X = math.frexp(amax)[1] - 1 - f.emax
+            for jj, val in enumerate(blk):
+                y = val / 2.0 ** X
+                d = np.abs(mags - min(y, f.max_value))
+                cand = np.flatnonzero(d == d.min())
+                c = cand[0] if cand.size == 1 else [c for c in cand if c % 2 == 0][0]
+                out[i, b0 + jj] = mags[c] * 2.0 ** X
+    return out
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_plain_probabilities_match_loops(fmt, causal):
+    """The exp-then-quantize floor: P^ blocked along the keys of each row, in the
+    operand format, from 2**(s - row max); and its output O / l."""
+    S, D = 75, 64                       # a ragged third key block
+    q, k, v = _head(S, D, 600, scale=1.4)
+    rows = np.array([0, 1, 2, 17, 40, 74])
+    out, info = O.plain_mx_attention(q, k, v, fmt, causal, rows=rows, return_info=True)
+    vis = _visible(rows, S, causal)
+    want = _loop_plain_rows(info["scores"], vis, fmt)
+    assert np.array_equal(info["P"], want)
+    # the scores are those of the fused path (the same pre-scaled q'^)
+    _, finfo = O.fused_attention(q, k, v, fmt, causal, rows=rows, return_info=True)
+    assert np.array_equal(info["scores"], finfo["scores"])
+    _, _, vh = quantized_operands(q, k, v, fmt)
+    for r in range(rows.size):
+        num = [math.fsum(want[r, j] * vh[j, d] for j in range(S)) for d in range(D)]
+        den = math.fsum(want[r])
+        ref = bf16_round(np.array(num) / den)
+        # one bf16 rounding apart at most (summation order)
+        assert np.all(np.abs(out[r] - ref) <= np.abs(ref) * 2.0 ** -7 + 1e-30)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_whole_binade_guess_shift_is_exact(fmt):
+    """Lowering the guess by K whole binades (the fallback's re-basing) raises
+    kappa by exactly K and leaves every code and every P~ unchanged."""
+    f = FORMATS[fmt]
+    rng = np.random.default_rng(21)
+    R, S = 8, 96
+    s = rng.normal(0.0, 1.5, (R, S))
+    # guesses a hair above each row max: top block in binade 0, kappa = 0
+    m = s.max(axis=1) + 2.0 ** -(f.mbits + 3)
+    vis = np.ones((R, S), bool)
+    base = fused_probabilities(s, m, vis, f)
+    assert np.all(base["kappa"] == 0)
+    for K in (1, 3, 17, 60):
+        sh = fused_probabilities(s, m - K, vis, f)
+        assert np.all(sh["kappa"] == K)
+        assert np.array_equal(sh["codes"], base["codes"])
+        assert np.array_equal(sh["P"], base["P"])
+        assert np.array_equal(sh["delta"], base["delta"])
