@@ -151,6 +151,41 @@ int fsa_attention_fwd_ex(const void* q, const void* k, const void* v, void* out,
                          int B, int H, int S, int D, int fmt, int causal,
                          const fsa_options* opt, void* stream);
 
+/*
+ * fsa_debug_operands -- the MX operands exactly as fsa_attention_fwd's
+ * kernels consume them (a debug view for bit-exact checks of the operand
+ * quantisation; MX operands: Fused-Softmax for efficient quantized attention,
+ * summary; block rule as for fsa_quantize_mx).
+ *
+ * q, k, v : device, bf16 [B][H][S][D], 16-byte aligned; D 64 or 128; every
+ *     head takes element format fmt.  Let bits = 8, 6, 4 and
+ *     Sk = S rounded up to 128.  Each output pair may be NULL to skip it;
+ *     outputs are device memory owned by the caller, code buffers 16-byte
+ *     aligned.
+ * q_codes  [B][H][S][D*bits/8], q_scales [B][H][S][D/32]: Q times
+ *     fp32(log2(e)/sqrt(D)) MX-quantised along D by the attention kernel's
+ *     own prologue code, in the packing of fsa_quantize_mx.  Each scale byte
+ *     is the block's E8M0 byte raised by 23 (the kernel puts 2^23 on Q's
+ *     scale), at most 254; 255 marks a NaN/Inf block.
+ * k_codes  [B][H][Sk][D*bits/8]: K quantised along D (padding rows 0);
+ * k_scales [B][H][Sk/128][128*D/32]: per 128-key tile, the key-tile order
+ *     of the score product (byte of key row r, D block b at
+ *     (32 (b%2) + rho) * D/16 + u * D/32 + beta * D/64 + b/2, with r = 64 u
+ *     + kk, rho = 8 j + 4 x + kk%4 and (x, beta) = (kk/16%2, kk/32) for FP8,
+ *     (kk/32, kk/16%2) otherwise, j = kk/4%4); padding rows 0;
+ * v_codes  [B][H][D][Sk*bits/8]: V quantised along the keys, transposed
+ *     (padding keys 0);
+ * v_scales [B][H][Sk/128][4*D]: per 128-key tile, the byte of row d and
+ *     key block kb (0..3) at (32 (kb%2) + d%32) * D/16 + (kb/2) * D/32 + d/32;
+ *     padding blocks 0.
+ * Errors: FSA_ERR_INVALID_ARG (null inputs, an output pair half NULL,
+ * sizes, fmt, alignment), FSA_ERR_UNSUPPORTED (D), FSA_ERR_HIP (launch).
+ * Stream-ordered like the other calls.
+ */
+int fsa_debug_operands(const void* q, const void* k, const void* v, int B, int H, int S, int D,
+                       int fmt, void* q_codes, void* q_scales, void* k_codes, void* k_scales,
+                       void* v_codes, void* v_scales, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* fsa_strerror(int status);
 

@@ -255,7 +255,7 @@ def fused_attention(q, k, v, fmt, causal: bool = False, rows=None, bias: float =
     ``q, k, v`` are [S, D] arrays of bf16 values; ``rows`` selects query rows
     (all by default); ``bias`` is added to the frozen max (binades).  With
     ``return_info`` also returns the frozen max, the fallback offsets, the
-    log2-domain scores and the P~ values.
+    log2-domain scores, the P~ values, the dequantised v^ and the visibility.
     """
     f = _fmt(fmt)
     q = np.asarray(q, np.float64)
@@ -275,7 +275,7 @@ def fused_attention(q, k, v, fmt, causal: bool = False, rows=None, bias: float =
     if not return_info:
         return out
     info = dict(fp)
-    info.update(m_tilde=m_tilde, l=l, scores=s)
+    info.update(m_tilde=m_tilde, l=l, scores=s, v_hat=vh, visible=vis)
     return out, info
 
 

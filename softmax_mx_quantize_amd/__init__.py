@@ -59,13 +59,16 @@ def _load() -> ctypes.CDLL:
     lib.fsa_strerror.restype = ctypes.c_char_p
     lib.fsa_release_workspace.argtypes = []
     lib.fsa_release_workspace.restype = i32
+    lib.fsa_debug_operands.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.fsa_debug_operands.restype = i32
     return lib
 
 
 lib = _load()
 
 EXPORTS = ("fsa_quantize_mx", "fsa_attention_fwd", "fsa_attention_fwd_ex",
-           "fsa_attention_bf16_ref", "fsa_strerror", "fsa_release_workspace")
+           "fsa_attention_bf16_ref", "fsa_strerror", "fsa_release_workspace",
+           "fsa_debug_operands")
 
 
 def strerror(status: int) -> str:
@@ -91,6 +94,18 @@ def _bf16_cuda(*ts) -> None:
     for t in ts:
         if not (t.is_cuda and t.dtype == torch.bfloat16 and t.is_contiguous()):
             raise ValueError("expected contiguous bf16 CUDA tensors")
+
+
+def _out_like(out, q):
+    """A caller's output tensor must match q in shape, dtype, device and
+    layout (the kernels write whole bf16 rows); a new one otherwise."""
+    import torch
+    if out is None:
+        return torch.empty_like(q)
+    _bf16_cuda(out)
+    if out.shape != q.shape or out.device != q.device:
+        raise ValueError("out must be a contiguous bf16 tensor of q's shape on q's device")
+    return out
 
 
 def quantize_mx(x, fmt: Union[str, int], block_along_rows: bool = False):
@@ -123,8 +138,9 @@ def attention_fwd(q, k, v, fmt: Union[str, int] = "e4m3", causal: bool = False, 
     B, H, S, D = q.shape
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must have the same shape")
-    if out is None:
-        out = torch.empty_like(q)
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one device")
+    out = _out_like(out, q)
     opt = Options()
     opt.guess_bias = float(guess_bias)
     kappa = mg = None
@@ -155,10 +171,36 @@ def attention_bf16_ref(q, k, v, causal: bool = False, out=None):
     import torch
     _bf16_cuda(q, k, v)
     B, H, S, D = q.shape
-    if out is None:
-        out = torch.empty_like(q)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one device")
+    out = _out_like(out, q)
     _check(lib.fsa_attention_bf16_ref(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                       B, H, S, D, int(causal), _stream(q)), "fsa_attention_bf16_ref")
+    return out
+
+
+def debug_operands(q, k, v, fmt: Union[str, int] = "e4m3"):
+    """The MX operands as the attention kernels consume them (layouts in
+    ``include/fsa.h``): a dict of uint8 tensors q_codes, q_scales, k_codes,
+    k_scales (key-tile order), v_codes (transposed), v_scales (tile order)."""
+    import torch
+    _bf16_cuda(q, k, v)
+    B, H, S, D = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape")
+    f = _fmt_id(fmt)
+    bits = BITS.get(f, 8)
+    sk = (S + 127) // 128 * 128
+    u8 = lambda *shape: torch.empty(shape, dtype=torch.uint8, device=q.device)
+    out = {"q_codes": u8(B, H, S, D * bits // 8), "q_scales": u8(B, H, S, D // 32),
+           "k_codes": u8(B, H, sk, D * bits // 8), "k_scales": u8(B, H, sk // 128, 128 * D // 32),
+           "v_codes": u8(B, H, D, sk * bits // 8), "v_scales": u8(B, H, sk // 128, 4 * D)}
+    p = {n: t.data_ptr() for n, t in out.items()}
+    _check(lib.fsa_debug_operands(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, S, D, f,
+                                  p["q_codes"], p["q_scales"], p["k_codes"], p["k_scales"],
+                                  p["v_codes"], p["v_scales"], _stream(q)), "fsa_debug_operands")
     return out
 
 

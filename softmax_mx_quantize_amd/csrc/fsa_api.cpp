@@ -290,6 +290,51 @@ int fsa_attention_bf16_ref(const void* q, const void* k, const void* v, void* ou
              : FSA_ERR_HIP;
 }
 
+int fsa_debug_operands(const void* q, const void* k, const void* v, int B, int H, int S, int D,
+                       int fmt, void* q_codes, void* q_scales, void* k_codes, void* k_scales,
+                       void* v_codes, void* v_scales, void* stream_) {
+  if (!q || !k || !v) return FSA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || S <= 0 || D <= 0 || !fmt_ok(fmt)) return FSA_ERR_INVALID_ARG;
+  if ((q_codes == nullptr) != (q_scales == nullptr) || (k_codes == nullptr) != (k_scales == nullptr) ||
+      (v_codes == nullptr) != (v_scales == nullptr))
+    return FSA_ERR_INVALID_ARG;
+  if ((double)B * H * S * D > 1099511627776.0) return FSA_ERR_INVALID_ARG;
+  for (const void* p : {q, k, v})
+    if (reinterpret_cast<uintptr_t>(p) & 15) return FSA_ERR_INVALID_ARG;
+  for (const void* p : {(const void*)q_codes, (const void*)k_codes, (const void*)v_codes})
+    if (reinterpret_cast<uintptr_t>(p) & 15) return FSA_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return FSA_ERR_UNSUPPORTED;
+  if (round_up(S, kKeyTile) * D * 2 >= ((int64_t)1 << 31)) return FSA_ERR_UNSUPPORTED;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const int bits = fmt_bits(fmt);
+  const int64_t nbh = (int64_t)B * H;
+  const int64_t sk = round_up(S, kKeyTile);
+  const int64_t rb = (int64_t)D * bits / 8;
+  if (q_codes) {
+    fsa::QDumpArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.rows = nbh * S;
+    a.qmul = (float)((1.0 / std::log(2.0)) / std::sqrt((double)D));
+    a.codes = static_cast<uint8_t*>(q_codes);
+    a.scales = static_cast<uint8_t*>(q_scales);
+    if (fsa::launch_q_operand_dump(a, kern_fmt(fmt), D, stream) != hipSuccess) return FSA_ERR_HIP;
+  }
+  // the same quantiser calls as the attention path makes into its workspace
+  if (k_codes) {
+    const int st = quantize(static_cast<const uint16_t*>(k), static_cast<uint8_t*>(k_codes),
+                            static_cast<uint8_t*>(k_scales), nbh, S, D, sk, D / 32, rb, D / 32, fmt, 0,
+                            stream, 1.0f, fsa::SCALES_KEY_TILES);
+    if (st != FSA_OK) return st;
+  }
+  if (v_codes) {
+    const int st = quantize(static_cast<const uint16_t*>(v), static_cast<uint8_t*>(v_codes),
+                            static_cast<uint8_t*>(v_scales), nbh, S, D, D, sk / 32, sk * bits / 8, sk / 32,
+                            fmt, 1, stream, 1.0f, fsa::SCALES_DIM_TILES);
+    if (st != FSA_OK) return st;
+  }
+  return FSA_OK;
+}
+
 int fsa_release_workspace(void) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FSA_ERR_HIP;

@@ -100,12 +100,18 @@ __device__ __forceinline__ int block_level(uint32_t m) {
 }
 
 // Truncation toward zero to u32 (v_cvt_u32_f32, which saturates and maps NaN
-// and negatives to 0; the exponential relies on that).  It must stay a
-// compiler-visible conversion: the epilogue feeds it straight from MFMA
-// results, and only instructions the compiler sees get the wait states that
-// reading an MFMA result requires.  Its input must come straight from the
-// product (never a select with constants), so that no out-of-range case can
-// be folded away at compile time; masking happens on the integer result.
+// and negatives to 0; the exponential relies on that).  C++ leaves those
+// cases undefined (LLVM: poison), so what holds is the instruction the
+// backend emits for the plain conversion, and a host test checks that it
+// stays one bare v_cvt_u32_f32.  llvm.fptoui.sat.i32.f32 states the
+// saturation in IR, but this compiler lowers it with two compare/select
+// pairs around the same instruction (four more vector instructions per
+// score element).  It must stay a compiler-visible conversion: the epilogue
+// feeds it straight from MFMA results, and only instructions the compiler
+// sees get the wait states that reading an MFMA result requires.  Its input
+// must come straight from the product (never a select with constants), so
+// that no out-of-range case can be folded away at compile time; masking
+// happens on the integer result.
 __device__ __forceinline__ uint32_t cvt_u32_trunc(float y) {
   return (uint32_t)y;
 }

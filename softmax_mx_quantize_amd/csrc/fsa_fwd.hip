@@ -587,9 +587,9 @@ fsa_fwd_kernel(AttnArgs a) {
   // scheduler interleaves further and lengthens live ranges until registers
   // spill (measured: every D=128 kernel spills, the FP8 one 335 registers),
   // and spill reloads do not mix safely with the LDS DMA in flight, whose
-  // completions the compiler cannot see.  ALWAYS_ISSUE: the loads of tile
-  // t+2 are issued even past the last tile (their stage is never read again;
-  // past the slab the buffer loads return zeros), which keeps the sweep over
+  // completions the compiler cannot see.  ALWAYS_ISSUE: the full-tile sweep
+  // issues the load of step t+2 even past the last tile (it reloads the last
+  // tile into a stage that is never read again), which keeps the sweep over
   // full tiles free of branches.
   auto step = [&](int t, auto st_tag, auto masked_tag, auto always_tag) __attribute__((always_inline)) {
     uint8_t* kb = kstage(st_tag);
@@ -613,8 +613,12 @@ fsa_fwd_kernel(AttnArgs a) {
     wait_dma();
     ring_barrier();
     if (decltype(always_tag)::value || t + 2 < n_tiles) {
-      issue_k(t + 2, kb);
-      issue_v(t + 2, vb);
+      // past the last tile the full-tile sweep reloads the last one (its
+      // stage is never read again): every load stays inside the slab, whose
+      // range check does not cover the tile offset in the scalar operand
+      const int tn = min(t + 2, n_tiles - 1);
+      issue_k(tn, kb);
+      issue_v(tn, vb);
     }
   };
   using F0 = std::false_type;
@@ -672,9 +676,9 @@ fsa_fwd_kernel(AttnArgs a) {
     if (t + 1 < n_tiles) step(t + 1, I1{}, T1{}, F0{});
   }
 
-  // The full-tile sweep issues two tiles past the last one; their loads
-  // return zeros at once, but none may still be writing this workgroup's
-  // LDS when the workgroup ends and the LDS passes to the next one.
+  // The full-tile sweep may have reloaded the last tile past the end; none
+  // of those loads may still be writing this workgroup's LDS when the
+  // workgroup ends and the LDS passes to the next one.
   wait_dma();
 
   // row offset in binades (the oracle's kappa); rows beyond EXT come out
@@ -744,6 +748,66 @@ hipError_t launch_fsa_fwd(const AttnArgs& a, int fmt, int D, int causal, hipStre
   if (fmt == FMT_E4M3) return launch32_2<FMT_E4M3>(a, D, causal, stream);
   if (fmt == FMT_E2M3) return launch32_2<FMT_E2M3>(a, D, causal, stream);
   return launch32_2<FMT_E2M1>(a, D, causal, stream);
+}
+
+namespace {
+
+// One wave per 32 query rows, lanes laid out as in the attention kernel's
+// prologue (lane (h, n) = 32 h + n holds D block 2c + h of query n for each
+// 64-wide D chunk c); each lane writes its operand bytes and scale byte back
+// in the public row layout.
+template <int F, int D>
+__global__ void __attribute__((amdgpu_flat_work_group_size(64, 64))) q_operand_dump_kernel(QDumpArgs a) {
+  constexpr int BITS = Fmt<F>::bits;
+  constexpr int ND = D / 64, NDB = D / 32, RB = D * BITS / 8;
+  const int lane = threadIdx.x;
+  const int hh = lane >> 5, n = lane & 31;
+  const int64_t r = (int64_t)blockIdx.x * 32 + n;
+  const bool live = r < a.rows;
+  const uint16_t* qrow = live ? a.q + r * D : nullptr;
+#pragma unroll
+  for (int c = 0; c < ND; ++c) {
+    int sc = 0;
+    const int blk = 2 * c + hh;
+    if constexpr (BITS == 8) {
+      const v8i o = q_operand32_e4m3<D>(qrow, a.qmul, c, hh, sc);
+      if (live) {
+        uint8_t* row = a.codes + r * RB;
+        *reinterpret_cast<uint4*>(row + 64 * c + 16 * hh) = make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint4*>(row + 64 * c + 32 + 16 * hh) = make_uint4(o[4], o[5], o[6], o[7]);
+      }
+    } else {
+      const opv<F> o = q_operand<F, D>(qrow, a.qmul, blk, sc);
+      if (live) {
+        uint8_t* dst = a.codes + r * RB + blk * 4 * BITS;
+        if constexpr (BITS == 6) {
+          uint2* d2 = reinterpret_cast<uint2*>(dst);
+          d2[0] = make_uint2(o[0], o[1]);
+          d2[1] = make_uint2(o[2], o[3]);
+          d2[2] = make_uint2(o[4], o[5]);
+        } else {
+          *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+      }
+    }
+    if (live) a.scales[r * NDB + blk] = (uint8_t)sc;
+  }
+}
+
+template <int F>
+hipError_t launch_q_dump_fmt(const QDumpArgs& a, int D, hipStream_t stream) {
+  const dim3 grid((unsigned)((a.rows + 31) / 32));
+  if (D == 128) hipLaunchKernelGGL((q_operand_dump_kernel<F, 128>), grid, dim3(64), 0, stream, a);
+  else hipLaunchKernelGGL((q_operand_dump_kernel<F, 64>), grid, dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_q_operand_dump(const QDumpArgs& a, int fmt, int D, hipStream_t stream) {
+  if (fmt == FMT_E4M3) return launch_q_dump_fmt<FMT_E4M3>(a, D, stream);
+  if (fmt == FMT_E2M3) return launch_q_dump_fmt<FMT_E2M3>(a, D, stream);
+  return launch_q_dump_fmt<FMT_E2M1>(a, D, stream);
 }
 
 }  // namespace fsa

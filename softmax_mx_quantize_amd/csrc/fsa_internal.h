@@ -82,6 +82,21 @@ struct AttnArgs {
 
 hipError_t launch_fsa_fwd(const AttnArgs& a, int fmt, int D, int causal, hipStream_t stream);
 
+// The attention kernel's Q' operands written out (a debug view): rows of
+// bf16 Q [rows][D] times qmul, MX-quantised by the very device functions of
+// the kernel's prologue.  codes [rows][D*bits/8] in the public packing,
+// scales [rows][D/32]: each block's E8M0 byte raised by 23 as the score
+// product consumes it (2^23 rides on Q's scale; 254 at most, 255 for NaN).
+struct QDumpArgs {
+  const uint16_t* q;
+  int64_t rows;
+  float qmul;
+  uint8_t* codes;
+  uint8_t* scales;
+};
+
+hipError_t launch_q_operand_dump(const QDumpArgs& a, int fmt, int D, hipStream_t stream);
+
 // Plain BF16 flash attention.
 constexpr int BF16_KEY_TILE = 64;
 struct Bf16Args {

@@ -20,7 +20,8 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ("fsa_quantize_mx", "fsa_attention_fwd", "fsa_attention_bf16_ref",
-              "fsa_attention_fwd_ex", "fsa_strerror", "fsa_release_workspace"):
+              "fsa_attention_fwd_ex", "fsa_strerror", "fsa_release_workspace",
+              "fsa_debug_operands"):
         assert n in names
 
 
@@ -64,6 +65,13 @@ def test_strerror_and_argument_validation_without_gpu():
                                  None) == -2
     assert lib.fsa_attention_bf16_ref(fake, fake + 4096, fake + 8192, fake + 12288, 1, 1, 1 << 23, 128, 0,
                                       None) == -2
+    # debug view: a half-given output pair, an unknown format
+    assert lib.fsa_debug_operands(fake, fake, fake, 1, 1, 8, 64, 0, fake, None, None, None, None, None,
+                                  None) == -1
+    assert lib.fsa_debug_operands(fake, fake, fake, 1, 1, 8, 64, 5, None, None, None, None, None, None,
+                                  None) == -1
+    assert lib.fsa_debug_operands(fake, fake, fake, 1, 1, 8, 96, 0, None, None, None, None, None, None,
+                                  None) == -2
     # bad per-head format in the options
     opt = fsa.Options()
     hf = (ctypes.c_int * 2)(0, 9)

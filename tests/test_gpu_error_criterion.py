@@ -27,7 +27,7 @@ import pytest
 
 import workloads as W
 import oracle as O
-from gpu_helpers import announce, to_dev, from_dev_bf16
+from gpu_helpers import announce, to_dev, from_dev_bf16, workload_tensors
 
 pytestmark = pytest.mark.gpu
 
@@ -44,10 +44,10 @@ def _threads():
     return max(1, min(16, n))
 
 
-def _head_errors(w, h, rows, g_rows):
+def _head_errors(w, h, qkv, rows, g_rows):
     """Per-row squared errors of the GPU output and of the plain MX path
     against exact attention for one head (oracle on the host)."""
-    qh, kh, vh = (W.bf16_bits_to_f64(x) for x in W.generate_head(w, 0, h))
+    qh, kh, vh = (W.bf16_bits_to_f64(x[0, h]) for x in qkv)
     ex = O.exact_attention(qh, kh, vh, w.causal, rows=rows)
     pl = O.plain_mx_attention(qh, kh, vh, w.head_fmts[h], w.causal, rows=rows)
     ef = np.sum((g_rows - ex) ** 2, axis=1)
@@ -61,18 +61,22 @@ def test_fused_error_within_1p1_of_plain_mx_per_head(name, n_rows):
     import softmax_mx_quantize_amd as fsa
     w = W.WORKLOADS[name]
     announce("error criterion", name, "rows per head", n_rows)
-    q, k, v = W.generate(w)
+    q, k, v = workload_tensors(w)
     hf = list(w.head_fmts)
     kw = {} if len(set(hf)) == 1 else {"head_fmt": hf}
     out = fsa.attention_fwd(to_dev(q), to_dev(k), to_dev(v), hf[0], w.causal, **kw)
     torch.cuda.synchronize()
     g = from_dev_bf16(out)
-    del out, q, k, v
+    del out
     samples = {h: np.sort(np.random.default_rng([77, h]).choice(w.S, n_rows, replace=False))
                for h in range(w.H)}
+    res = {}
     with concurrent.futures.ThreadPoolExecutor(_threads()) as ex:
-        futs = {h: ex.submit(_head_errors, w, h, samples[h], g[0, h, samples[h]]) for h in range(w.H)}
-        res = {h: f.result() for h, f in futs.items()}
+        futs = {ex.submit(_head_errors, w, h, (q, k, v), samples[h], g[0, h, samples[h]]): h
+                for h in range(w.H)}
+        for f in concurrent.futures.as_completed(futs):
+            res[futs[f]] = f.result()
+            print("  oracle done for head %d (%d of %d)" % (futs[f], len(res), w.H), flush=True)
     rng = np.random.default_rng(5)
     worst, EF, EP = [], 0.0, 0.0
     for h in range(w.H):
