@@ -46,7 +46,8 @@ typedef enum fsa_status {
   FSA_ERR_INVALID_ARG = -1,  /* null pointer, non-positive or overflowing size, bad enum */
   FSA_ERR_UNSUPPORTED = -2,  /* valid but not implemented (e.g. head dim other than 64/128) */
   FSA_ERR_HIP = -3,          /* a HIP runtime call or kernel launch failed */
-  FSA_ERR_NO_MEMORY = -4     /* workspace allocation failed */
+  FSA_ERR_NO_MEMORY = -4,    /* workspace allocation failed */
+  FSA_ERR_TOO_LARGE = -5     /* one head exceeds the fixed scratch of fsa_attention_fwd_noalloc */
 } fsa_status;
 
 typedef enum fsa_fmt {
@@ -133,7 +134,8 @@ typedef struct fsa_options {
    * row fall back; 0 in normal use. */
   float guess_bias;
   /* Optional device int32 [B][H][S]: receives each row's fallback offset in
-   * binades (0 for rows whose scores stayed under the frozen max). */
+   * binades (0 for rows whose scores stayed under the frozen max).  Give
+   * both row arrays or neither (else FSA_ERR_INVALID_ARG). */
   int32_t* row_kappa;
   /* Optional device float [B][H][S]: receives each row's frozen max, in
    * the same binade units as guess_bias. */
@@ -185,6 +187,28 @@ int fsa_attention_fwd_ex(const void* q, const void* k, const void* v, void* out,
 int fsa_debug_operands(const void* q, const void* k, const void* v, int B, int H, int S, int D,
                        int fmt, void* q_codes, void* q_scales, void* k_codes, void* k_scales,
                        void* v_codes, void* v_scales, void* stream);
+
+/*
+ * fsa_attention_fwd_noalloc -- fsa_attention_fwd_ex that allocates nothing.
+ *
+ * For callers that cannot allocate device memory: code under stream/graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, options, results and errors as fsa_attention_fwd_ex; the
+ * quantised operands, per-row offsets and fallback flag live in a fixed
+ * 64 MiB device array of the library (one per device, held until the
+ * process ends; its address is looked up once per device on the first call
+ * there) instead of the growing workspace.  Heads are processed in groups
+ * of one batch entry that fit the array, each quantised and attended in
+ * turn on `stream`.  FSA_ERR_TOO_LARGE if a single head does not fit (about
+ * 264 * S bytes per head at FP8, D = 128; S up to ~250k).  Every call on a
+ * device shares that device's array: calls that overlap in time on one
+ * device (different streams, or threads) race and must be serialised by
+ * the caller.  event_after_quantize, if given, is recorded after the first
+ * group's quantisation.
+ */
+int fsa_attention_fwd_noalloc(const void* q, const void* k, const void* v, void* out,
+                              int B, int H, int S, int D, int fmt, int causal,
+                              const fsa_options* opt, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* fsa_strerror(int status);

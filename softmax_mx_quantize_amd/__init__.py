@@ -21,7 +21,7 @@ LIB_PATH = os.environ.get("FSA_LIB_PATH") or os.path.join(_HERE, "libfsa.so")
 FMT = {"e4m3": 0, "e2m3": 1, "e2m1": 2}
 BITS = {0: 8, 1: 6, 2: 4}
 STATUS = {0: "FSA_OK", -1: "FSA_ERR_INVALID_ARG", -2: "FSA_ERR_UNSUPPORTED",
-          -3: "FSA_ERR_HIP", -4: "FSA_ERR_NO_MEMORY"}
+          -3: "FSA_ERR_HIP", -4: "FSA_ERR_NO_MEMORY", -5: "FSA_ERR_TOO_LARGE"}
 
 
 class FsaError(RuntimeError):
@@ -53,6 +53,8 @@ def _load() -> ctypes.CDLL:
     lib.fsa_attention_fwd_ex.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                          ctypes.POINTER(Options), vp]
     lib.fsa_attention_fwd_ex.restype = i32
+    lib.fsa_attention_fwd_noalloc.argtypes = lib.fsa_attention_fwd_ex.argtypes
+    lib.fsa_attention_fwd_noalloc.restype = i32
     lib.fsa_attention_bf16_ref.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.fsa_attention_bf16_ref.restype = i32
     lib.fsa_strerror.argtypes = [i32]
@@ -68,7 +70,7 @@ lib = _load()
 
 EXPORTS = ("fsa_quantize_mx", "fsa_attention_fwd", "fsa_attention_fwd_ex",
            "fsa_attention_bf16_ref", "fsa_strerror", "fsa_release_workspace",
-           "fsa_debug_operands")
+           "fsa_debug_operands", "fsa_attention_fwd_noalloc")
 
 
 def strerror(status: int) -> str:
@@ -127,11 +129,14 @@ def quantize_mx(x, fmt: Union[str, int], block_along_rows: bool = False):
 
 def attention_fwd(q, k, v, fmt: Union[str, int] = "e4m3", causal: bool = False, *,
                   guess_bias: float = 0.0, head_fmt: Optional[Sequence[Union[str, int]]] = None,
-                  return_rows: bool = False, event_after_quantize=None, out=None):
+                  return_rows: bool = False, event_after_quantize=None, out=None,
+                  no_alloc: bool = False):
     """Fused-softmax attention; q, k, v bf16 [B, H, S, D] CUDA tensors.
 
     With ``return_rows`` also returns the per-row fallback offsets (int32)
-    and frozen maxima (float32), each [B, H, S].
+    and frozen maxima (float32), each [B, H, S].  ``no_alloc`` calls
+    ``fsa_attention_fwd_noalloc`` (the library allocates nothing; the
+    tensors here are still torch's).
     """
     import torch
     _bf16_cuda(q, k, v)
@@ -157,10 +162,10 @@ def attention_fwd(q, k, v, fmt: Union[str, int] = "e4m3", causal: bool = False, 
             raise ValueError("head_fmt needs one entry per head")
         hf = (ctypes.c_int * H)(*[_fmt_id(x) for x in head_fmt])
         opt.head_fmt = hf
-    st = lib.fsa_attention_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                  B, H, S, D, _fmt_id(fmt), int(causal), ctypes.byref(opt),
-                                  _stream(q))
-    _check(st, "fsa_attention_fwd")
+    fn = lib.fsa_attention_fwd_noalloc if no_alloc else lib.fsa_attention_fwd_ex
+    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, S, D, _fmt_id(fmt),
+            int(causal), ctypes.byref(opt), _stream(q))
+    _check(st, "fsa_attention_fwd_noalloc" if no_alloc else "fsa_attention_fwd")
     if return_rows:
         return out, kappa, mg
     return out

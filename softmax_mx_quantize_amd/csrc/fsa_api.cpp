@@ -80,11 +80,6 @@ struct Carver {
   }
 };
 
-struct RunLayout {
-  int h0, hrun, fmt;
-  size_t kc, ks, vc, vs;
-};
-
 int validate_attn(const void* q, const void* k, const void* v, void* out, int B, int H, int S,
                   int D, int causal) {
   if (!q || !k || !v || !out) return FSA_ERR_INVALID_ARG;
@@ -125,6 +120,236 @@ int quantize(const uint16_t* x, uint8_t* codes, uint8_t* scales, int64_t batch, 
   return fsa::launch_mx_quant(a, fmt, mode, stream) == hipSuccess ? FSA_OK : FSA_ERR_HIP;
 }
 
+// ---- the attention call, shared by the allocating and the allocation-free
+// entry points
+
+// One launch group: batch entries [b0, b0 + nb) and heads [h0, h0 + n) of
+// each, all of format fmt.
+struct Piece {
+  int b0, nb, h0, n, fmt;
+};
+
+// Sub-allocation of one piece's quantised operands (and, when the caller
+// gives no per-row arrays, its rows' kappa and frozen max).
+struct PieceLayout {
+  size_t kc, ks, vc, vs, rk, rm;
+};
+
+PieceLayout carve_piece(Carver& cv, const Piece& p, int S, int D, int64_t sk_alloc, bool own_rows) {
+  const int bits = fmt_bits(p.fmt);
+  const int64_t nbh = (int64_t)p.nb * p.n;
+  PieceLayout l{};
+  l.kc = cv.take((size_t)(nbh * sk_alloc * D * bits / 8));
+  l.ks = cv.take((size_t)(nbh * sk_alloc * (D / 32)));
+  l.vc = cv.take((size_t)(nbh * D * sk_alloc * bits / 8));
+  l.vs = cv.take((size_t)(nbh * D * (sk_alloc / 32)));
+  if (own_rows) {
+    l.rk = cv.take((size_t)nbh * S * 4);
+    l.rm = cv.take((size_t)nbh * S * 4);
+  }
+  return l;
+}
+
+struct Call {
+  const uint16_t *q, *k, *v;
+  uint16_t* out;
+  int B, H, S, D, causal;
+  int64_t sk_alloc;
+  float score_scale;
+  hipStream_t stream;
+  const fsa_options* opt;
+};
+
+// MX-quantise K (blocks along D) and V (blocks along the keys, stored
+// transposed) of a piece; padding rows and blocks get zero codes.
+int quantize_piece(const Call& c, const Piece& p, uint8_t* base, const PieceLayout& l) {
+  const int bits = fmt_bits(p.fmt);
+  const int64_t rb = (int64_t)c.D * bits / 8, sk = c.sk_alloc;
+  for (int b = p.b0; b < p.b0 + p.nb; ++b) {
+    const int64_t src = ((int64_t)b * c.H + p.h0) * c.S * c.D;
+    const int64_t w0 = (int64_t)(b - p.b0) * p.n;
+    int st = quantize(c.k + src, base + l.kc + w0 * sk * rb, base + l.ks + w0 * sk * (c.D / 32), p.n, c.S,
+                      c.D, sk, c.D / 32, rb, c.D / 32, p.fmt, 0, c.stream, 1.0f, fsa::SCALES_KEY_TILES);
+    if (st != FSA_OK) return st;
+    st = quantize(c.v + src, base + l.vc + w0 * c.D * (sk * bits / 8), base + l.vs + w0 * c.D * (sk / 32),
+                  p.n, c.S, c.D, c.D, sk / 32, sk * bits / 8, sk / 32, p.fmt, 1, c.stream, 1.0f,
+                  fsa::SCALES_DIM_TILES);
+    if (st != FSA_OK) return st;
+  }
+  return FSA_OK;
+}
+
+// The fused kernel's two launches (sweep, then fallback pass) for a piece.
+// Q and O are read and written in place (Q is quantised in the kernel,
+// times log2(e)/sqrt(D), so that the score product comes out in binades of
+// the probability).  Per-row kappa and frozen max: `whole` arrays span
+// [B][H][S] (the caller's, or the workspace's); otherwise they are the
+// piece's own (one batch entry, S rows per head from its first head).
+int attend_piece(const Call& c, const Piece& p, uint8_t* base, const PieceLayout& l, int32_t* rk,
+                 float* rm, bool whole, uint64_t* flag) {
+  const int64_t boff = (int64_t)p.b0 * c.H;            // first head row of the piece's batch entries
+  fsa::AttnArgs a;
+  a.q = c.q + boff * c.S * c.D;
+  a.out = c.out + boff * c.S * c.D;
+  a.qmul = c.score_scale;
+  a.kc = base + l.kc; a.ks = base + l.ks;
+  a.vc = base + l.vc; a.vs = base + l.vs;
+  if (whole) {
+    a.row_kappa = rk + boff * c.S;
+    a.row_mguess = rm + boff * c.S;
+    a.row_bh0 = 0;
+  } else {
+    if (p.nb != 1) return FSA_ERR_INVALID_ARG;         // piece rows cover one batch entry
+    a.row_kappa = rk;
+    a.row_mguess = rm;
+    a.row_bh0 = p.h0;
+  }
+  a.B = p.nb; a.H = c.H; a.S = c.S;
+  a.h0 = p.h0; a.hrun = p.n;
+  a.sk_alloc = (int)c.sk_alloc;
+  a.bias = c.opt ? c.opt->guess_bias : 0.0f;
+  a.fb_flag = flag;
+  a.call_id = next_call_id();
+  return fsa::launch_fsa_fwd(a, kern_fmt(p.fmt), c.D, c.causal, c.stream) == hipSuccess ? FSA_OK
+                                                                                       : FSA_ERR_HIP;
+}
+
+int record_event(const Call& c) {
+  if (c.opt && c.opt->event_after_quantize &&
+      hipEventRecord(static_cast<hipEvent_t>(c.opt->event_after_quantize), c.stream) != hipSuccess)
+    return FSA_ERR_HIP;
+  return FSA_OK;
+}
+
+// Fixed scratch of the allocation-free entry point: one copy per device
+// (each device that runs it holds it until the process ends).  In host code
+// `scratch` names a host-side stand-in; its device address on each device
+// comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address is handed to kernels.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::unordered_map<int, uint8_t*> g_scratch;
+
+int scratch_address(uint8_t** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FSA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch.find(dev);
+  if (it == g_scratch.end()) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return FSA_ERR_HIP;
+    }
+    it = g_scratch.emplace(dev, static_cast<uint8_t*>(p)).first;
+  }
+  *out = it->second;
+  return FSA_OK;
+}
+
+int attention(const void* q, const void* k, const void* v, void* out, int B, int H, int S, int D,
+              int fmt, int causal, const fsa_options* opt, void* stream_, bool no_alloc) {
+  int st = validate_attn(q, k, v, out, B, H, S, D, causal);
+  if (st != FSA_OK) return st;
+  const int* head_fmt = opt ? opt->head_fmt : nullptr;
+  if (head_fmt) {
+    for (int h = 0; h < H; ++h)
+      if (!fmt_ok(head_fmt[h])) return FSA_ERR_INVALID_ARG;
+  } else if (!fmt_ok(fmt)) {
+    return FSA_ERR_INVALID_ARG;
+  }
+  if (opt && (opt->row_kappa == nullptr) != (opt->row_max_guess == nullptr)) return FSA_ERR_INVALID_ARG;
+  const bool own_rows = !(opt && opt->row_kappa);
+
+  Call c;
+  c.q = static_cast<const uint16_t*>(q);
+  c.k = static_cast<const uint16_t*>(k);
+  c.v = static_cast<const uint16_t*>(v);
+  c.out = static_cast<uint16_t*>(out);
+  c.B = B; c.H = H; c.S = S; c.D = D; c.causal = causal;
+  c.sk_alloc = round_up(S, kKeyTile);
+  c.score_scale = (float)((1.0 / std::log(2.0)) / std::sqrt((double)D));
+  c.stream = static_cast<hipStream_t>(stream_);
+  c.opt = opt;
+
+  // runs of consecutive heads with one format, each over every batch entry
+  std::vector<Piece> runs;
+  for (int h = 0; h < H;) {
+    const int f = head_fmt ? head_fmt[h] : fmt;
+    int e = h + 1;
+    while (e < H && (head_fmt ? head_fmt[e] : fmt) == f) ++e;
+    runs.push_back(Piece{0, B, h, e - h, f});
+    h = e;
+  }
+
+  if (!no_alloc) {
+    // all runs side by side in the growing workspace: quantise everything,
+    // then attend (the event between the two marks the attention kernels)
+    Carver cv;
+    std::vector<PieceLayout> lay;
+    for (const Piece& p : runs) lay.push_back(carve_piece(cv, p, S, D, c.sk_alloc, false));
+    const size_t rk = own_rows ? cv.take((size_t)B * H * S * 4) : 0;
+    const size_t rm = own_rows ? cv.take((size_t)B * H * S * 4) : 0;
+    const size_t flag_off = cv.take(8);
+    uint8_t* ws = nullptr;
+    st = workspace(cv.off, &ws);
+    if (st != FSA_OK) return st;
+    for (size_t i = 0; i < runs.size(); ++i) {
+      st = quantize_piece(c, runs[i], ws, lay[i]);
+      if (st != FSA_OK) return st;
+    }
+    if ((st = record_event(c)) != FSA_OK) return st;
+    int32_t* rkp = own_rows ? reinterpret_cast<int32_t*>(ws + rk) : opt->row_kappa;
+    float* rmp = own_rows ? reinterpret_cast<float*>(ws + rm) : opt->row_max_guess;
+    for (size_t i = 0; i < runs.size(); ++i) {
+      st = attend_piece(c, runs[i], ws, lay[i], rkp, rmp, true, reinterpret_cast<uint64_t*>(ws + flag_off));
+      if (st != FSA_OK) return st;
+    }
+    return FSA_OK;
+  }
+
+  // allocation-free: pieces of one batch entry and as many heads as the
+  // fixed scratch holds, each quantised and attended in turn (stream order
+  // keeps a piece's reuse of the scratch behind the previous piece's
+  // kernels)
+  uint8_t* base = nullptr;
+  if ((st = scratch_address(&base)) != FSA_OK) return st;
+  bool event_done = false;
+  for (const Piece& r : runs) {
+    int n_fit = 0;
+    for (int n = r.n; n >= 1; --n) {
+      Carver cv;
+      carve_piece(cv, Piece{0, 1, r.h0, n, r.fmt}, S, D, c.sk_alloc, own_rows);
+      cv.take(8);
+      if (cv.off <= kScratchBytes) { n_fit = n; break; }
+    }
+    if (n_fit == 0) return FSA_ERR_TOO_LARGE;          // one head does not fit
+    for (int b = 0; b < B; ++b)
+      for (int h = r.h0; h < r.h0 + r.n; h += n_fit) {
+        const Piece p{b, 1, h, std::min(n_fit, r.h0 + r.n - h), r.fmt};
+        Carver cv;
+        const PieceLayout l = carve_piece(cv, p, S, D, c.sk_alloc, own_rows);
+        const size_t flag_off = cv.take(8);
+        if ((st = quantize_piece(c, p, base, l)) != FSA_OK) return st;
+        if (!event_done) {
+          if ((st = record_event(c)) != FSA_OK) return st;
+          event_done = true;
+        }
+        if (own_rows)
+          st = attend_piece(c, p, base, l, reinterpret_cast<int32_t*>(base + l.rk),
+                            reinterpret_cast<float*>(base + l.rm), false,
+                            reinterpret_cast<uint64_t*>(base + flag_off));
+        else
+          st = attend_piece(c, p, base, l, opt->row_kappa, opt->row_max_guess, true,
+                            reinterpret_cast<uint64_t*>(base + flag_off));
+        if (st != FSA_OK) return st;
+      }
+  }
+  return FSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -136,6 +361,7 @@ const char* fsa_strerror(int status) {
     case FSA_ERR_UNSUPPORTED: return "unsupported configuration";
     case FSA_ERR_HIP: return "HIP runtime or launch error";
     case FSA_ERR_NO_MEMORY: return "device memory allocation failed";
+    case FSA_ERR_TOO_LARGE: return "one head exceeds the fixed 64 MiB scratch of the allocation-free call";
     default: return "unknown status";
   }
 }
@@ -161,106 +387,13 @@ int fsa_quantize_mx(const void* x_bf16, void* codes, void* scales_e8m0, int64_t 
 int fsa_attention_fwd_ex(const void* q, const void* k, const void* v, void* out, int B, int H,
                          int S, int D, int fmt, int causal, const fsa_options* opt,
                          void* stream_) {
-  int st = validate_attn(q, k, v, out, B, H, S, D, causal);
-  if (st != FSA_OK) return st;
-  const int* head_fmt = opt ? opt->head_fmt : nullptr;
-  if (head_fmt) {
-    for (int h = 0; h < H; ++h)
-      if (!fmt_ok(head_fmt[h])) return FSA_ERR_INVALID_ARG;
-  } else if (!fmt_ok(fmt)) {
-    return FSA_ERR_INVALID_ARG;
-  }
-  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  return attention(q, k, v, out, B, H, S, D, fmt, causal, opt, stream_, false);
+}
 
-  // runs of consecutive heads with one format
-  std::vector<RunLayout> runs;
-  for (int h = 0; h < H;) {
-    const int f = head_fmt ? head_fmt[h] : fmt;
-    int e = h + 1;
-    while (e < H && (head_fmt ? head_fmt[e] : fmt) == f) ++e;
-    RunLayout rl{};
-    rl.h0 = h;
-    rl.hrun = e - h;
-    rl.fmt = f;
-    runs.push_back(rl);
-    h = e;
-  }
-
-  const int64_t sk_alloc = round_up(S, kKeyTile);
-  Carver cv;
-  for (RunLayout& rl : runs) {
-    const int bits = fmt_bits(rl.fmt);
-    const int64_t nbh = (int64_t)B * rl.hrun;
-    rl.kc = cv.take((size_t)(nbh * sk_alloc * D * bits / 8));
-    rl.ks = cv.take((size_t)(nbh * sk_alloc * (D / 32)));
-    rl.vc = cv.take((size_t)(nbh * D * sk_alloc * bits / 8));
-    rl.vs = cv.take((size_t)(nbh * D * (sk_alloc / 32)));
-  }
-  // per-row frozen max and fallback offset, which the fallback pass reads
-  // back; the caller's arrays when given
-  const int64_t n_rows = (int64_t)B * H * S;
-  const bool own_kappa = !(opt && opt->row_kappa);
-  const bool own_mguess = !(opt && opt->row_max_guess);
-  const size_t rk_off = own_kappa ? cv.take((size_t)n_rows * 4) : 0;
-  const size_t rm_off = own_mguess ? cv.take((size_t)n_rows * 4) : 0;
-  const size_t flag_off = cv.take(8);
-  uint8_t* ws = nullptr;
-  st = workspace(cv.off, &ws);
-  if (st != FSA_OK) return st;
-  int32_t* row_kappa = own_kappa ? reinterpret_cast<int32_t*>(ws + rk_off) : opt->row_kappa;
-  float* row_mguess = own_mguess ? reinterpret_cast<float*>(ws + rm_off) : opt->row_max_guess;
-
-  const uint16_t* qb = static_cast<const uint16_t*>(q);
-  const uint16_t* kb = static_cast<const uint16_t*>(k);
-  const uint16_t* vb = static_cast<const uint16_t*>(v);
-
-  // MX-quantise K (blocks along D) and V (blocks along the keys, stored
-  // transposed) for every run; padding rows and blocks get zero codes.  Q is
-  // quantised inside the attention kernel, after scaling by the softmax scale
-  // in binades, c = fp32(log2(e) / sqrt(D)), so that the score product comes
-  // out in binades of the probability.
-  const float score_scale = (float)((1.0 / std::log(2.0)) / std::sqrt((double)D));
-  for (const RunLayout& rl : runs) {
-    const int bits = fmt_bits(rl.fmt);
-    const int64_t rb = (int64_t)D * bits / 8;
-    for (int b = 0; b < B; ++b) {
-      const int64_t src = ((int64_t)b * H + rl.h0) * S * D;
-      const int64_t w0 = (int64_t)b * rl.hrun;
-      st = quantize(kb + src, ws + rl.kc + w0 * sk_alloc * rb, ws + rl.ks + w0 * sk_alloc * (D / 32),
-                    rl.hrun, S, D, sk_alloc, D / 32, rb, D / 32, rl.fmt, 0, stream, 1.0f,
-                    fsa::SCALES_KEY_TILES);
-      if (st != FSA_OK) return st;
-      st = quantize(vb + src, ws + rl.vc + w0 * D * (sk_alloc * bits / 8),
-                    ws + rl.vs + w0 * D * (sk_alloc / 32), rl.hrun, S, D, D, sk_alloc / 32,
-                    sk_alloc * bits / 8, sk_alloc / 32, rl.fmt, 1, stream, 1.0f,
-                    fsa::SCALES_DIM_TILES);
-      if (st != FSA_OK) return st;
-    }
-  }
-  if (opt && opt->event_after_quantize) {
-    if (hipEventRecord(static_cast<hipEvent_t>(opt->event_after_quantize), stream) != hipSuccess)
-      return FSA_ERR_HIP;
-  }
-
-  for (const RunLayout& rl : runs) {
-    fsa::AttnArgs a;
-    a.q = qb;
-    a.qmul = score_scale;
-    a.kc = ws + rl.kc; a.ks = ws + rl.ks;
-    a.vc = ws + rl.vc; a.vs = ws + rl.vs;
-    a.out = static_cast<uint16_t*>(out);
-    a.row_kappa = row_kappa;
-    a.row_mguess = row_mguess;
-    a.B = B; a.H = H; a.S = S;
-    a.h0 = rl.h0; a.hrun = rl.hrun;
-    a.sk_alloc = (int)sk_alloc;
-    a.bias = opt ? opt->guess_bias : 0.0f;
-    a.fb_flag = reinterpret_cast<uint64_t*>(ws + flag_off);
-    a.call_id = next_call_id();
-    if (fsa::launch_fsa_fwd(a, kern_fmt(rl.fmt), D, causal, stream) != hipSuccess)
-      return FSA_ERR_HIP;
-  }
-  return FSA_OK;
+int fsa_attention_fwd_noalloc(const void* q, const void* k, const void* v, void* out, int B, int H,
+                              int S, int D, int fmt, int causal, const fsa_options* opt,
+                              void* stream_) {
+  return attention(q, k, v, out, B, H, S, D, fmt, causal, opt, stream_, true);
 }
 
 int fsa_attention_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int S,

@@ -304,7 +304,7 @@ fsa_fwd_kernel(AttnArgs a) {
   [[maybe_unused]] int kap_in = 0;
   if constexpr (REBASE) {
     if (*a.fb_flag != a.call_id) return;                    // the same for every workgroup
-    kap_in = q < S ? a.row_kappa[bh * S + q] : 0;
+    kap_in = q < S ? a.row_kappa[(bh - a.row_bh0) * S + q] : 0;
     if (!__syncthreads_or(kap_in > EXT)) return;            // the same for the whole workgroup
   }
 
@@ -407,7 +407,7 @@ fsa_fwd_kernel(AttnArgs a) {
   __syncthreads();
   if (n_tiles > 1) { issue_k(1, kl1); issue_v(1, vl1); }
   if constexpr (REBASE) {
-    mg = q < S ? a.row_mguess[bh * S + q] : 0.0f;
+    mg = q < S ? a.row_mguess[(bh - a.row_bh0) * S + q] : 0.0f;
   } else {
     const uint2 ksc = k_scales(kl0);
     v16f s0[2][2];
@@ -459,7 +459,7 @@ fsa_fwd_kernel(AttnArgs a) {
     // statistics of 2^23 s, back to binades (exact power-of-two scaling)
     mg = __builtin_fmaxf(mx, mean + z * sd) * 0x1p-23f + a.bias;
     // stored now, so that it need not stay live across the sweep
-    if (q < S && hh == 0) a.row_mguess[bh * S + q] = mg;
+    if (q < S && hh == 0) a.row_mguess[(bh - a.row_bh0) * S + q] = mg;
   }
 
   // ---- main sweep (no online max, no rescaling; a block above the guess
@@ -714,7 +714,7 @@ fsa_fwd_kernel(AttnArgs a) {
                             ((uint32_t)f32_to_bf16_rne(O[db][4 * gq + 3] * inv) << 16);
         *reinterpret_cast<uint2*>(orow + 32 * db + 8 * gq + 4 * he) = make_uint2(lo, hi);
       }
-    if (he == 0) a.row_kappa[row] = kap;
+    if (he == 0) a.row_kappa[(bh - a.row_bh0) * S + qe] = kap;
   }
   // tell the REBASE pass of this call that it has work (one vector store);
   // rows past S (a ragged last query tile) never ask for it

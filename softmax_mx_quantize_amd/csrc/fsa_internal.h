@@ -69,8 +69,9 @@ struct AttnArgs {
   const uint8_t* kc; const uint8_t* ks;
   const uint8_t* vc; const uint8_t* vs;
   uint16_t* out;                 // bf16 [B][H][S][D]
-  int32_t* row_kappa;            // [B][H][S], written by the first pass, read by the fallback pass
-  float* row_mguess;             // [B][H][S], likewise (frozen max, binades)
+  int32_t* row_kappa;            // rows of heads bh >= row_bh0 (bh = b*H + h), S per head:
+  float* row_mguess;             //   kappa and frozen max (binades), written by the first
+  int64_t row_bh0;               //   pass and read by the fallback pass
   int B, H, S;
   int h0, hrun;                  // heads [h0, h0+hrun) of each batch entry
   int sk_alloc;
