@@ -5,7 +5,10 @@ One step = one call of ``fsa_attention_fwd`` on the 16K-token Video-DiT-shaped
 workload (B=1, H=40, S=16384, D=128, non-causal, MXFP8 E4M3): MX quantisation
 of Q, K, V plus the fused attention kernel, inputs resident in HBM.  The same
 inputs are also timed with E2M3 and E2M1 operands and through the BF16
-flash-attention baseline.  FLOPs are 4*B*H*S^2*D (halved for causal).
+flash-attention baseline, and under causal masking; the outlier workload
+(MXFP4, S=32768, planted +8 sigma scores) and the long hybrid FP6/FP4
+schedule (S=75600) are timed as well ("workloads" in the JSON line).  FLOPs
+are 4*B*H*S^2*D (halved for causal).
 
 Prints ONE JSON line.  Options:
   --gpus N        only 1 is supported (the path is a single-GPU kernel)
@@ -13,6 +16,7 @@ Prints ONE JSON line.  Options:
   --warmup W      untimed steps first (default 10: the first launches after
                   idle run up to 30 % slower while the clock settles)
   --no-cpu        skip the CPU-oracle baseline
+  --no-extra      skip the other workloads (outliers, hybrid, causal)
   --only FMT      time only one element format (e4m3, e2m3, e2m1)
   --workload NAME time another workload of workloads.py instead (its own
                   formats, per head for the hybrid schedule) and print one
@@ -119,13 +123,14 @@ def write_traffic(fetch_db: str, write_db: str, copy_bytes: int) -> dict:
     return out
 
 
-def time_fsa(fsa, torch, q, k, v, fmt, steps, warmup):
+def time_fsa(fsa, torch, q, k, v, fmt, steps, warmup, causal=False, **kw):
     """Whole-step time (ms) and fused-kernel time (ms, from HIP events on the
-    stream the library launches on)."""
+    stream the library launches on: recorded by the library between the
+    quantisation and the attention kernels, and after the call)."""
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
-        fsa.attention_fwd(q, k, v, fmt, False, out=out)
+        fsa.attention_fwd(q, k, v, fmt, causal, out=out, **kw)
     torch.cuda.synchronize()
     mids = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -134,7 +139,7 @@ def time_fsa(fsa, torch, q, k, v, fmt, steps, warmup):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        fsa.attention_fwd(q, k, v, fmt, False, out=out, event_after_quantize=mids[i])
+        fsa.attention_fwd(q, k, v, fmt, causal, out=out, event_after_quantize=mids[i], **kw)
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
@@ -185,38 +190,30 @@ def cpu_baseline(w, budget_s: float = 15.0):
     }
 
 
-def bench_workload(name: str, steps: int, warmup: int) -> dict:
-    """Whole-call and kernel TFLOP/s of one workload in its own formats."""
+EXTRA_WORKLOADS = ("outliers_e2m1", "hybrid_long", "video_dit_e4m3_causal")
+
+
+def bench_workload(name: str, steps: int, warmup: int, tensors=None) -> dict:
+    """Whole-call and kernel TFLOP/s of one workload in its own formats
+    (per head for the hybrid schedule), inputs resident in HBM."""
     import numpy as np
     import torch
     import softmax_mx_quantize_amd as fsa
     import workloads as W
     w = W.WORKLOADS[name]
-    print("[bench] generating %s inputs" % w.name, file=sys.stderr, flush=True)
-    qb, kb, vb = W.generate(w)
-    dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
-    q, k, v = dev(qb), dev(kb), dev(vb)
-    del qb, kb, vb
+    if tensors is None:
+        print("[bench] generating %s inputs" % w.name, file=sys.stderr, flush=True)
+        qb, kb, vb = W.generate(w, workers=16)
+        dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        q, k, v = dev(qb), dev(kb), dev(vb)
+        del qb, kb, vb
+    else:
+        q, k, v = tensors
+    print("[bench] timing %s" % w.name, file=sys.stderr, flush=True)
     hf = list(w.head_fmts)
     kw = {} if len(set(hf)) == 1 else {"head_fmt": hf}
-    out = torch.empty_like(q)
-    stream = torch.cuda.current_stream()
-    call = lambda ev=None: fsa.attention_fwd(q, k, v, hf[0], w.causal, out=out, event_after_quantize=ev, **kw)
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    mids = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    for m in mids:
-        m.record(stream)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        call(mids[i])
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    kern_ms = sum(m.elapsed_time(e) for m, e in zip(mids, ends)) / steps
+    wall_ms, kern_ms, _ = time_fsa(fsa, torch, q, k, v, hf[0], steps, warmup, w.causal, **kw)
+    # the hybrid heads run at the FP6/FP4 peak (both 10.1 PFLOP/s)
     peak = max(PEAK_TFLOPS[f] for f in hf)
     return {"workload": w.name, "B": w.B, "H": w.H, "S": w.S, "D": w.D, "causal": w.causal,
             "head_fmts": sorted(set(hf)), "steps": steps, "warmup": warmup,
@@ -231,6 +228,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only", default=None)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--copy-bytes", type=int, default=0)
@@ -288,6 +286,16 @@ def main() -> int:
         for fmt in fmts:
             per[fmt]["speedup_vs_bf16"] = bms / per[fmt]["ms_per_step"]
 
+    # the other workloads of the method: planted outliers (fallbacks),
+    # the long hybrid FP6/FP4 schedule, and causal masking
+    extra = {}
+    if not args.only and not args.no_extra:
+        extra["video_dit_e4m3_causal"] = bench_workload("video_dit_e4m3_causal", args.steps,
+                                                        args.warmup, tensors=(q, k, v))
+        for name in ("outliers_e2m1", "hybrid_long"):
+            extra[name] = bench_workload(name, args.steps, args.warmup)
+            torch.cuda.empty_cache()
+
     if args.copy_bytes:
         # a plain streaming kernel of known traffic: reads and writes copy_bytes
         n = args.copy_bytes // 4
@@ -326,6 +334,7 @@ def main() -> int:
         },
         "formats": per,
         "bf16_baseline": bf16,
+        "workloads": extra,
     }
     if not args.no_cpu:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)

@@ -83,17 +83,24 @@ __device__ __forceinline__ float conv_scale(int sb) {
   return __uint_as_float((uint32_t)(sb + REF) << 23);
 }
 
+// Largest block level whose offset the first pass records exactly: the
+// patterns themselves stay exact up to level 511 (y < 2^32); rows at
+// KSAT binades or more above their guess are marked as KSAT and measured
+// again by the fallback pass.
+constexpr int LEVEL_MAX = 510;
+constexpr int KSAT = LEVEL_MAX - (127 + REF);
+static_assert(KSAT > EXT, "offsets beyond the in-sweep shifts must be recorded");
+
 // Level of a block whose largest pattern is m: the binade plus 127 + REF,
 // i.e. the exponent field of m after rounding its mantissa to M bits
 // (nearest, ties to even): floor(RNE(2^M m / 2^23) / 2^M).  For a pattern
 // from y >= 2^23 this is the binade of block_binade below; smaller patterns
 // lie below every level the shifts distinguish.  m is clamped first so that
-// the rounding cannot carry out of 32 bits; the clamp sits one level above
-// the largest shift (127 + REF + EXT), so the row still reaches the
-// fallback.
+// the rounding cannot carry out of 32 bits; up to LEVEL_MAX the level is
+// exact, so the first pass knows the offset of every row below KSAT.
 template <int M>
 __device__ __forceinline__ int block_level(uint32_t m) {
-  constexpr uint32_t LIM = (uint32_t)(127 + REF + EXT + 1) << 23;
+  constexpr uint32_t LIM = (uint32_t)LEVEL_MAX << 23;
   const uint32_t mc = min(m, LIM);
   const uint32_t lsb = (mc >> (23 - M)) & 1u;
   return (int)((mc + (1u << (22 - M)) - 1u + lsb) >> 23);

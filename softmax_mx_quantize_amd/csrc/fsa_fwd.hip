@@ -149,10 +149,12 @@ __device__ __forceinline__ v8i q_operand32_e4m3(const uint16_t* row, float mult,
 
 // REBASE: the fallback pass of a call.  A workgroup does nothing unless
 // the first pass stamped the call's flag and left one of its rows more than
-// EXT binades above its frozen max; it then measures each row's offset kappa
-// exactly from the fp32 scores (a scores-only sweep), sweeps again from the
-// reference raised by kappa whole binades (no shift is then clamped), and
-// overwrites the rows the first pass left beyond EXT.
+// EXT binades above its frozen max; it then sweeps again from the reference
+// raised by each row's offset kappa (whole binades, so no shift is clamped)
+// and overwrites the rows the first pass left beyond EXT.  The first pass
+// records kappa exactly below KSAT; only a workgroup with a row at KSAT or
+// beyond first measures its rows' offsets from the fp32 scores in a
+// scores-only sweep.
 template <int F, int D, bool CAUSAL, bool REBASE>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
 fsa_fwd_kernel(AttnArgs a) {
@@ -623,8 +625,8 @@ fsa_fwd_kernel(AttnArgs a) {
   };
   using F0 = std::false_type;
   using T1 = std::true_type;
-  [[maybe_unused]] int kap_x = 0;
-  if constexpr (REBASE) {
+  [[maybe_unused]] int kap_x = kap_in;
+  if (REBASE && __syncthreads_or(kap_in >= KSAT)) {
     // scores-only sweep: the largest binade of any visible score above the
     // frozen max, exact to HI_BINADE (the bit patterns saturate far sooner)
     int km = -(1 << 30);
@@ -659,6 +661,8 @@ fsa_fwd_kernel(AttnArgs a) {
     wait_dma();
     __syncthreads();
     if (n_tiles > 1) { issue_k(1, kl1); issue_v(1, vl1); }
+  }
+  if constexpr (REBASE) {
     c0 = __builtin_fmaf(-8388608.0f, mg, 8388608.0f * (float)(127 + REF - kap_x));
 #pragma unroll
     for (int i = 0; i < 16; ++i) minit[i] = c0;

@@ -140,6 +140,12 @@ def test_rows_far_above_the_guess(fmt):
     ref, rk, bd, inf = _oracle_heads(q, k, v, [fmt], False, bias=-100.0)
     assert np.all(rk > 64)
     _check(g, kap, mg, ref, rk, bd, inf)
+    # beyond the offsets the first pass records (321 binades): the fallback
+    # pass measures them again from the scores
+    g, kap, mg = _run(q, k, v, fmt, False, guess_bias=-400.0)
+    ref, rk, bd, inf = _oracle_heads(q, k, v, [fmt], False, bias=-400.0)
+    assert np.all(rk > 321)
+    _check(g, kap, mg, ref, rk, bd, inf)
 
 
 def test_tiny_workload_parity_and_error_criterion():

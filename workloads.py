@@ -70,6 +70,10 @@ WORKLOADS: Dict[str, Workload] = {
     # The same tensors with E2M1 elements.
     "video_dit_e2m1": Workload("video_dit_e2m1", 1, 40, 16384, 128, False, 1,
                                _uniform_fmt("e2m1", 40), gain_range=(0.5, 2.0)),
+    # The Video-DiT E4M3 tensors with causal masking (key j visible to query
+    # i iff j <= i): the masked tiles and the causal tile skipping.
+    "video_dit_e4m3_causal": Workload("video_dit_e4m3_causal", 1, 40, 16384, 128, True, 1,
+                                      _uniform_fmt("e4m3", 40), gain_range=(0.5, 2.0)),
     # E2M1 with planted +8 sigma scores in 1 % of the query rows.
     "outliers_e2m1": Workload("outliers_e2m1", 1, 40, 32768, 128, False, 3,
                               _uniform_fmt("e2m1", 40), outlier_frac=0.01),
