@@ -127,7 +127,17 @@ int fsa_attention_fwd(const void* q, const void* k, const void* v, void* out,
 int fsa_attention_bf16_ref(const void* q, const void* k, const void* v, void* out,
                            int B, int H, int S, int D, int causal, void* stream);
 
-/* Test and benchmark hooks for fsa_attention_fwd_ex.  Zero-initialise. */
+/* Element strides of strided views: for each tensor, the strides of the
+ * batch, head and row indices (element (b, h, s, d) at b*st[0] + h*st[1] +
+ * s*st[2] + d).  D is contiguous; each stride a multiple of 8 (16-byte
+ * aligned rows) and the row stride at least D.  A [B][S][H][D] tensor viewed
+ * as [B][H][S][D], for instance, has strides {S*H*D, D, H*D}. */
+typedef struct fsa_layout {
+  int64_t q[3], k[3], v[3], out[3];
+} fsa_layout;
+
+/* Options of fsa_attention_fwd_ex / fsa_attention_fwd_noalloc.
+ * Zero-initialise. */
 typedef struct fsa_options {
   /* Added to every frozen max, in binades of the probability (units of
    * log2(e) * q.k / sqrt(D)).  A negative value of a few binades makes every
@@ -143,9 +153,15 @@ typedef struct fsa_options {
   /* Optional hipEvent_t (as void*) recorded on `stream` between the
    * quantisation kernels and the attention kernel, for kernel-only timing. */
   void* event_after_quantize;
-  /* Optional host array of H fsa_fmt values: per-head element format (one
-   * launch for a hybrid schedule).  NULL: every head uses `fmt`. */
+  /* Optional host array of H fsa_fmt values: per-head element format (the
+   * hybrid MXFP6/MXFP4 schedule of Fused-Softmax for efficient quantized
+   * attention, summary).  Every format runs in the same launches: one
+   * quantiser launch for K, one for V and one attention launch pair per
+   * call (per 256 heads).  NULL: every head uses `fmt`. */
   const int* head_fmt;
+  /* Optional strides of q, k, v and out (strided views); NULL: contiguous
+   * [B][H][S][D].  Bad strides give FSA_ERR_INVALID_ARG. */
+  const fsa_layout* layout;
 } fsa_options;
 
 /* fsa_attention_fwd with hooks; opt may be NULL.  Same errors. */

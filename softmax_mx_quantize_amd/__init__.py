@@ -30,6 +30,12 @@ class FsaError(RuntimeError):
         self.status = status
 
 
+class Layout(ctypes.Structure):
+    """Mirror of ``fsa_layout``: element strides (batch, head, row) per tensor."""
+    _fields_ = [("q", ctypes.c_int64 * 3), ("k", ctypes.c_int64 * 3),
+                ("v", ctypes.c_int64 * 3), ("out", ctypes.c_int64 * 3)]
+
+
 class Options(ctypes.Structure):
     """Mirror of ``fsa_options``."""
     _fields_ = [
@@ -38,6 +44,7 @@ class Options(ctypes.Structure):
         ("row_max_guess", ctypes.c_void_p),
         ("event_after_quantize", ctypes.c_void_p),
         ("head_fmt", ctypes.POINTER(ctypes.c_int)),
+        ("layout", ctypes.POINTER(Layout)),
     ]
 
 
@@ -98,15 +105,35 @@ def _bf16_cuda(*ts) -> None:
             raise ValueError("expected contiguous bf16 CUDA tensors")
 
 
+def _bf16_rows(*ts) -> None:
+    """bf16 CUDA tensors [B, H, S, D] whose rows are contiguous (strided
+    views, e.g. of a [B, S, H, D] tensor, are fine)."""
+    import torch
+    for t in ts:
+        if not (t.is_cuda and t.dtype == torch.bfloat16 and t.dim() == 4 and t.stride(-1) == 1):
+            raise ValueError("expected bf16 CUDA tensors [B, H, S, D] with contiguous rows")
+
+
+def _layout(q, k, v, out):
+    """An fsa_layout when any tensor is not contiguous [B, H, S, D]."""
+    if all(t.is_contiguous() for t in (q, k, v, out)):
+        return None
+    lay = Layout()
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        getattr(lay, name)[:] = [t.stride(0), t.stride(1), t.stride(2)]
+    return lay
+
+
 def _out_like(out, q):
-    """A caller's output tensor must match q in shape, dtype, device and
-    layout (the kernels write whole bf16 rows); a new one otherwise."""
+    """A caller's output tensor must match q in shape, dtype and device,
+    with contiguous rows (the kernels write whole bf16 rows); a new
+    contiguous one otherwise."""
     import torch
     if out is None:
-        return torch.empty_like(q)
-    _bf16_cuda(out)
+        return torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    _bf16_rows(out)
     if out.shape != q.shape or out.device != q.device:
-        raise ValueError("out must be a contiguous bf16 tensor of q's shape on q's device")
+        raise ValueError("out must be a bf16 tensor of q's shape on q's device, rows contiguous")
     return out
 
 
@@ -131,7 +158,8 @@ def attention_fwd(q, k, v, fmt: Union[str, int] = "e4m3", causal: bool = False, 
                   guess_bias: float = 0.0, head_fmt: Optional[Sequence[Union[str, int]]] = None,
                   return_rows: bool = False, event_after_quantize=None, out=None,
                   no_alloc: bool = False):
-    """Fused-softmax attention; q, k, v bf16 [B, H, S, D] CUDA tensors.
+    """Fused-softmax attention; q, k, v bf16 [B, H, S, D] CUDA tensors
+    (strided views with contiguous rows are passed with their strides).
 
     With ``return_rows`` also returns the per-row fallback offsets (int32)
     and frozen maxima (float32), each [B, H, S].  ``no_alloc`` calls
@@ -139,7 +167,7 @@ def attention_fwd(q, k, v, fmt: Union[str, int] = "e4m3", causal: bool = False, 
     tensors here are still torch's).
     """
     import torch
-    _bf16_cuda(q, k, v)
+    _bf16_rows(q, k, v)
     B, H, S, D = q.shape
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must have the same shape")
@@ -156,6 +184,9 @@ def attention_fwd(q, k, v, fmt: Union[str, int] = "e4m3", causal: bool = False, 
         opt.row_max_guess = mg.data_ptr()
     if event_after_quantize is not None:
         opt.event_after_quantize = event_after_quantize.cuda_event
+    lay = _layout(q, k, v, out)
+    if lay is not None:
+        opt.layout = ctypes.pointer(lay)
     hf = None
     if head_fmt is not None:
         if len(head_fmt) != H:
@@ -181,6 +212,7 @@ def attention_bf16_ref(q, k, v, causal: bool = False, out=None):
     if k.device != q.device or v.device != q.device:
         raise ValueError("q, k, v must be on one device")
     out = _out_like(out, q)
+    _bf16_cuda(out)                 # the baseline writes contiguous [B, H, S, D]
     _check(lib.fsa_attention_bf16_ref(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                       B, H, S, D, int(causal), _stream(q)), "fsa_attention_bf16_ref")
     return out

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstddef>
@@ -99,11 +100,12 @@ int validate_attn(const void* q, const void* k, const void* v, void* out, int B,
   return FSA_OK;
 }
 
+// One quantiser launch over `batch` contiguous [rows][cols] inputs of one
+// format; outputs are contiguous too (out_rows rows of nb_out blocks each).
 int quantize(const uint16_t* x, uint8_t* codes, uint8_t* scales, int64_t batch, int64_t rows,
-             int64_t cols, int64_t out_rows, int64_t nb_out, int64_t code_stride,
-             int64_t scale_stride, int fmt, int mode, hipStream_t stream, float mult = 1.0f,
+             int64_t cols, int64_t out_rows, int64_t nb_out, int fmt, int mode, hipStream_t stream,
              int scale_layout = fsa::SCALES_ROWS) {
-  fsa::QuantArgs a;
+  fsa::QuantArgs a{};
   a.x = x;
   a.codes = codes;
   a.scales = scales;
@@ -112,43 +114,31 @@ int quantize(const uint16_t* x, uint8_t* codes, uint8_t* scales, int64_t batch, 
   a.cols = cols;
   a.out_rows = out_rows;
   a.nb_out = nb_out;
-  a.code_stride = code_stride;
-  a.scale_stride = scale_stride;
+  a.code_slab = out_rows * nb_out * 4 * fmt_bits(fmt);
+  a.x_sb = rows * cols;
+  a.x_sh = 0;
+  a.x_sr = cols;
+  a.nh = 1;
   a.batch0 = 0;
-  a.mult = mult;
+  a.mult = 1.0f;
   a.scale_layout = scale_layout;
-  return fsa::launch_mx_quant(a, fmt, mode, stream) == hipSuccess ? FSA_OK : FSA_ERR_HIP;
+  a.fmt[0] = (uint8_t)kern_fmt(fmt);
+  return fsa::launch_mx_quant(a, 1 << kern_fmt(fmt), mode, stream) == hipSuccess ? FSA_OK : FSA_ERR_HIP;
 }
 
 // ---- the attention call, shared by the allocating and the allocation-free
 // entry points
 
+// Element strides (batch entry, head, row) of the four tensors.
+struct Strides {
+  int64_t q[3], k[3], v[3], o[3];
+};
+
 // One launch group: batch entries [b0, b0 + nb) and heads [h0, h0 + n) of
-// each, all of format fmt.
+// each, each head in its own format.
 struct Piece {
-  int b0, nb, h0, n, fmt;
+  int b0, nb, h0, n;
 };
-
-// Sub-allocation of one piece's quantised operands (and, when the caller
-// gives no per-row arrays, its rows' kappa and frozen max).
-struct PieceLayout {
-  size_t kc, ks, vc, vs, rk, rm;
-};
-
-PieceLayout carve_piece(Carver& cv, const Piece& p, int S, int D, int64_t sk_alloc, bool own_rows) {
-  const int bits = fmt_bits(p.fmt);
-  const int64_t nbh = (int64_t)p.nb * p.n;
-  PieceLayout l{};
-  l.kc = cv.take((size_t)(nbh * sk_alloc * D * bits / 8));
-  l.ks = cv.take((size_t)(nbh * sk_alloc * (D / 32)));
-  l.vc = cv.take((size_t)(nbh * D * sk_alloc * bits / 8));
-  l.vs = cv.take((size_t)(nbh * D * (sk_alloc / 32)));
-  if (own_rows) {
-    l.rk = cv.take((size_t)nbh * S * 4);
-    l.rm = cv.take((size_t)nbh * S * 4);
-  }
-  return l;
-}
 
 struct Call {
   const uint16_t *q, *k, *v;
@@ -158,24 +148,79 @@ struct Call {
   float score_scale;
   hipStream_t stream;
   const fsa_options* opt;
+  Strides st;
+  std::vector<int> fmt;            // per head
 };
 
-// MX-quantise K (blocks along D) and V (blocks along the keys, stored
-// transposed) of a piece; padding rows and blocks get zero codes.
-int quantize_piece(const Call& c, const Piece& p, uint8_t* base, const PieceLayout& l) {
-  const int bits = fmt_bits(p.fmt);
-  const int64_t rb = (int64_t)c.D * bits / 8, sk = c.sk_alloc;
-  for (int b = p.b0; b < p.b0 + p.nb; ++b) {
-    const int64_t src = ((int64_t)b * c.H + p.h0) * c.S * c.D;
-    const int64_t w0 = (int64_t)(b - p.b0) * p.n;
-    int st = quantize(c.k + src, base + l.kc + w0 * sk * rb, base + l.ks + w0 * sk * (c.D / 32), p.n, c.S,
-                      c.D, sk, c.D / 32, rb, c.D / 32, p.fmt, 0, c.stream, 1.0f, fsa::SCALES_KEY_TILES);
-    if (st != FSA_OK) return st;
-    st = quantize(c.v + src, base + l.vc + w0 * c.D * (sk * bits / 8), base + l.vs + w0 * c.D * (sk / 32),
-                  p.n, c.S, c.D, c.D, sk / 32, sk * bits / 8, sk / 32, p.fmt, 1, c.stream, 1.0f,
-                  fsa::SCALES_DIM_TILES);
-    if (st != FSA_OK) return st;
+int piece_bits(const Call& c, const Piece& p) {
+  int bits = 4;
+  for (int h = p.h0; h < p.h0 + p.n; ++h) bits = std::max(bits, fmt_bits(c.fmt[h]));
+  return bits;
+}
+
+int piece_fset(const Call& c, const Piece& p) {
+  int fs = 0;
+  for (int h = p.h0; h < p.h0 + p.n; ++h) fs |= 1 << kern_fmt(c.fmt[h]);
+  return fs;
+}
+
+// Sub-allocation of one piece's quantised operands (slabs of the widest
+// format present) and, when the caller gives no per-row arrays, its rows'
+// kappa and frozen max.
+struct PieceLayout {
+  size_t kc, ks, vc, vs, rk, rm;
+  int64_t kc_slab, vc_slab;
+};
+
+PieceLayout carve_piece(Carver& cv, const Call& c, const Piece& p, bool own_rows, int bits = 0) {
+  if (bits == 0) bits = piece_bits(c, p);
+  const int64_t nbh = (int64_t)p.nb * p.n;
+  PieceLayout l{};
+  l.kc_slab = c.sk_alloc * c.D * bits / 8;
+  l.vc_slab = (int64_t)c.D * c.sk_alloc * bits / 8;
+  l.kc = cv.take((size_t)(nbh * l.kc_slab));
+  l.ks = cv.take((size_t)(nbh * c.sk_alloc * (c.D / 32)));
+  l.vc = cv.take((size_t)(nbh * l.vc_slab));
+  l.vs = cv.take((size_t)(nbh * c.D * (c.sk_alloc / 32)));
+  if (own_rows) {
+    l.rk = cv.take((size_t)nbh * c.S * 4);
+    l.rm = cv.take((size_t)nbh * c.S * 4);
   }
+  return l;
+}
+
+// MX-quantise K (blocks along D) and V (blocks along the keys, stored
+// transposed) of a piece, each head in its own format, in one launch each;
+// padding rows and blocks get zero codes.
+int quantize_piece(const Call& c, const Piece& p, uint8_t* base, const PieceLayout& l) {
+  fsa::QuantArgs a{};
+  a.batch = (int64_t)p.nb * p.n;
+  a.rows = c.S;
+  a.cols = c.D;
+  a.nh = p.n;
+  a.mult = 1.0f;
+  for (int j = 0; j < p.n; ++j) a.fmt[j] = (uint8_t)kern_fmt(c.fmt[p.h0 + j]);
+  const int fset = piece_fset(c, p);
+  // K: output rows are keys (padded to sk_alloc), blocks along D
+  a.x = c.k + p.b0 * c.st.k[0] + p.h0 * c.st.k[1];
+  a.x_sb = c.st.k[0]; a.x_sh = c.st.k[1]; a.x_sr = c.st.k[2];
+  a.codes = base + l.kc;
+  a.scales = base + l.ks;
+  a.out_rows = c.sk_alloc;
+  a.nb_out = c.D / 32;
+  a.code_slab = l.kc_slab;
+  a.scale_layout = fsa::SCALES_KEY_TILES;
+  if (fsa::launch_mx_quant(a, fset, 0, c.stream) != hipSuccess) return FSA_ERR_HIP;
+  // V: output rows are the D columns, blocks along the keys
+  a.x = c.v + p.b0 * c.st.v[0] + p.h0 * c.st.v[1];
+  a.x_sb = c.st.v[0]; a.x_sh = c.st.v[1]; a.x_sr = c.st.v[2];
+  a.codes = base + l.vc;
+  a.scales = base + l.vs;
+  a.out_rows = c.D;
+  a.nb_out = c.sk_alloc / 32;
+  a.code_slab = l.vc_slab;
+  a.scale_layout = fsa::SCALES_DIM_TILES;
+  if (fsa::launch_mx_quant(a, fset, 1, c.stream) != hipSuccess) return FSA_ERR_HIP;
   return FSA_OK;
 }
 
@@ -187,13 +232,16 @@ int quantize_piece(const Call& c, const Piece& p, uint8_t* base, const PieceLayo
 // piece's own (one batch entry, S rows per head from its first head).
 int attend_piece(const Call& c, const Piece& p, uint8_t* base, const PieceLayout& l, int32_t* rk,
                  float* rm, bool whole, uint64_t* flag) {
-  const int64_t boff = (int64_t)p.b0 * c.H;            // first head row of the piece's batch entries
-  fsa::AttnArgs a;
-  a.q = c.q + boff * c.S * c.D;
-  a.out = c.out + boff * c.S * c.D;
+  fsa::AttnArgs a{};
+  a.q = c.q + p.b0 * c.st.q[0];
+  a.out = c.out + p.b0 * c.st.o[0];
+  a.q_sb = c.st.q[0]; a.q_sh = c.st.q[1]; a.q_ss = c.st.q[2];
+  a.o_sb = c.st.o[0]; a.o_sh = c.st.o[1]; a.o_ss = c.st.o[2];
   a.qmul = c.score_scale;
   a.kc = base + l.kc; a.ks = base + l.ks;
   a.vc = base + l.vc; a.vs = base + l.vs;
+  a.kc_slab = l.kc_slab; a.vc_slab = l.vc_slab;
+  const int64_t boff = (int64_t)p.b0 * c.H;            // first head row of the piece's batch entries
   if (whole) {
     a.row_kappa = rk + boff * c.S;
     a.row_mguess = rm + boff * c.S;
@@ -210,8 +258,32 @@ int attend_piece(const Call& c, const Piece& p, uint8_t* base, const PieceLayout
   a.bias = c.opt ? c.opt->guess_bias : 0.0f;
   a.fb_flag = flag;
   a.call_id = next_call_id();
-  return fsa::launch_fsa_fwd(a, kern_fmt(p.fmt), c.D, c.causal, c.stream) == hipSuccess ? FSA_OK
-                                                                                       : FSA_ERR_HIP;
+  // formats per head, and the order workgroups take the heads in: the
+  // formats interleaved, so that each XCD's contiguous share of the items
+  // holds each format in proportion
+  std::vector<int> by_fmt[3];
+  for (int j = 0; j < p.n; ++j) {
+    const int f = kern_fmt(c.fmt[p.h0 + j]);
+    a.hfmt[j] = (uint8_t)f;
+    by_fmt[f].push_back(j);
+  }
+  {
+    size_t at[3] = {0, 0, 0};
+    int slot = 0;
+    while (slot < p.n) {
+      // take next from the format that is furthest behind its share
+      int best = -1;
+      double lag = 0.0;
+      for (int f = 0; f < 3; ++f) {
+        if (at[f] >= by_fmt[f].size()) continue;
+        const double want = (double)(slot + 1) * by_fmt[f].size() / p.n - (double)at[f];
+        if (best < 0 || want > lag) { best = f; lag = want; }
+      }
+      a.horder[slot++] = (uint8_t)by_fmt[best][at[best]++];
+    }
+  }
+  return fsa::launch_fsa_fwd(a, piece_fset(c, p), c.D, c.causal, c.stream) == hipSuccess ? FSA_OK
+                                                                                          : FSA_ERR_HIP;
 }
 
 int record_event(const Call& c) {
@@ -249,6 +321,23 @@ int scratch_address(uint8_t** out) {
   return FSA_OK;
 }
 
+// Strides of a tensor argument: the caller's, or those of a contiguous
+// [B][H][S][D] tensor.  Rows must start 16 bytes apart multiples (the
+// kernels load 16-byte vectors); D is contiguous.
+bool take_strides(const int64_t* given, int H, int S, int D, int64_t out[3]) {
+  if (!given) {
+    out[0] = (int64_t)H * S * D;
+    out[1] = (int64_t)S * D;
+    out[2] = D;
+    return true;
+  }
+  for (int i = 0; i < 3; ++i) {
+    if (given[i] < 0 || given[i] % 8 != 0) return false;
+    out[i] = given[i];
+  }
+  return out[2] >= D;
+}
+
 int attention(const void* q, const void* k, const void* v, void* out, int B, int H, int S, int D,
               int fmt, int causal, const fsa_options* opt, void* stream_, bool no_alloc) {
   int st = validate_attn(q, k, v, out, B, H, S, D, causal);
@@ -273,38 +362,38 @@ int attention(const void* q, const void* k, const void* v, void* out, int B, int
   c.score_scale = (float)((1.0 / std::log(2.0)) / std::sqrt((double)D));
   c.stream = static_cast<hipStream_t>(stream_);
   c.opt = opt;
-
-  // runs of consecutive heads with one format, each over every batch entry
-  std::vector<Piece> runs;
-  for (int h = 0; h < H;) {
-    const int f = head_fmt ? head_fmt[h] : fmt;
-    int e = h + 1;
-    while (e < H && (head_fmt ? head_fmt[e] : fmt) == f) ++e;
-    runs.push_back(Piece{0, B, h, e - h, f});
-    h = e;
-  }
+  const fsa_layout* lay = opt ? opt->layout : nullptr;
+  if (!take_strides(lay ? lay->q : nullptr, H, S, D, c.st.q) ||
+      !take_strides(lay ? lay->k : nullptr, H, S, D, c.st.k) ||
+      !take_strides(lay ? lay->v : nullptr, H, S, D, c.st.v) ||
+      !take_strides(lay ? lay->out : nullptr, H, S, D, c.st.o))
+    return FSA_ERR_INVALID_ARG;
+  c.fmt.assign(H, fmt);
+  if (head_fmt) c.fmt.assign(head_fmt, head_fmt + H);
 
   if (!no_alloc) {
-    // all runs side by side in the growing workspace: quantise everything,
-    // then attend (the event between the two marks the attention kernels)
+    // every batch entry and up to MAX_HEAD_TABLE heads per piece, side by
+    // side in the growing workspace: quantise everything, then attend (the
+    // event between the two marks the attention kernels)
+    std::vector<Piece> pieces;
+    for (int h = 0; h < H; h += fsa::MAX_HEAD_TABLE)
+      pieces.push_back(Piece{0, B, h, std::min(fsa::MAX_HEAD_TABLE, H - h)});
     Carver cv;
-    std::vector<PieceLayout> lay;
-    for (const Piece& p : runs) lay.push_back(carve_piece(cv, p, S, D, c.sk_alloc, false));
+    std::vector<PieceLayout> lays;
+    for (const Piece& p : pieces) lays.push_back(carve_piece(cv, c, p, false));
     const size_t rk = own_rows ? cv.take((size_t)B * H * S * 4) : 0;
     const size_t rm = own_rows ? cv.take((size_t)B * H * S * 4) : 0;
     const size_t flag_off = cv.take(8);
     uint8_t* ws = nullptr;
     st = workspace(cv.off, &ws);
     if (st != FSA_OK) return st;
-    for (size_t i = 0; i < runs.size(); ++i) {
-      st = quantize_piece(c, runs[i], ws, lay[i]);
-      if (st != FSA_OK) return st;
-    }
+    for (size_t i = 0; i < pieces.size(); ++i)
+      if ((st = quantize_piece(c, pieces[i], ws, lays[i])) != FSA_OK) return st;
     if ((st = record_event(c)) != FSA_OK) return st;
     int32_t* rkp = own_rows ? reinterpret_cast<int32_t*>(ws + rk) : opt->row_kappa;
     float* rmp = own_rows ? reinterpret_cast<float*>(ws + rm) : opt->row_max_guess;
-    for (size_t i = 0; i < runs.size(); ++i) {
-      st = attend_piece(c, runs[i], ws, lay[i], rkp, rmp, true, reinterpret_cast<uint64_t*>(ws + flag_off));
+    for (size_t i = 0; i < pieces.size(); ++i) {
+      st = attend_piece(c, pieces[i], ws, lays[i], rkp, rmp, true, reinterpret_cast<uint64_t*>(ws + flag_off));
       if (st != FSA_OK) return st;
     }
     return FSA_OK;
@@ -316,37 +405,37 @@ int attention(const void* q, const void* k, const void* v, void* out, int B, int
   // kernels)
   uint8_t* base = nullptr;
   if ((st = scratch_address(&base)) != FSA_OK) return st;
-  bool event_done = false;
-  for (const Piece& r : runs) {
-    int n_fit = 0;
-    for (int n = r.n; n >= 1; --n) {
-      Carver cv;
-      carve_piece(cv, Piece{0, 1, r.h0, n, r.fmt}, S, D, c.sk_alloc, own_rows);
-      cv.take(8);
-      if (cv.off <= kScratchBytes) { n_fit = n; break; }
-    }
-    if (n_fit == 0) return FSA_ERR_TOO_LARGE;          // one head does not fit
-    for (int b = 0; b < B; ++b)
-      for (int h = r.h0; h < r.h0 + r.n; h += n_fit) {
-        const Piece p{b, 1, h, std::min(n_fit, r.h0 + r.n - h), r.fmt};
-        Carver cv;
-        const PieceLayout l = carve_piece(cv, p, S, D, c.sk_alloc, own_rows);
-        const size_t flag_off = cv.take(8);
-        if ((st = quantize_piece(c, p, base, l)) != FSA_OK) return st;
-        if (!event_done) {
-          if ((st = record_event(c)) != FSA_OK) return st;
-          event_done = true;
-        }
-        if (own_rows)
-          st = attend_piece(c, p, base, l, reinterpret_cast<int32_t*>(base + l.rk),
-                            reinterpret_cast<float*>(base + l.rm), false,
-                            reinterpret_cast<uint64_t*>(base + flag_off));
-        else
-          st = attend_piece(c, p, base, l, opt->row_kappa, opt->row_max_guess, true,
-                            reinterpret_cast<uint64_t*>(base + flag_off));
-        if (st != FSA_OK) return st;
-      }
+  // as many heads per piece as fit at the widest format of the call
+  int n_fit = 0;
+  for (int n = std::min(H, fsa::MAX_HEAD_TABLE); n >= 1; --n) {
+    Carver cv;
+    carve_piece(cv, c, Piece{0, 1, 0, n}, own_rows, piece_bits(c, Piece{0, 1, 0, H}));
+    cv.take(8);
+    if (cv.off <= kScratchBytes) { n_fit = n; break; }
   }
+  if (n_fit == 0) return FSA_ERR_TOO_LARGE;          // one head does not fit
+  bool event_done = false;
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < H; h += n_fit) {
+      const Piece p{b, 1, h, std::min(n_fit, H - h)};
+      Carver cv;
+      const PieceLayout l = carve_piece(cv, c, p, own_rows);
+      const size_t flag_off = cv.take(8);
+      if (cv.off > kScratchBytes) return FSA_ERR_TOO_LARGE;
+      if ((st = quantize_piece(c, p, base, l)) != FSA_OK) return st;
+      if (!event_done) {
+        if ((st = record_event(c)) != FSA_OK) return st;
+        event_done = true;
+      }
+      if (own_rows)
+        st = attend_piece(c, p, base, l, reinterpret_cast<int32_t*>(base + l.rk),
+                          reinterpret_cast<float*>(base + l.rm), false,
+                          reinterpret_cast<uint64_t*>(base + flag_off));
+      else
+        st = attend_piece(c, p, base, l, opt->row_kappa, opt->row_max_guess, true,
+                          reinterpret_cast<uint64_t*>(base + flag_off));
+      if (st != FSA_OK) return st;
+    }
   return FSA_OK;
 }
 
@@ -379,9 +468,8 @@ int fsa_quantize_mx(const void* x_bf16, void* codes, void* scales_e8m0, int64_t 
   if ((double)batch * out_rows * nb > 2147483647.0 * 256.0) return FSA_ERR_INVALID_ARG;
   if ((double)batch * rows * cols > 9.0e18) return FSA_ERR_INVALID_ARG;
   return quantize(static_cast<const uint16_t*>(x_bf16), static_cast<uint8_t*>(codes),
-                  static_cast<uint8_t*>(scales_e8m0), batch, rows, cols, out_rows, nb,
-                  nb * 4 * bits, nb, fmt, block_along_rows,
-                  static_cast<hipStream_t>(stream));
+                  static_cast<uint8_t*>(scales_e8m0), batch, rows, cols, out_rows, nb, fmt,
+                  block_along_rows, static_cast<hipStream_t>(stream));
 }
 
 int fsa_attention_fwd_ex(const void* q, const void* k, const void* v, void* out, int B, int H,
@@ -455,14 +543,14 @@ int fsa_debug_operands(const void* q, const void* k, const void* v, int B, int H
   // the same quantiser calls as the attention path makes into its workspace
   if (k_codes) {
     const int st = quantize(static_cast<const uint16_t*>(k), static_cast<uint8_t*>(k_codes),
-                            static_cast<uint8_t*>(k_scales), nbh, S, D, sk, D / 32, rb, D / 32, fmt, 0,
-                            stream, 1.0f, fsa::SCALES_KEY_TILES);
+                            static_cast<uint8_t*>(k_scales), nbh, S, D, sk, D / 32, fmt, 0, stream,
+                            fsa::SCALES_KEY_TILES);
     if (st != FSA_OK) return st;
   }
   if (v_codes) {
     const int st = quantize(static_cast<const uint16_t*>(v), static_cast<uint8_t*>(v_codes),
-                            static_cast<uint8_t*>(v_scales), nbh, S, D, D, sk / 32, sk * bits / 8, sk / 32,
-                            fmt, 1, stream, 1.0f, fsa::SCALES_DIM_TILES);
+                            static_cast<uint8_t*>(v_scales), nbh, S, D, D, sk / 32, fmt, 1, stream,
+                            fsa::SCALES_DIM_TILES);
     if (st != FSA_OK) return st;
   }
   return FSA_OK;

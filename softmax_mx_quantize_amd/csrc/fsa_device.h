@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fsa {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -58,6 +60,27 @@ template <> struct Fmt<FMT_E2M1> {
   static constexpr float maxval = 6.0f;
   static constexpr uint32_t one_code = 0x2;
 };
+
+// Calls fn(std::integral_constant<int, F>) for the element format f, which
+// must be in the bit set FSET (1 << FMT_*); with a single format the call
+// is direct and f is not read.
+template <int FSET, typename Fn>
+__device__ __forceinline__ void with_format(int f, Fn&& fn) {
+  if constexpr (FSET == (1 << FMT_E4M3)) fn(std::integral_constant<int, FMT_E4M3>{});
+  else if constexpr (FSET == (1 << FMT_E2M3)) fn(std::integral_constant<int, FMT_E2M3>{});
+  else if constexpr (FSET == (1 << FMT_E2M1)) fn(std::integral_constant<int, FMT_E2M1>{});
+  else {
+    if constexpr ((FSET >> FMT_E4M3) & 1) {
+      if (f == FMT_E4M3) { fn(std::integral_constant<int, FMT_E4M3>{}); return; }
+    }
+    if constexpr ((FSET >> FMT_E2M3) & 1) {
+      if (f == FMT_E2M3) { fn(std::integral_constant<int, FMT_E2M3>{}); return; }
+    }
+    if constexpr ((FSET >> FMT_E2M1) & 1) {
+      if (f == FMT_E2M1) { fn(std::integral_constant<int, FMT_E2M1>{}); return; }
+    }
+  }
+}
 
 // Matrix-core operand of 32 elements in the format's packing: FP8 8 dwords,
 // FP6 6 dwords, FP4 4 dwords.  The narrow FP6/FP4 vectors keep registers

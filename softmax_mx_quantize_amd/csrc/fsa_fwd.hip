@@ -155,9 +155,14 @@ __device__ __forceinline__ v8i q_operand32_e4m3(const uint16_t* row, float mult,
 // records kappa exactly below KSAT; only a workgroup with a row at KSAT or
 // beyond first measures its rows' offsets from the fp32 scores in a
 // scores-only sweep.
+//
+// One workgroup's work: query tile q_wg of head h of batch entry b, whose
+// quantised K^ / V^T are slab wi of the workspace, in element format F.
+// The LDS stages are the kernel's (their size depends on D only).
 template <int F, int D, bool CAUSAL, bool REBASE>
-__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
-fsa_fwd_kernel(AttnArgs a) {
+__device__ __forceinline__ void attn_body(const AttnArgs& a, const int b, const int h,
+                                          const int64_t wi, const int q_wg, uint8_t* kl0,
+                                          uint8_t* kl1, uint8_t* vl0, uint8_t* vl1) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer-resource types exist only in the device pass
   constexpr int NWAVES = 4;
   constexpr int BITS = Fmt<F>::bits;
@@ -194,10 +199,7 @@ fsa_fwd_kernel(AttnArgs a) {
   // Two-stage rings (two workgroups share a CU); one LDS object per stage,
   // always addressed through a compile-time stage index so that the
   // compiler sees that reads of one stage never alias the DMA into the other.
-  __shared__ __align__(16) uint8_t kl0[KSTAGE];
-  __shared__ __align__(16) uint8_t kl1[KSTAGE];
-  __shared__ __align__(16) uint8_t vl0[VSTAGE];
-  __shared__ __align__(16) uint8_t vl1[VSTAGE];
+  static_assert(KSTAGE == attn_kstage_bytes(D) && VSTAGE == attn_vstage_bytes(D), "LDS stages");
   auto kstage = [&](auto st_tag) __attribute__((always_inline)) -> uint8_t* {
     if constexpr (decltype(st_tag)::value == 0) return kl0; else return kl1;
   };
@@ -211,29 +213,17 @@ fsa_fwd_kernel(AttnArgs a) {
   const int hh = lane >> 5;                  // lane half
   const int n = lane & 31;                   // query column / A row of the products
 
-  // XCD-aware work order: workgroup i runs on XCD i % 8; each XCD takes a
-  // contiguous run of (head, query tile) items so that the workgroups
-  // sharing its L2 sweep the same head's K^ and V^.
-  const int nq = (a.S + QW - 1) / QW;
-  const int n_items = nq * a.B * a.hrun;
-  const int per_xcd = (n_items + 7) / 8;
-  // (The REBASE pass deals its items round-robin instead: its few busy
-  // workgroups, often all from one head, then spread over every XCD.)
-  const int item = REBASE ? (int)blockIdx.x : (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-  if (item >= n_items) return;
-  const int64_t wi = item / nq;
-  const int b = (int)wi / a.hrun;
-  const int h = a.h0 + ((int)wi - b * a.hrun);
   const int64_t bh = (int64_t)b * a.H + h;
   const int S = a.S;
-  const int q_wg = (item - (int)wi * nq) * QW;
   const int q_wave = q_wg + wave * 32;
   const int q = q_wave + n;                  // this lane's query
 
-  const uint8_t* kc = a.kc + wi * (int64_t)a.sk_alloc * RB;
+  // slabs of the widest format in the launch; this head's rows are packed
+  // in its own format at their start
+  const uint8_t* kc = a.kc + wi * a.kc_slab;
   const uint8_t* ks = a.ks + wi * (int64_t)a.sk_alloc * NDB;
   const int64_t v_row = (int64_t)a.sk_alloc * BITS / 8;
-  const uint8_t* vc = a.vc + wi * (int64_t)D * v_row;
+  const uint8_t* vc = a.vc + wi * a.vc_slab;
   const int vs_row = a.sk_alloc / 32;
   const uint8_t* vs = a.vs + wi * (int64_t)D * vs_row;
 
@@ -322,7 +312,7 @@ fsa_fwd_kernel(AttnArgs a) {
   int qsc[ND];
 #pragma unroll
   for (int c = 0; c < ND; ++c) {
-    const uint16_t* qrow = q < S ? a.q + (bh * S + q) * (int64_t)D : nullptr;
+    const uint16_t* qrow = q < S ? a.q + b * a.q_sb + h * a.q_sh + (int64_t)q * a.q_ss : nullptr;
     if constexpr (BITS == 8) qf[c] = q_operand32_e4m3<D>(qrow, a.qmul, c, hh, qsc[c]);
     else qf[c] = q_operand<F, D>(qrow, a.qmul, 2 * c + hh, qsc[c]);
   }
@@ -706,8 +696,7 @@ fsa_fwd_kernel(AttnArgs a) {
   const int he = lane_e >> 5;
   if (qe < S && (!REBASE || kap_in > EXT)) {
     const float inv = 1.0f / lsum;
-    const int64_t row = bh * S + qe;
-    uint16_t* orow = a.out + row * (int64_t)D;
+    uint16_t* orow = a.out + b * a.o_sb + h * a.o_sh + (int64_t)qe * a.o_ss;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -727,31 +716,72 @@ fsa_fwd_kernel(AttnArgs a) {
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
+// The attention kernel over the heads [h0, h0 + hrun) of every batch entry,
+// each in its own element format from FSET (a bit set of FMT_*): one
+// launch for a hybrid schedule.  The format is uniform per workgroup, so
+// the branch into its body is a scalar one.
+template <int FSET, int D, bool CAUSAL, bool REBASE>
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
+fsa_fwd_kernel(AttnArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __shared__ __align__(16) uint8_t kl0[attn_kstage_bytes(D)];
+  __shared__ __align__(16) uint8_t kl1[attn_kstage_bytes(D)];
+  __shared__ __align__(16) uint8_t vl0[attn_vstage_bytes(D)];
+  __shared__ __align__(16) uint8_t vl1[attn_vstage_bytes(D)];
+  constexpr int QW = 128;                    // queries per workgroup
+  // XCD-aware work order: workgroup i runs on XCD i % 8; each XCD takes a
+  // contiguous run of (batch entry, head slot, query tile) items so that
+  // the workgroups sharing its L2 sweep the same head's K^ and V^.  Head
+  // slots follow a.horder, which interleaves the formats of a hybrid
+  // schedule so that every XCD gets its share of each.
+  const int nq = (a.S + QW - 1) / QW;
+  const int n_items = nq * a.B * a.hrun;
+  const int per_xcd = (n_items + 7) / 8;
+  // (The REBASE pass deals its items round-robin instead: its few busy
+  // workgroups, often all from one head, then spread over every XCD.)
+  const int item = REBASE ? (int)blockIdx.x : (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (item >= n_items) return;
+  const int bs = item / nq;                  // (batch entry, head slot)
+  const int b = bs / a.hrun;
+  const int j = a.horder[bs - b * a.hrun];   // head within the launch
+  const int64_t wi = (int64_t)b * a.hrun + j;
+  const int q_wg = (item - bs * nq) * QW;
+  const int f = (FSET & (FSET - 1)) ? a.hfmt[j] : 0;
+  with_format<FSET>(f, [&](auto fc) {
+    attn_body<decltype(fc)::value, D, CAUSAL, REBASE>(a, b, a.h0 + j, wi, q_wg, kl0, kl1, vl0, vl1);
+  });
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
 namespace {
 
-template <int F, int D, bool CAUSAL>
+template <int FSET, int D, bool CAUSAL>
 hipError_t launch32_3(const AttnArgs& a, hipStream_t stream) {
   constexpr int QW = 128;
   const int n_items = (a.S + QW - 1) / QW * a.B * a.hrun;
   dim3 grid((n_items + 7) / 8 * 8);
-  hipLaunchKernelGGL((fsa_fwd_kernel<F, D, CAUSAL, false>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((fsa_fwd_kernel<FSET, D, CAUSAL, false>), grid, dim3(256), 0, stream, a);
   // the fallback pass: ~4 us when the first pass left no row beyond EXT
-  hipLaunchKernelGGL((fsa_fwd_kernel<F, D, CAUSAL, true>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((fsa_fwd_kernel<FSET, D, CAUSAL, true>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int F>
+template <int FSET>
 hipError_t launch32_2(const AttnArgs& a, int D, int causal, hipStream_t stream) {
-  if (D == 128) return causal ? launch32_3<F, 128, true>(a, stream) : launch32_3<F, 128, false>(a, stream);
-  return causal ? launch32_3<F, 64, true>(a, stream) : launch32_3<F, 64, false>(a, stream);
+  if (D == 128) return causal ? launch32_3<FSET, 128, true>(a, stream) : launch32_3<FSET, 128, false>(a, stream);
+  return causal ? launch32_3<FSET, 64, true>(a, stream) : launch32_3<FSET, 64, false>(a, stream);
 }
 
 }  // namespace
 
-hipError_t launch_fsa_fwd(const AttnArgs& a, int fmt, int D, int causal, hipStream_t stream) {
-  if (fmt == FMT_E4M3) return launch32_2<FMT_E4M3>(a, D, causal, stream);
-  if (fmt == FMT_E2M3) return launch32_2<FMT_E2M3>(a, D, causal, stream);
-  return launch32_2<FMT_E2M1>(a, D, causal, stream);
+hipError_t launch_fsa_fwd(const AttnArgs& a, int fset, int D, int causal, hipStream_t stream) {
+  switch (fset) {
+    case 1 << FMT_E4M3: return launch32_2<1 << FMT_E4M3>(a, D, causal, stream);
+    case 1 << FMT_E2M3: return launch32_2<1 << FMT_E2M3>(a, D, causal, stream);
+    case 1 << FMT_E2M1: return launch32_2<1 << FMT_E2M1>(a, D, causal, stream);
+    case (1 << FMT_E2M3) | (1 << FMT_E2M1): return launch32_2<(1 << FMT_E2M3) | (1 << FMT_E2M1)>(a, D, causal, stream);
+    default: return launch32_2<7>(a, D, causal, stream);
+  }
 }
 
 namespace {

@@ -6,24 +6,33 @@
 
 namespace fsa {
 
-// MX quantiser geometry.  MODE 0: blocks along `cols`; output row o in
-// [0, batch*out_rows) maps to input row o % out_rows (rows >= `rows` are
-// padding and get zero codes and scale byte 0).  MODE 1: blocks along
-// `rows`, output row o in [0, batch*cols) is input column o % cols
-// (out_rows must equal cols).  Blocks b >= ceil(valid/32) up to nb_out are
-// zero padding.
+// Heads of one launch whose formats and order travel in the kernel
+// arguments (at most this many per launch).
+constexpr int MAX_HEAD_TABLE = 256;
+
+// MX quantiser geometry.  The launch covers `batch` slabs; slab w reads head
+// w % nh of batch entry w / nh: element (r, c) at x + (w / nh) * x_sb +
+// (w % nh) * x_sh + r * x_sr + c (columns contiguous).  MODE 0: blocks along
+// `cols`, output row r of slab w is input row r (rows >= `rows` are padding:
+// zero codes, scale byte 0).  MODE 1: blocks along `rows`, output row r of
+// slab w is input column r (out_rows must equal cols).  Blocks
+// b >= ceil(valid/32) up to nb_out are zero padding.  A code row takes
+// nb_out * 4 * bits bytes (bits of the slab's format), a slab's codes start
+// at w * code_slab; scale rows take nb_out bytes, out_rows of them per slab.
 struct QuantArgs {
   const uint16_t* x;
   uint8_t* codes;
   uint8_t* scales;
   int64_t batch, rows, cols;
-  int64_t out_rows;      // output rows per batch
+  int64_t out_rows;      // output rows per slab
   int64_t nb_out;        // blocks per output row
-  int64_t code_stride;   // bytes between output code rows
-  int64_t scale_stride;  // bytes between output scale rows
-  int64_t batch0;        // first batch entry of this launch (columns mode)
+  int64_t code_slab;     // bytes between slabs' codes
+  int64_t x_sb, x_sh, x_sr;   // input element strides
+  int nh;                // heads per batch entry
+  int64_t batch0;        // first slab of this launch (columns mode)
   float mult;            // every input value is multiplied by this (fp32) first
   int scale_layout;      // SCALES_* below
+  uint8_t fmt[MAX_HEAD_TABLE];  // element format (FMT_*) of head slot w % nh
 };
 
 // Scale byte layouts.  ROWS: scales[row][block] (the public layout).  The two
@@ -56,19 +65,26 @@ __host__ __device__ inline int dim_tile_byte(int dd, int kb, int d) {
   return (32 * (kb & 1) + (dd & 31)) * (d / 16) + (kb >> 1) * (d / 32) + (dd >> 5);
 }
 
-hipError_t launch_mx_quant(const QuantArgs& a, int fmt, int mode, hipStream_t stream);
+// `fset`: the formats present in a.fmt[0, nh), as a bit set (1 << FMT_*).
+hipError_t launch_mx_quant(const QuantArgs& a, int fset, int mode, hipStream_t stream);
 
-// Fused attention for the heads [h0, h0+hrun) of every batch entry.  Q is
-// read as bf16 and MX-quantised in the kernel (times qmul); K^ and V^ come
-// from the quantiser.  Workspace slabs are indexed by w = b*hrun + (h - h0):
-//   K^ codes [BH][sk_alloc][D*bits/8], scales in the KEY_TILES layout
-//   V^ (transposed) codes [BH][D][sk_alloc*bits/8], scales in DIM_TILES
-// sk_alloc covers every key tile; the padding holds zero codes.
+// Fused attention for the heads [h0, h0+hrun) of every batch entry, head
+// h0 + j in element format hfmt[j].  Q is read as bf16 and MX-quantised in
+// the kernel (times qmul); K^ and V^ come from the quantiser.  Workspace
+// slabs are indexed by w = b*hrun + j, kc_slab / vc_slab bytes apart (the
+// widest format's size), each packed in its head's own format:
+//   K^ codes [sk_alloc][D*bits/8], scales [sk_alloc][D/32] in the KEY_TILES
+//   layout; V^ (transposed) codes [D][sk_alloc*bits/8], scales in DIM_TILES.
+// sk_alloc covers every key tile; the padding holds zero codes.  Q and O
+// element (b, h, s, d) sit at b*sb + h*sh + s*ss + d.
 struct AttnArgs {
-  const uint16_t* q;             // bf16 [B][H][S][D]
+  const uint16_t* q;             // bf16
   const uint8_t* kc; const uint8_t* ks;
   const uint8_t* vc; const uint8_t* vs;
-  uint16_t* out;                 // bf16 [B][H][S][D]
+  uint16_t* out;                 // bf16
+  int64_t q_sb, q_sh, q_ss;      // element strides of Q
+  int64_t o_sb, o_sh, o_ss;      // element strides of O
+  int64_t kc_slab, vc_slab;      // bytes between K^ / V^T code slabs
   int32_t* row_kappa;            // rows of heads bh >= row_bh0 (bh = b*H + h), S per head:
   float* row_mguess;             //   kappa and frozen max (binades), written by the first
   int64_t row_bh0;               //   pass and read by the fallback pass
@@ -79,9 +95,17 @@ struct AttnArgs {
   float bias;                    // added to every frozen max, binades
   uint64_t* fb_flag;             // stamped with call_id when a row needs the fallback
   uint64_t call_id;              // unique per call (never 0)
+  uint8_t hfmt[MAX_HEAD_TABLE];  // element format (FMT_*) of head h0 + j
+  uint8_t horder[MAX_HEAD_TABLE];  // head slot -> j: the order workgroups take heads in
 };
 
-hipError_t launch_fsa_fwd(const AttnArgs& a, int fmt, int D, int causal, hipStream_t stream);
+// LDS stages of the attention kernel (128-byte rows): one 128-key tile of
+// K^ rows plus its scales, and D rows of V^T plus theirs.
+constexpr int attn_kstage_bytes(int d) { return 128 * 128 + 128 * (d / 32); }
+constexpr int attn_vstage_bytes(int d) { return d * 128 + 4 * d; }
+
+// `fset`: the formats present in a.hfmt[0, hrun), as a bit set (1 << FMT_*).
+hipError_t launch_fsa_fwd(const AttnArgs& a, int fset, int D, int causal, hipStream_t stream);
 
 // The attention kernel's Q' operands written out (a debug view): rows of
 // bf16 Q [rows][D] times qmul, MX-quantised by the very device functions of

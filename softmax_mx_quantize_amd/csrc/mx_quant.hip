@@ -17,16 +17,18 @@
 // (64-byte loads per thread, contiguous across the wave).  Columns mode: the
 // block runs along the row axis and the output is transposed; a workgroup
 // stages a 128-row x 32-column tile in LDS with 16-byte loads first.
+#include <type_traits>
+
 #include "fsa_device.h"
 #include "fsa_internal.h"
 
 namespace fsa {
 
 // Quantise one block of 32 values (already multiplied by a.mult) and write
-// its codes and scale byte: output row o (over all batch entries), block b.
+// its codes and scale byte: slab w, output row r, block b.
 template <int F>
 __device__ __forceinline__ void quantize_block(const QuantArgs& a, float (&v)[32], bool bad,
-                                               int64_t o, int64_t b) {
+                                               int64_t w, int64_t r, int64_t b) {
   constexpr int BITS = Fmt<F>::bits;
   constexpr int OUT_BYTES = 4 * BITS;   // 32 elements
   float amax = 0.0f;
@@ -37,50 +39,49 @@ __device__ __forceinline__ void quantize_block(const QuantArgs& a, float (&v)[32
   float y[32];
 #pragma unroll
   for (int j = 0; j < 32; ++j) y[j] = __builtin_ldexpf(v[j], -X);
-  uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  Pack32<F, true>::run(y, w);
+  uint32_t wd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  Pack32<F, true>::run(y, wd);
   uint8_t sbyte = (uint8_t)(X + 127);
   if (bad) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = 0;
+    for (int i = 0; i < 8; ++i) wd[i] = 0;
     sbyte = 0xFF;
   }
-  uint8_t* dst = a.codes + o * a.code_stride + b * OUT_BYTES;
+  uint8_t* dst = a.codes + w * a.code_slab + r * (a.nb_out * OUT_BYTES) + b * OUT_BYTES;
   if (BITS == 8) {
     uint4* d4 = reinterpret_cast<uint4*>(dst);
-    d4[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    d4[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    d4[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    d4[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
   } else if (BITS == 6) {
     uint2* d2 = reinterpret_cast<uint2*>(dst);
-    d2[0] = make_uint2(w[0], w[1]);
-    d2[1] = make_uint2(w[2], w[3]);
-    d2[2] = make_uint2(w[4], w[5]);
+    d2[0] = make_uint2(wd[0], wd[1]);
+    d2[1] = make_uint2(wd[2], wd[3]);
+    d2[2] = make_uint2(wd[4], wd[5]);
   } else {
-    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(dst) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
   }
-  int64_t so = o * a.scale_stride + b;
+  const int64_t nb = a.nb_out;
+  int64_t so = (w * a.out_rows + r) * nb + b;
   if (a.scale_layout == SCALES_KEY_TILES) {
-    // o = (batch, key row), b = block along D; rows per batch entry are a
-    // whole number of 128-key tiles
-    const int nb = (int)a.nb_out;
-    const int64_t bt = o / a.out_rows;
-    const int64_t row = o - bt * a.out_rows;
-    so = bt * a.out_rows * nb + (row >> 7) * 128 * nb + key_tile_byte((int)(row & 127), (int)b, 32 * nb, BITS);
+    // r = key row, b = block along D; rows per slab are a whole number of
+    // 128-key tiles
+    so = w * a.out_rows * nb + (r >> 7) * 128 * nb + key_tile_byte((int)(r & 127), (int)b, 32 * (int)nb, BITS);
   } else if (a.scale_layout == SCALES_DIM_TILES) {
-    // o = (batch, d), b = key block; blocks per row are a whole number of
-    // 4-block tiles
-    const int64_t bt = o / a.out_rows;
-    const int d = (int)(o - bt * a.out_rows);
-    so = bt * a.out_rows * a.nb_out + (b >> 2) * 4 * a.out_rows +
-         dim_tile_byte(d, (int)(b & 3), (int)a.out_rows);
+    // r = d, b = key block; blocks per row are a whole number of 4-block tiles
+    so = w * a.out_rows * nb + (b >> 2) * 4 * a.out_rows + dim_tile_byte((int)r, (int)(b & 3), (int)a.out_rows);
   }
   a.scales[so] = sbyte;
+}
+
+__device__ __forceinline__ const uint16_t* slab_input(const QuantArgs& a, int64_t w) {
+  const int64_t b = w / a.nh;
+  return a.x + b * a.x_sb + (w - b * a.nh) * a.x_sh;
 }
 
 // Rows mode: blocks along the contiguous axis; one thread per block,
 // consecutive threads take consecutive blocks of a row (64-byte loads per
 // thread, contiguous across the wave).
-template <int F, bool VEC>
+template <int FSET, bool VEC>
 __global__ void __launch_bounds__(256) mx_quant_rows_kernel(QuantArgs a) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t n_out_rows = a.batch * a.out_rows;
@@ -89,20 +90,20 @@ __global__ void __launch_bounds__(256) mx_quant_rows_kernel(QuantArgs a) {
   const int64_t b = t - o * a.nb_out;
   float v[32];
   bool bad = false;
-  const int64_t bt = o / a.out_rows;
-  const int64_t r = o - bt * a.out_rows;
+  const int64_t w = o / a.out_rows;
+  const int64_t r = o - w * a.out_rows;
   const int64_t c0 = b * 32;
   const bool row_ok = r < a.rows;
-  const uint16_t* src = a.x + (bt * a.rows + r) * a.cols + c0;
+  const uint16_t* src = slab_input(a, w) + r * a.x_sr + c0;
   if (VEC && row_ok && c0 + 32 <= a.cols) {
     const uint4* s4 = reinterpret_cast<const uint4*>(src);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       uint4 q = s4[i];
-      uint32_t w[4] = {q.x, q.y, q.z, q.w};
+      uint32_t wq[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        uint32_t lo = w[k] & 0xFFFF, hi = w[k] >> 16;
+        uint32_t lo = wq[k] & 0xFFFF, hi = wq[k] >> 16;
         bad |= ((lo & 0x7F80) == 0x7F80) | ((hi & 0x7F80) == 0x7F80);
         v[8 * i + 2 * k] = bf16_bits_to_float(lo) * a.mult;
         v[8 * i + 2 * k + 1] = bf16_bits_to_float(hi) * a.mult;
@@ -117,7 +118,8 @@ __global__ void __launch_bounds__(256) mx_quant_rows_kernel(QuantArgs a) {
       v[j] = bf16_bits_to_float(bits) * a.mult;
     }
   }
-  quantize_block<F>(a, v, bad, o, b);
+  const int f = (FSET & (FSET - 1)) ? a.fmt[w % a.nh] : 0;
+  with_format<FSET>(f, [&](auto F) { quantize_block<decltype(F)::value>(a, v, bad, w, r, b); });
 }
 
 // Columns mode: blocks run along the row axis and the output is transposed.
@@ -125,19 +127,19 @@ __global__ void __launch_bounds__(256) mx_quant_rows_kernel(QuantArgs a) {
 // LDS with 16-byte loads (a row segment of 64 bytes per input row), then
 // thread (column c = t % 32, block kb = t / 32) quantises the 32 rows of
 // block kb in its column.  Row tiles run fastest in the grid: with 128 row
-// tiles per batch entry (or any multiple of 8), the workgroup that reads the
-// other half of a row's 128-byte lines runs on the same XCD and finds them
-// in its L2.  Measured slower: column blocks fastest (the halves spread over
-// XCDs, +25 %), and 128 x 64 tiles of whole lines on 256 threads (+4 %).
+// tiles per slab (or any multiple of 8), the workgroup that reads the other
+// half of a row's 128-byte lines runs on the same XCD and finds them in its
+// L2.  Measured slower: column blocks fastest (the halves spread over XCDs,
+// +25 %), and 128 x 64 tiles of whole lines on 256 threads (+4 %).
 constexpr int QC_ROWS = 128, QC_COLS = 32;
-template <int F, bool VEC>
+template <int FSET, bool VEC>
 __global__ void __launch_bounds__(128) mx_quant_cols_kernel(QuantArgs a) {
   __shared__ __align__(16) uint16_t tile[QC_ROWS][QC_COLS];
   const int t = threadIdx.x;
-  const int64_t bt = a.batch0 + blockIdx.z;
+  const int64_t w = a.batch0 + blockIdx.z;
   const int64_t col0 = (int64_t)blockIdx.y * QC_COLS;
   const int64_t row0 = (int64_t)blockIdx.x * QC_ROWS;
-  const uint16_t* src = a.x + bt * a.rows * a.cols;
+  const uint16_t* src = slab_input(a, w);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = t + 128 * i;               // 16-byte chunk: row c/4, part c%4
@@ -146,12 +148,12 @@ __global__ void __launch_bounds__(128) mx_quant_cols_kernel(QuantArgs a) {
     uint4 q = make_uint4(0, 0, 0, 0);
     if (VEC) {
       if (gr < a.rows && gc + 8 <= a.cols)
-        q = *reinterpret_cast<const uint4*>(src + gr * a.cols + gc);
+        q = *reinterpret_cast<const uint4*>(src + gr * a.x_sr + gc);
     } else if (gr < a.rows) {
-      uint32_t h[8];
+      uint32_t hq[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) h[e] = gc + e < a.cols ? src[gr * a.cols + gc + e] : 0u;
-      q = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+      for (int e = 0; e < 8; ++e) hq[e] = gc + e < a.cols ? src[gr * a.x_sr + gc + e] : 0u;
+      q = make_uint4(hq[0] | (hq[1] << 16), hq[2] | (hq[3] << 16), hq[4] | (hq[5] << 16), hq[6] | (hq[7] << 16));
     }
     *reinterpret_cast<uint4*>(&tile[row][part * 8]) = q;
   }
@@ -168,21 +170,24 @@ __global__ void __launch_bounds__(128) mx_quant_cols_kernel(QuantArgs a) {
     bad |= (bits & 0x7F80) == 0x7F80;
     v[j] = bf16_bits_to_float(bits) * a.mult;
   }
-  quantize_block<F>(a, v, bad, bt * a.out_rows + col, b);
+  const int f = (FSET & (FSET - 1)) ? a.fmt[w % a.nh] : 0;
+  with_format<FSET>(f, [&](auto F) { quantize_block<decltype(F)::value>(a, v, bad, w, col, b); });
 }
 
-template <int F>
-static hipError_t launch_quant_fmt(const QuantArgs& a, int mode, hipStream_t stream) {
-  const bool aligned = (reinterpret_cast<uintptr_t>(a.x) & 15) == 0;
+template <int FSET>
+static hipError_t launch_quant_set(const QuantArgs& a, int mode, hipStream_t stream) {
+  // 16-byte loads need every row start 16-byte aligned
+  const bool aligned = (reinterpret_cast<uintptr_t>(a.x) & 15) == 0 && a.x_sr % 8 == 0 &&
+                       a.x_sh % 8 == 0 && a.x_sb % 8 == 0;
   if (mode == 0) {
     const int64_t total = a.batch * a.out_rows * a.nb_out;
     const int64_t grid = (total + 255) / 256;
     if (a.cols % 32 == 0 && aligned)
-      hipLaunchKernelGGL((mx_quant_rows_kernel<F, true>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((mx_quant_rows_kernel<FSET, true>), dim3((unsigned)grid), dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL((mx_quant_rows_kernel<F, false>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((mx_quant_rows_kernel<FSET, false>), dim3((unsigned)grid), dim3(256), 0, stream, a);
   } else {
-    // batch entries go in grid.z, in launches of at most 65535
+    // slabs go in grid.z, in launches of at most 65535
     for (int64_t b0 = 0; b0 < a.batch; b0 += 65535) {
       QuantArgs c = a;
       c.batch0 = b0;
@@ -190,18 +195,21 @@ static hipError_t launch_quant_fmt(const QuantArgs& a, int mode, hipStream_t str
       const dim3 grid((unsigned)((a.nb_out + QC_ROWS / 32 - 1) / (QC_ROWS / 32)),
                       (unsigned)((a.cols + QC_COLS - 1) / QC_COLS), (unsigned)nb);
       if (a.cols % 8 == 0 && aligned)
-        hipLaunchKernelGGL((mx_quant_cols_kernel<F, true>), grid, dim3(128), 0, stream, c);
+        hipLaunchKernelGGL((mx_quant_cols_kernel<FSET, true>), grid, dim3(128), 0, stream, c);
       else
-        hipLaunchKernelGGL((mx_quant_cols_kernel<F, false>), grid, dim3(128), 0, stream, c);
+        hipLaunchKernelGGL((mx_quant_cols_kernel<FSET, false>), grid, dim3(128), 0, stream, c);
     }
   }
   return hipGetLastError();
 }
 
-hipError_t launch_mx_quant(const QuantArgs& a, int fmt, int mode, hipStream_t stream) {
-  if (fmt == FMT_E4M3) return launch_quant_fmt<FMT_E4M3>(a, mode, stream);
-  if (fmt == FMT_E2M3) return launch_quant_fmt<FMT_E2M3>(a, mode, stream);
-  return launch_quant_fmt<FMT_E2M1>(a, mode, stream);
+hipError_t launch_mx_quant(const QuantArgs& a, int fset, int mode, hipStream_t stream) {
+  switch (fset) {
+    case 1 << FMT_E4M3: return launch_quant_set<1 << FMT_E4M3>(a, mode, stream);
+    case 1 << FMT_E2M3: return launch_quant_set<1 << FMT_E2M3>(a, mode, stream);
+    case 1 << FMT_E2M1: return launch_quant_set<1 << FMT_E2M1>(a, mode, stream);
+    default: return launch_quant_set<7>(a, mode, stream);
+  }
 }
 
 }  // namespace fsa

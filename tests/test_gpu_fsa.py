@@ -213,3 +213,31 @@ def test_hybrid_heads_two_batches():
     q, k, v = (W.random_bf16((2, 4, S, D), seed, 1.1) for seed in (41, 42, 43))
     g, kap, mg = _run(q, k, v, "e2m3", False, head_fmt=fmts)
     _check(g, kap, mg, *_oracle_heads(q, k, v, fmts, False))
+
+
+@pytest.mark.parametrize("fmts", [["e2m3", "e2m1", "e2m1", "e2m3", "e2m1", "e2m3"],
+                                  ["e2m3", "e4m3", "e2m1", "e4m3", "e2m1", "e2m3"]],
+                         ids=["fp6-fp4", "all-three"])
+def test_hybrid_one_launch_strided(fmts):
+    """Interleaved per-head formats in one launch, B = 2, over strided views:
+    q, k and v stored [B, S, H, D] and read through [B, H, S, D] views, the
+    output written into such a view too.  Every head must equal both the
+    oracle and the same head computed alone in its format, contiguously
+    (bit for bit: the same kernel body)."""
+    import torch
+    import softmax_mx_quantize_amd as fsa
+    announce("fsa hybrid one launch strided", fmts)
+    B, H, S, D = 2, len(fmts), 300, 128
+    q, k, v = (W.random_bf16((B, H, S, D), seed, 1.2) for seed in (71, 72, 73))
+    bshd = lambda x: to_dev(np.ascontiguousarray(x.transpose(0, 2, 1, 3))).transpose(1, 2)
+    dq, dk, dv = bshd(q), bshd(k), bshd(v)
+    assert not dq.is_contiguous()
+    out = torch.empty((B, S, H, D), dtype=torch.bfloat16, device="cuda").transpose(1, 2)
+    o, kap, mg = fsa.attention_fwd(dq, dk, dv, fmts[0], False, head_fmt=fmts, out=out, return_rows=True)
+    torch.cuda.synchronize()
+    g = from_dev_bf16(o.contiguous())
+    _check(g, kap.cpu().numpy(), mg.cpu().numpy(), *_oracle_heads(q, k, v, fmts, False))
+    for f in sorted(set(fmts)):
+        alone = from_dev_bf16(fsa.attention_fwd(to_dev(q), to_dev(k), to_dev(v), f, False))
+        heads = [h for h in range(H) if fmts[h] == f]
+        assert np.array_equal(g[:, heads], alone[:, heads]), f
