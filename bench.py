@@ -7,8 +7,10 @@ of Q, K, V plus the fused attention kernel, inputs resident in HBM.  The same
 inputs are also timed with E2M3 and E2M1 operands and through the BF16
 flash-attention baseline, and under causal masking; the outlier workload
 (MXFP4, S=32768, planted +8 sigma scores) and the long hybrid FP6/FP4
-schedule (S=75600) are timed as well ("workloads" in the JSON line).  FLOPs
-are 4*B*H*S^2*D (halved for causal).
+schedule (S=75600) are timed as well ("workloads" in the JSON line), and the
+P~ variants of fsa_options.p_variant on the Video-DiT tensors ("variants";
+an E4M3 P~ over FP6/FP4 operands is rated against the MXFP8 peak, since half
+its products run at FP8 width).  FLOPs are 4*B*H*S^2*D (halved for causal).
 
 Prints ONE JSON line.  Options:
   --gpus N        only 1 is supported (the path is a single-GPU kernel)
@@ -286,6 +288,21 @@ def main() -> int:
         for fmt in fmts:
             per[fmt]["speedup_vs_bf16"] = bms / per[fmt]["ms_per_step"]
 
+    # the P~ variants on the same inputs (kernel time: quantisation excluded)
+    variants = {}
+    if not args.only and not args.no_extra:
+        for vname, fmt in (("row", "e4m3"), ("e4m3", "e2m3"), ("e4m3", "e2m1"), ("affine", "e2m1"),
+                           ("exact_exp", "e4m3"), ("exact_exp", "e2m3"), ("exact_exp", "e2m1")):
+            print("[bench] timing variant %s over %s" % (vname, fmt), file=sys.stderr, flush=True)
+            wall_ms, kern_ms, _ = time_fsa(fsa, torch, q, k, v, fmt, args.steps, args.warmup,
+                                           p_variant=vname)
+            # peak of the narrower of the two product formats the variant runs
+            peak = PEAK_TFLOPS["e4m3" if (fmt == "e4m3" or vname == "e4m3") else fmt]
+            variants["%s-%s" % (vname, fmt)] = {
+                "ms_per_step": wall_ms, "tflops": flops / (wall_ms * 1e-3) / 1e12,
+                "kernel_ms": kern_ms, "kernel_tflops": flops / (kern_ms * 1e-3) / 1e12,
+                "kernel_frac_of_peak": flops / (kern_ms * 1e-3) / 1e12 / peak, "peak_tflops": peak}
+
     # the other workloads of the method: planted outliers (fallbacks),
     # the long hybrid FP6/FP4 schedule, and causal masking
     extra = {}
@@ -335,6 +352,7 @@ def main() -> int:
         "formats": per,
         "bf16_baseline": bf16,
         "workloads": extra,
+        "variants": variants,
     }
     if not args.no_cpu:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)

@@ -127,6 +127,33 @@ int fsa_attention_fwd(const void* q, const void* k, const void* v, void* out,
 int fsa_attention_bf16_ref(const void* q, const void* k, const void* v, void* out,
                            int B, int H, int S, int D, int causal, void* stream);
 
+/* Variants of the quantised probabilities P~ (fsa_options.p_variant).  The
+ * pages leave the exponential's approximation and the MX quantisation of P
+ * open ("Moving softmax to matrix operations speeds up AI inference by over
+ * 2x", "Read it as" and the "How it works" figure); the exact definitions
+ * are the oracle's.
+ *   FSA_P_BLOCK      bit-pattern exponential, each 32-key block of P~ shifted
+ *                    to its own E8M0 scale (the default);
+ *   FSA_P_ROW_SCALE  one scale for the whole row (every head E4M3); a value
+ *                    past 448 sends its row to the fallback pass;
+ *   FSA_P_E4M3       E4M3 P~ over FP6/FP4 Q, K, V (every head E2M3 or
+ *                    E2M1), through the mixed-width scaled product;
+ *   FSA_P_AFFINE     E2M1 codes from one affine rule of the score in the
+ *                    code domain, with an exponent-only block scale from the
+ *                    block's maximum ("EFQ-Softmax: Exp-Free Quantization
+ *                    for Softmax", abstract; every head E2M1);
+ *   FSA_P_EXACT_EXP  the vector unit's exp2 in place of the bit pattern:
+ *                    P~ is 2^x itself rounded onto the element grid (the
+ *                    rounding thresholds of the exact map).
+ * A variant whose format condition fails gives FSA_ERR_UNSUPPORTED. */
+typedef enum fsa_p_variant {
+  FSA_P_BLOCK = 0,
+  FSA_P_ROW_SCALE = 1,
+  FSA_P_E4M3 = 2,
+  FSA_P_AFFINE = 3,
+  FSA_P_EXACT_EXP = 4
+} fsa_p_variant;
+
 /* Element strides of strided views: for each tensor, the strides of the
  * batch, head and row indices (element (b, h, s, d) at b*st[0] + h*st[1] +
  * s*st[2] + d).  D is contiguous; each stride a multiple of 8 (16-byte
@@ -162,6 +189,8 @@ typedef struct fsa_options {
   /* Optional strides of q, k, v and out (strided views); NULL: contiguous
    * [B][H][S][D].  Bad strides give FSA_ERR_INVALID_ARG. */
   const fsa_layout* layout;
+  /* fsa_p_variant of P~ (0: the default). */
+  int p_variant;
 } fsa_options;
 
 /* fsa_attention_fwd with hooks; opt may be NULL.  Same errors. */

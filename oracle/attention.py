@@ -202,41 +202,102 @@ def placement_exponent(fmt) -> int:
     return f.emax - 1 if f.name == "e4m3" else f.emax
 
 
-def block_binades(t: np.ndarray, vis: np.ndarray, fmt) -> np.ndarray:
+def block_binades(t: np.ndarray, vis: np.ndarray, fmt, exact: bool = False) -> np.ndarray:
     """e_b of step 5 for rows of guess-relative scores t [R, S]: the binade of
     each 32-key block's largest visible value after rounding to M mantissa
-    bits (half to even).  Blocks with no visible key give -inf."""
+    bits (half to even).  Blocks with no visible key give -inf.  The value
+    is the bit-pattern exponential's (its mantissa is frac(t), so the
+    rounding is that of 2^M t), or with ``exact`` the exact 2^t's."""
     f = _fmt(fmt)
     R, S = t.shape
     nb = (S + BLOCK - 1) // BLOCK
     tp = np.full((R, nb * BLOCK), -np.inf)
     tp[:, :S] = np.where(vis, t, -np.inf)
     g = tp.reshape(R, nb, BLOCK).max(axis=2)
-    with np.errstate(invalid="ignore"):
+    with np.errstate(invalid="ignore", over="ignore"):
+        if exact:
+            fin = np.isfinite(g)
+            e0 = np.floor(np.where(fin, g, 0.0))
+            mant = np.exp2(np.where(fin, g, 0.0) - e0)          # 2^frac(t) in [1, 2)
+            up = np.rint(mant * 2 ** f.mbits) >= 2 ** (f.mbits + 1)
+            return np.where(fin, e0 + up, -np.inf)
         c = np.rint((2 ** f.mbits) * g)            # np.rint: half to even
     return np.floor(c / (2 ** f.mbits))
 
 
+P_MODES = ("block", "row", "efq", "exp")
+
+
+def overflow_threshold(fmt) -> float:
+    """Smallest value that rounds beyond the format's largest finite element
+    (the midpoint to the next grid point): 464 for E4M3."""
+    f = _fmt(fmt)
+    top = f.max_value
+    return top + math.ldexp(1.0, int(math.floor(math.log2(top))) - f.mbits - 1)
+
+
 def fused_probabilities(s: np.ndarray, m_tilde: np.ndarray, vis: np.ndarray,
-                        fmt) -> Dict[str, np.ndarray]:
+                        fmt, mode: str = "block") -> Dict[str, np.ndarray]:
     """Steps 4-6 of the module doc for rows of log2-domain scores ``s`` [R, S].
+
+    ``fmt`` is the element format of P~.  ``mode`` picks the P~ variant:
+
+    * "block" (step 5): each 32-key block shifted to the placement binade.
+    * "row": one scale for the whole row, Delta = 0 in every block (E4M3
+      only: its 17 binades leave no block of a softmax row needing a shift
+      of its own).  A row falls back only when its largest value,
+      mitchell_exp2(t_max + pl), reaches the format's overflow threshold
+      (464 for E4M3: it would round beyond 448); it is then recomputed with
+      kappa = max_b e_b whole binades.  Otherwise kappa = 0.
+    * "efq" (E2M1 only): the codes come from a single affine rule in the
+      code domain (EFQ-Softmax: Exp-Free Quantization for Softmax, abstract:
+      an exponent-only block scale from the local maximum, then nonnegative
+      E2M1 codes by one affine map of the shifted score).  With x as in
+      step 5, code = clamp(round_half_even(2 x + 2), 0, 7): for values of
+      1 and above this is the element the bit-pattern map rounds to; below,
+      codes follow the line (x in [-0.75, -0.25) gives 0.5, lower gives 0).
+    * "exp": as "block", with the exact exponential 2**x in place of the
+      bit-pattern one, i.e. the rounding thresholds of the exact map (the
+      threshold-corrected variant); a block's binade is then that of its
+      largest exact value once rounded.
 
     Returns the P~ values (float64), the element codes, the per-block shifts
     Delta, the E8M0 scale bytes of P~, the per-row binade offset kappa
     (> 0 for rows that fell back) and the guess-relative block binades e_b.
     """
     f = _fmt(fmt)
+    if mode not in P_MODES:
+        raise ValueError("unknown P~ mode " + repr(mode))
+    if mode == "row" and f.name != "e4m3":
+        raise ValueError("the one-scale-per-row P~ is defined for E4M3")
+    if mode == "efq" and f.name != "e2m1":
+        raise ValueError("the affine-rule P~ is defined for E2M1")
     pl = placement_exponent(f)
     cap = 127 - pl
     R, S = s.shape
     t = np.asarray(s, np.float64) - np.asarray(m_tilde, np.float64)[:, None]
-    e = block_binades(t, vis, f)
-    kappa = np.maximum(0.0, np.max(e, axis=1)) if e.size else np.zeros(R)
-    delta = np.where(np.isfinite(e), np.minimum(kappa[:, None] - e, cap), cap)
+    e = block_binades(t, vis, f, exact=(mode == "exp"))
+    emax = np.max(e, axis=1) if e.size else np.full(R, -np.inf)
+    if mode == "row":
+        tmax = np.where(vis, t, -np.inf).max(axis=1) if S else np.full(R, -np.inf)
+        over = mitchell_exp2(tmax + pl) >= overflow_threshold(f)
+        kappa = np.where(over, emax, 0.0)
+        delta = np.zeros_like(e)
+    else:
+        kappa = np.maximum(0.0, emax)
+        delta = np.where(np.isfinite(e), np.minimum(kappa[:, None] - e, cap), cap)
     delta_full = np.repeat(delta, BLOCK, axis=1)[:, :S]
     x = np.where(vis, t - kappa[:, None] + pl + delta_full, -np.inf)
-    vals = round_to_format(mitchell_exp2(x), f)
-    code = encode_values(vals, f).astype(np.int64)
+    if mode == "efq":
+        with np.errstate(invalid="ignore"):
+            c = np.rint(2.0 ** f.mbits * (x + f.bias))
+        code = np.clip(np.where(np.isfinite(c), c, 0.0), 0, f.max_code).astype(np.int64)
+        vals = decode(code, f)
+    else:
+        with np.errstate(over="ignore"):
+            p = np.exp2(x) if mode == "exp" else mitchell_exp2(x)
+        vals = round_to_format(p, f)
+        code = encode_values(vals, f).astype(np.int64)
     P = vals * np.ldexp(1.0, (-pl - delta_full).astype(np.int32))
     return {
         "P": P,
@@ -249,15 +310,19 @@ def fused_probabilities(s: np.ndarray, m_tilde: np.ndarray, vis: np.ndarray,
 
 
 def fused_attention(q, k, v, fmt, causal: bool = False, rows=None, bias: float = 0.0,
-                    return_info: bool = False):
+                    return_info: bool = False, p_fmt=None, p_mode: str = "block"):
     """Fused-Softmax attention output (bf16 values as float64) for one head.
 
     ``q, k, v`` are [S, D] arrays of bf16 values; ``rows`` selects query rows
-    (all by default); ``bias`` is added to the frozen max (binades).  With
+    (all by default); ``bias`` is added to the frozen max (binades).  ``fmt``
+    is the element format of q'^, k^ and v^; ``p_fmt`` that of P~ (the same
+    by default; E4M3 P~ over FP6/FP4 operands is the mixed variant) and
+    ``p_mode`` its variant (see ``fused_probabilities``).  With
     ``return_info`` also returns the frozen max, the fallback offsets, the
     log2-domain scores, the P~ values, the dequantised v^ and the visibility.
     """
     f = _fmt(fmt)
+    pf = f if p_fmt is None else _fmt(p_fmt)
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -267,7 +332,7 @@ def fused_attention(q, k, v, fmt, causal: bool = False, rows=None, bias: float =
     s = qh @ kh.T
     vis = _visible(rows, S, causal)
     m_tilde = frozen_max(s, vis, bias)
-    fp = fused_probabilities(s, m_tilde, vis, f)
+    fp = fused_probabilities(s, m_tilde, vis, pf, p_mode)
     P = fp["P"]
     O = P @ vh
     l = P.sum(axis=1)
@@ -293,17 +358,19 @@ def plain_probabilities(s: np.ndarray, vis: np.ndarray, fmt) -> np.ndarray:
 
 
 def plain_mx_attention(q, k, v, fmt, causal: bool = False, rows=None,
-                       return_info: bool = False):
+                       return_info: bool = False, p_fmt=None):
     """Exp-then-quantize attention (bf16 values as float64) for one head.
 
     The same MX operands as ``fused_attention`` (q'^ of step 1, k^, v^), so
     the same log2-domain scores s; exact row max and exact exponential in
     float64, P = 2**(s - max s) = exp((q'.k - max) ...) in the softmax scale;
     P MX-quantised along the keys (``plain_probabilities``);
-    out = bf16(sum P^ v^ / sum P^).  With ``return_info`` also returns the
+    out = bf16(sum P^ v^ / sum P^).  ``p_fmt`` is the format of P^ (that of
+    the operands by default).  With ``return_info`` also returns the
     dequantised P^ and the scores.
     """
     f = _fmt(fmt)
+    pf = f if p_fmt is None else _fmt(p_fmt)
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -312,7 +379,7 @@ def plain_mx_attention(q, k, v, fmt, causal: bool = False, rows=None,
     qh, kh, vh = quantized_operands(q[rows], k, v, f)
     s = qh @ kh.T
     vis = _visible(rows, S, causal)
-    Pq = plain_probabilities(s, vis, f)
+    Pq = plain_probabilities(s, vis, pf)
     O = Pq @ vh
     l = Pq.sum(axis=1)
     out = bf16_round(O / l[:, None])

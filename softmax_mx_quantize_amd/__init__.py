@@ -45,7 +45,12 @@ class Options(ctypes.Structure):
         ("event_after_quantize", ctypes.c_void_p),
         ("head_fmt", ctypes.POINTER(ctypes.c_int)),
         ("layout", ctypes.POINTER(Layout)),
+        ("p_variant", ctypes.c_int),
     ]
+
+
+# fsa_p_variant
+P_VARIANT = {"block": 0, "row": 1, "e4m3": 2, "affine": 3, "exact_exp": 4}
 
 
 def _load() -> ctypes.CDLL:
@@ -157,14 +162,15 @@ def quantize_mx(x, fmt: Union[str, int], block_along_rows: bool = False):
 def attention_fwd(q, k, v, fmt: Union[str, int] = "e4m3", causal: bool = False, *,
                   guess_bias: float = 0.0, head_fmt: Optional[Sequence[Union[str, int]]] = None,
                   return_rows: bool = False, event_after_quantize=None, out=None,
-                  no_alloc: bool = False):
+                  no_alloc: bool = False, p_variant: Union[str, int] = "block"):
     """Fused-softmax attention; q, k, v bf16 [B, H, S, D] CUDA tensors
     (strided views with contiguous rows are passed with their strides).
 
     With ``return_rows`` also returns the per-row fallback offsets (int32)
     and frozen maxima (float32), each [B, H, S].  ``no_alloc`` calls
     ``fsa_attention_fwd_noalloc`` (the library allocates nothing; the
-    tensors here are still torch's).
+    tensors here are still torch's).  ``p_variant`` picks the P~ variant
+    (``fsa_p_variant``: "block", "row", "e4m3", "affine", "exact_exp").
     """
     import torch
     _bf16_rows(q, k, v)
@@ -176,6 +182,7 @@ def attention_fwd(q, k, v, fmt: Union[str, int] = "e4m3", causal: bool = False, 
     out = _out_like(out, q)
     opt = Options()
     opt.guess_bias = float(guess_bias)
+    opt.p_variant = P_VARIANT[p_variant] if isinstance(p_variant, str) else int(p_variant)
     kappa = mg = None
     if return_rows:
         kappa = torch.empty((B, H, S), dtype=torch.int32, device=q.device)

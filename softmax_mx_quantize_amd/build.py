@@ -20,12 +20,14 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.environ.get("FSA_BUILD_DIR") or os.path.join(PKG, "_build")
 LIB = os.environ.get("FSA_LIB_OUT") or os.path.join(PKG, "libfsa.so")
 
-SOURCES = ["fsa_api.cpp", "mx_quant.hip", "fsa_fwd.hip", "bf16_fa.hip"]
+SOURCES = ["fsa_api.cpp", "mx_quant.hip", "fsa_fwd.hip", "fsa_fwd_var.hip", "fsa_fwd_exp.hip",
+           "bf16_fa.hip"]
 
 # Per-source options.  The fused kernel runs two waves per SIMD and consumes
 # the score MFMA results on the vector units; asking for the VGPR form of
 # every MFMA keeps them out of AGPRs (no accvgpr moves in the loop).
-SOURCE_FLAGS = {"fsa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+SOURCE_FLAGS = {n: ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+                for n in ("fsa_fwd.hip", "fsa_fwd_var.hip", "fsa_fwd_exp.hip")}
 
 # Packed fp32 VALU instructions are disabled on purpose (the target feature is
 # switched off for the device pass; the host pass ignores it with a warning).
@@ -60,7 +62,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     # -z defs: an unresolved symbol (e.g. a kernel template that was never

@@ -141,6 +141,7 @@ struct Piece {
 };
 
 struct Call {
+  int pm = 0, px = 0;              // P~ variant (PM_*) and E4M3 P~ over FP6/FP4
   const uint16_t *q, *k, *v;
   uint16_t* out;
   int B, H, S, D, causal;
@@ -210,6 +211,7 @@ int quantize_piece(const Call& c, const Piece& p, uint8_t* base, const PieceLayo
   a.nb_out = c.D / 32;
   a.code_slab = l.kc_slab;
   a.scale_layout = fsa::SCALES_KEY_TILES;
+  a.key8 = c.px;
   if (fsa::launch_mx_quant(a, fset, 0, c.stream) != hipSuccess) return FSA_ERR_HIP;
   // V: output rows are the D columns, blocks along the keys
   a.x = c.v + p.b0 * c.st.v[0] + p.h0 * c.st.v[1];
@@ -220,6 +222,7 @@ int quantize_piece(const Call& c, const Piece& p, uint8_t* base, const PieceLayo
   a.nb_out = c.sk_alloc / 32;
   a.code_slab = l.vc_slab;
   a.scale_layout = fsa::SCALES_DIM_TILES;
+  a.key8 = 0;
   if (fsa::launch_mx_quant(a, fset, 1, c.stream) != hipSuccess) return FSA_ERR_HIP;
   return FSA_OK;
 }
@@ -282,8 +285,9 @@ int attend_piece(const Call& c, const Piece& p, uint8_t* base, const PieceLayout
       a.horder[slot++] = (uint8_t)by_fmt[best][at[best]++];
     }
   }
-  return fsa::launch_fsa_fwd(a, piece_fset(c, p), c.D, c.causal, c.stream) == hipSuccess ? FSA_OK
-                                                                                          : FSA_ERR_HIP;
+  return fsa::launch_fsa_fwd(a, piece_fset(c, p), c.pm, c.px, c.D, c.causal, c.stream) == hipSuccess
+             ? FSA_OK
+             : FSA_ERR_HIP;
 }
 
 int record_event(const Call& c) {
@@ -370,6 +374,35 @@ int attention(const void* q, const void* k, const void* v, void* out, int B, int
     return FSA_ERR_INVALID_ARG;
   c.fmt.assign(H, fmt);
   if (head_fmt) c.fmt.assign(head_fmt, head_fmt + H);
+  // the P~ variant and the formats it needs
+  const int pv = opt ? opt->p_variant : FSA_P_BLOCK;
+  auto all_fmt = [&](std::initializer_list<int> ok) {
+    for (int f : c.fmt)
+      if (std::find(ok.begin(), ok.end(), f) == ok.end()) return false;
+    return true;
+  };
+  switch (pv) {
+    case FSA_P_BLOCK: break;
+    case FSA_P_ROW_SCALE:
+      if (!all_fmt({FSA_MXFP8_E4M3})) return FSA_ERR_UNSUPPORTED;
+      c.pm = 1;
+      break;
+    case FSA_P_E4M3:
+      if (!all_fmt({FSA_MXFP6_E2M3, FSA_MXFP4_E2M1})) return FSA_ERR_UNSUPPORTED;
+      c.px = 1;
+      break;
+    case FSA_P_AFFINE:
+      if (!all_fmt({FSA_MXFP4_E2M1})) return FSA_ERR_UNSUPPORTED;
+      c.pm = 2;
+      break;
+    case FSA_P_EXACT_EXP:
+      // built for single formats and the FP6/FP4 hybrid
+      if (!all_fmt({FSA_MXFP8_E4M3}) && !all_fmt({FSA_MXFP6_E2M3, FSA_MXFP4_E2M1}))
+        return FSA_ERR_UNSUPPORTED;
+      c.pm = 3;
+      break;
+    default: return FSA_ERR_INVALID_ARG;
+  }
 
   if (!no_alloc) {
     // every batch entry and up to MAX_HEAD_TABLE heads per piece, side by

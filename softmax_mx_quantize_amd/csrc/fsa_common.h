@@ -40,10 +40,18 @@ namespace fsa {
 __device__ v4f mfma_scale_v4(v4i a, v4i b, v4f c, int cbsz, int blgp, int opsel_a, int sa,
                              int opsel_b, int sb)
     __asm("llvm.amdgcn.mfma.scale.f32.16x16x128.f8f6f4.v4i32.v4i32");
-// Mixed widths: an FP4 A operand with an FP8 or FP6 B operand.
+// Mixed widths: an FP4 A operand with an FP6 B operand.
 __device__ v4f mfma_scale_v4_v6(v4i a, v6i b, v4f c, int cbsz, int blgp, int opsel_a, int sa,
                                 int opsel_b, int sb)
     __asm("llvm.amdgcn.mfma.scale.f32.16x16x128.f8f6f4.v4i32.v6i32");
+
+// P~ variants (the epilogue's modes).  BLOCK: each 32-key block shifted to
+// the placement binade (the default).  ROW: one scale per row (E4M3).  EFQ:
+// codes by one affine rule in the code domain (E2M1; EFQ-Softmax:
+// Exp-Free Quantization for Softmax, abstract).  EXP: the exact exponential
+// (the vector unit's exp2) in place of the bit pattern, i.e. P~ rounded from
+// 2^x itself: the rounding thresholds of the exact map.
+enum { PM_BLOCK = 0, PM_ROW = 1, PM_EFQ = 2, PM_EXP = 3 };
 
 namespace {
 
@@ -174,8 +182,9 @@ __device__ __forceinline__ int p_scale(int s_lo, int s_hi, int g) {
 // NaN/Inf blocks get scale 0xFF and zero codes) with Q' = fp32(q * mult).
 // `row` is null for padding rows.  Returns the codes in operand order and
 // sets `sc` to the E8M0 byte of the block this lane group scales, raised by
-// 23 (2^23 rides on Q's scale; 255 stays NaN).
-template <int F, int D>
+// RAISE (2^23 rides on Q's scale for the bit-pattern exponential; 255 stays
+// NaN).
+template <int F, int D, int RAISE>
 __device__ __forceinline__ opv<F> q_operand(const uint16_t* row, float mult, int g, int& sc) {
   constexpr int BITS = Fmt<F>::bits;
   float v[32];
@@ -227,7 +236,7 @@ __device__ __forceinline__ opv<F> q_operand(const uint16_t* row, float mult, int
   if (bad_lo) { for (int i = 0; i < 4; ++i) w[i] = 0; }
   if (bad_hi) { for (int i = 4; i < 8; ++i) w[i] = 0; }
   if (BITS != 8 && bad_lo) { for (int i = 0; i < 8; ++i) w[i] = 0; }
-  auto raised = [](int x, bool bad) { return bad ? 255 : min(x + 127 + 23, 254); };
+  auto raised = [](int x, bool bad) { return bad ? 255 : min(x + 127 + RAISE, 254); };
   int s_lo = raised(x_lo, bad_lo), s_hi = raised(x_hi, bad_hi);
   if (BITS == 8 && D < 128) s_hi = 127;                // blocks past D: zeros
   if (BITS != 8 && 32 * g >= D) s_lo = s_hi = 127;

@@ -32,6 +32,7 @@ struct QuantArgs {
   int64_t batch0;        // first slab of this launch (columns mode)
   float mult;            // every input value is multiplied by this (fp32) first
   int scale_layout;      // SCALES_* below
+  int key8;              // KEY_TILES in the FP8 key order whatever the codes (E4M3 P~)
   uint8_t fmt[MAX_HEAD_TABLE];  // element format (FMT_*) of head slot w % nh
 };
 
@@ -104,8 +105,13 @@ struct AttnArgs {
 constexpr int attn_kstage_bytes(int d) { return 128 * 128 + 128 * (d / 32); }
 constexpr int attn_vstage_bytes(int d) { return d * 128 + 4 * d; }
 
-// `fset`: the formats present in a.hfmt[0, hrun), as a bit set (1 << FMT_*).
-hipError_t launch_fsa_fwd(const AttnArgs& a, int fset, int D, int causal, hipStream_t stream);
+// `fset`: the formats present in a.hfmt[0, hrun), as a bit set (1 << FMT_*);
+// `pm` the P~ variant (PM_* of fsa_common.h: 0 block scales, 1 one scale
+// per row, 2 affine E2M1 codes, 3 exact exponential); `px` = 1 for E4M3
+// P~ over FP6/FP4 operands.  hipErrorInvalidValue for a combination that
+// is not built.
+hipError_t launch_fsa_fwd(const AttnArgs& a, int fset, int pm, int px, int D, int causal,
+                          hipStream_t stream);
 
 // The attention kernel's Q' operands written out (a debug view): rows of
 // bf16 Q [rows][D] times qmul, MX-quantised by the very device functions of

@@ -65,7 +65,8 @@ __device__ __forceinline__ void quantize_block(const QuantArgs& a, float (&v)[32
   if (a.scale_layout == SCALES_KEY_TILES) {
     // r = key row, b = block along D; rows per slab are a whole number of
     // 128-key tiles
-    so = w * a.out_rows * nb + (r >> 7) * 128 * nb + key_tile_byte((int)(r & 127), (int)b, 32 * (int)nb, BITS);
+    so = w * a.out_rows * nb + (r >> 7) * 128 * nb +
+         key_tile_byte((int)(r & 127), (int)b, 32 * (int)nb, a.key8 ? 8 : BITS);
   } else if (a.scale_layout == SCALES_DIM_TILES) {
     // r = d, b = key block; blocks per row are a whole number of 4-block tiles
     so = w * a.out_rows * nb + (b >> 2) * 4 * a.out_rows + dim_tile_byte((int)r, (int)(b & 3), (int)a.out_rows);

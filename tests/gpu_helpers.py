@@ -45,7 +45,7 @@ def workload_tensors(w):
     return _TENSOR_CACHE[key]
 
 
-def kappa_borderline(scores, m_tilde, rows, S, causal, mbits, eps=2e-3):
+def kappa_borderline(scores, m_tilde, rows, S, causal, mbits, eps=2e-3, exact=False):
     """Rows whose fallback offset kappa may legitimately differ by one between
     the GPU and the oracle: kappa steps where the row's largest visible
     guess-relative score t_max crosses j - 2^-(M+1) (j >= 1), and the kernel
@@ -54,9 +54,13 @@ def kappa_borderline(scores, m_tilde, rows, S, causal, mbits, eps=2e-3):
     j = np.arange(S)[None, :]
     vis = (j <= np.asarray(rows)[:, None]) if causal else np.ones((len(rows), S), bool)
     t = np.where(vis, scores - np.asarray(m_tilde)[:, None], -np.inf).max(axis=1)
-    half = 2.0 ** -(mbits + 1)
-    jn = np.maximum(1.0, np.rint(t + half))
-    return np.abs(t - (jn - half)) < eps
+    if exact:
+        # the exact value 2^t rounds up a binade at frac(t) = log2(2 - 2^-(M+1))
+        step = 1.0 - np.log2(2.0 - 2.0 ** -(mbits + 1))
+    else:
+        step = 2.0 ** -(mbits + 1)
+    jn = np.maximum(1.0, np.rint(t + step))
+    return np.abs(t - (jn - step)) < eps
 
 
 def check_kappa(gpu_kap, ref_kap, borderline):

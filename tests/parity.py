@@ -33,10 +33,10 @@ def eps_rows(gpu_m_tilde, info):
     return EPS_PLACE + np.abs(np.asarray(gpu_m_tilde, np.float64) - info["m_tilde"])
 
 
-def tie_allowance(info, fmt, out_ref, eps_x):
+def tie_allowance(info, fmt, out_ref, eps_x, mode="block"):
     """Per-row bound on the output change that near-tie codes can cause;
     ``eps_x`` (binades, scalar or per row) bounds how far the kernel's t may
-    sit from the exact one."""
+    sit from the exact one; ``fmt`` and ``mode`` are P~'s format and variant."""
     f = FORMATS[fmt]
     M = f.mbits
     pl = placement_exponent(f)
@@ -46,26 +46,48 @@ def tie_allowance(info, fmt, out_ref, eps_x):
     t = s - m[:, None]
     dfull = np.repeat(delta, 32, axis=1)[:, :S]
     x = np.where(vis, t - kap[:, None] + pl + dfull, -np.inf)
-    p = mitchell_exp2(x)
-    with np.errstate(divide="ignore", invalid="ignore"):
-        e = np.floor(np.log2(np.where(p > 0, p, 1.0)))
-        e = np.maximum(e, 1 - f.bias)                      # subnormal grid below emin
-        q = np.ldexp(1.0, (e - M).astype(np.int64))
-        r = p / q
-        dist = np.abs(r - np.floor(r) - 0.5) * q           # value distance to the tie
-        slope = np.ldexp(1.0, np.floor(np.where(np.isfinite(x), x, 0.0)).astype(np.int64))
     ex = np.broadcast_to(np.asarray(eps_x, np.float64).reshape(-1, 1), (R, 1))
-    near = vis & (p > 0) & (p < f.max_value) & (dist <= slope * ex)
+    if mode == "efq":
+        # ties of the code-domain rounding: 2 x + 2 within 2 eps of k + 1/2
+        with np.errstate(invalid="ignore"):
+            c = 2.0 * x + 2.0
+            lo = np.clip(np.floor(c), 0, f.max_code)
+            near = vis & np.isfinite(c) & (np.abs(c - np.floor(c) - 0.5) <= 2.0 * ex) & (c > 0) & (c < f.max_code)
+        from oracle import decode
+        q = np.where(near, decode(np.minimum(lo + 1, f.max_code).astype(np.int64), f)
+                     - decode(lo.astype(np.int64), f), 0.0)
+    else:
+        with np.errstate(over="ignore"):
+            p = np.exp2(x) if mode == "exp" else mitchell_exp2(x)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            e = np.floor(np.log2(np.where(p > 0, p, 1.0)))
+            e = np.maximum(e, 1 - f.bias)                      # subnormal grid below emin
+            q = np.ldexp(1.0, (e - M).astype(np.int64))
+            r = p / q
+            dist = np.abs(r - np.floor(r) - 0.5) * q           # value distance to the tie
+            if mode == "exp":
+                slope = p * np.log(2.0)
+            else:
+                slope = np.ldexp(1.0, np.floor(np.where(np.isfinite(x), x, 0.0)).astype(np.int64))
+        near = vis & (p > 0) & (p < f.max_value) & (dist <= slope * ex)
     # blocks whose largest value decides its binade within eps_x of a tie
     nb = delta.shape[1]
     tp = np.full((R, nb * 32), -np.inf)
     tp[:, :S] = np.where(vis, t, -np.inf)
     tmax = tp.reshape(R, nb, 32).max(axis=2)
-    with np.errstate(invalid="ignore"):
-        c = (2 ** M) * tmax
-        k = np.rint((c + 0.5) / 2 ** M) * 2 ** M - 0.5
-        tied = np.isfinite(c) & (np.abs(c - k) <= (2 ** M) * ex)
+    with np.errstate(invalid="ignore", over="ignore"):
+        if mode == "exp":
+            # the binade steps where 2^frac(t_max) rounds up to 2: 2^f = 2 - 2^-(M+1)
+            f_up = np.log2(2.0 - 2.0 ** -(M + 1))
+            fr = tmax - np.floor(np.where(np.isfinite(tmax), tmax, 0.0))
+            tied = np.isfinite(tmax) & (np.abs(fr - f_up) <= ex)
+        else:
+            c = (2 ** M) * tmax
+            k = np.rint((c + 0.5) / 2 ** M) * 2 ** M - 0.5
+            tied = np.isfinite(c) & (np.abs(c - k) <= (2 ** M) * ex)
     tied_el = np.repeat(tied, 32, axis=1)[:, :S] & vis
+    if mode == "row":
+        tied_el[:] = False                                # no block shifts
     step = np.where(near, q, 0.0) + np.where(tied_el, 2.0 * q, 0.0)
     step = step * np.ldexp(1.0, (-pl - dfull).astype(np.int64))
     vh = info["v_hat"]
@@ -76,10 +98,10 @@ def tie_allowance(info, fmt, out_ref, eps_x):
     return allow / info["l"]
 
 
-def excess_rel_l2(gpu_rows, ref_rows, info, fmt, eps_x):
+def excess_rel_l2(gpu_rows, ref_rows, info, fmt, eps_x, mode="block"):
     """Relative L2 of the part of the difference that near-tie codes cannot
     explain; also returns the number of rows that got an allowance."""
-    allow = tie_allowance(info, fmt, ref_rows, eps_x)
+    allow = tie_allowance(info, fmt, ref_rows, eps_x, mode)
     d = np.linalg.norm(np.asarray(gpu_rows) - np.asarray(ref_rows), axis=-1)
     ex = np.maximum(0.0, d - allow)
     return float(np.linalg.norm(ex) / np.linalg.norm(ref_rows)), int(np.count_nonzero(allow))

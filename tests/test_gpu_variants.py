@@ -1,0 +1,206 @@
+"""P~ variants (fsa_options.p_variant) on the GPU against the oracle's
+definitions (oracle.attention.fused_probabilities modes):
+
+* "row"       one scale per row, E4M3;
+* "e4m3"      E4M3 P~ over FP6/FP4 operands (mixed-width products);
+* "affine"    E2M1 codes by one affine rule (EFQ-style);
+* "exact_exp" the exact exponential in place of the bit pattern.
+
+Parity bar as for the default map: relative L2 <= 2e-3 beyond what the
+kernel's fp32 exponent placement can move near-tie codes, frozen max to fp32
+rounding, fallback offsets exact outside the borderline rows.  The error
+criterion (fused <= 1.1 x exp-then-quantize against exact attention, per
+head) is asserted for the variants that meet it on the oracle; for "row"
+and "affine" the oracle itself exceeds it on some heads (one E4M3 scale
+flushes the tail of high-gain rows; the affine rule flushes values below
+0.59 of a binade), so their ratios are printed and held to that accuracy.
+"""
+
+import concurrent.futures
+import os
+
+import numpy as np
+import pytest
+
+import workloads as W
+import oracle as O
+from oracle import FORMATS
+from oracle.attention import mitchell_exp2
+from gpu_helpers import (announce, to_dev, from_dev_bf16, rel_l2, workload_tensors, check_kappa,
+                         kappa_borderline)
+from parity import excess_rel_l2, eps_rows
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+# name, operand formats, oracle keywords, P~ format, oracle mode
+VARIANTS = [
+    ("row", "e4m3", dict(p_mode="row"), "e4m3", "row"),
+    ("e4m3", "e2m3", dict(p_fmt="e4m3"), "e4m3", "block"),
+    ("e4m3", "e2m1", dict(p_fmt="e4m3"), "e4m3", "block"),
+    ("affine", "e2m1", dict(p_mode="efq"), "e2m1", "efq"),
+    ("exact_exp", "e4m3", dict(p_mode="exp"), "e4m3", "exp"),
+    ("exact_exp", "e2m3", dict(p_mode="exp"), "e2m3", "exp"),
+    ("exact_exp", "e2m1", dict(p_mode="exp"), "e2m1", "exp"),
+]
+IDS = ["%s-%s" % (v[0], v[1]) for v in VARIANTS]
+
+
+def _run(q, k, v, fmt, variant, causal=False, **kw):
+    import torch
+    import softmax_mx_quantize_amd as fsa
+    out, kap, mg = fsa.attention_fwd(to_dev(q), to_dev(k), to_dev(v), fmt, causal, return_rows=True,
+                                     p_variant=variant, **kw)
+    torch.cuda.synchronize()
+    return from_dev_bf16(out), kap.cpu().numpy(), mg.cpu().numpy()
+
+
+def _borderline(info, rows, S, causal, pfmt, mode, eps=2e-3):
+    """Rows whose kappa may differ by one: near a whole-binade step of the
+    top block (all variants), and for one scale per row also near the
+    overflow threshold that decides whether the row falls back at all."""
+    border = kappa_borderline(info["scores"], info["m_tilde"], rows, S, causal, FORMATS[pfmt].mbits, eps,
+                              exact=(mode == "exp"))
+    if mode == "row":
+        j = np.arange(S)[None, :]
+        vis = (j <= np.asarray(rows)[:, None]) if causal else np.ones((len(rows), S), bool)
+        tmax = np.where(vis, info["scores"] - info["m_tilde"][:, None], -np.inf).max(axis=1)
+        # the score whose Mitchell value at the placement reaches the threshold
+        thr = O.attention.overflow_threshold(pfmt)
+        e = np.floor(np.log2(thr))
+        t_over = e + thr / 2.0 ** e - 1.0 - O.attention.placement_exponent(pfmt)
+        border |= np.abs(tmax - t_over) < eps
+    return border
+
+
+def _check(g, kap, mg, q, k, v, fmt, okw, pfmt, mode, causal=False, rows=None, bias=0.0):
+    B, H, S, D = g.shape
+    num = den = 0.0
+    for b in range(B):
+        for h in range(H):
+            qh, kh, vh = (W.bf16_bits_to_f64(x[b, h]) for x in (q, k, v))
+            ref, info = O.fused_attention(qh, kh, vh, fmt, causal, rows=rows, bias=bias,
+                                          return_info=True, **okw)
+            rws = np.arange(S) if rows is None else np.asarray(rows)
+            gr, kr, mr = g[b, h, rws], kap[b, h, rws], mg[b, h, rws]
+            dm = np.abs(mr - info["m_tilde"])
+            assert np.all(dm <= 1e-4 * np.maximum(1.0, np.abs(info["m_tilde"]))), dm.max()
+            ex, _ = excess_rel_l2(gr, ref, info, pfmt, eps_rows(mr, info), mode)
+            num += (ex * np.linalg.norm(ref)) ** 2
+            den += np.linalg.norm(ref) ** 2
+            check_kappa(kr, info["kappa"], _borderline(info, rws, S, causal, pfmt, mode))
+    err = float(np.sqrt(num / den))
+    print("beyond near-tie codes %.2e" % err)
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=IDS)
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_variant_small_ragged(variant, D, causal):
+    name, fmt, okw, pfmt, mode = variant
+    S = 333
+    announce("variant small", name, fmt, D, causal)
+    q, k, v = (W.random_bf16((2, 2, S, D), seed, 1.3) for seed in (81, 82, 83))
+    g, kap, mg = _run(q, k, v, fmt, name, causal)
+    _check(g, kap, mg, q, k, v, fmt, okw, pfmt, mode, causal)
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=IDS)
+def test_variant_fallbacks(variant):
+    """Every row above its guess: by a few binades (in-sweep shifts, or the
+    re-based pass for one scale per row) and by ~100 binades (re-based)."""
+    name, fmt, okw, pfmt, mode = variant
+    announce("variant fallback", name, fmt)
+    q, k, v = (W.random_bf16((1, 2, 400, 128), seed, 1.0) for seed in (84, 85, 86))
+    for bias in (-8.0, -100.0):
+        g, kap, mg = _run(q, k, v, fmt, name, guess_bias=bias)
+        assert np.all(kap > 0)
+        _check(g, kap, mg, q, k, v, fmt, okw, pfmt, mode, bias=bias)
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=IDS)
+def test_variant_v_ones(variant):
+    import torch
+    name, fmt, okw, pfmt, mode = variant
+    announce("variant v=1", name, fmt)
+    q, k = (W.random_bf16((1, 2, 300, 128), seed, 2.0) for seed in (87, 88))
+    v = W.f32_to_bf16_bits(np.ones((1, 2, 300, 128), np.float32))
+    for causal in (False, True):
+        g, _, _ = _run(q, k, v, fmt, name, causal)
+        assert np.array_equal(g, np.ones_like(g))
+
+
+def test_variant_rejects_unbuilt_formats():
+    import torch
+    import softmax_mx_quantize_amd as fsa
+    q = torch.zeros((1, 2, 64, 128), dtype=torch.bfloat16, device="cuda")
+    for variant, fmt in (("row", "e2m1"), ("affine", "e4m3"), ("e4m3", "e4m3")):
+        with pytest.raises(fsa.FsaError) as e:
+            fsa.attention_fwd(q, q, q, fmt, p_variant=variant)
+        assert e.value.status == -2
+
+
+def _threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except Exception:
+        n = os.cpu_count() or 4
+    return max(1, min(16, n))
+
+
+# full-size variants: Video-DiT tensors, each variant's own formats
+FULL = [("row", "e4m3"), ("e4m3", "e2m3"), ("e4m3", "e2m1"), ("affine", "e2m1"),
+        ("exact_exp", "e4m3"), ("exact_exp", "e2m3"), ("exact_exp", "e2m1")]
+CRIT_MET = {"e4m3", "exact_exp"}
+# variants whose definition misses the 1.1 bar on some heads (host runs of
+# the oracle: up to ~1.4 for one E4M3 scale per row, ~1.5 for the affine
+# E2M1 codes): a looser bound that still catches a broken kernel
+CRIT_ORACLE = {("row", "e4m3"): 2.0, ("affine", "e2m1"): 2.0}
+
+
+@pytest.mark.parametrize("name,fmt", FULL, ids=["%s-%s" % f for f in FULL])
+def test_variant_full_size(name, fmt):
+    """One row of every query tile of two heads against the oracle, then the
+    error criterion on every head (256 rows each)."""
+    import torch
+    import softmax_mx_quantize_amd as fsa
+    variant = [v for v in VARIANTS if v[0] == name and v[1] == fmt][0]
+    _, _, okw, pfmt, mode = variant
+    w = W.WORKLOADS["video_dit_e4m3"]
+    announce("variant full size", name, fmt)
+    q, k, v = workload_tensors(w)
+    out, kap, mg = fsa.attention_fwd(to_dev(q), to_dev(k), to_dev(v), fmt, False, return_rows=True,
+                                     p_variant=name)
+    torch.cuda.synchronize()
+    g = from_dev_bf16(out)
+    kap = kap.cpu().numpy()
+    mg = mg.cpu().numpy()
+    del out
+    n_q = w.S // 128
+    for h in (0, 23):
+        rows = np.arange(n_q) * 128 + (np.arange(n_q) * 37 + h) % 128
+        qh, kh, vh = (W.bf16_bits_to_f64(x[0, h]) for x in (q, k, v))
+        ref, info = O.fused_attention(qh, kh, vh, fmt, False, rows=rows, return_info=True, **okw)
+        ex, n_allow = excess_rel_l2(g[0, h, rows], ref, info, pfmt, eps_rows(mg[0, h, rows], info), mode)
+        print("%s-%s head %d: rel L2 %.2e, beyond near-tie codes %.2e" % (name, fmt, h, rel_l2(g[0, h, rows], ref), ex))
+        assert ex <= TOL, (h, ex)
+        check_kappa(kap[0, h, rows], info["kappa"], _borderline(info, rows, w.S, False, pfmt, mode))
+
+    def errs(h):
+        rows = np.sort(np.random.default_rng([91, h]).choice(w.S, 256, replace=False))
+        qh, kh, vh = (W.bf16_bits_to_f64(x[0, h]) for x in (q, k, v))
+        exa = O.exact_attention(qh, kh, vh, rows=rows)
+        pl = O.plain_mx_attention(qh, kh, vh, fmt, rows=rows, p_fmt=pfmt)
+        return (np.sum((g[0, h, rows] - exa) ** 2, axis=1), np.sum((pl - exa) ** 2, axis=1))
+
+    with concurrent.futures.ThreadPoolExecutor(_threads()) as pool:
+        res = list(pool.map(errs, range(w.H)))
+    ratios = [float(np.sqrt(a.sum() / b.sum())) for a, b in res]
+    pooled = float(np.sqrt(sum(a.sum() for a, _ in res) / sum(b.sum() for _, b in res)))
+    print("%s-%s per-head ratios: %s; pooled %.3f" % (name, fmt, " ".join("%.3f" % r for r in ratios), pooled))
+    if name in CRIT_MET:
+        assert pooled <= 1.1
+        assert max(ratios) <= 1.1 + 0.02, max(ratios)
+    else:
+        assert max(ratios) <= CRIT_ORACLE[(name, fmt)], max(ratios)

@@ -101,31 +101,39 @@ def _nearest(vals_table, a):
     return vals_table[cand[0]] if cand.size == 1 else vals_table[[c for c in cand if c % 2 == 0][0]]
 
 
+@pytest.mark.parametrize("mode", ["block", "exp"])
 @pytest.mark.parametrize("fmt", FMTS)
-def test_probability_map_against_independent_route(fmt):
-    """P~ of single-block rows, recomputed with math.ldexp and brute-force rounding
-    from the exact score differences."""
+def test_probability_map_against_independent_route(fmt, mode):
+    """P~ of single-block rows, recomputed with math.ldexp (bit-pattern
+    exponential) or math.pow (the exact one) and brute-force rounding from
+    the exact score differences."""
     f = FORMATS[fmt]
     rng = np.random.default_rng(17)
     R = 64
     s = rng.normal(0, 4, size=(R, 32))                 # log2-domain scores
     m = (s.max(axis=1) + rng.uniform(0.0, 6.0, R)).astype(np.float32).astype(np.float64)
     vis = np.ones((R, 32), bool)
-    fp = fused_probabilities(s, m, vis, f)
+    fp = fused_probabilities(s, m, vis, f, mode=mode)
+    expo = _mitchell_value if mode == "block" else (lambda x: math.pow(2.0, x))
     table = decode(np.arange(f.max_code + 1), f)
     pl = f.emax - 1 if fmt == "e4m3" else f.emax
     M = f.mbits
     for i in range(R):
         t = s[i] - m[i]
-        # block binade from the largest score, in element codes (half to even)
-        x = (2 ** M) * max(t)
-        code = round(x)                                 # Python rounds half to even
-        e = math.floor(code / 2 ** M)
+        if mode == "block":
+            # block binade from the largest score, in element codes (half to even)
+            x = (2 ** M) * max(t)
+            code = round(x)                             # Python rounds half to even
+            e = math.floor(code / 2 ** M)
+        else:
+            # binade of the largest exact value once its mantissa is rounded
+            mant, ex = math.frexp(2.0 ** max(t))        # 2^t = mant * 2^ex, mant in [0.5, 1)
+            e = ex - 1 + (round(2 * mant * 2 ** M) == 2 ** (M + 1))
         delta = min(-e, 127 - pl)
         assert fp["kappa"][i] == 0
         assert fp["delta"][i, 0] == delta
         for j in range(32):
-            p = _mitchell_value(pl + delta + t[j])
+            p = expo(pl + delta + t[j])
             want = _nearest(table, min(p, f.max_value * 2)) * 2.0 ** (-pl - delta)
             assert fp["P"][i, j] == want, (i, j)
 
@@ -307,3 +315,76 @@ def test_whole_binade_guess_shift_is_exact(fmt):
         assert np.array_equal(sh["codes"], base["codes"])
         assert np.array_equal(sh["P"], base["P"])
         assert np.array_equal(sh["delta"], base["delta"])
+
+
+
+# ---- P~ variants (see fused_probabilities) ----
+
+def test_variant_row_scale_closed_form_and_fallback():
+    """One scale per row: every element is mitchell(t + pl) rounded, with no
+    block shift; a row falls back exactly when its largest value reaches
+    464 (it would round past 448), and then by its top block's binade."""
+    f = FORMATS["e4m3"]
+    table = decode(np.arange(f.max_code + 1), f)
+    rng = np.random.default_rng(31)
+    s = rng.normal(0.0, 3.0, (6, 64))
+    m = s.max(axis=1) + np.array([0.3, 0.0, -0.5, -1.8, -1.9, -4.0])
+    vis = np.ones_like(s, bool)
+    fp = fused_probabilities(s, m, vis, "e4m3", mode="row")
+    assert np.all(fp["delta"] == 0)
+    for i in range(6):
+        t = s[i] - m[i]
+        over = _mitchell_value(max(t) + 7) >= 464.0
+        assert fp["kappa"][i] == (math.floor(round(8 * max(t)) / 8) if over else 0), i
+        for j in range(64):
+            want = _nearest(table, min(_mitchell_value(t[j] - fp["kappa"][i] + 7), 896.0)) * 2.0 ** -7
+            assert fp["P"][i, j] == want, (i, j)
+    assert list(fp["kappa"][:3]) == [0, 0, 0] and fp["kappa"][4] >= 1 and fp["kappa"][5] >= 4
+
+
+def test_variant_affine_codes_closed_form():
+    """Affine E2M1 codes: the default map wherever the value is 1 or more
+    (in units of the block's placement), the straight line below it."""
+    rng = np.random.default_rng(32)
+    s = rng.normal(0.0, 2.0, (16, 96))
+    m = (s.max(axis=1) + rng.uniform(0, 3, 16)).astype(np.float32).astype(np.float64)
+    vis = np.ones_like(s, bool)
+    aff = fused_probabilities(s, m, vis, "e2m1", mode="efq")
+    ref = fused_probabilities(s, m, vis, "e2m1")
+    assert np.array_equal(aff["delta"], ref["delta"]) and np.array_equal(aff["kappa"], ref["kappa"])
+    x = s - m[:, None] + 2 + np.repeat(ref["delta"], 32, axis=1)[:, :96]
+    hi = x >= 0.0
+    assert np.array_equal(aff["codes"][hi], ref["codes"][hi])
+    # below 1: code 1 (0.5) on [-0.75, -0.25), code 2 (1.0) from -0.25, 0 under -0.75
+    lo = ~hi
+    want = np.where(x >= -0.25, 2, np.where(x >= -0.75, 1, 0))
+    exact_tie = np.isclose((2 * x + 2) % 1.0, 0.5)
+    assert np.array_equal(aff["codes"][lo & ~exact_tie], want[lo & ~exact_tie])
+    # monotone in the score within a block
+    for i in range(16):
+        o = np.argsort(s[i, :32])
+        assert np.all(np.diff(aff["P"][i, :32][o]) >= 0)
+
+
+@pytest.mark.parametrize("variant", [("e4m3", dict(p_mode="row")), ("e2m3", dict(p_fmt="e4m3")),
+                                     ("e2m1", dict(p_fmt="e4m3")), ("e2m1", dict(p_mode="efq")),
+                                     ("e4m3", dict(p_mode="exp")), ("e2m1", dict(p_mode="exp"))])
+def test_variants_v_ones_and_q_zero(variant):
+    fmt, kw = variant
+    q, k, v = _head(96, 64, 700, scale=1.5)
+    out = O.fused_attention(q, k, np.ones_like(v), fmt, **kw)
+    assert np.array_equal(out, np.ones_like(out))
+    vh = mx_dequantize(*mx_quantize(np.ascontiguousarray(v.T), fmt), fmt)[:, :96].T
+    out = O.fused_attention(np.zeros_like(q), k, v, fmt, **kw)
+    assert np.array_equal(out, np.broadcast_to(bf16_round(vh.sum(axis=0) / 96.0), out.shape))
+
+
+def test_e4m3_probabilities_over_fp4_operands_are_more_accurate():
+    """E4M3 P~ over FP4 operands: the same operands as the FP4 default, a
+    finer P~; its error against exact attention is lower."""
+    w = W.WORKLOADS["tiny"]
+    q, k, v = (W.bf16_bits_to_f64(a[0, 0]) for a in W.generate(w))
+    ex = O.exact_attention(q, k, v)
+    e_mix = rel_l2(O.fused_attention(q, k, v, "e2m1", p_fmt="e4m3"), ex)
+    e_fp4 = rel_l2(O.fused_attention(q, k, v, "e2m1"), ex)
+    assert e_mix < e_fp4
