@@ -27,10 +27,11 @@
  *     detected before anything is enqueued.  No C++ exception crosses the ABI.
  *   - Calls on distinct streams are thread-safe.  The library keeps a per-
  *     device workspace (quantised operands) that it allocates on first use and
- *     grows as needed; calls that share a device and overlap in time on
- *     different streams serialise on the workspace through stream ordering of
- *     the caller's choosing, so give concurrent attention calls on one device
- *     the same stream.
+ *     grows as needed, stream-ordered (hipMallocAsync on the call's stream,
+ *     the old buffer freed with hipFreeAsync on the stream of the call that
+ *     last used it).  Calls that share a device use the same workspace, so
+ *     give the attention calls of one device one stream, or order their
+ *     streams yourself.
  */
 #ifndef FSA_H
 #define FSA_H
@@ -191,6 +192,10 @@ typedef struct fsa_options {
   const fsa_layout* layout;
   /* fsa_p_variant of P~ (0: the default). */
   int p_variant;
+  /* 1: do not launch the fallback pass (a benchmark hook: rows whose scores
+   * exceed their frozen max by more than 64 binades then come out wrong,
+   * and row_kappa shows them as 65 or more). */
+  int skip_fallback_pass;
 } fsa_options;
 
 /* fsa_attention_fwd with hooks; opt may be NULL.  Same errors. */
@@ -258,8 +263,8 @@ int fsa_attention_fwd_noalloc(const void* q, const void* k, const void* v, void*
 /* Static description of a status code (never NULL). */
 const char* fsa_strerror(int status);
 
-/* Frees the current device's workspace.  Call only when no enqueued work
- * still uses it (e.g. after a device synchronise).  Returns FSA_OK or
+/* Frees the current device's workspace after the work of the last call
+ * that used it (waits for that call's stream).  Returns FSA_OK or
  * FSA_ERR_HIP. */
 int fsa_release_workspace(void);
 

@@ -46,6 +46,7 @@ class Options(ctypes.Structure):
         ("head_fmt", ctypes.POINTER(ctypes.c_int)),
         ("layout", ctypes.POINTER(Layout)),
         ("p_variant", ctypes.c_int),
+        ("skip_fallback_pass", ctypes.c_int),
     ]
 
 
@@ -162,7 +163,8 @@ def quantize_mx(x, fmt: Union[str, int], block_along_rows: bool = False):
 def attention_fwd(q, k, v, fmt: Union[str, int] = "e4m3", causal: bool = False, *,
                   guess_bias: float = 0.0, head_fmt: Optional[Sequence[Union[str, int]]] = None,
                   return_rows: bool = False, event_after_quantize=None, out=None,
-                  no_alloc: bool = False, p_variant: Union[str, int] = "block"):
+                  no_alloc: bool = False, p_variant: Union[str, int] = "block",
+                  skip_fallback_pass: bool = False):
     """Fused-softmax attention; q, k, v bf16 [B, H, S, D] CUDA tensors
     (strided views with contiguous rows are passed with their strides).
 
@@ -183,6 +185,7 @@ def attention_fwd(q, k, v, fmt: Union[str, int] = "e4m3", causal: bool = False, 
     opt = Options()
     opt.guess_bias = float(guess_bias)
     opt.p_variant = P_VARIANT[p_variant] if isinstance(p_variant, str) else int(p_variant)
+    opt.skip_fallback_pass = int(bool(skip_fallback_pass))
     kappa = mg = None
     if return_rows:
         kappa = torch.empty((B, H, S), dtype=torch.int32, device=q.device)

@@ -32,34 +32,37 @@ int kern_fmt(int fmt) { return fmt == FSA_MXFP8_E4M3 ? 0 : (fmt == FSA_MXFP6_E2M
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
+  hipStream_t stream = nullptr;      // the stream of the last call that used it
 };
 
 std::mutex g_mu;
 std::unordered_map<int, Workspace> g_ws;
 
-// Returns a device buffer of at least `need` bytes for the current device.
-// Growing it synchronises the device first so that no enqueued kernel still
-// reads the old buffer.
-int workspace(size_t need, uint8_t** out) {
+// Returns a device buffer of at least `need` bytes for the current device,
+// for work enqueued on `stream`.  Growing it is stream-ordered: the new
+// buffer comes from hipMallocAsync on `stream`, and the old one is released
+// with hipFreeAsync on the stream of the call that last used it, after that
+// call's kernels (no device-wide synchronisation).
+int workspace(size_t need, hipStream_t stream, uint8_t** out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FSA_ERR_HIP;
   std::lock_guard<std::mutex> lock(g_mu);
   Workspace& w = g_ws[dev];
   if (w.bytes < need) {
-    if (w.ptr) {
-      if (hipDeviceSynchronize() != hipSuccess) return FSA_ERR_HIP;
-      if (hipFree(w.ptr) != hipSuccess) return FSA_ERR_HIP;
-      w.ptr = nullptr;
-      w.bytes = 0;
-    }
     const size_t sz = round_up((int64_t)need, 1 << 21);
-    if (hipMalloc(&w.ptr, sz) != hipSuccess) {
+    void* np = nullptr;
+    if (hipMallocAsync(&np, sz, stream) != hipSuccess) {
       (void)hipGetLastError();
-      w.ptr = nullptr;
       return FSA_ERR_NO_MEMORY;
     }
+    if (w.ptr && hipFreeAsync(w.ptr, w.stream) != hipSuccess) {
+      (void)hipFreeAsync(np, stream);
+      return FSA_ERR_HIP;
+    }
+    w.ptr = np;
     w.bytes = sz;
   }
+  w.stream = stream;
   *out = static_cast<uint8_t*>(w.ptr);
   return FSA_OK;
 }
@@ -261,6 +264,7 @@ int attend_piece(const Call& c, const Piece& p, uint8_t* base, const PieceLayout
   a.bias = c.opt ? c.opt->guess_bias : 0.0f;
   a.fb_flag = flag;
   a.call_id = next_call_id();
+  a.skip_fallback = c.opt ? c.opt->skip_fallback_pass : 0;
   // formats per head, and the order workgroups take the heads in: the
   // formats interleaved, so that each XCD's contiguous share of the items
   // holds each format in proportion
@@ -418,7 +422,7 @@ int attention(const void* q, const void* k, const void* v, void* out, int B, int
     const size_t rm = own_rows ? cv.take((size_t)B * H * S * 4) : 0;
     const size_t flag_off = cv.take(8);
     uint8_t* ws = nullptr;
-    st = workspace(cv.off, &ws);
+    st = workspace(cv.off, c.stream, &ws);
     if (st != FSA_OK) return st;
     for (size_t i = 0; i < pieces.size(); ++i)
       if ((st = quantize_piece(c, pieces[i], ws, lays[i])) != FSA_OK) return st;
@@ -535,7 +539,7 @@ int fsa_attention_bf16_ref(const void* q, const void* k, const void* v, void* ou
   a.S = S;
   a.s_alloc = (int)round_up(S, fsa::BF16_KEY_TILE);
   uint8_t* ws = nullptr;
-  const int wst = workspace((size_t)a.BH * D * a.s_alloc * 2, &ws);
+  const int wst = workspace((size_t)a.BH * D * a.s_alloc * 2, static_cast<hipStream_t>(stream), &ws);
   if (wst != FSA_OK) return wst;
   a.vt = reinterpret_cast<uint16_t*>(ws);
   a.scale_log2 = (float)(1.0 / std::log(2.0) / std::sqrt((double)D));
@@ -595,7 +599,10 @@ int fsa_release_workspace(void) {
   std::lock_guard<std::mutex> lock(g_mu);
   auto it = g_ws.find(dev);
   if (it == g_ws.end() || !it->second.ptr) return FSA_OK;
-  if (hipFree(it->second.ptr) != hipSuccess) return FSA_ERR_HIP;
+  // after the last call's kernels on its stream; the caller has finished
+  // with every call (documented), so waiting on that stream suffices
+  if (hipFreeAsync(it->second.ptr, it->second.stream) != hipSuccess) return FSA_ERR_HIP;
+  if (hipStreamSynchronize(it->second.stream) != hipSuccess) return FSA_ERR_HIP;
   it->second = Workspace();
   return FSA_OK;
 }

@@ -907,7 +907,8 @@ hipError_t launch_attn3(const AttnArgs& a, hipStream_t stream) {
   dim3 grid((n_items + 7) / 8 * 8);
   hipLaunchKernelGGL((fsa_fwd_kernel<FSET, PM, PX, D, CAUSAL, false>), grid, dim3(256), 0, stream, a);
   // the fallback pass: ~4 us when the first pass left no row beyond EXT
-  hipLaunchKernelGGL((fsa_fwd_kernel<FSET, PM, PX, D, CAUSAL, true>), grid, dim3(256), 0, stream, a);
+  if (!a.skip_fallback)
+    hipLaunchKernelGGL((fsa_fwd_kernel<FSET, PM, PX, D, CAUSAL, true>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

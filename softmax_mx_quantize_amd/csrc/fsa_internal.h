@@ -96,6 +96,7 @@ struct AttnArgs {
   float bias;                    // added to every frozen max, binades
   uint64_t* fb_flag;             // stamped with call_id when a row needs the fallback
   uint64_t call_id;              // unique per call (never 0)
+  int skip_fallback;             // 1: no fallback-pass launch (rows beyond EXT stay wrong)
   uint8_t hfmt[MAX_HEAD_TABLE];  // element format (FMT_*) of head h0 + j
   uint8_t horder[MAX_HEAD_TABLE];  // head slot -> j: the order workgroups take heads in
 };

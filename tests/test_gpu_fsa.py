@@ -241,3 +241,41 @@ def test_hybrid_one_launch_strided(fmts):
         alone = from_dev_bf16(fsa.attention_fwd(to_dev(q), to_dev(k), to_dev(v), f, False))
         heads = [h for h in range(H) if fmts[h] == f]
         assert np.array_equal(g[:, heads], alone[:, heads]), f
+
+
+def test_workspace_grows_and_is_released():
+    """Growing the workspace (stream-ordered) and releasing it leave results
+    unchanged: a small call, a larger one, a release, the small one again."""
+    import torch
+    import softmax_mx_quantize_amd as fsa
+    announce("fsa workspace growth")
+    small = [W.random_bf16((1, 2, 200, 128), seed, 1.0) for seed in (101, 102, 103)]
+    large = [W.random_bf16((1, 8, 3000, 128), seed, 1.0) for seed in (104, 105, 106)]
+    a = fsa.attention_fwd(*(to_dev(x) for x in small), "e2m3")
+    b = fsa.attention_fwd(*(to_dev(x) for x in large), "e2m3")
+    torch.cuda.synchronize()
+    fsa.release_workspace()
+    c = fsa.attention_fwd(*(to_dev(x) for x in small), "e2m3")
+    d = fsa.attention_fwd(*(to_dev(x) for x in large), "e2m3")
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+    assert torch.equal(b.view(torch.int16), d.view(torch.int16))
+
+
+def test_skip_fallback_pass_hook():
+    """Without the fallback pass, rows beyond the in-sweep shifts keep the
+    first pass's offsets (65 binades or more); every other row is unchanged."""
+    announce("fsa skip fallback pass")
+    S, D = 300, 128
+    q, k, v = (W.bf16_bits_to_f64(W.random_bf16((1, 1, S, D), seed, 1.0)) for seed in (12, 13, 14))
+    c = O.attention.score_scale(D)
+    far = [5, 77, 200]
+    for i, j in zip(far, (140, 290, 131)):
+        q[0, 0, i] = k[0, 0, j] * (300.0 / (c * float(k[0, 0, j] @ k[0, 0, j])))
+    q, k, v = (W.f32_to_bf16_bits(x.astype(np.float32)) for x in (q, k, v))
+    full, kf, _ = _run(q, k, v, "e2m1")
+    part, kp, _ = _run(q, k, v, "e2m1", skip_fallback_pass=True)
+    near = np.setdiff1d(np.arange(S), far)
+    assert np.all(kp[0, 0, far] >= 65) and np.all(kf[0, 0, far] > 64)
+    assert np.array_equal(part[0, 0, near], full[0, 0, near])
+    assert np.array_equal(kp[0, 0, near], kf[0, 0, near])
