@@ -10,9 +10,11 @@ from __future__ import annotations
 
 import concurrent.futures
 import os
+import re
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -60,6 +62,65 @@ def _compile(src: str) -> str:
     return obj
 
 
+OBJDUMP = "/opt/rocm/llvm/bin/llvm-objdump"
+
+
+def _vregs(operand: str) -> set:
+    m = re.match(r"v\[(\d+):(\d+)\]$", operand)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", operand)
+    return {int(m.group(1))} if m else set()
+
+
+def mfma_partial_overlaps(disasm: str):
+    """(count, offenders) over the matrix-core instructions of a gfx950
+    disassembly: an offender's result registers D cover part, but not all,
+    of its accumulator input C (operands D, A, B, C, ...).  A 32x32 product
+    reads C and writes D over several passes, so D must sit exactly on C or
+    apart from it; some instruction schedules (LLVM's max-ILP one) give the
+    scaled 32x32x64 product a D that overlaps C by part, and the kernel then
+    returns wrong rows."""
+    bad, n = [], 0
+    for line in disasm.splitlines():
+        text = line.split("//")[0].strip()
+        if not text.startswith("v_mfma"):
+            continue
+        n += 1
+        ops = [o.strip().split()[0] for o in text.split(None, 1)[1].split(",")]
+        d, c = _vregs(ops[0]), _vregs(ops[3])
+        if d & c and d != c:
+            bad.append(text)
+    return n, bad
+
+
+def scan_library(lib: str):
+    """Disassembles every gfx950 code object of the library (built here from
+    source) and returns (matrix-core instruction count, offenders), or None
+    when llvm-objdump is not installed."""
+    if not os.path.exists(OBJDUMP):
+        return None
+    with tempfile.TemporaryDirectory() as tmp:
+        # the extractor writes the code objects next to its input
+        copy = os.path.join(tmp, "lib.so")
+        shutil.copyfile(lib, copy)
+        r = subprocess.run([OBJDUMP, "--offloading", copy], capture_output=True, text=True, cwd=tmp)
+        if r.returncode != 0:
+            raise RuntimeError("code object extraction failed:\n" + r.stderr[-2000:])
+        total, bad = 0, []
+        for name in sorted(os.listdir(tmp)):
+            path = os.path.join(tmp, name)
+            if "gfx950" not in name or os.path.getsize(path) == 0:
+                continue
+            d = subprocess.run([OBJDUMP, "-d", "--mcpu=gfx950", path], capture_output=True, text=True)
+            if d.returncode != 0:
+                raise RuntimeError("disassembly failed:\n" + d.stderr[-2000:])
+            n, b = mfma_partial_overlaps(d.stdout)
+            total += n
+            bad += b
+    return total, bad
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
@@ -71,6 +132,11 @@ def build(verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
+    scan = scan_library(tmp)
+    if scan is not None and scan[1]:
+        os.remove(tmp)
+        raise RuntimeError("matrix-core accumulator registers partly overwritten by the result "
+                           "(%d instructions), e.g.:\n  %s" % (len(scan[1]), "\n  ".join(scan[1][:3])))
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)
