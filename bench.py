@@ -48,7 +48,9 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"e4m3": 5000.0, "e2m3": 10100.0, "e2m1": 10100.0, "bf16": 2500.0}
 METRIC = "attention fwd TFLOP/s and % of MX MFMA peak (MXFP8/6/4, S=16K, D=128)"
 KERNEL_SOURCES = ("softmax_mx_quantize_amd/csrc/fsa_common.h",
+                  "softmax_mx_quantize_amd/csrc/fsa_attn.h",
                   "softmax_mx_quantize_amd/csrc/fsa_fwd.hip",
+                  "softmax_mx_quantize_amd/csrc/fsa_internal.h",
                   "softmax_mx_quantize_amd/csrc/fsa_device.h",
                   "softmax_mx_quantize_amd/csrc/lds_dma.h")
 
@@ -74,7 +76,21 @@ def stored_traffic(fmt: str):
     return d.get("bytes_per_launch", {}).get(fmt)
 
 
-FMT_OF_TEMPLATE = {"0": "e4m3", "1": "e2m3", "2": "e2m1"}
+# fsa_fwd_kernel<FSET, PM, PX, D, CAUSAL, REBASE>: FSET is the set of formats
+# the launch holds (bit 0 E4M3, bit 1 E2M3, bit 2 E2M1), PM the P~ variant,
+# PX 1 for E4M3 P~ over FP6/FP4 operands.
+FMT_OF_FSET = {1: "e4m3", 2: "e2m3", 4: "e2m1"}
+
+
+def traffic_key(kernel_name: str) -> str:
+    """Key of profiles/fsa_fwd_traffic.json for one fused-kernel instance:
+    the format for the default P~ map of a one-format launch, else a tag
+    naming the format set and the variant."""
+    args = [a.strip() for a in kernel_name.split("fsa_fwd_kernel<")[1].split(">")[0].split(",")]
+    fset, pm, px = int(args[0]), int(args[1]), int(args[2])
+    if pm == 0 and px == 0 and fset in FMT_OF_FSET:
+        return FMT_OF_FSET[fset]
+    return "fset%d_pm%d_px%d" % (fset, pm, px)
 
 
 def _pmc_per_kernel(db_path: str, counter: str):
@@ -114,7 +130,7 @@ def write_traffic(fetch_db: str, write_db: str, copy_bytes: int) -> dict:
     for k in fetch:
         if "fsa_fwd_kernel<" not in k:
             continue
-        fmt = FMT_OF_TEMPLATE[k.split("fsa_fwd_kernel<")[1].split(",")[0].strip()]
+        fmt = traffic_key(k)
         fb = fetch[k] * 1024.0 * f_scale
         wb = write.get(k, 0.0) * 1024.0 * w_scale
         out["fetch_bytes"][fmt] = out["fetch_bytes"].get(fmt, 0.0) + fb
