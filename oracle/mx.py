@@ -8,6 +8,9 @@ below are those of the OCP Microscaling Formats (MX) v1.0 specification:
 * FP8 E4M3: 1 sign, 4 exponent bits (bias 7), 3 mantissa bits, no infinity,
   the all-ones pattern is NaN, largest finite 448.
 * FP6 E2M3: 1 sign, 2 exponent bits (bias 1), 3 mantissa bits, largest 7.5.
+* FP6 E3M2: 1 sign, 3 exponent bits (bias 3), 2 mantissa bits, largest 28
+  (the other FP6 element type of the OCP specification; here only a
+  probability format, not an operand format of the attention path).
 * FP4 E2M1: 1 sign, 2 exponent bits (bias 1), 1 mantissa bit, largest 6.
 * E8M0 scale: an unsigned byte X+127 meaning 2**X; 0xFF is NaN.
 
@@ -65,6 +68,7 @@ FORMATS: Dict[str, Format] = {
     "e4m3": Format("e4m3", 4, 3, 7, 0x7E),
     "e2m3": Format("e2m3", 2, 3, 1, 0x1F),
     "e2m1": Format("e2m1", 2, 1, 1, 0x07),
+    "e3m2": Format("e3m2", 3, 2, 3, 0x1F),
 }
 
 

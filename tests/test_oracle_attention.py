@@ -102,7 +102,7 @@ def _nearest(vals_table, a):
 
 
 @pytest.mark.parametrize("mode", ["block", "exp"])
-@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("fmt", FMTS + ["e3m2"])
 def test_probability_map_against_independent_route(fmt, mode):
     """P~ of single-block rows, recomputed with math.ldexp (bit-pattern
     exponential) or math.pow (the exact one) and brute-force rounding from
@@ -368,7 +368,8 @@ def test_variant_affine_codes_closed_form():
 
 @pytest.mark.parametrize("variant", [("e4m3", dict(p_mode="row")), ("e2m3", dict(p_fmt="e4m3")),
                                      ("e2m1", dict(p_fmt="e4m3")), ("e2m1", dict(p_mode="efq")),
-                                     ("e4m3", dict(p_mode="exp")), ("e2m1", dict(p_mode="exp"))])
+                                     ("e4m3", dict(p_mode="exp")), ("e2m1", dict(p_mode="exp")),
+                                     ("e2m3", dict(p_fmt="e3m2"))])
 def test_variants_v_ones_and_q_zero(variant):
     fmt, kw = variant
     q, k, v = _head(96, 64, 700, scale=1.5)
@@ -388,3 +389,22 @@ def test_e4m3_probabilities_over_fp4_operands_are_more_accurate():
     e_mix = rel_l2(O.fused_attention(q, k, v, "e2m1", p_fmt="e4m3"), ex)
     e_fp4 = rel_l2(O.fused_attention(q, k, v, "e2m1"), ex)
     assert e_mix < e_fp4
+
+
+def test_e3m2_probabilities_keep_more_binades_with_coarser_steps():
+    """E3M2 P~ (placement 2^4, smallest step 2^-4) against E2M3 (placement
+    2^2, smallest step 2^-3), on one block whose top score sits at the
+    guess: both give 1 there; 2^-6 survives only in E3M2 (E2M3 flushes
+    anything below 2^-6 of the block's top); near the top E3M2's two
+    mantissa bits are coarser (the bit-pattern value 0.95 of t = -0.1
+    rounds to 0.9375 in E2M3 and to 1 in E3M2); 2^-9 is half of E3M2's
+    smallest step and rounds to zero (ties to even), 1.5 * 2^-9 up to it."""
+    t = np.array([0.0, -0.1, -6.0, -9.0, -8.5, -2.0])
+    s = np.full((1, 32), -60.0)
+    s[0, : t.size] = t
+    m = np.zeros(1)
+    vis = np.ones_like(s, bool)
+    p6 = fused_probabilities(s, m, vis, "e2m3")["P"][0, : t.size]
+    p5 = fused_probabilities(s, m, vis, "e3m2")["P"][0, : t.size]
+    assert list(p6) == [1.0, 0.9375, 0.0, 0.0, 0.0, 0.25]
+    assert list(p5) == [1.0, 1.0, 2.0 ** -6, 0.0, 2.0 ** -8, 0.25]

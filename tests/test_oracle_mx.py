@@ -16,7 +16,7 @@ from oracle import (FORMATS, decode, encode_values, round_to_format, mx_quantize
                     mx_dequantize, pack_codes, unpack_codes, bf16_round)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
-FMTS = ["e4m3", "e2m3", "e2m1"]
+FMTS = ["e4m3", "e2m3", "e2m1", "e3m2"]
 
 
 def _golden_tables():
@@ -31,7 +31,7 @@ def _golden_tables():
 
 def test_element_tables_match_ocp_values():
     t = _golden_tables()
-    for fmt in ("e2m1", "e2m3"):
+    for fmt in ("e2m1", "e2m3", "e3m2"):
         want = np.array([float(v) for v in t[fmt]])
         got = decode(np.arange(len(want)), fmt)
         assert np.array_equal(got, want), fmt
