@@ -307,7 +307,8 @@ def main() -> int:
     # the P~ variants on the same inputs (kernel time: quantisation excluded)
     variants = {}
     if not args.only and not args.no_extra:
-        for vname, fmt in (("row", "e4m3"), ("e4m3", "e2m3"), ("e4m3", "e2m1"), ("affine", "e2m1"),
+        for vname, fmt in (("row", "e4m3"), ("e4m3", "e2m3"), ("e4m3", "e2m1"), ("e3m2", "e2m3"),
+                           ("affine", "e2m1"),
                            ("exact_exp", "e4m3"), ("exact_exp", "e2m3"), ("exact_exp", "e2m1")):
             print("[bench] timing variant %s over %s" % (vname, fmt), file=sys.stderr, flush=True)
             wall_ms, kern_ms, _ = time_fsa(fsa, torch, q, k, v, fmt, args.steps, args.warmup,

@@ -145,14 +145,18 @@ int fsa_attention_bf16_ref(const void* q, const void* k, const void* v, void* ou
  *                    for Softmax", abstract; every head E2M1);
  *   FSA_P_EXACT_EXP  the vector unit's exp2 in place of the bit pattern:
  *                    P~ is 2^x itself rounded onto the element grid (the
- *                    rounding thresholds of the exact map).
+ *                    rounding thresholds of the exact map);
+ *   FSA_P_E3M2       E3M2 P~ (FP6 with three exponent bits: eight binades
+ *                    below a block's top instead of five, two mantissa bits
+ *                    instead of three) over E2M3 Q, K, V (every head E2M3).
  * A variant whose format condition fails gives FSA_ERR_UNSUPPORTED. */
 typedef enum fsa_p_variant {
   FSA_P_BLOCK = 0,
   FSA_P_ROW_SCALE = 1,
   FSA_P_E4M3 = 2,
   FSA_P_AFFINE = 3,
-  FSA_P_EXACT_EXP = 4
+  FSA_P_EXACT_EXP = 4,
+  FSA_P_E3M2 = 5
 } fsa_p_variant;
 
 /* Element strides of strided views: for each tensor, the strides of the

@@ -51,7 +51,7 @@ class Options(ctypes.Structure):
 
 
 # fsa_p_variant
-P_VARIANT = {"block": 0, "row": 1, "e4m3": 2, "affine": 3, "exact_exp": 4}
+P_VARIANT = {"block": 0, "row": 1, "e4m3": 2, "affine": 3, "exact_exp": 4, "e3m2": 5}
 
 
 def _load() -> ctypes.CDLL:
@@ -172,7 +172,7 @@ def attention_fwd(q, k, v, fmt: Union[str, int] = "e4m3", causal: bool = False, 
     and frozen maxima (float32), each [B, H, S].  ``no_alloc`` calls
     ``fsa_attention_fwd_noalloc`` (the library allocates nothing; the
     tensors here are still torch's).  ``p_variant`` picks the P~ variant
-    (``fsa_p_variant``: "block", "row", "e4m3", "affine", "exact_exp").
+    (``fsa_p_variant``: "block", "row", "e4m3", "affine", "exact_exp", "e3m2").
     """
     import torch
     _bf16_rows(q, k, v)

@@ -144,7 +144,7 @@ struct Piece {
 };
 
 struct Call {
-  int pm = 0, px = 0;              // P~ variant (PM_*) and E4M3 P~ over FP6/FP4
+  int pm = 0, px = 0;              // P~ variant (PM_*); P~ format (1 E4M3, 2 E3M2; 0 the operands')
   const uint16_t *q, *k, *v;
   uint16_t* out;
   int B, H, S, D, causal;
@@ -214,7 +214,7 @@ int quantize_piece(const Call& c, const Piece& p, uint8_t* base, const PieceLayo
   a.nb_out = c.D / 32;
   a.code_slab = l.kc_slab;
   a.scale_layout = fsa::SCALES_KEY_TILES;
-  a.key8 = c.px;
+  a.key8 = c.px == 1;              // FP8 key order for E4M3 P~ only
   if (fsa::launch_mx_quant(a, fset, 0, c.stream) != hipSuccess) return FSA_ERR_HIP;
   // V: output rows are the D columns, blocks along the keys
   a.x = c.v + p.b0 * c.st.v[0] + p.h0 * c.st.v[1];
@@ -394,6 +394,10 @@ int attention(const void* q, const void* k, const void* v, void* out, int B, int
     case FSA_P_E4M3:
       if (!all_fmt({FSA_MXFP6_E2M3, FSA_MXFP4_E2M1})) return FSA_ERR_UNSUPPORTED;
       c.px = 1;
+      break;
+    case FSA_P_E3M2:
+      if (!all_fmt({FSA_MXFP6_E2M3})) return FSA_ERR_UNSUPPORTED;
+      c.px = 2;
       break;
     case FSA_P_AFFINE:
       if (!all_fmt({FSA_MXFP4_E2M1})) return FSA_ERR_UNSUPPORTED;

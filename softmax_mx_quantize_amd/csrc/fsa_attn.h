@@ -71,11 +71,14 @@ __device__ __forceinline__ v16f mma32(const opv<F>& a, const opv<F>& b, const v1
     return mfma32_v4(a, b, c, Fmt<F>::mfma, Fmt<F>::mfma, OA, sa, 0, sb);
 }
 // O^T += V^T P~^T with V^T in format F (A) and P~ in format P (B): the same
-// format, or FP6/FP4 V^T with FP8 P~ (mixed widths).
+// format, E2M3 V^T with E3M2 P~ (same width, two element formats), or
+// FP6/FP4 V^T with FP8 P~ (mixed widths).
 template <int F, int P, int OA>
 __device__ __forceinline__ v16f mma32_pv(const opv<F>& a, const opv<P>& b, const v16f& c, int sa,
                                          int sb) {
   if constexpr (F == P) return mma32<F, OA>(a, b, c, sa, sb);
+  else if constexpr (Fmt<F>::bits == 6 && Fmt<P>::bits == 6)
+    return mfma32_v6(a, b, c, Fmt<F>::mfma, Fmt<P>::mfma, OA, sa, 0, sb);
   else if constexpr (Fmt<F>::bits == 6)
     return mfma32_v6_v8(a, b, c, Fmt<F>::mfma, Fmt<P>::mfma, OA, sa, 0, sb);
   else
@@ -204,7 +207,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int b, const 
   constexpr int PBITS = Fmt<P>::bits;        // P~ codes
   constexpr bool KEY8 = PBITS == 8;          // FP8 key order of the score rows
   constexpr int KOB = KEY8 ? 8 : 4;          // key-order argument of the layouts
-  static_assert(P == F || (P == FMT_E4M3 && PM == PM_BLOCK), "E4M3 P~ over FP6/FP4 operands");
+  static_assert(P == F || (P == FMT_E4M3 && PM == PM_BLOCK) ||
+                    (P == FMT_E3M2 && F == FMT_E2M3 && PM == PM_BLOCK),
+                "E4M3 P~ over FP6/FP4 operands, E3M2 P~ over E2M3 operands");
   static_assert(PM != PM_ROW || (F == FMT_E4M3 && P == FMT_E4M3), "one scale per row: E4M3");
   static_assert(PM != PM_EFQ || (F == FMT_E2M1 && P == FMT_E2M1), "affine codes: E2M1");
   // Exact exponential: the score product yields t + REF in binades (no 2^23
@@ -691,7 +696,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int b, const 
         const auto sbs = __builtin_amdgcn_permlane32_swap((uint32_t)sb, (uint32_t)sb, false, false);
         Pack32<P, false>::run(pv, w, conv_scale((int)sbs[0]), conv_scale((int)sbs[1]));
       } else if constexpr (PBITS == 6) {
-        pack_fp6_split(pv, w, conv_scale(sb));
+        pack_fp6_split<P>(pv, w, conv_scale(sb));
       } else {
         Pack32<P, false>::run(pv, w, conv_scale(sb), conv_scale(sb));
       }
@@ -899,9 +904,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int b, const 
 
 // The attention kernel over the heads [h0, h0 + hrun) of every batch entry,
 // each in its own element format from FSET (a bit set of FMT_*): one
-// launch for a hybrid schedule.  PM is the P~ variant, PX = 1 puts P~ in
-// E4M3 over FP6/FP4 operands.  The format is uniform per workgroup, so
-// the branch into its body is a scalar one.
+// launch for a hybrid schedule.  PM is the P~ variant; PX picks a P~
+// format other than the operands': 1 E4M3 over FP6/FP4, 2 E3M2 over E2M3.
+// The format is uniform per workgroup, so the branch into its body is a
+// scalar one.
 template <int FSET, int PM, int PX, int D, bool CAUSAL, bool REBASE>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
 fsa_fwd_kernel(AttnArgs a) {
@@ -934,8 +940,8 @@ fsa_fwd_kernel(AttnArgs a) {
   const int f = (FSET & (FSET - 1)) ? a.hfmt[j] : 0;
   with_format<FSET>(f, [&](auto fc) {
     constexpr int FC = decltype(fc)::value;
-    attn_body<FC, PX ? (int)FMT_E4M3 : FC, PM, D, CAUSAL, REBASE>(a, b, a.h0 + j, wi, q_wg, kl0, kl1,
-                                                                   vl0, vl1);
+    constexpr int PF = PX == 1 ? (int)FMT_E4M3 : PX == 2 ? (int)FMT_E3M2 : FC;
+    attn_body<FC, PF, PM, D, CAUSAL, REBASE>(a, b, a.h0 + j, wi, q_wg, kl0, kl1, vl0, vl1);
   });
 #endif  // __HIP_DEVICE_COMPILE__
 }

@@ -37,6 +37,9 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef short v2s __attribute__((ext_vector_type(2)));
 
 enum { FMT_E4M3 = 0, FMT_E2M3 = 1, FMT_E2M1 = 2 };
+// FP6 E3M2: a probability format only (P~ over E2M3 operands), never an
+// operand format of a launch, so it has no bit in a format set.
+enum { FMT_E3M2 = 3 };
 
 // Per-format constants.  emax: exponent of the largest normal binade;
 // e_top: its biased exponent; cap: the largest upward block shift that keeps
@@ -59,6 +62,12 @@ template <> struct Fmt<FMT_E2M1> {
   static constexpr int mfma = 4;
   static constexpr float maxval = 6.0f;
   static constexpr uint32_t one_code = 0x2;
+};
+template <> struct Fmt<FMT_E3M2> {
+  static constexpr int bits = 6, mbits = 2, bias = 3, emax = 4, e_top = 7;
+  static constexpr int mfma = 3;
+  static constexpr float maxval = 28.0f;
+  static constexpr uint32_t one_code = 0x0C;
 };
 
 // Calls fn(std::integral_constant<int, F>) for the element format f, which
@@ -89,6 +98,7 @@ template <int F> struct Operand;
 template <> struct Operand<FMT_E4M3> { typedef v8i type; static constexpr int words = 8; };
 template <> struct Operand<FMT_E2M3> { typedef v6i type; static constexpr int words = 6; };
 template <> struct Operand<FMT_E2M1> { typedef v4i type; static constexpr int words = 4; };
+template <> struct Operand<FMT_E3M2> { typedef v6i type; static constexpr int words = 6; };
 template <int F> using opv = typename Operand<F>::type;
 
 template <int F>
@@ -170,18 +180,29 @@ template <bool CLAMP> struct Pack32<FMT_E2M3, CLAMP> {
 
 // FP6 pack of 32 values held as even elements (v[0..15]) then odd elements
 // (v[16..31]): the two sources of the 32-element conversion, so that callers
-// can produce them in place.  Same conversion and wait states as above.
+// can produce them in place.  Same conversion and wait states as above;
+// F = FMT_E3M2 takes the E3M2 ("bf6") form of the conversion.
+template <int F = FMT_E2M3>
 __device__ __forceinline__ void pack_fp6_split(const float* v, uint32_t* w, float scale) {
+  static_assert(F == FMT_E2M3 || F == FMT_E3M2, "FP6 formats");
   v16f ev, od;
 #pragma unroll
   for (int i = 0; i < 16; ++i) { ev[i] = v[i]; od[i] = v[16 + i]; }
   v6i r;
-  asm volatile(
-      "v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3\n\t"
-      "s_nop 7\n\t"
-      "s_nop 7"
-      : "=&v"(r)
-      : "v"(ev), "v"(od), "v"(scale));
+  if constexpr (F == FMT_E2M3)
+    asm volatile(
+        "v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3\n\t"
+        "s_nop 7\n\t"
+        "s_nop 7"
+        : "=&v"(r)
+        : "v"(ev), "v"(od), "v"(scale));
+  else
+    asm volatile(
+        "v_cvt_scalef32_2xpk16_bf6_f32 %0, %1, %2, %3\n\t"
+        "s_nop 7\n\t"
+        "s_nop 7"
+        : "=&v"(r)
+        : "v"(ev), "v"(od), "v"(scale));
 #pragma unroll
   for (int i = 0; i < 6; ++i) w[i] = (uint32_t)r[i];
 }

@@ -108,9 +108,9 @@ constexpr int attn_vstage_bytes(int d) { return d * 128 + 4 * d; }
 
 // `fset`: the formats present in a.hfmt[0, hrun), as a bit set (1 << FMT_*);
 // `pm` the P~ variant (PM_* of fsa_common.h: 0 block scales, 1 one scale
-// per row, 2 affine E2M1 codes, 3 exact exponential); `px` = 1 for E4M3
-// P~ over FP6/FP4 operands.  hipErrorInvalidValue for a combination that
-// is not built.
+// per row, 2 affine E2M1 codes, 3 exact exponential); `px` the P~ format
+// when it differs from the operands' (1 E4M3 over FP6/FP4, 2 E3M2 over
+// E2M3).  hipErrorInvalidValue for a combination that is not built.
 hipError_t launch_fsa_fwd(const AttnArgs& a, int fset, int pm, int px, int D, int causal,
                           hipStream_t stream);
 

@@ -3,6 +3,7 @@ definitions (oracle.attention.fused_probabilities modes):
 
 * "row"       one scale per row, E4M3;
 * "e4m3"      E4M3 P~ over FP6/FP4 operands (mixed-width products);
+* "e3m2"      E3M2 P~ over E2M3 operands (two FP6 element formats);
 * "affine"    E2M1 codes by one affine rule (EFQ-style);
 * "exact_exp" the exact exponential in place of the bit pattern.
 
@@ -38,6 +39,7 @@ VARIANTS = [
     ("row", "e4m3", dict(p_mode="row"), "e4m3", "row"),
     ("e4m3", "e2m3", dict(p_fmt="e4m3"), "e4m3", "block"),
     ("e4m3", "e2m1", dict(p_fmt="e4m3"), "e4m3", "block"),
+    ("e3m2", "e2m3", dict(p_fmt="e3m2"), "e3m2", "block"),
     ("affine", "e2m1", dict(p_mode="efq"), "e2m1", "efq"),
     ("exact_exp", "e4m3", dict(p_mode="exp"), "e4m3", "exp"),
     ("exact_exp", "e2m3", dict(p_mode="exp"), "e2m3", "exp"),
@@ -135,7 +137,8 @@ def test_variant_rejects_unbuilt_formats():
     import torch
     import softmax_mx_quantize_amd as fsa
     q = torch.zeros((1, 2, 64, 128), dtype=torch.bfloat16, device="cuda")
-    for variant, fmt in (("row", "e2m1"), ("affine", "e4m3"), ("e4m3", "e4m3")):
+    for variant, fmt in (("row", "e2m1"), ("affine", "e4m3"), ("e4m3", "e4m3"), ("e3m2", "e2m1"),
+                         ("e3m2", "e4m3")):
         with pytest.raises(fsa.FsaError) as e:
             fsa.attention_fwd(q, q, q, fmt, p_variant=variant)
         assert e.value.status == -2
@@ -150,9 +153,9 @@ def _threads():
 
 
 # full-size variants: Video-DiT tensors, each variant's own formats
-FULL = [("row", "e4m3"), ("e4m3", "e2m3"), ("e4m3", "e2m1"), ("affine", "e2m1"),
+FULL = [("row", "e4m3"), ("e4m3", "e2m3"), ("e4m3", "e2m1"), ("e3m2", "e2m3"), ("affine", "e2m1"),
         ("exact_exp", "e4m3"), ("exact_exp", "e2m3"), ("exact_exp", "e2m1")]
-CRIT_MET = {"e4m3", "exact_exp"}
+CRIT_MET = {"e4m3", "e3m2", "exact_exp"}
 # variants whose definition misses the 1.1 bar on some heads (host runs of
 # the oracle: up to ~1.4 for one E4M3 scale per row, ~1.5 for the affine
 # E2M1 codes): a looser bound that still catches a broken kernel
