@@ -279,3 +279,43 @@ def test_skip_fallback_pass_hook():
     assert np.all(kp[0, 0, far] >= 65) and np.all(kf[0, 0, far] > 64)
     assert np.array_equal(part[0, 0, near], full[0, 0, near])
     assert np.array_equal(kp[0, 0, near], kf[0, 0, near])
+
+
+@pytest.mark.parametrize("fmt,causal", [("e2m1", False), ("e4m3", True)])
+def test_long_head_sampled_rows(fmt, causal):
+    """One head of 2^21 + 37 keys (ragged last tile; key offsets and buffer
+    ranges far past the workloads'): rows at both ends, at tile and block
+    boundaries and in the middle, against the oracle over all keys."""
+    import torch
+    import softmax_mx_quantize_amd as fsa
+    S, D = 2 ** 21 + 37, 128
+    announce("fsa long head", fmt, causal, S)
+    q, k, v = (W.random_bf16((1, 1, S, D), seed, 1.0) for seed in (61, 62, 63))
+    rows = np.array([0, 1, 127, 128, 4097, S // 2 + 3, S - 130, S - 129, S - 38, S - 1])
+    out, kap, mg = fsa.attention_fwd(to_dev(q), to_dev(k), to_dev(v), fmt, causal, return_rows=True)
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(rows).cuda()
+    g = from_dev_bf16(out[:, :, idx])
+    kr = kap[:, :, idx].cpu().numpy()
+    mr = mg[:, :, idx].cpu().numpy()
+    del out, kap, mg
+    ref, kaps, border, infos = _oracle_heads(q, k, v, [fmt], causal, rows=rows)
+    info, f = infos[0]
+    dm = np.abs(mr[0, 0] - info["m_tilde"])
+    assert np.all(dm <= 1e-4 * np.maximum(1.0, np.abs(info["m_tilde"]))), dm.max()
+    ex, _ = excess_rel_l2(g[0, 0], ref[0], info, f, eps_rows(mr[0, 0], info))
+    print("rel L2 %.2e, beyond near-tie codes %.2e" % (rel_l2(g[0, 0], ref[0]), ex))
+    assert ex <= TOL, ex
+    check_kappa(kr.ravel(), kaps.ravel(), border.ravel())
+
+
+def test_many_heads_split_into_pieces():
+    """300 heads (more than one launch's head table of 256, so the call runs
+    in two pieces), cycling through the three formats, with per-row outputs:
+    every row of every head against the oracle."""
+    H, S, D = 300, 150, 64
+    announce("fsa many heads", H)
+    q, k, v = (W.random_bf16((1, H, S, D), seed, 1.2) for seed in (64, 65, 66))
+    fmts = [FMTS[h % 3] for h in range(H)]
+    g, kap, mg = _run(q, k, v, fmts[0], False, head_fmt=fmts)
+    _check(g, kap, mg, *_oracle_heads(q, k, v, fmts, False))
