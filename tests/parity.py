@@ -9,7 +9,8 @@ rounding tie, its code may fall on either side; where a block's largest
 value lies that close to the tie that decides the block's binade, every
 code of the block may be rounded one binade coarser or finer.  Each such
 element may therefore move P~ by one grid step (two in a tied block), and
-the row's output by that step times |v^_j - out| / l.
+the row's output by those steps times |v^_j - out|, over l less the steps
+(the flips may lower the row sum).
 
 ``excess_rel_l2`` removes exactly that allowance row by row and returns the
 relative L2 of what is left, which is held to the same 2e-3 as everything
@@ -90,12 +91,18 @@ def tie_allowance(info, fmt, out_ref, eps_x, mode="block"):
         tied_el[:] = False                                # no block shifts
     step = np.where(near, q, 0.0) + np.where(tied_el, 2.0 * q, 0.0)
     step = step * np.ldexp(1.0, (-pl - dfull).astype(np.int64))
+    # A set of flips delta_j (|delta_j| <= step_j) moves the row to
+    # (O + sum delta_j v_j) / (l + sum delta_j), i.e. by
+    # sum delta_j (v_j - out) / (l + sum delta_j): at most
+    # sum step_j |v_j - out| / (l - sum step_j).
     vh = info["v_hat"]
-    allow = np.zeros(R)
+    num = np.zeros(R)
     rows, cols = np.nonzero(step)
     for i, j in zip(rows, cols):
-        allow[i] += step[i, j] * np.linalg.norm(vh[j] - out_ref[i])
-    return allow / info["l"]
+        num[i] += step[i, j] * np.linalg.norm(vh[j] - out_ref[i])
+    l = info["l"]
+    den = l - step.sum(axis=1)
+    return np.where(num > 0, num / np.maximum(den, 1e-300), 0.0)
 
 
 def excess_rel_l2(gpu_rows, ref_rows, info, fmt, eps_x, mode="block"):

@@ -1,0 +1,127 @@
+"""Pins of the parity tolerance (tests/parity.py) on the CPU.
+
+The GPU tests forgive exactly the output change that codes near a rounding
+tie can make when t is placed to within eps binades.  These tests check that
+bound against simulated kernels built from the oracle's own probability map:
+a kernel whose t is off by a known amount is the oracle with its frozen max
+moved by that amount (t = s - m~), so its codes flip exactly where the
+exact value sits within that distance of a tie.
+
+* an error within eps is absorbed in full (nothing is left over); eps is
+  taken at 1e-3 binades here, where every format flips enough codes on a
+  small head to exercise the bound (it is linear in eps; the kernel's own
+  EPS_PLACE of 3e-5 flips too few FP6/FP4 codes on a CPU-sized sample);
+* the same error with no allowance, or a much larger error, is not;
+* a code moved one step away from any tie is not absorbed at all.
+"""
+
+import numpy as np
+import pytest
+
+import workloads as W
+import oracle as O
+from oracle.attention import fused_probabilities
+from parity import EPS_PLACE, excess_rel_l2, tie_allowance
+
+FMTS = ["e4m3", "e2m3", "e2m1"]
+
+
+def _case(fmt, seed=91, S=512, rows=48, scale=1.6):
+    q, k, v = (W.random_bf16((1, 1, S, 64), seed + i, scale) for i in range(3))
+    qh, kh, vh = (W.bf16_bits_to_f64(x[0, 0]) for x in (q, k, v))
+    _, info = O.fused_attention(qh, kh, vh, fmt, rows=np.arange(rows), return_info=True)
+    out = info["P"] @ info["v_hat"] / info["l"][:, None]       # unrounded output rows
+    return info, out
+
+
+def _shifted(info, fmt, delta):
+    """Output rows of a kernel whose t is larger by ``delta`` binades in
+    every row (its frozen max lower by delta)."""
+    fp = fused_probabilities(info["scores"], info["m_tilde"] - delta, info["visible"], fmt)
+    P = fp["P"]
+    return P @ info["v_hat"] / P.sum(axis=1)[:, None]
+
+
+EPS = 1e-3
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_placement_error_within_eps_is_absorbed(fmt):
+    info, out = _case(fmt)
+    for delta in (0.8 * EPS, -0.8 * EPS):
+        k_out = _shifted(info, fmt, delta)
+        plain = O.rel_l2(k_out, out)
+        ex, n_rows = excess_rel_l2(k_out, out, info, fmt, EPS)
+        assert plain > 0.0 and n_rows > 0        # some codes did flip
+        assert ex <= 1e-3 * plain, (delta, ex, plain)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_without_allowance_nothing_is_forgiven(fmt):
+    info, out = _case(fmt)
+    k_out = _shifted(info, fmt, 0.8 * EPS)
+    assert np.all(tie_allowance(info, fmt, out, 0.0) == 0.0)
+    ex, n_rows = excess_rel_l2(k_out, out, info, fmt, 0.0)
+    assert n_rows == 0
+    assert ex == pytest.approx(O.rel_l2(k_out, out), rel=1e-12)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_larger_placement_error_is_not_absorbed(fmt):
+    info, out = _case(fmt)
+    k_out = _shifted(info, fmt, 0.05)          # 50 x the allowed placement error
+    plain = O.rel_l2(k_out, out)
+    ex, _ = excess_rel_l2(k_out, out, info, fmt, EPS)
+    assert ex >= 0.5 * plain > 0.0, (ex, plain)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_code_moved_away_from_ties_is_not_absorbed(fmt):
+    """The largest element of a row that has no element within the kernel's
+    placement error of a tie is moved one grid step: the allowance gives
+    that row nothing."""
+    info, out = _case(fmt)
+    f = O.FORMATS[fmt]
+    allow = tie_allowance(info, fmt, out, EPS_PLACE)
+    P = info["P"].copy()
+    # a row with no allowance and an element of large weight
+    i = int(np.flatnonzero(allow == 0.0)[0])
+    j = int(np.argmax(P[i]))
+    # one grid step at that element's binade, in P~ units
+    step = np.ldexp(1.0, int(np.floor(np.log2(P[i, j]))) - f.mbits)
+    P[i, j] -= step
+    k_out = out.copy()
+    k_out[i] = P[i] @ info["v_hat"] / P[i].sum()
+    ex, _ = excess_rel_l2(k_out, out, info, fmt, EPS_PLACE)
+    assert ex == pytest.approx(O.rel_l2(k_out, out), rel=1e-12)
+    assert ex > 0.0
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_block_moved_across_its_binade_tie_is_absorbed(fmt):
+    """Each row's largest block has its largest value delta/2 above the tie
+    that decides its binade, below the guess (so every row's offset stays
+    0): a kernel with t lower by delta puts that whole block one binade lower
+    and re-rounds every code on the other grid; the allowance covers it, and
+    without its tied-block term it would not."""
+    info0, _ = _case(fmt)
+    M = O.FORMATS[fmt].mbits
+    s, vis, vh = info0["scores"], info0["visible"], info0["v_hat"]
+    R, S = s.shape
+    delta = 0.8 * EPS
+    t_tie = -1.0 - 2.0 ** -(M + 1)                 # binade -1 rounds up to 0 above this
+    m = s.max(axis=1) - (t_tie + delta / 2)        # the row's largest score at the tie
+    top = s.reshape(R, S // 32, 32).max(axis=2).argmax(axis=1)
+    fp = fused_probabilities(s, m, vis, fmt)
+    assert np.all(fp["kappa"] == 0)
+    P = fp["P"]
+    info = dict(fp)
+    info.update(m_tilde=m, l=P.sum(axis=1), scores=s, v_hat=vh, visible=vis)
+    out = P @ vh / info["l"][:, None]
+    kp = fused_probabilities(s, m + delta, vis, fmt)
+    rr = np.arange(R)
+    assert np.all(kp["delta"][rr, top] == fp["delta"][rr, top] + 1)   # the top blocks moved
+    k_out = kp["P"] @ vh / kp["P"].sum(axis=1)[:, None]
+    plain = O.rel_l2(k_out, out)
+    ex, _ = excess_rel_l2(k_out, out, info, fmt, EPS)
+    assert plain > 0.0 and ex <= 1e-3 * plain, (ex, plain)
