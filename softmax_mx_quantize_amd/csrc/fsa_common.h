@@ -149,34 +149,6 @@ __device__ __forceinline__ v4f row_sum(const v4i& ones, const opv<F>& p, const v
     return mfma_scale_v4(ones, p, c, Fmt<FMT_E2M1>::mfma, Fmt<F>::mfma, 0, 127, 0, sp);
 }
 
-// Cross-lane exchanges on the vector unit (v_permlane16/32_swap; the swap
-// trades the odd 16-lane rows of its first operand with the even rows of its
-// second, resp. the upper 32 lanes of the first with the lower 32 of the
-// second), so that the epilogue waits on no LDS round trip.
-// x of lane ^ 48 for lane groups 1 and 2 (rows 1 and 2 trade places); the
-// result is unspecified in groups 0 and 3.
-__device__ __forceinline__ int swap_rows12(int x, int g) {
-  const auto h = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
-  // h[0] rows: x0 x1 x0 x1; h[1] rows: x2 x3 x2 x3
-  const auto q = __builtin_amdgcn_permlane16_swap((uint32_t)h[0], (uint32_t)h[1], false, false);
-  // q[0] rows: x0 x2 x0 x2; q[1] rows: x1 x3 x1 x3
-  return (int)(g == 1 ? q[0] : q[1]);
-}
-
-// Scale operand of the P~ B operand.  FP6/FP4: the lane's own block.  FP8:
-// lane group c supplies the scale of key block c; blocks 0/2 are the low/high
-// halves held by groups 0-1, blocks 1/3 those held by groups 2-3, so groups
-// 1 and 2 take the value from the lane 48 apart (a branch-free exchange).
-template <int BITS>
-__device__ __forceinline__ int p_scale(int s_lo, int s_hi, int g) {
-  if (BITS != 8) return s_lo;
-  const int give = g >= 2 ? s_lo : s_hi;            // what the partner needs
-  const int got = swap_rows12(give, g);
-  const int own = g < 2 ? s_lo : s_hi;
-  const bool cross = (g == 1) | (g == 2);
-  return cross ? got : own;
-}
-
 // The lane's Q' operand of the score product, MX-quantised here from the
 // bf16 row (the same rule as the quantiser: OCP floor scale, RNE, saturation,
 // NaN/Inf blocks get scale 0xFF and zero codes) with Q' = fp32(q * mult).
@@ -186,61 +158,37 @@ __device__ __forceinline__ int p_scale(int s_lo, int s_hi, int g) {
 // NaN).
 template <int F, int D, int RAISE>
 __device__ __forceinline__ opv<F> q_operand(const uint16_t* row, float mult, int g, int& sc) {
-  constexpr int BITS = Fmt<F>::bits;
+  static_assert(Fmt<F>::bits != 8, "FP8 Q' operands: q_operand32_e4m3");
   float v[32];
-  bool bad_lo = false, bad_hi = false;
-  // element k of the operand: FP6/FP4 column 32g + k; FP8 column 16g + k
-  // (k < 16) and 64 + 16g + (k - 16)
-  auto column = [&](int k) { return BITS == 8 ? (k < 16 ? 16 * g + k : 64 + 16 * g + k - 16) : 32 * g + k; };
+  bool bad = false;
+  // element k of the operand: column 32g + k
 #pragma unroll
   for (int c = 0; c < 4; ++c) {                      // four 8-element chunks
-    const int col = column(8 * c);
+    const int col = 32 * g + 8 * c;
     uint4 w = make_uint4(0, 0, 0, 0);
     if (row != nullptr && col < D) w = *reinterpret_cast<const uint4*>(row + col);
     const uint32_t h[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t lo = h[e] & 0xFFFF, hi = h[e] >> 16;
-      const bool nan_inf = ((lo & 0x7F80) == 0x7F80) | ((hi & 0x7F80) == 0x7F80);
-      if (c < 2) bad_lo |= nan_inf; else bad_hi |= nan_inf;
+      bad |= ((lo & 0x7F80) == 0x7F80) | ((hi & 0x7F80) == 0x7F80);
       v[8 * c + 2 * e] = bf16_bits_to_float(lo) * mult;
       v[8 * c + 2 * e + 1] = bf16_bits_to_float(hi) * mult;
     }
   }
-  float a_lo = 0.0f, a_hi = 0.0f;
+  float amax = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    a_lo = __builtin_fmaxf(a_lo, __builtin_fabsf(v[k]));
-    a_hi = __builtin_fmaxf(a_hi, __builtin_fabsf(v[16 + k]));
-  }
-  if (BITS == 8) {
-    // each MX block is two half blocks held by lanes 16 apart
-    a_lo = __builtin_fmaxf(a_lo, __shfl_xor(a_lo, 16));
-    a_hi = __builtin_fmaxf(a_hi, __shfl_xor(a_hi, 16));
-    bad_lo |= __shfl_xor((int)bad_lo, 16) != 0;
-    bad_hi |= __shfl_xor((int)bad_hi, 16) != 0;
-  } else {
-    a_lo = a_hi = __builtin_fmaxf(a_lo, a_hi);
-    bad_lo = bad_hi = bad_lo | bad_hi;
-  }
-  auto scale_exp = [](float amax) {
-    int X = amax > 0.0f ? floor_log2(amax) - Fmt<F>::emax : -127;
-    return X < -127 ? -127 : (X > 127 ? 127 : X);
-  };
-  const int x_lo = scale_exp(a_lo), x_hi = scale_exp(a_hi);
+  for (int k = 0; k < 32; ++k) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[k]));
+  int x = amax > 0.0f ? floor_log2(amax) - Fmt<F>::emax : -127;
+  x = x < -127 ? -127 : (x > 127 ? 127 : x);
   float y[32];
 #pragma unroll
-  for (int k = 0; k < 32; ++k) y[k] = __builtin_ldexpf(v[k], -(k < 16 ? x_lo : x_hi));
+  for (int k = 0; k < 32; ++k) y[k] = __builtin_ldexpf(v[k], -x);
   uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   Pack32<F, true>::run(y, w);
-  if (bad_lo) { for (int i = 0; i < 4; ++i) w[i] = 0; }
-  if (bad_hi) { for (int i = 4; i < 8; ++i) w[i] = 0; }
-  if (BITS != 8 && bad_lo) { for (int i = 0; i < 8; ++i) w[i] = 0; }
-  auto raised = [](int x, bool bad) { return bad ? 255 : min(x + 127 + RAISE, 254); };
-  int s_lo = raised(x_lo, bad_lo), s_hi = raised(x_hi, bad_hi);
-  if (BITS == 8 && D < 128) s_hi = 127;                // blocks past D: zeros
-  if (BITS != 8 && 32 * g >= D) s_lo = s_hi = 127;
-  sc = p_scale<BITS>(s_lo, s_hi, g);
+  if (bad) { for (int i = 0; i < 8; ++i) w[i] = 0; }
+  sc = bad ? 255 : min(x + 127 + RAISE, 254);
+  if (32 * g >= D) sc = 127;                          // blocks past D: zeros
   opv<F> o;
 #pragma unroll
   for (int i = 0; i < Operand<F>::words; ++i) o[i] = (int)w[i];

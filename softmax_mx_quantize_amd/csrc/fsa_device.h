@@ -101,14 +101,6 @@ template <> struct Operand<FMT_E2M1> { typedef v4i type; static constexpr int wo
 template <> struct Operand<FMT_E3M2> { typedef v6i type; static constexpr int words = 6; };
 template <int F> using opv = typename Operand<F>::type;
 
-template <int F>
-__device__ __forceinline__ opv<F> zero_operand() {
-  opv<F> o;
-#pragma unroll
-  for (int i = 0; i < Operand<F>::words; ++i) o[i] = 0;
-  return o;
-}
-
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t b) {
   return __uint_as_float(b << 16);
 }
@@ -119,11 +111,6 @@ __device__ __forceinline__ int floor_log2(float a) {
   int e = (int)((u >> 23) & 0xFF);
   if (e != 0) return e - 127;
   return (31 - __clz(u & 0x7FFFFF)) - 149;
-}
-
-// 2^n as float for -126 <= n <= 127.
-__device__ __forceinline__ float exp2i(int n) {
-  return __uint_as_float((uint32_t)(n + 127) << 23);
 }
 
 // Convert 32 fp32 values to packed element codes: each value is divided by

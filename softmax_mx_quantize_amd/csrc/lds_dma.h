@@ -33,10 +33,6 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 }
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// Wait until at most N of this wave's memory loads are still outstanding
-// (loads complete in issue order for the counter).
-template <int N>
-__device__ __forceinline__ void wait_dma_keep() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 // Workgroup barrier for the LDS ring.  __syncthreads() releases at
 // workgroup scope, which makes the compiler wait for every LDS DMA still in
 // flight (vmcnt(0)) and so drains the prefetch ring at each tile.  Here the
