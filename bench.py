@@ -56,10 +56,16 @@ KERNEL_SOURCES = ("softmax_mx_quantize_amd/csrc/fsa_common.h",
 
 
 def kernel_hash() -> str:
+    """Hash of the kernel sources' code: comments and whitespace are left
+    out, so that editing a comment does not invalidate stored counters."""
+    import re
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -736,7 +736,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int b, const 
   using I1 = std::integral_constant<int, 1>;
   // Tile t+1 lands while tile t is read; after the barrier that ends step t
   // its stages take tile t+2.
-  // One tile in three fenced phases: the scores of chunk 0; those of chunk 1
+  // One tile in four phases split by fences: the scores of chunk 0; those of chunk 1
   // beside the epilogue of chunk 0; the P V products of chunk 0 beside the
   // epilogue of chunk 1; then those of chunk 1.  Left unfenced, the
   // scheduler interleaves further and lengthens live ranges until registers
