@@ -262,6 +262,34 @@ def test_workspace_grows_and_is_released():
     assert torch.equal(b.view(torch.int16), d.view(torch.int16))
 
 
+
+def test_side_stream_calls_match_default_stream():
+    """Calls on a stream other than the default one, with the workspace
+    growing twice there (each old buffer freed on the stream that used it),
+    give the default stream's results bit for bit; a later call back on the
+    default stream does too."""
+    import torch
+    import softmax_mx_quantize_amd as fsa
+    announce("fsa side stream")
+    small = [to_dev(W.random_bf16((1, 2, 200, 128), seed, 1.0)) for seed in (111, 112, 113)]
+    large = [to_dev(W.random_bf16((1, 8, 3000, 128), seed, 1.0)) for seed in (114, 115, 116)]
+    ref_small = fsa.attention_fwd(*small, "e4m3")
+    ref_large = fsa.attention_fwd(*large, "e4m3")
+    torch.cuda.synchronize()
+    fsa.release_workspace()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        a = fsa.attention_fwd(*small, "e4m3")
+        b = fsa.attention_fwd(*large, "e4m3")
+        c = fsa.attention_fwd(*small, "e4m3")
+    side.synchronize()
+    torch.cuda.current_stream().wait_stream(side)
+    d = fsa.attention_fwd(*large, "e4m3")
+    torch.cuda.synchronize()
+    for got, want in ((a, ref_small), (b, ref_large), (c, ref_small), (d, ref_large)):
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+
 def test_skip_fallback_pass_hook():
     """Without the fallback pass, rows beyond the in-sweep shifts keep the
     first pass's offsets (65 binades or more); every other row is unchanged."""
