@@ -172,7 +172,7 @@ int piece_fset(const Call& c, const Piece& p) {
 // format present) and, when the caller gives no per-row arrays, its rows'
 // kappa and frozen max.
 struct PieceLayout {
-  size_t kc, ks, vc, vs, rk, rm;
+  size_t kc, ks, vc, vs, rk, rm, nk;
   int64_t kc_slab, vc_slab;
 };
 
@@ -186,6 +186,7 @@ PieceLayout carve_piece(Carver& cv, const Call& c, const Piece& p, bool own_rows
   l.ks = cv.take((size_t)(nbh * c.sk_alloc * (c.D / 32)));
   l.vc = cv.take((size_t)(nbh * l.vc_slab));
   l.vs = cv.take((size_t)(nbh * c.D * (c.sk_alloc / 32)));
+  l.nk = cv.take((size_t)nbh * sizeof(uint64_t));
   if (own_rows) {
     l.rk = cv.take((size_t)nbh * c.S * 4);
     l.rm = cv.take((size_t)nbh * c.S * 4);
@@ -205,17 +206,9 @@ int quantize_piece(const Call& c, const Piece& p, uint8_t* base, const PieceLayo
   a.mult = 1.0f;
   for (int j = 0; j < p.n; ++j) a.fmt[j] = (uint8_t)kern_fmt(c.fmt[p.h0 + j]);
   const int fset = piece_fset(c, p);
-  // K: output rows are keys (padded to sk_alloc), blocks along D
-  a.x = c.k + p.b0 * c.st.k[0] + p.h0 * c.st.k[1];
-  a.x_sb = c.st.k[0]; a.x_sh = c.st.k[1]; a.x_sr = c.st.k[2];
-  a.codes = base + l.kc;
-  a.scales = base + l.ks;
-  a.out_rows = c.sk_alloc;
-  a.nb_out = c.D / 32;
-  a.code_slab = l.kc_slab;
-  a.scale_layout = fsa::SCALES_KEY_TILES;
-  a.key8 = c.px == 1;              // FP8 key order for E4M3 P~ only
-  if (fsa::launch_mx_quant(a, fset, 0, c.stream) != hipSuccess) return FSA_ERR_HIP;
+  // V first: its launch also clears each head's NaN-key slot, which K's
+  // launch then lowers to the first key row holding NaN or Inf
+  a.nan_key = reinterpret_cast<uint64_t*>(base + l.nk);
   // V: output rows are the D columns, blocks along the keys
   a.x = c.v + p.b0 * c.st.v[0] + p.h0 * c.st.v[1];
   a.x_sb = c.st.v[0]; a.x_sh = c.st.v[1]; a.x_sr = c.st.v[2];
@@ -226,7 +219,20 @@ int quantize_piece(const Call& c, const Piece& p, uint8_t* base, const PieceLayo
   a.code_slab = l.vc_slab;
   a.scale_layout = fsa::SCALES_DIM_TILES;
   a.key8 = 0;
+  a.nan_init = 1;                  // clears each head's NaN-key slot for K's launch
   if (fsa::launch_mx_quant(a, fset, 1, c.stream) != hipSuccess) return FSA_ERR_HIP;
+  // K: output rows are keys (padded to sk_alloc), blocks along D
+  a.x = c.k + p.b0 * c.st.k[0] + p.h0 * c.st.k[1];
+  a.x_sb = c.st.k[0]; a.x_sh = c.st.k[1]; a.x_sr = c.st.k[2];
+  a.codes = base + l.kc;
+  a.scales = base + l.ks;
+  a.out_rows = c.sk_alloc;
+  a.nb_out = c.D / 32;
+  a.code_slab = l.kc_slab;
+  a.scale_layout = fsa::SCALES_KEY_TILES;
+  a.key8 = c.px == 1;              // FP8 key order for E4M3 P~ only
+  a.nan_init = 0;                  // rows with NaN/Inf blocks: atomic minimum
+  if (fsa::launch_mx_quant(a, fset, 0, c.stream) != hipSuccess) return FSA_ERR_HIP;
   return FSA_OK;
 }
 
@@ -247,6 +253,7 @@ int attend_piece(const Call& c, const Piece& p, uint8_t* base, const PieceLayout
   a.kc = base + l.kc; a.ks = base + l.ks;
   a.vc = base + l.vc; a.vs = base + l.vs;
   a.kc_slab = l.kc_slab; a.vc_slab = l.vc_slab;
+  a.nan_key = reinterpret_cast<const uint64_t*>(base + l.nk);
   const int64_t boff = (int64_t)p.b0 * c.H;            // first head row of the piece's batch entries
   if (whole) {
     a.row_kappa = rk + boff * c.S;

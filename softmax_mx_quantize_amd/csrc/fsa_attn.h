@@ -881,7 +881,13 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int b, const 
   const int qe = q_wave + (lane_e & 31);
   const int he = lane_e >> 5;
   if (qe < S && (!REBASE || kap_in > EXT)) {
-    const float inv = 1.0f / lsum;
+    // A key holding NaN or Inf (its K^ block scale is NaN) makes every score
+    // against it NaN, which the truncating conversion would turn into a zero
+    // probability: rows that see such a key are written NaN instead, as
+    // softmax propagates it.  The quantiser recorded the first such key.
+    const uint64_t nk = a.nan_key[wi];
+    const bool poisoned = CAUSAL ? nk <= (uint64_t)qe : nk < (uint64_t)S;
+    const float inv = poisoned ? __builtin_nanf("") : 1.0f / lsum;
     uint16_t* orow = a.out + b * a.o_sb + h * a.o_sh + (int64_t)qe * a.o_ss;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)

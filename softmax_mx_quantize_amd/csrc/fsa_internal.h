@@ -33,6 +33,12 @@ struct QuantArgs {
   float mult;            // every input value is multiplied by this (fp32) first
   int scale_layout;      // SCALES_* below
   int key8;              // KEY_TILES in the FP8 key order whatever the codes (E4M3 P~)
+  // Per slab, the first row of a block holding NaN or Inf (the attention
+  // path's K^: every score against that key is NaN).  Rows mode: atomic
+  // minimum of the row over such blocks; columns mode with nan_init: set to
+  // all ones first (the call launches V's quantiser before K's).  Null: off.
+  uint64_t* nan_key;
+  int nan_init;
   uint8_t fmt[MAX_HEAD_TABLE];  // element format (FMT_*) of head slot w % nh
 };
 
@@ -97,6 +103,7 @@ struct AttnArgs {
   uint64_t* fb_flag;             // stamped with call_id when a row needs the fallback
   uint64_t call_id;              // unique per call (never 0)
   int skip_fallback;             // 1: no fallback-pass launch (rows beyond EXT stay wrong)
+  const uint64_t* nan_key;       // per slab: first key row with a NaN/Inf K^ block (~0: none)
   uint8_t hfmt[MAX_HEAD_TABLE];  // element format (FMT_*) of head h0 + j
   uint8_t horder[MAX_HEAD_TABLE];  // head slot -> j: the order workgroups take heads in
 };

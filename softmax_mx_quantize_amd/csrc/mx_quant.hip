@@ -119,6 +119,7 @@ __global__ void __launch_bounds__(256) mx_quant_rows_kernel(QuantArgs a) {
       v[j] = bf16_bits_to_float(bits) * a.mult;
     }
   }
+  if (bad && a.nan_key) atomicMin(reinterpret_cast<unsigned long long*>(a.nan_key + w), (unsigned long long)r);
   const int f = (FSET & (FSET - 1)) ? a.fmt[w % a.nh] : 0;
   with_format<FSET>(f, [&](auto F) { quantize_block<decltype(F)::value>(a, v, bad, w, r, b); });
 }
@@ -138,6 +139,7 @@ __global__ void __launch_bounds__(128) mx_quant_cols_kernel(QuantArgs a) {
   __shared__ __align__(16) uint16_t tile[QC_ROWS][QC_COLS];
   const int t = threadIdx.x;
   const int64_t w = a.batch0 + blockIdx.z;
+  if (a.nan_init && blockIdx.x == 0 && blockIdx.y == 0 && t == 0) a.nan_key[w] = ~0ull;
   const int64_t col0 = (int64_t)blockIdx.y * QC_COLS;
   const int64_t row0 = (int64_t)blockIdx.x * QC_ROWS;
   const uint16_t* src = slab_input(a, w);
