@@ -290,6 +290,32 @@ def test_side_stream_calls_match_default_stream():
     for got, want in ((a, ref_small), (b, ref_large), (c, ref_small), (d, ref_large)):
         assert torch.equal(got.view(torch.int16), want.view(torch.int16))
 
+
+@pytest.mark.parametrize("case", ["q_zero", "k_zero", "v_const"])
+def test_degenerate_inputs(case):
+    """All-zero queries or keys (every score 0: uniform weights, the output
+    is the mean of V^ over the visible keys) and a constant V (the output is
+    that constant once quantised: -3.25 in E4M3 and E2M3, -3 in E2M1):
+    against the oracle in every format, causal or not."""
+    announce("fsa degenerate", case)
+    S, D = 333, 128
+    for fmt in FMTS:
+        for causal in (False, True):
+            q, k, v = (W.random_bf16((1, 2, S, D), seed, 1.3) for seed in (131, 132, 133))
+            if case == "q_zero":
+                q[:] = 0
+            elif case == "k_zero":
+                k[:] = 0
+            else:
+                v[:] = W.f32_to_bf16_bits(np.full(v.shape, -3.25, np.float32))
+            g, kap, mg = _run(q, k, v, fmt, causal)
+            ref, kaps, border, infos = _oracle_heads(q, k, v, [fmt] * 2, causal)
+            _check(g, kap, mg, ref, kaps, border, infos)
+            if case == "v_const":
+                c = ref.ravel()[0]
+                assert c == (-3.0 if fmt == "e2m1" else -3.25)
+                assert np.all(ref == c) and np.all(g == c)
+
 def test_skip_fallback_pass_hook():
     """Without the fallback pass, rows beyond the in-sweep shifts keep the
     first pass's offsets (65 binades or more); every other row is unchanged."""
