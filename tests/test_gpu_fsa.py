@@ -67,8 +67,13 @@ def _check(gpu_out, gpu_kap, gpu_mg, ref_out, ref_kap, border, infos, rows=None)
     num = 0.0
     for x in range(B * H):
         info, fmt = infos[x]
+        # the guess is evaluated in fp32 from fp32 scores, so its error scales
+        # with the window's largest score, not with the guess itself (which
+        # can be near zero: mean + z std of two keys of -1.7 and -4.3)
+        win = info["visible"][:, :128]
+        mag = np.max(np.where(win, np.abs(info["scores"][:, :128]), 0.0), axis=1)
         dm = np.abs(mg[x] - info["m_tilde"])
-        assert np.all(dm <= 1e-4 * np.maximum(1.0, np.abs(info["m_tilde"]))), dm.max()
+        assert np.all(dm <= 1e-4 * np.maximum(1.0, np.maximum(np.abs(info["m_tilde"]), mag))), dm.max()
         ex, _ = excess_rel_l2(g[x], ref_out[x], info, fmt, eps_rows(mg[x], info))
         num += (ex * np.linalg.norm(ref_out[x])) ** 2
     err = float(np.sqrt(num) / np.linalg.norm(ref_out))

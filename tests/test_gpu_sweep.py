@@ -1,0 +1,54 @@
+"""A seeded sweep of mixed call shapes against the float64 oracle, all rows.
+
+Each case draws B in {1, 2}, H in {1, 2, 3} (per-head formats drawn
+independently, so most multi-head cases are hybrid launches), S in [1, 700]
+(ragged key and query tiles), D in {64, 128}, causal or not, an input scale
+(score spread) and a frozen-max bias: 0, or a lowered guess that sends rows
+through the in-sweep shifts (-8 binades) or the second pass (-100).  The
+bar is the one of the other parity tests (tests/parity.py).
+"""
+
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_helpers import announce
+from test_gpu_fsa import _run, _oracle_heads, _check
+
+pytestmark = pytest.mark.gpu
+FMTS = ["e4m3", "e2m3", "e2m1"]
+
+
+def _cases(n=48, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        B = int(rng.integers(1, 3))
+        H = int(rng.integers(1, 4))
+        S = int(rng.integers(1, 701))
+        D = int(rng.choice([64, 128]))
+        causal = bool(rng.integers(0, 2))
+        fmts = [FMTS[int(j)] for j in rng.integers(0, 3, size=H)]
+        scale = float(rng.uniform(0.5, 2.5))
+        bias = float(rng.choice([0.0, 0.0, -8.0, -100.0]))
+        out.append((i, B, H, S, D, causal, tuple(fmts), scale, bias))
+    return out
+
+
+CASES = _cases()
+
+
+def _id(c):
+    i, B, H, S, D, causal, fmts, scale, bias = c
+    return "c%02d-B%dH%dS%dD%d%s-%s-x%.1f-b%g" % (i, B, H, S, D, "-causal" if causal else "",
+                                                   "+".join(fmts), scale, bias)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[_id(c) for c in CASES])
+def test_mixed_shapes_all_rows(case):
+    i, B, H, S, D, causal, fmts, scale, bias = case
+    announce("fsa sweep", _id(case))
+    q, k, v = (W.random_bf16((B, H, S, D), 500 + 3 * i + j, scale if j < 2 else 1.0)
+               for j in range(3))
+    g, kap, mg = _run(q, k, v, fmts[0], causal, head_fmt=list(fmts), guess_bias=bias)
+    _check(g, kap, mg, *_oracle_heads(q, k, v, list(fmts), causal, bias=bias))
