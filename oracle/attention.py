@@ -245,10 +245,13 @@ def fused_probabilities(s: np.ndarray, m_tilde: np.ndarray, vis: np.ndarray,
     * "block" (step 5): each 32-key block shifted to the placement binade.
     * "row": one scale for the whole row, Delta = 0 in every block (E4M3
       only: its 17 binades leave no block of a softmax row needing a shift
-      of its own).  A row falls back only when its largest value,
+      of its own).  A row falls back when its largest value,
       mitchell_exp2(t_max + pl), reaches the format's overflow threshold
-      (464 for E4M3: it would round beyond 448); it is then recomputed with
-      kappa = max_b e_b whole binades.  Otherwise kappa = 0.
+      (464 for E4M3: it would round beyond 448), or when that value rounds
+      to zero (a guess so far above the row that the row scale flushes every
+      code, which would leave l = 0); it is then recomputed with
+      kappa = max_b e_b whole binades (negative in the second case).
+      Otherwise kappa = 0.
     * "efq" (E2M1 only): the codes come from a single affine rule in the
       code domain (EFQ-Softmax: Exp-Free Quantization for Softmax, abstract:
       an exponent-only block scale from the local maximum, then nonnegative
@@ -280,8 +283,11 @@ def fused_probabilities(s: np.ndarray, m_tilde: np.ndarray, vis: np.ndarray,
     emax = np.max(e, axis=1) if e.size else np.full(R, -np.inf)
     if mode == "row":
         tmax = np.where(vis, t, -np.inf).max(axis=1) if S else np.full(R, -np.inf)
-        over = mitchell_exp2(tmax + pl) >= overflow_threshold(f)
-        kappa = np.where(over, emax, 0.0)
+        with np.errstate(over="ignore"):
+            top = mitchell_exp2(tmax + pl)
+        over = top >= overflow_threshold(f)
+        flush = np.isfinite(tmax) & (round_to_format(top, f) == 0.0)
+        kappa = np.where(over | flush, emax, 0.0)
         delta = np.zeros_like(e)
     else:
         kappa = np.maximum(0.0, emax)

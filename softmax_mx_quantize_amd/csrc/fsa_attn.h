@@ -818,7 +818,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int b, const 
     } else {
       km = block_binade<MB>(tm);
     }
-    kap_x = km > 0 ? km : 0;
+    // one scale per row re-bases a flushed row downwards too (negative kappa)
+    kap_x = PM == PM_ROW || km > 0 ? km : 0;
     // restart the ring for the sweep from the raised reference
     issue_k(0, kl0);
     issue_v(0, vl0);
@@ -867,10 +868,12 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int b, const 
   if constexpr (L32) lsum = L[0];
   else lsum = __shfl(L[0], n < 16 ? n : n + 16);
   // one scale per row: a code past the format's range in either half of the
-  // row sends it to the fallback pass, which measures its offset
+  // row, or a row whose every code flushed to zero (a guess so far above it
+  // that the row sum is 0), sends it to the fallback pass, which measures
+  // its offset
   if constexpr (PM == PM_ROW && !REBASE) {
     const uint32_t ov = (over | (uint32_t)__shfl_xor((int)over, 32)) & 0x80808080u;
-    kap = ov ? KSAT : 0;
+    kap = ov || lsum == 0.0f ? KSAT : 0;
   }
 
   // ---- normalise and store: register i of O[db] is d = 32 db + 8 (i/4) + 4h + i%4.

@@ -5,7 +5,8 @@ independently, so most multi-head cases are hybrid launches), S in [1, 700]
 (ragged key and query tiles), D in {64, 128}, causal or not, an input scale
 (score spread) and a frozen-max bias: 0, or a lowered guess that sends rows
 through the in-sweep shifts (-8 binades) or the second pass (-100).  The
-bar is the one of the other parity tests (tests/parity.py).
+bar is the one of the other parity tests (tests/parity.py).  A second sweep
+draws the same kinds of shapes for each P~ variant (one format per call).
 """
 
 import numpy as np
@@ -14,6 +15,7 @@ import pytest
 import workloads as W
 from gpu_helpers import announce
 from test_gpu_fsa import _run, _oracle_heads, _check
+from test_gpu_variants import VARIANTS, _run as _vrun, _check as _vcheck
 
 pytestmark = pytest.mark.gpu
 FMTS = ["e4m3", "e2m3", "e2m1"]
@@ -52,3 +54,38 @@ def test_mixed_shapes_all_rows(case):
                for j in range(3))
     g, kap, mg = _run(q, k, v, fmts[0], causal, head_fmt=list(fmts), guess_bias=bias)
     _check(g, kap, mg, *_oracle_heads(q, k, v, list(fmts), causal, bias=bias))
+
+
+def _variant_cases(per=4, seed=2025):
+    rng = np.random.default_rng(seed)
+    out = []
+    for vi, var in enumerate(VARIANTS):
+        for r in range(per):
+            B = int(rng.integers(1, 3))
+            H = int(rng.integers(1, 3))
+            S = int(rng.integers(1, 601))
+            D = int(rng.choice([64, 128]))
+            causal = bool(rng.integers(0, 2))
+            scale = float(rng.uniform(0.5, 2.5))
+            bias = float(rng.choice([0.0, 0.0, -8.0, -100.0]))
+            out.append((vi * per + r, var, B, H, S, D, causal, scale, bias))
+    return out
+
+
+VCASES = _variant_cases()
+
+
+def _vid(c):
+    i, var, B, H, S, D, causal, scale, bias = c
+    return "v%02d-%s-%s-B%dH%dS%dD%d%s-x%.1f-b%g" % (i, var[0], var[1], B, H, S, D,
+                                                    "-causal" if causal else "", scale, bias)
+
+
+@pytest.mark.parametrize("case", VCASES, ids=[_vid(c) for c in VCASES])
+def test_variant_mixed_shapes_all_rows(case):
+    i, (name, fmt, okw, pfmt, mode), B, H, S, D, causal, scale, bias = case
+    announce("fsa variant sweep", _vid(case))
+    q, k, v = (W.random_bf16((B, H, S, D), 900 + 3 * i + j, scale if j < 2 else 1.0)
+               for j in range(3))
+    g, kap, mg = _vrun(q, k, v, fmt, name, causal, guess_bias=bias)
+    _vcheck(g, kap, mg, q, k, v, fmt, okw, pfmt, mode, causal, bias=bias)

@@ -85,8 +85,11 @@ def _check(g, kap, mg, q, k, v, fmt, okw, pfmt, mode, causal=False, rows=None, b
                                           return_info=True, **okw)
             rws = np.arange(S) if rows is None else np.asarray(rows)
             gr, kr, mr = g[b, h, rws], kap[b, h, rws], mg[b, h, rws]
+            # fp32 guess from fp32 scores: its error follows the window's scores
+            win = info["visible"][:, :128]
+            mag = np.max(np.where(win, np.abs(info["scores"][:, :128]), 0.0), axis=1)
             dm = np.abs(mr - info["m_tilde"])
-            assert np.all(dm <= 1e-4 * np.maximum(1.0, np.abs(info["m_tilde"]))), dm.max()
+            assert np.all(dm <= 1e-4 * np.maximum(1.0, np.maximum(np.abs(info["m_tilde"]), mag))), dm.max()
             ex, _ = excess_rel_l2(gr, ref, info, pfmt, eps_rows(mr, info), mode)
             num += (ex * np.linalg.norm(ref)) ** 2
             den += np.linalg.norm(ref) ** 2
@@ -119,6 +122,19 @@ def test_variant_fallbacks(variant):
         g, kap, mg = _run(q, k, v, fmt, name, guess_bias=bias)
         assert np.all(kap > 0)
         _check(g, kap, mg, q, k, v, fmt, okw, pfmt, mode, bias=bias)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_row_scale_guess_far_above(causal):
+    """One scale per row with the guess 32 binades above every row: each
+    code would flush to zero (a zero row sum); the row falls back and is
+    re-based downwards by its own top binade (negative kappa)."""
+    announce("variant row, guess far above", causal)
+    okw, pfmt, mode = dict(p_mode="row"), "e4m3", "row"
+    q, k, v = (W.random_bf16((1, 2, 333, 128), seed, 1.0) for seed in (94, 95, 96))
+    g, kap, mg = _run(q, k, v, "e4m3", "row", causal, guess_bias=32.0)
+    assert np.all(np.isfinite(g)) and np.all(kap < 0)
+    _check(g, kap, mg, q, k, v, "e4m3", okw, pfmt, mode, causal, bias=32.0)
 
 
 @pytest.mark.parametrize("variant", VARIANTS, ids=IDS)

@@ -323,23 +323,48 @@ def test_whole_binade_guess_shift_is_exact(fmt):
 def test_variant_row_scale_closed_form_and_fallback():
     """One scale per row: every element is mitchell(t + pl) rounded, with no
     block shift; a row falls back exactly when its largest value reaches
-    464 (it would round past 448), and then by its top block's binade."""
+    464 (it would round past 448) or rounds to zero (every code flushed),
+    and then by its top block's binade."""
     f = FORMATS["e4m3"]
     table = decode(np.arange(f.max_code + 1), f)
     rng = np.random.default_rng(31)
-    s = rng.normal(0.0, 3.0, (6, 64))
-    m = s.max(axis=1) + np.array([0.3, 0.0, -0.5, -1.8, -1.9, -4.0])
+    s = rng.normal(0.0, 3.0, (8, 64))
+    m = s.max(axis=1) + np.array([0.3, 0.0, -0.5, -1.8, -1.9, -4.0, 18.0, 25.0])
     vis = np.ones_like(s, bool)
     fp = fused_probabilities(s, m, vis, "e4m3", mode="row")
     assert np.all(fp["delta"] == 0)
-    for i in range(6):
+    for i in range(8):
         t = s[i] - m[i]
         over = _mitchell_value(max(t) + 7) >= 464.0
-        assert fp["kappa"][i] == (math.floor(round(8 * max(t)) / 8) if over else 0), i
+        flush = _nearest(table, _mitchell_value(max(t) + 7)) == 0.0
+        assert fp["kappa"][i] == (math.floor(round(8 * max(t)) / 8) if over or flush else 0), i
         for j in range(64):
             want = _nearest(table, min(_mitchell_value(t[j] - fp["kappa"][i] + 7), 896.0)) * 2.0 ** -7
             assert fp["P"][i, j] == want, (i, j)
     assert list(fp["kappa"][:3]) == [0, 0, 0] and fp["kappa"][4] >= 1 and fp["kappa"][5] >= 4
+    # 18 and 25 binades above the row: every code would flush; the fallback
+    # brings the top block back to the placement binade
+    assert fp["kappa"][6] <= -18 and fp["kappa"][7] <= -25
+    assert np.all(fp["P"][6:].max(axis=1) >= 1.0)
+
+
+def test_variant_row_scale_fallback_forgets_the_guess():
+    """A row that falls back, on either side (guess 48 binades low: its top
+    value overflows; 32 or 40 binades high: every code flushes), is
+    recomputed from its own top binade, so its output no longer depends on
+    the guess.  The biases keep every guess in one fp32 binade, [32, 64) in
+    magnitude, so that the guesses differ by whole binades exactly."""
+    q, k, v = (W.random_bf16((200, 64), 300 + j, 1.0) for j in range(3))
+    qh, kh, vh = (W.bf16_bits_to_f64(x) for x in (q, k, v))
+    res = {b: O.fused_attention(qh, kh, vh, "e4m3", bias=b, return_info=True, p_mode="row")
+           for b in (-48.0, 32.0, 40.0)}
+    out0, info0 = O.fused_attention(qh, kh, vh, "e4m3", bias=0.0, return_info=True, p_mode="row")
+    assert np.all((info0["m_tilde"] >= 0.0) & (info0["m_tilde"] < 16.0))
+    for b, (o, info) in res.items():
+        assert np.all(np.isfinite(o)) and np.all(info["l"] > 0)
+        assert np.array_equal(o, res[32.0][0]), b
+        assert np.array_equal(info["kappa"], res[32.0][1]["kappa"] + 32 - int(b)), b
+    assert np.all(res[32.0][1]["kappa"] < 0) and np.all(res[-48.0][1]["kappa"] > 0)
 
 
 def test_variant_affine_codes_closed_form():
