@@ -247,11 +247,8 @@ def fused_probabilities(s: np.ndarray, m_tilde: np.ndarray, vis: np.ndarray,
       only: its 17 binades leave no block of a softmax row needing a shift
       of its own).  A row falls back when its largest value,
       mitchell_exp2(t_max + pl), reaches the format's overflow threshold
-      (464 for E4M3: it would round beyond 448), or when that value rounds
-      to zero (a guess so far above the row that the row scale flushes every
-      code, which would leave l = 0); it is then recomputed with
-      kappa = max_b e_b whole binades (negative in the second case).
-      Otherwise kappa = 0.
+      (464 for E4M3: it would round beyond 448); it is then recomputed with
+      kappa = max_b e_b whole binades.  Otherwise kappa = 0.
     * "efq" (E2M1 only): the codes come from a single affine rule in the
       code domain (EFQ-Softmax: Exp-Free Quantization for Softmax, abstract:
       an exponent-only block scale from the local maximum, then nonnegative
@@ -263,6 +260,12 @@ def fused_probabilities(s: np.ndarray, m_tilde: np.ndarray, vis: np.ndarray,
       bit-pattern one, i.e. the rounding thresholds of the exact map (the
       threshold-corrected variant); a block's binade is then that of its
       largest exact value once rounded.
+
+    In every mode, a row whose codes would all be zero (a guess so far above
+    the row that no shift within the scale range reaches it: the row scale
+    in "row" mode, Delta capped at 127 - pl otherwise), which would leave
+    l = 0 and the output 0/0, falls back as well: kappa = max_b e_b, a
+    negative offset that re-bases it downwards.
 
     Returns the P~ values (float64), the element codes, the per-block shifts
     Delta, the E8M0 scale bytes of P~, the per-row binade offset kappa
@@ -284,27 +287,36 @@ def fused_probabilities(s: np.ndarray, m_tilde: np.ndarray, vis: np.ndarray,
     if mode == "row":
         tmax = np.where(vis, t, -np.inf).max(axis=1) if S else np.full(R, -np.inf)
         with np.errstate(over="ignore"):
-            top = mitchell_exp2(tmax + pl)
-        over = top >= overflow_threshold(f)
-        flush = np.isfinite(tmax) & (round_to_format(top, f) == 0.0)
-        kappa = np.where(over | flush, emax, 0.0)
-        delta = np.zeros_like(e)
+            over = mitchell_exp2(tmax + pl) >= overflow_threshold(f)
+        kappa = np.where(over, emax, 0.0)
     else:
         kappa = np.maximum(0.0, emax)
-        delta = np.where(np.isfinite(e), np.minimum(kappa[:, None] - e, cap), cap)
-    delta_full = np.repeat(delta, BLOCK, axis=1)[:, :S]
-    x = np.where(vis, t - kappa[:, None] + pl + delta_full, -np.inf)
-    if mode == "efq":
-        with np.errstate(invalid="ignore"):
-            c = np.rint(2.0 ** f.mbits * (x + f.bias))
-        code = np.clip(np.where(np.isfinite(c), c, 0.0), 0, f.max_code).astype(np.int64)
-        vals = decode(code, f)
-    else:
-        with np.errstate(over="ignore"):
-            p = np.exp2(x) if mode == "exp" else mitchell_exp2(x)
-        vals = round_to_format(p, f)
-        code = encode_values(vals, f).astype(np.int64)
-    P = vals * np.ldexp(1.0, (-pl - delta_full).astype(np.int32))
+
+    def place(kappa):
+        if mode == "row":
+            delta = np.zeros_like(e)
+        else:
+            delta = np.where(np.isfinite(e), np.minimum(kappa[:, None] - e, cap), cap)
+        delta_full = np.repeat(delta, BLOCK, axis=1)[:, :S]
+        x = np.where(vis, t - kappa[:, None] + pl + delta_full, -np.inf)
+        if mode == "efq":
+            with np.errstate(invalid="ignore"):
+                c = np.rint(2.0 ** f.mbits * (x + f.bias))
+            code = np.clip(np.where(np.isfinite(c), c, 0.0), 0, f.max_code).astype(np.int64)
+            vals = decode(code, f)
+        else:
+            with np.errstate(over="ignore"):
+                p = np.exp2(x) if mode == "exp" else mitchell_exp2(x)
+            vals = round_to_format(p, f)
+            code = encode_values(vals, f).astype(np.int64)
+        return delta, code, vals * np.ldexp(1.0, (-pl - delta_full).astype(np.int32))
+
+    delta, code, P = place(kappa)
+    # rows whose every code flushed: re-based downwards by their top binade
+    flush = (P.sum(axis=1) == 0.0) & vis.any(axis=1) & np.isfinite(emax)
+    if flush.any():
+        kappa = np.where(flush, emax, kappa)
+        delta, code, P = place(kappa)
     return {
         "P": P,
         "codes": code,

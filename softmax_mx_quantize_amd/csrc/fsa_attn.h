@@ -818,8 +818,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int b, const 
     } else {
       km = block_binade<MB>(tm);
     }
-    // one scale per row re-bases a flushed row downwards too (negative kappa)
-    kap_x = PM == PM_ROW || km > 0 ? km : 0;
+    // a row far above its guess (km >= KSAT) or one whose codes all flushed
+    // (km < 0: re-based downwards); the measure stops at -(127 + REF)
+    kap_x = km;
     // restart the ring for the sweep from the raised reference
     issue_k(0, kl0);
     issue_v(0, vl0);
@@ -868,13 +869,15 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int b, const 
   if constexpr (L32) lsum = L[0];
   else lsum = __shfl(L[0], n < 16 ? n : n + 16);
   // one scale per row: a code past the format's range in either half of the
-  // row, or a row whose every code flushed to zero (a guess so far above it
-  // that the row sum is 0), sends it to the fallback pass, which measures
-  // its offset
+  // row sends it to the fallback pass, which measures its offset
   if constexpr (PM == PM_ROW && !REBASE) {
     const uint32_t ov = (over | (uint32_t)__shfl_xor((int)over, 32)) & 0x80808080u;
-    kap = ov || lsum == 0.0f ? KSAT : 0;
+    kap = ov ? KSAT : 0;
   }
+  // A row whose every code flushed to zero (a guess so far above it that no
+  // shift within the scale range reaches it: the row sum is 0) is measured
+  // by the fallback pass too, and re-based downwards.
+  if constexpr (!REBASE) kap = lsum == 0.0f ? KSAT : kap;
 
   // ---- normalise and store: register i of O[db] is d = 32 db + 8 (i/4) + 4h + i%4.
   // The row index is recomputed from an opaque lane index, so that the

@@ -3,8 +3,10 @@
 Each case draws B in {1, 2}, H in {1, 2, 3} (per-head formats drawn
 independently, so most multi-head cases are hybrid launches), S in [1, 700]
 (ragged key and query tiles), D in {64, 128}, causal or not, an input scale
-(score spread) and a frozen-max bias: 0, or a lowered guess that sends rows
-through the in-sweep shifts (-8 binades) or the second pass (-100).  The
+(score spread) and a frozen-max bias: 0, a lowered guess that sends rows
+through the in-sweep shifts (-8 binades) or the second pass (-100), or a
+raised one (32: one E4M3 scale per row flushes; 150: every map flushes),
+whose rows are re-based downwards.  The
 bar is the one of the other parity tests (tests/parity.py).  A second sweep
 draws the same kinds of shapes for each P~ variant (one format per call).
 """
@@ -32,7 +34,7 @@ def _cases(n=48, seed=2024):
         causal = bool(rng.integers(0, 2))
         fmts = [FMTS[int(j)] for j in rng.integers(0, 3, size=H)]
         scale = float(rng.uniform(0.5, 2.5))
-        bias = float(rng.choice([0.0, 0.0, -8.0, -100.0]))
+        bias = float(rng.choice([0.0, 0.0, -8.0, -100.0, 32.0, 150.0]))
         out.append((i, B, H, S, D, causal, tuple(fmts), scale, bias))
     return out
 
@@ -67,7 +69,7 @@ def _variant_cases(per=4, seed=2025):
             D = int(rng.choice([64, 128]))
             causal = bool(rng.integers(0, 2))
             scale = float(rng.uniform(0.5, 2.5))
-            bias = float(rng.choice([0.0, 0.0, -8.0, -100.0]))
+            bias = float(rng.choice([0.0, 0.0, -8.0, -100.0, 32.0, 150.0]))
             out.append((vi * per + r, var, B, H, S, D, causal, scale, bias))
     return out
 

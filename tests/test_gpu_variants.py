@@ -124,17 +124,25 @@ def test_variant_fallbacks(variant):
         _check(g, kap, mg, q, k, v, fmt, okw, pfmt, mode, bias=bias)
 
 
+# guesses far above every row: 32 binades flush every code under one E4M3
+# scale per row; 160 binades exceed what the largest block shift can reach
+FAR_ABOVE = ([("row", "e4m3", dict(p_mode="row"), "e4m3", "row", 32.0)] +
+             [("block", f, {}, f, "block", 160.0) for f in ("e4m3", "e2m3", "e2m1")] +
+             [v + (160.0,) for v in VARIANTS if v[0] != "row"])
+
+
 @pytest.mark.parametrize("causal", [False, True])
-def test_row_scale_guess_far_above(causal):
-    """One scale per row with the guess 32 binades above every row: each
-    code would flush to zero (a zero row sum); the row falls back and is
-    re-based downwards by its own top binade (negative kappa)."""
-    announce("variant row, guess far above", causal)
-    okw, pfmt, mode = dict(p_mode="row"), "e4m3", "row"
+@pytest.mark.parametrize("case", FAR_ABOVE, ids=["%s-%s" % c[:2] for c in FAR_ABOVE])
+def test_guess_far_above_rows_fall_back(case, causal):
+    """With the guess far above every row, each code would flush to zero (a
+    zero row sum, 0/0 out); the rows fall back and are re-based downwards by
+    their own top binade (negative kappa)."""
+    name, fmt, okw, pfmt, mode, bias = case
+    announce("guess far above", name, fmt, bias, causal)
     q, k, v = (W.random_bf16((1, 2, 333, 128), seed, 1.0) for seed in (94, 95, 96))
-    g, kap, mg = _run(q, k, v, "e4m3", "row", causal, guess_bias=32.0)
+    g, kap, mg = _run(q, k, v, fmt, name, causal, guess_bias=bias)
     assert np.all(np.isfinite(g)) and np.all(kap < 0)
-    _check(g, kap, mg, q, k, v, "e4m3", okw, pfmt, mode, causal, bias=32.0)
+    _check(g, kap, mg, q, k, v, fmt, okw, pfmt, mode, causal, bias=bias)
 
 
 @pytest.mark.parametrize("variant", VARIANTS, ids=IDS)

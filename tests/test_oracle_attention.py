@@ -367,6 +367,31 @@ def test_variant_row_scale_fallback_forgets_the_guess():
     assert np.all(res[32.0][1]["kappa"] < 0) and np.all(res[-48.0][1]["kappa"] > 0)
 
 
+@pytest.mark.parametrize("fmt,mode", [("e4m3", "block"), ("e2m3", "block"), ("e2m1", "block"),
+                                      ("e4m3", "exp"), ("e2m1", "efq")])
+def test_flushed_rows_fall_back_like_rows_far_above(fmt, mode):
+    """A guess 144 or 176 binades above every row puts each block beyond the
+    largest shift (127 - pl binades): every code would flush and l = 0.
+    Such rows are re-based downwards by their top binade (kappa < 0), which
+    makes them the same rows as with the guess 144 binades below (kappa > 0,
+    re-based upwards): identical outputs, offsets apart by the whole
+    binades between the guesses.  The biases keep every guess in one fp32
+    binade, [128, 256) in magnitude, so that they differ by whole binades
+    exactly."""
+    q, k, v = (W.random_bf16((160, 64), 340 + j, 1.0) for j in range(3))
+    qh, kh, vh = (W.bf16_bits_to_f64(x) for x in (q, k, v))
+    okw = dict(p_mode=mode) if mode != "block" else {}
+    _, info0 = O.fused_attention(qh, kh, vh, fmt, bias=0.0, return_info=True, **okw)
+    assert np.all(np.abs(info0["m_tilde"]) < 16.0)
+    res = {b: O.fused_attention(qh, kh, vh, fmt, bias=b, return_info=True, **okw)
+           for b in (-144.0, 144.0, 176.0)}
+    for b, (o, info) in res.items():
+        assert np.all(np.isfinite(o)) and np.all(info["l"] > 0), b
+        assert np.array_equal(o, res[-144.0][0]), b
+        assert np.array_equal(info["kappa"], res[-144.0][1]["kappa"] - 144 - int(b)), b
+    assert np.all(res[-144.0][1]["kappa"] > 0) and np.all(res[144.0][1]["kappa"] < 0)
+
+
 def test_variant_affine_codes_closed_form():
     """Affine E2M1 codes: the default map wherever the value is 1 or more
     (in units of the block's placement), the straight line below it."""
