@@ -261,11 +261,12 @@ def fused_probabilities(s: np.ndarray, m_tilde: np.ndarray, vis: np.ndarray,
       threshold-corrected variant); a block's binade is then that of its
       largest exact value once rounded.
 
-    In every mode, a row whose codes would all be zero (a guess so far above
-    the row that no shift within the scale range reaches it: the row scale
-    in "row" mode, Delta capped at 127 - pl otherwise), which would leave
-    l = 0 and the output 0/0, falls back as well: kappa = max_b e_b, a
-    negative offset that re-bases it downwards.
+    Rows far below the guess fall back as well, re-based downwards by a
+    negative kappa = max_b e_b: in the block modes a row whose top block
+    needs a shift beyond 127 - pl binades (its scale would clamp, leaving
+    the block off the placement binade and, further down, the row sum at 0
+    or below fp32's range); with one scale per row a row whose codes would
+    all be zero (l = 0, the output 0/0).
 
     Returns the P~ values (float64), the element codes, the per-block shifts
     Delta, the E8M0 scale bytes of P~, the per-row binade offset kappa
@@ -290,7 +291,11 @@ def fused_probabilities(s: np.ndarray, m_tilde: np.ndarray, vis: np.ndarray,
             over = mitchell_exp2(tmax + pl) >= overflow_threshold(f)
         kappa = np.where(over, emax, 0.0)
     else:
-        kappa = np.maximum(0.0, emax)
+        # a top block beyond the largest shift (more than cap binades below
+        # the guess) is re-based downwards so that it lands in the placement
+        # binade all the same
+        low = np.isfinite(emax) & (emax < -cap)
+        kappa = np.where(low, emax, np.maximum(0.0, emax))
 
     def place(kappa):
         if mode == "row":
@@ -312,7 +317,9 @@ def fused_probabilities(s: np.ndarray, m_tilde: np.ndarray, vis: np.ndarray,
         return delta, code, vals * np.ldexp(1.0, (-pl - delta_full).astype(np.int32))
 
     delta, code, P = place(kappa)
-    # rows whose every code flushed: re-based downwards by their top binade
+    # one scale per row: rows whose every code flushed, re-based downwards
+    # by their top binade (the block modes never get here: their top block
+    # always lands in the placement binade)
     flush = (P.sum(axis=1) == 0.0) & vis.any(axis=1) & np.isfinite(emax)
     if flush.any():
         kappa = np.where(flush, emax, kappa)
@@ -337,7 +344,8 @@ def fused_attention(q, k, v, fmt, causal: bool = False, rows=None, bias: float =
     by default; E4M3 P~ over FP6/FP4 operands is the mixed variant) and
     ``p_mode`` its variant (see ``fused_probabilities``).  With
     ``return_info`` also returns the frozen max, the fallback offsets, the
-    log2-domain scores, the P~ values, the dequantised v^ and the visibility.
+    log2-domain scores, the P~ values, the dequantised q'^, k^ and v^ and the
+    visibility.
     """
     f = _fmt(fmt)
     pf = f if p_fmt is None else _fmt(p_fmt)
@@ -358,7 +366,7 @@ def fused_attention(q, k, v, fmt, causal: bool = False, rows=None, bias: float =
     if not return_info:
         return out
     info = dict(fp)
-    info.update(m_tilde=m_tilde, l=l, scores=s, v_hat=vh, visible=vis)
+    info.update(m_tilde=m_tilde, l=l, scores=s, q_hat=qh, k_hat=kh, v_hat=vh, visible=vis)
     return out, info
 
 

@@ -818,8 +818,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int b, const 
     } else {
       km = block_binade<MB>(tm);
     }
-    // a row far above its guess (km >= KSAT) or one whose codes all flushed
-    // (km < 0: re-based downwards); the measure stops at -(127 + REF)
+    // a row far above its guess (km >= KSAT) or far below it (km < 0:
+    // re-based downwards); the measure stops at -(127 + REF)
     kap_x = km;
     // restart the ring for the sweep from the raised reference
     issue_k(0, kl0);
@@ -856,6 +856,12 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int b, const 
   // wrong here and are recomputed by the REBASE pass
   int kap = kmax - (127 + REF);
   kap = max(kap, __shfl_xor(kap, 32));
+  // a top block beyond the largest shift (the row more than CAP binades
+  // below its guess, its scale clamped at XLO) is measured by the fallback
+  // pass and re-based downwards, so that it still lands in the placement
+  // binade; one scale per row has no block levels (its case is the zero
+  // row sum below)
+  if constexpr (PM != PM_ROW && !REBASE) kap = kap < -CAP ? KSAT : kap;
   kap = kap > 0 ? kap : 0;
   if constexpr (REBASE) kap = kap_x;
   // exact exponential: 2^(t + REF) leaves fp32's range (an infinite pattern)
@@ -874,10 +880,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int b, const 
     const uint32_t ov = (over | (uint32_t)__shfl_xor((int)over, 32)) & 0x80808080u;
     kap = ov ? KSAT : 0;
   }
-  // A row whose every code flushed to zero (a guess so far above it that no
-  // shift within the scale range reaches it: the row sum is 0) is measured
-  // by the fallback pass too, and re-based downwards.
-  if constexpr (!REBASE) kap = lsum == 0.0f ? KSAT : kap;
+  // One scale per row: a row whose every code flushed to zero (a guess more
+  // than the format's range above it: the row sum is 0) is measured by the
+  // fallback pass too, and re-based downwards.
+  if constexpr (PM == PM_ROW && !REBASE) kap = lsum == 0.0f ? KSAT : kap;
 
   // ---- normalise and store: register i of O[db] is d = 32 db + 8 (i/4) + 4h + i%4.
   // The row index is recomputed from an opaque lane index, so that the

@@ -27,17 +27,50 @@ from oracle.attention import mitchell_exp2, placement_exponent
 # being 2^-17 binades
 EPS_PLACE = 3e-5
 
+# The score product itself, per operand format, in binades per unit of the
+# product's absolute mass sum_d |q'^_d k^_d|: with FP8 operands the matrix
+# core's accumulation is not exact (measured on MI355X against exact scores,
+# the kernel's frozen max of one-key rows: error / mass at most 2.3e-5,
+# median 1.1e-6, over 24,576 products at D = 64 and 128 and scores up to 165
+# binades); FP6 and FP4 products came out exact (error 0 in every case).
+SCORE_REL = {"e4m3": 4e-5}
 
-def eps_rows(gpu_m_tilde, info):
-    """Per-row margin: the kernel's fp32 placement plus its frozen max's
-    distance from the oracle's (held to fp32 rounding by the tests)."""
-    return EPS_PLACE + np.abs(np.asarray(gpu_m_tilde, np.float64) - info["m_tilde"])
+
+def score_eps(info, fmt):
+    """Per-element bound (binades) on the kernel's score error for operands
+    in ``fmt``: 0, or SCORE_REL times the product's absolute mass."""
+    c = SCORE_REL.get(fmt, 0.0)
+    if c == 0.0:
+        return 0.0
+    return c * (np.abs(info["q_hat"]) @ np.abs(info["k_hat"]).T)
+
+
+def eps_rows(gpu_m_tilde, info, fmt=None):
+    """Margin of the kernel's t: its fp32 placement plus its frozen max's
+    distance from the oracle's (held to fp32 rounding by the tests), per row;
+    with the operand format ``fmt`` also each score's own product error, per
+    element."""
+    base = EPS_PLACE + np.abs(np.asarray(gpu_m_tilde, np.float64) - info["m_tilde"])
+    se = 0.0 if fmt is None else score_eps(info, fmt)
+    return base if np.isscalar(se) else base[:, None] + se
+
+
+def kappa_eps(info, fmt, base=2e-3):
+    """Per-row margin for a row's fallback offset: ``base`` plus the score
+    error of its largest guess-relative score."""
+    se = score_eps(info, fmt)
+    if np.isscalar(se):
+        return np.full(len(info["m_tilde"]), base)
+    t = np.where(info["visible"], info["scores"] - info["m_tilde"][:, None], -np.inf)
+    top = np.argmax(t, axis=1)
+    return base + se[np.arange(len(top)), top]
 
 
 def tie_allowance(info, fmt, out_ref, eps_x, mode="block"):
     """Per-row bound on the output change that near-tie codes can cause;
-    ``eps_x`` (binades, scalar or per row) bounds how far the kernel's t may
-    sit from the exact one; ``fmt`` and ``mode`` are P~'s format and variant."""
+    ``eps_x`` (binades: scalar, per row or per element) bounds how far the
+    kernel's t may sit from the exact one; ``fmt`` and ``mode`` are P~'s
+    format and variant."""
     f = FORMATS[fmt]
     M = f.mbits
     pl = placement_exponent(f)
@@ -47,7 +80,11 @@ def tie_allowance(info, fmt, out_ref, eps_x, mode="block"):
     t = s - m[:, None]
     dfull = np.repeat(delta, 32, axis=1)[:, :S]
     x = np.where(vis, t - kap[:, None] + pl + dfull, -np.inf)
-    ex = np.broadcast_to(np.asarray(eps_x, np.float64).reshape(-1, 1), (R, 1))
+    ea = np.asarray(eps_x, np.float64)
+    if ea.ndim == 2:                                       # per element
+        ex = ea
+    else:                                                  # scalar or per row
+        ex = np.broadcast_to(ea.reshape(-1, 1), (R, 1))
     if mode == "efq":
         # ties of the code-domain rounding: 2 x + 2 within 2 eps of k + 1/2
         with np.errstate(invalid="ignore"):
@@ -76,6 +113,10 @@ def tie_allowance(info, fmt, out_ref, eps_x, mode="block"):
     tp = np.full((R, nb * 32), -np.inf)
     tp[:, :S] = np.where(vis, t, -np.inf)
     tmax = tp.reshape(R, nb, 32).max(axis=2)
+    if ex.shape[1] > 1:                                    # a block's margin: its largest
+        ep = np.zeros((R, nb * 32))
+        ep[:, :S] = ex
+        ex = ep.reshape(R, nb, 32).max(axis=2)
     with np.errstate(invalid="ignore", over="ignore"):
         if mode == "exp":
             # the binade steps where 2^frac(t_max) rounds up to 2: 2^f = 2 - 2^-(M+1)

@@ -8,7 +8,9 @@ through the in-sweep shifts (-8 binades) or the second pass (-100), or a
 raised one (32: one E4M3 scale per row flushes; 150: every map flushes),
 whose rows are re-based downwards.  The
 bar is the one of the other parity tests (tests/parity.py).  A second sweep
-draws the same kinds of shapes for each P~ variant (one format per call).
+draws the same kinds of shapes for each P~ variant (one format per call); a
+third draws extreme score spreads (input scales 0.05 to 6: nearly uniform
+rows up to rows whose scores spread over a hundred binades) in every map.
 """
 
 import numpy as np
@@ -88,6 +90,42 @@ def test_variant_mixed_shapes_all_rows(case):
     i, (name, fmt, okw, pfmt, mode), B, H, S, D, causal, scale, bias = case
     announce("fsa variant sweep", _vid(case))
     q, k, v = (W.random_bf16((B, H, S, D), 900 + 3 * i + j, scale if j < 2 else 1.0)
+               for j in range(3))
+    g, kap, mg = _vrun(q, k, v, fmt, name, causal, guess_bias=bias)
+    _vcheck(g, kap, mg, q, k, v, fmt, okw, pfmt, mode, causal, bias=bias)
+
+
+MAPS = [("block", f, {}, f, "block") for f in FMTS] + VARIANTS
+
+
+def _extreme_cases(n=24, seed=2026):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        var = MAPS[int(rng.integers(0, len(MAPS)))]
+        S = int(rng.integers(1, 501))
+        D = int(rng.choice([64, 128]))
+        causal = bool(rng.integers(0, 2))
+        scale = float(rng.choice([0.05, 3.5, 5.0, 6.0]))
+        bias = float(rng.choice([0.0, -8.0, -100.0]))
+        out.append((i, var, S, D, causal, scale, bias))
+    return out
+
+
+XCASES = _extreme_cases()
+
+
+def _xid(c):
+    i, var, S, D, causal, scale, bias = c
+    return "x%02d-%s-%s-S%dD%d%s-x%.2f-b%g" % (i, var[0], var[1], S, D, "-causal" if causal else "",
+                                               scale, bias)
+
+
+@pytest.mark.parametrize("case", XCASES, ids=[_xid(c) for c in XCASES])
+def test_extreme_score_spreads_all_rows(case):
+    i, (name, fmt, okw, pfmt, mode), S, D, causal, scale, bias = case
+    announce("fsa extreme sweep", _xid(case))
+    q, k, v = (W.random_bf16((1, 1, S, D), 1300 + 3 * i + j, scale if j < 2 else 1.0)
                for j in range(3))
     g, kap, mg = _vrun(q, k, v, fmt, name, causal, guess_bias=bias)
     _vcheck(g, kap, mg, q, k, v, fmt, okw, pfmt, mode, causal, bias=bias)

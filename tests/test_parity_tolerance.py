@@ -12,7 +12,10 @@ exact value sits within that distance of a tie.
   small head to exercise the bound (it is linear in eps; the kernel's own
   EPS_PLACE of 3e-5 flips too few FP6/FP4 codes on a CPU-sized sample);
 * the same error with no allowance, or a much larger error, is not;
-* a code moved one step away from any tie is not absorbed at all.
+* a code moved one step away from any tie is not absorbed at all;
+* FP8 score products: scores each off by up to their own bound (a fraction
+  of their absolute mass) are absorbed by the per-element margin, and not
+  by the per-row one alone.
 """
 
 import numpy as np
@@ -21,7 +24,7 @@ import pytest
 import workloads as W
 import oracle as O
 from oracle.attention import fused_probabilities
-from parity import EPS_PLACE, excess_rel_l2, tie_allowance
+from parity import EPS_PLACE, SCORE_REL, excess_rel_l2, score_eps, tie_allowance
 
 FMTS = ["e4m3", "e2m3", "e2m1"]
 
@@ -125,3 +128,25 @@ def test_block_moved_across_its_binade_tie_is_absorbed(fmt):
     plain = O.rel_l2(k_out, out)
     ex, _ = excess_rel_l2(k_out, out, info, fmt, EPS)
     assert plain > 0.0 and ex <= 1e-3 * plain, (ex, plain)
+
+
+def test_score_errors_within_their_bound_are_absorbed():
+    """A simulated FP8 kernel whose every score is off by +-0.8 of its bound
+    (SCORE_REL times sum_d |q'^_d k^_d|): the per-element margin absorbs the
+    flips this causes; the per-row EPS_PLACE alone does not."""
+    fmt = "e4m3"
+    q, k, v = (W.random_bf16((1, 1, 512, 64), 95 + i, 3.0) for i in range(3))
+    qh, kh, vh = (W.bf16_bits_to_f64(x[0, 0]) for x in (q, k, v))
+    _, info = O.fused_attention(qh, kh, vh, fmt, rows=np.arange(48), return_info=True)
+    out = info["P"] @ info["v_hat"] / info["l"][:, None]
+    se = score_eps(info, fmt)
+    assert SCORE_REL[fmt] > 0 and se.shape == info["scores"].shape
+    sign = np.where(np.random.default_rng(5).random(se.shape) < 0.5, -1.0, 1.0)
+    fp = fused_probabilities(info["scores"] + 0.8 * sign * se, info["m_tilde"], info["visible"], fmt)
+    k_out = fp["P"] @ info["v_hat"] / fp["P"].sum(axis=1)[:, None]
+    plain = O.rel_l2(k_out, out)
+    assert plain > 0.0
+    ex, _ = excess_rel_l2(k_out, out, info, fmt, EPS_PLACE + se)
+    assert ex <= 1e-3 * plain, (ex, plain)
+    ex0, _ = excess_rel_l2(k_out, out, info, fmt, EPS_PLACE)
+    assert ex0 >= 0.1 * plain, (ex0, plain)
