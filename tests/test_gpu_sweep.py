@@ -10,7 +10,11 @@ whose rows are re-based downwards.  The
 bar is the one of the other parity tests (tests/parity.py).  A second sweep
 draws the same kinds of shapes for each P~ variant (one format per call); a
 third draws extreme score spreads (input scales 0.05 to 6: nearly uniform
-rows up to rows whose scores spread over a hundred binades) in every map.
+rows up to rows whose scores spread over a hundred binades) in every map; a
+fourth passes each of q, k, v and out in its own layout (contiguous
+[B, H, S, D], a [B, S, H, D] tensor viewed as [B, H, S, D], or rows padded
+to a longer stride); a fifth compares the allocation-free entry point with
+the allocating one bit for bit.
 """
 
 import numpy as np
@@ -129,3 +133,110 @@ def test_extreme_score_spreads_all_rows(case):
                for j in range(3))
     g, kap, mg = _vrun(q, k, v, fmt, name, causal, guess_bias=bias)
     _vcheck(g, kap, mg, q, k, v, fmt, okw, pfmt, mode, causal, bias=bias)
+
+
+LAYOUTS = ["bhsd", "bshd", "pad8", "pad16"]
+
+
+def _layout_cases(n=24, seed=2027):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        B = int(rng.integers(1, 3))
+        H = int(rng.integers(1, 5))
+        S = int(rng.integers(1, 401))
+        D = int(rng.choice([64, 128]))
+        causal = bool(rng.integers(0, 2))
+        fmts = tuple(FMTS[int(j)] for j in rng.integers(0, 3, size=H))
+        lay = tuple(LAYOUTS[int(j)] for j in rng.integers(0, len(LAYOUTS), size=4))
+        out.append((i, B, H, S, D, causal, fmts, lay))
+    return out
+
+
+LCASES = _layout_cases()
+
+
+def _lid(c):
+    i, B, H, S, D, causal, fmts, lay = c
+    return "l%02d-B%dH%dS%dD%d%s-%s-%s" % (i, B, H, S, D, "-causal" if causal else "", "+".join(fmts),
+                                          "/".join(lay))
+
+
+def _view(x, lay):
+    """A [B, H, S, D] bf16 device view of the host bits ``x`` (None: an
+    uninitialised output) stored in layout ``lay``."""
+    import torch
+    from gpu_helpers import to_dev
+    B, H, S, D = x.shape
+    if lay == "bhsd":
+        return to_dev(x)
+    if lay == "bshd":
+        return to_dev(np.ascontiguousarray(x.transpose(0, 2, 1, 3))).transpose(1, 2)
+    pad = int(lay[3:])
+    store = torch.zeros((B, H, S, D + pad), dtype=torch.bfloat16, device="cuda")
+    store[..., :D] = to_dev(x)
+    return store[..., :D]
+
+
+@pytest.mark.parametrize("case", LCASES, ids=[_lid(c) for c in LCASES])
+def test_strided_layouts_all_rows(case):
+    import torch
+    import softmax_mx_quantize_amd as fsa
+    from gpu_helpers import from_dev_bf16
+    i, B, H, S, D, causal, fmts, lay = case
+    announce("fsa layout sweep", _lid(case))
+    q, k, v = (W.random_bf16((B, H, S, D), 1700 + 3 * i + j, 1.2) for j in range(3))
+    dq, dk, dv = (_view(x, l) for x, l in zip((q, k, v), lay))
+    out = _view(np.zeros((B, H, S, D), np.uint16), lay[3])
+    o, kap, mg = fsa.attention_fwd(dq, dk, dv, fmts[0], causal, head_fmt=list(fmts), out=out,
+                                   return_rows=True)
+    torch.cuda.synchronize()
+    assert o.data_ptr() == out.data_ptr()
+    g = from_dev_bf16(o.contiguous())
+    _check(g, kap.cpu().numpy(), mg.cpu().numpy(), *_oracle_heads(q, k, v, list(fmts), causal))
+
+
+def _noalloc_cases(n=24, seed=2028):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        B = int(rng.integers(1, 3))
+        H = int(rng.integers(1, 5))
+        S = int(rng.integers(1, 3001))
+        D = int(rng.choice([64, 128]))
+        causal = bool(rng.integers(0, 2))
+        fmts = tuple(FMTS[int(j)] for j in rng.integers(0, 3, size=H))
+        bias = float(rng.choice([0.0, 0.0, -8.0, -100.0, 150.0]))
+        variant = str(rng.choice(["block", "block", "exact_exp"]))
+        if variant == "exact_exp" and "e4m3" in fmts and len(set(fmts)) > 1:
+            # built for one format per call or the FP6/FP4 hybrid
+            fmts = tuple("e2m3" if f == "e4m3" else f for f in fmts)
+        out.append((i, B, H, S, D, causal, fmts, bias, variant))
+    return out
+
+
+NCASES = _noalloc_cases()
+
+
+def _nid(c):
+    i, B, H, S, D, causal, fmts, bias, variant = c
+    return "n%02d-B%dH%dS%dD%d%s-%s-b%g-%s" % (i, B, H, S, D, "-causal" if causal else "",
+                                               "+".join(fmts), bias, variant)
+
+
+@pytest.mark.parametrize("case", NCASES, ids=[_nid(c) for c in NCASES])
+def test_noalloc_matches_allocating_call(case):
+    """The allocation-free entry point runs the same kernels on the same
+    inputs: outputs, fallback offsets and frozen maxima bit for bit."""
+    import torch
+    import softmax_mx_quantize_amd as fsa
+    from gpu_helpers import to_dev
+    i, B, H, S, D, causal, fmts, bias, variant = case
+    announce("fsa no-alloc sweep", _nid(case))
+    q, k, v = (to_dev(W.random_bf16((B, H, S, D), 1900 + 3 * i + j, 1.2)) for j in range(3))
+    kw = dict(head_fmt=list(fmts), guess_bias=bias, p_variant=variant, return_rows=True)
+    a = fsa.attention_fwd(q, k, v, fmts[0], causal, **kw)
+    b = fsa.attention_fwd(q, k, v, fmts[0], causal, no_alloc=True, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])

@@ -164,6 +164,10 @@ def test_variant_rejects_unbuilt_formats():
         with pytest.raises(fsa.FsaError) as e:
             fsa.attention_fwd(q, q, q, fmt, p_variant=variant)
         assert e.value.status == -2
+    # the exact exponential over FP8 heads mixed with FP6/FP4 ones is not built
+    with pytest.raises(fsa.FsaError) as e:
+        fsa.attention_fwd(q, q, q, "e4m3", p_variant="exact_exp", head_fmt=["e4m3", "e2m1"])
+    assert e.value.status == -2
 
 
 def _threads():
