@@ -14,7 +14,8 @@ rows up to rows whose scores spread over a hundred binades) in every map; a
 fourth passes each of q, k, v and out in its own layout (contiguous
 [B, H, S, D], a [B, S, H, D] tensor viewed as [B, H, S, D], or rows padded
 to a longer stride); a fifth compares the allocation-free entry point with
-the allocating one bit for bit.
+the allocating one bit for bit; a sixth draws long sequences (2,000 to
+20,000 keys) and checks sampled rows, the first and last among them.
 """
 
 import numpy as np
@@ -240,3 +241,40 @@ def test_noalloc_matches_allocating_call(case):
     torch.cuda.synchronize()
     assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
     assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+
+
+def _long_cases(n=12, seed=2029):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        B = int(rng.integers(1, 3))
+        H = int(rng.integers(1, 4))
+        S = int(rng.integers(2000, 20001))
+        D = int(rng.choice([64, 128]))
+        causal = bool(rng.integers(0, 2))
+        fmts = tuple(FMTS[int(j)] for j in rng.integers(0, 3, size=H))
+        scale = float(rng.uniform(0.5, 2.0))
+        bias = float(rng.choice([0.0, 0.0, -8.0, -100.0, 150.0]))
+        rows = np.unique(np.concatenate([[0, S - 1], rng.integers(0, S, size=62)]))
+        out.append((i, B, H, S, D, causal, fmts, scale, bias, rows))
+    return out
+
+
+GCASES = _long_cases()
+
+
+def _gid(c):
+    i, B, H, S, D, causal, fmts, scale, bias, rows = c
+    return "g%02d-B%dH%dS%dD%d%s-%s-x%.1f-b%g" % (i, B, H, S, D, "-causal" if causal else "",
+                                                  "+".join(fmts), scale, bias)
+
+
+@pytest.mark.parametrize("case", GCASES, ids=[_gid(c) for c in GCASES])
+def test_long_sequences_sampled_rows(case):
+    i, B, H, S, D, causal, fmts, scale, bias, rows = case
+    announce("fsa long sweep", _gid(case))
+    q, k, v = (W.random_bf16((B, H, S, D), 2100 + 3 * i + j, scale if j < 2 else 1.0)
+               for j in range(3))
+    g, kap, mg = _run(q, k, v, fmts[0], causal, head_fmt=list(fmts), guess_bias=bias)
+    ref, rk, bd, inf = _oracle_heads(q, k, v, list(fmts), causal, rows=rows, bias=bias)
+    _check(g, kap, mg, ref.reshape(B * H, len(rows), D), rk, bd, inf, rows=rows)
