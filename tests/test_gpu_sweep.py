@@ -15,7 +15,10 @@ fourth passes each of q, k, v and out in its own layout (contiguous
 [B, H, S, D], a [B, S, H, D] tensor viewed as [B, H, S, D], or rows padded
 to a longer stride); a fifth compares the allocation-free entry point with
 the allocating one bit for bit; a sixth draws long sequences (2,000 to
-20,000 keys) and checks sampled rows, the first and last among them.
+20,000 keys) and checks sampled rows, the first and last among them.  Two
+more cover the public MX quantiser (random ragged shapes, per-row binade
+spreads, both block axes: bit for bit) and the BF16 baseline (random shapes
+against exact attention).
 """
 
 import numpy as np
@@ -278,3 +281,62 @@ def test_long_sequences_sampled_rows(case):
     g, kap, mg = _run(q, k, v, fmts[0], causal, head_fmt=list(fmts), guess_bias=bias)
     ref, rk, bd, inf = _oracle_heads(q, k, v, list(fmts), causal, rows=rows, bias=bias)
     _check(g, kap, mg, ref.reshape(B * H, len(rows), D), rk, bd, inf, rows=rows)
+
+
+def _quant_cases(n=36, seed=2030):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        shape = (int(rng.integers(1, 4)), int(rng.integers(1, 400)), int(rng.integers(1, 400)))
+        fmt = FMTS[int(rng.integers(0, 3))]
+        along = int(rng.integers(0, 2))
+        spread = int(rng.choice([0, 8, 40]))
+        out.append((i, shape, fmt, along, spread))
+    return out
+
+
+QCASES = _quant_cases()
+
+
+@pytest.mark.parametrize("case", QCASES, ids=["q%02d-%dx%dx%d-%s-rows%d-e%d" % ((c[0],) + c[1] + c[2:])
+                                              for c in QCASES])
+def test_quantizer_shapes_bit_exact(case):
+    from test_gpu_quant import _gpu_quant, _oracle
+    i, shape, fmt, along, spread = case
+    announce("quant sweep", case)
+    rng = np.random.default_rng(2300 + i)
+    # blocks at binades spread over +-spread (along the blocks' axis: per element)
+    e = rng.integers(-spread, spread + 1, size=shape) if spread else 0
+    x = (rng.standard_normal(shape) * np.exp2(e)).astype(np.float32)
+    bits = W.f32_to_bf16_bits(x)
+    gc, gs = _gpu_quant(bits, fmt, along)
+    oc, os_ = _oracle(bits, fmt, along)
+    assert np.array_equal(gs, os_)
+    assert np.array_equal(gc, oc)
+
+
+def _bf16_cases(n=16, seed=2031):
+    rng = np.random.default_rng(seed)
+    return [(i, int(rng.integers(1, 3)), int(rng.integers(1, 4)), int(rng.integers(1, 1500)),
+             int(rng.choice([64, 128])), bool(rng.integers(0, 2)), float(rng.uniform(0.5, 2.5)))
+            for i in range(n)]
+
+
+BCASES = _bf16_cases()
+
+
+@pytest.mark.parametrize("case", BCASES, ids=["b%02d-B%dH%dS%dD%d-c%d-x%.1f" % (c[0], c[1], c[2], c[3], c[4],
+                                                                              c[5], c[6]) for c in BCASES])
+def test_bf16_baseline_shapes(case):
+    import oracle as O
+    from test_gpu_bf16 import _run as _brun, TOL as BTOL
+    from gpu_helpers import rel_l2
+    i, B, H, S, D, causal, scale = case
+    announce("bf16 sweep", case)
+    q, k, v = (W.random_bf16((B, H, S, D), 2500 + 3 * i + j, scale if j < 2 else 1.0) for j in range(3))
+    g = _brun(q, k, v, causal)
+    for b in range(B):
+        for h in range(H):
+            qh, kh, vh = (W.bf16_bits_to_f64(x[b, h]) for x in (q, k, v))
+            ex = O.exact_attention(qh, kh, vh, causal)
+            assert rel_l2(g[b, h], ex) <= BTOL, (b, h)
