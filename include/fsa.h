@@ -25,13 +25,15 @@
  *     the caller's next synchronisation, not from the call.
  *   - Return value: FSA_OK (0) or a negative fsa_status.  Argument errors are
  *     detected before anything is enqueued.  No C++ exception crosses the ABI.
- *   - Calls on distinct streams are thread-safe.  The library keeps a per-
- *     device workspace (quantised operands) that it allocates on first use and
- *     grows as needed, stream-ordered (hipMallocAsync on the call's stream,
- *     the old buffer freed with hipFreeAsync on the stream of the call that
- *     last used it).  Calls that share a device use the same workspace, so
- *     give the attention calls of one device one stream, or order their
- *     streams yourself.
+ *   - Calls are thread-safe.  The library keeps a per-device workspace
+ *     (quantised operands) that it allocates on first use and grows as
+ *     needed, stream-ordered (hipMallocAsync on the call's stream, the old
+ *     buffer freed with hipFreeAsync on the stream of the call that last used
+ *     it).  Calls that share a device use the same workspace, so give the
+ *     attention calls of one device one stream, or order their streams
+ *     yourself.  Calls from several host threads on one stream are
+ *     serialised: each call enqueues all of its kernels before the next call
+ *     enqueues any.
  */
 #ifndef FSA_H
 #define FSA_H
@@ -255,10 +257,11 @@ int fsa_debug_operands(const void* q, const void* k, const void* v, int B, int H
  * of one batch entry that fit the array, each quantised and attended in
  * turn on `stream`.  FSA_ERR_TOO_LARGE if a single head does not fit (about
  * 264 * S bytes per head at FP8, D = 128; S up to ~250k).  Every call on a
- * device shares that device's array: calls that overlap in time on one
- * device (different streams, or threads) race and must be serialised by
- * the caller.  event_after_quantize, if given, is recorded after the first
- * group's quantisation.
+ * device shares that device's array: calls whose kernels overlap in time on
+ * one device (different streams) race and must be ordered by the caller;
+ * calls from several host threads on one stream are serialised like the
+ * other entry points'.  event_after_quantize, if given, is recorded after
+ * the first group's quantisation.
  */
 int fsa_attention_fwd_noalloc(const void* q, const void* k, const void* v, void* out,
                               int B, int H, int S, int D, int fmt, int causal,

@@ -36,6 +36,14 @@ struct Workspace {
 };
 
 std::mutex g_mu;
+
+// Serialises the enqueue sequences of the calls that use a device's shared
+// workspace or fixed scratch: from taking the buffer to the call's last
+// launch no other call may enqueue work into it.  Calls from several host
+// threads on one stream would otherwise interleave their kernels there (one
+// call's quantiser overwriting operands another call's attention has yet to
+// read).  Taken before g_mu, never after it.
+std::mutex g_call_mu;
 std::unordered_map<int, Workspace> g_ws;
 
 // Returns a device buffer of at least `need` bytes for the current device,
@@ -419,6 +427,7 @@ int attention(const void* q, const void* k, const void* v, void* out, int B, int
     default: return FSA_ERR_INVALID_ARG;
   }
 
+  std::lock_guard<std::mutex> call_lock(g_call_mu);
   if (!no_alloc) {
     // every batch entry and up to MAX_HEAD_TABLE heads per piece, side by
     // side in the growing workspace: quantise everything, then attend (the
@@ -550,6 +559,7 @@ int fsa_attention_bf16_ref(const void* q, const void* k, const void* v, void* ou
   a.S = S;
   a.s_alloc = (int)round_up(S, fsa::BF16_KEY_TILE);
   uint8_t* ws = nullptr;
+  std::lock_guard<std::mutex> call_lock(g_call_mu);
   const int wst = workspace((size_t)a.BH * D * a.s_alloc * 2, static_cast<hipStream_t>(stream), &ws);
   if (wst != FSA_OK) return wst;
   a.vt = reinterpret_cast<uint16_t*>(ws);
@@ -607,6 +617,7 @@ int fsa_debug_operands(const void* q, const void* k, const void* v, int B, int H
 int fsa_release_workspace(void) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FSA_ERR_HIP;
+  std::lock_guard<std::mutex> call_lock(g_call_mu);
   std::lock_guard<std::mutex> lock(g_mu);
   auto it = g_ws.find(dev);
   if (it == g_ws.end() || !it->second.ptr) return FSA_OK;

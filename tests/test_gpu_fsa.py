@@ -296,6 +296,44 @@ def test_side_stream_calls_match_default_stream():
         assert torch.equal(got.view(torch.int16), want.view(torch.int16))
 
 
+def test_host_threads_sharing_one_stream():
+    """Calls from four host threads on one stream, sizes mixed so that the
+    workspace grows meanwhile: every result equals the same call made alone
+    (each call's kernels stay together on the stream)."""
+    import threading
+    import torch
+    import softmax_mx_quantize_amd as fsa
+    announce("fsa host threads")
+    shapes = [(1, 2, 300, 128), (1, 6, 2500, 128), (2, 3, 700, 64), (1, 4, 4000, 128)]
+    fmts = ["e4m3", "e2m1", "e2m3", "e4m3"]
+    ins = [[to_dev(W.random_bf16(sh, 130 + 3 * t + j, 1.0)) for j in range(3)] for t, sh in enumerate(shapes)]
+    refs = []
+    for t in range(4):
+        refs.append(fsa.attention_fwd(*ins[t], fmts[t]))
+        torch.cuda.synchronize()
+    fsa.release_workspace()
+    outs = [[None] * 6 for _ in range(4)]
+    errs = []
+
+    def work(t):
+        try:
+            for r in range(6):
+                outs[t][r] = fsa.attention_fwd(*ins[t], fmts[t])
+        except Exception as e:                     # reported below
+            errs.append(e)
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errs, errs
+    for t in range(4):
+        for r in range(6):
+            assert torch.equal(outs[t][r].view(torch.int16), refs[t].view(torch.int16)), (t, r)
+
+
 @pytest.mark.parametrize("case", ["q_zero", "k_zero", "v_const"])
 def test_degenerate_inputs(case):
     """All-zero queries or keys (every score 0: uniform weights, the output
