@@ -78,6 +78,29 @@ def test_strerror_and_argument_validation_without_gpu():
     opt.head_fmt = hf
     assert lib.fsa_attention_fwd_ex(fake, fake, fake, fake + 4096, 1, 2, 8, 64, 0, 0,
                                     ctypes.byref(opt), None) == -1
+    # strided views: a stride off 16-byte rows, a row stride below D, a
+    # negative stride
+    for bad in ((512, 64, 60), (512, 64, 56), (-512, 64, 64)):
+        lay = fsa.Layout()
+        lay.q[:], lay.k[:], lay.v[:], lay.out[:] = (512, 64, 64), (512, 64, 64), (512, 64, 64), bad
+        opt = fsa.Options()
+        opt.layout = ctypes.pointer(lay)
+        assert lib.fsa_attention_fwd_ex(fake, fake + 4096, fake + 8192, fake + 12288, 1, 1, 8, 64, 0, 0,
+                                        ctypes.byref(opt), None) == -1, bad
+    # an unknown P~ variant; the per-row arrays given by half; a variant
+    # over formats it is not built for (one scale per row over FP4)
+    opt = fsa.Options()
+    opt.p_variant = 99
+    assert lib.fsa_attention_fwd_ex(fake, fake + 4096, fake + 8192, fake + 12288, 1, 1, 8, 64, 0, 0,
+                                    ctypes.byref(opt), None) == -1
+    opt = fsa.Options()
+    opt.row_kappa = fake
+    assert lib.fsa_attention_fwd_ex(fake, fake + 4096, fake + 8192, fake + 12288, 1, 1, 8, 64, 0, 0,
+                                    ctypes.byref(opt), None) == -1
+    opt = fsa.Options()
+    opt.p_variant = 1
+    assert lib.fsa_attention_fwd_ex(fake, fake + 4096, fake + 8192, fake + 12288, 1, 1, 8, 64, 2, 0,
+                                    ctypes.byref(opt), None) == -2
 
 
 def test_oracle_is_not_linked_into_the_product():
