@@ -7,7 +7,8 @@ frozen maxima must agree bit for bit (stronger than the 2e-3 parity bar).
 Two calls in a row, the second smaller; the first spans several scratch
 pieces (two per batch entry, two batch entries) and mixed formats, and one
 case forces every row through the fallback pass, which reads its per-row
-arrays back from the scratch.
+arrays back from the scratch.  A captured graph of one call replays
+correctly on new inputs.
 """
 
 import numpy as np
@@ -78,3 +79,45 @@ def test_noalloc_rejects_a_head_beyond_the_scratch():
     out = fsa.attention_fwd(q, q.clone(), q.clone(), "e4m3")
     torch.cuda.synchronize()
     assert out.shape == q.shape
+
+
+@pytest.mark.parametrize("fmt,causal", [("e4m3", False), ("e2m1", True)])
+def test_noalloc_call_replays_in_a_graph(fmt, causal):
+    """One allocation-free call captured in a graph, replayed on three sets
+    of inputs copied into its static tensors, with eager calls and
+    synchronisations between the replays: every replay equals an eager
+    allocation-free call on the same inputs, bit for bit (the path records
+    no memset and no allocation)."""
+    import torch
+    import softmax_mx_quantize_amd as fsa
+    announce("no-alloc graph", fmt, causal)
+    B, H, S, D = 1, 3, 700, 128
+    sets = [[to_dev(W.random_bf16((B, H, S, D), 3000 + 3 * r + j, 1.0 + 0.3 * r)) for j in range(3)]
+            for r in range(3)]
+    sq, sk, sv = (torch.empty_like(x) for x in sets[0])
+    sout = torch.empty_like(sq)
+    for x, y in zip((sq, sk, sv), sets[0]):
+        x.copy_(y)
+    # the first call on the device looks up the scratch's address: eager, before capture
+    fsa.attention_fwd(sq, sk, sv, fmt, causal, no_alloc=True, out=sout)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            fsa.attention_fwd(sq, sk, sv, fmt, causal, no_alloc=True, out=sout)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for r in range(3):
+        for x, y in zip((sq, sk, sv), sets[r]):
+            x.copy_(y)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = sout.clone()
+        want = fsa.attention_fwd(*sets[r], fmt, causal, no_alloc=True)
+        other = fsa.attention_fwd(*sets[(r + 1) % 3], fmt, causal)      # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16)), r
+        assert other.shape == got.shape
