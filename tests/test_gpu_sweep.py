@@ -18,7 +18,9 @@ the allocating one bit for bit; a sixth draws long sequences (2,000 to
 20,000 keys) and checks sampled rows, the first and last among them.  Two
 more cover the public MX quantiser (random ragged shapes, per-row binade
 spreads, both block axes: bit for bit) and the BF16 baseline (random shapes
-against exact attention).
+against exact attention); a last one checks the attention path's own
+operands (Q'^ from the prologue, K^ and V^T with their tile-ordered scales)
+bit for bit over random shapes.
 """
 
 import numpy as np
@@ -340,3 +342,34 @@ def test_bf16_baseline_shapes(case):
             qh, kh, vh = (W.bf16_bits_to_f64(x[b, h]) for x in (q, k, v))
             ex = O.exact_attention(qh, kh, vh, causal)
             assert rel_l2(g[b, h], ex) <= BTOL, (b, h)
+
+
+def _operand_cases(n=16, seed=2032):
+    rng = np.random.default_rng(seed)
+    return [(i, int(rng.integers(1, 3)), int(rng.integers(1, 3)), int(rng.integers(1, 900)),
+             int(rng.choice([64, 128])), FMTS[int(rng.integers(0, 3))], int(rng.choice([0, 6, 30])))
+            for i in range(n)]
+
+
+OCASES = _operand_cases()
+
+
+@pytest.mark.parametrize("case", OCASES, ids=["o%02d-B%dH%dS%dD%d-%s-e%d" % c for c in OCASES])
+def test_operands_shapes_bit_exact(case):
+    import torch
+    import softmax_mx_quantize_amd as fsa
+    from gpu_helpers import to_dev
+    from test_gpu_operands import _check_head
+    i, B, H, S, D, fmt, spread = case
+    announce("operands sweep", case)
+    rng = np.random.default_rng(2600 + i)
+    xs = []
+    for j in range(3):
+        e = rng.integers(-spread, spread + 1, size=(B, H, S, 1)) if spread else 0
+        xs.append(W.f32_to_bf16_bits((rng.standard_normal((B, H, S, D)) * np.exp2(e)).astype(np.float32)))
+    q, k, v = xs
+    got = fsa.debug_operands(to_dev(q), to_dev(k), to_dev(v), fmt)
+    torch.cuda.synchronize()
+    for b in range(B):
+        for h in range(H):
+            _check_head(got, *(W.bf16_bits_to_f64(x[b, h]) for x in (q, k, v)), fmt, b, h)
