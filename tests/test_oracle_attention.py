@@ -392,6 +392,33 @@ def test_flushed_rows_fall_back_like_rows_far_above(fmt, mode):
     assert np.all(res[-144.0][1]["kappa"] > 0) and np.all(res[144.0][1]["kappa"] < 0)
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m3", "e2m1"])
+def test_top_block_always_lands_in_the_placement_binade(fmt):
+    """The invariant the fallback keeps in the block map: in every row, its
+    largest value, in units of its block's scale, lies in the placement
+    binade [2^pl, 2^(pl+1)), whether the row sits above its guess, near it,
+    or far below it (guesses from 200 binades below to 200 above, across the
+    largest shift of 127 - pl binades)."""
+    f = FORMATS[fmt]
+    pl = O.attention.placement_exponent(f)
+    rng = np.random.default_rng(41)
+    s = rng.normal(0.0, 2.0, (400, 96))
+    top = s.max(axis=1)
+    # guess-relative top scores spread over [-200, 200], with rows packed
+    # around the low threshold -(127 - pl)
+    off = np.concatenate([rng.uniform(-200, 200, 200), -(127 - pl) + rng.uniform(-2, 2, 200)])
+    m = top - off
+    vis = np.ones_like(s, bool)
+    fp = fused_probabilities(s, m, vis, fmt)
+    dfull = np.repeat(fp["delta"], 32, axis=1)[:, :96]
+    vals = fp["P"] * np.ldexp(1.0, (pl + dfull).astype(np.int64))
+    vmax = vals.max(axis=1)
+    assert np.all((vmax >= 2.0 ** pl) & (vmax < 2.0 ** (pl + 1))), (off[vmax < 2.0 ** pl][:5])
+    # below the threshold the rows re-base downwards, above it they do not
+    assert np.all(fp["kappa"][off < -(127 - pl) - 1] < 0)
+    assert np.all(fp["kappa"][(off > -(127 - pl) + 1) & (off < 0)] == 0)
+
+
 def test_variant_affine_codes_closed_form():
     """Affine E2M1 codes: the default map wherever the value is 1 or more
     (in units of the block's placement), the straight line below it."""
