@@ -143,6 +143,23 @@ def test_guess_far_above_rows_fall_back(case, causal):
     _check(g, kap, mg, q, k, v, fmt, okw, pfmt, mode, causal, bias=bias)
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m3", "e2m1"])
+def test_guess_at_the_low_threshold(fmt):
+    """Guesses about 127 - pl binades above the rows, so that their top
+    blocks straddle the largest shift: rows below it are re-based downwards,
+    rows above it keep kappa = 0 and a clamped-free scale; the kernel and
+    the oracle agree row by row (rows within the margin of the threshold
+    itself left free)."""
+    pl = O.attention.placement_exponent(FORMATS[fmt])
+    bias = (127 - pl) - 1.5
+    announce("guess at the low threshold", fmt, bias)
+    q, k, v = (W.random_bf16((1, 2, 600, 128), seed, 1.0) for seed in (97, 98, 99))
+    g, kap, mg = _run(q, k, v, fmt, "block", guess_bias=bias)
+    assert np.all(np.isfinite(g))
+    assert (kap < 0).any() and (kap == 0).any()
+    _check(g, kap, mg, q, k, v, fmt, {}, fmt, "block", bias=bias)
+
+
 @pytest.mark.parametrize("variant", VARIANTS, ids=IDS)
 def test_variant_v_ones(variant):
     import torch
