@@ -175,7 +175,10 @@ typedef struct fsa_layout {
 typedef struct fsa_options {
   /* Added to every frozen max, in binades of the probability (units of
    * log2(e) * q.k / sqrt(D)).  A negative value of a few binades makes every
-   * row fall back; 0 in normal use. */
+   * row fall back, a positive one of more than 127 - pl (pl: the placement
+   * exponent of P~'s format) re-bases every row downwards; 0 in normal use.
+   * Finite with |guess_bias| <= 2^17, else FSA_ERR_INVALID_ARG (the fallback
+   * pass measures offsets within 2^18 binades either way). */
   float guess_bias;
   /* Optional device int32 [B][H][S]: receives each row's fallback offset in
    * binades (0 for rows whose scores stayed under the frozen max).  Give

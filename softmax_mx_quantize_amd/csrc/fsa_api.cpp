@@ -20,6 +20,9 @@
 namespace {
 
 constexpr int kKeyTile = 128;
+// largest |fsa_options::guess_bias|, in binades: half the span of offsets
+// the fallback pass measures, leaving the rest to the rows' own spread
+constexpr float kMaxGuessBias = 131072.0f;
 
 int fmt_bits(int fmt) { return fmt == FSA_MXFP8_E4M3 ? 8 : (fmt == FSA_MXFP6_E2M3 ? 6 : 4); }
 bool fmt_ok(int fmt) { return fmt == FSA_MXFP8_E4M3 || fmt == FSA_MXFP6_E2M3 || fmt == FSA_MXFP4_E2M1; }
@@ -373,6 +376,7 @@ int attention(const void* q, const void* k, const void* v, void* out, int B, int
     return FSA_ERR_INVALID_ARG;
   }
   if (opt && (opt->row_kappa == nullptr) != (opt->row_max_guess == nullptr)) return FSA_ERR_INVALID_ARG;
+  if (opt && !(std::fabs(opt->guess_bias) <= kMaxGuessBias)) return FSA_ERR_INVALID_ARG;
   const bool own_rows = !(opt && opt->row_kappa);
 
   Call c;

@@ -816,10 +816,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int b, const 
       const float fl = __builtin_floorf(t);
       km = (int)__builtin_fminf(fl, (float)HI_BINADE) + (t - fl >= F_UP ? 1 : 0);
     } else {
-      km = block_binade<MB>(tm);
+      km = block_binade<MB>(tm, LO_PATTERN);
     }
     // a row far above its guess (km >= KSAT) or far below it (km < 0:
-    // re-based downwards); the measure stops at -(127 + REF)
+    // re-based downwards); the measure spans +-HI_BINADE
     kap_x = km;
     // restart the ring for the sweep from the raised reference
     issue_k(0, kl0);

@@ -66,7 +66,11 @@ constexpr int REF = 62;
 // exponent-field value y.  y * 2^(M-23) is exact, and adding the integer
 // constant plus MAGIC rounds once, to nearest even.  Blocks whose largest
 // value lies below 2^-(127+REF) (or that are fully masked, y = -inf) count as
-// y = 0, which already puts them beyond the largest block shift.  Values
+// y = lo: 0 in the sweep, which already puts them beyond the largest block
+// shift.  The fallback pass measures a row's score itself (y negative for a
+// row more than 127 + REF binades below its guess) and passes a lower lo.
+// The rounding is exact for negative y too: the integer bias shifts y by a
+// whole number of binades, which rounding to nearest even commutes with.  Values
 // more than HI_BINADE binades above the reference count as exactly that
 // many (the MAGIC window holds 2^22 codes); the row then falls back with
 // kappa = HI_BINADE, which is exact for every score within 2^18 binades of
@@ -76,9 +80,13 @@ constexpr int HI_BINADE = 1 << 18;
 // alone; rows above it go to the re-based fallback pass.
 constexpr int EXT = 64;
 static_assert(HI_BINADE > EXT, "clamped binades must reach the fallback pass");
+// Lowest offset the fallback pass measures: rows down to HI_BINADE binades
+// below their guess (the frozen max can lie far above a row whose scores
+// have a light upper tail) are measured exactly, as rows far above are.
+constexpr float LO_PATTERN = -8388608.0f * (float)(HI_BINADE - 127 - REF);
 template <int M>
-__device__ __forceinline__ int block_binade(float y) {
-  const float yc = __builtin_amdgcn_fmed3f(y, 0.0f, 8388608.0f * (float)(127 + REF + HI_BINADE));
+__device__ __forceinline__ int block_binade(float y, float lo = 0.0f) {
+  const float yc = __builtin_amdgcn_fmed3f(y, lo, 8388608.0f * (float)(127 + REF + HI_BINADE));
   const float t = __builtin_fmaf(yc, (float)(1 << M) * 0x1p-23f,
                                  MAGIC - (float)((1 << M) * (127 + REF)));
   return (int)(__float_as_uint(t) - __float_as_uint(MAGIC)) >> M;

@@ -101,6 +101,14 @@ def test_strerror_and_argument_validation_without_gpu():
     opt.p_variant = 1
     assert lib.fsa_attention_fwd_ex(fake, fake + 4096, fake + 8192, fake + 12288, 1, 1, 8, 64, 2, 0,
                                     ctypes.byref(opt), None) == -2
+    # guess biases beyond 2^17 binades either way, and NaN
+    for bias in (131072.5, 1e9, -131072.5, float("inf"), float("nan")):
+        opt = fsa.Options()
+        opt.guess_bias = bias
+        assert lib.fsa_attention_fwd_ex(fake, fake + 4096, fake + 8192, fake + 12288, 1, 1, 8, 64, 0, 0,
+                                        ctypes.byref(opt), None) == -1, bias
+        assert lib.fsa_attention_fwd_noalloc(fake, fake + 4096, fake + 8192, fake + 12288, 1, 1, 8, 64,
+                                             0, 0, ctypes.byref(opt), None) == -1, bias
 
 
 def test_oracle_is_not_linked_into_the_product():

@@ -209,6 +209,22 @@ def test_rows_far_above_the_guess_causal(fmt):
     _check(g, kap, mg, ref, rk, bd, inf)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_far_below_their_frozen_max(fmt, causal):
+    """Keys in two opposite clusters: the window's mean + z * std lies
+    200 to 420 binades above each row's top score (bias 0), beyond the
+    reach of the scores' fp32 bit patterns (189 binades); the fallback pass
+    measures each row's offset from its scores and re-bases it downwards."""
+    announce("fsa far below", fmt, causal)
+    q, k, v = W.two_valued_keys(1, 2, 600, 128, seed=41)
+    g, kap, mg = _run(q, k, v, fmt, causal)
+    ref, rk, bd, inf = _oracle_heads(q, k, v, [fmt] * 2, causal)
+    assert (rk < -300).any() and np.mean(rk < -189) > 0.9
+    assert np.all(np.isfinite(g))
+    _check(g, kap, mg, ref, rk, bd, inf)
+
+
 def test_hybrid_heads_two_batches():
     """Per-head formats in one call with B = 2: each run of equal formats is
     quantised and launched per batch entry."""

@@ -143,6 +143,43 @@ def test_guess_far_above_rows_fall_back(case, causal):
     _check(g, kap, mg, q, k, v, fmt, okw, pfmt, mode, causal, bias=bias)
 
 
+# 230 binades: past 127 + REF = 189, where the scores' bit patterns
+# themselves turn negative, so that the fallback pass measures the rows'
+# offsets below zero
+FAR_BELOW = ([("row", "e4m3", dict(p_mode="row"), "e4m3", "row")] +
+             [("block", f, {}, f, "block") for f in ("e4m3", "e2m3", "e2m1")] +
+             [v for v in VARIANTS if v[0] != "row"])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", FAR_BELOW, ids=["%s-%s" % c[:2] for c in FAR_BELOW])
+def test_guess_230_binades_above_rows(case, causal):
+    """Rows about 230 binades below their guess (the largest bias the
+    library takes is 240): each is re-based downwards by its own top binade,
+    with kappa a few binades below -230 (the frozen max's spread term can
+    lie a little above the row's top score)."""
+    name, fmt, okw, pfmt, mode = case
+    bias = 230.0
+    announce("guess 230 above", name, fmt, causal)
+    q, k, v = (W.random_bf16((1, 2, 333, 128), seed, 1.0) for seed in (111, 112, 113))
+    g, kap, mg = _run(q, k, v, fmt, name, causal, guess_bias=bias)
+    assert np.all(np.isfinite(g)) and np.all(kap <= -200) and np.all(kap >= -240)
+    _check(g, kap, mg, q, k, v, fmt, okw, pfmt, mode, causal, bias=bias)
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=IDS)
+def test_variant_rows_far_below_their_frozen_max(variant):
+    """Two opposite key clusters (bias 0): every row 200 to 420 binades
+    below its frozen max, re-based downwards by the fallback pass."""
+    name, fmt, okw, pfmt, mode = variant
+    announce("variant far below", name, fmt)
+    q, k, v = W.two_valued_keys(1, 2, 600, 128, seed=42)
+    for causal in (False, True):
+        g, kap, mg = _run(q, k, v, fmt, name, causal)
+        assert np.all(np.isfinite(g)) and (kap < -189).any()
+        _check(g, kap, mg, q, k, v, fmt, okw, pfmt, mode, causal)
+
+
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m3", "e2m1"])
 def test_guess_at_the_low_threshold(fmt):
     """Guesses about 127 - pl binades above the rows, so that their top

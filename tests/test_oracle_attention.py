@@ -397,16 +397,17 @@ def test_top_block_always_lands_in_the_placement_binade(fmt):
     """The invariant the fallback keeps in the block map: in every row, its
     largest value, in units of its block's scale, lies in the placement
     binade [2^pl, 2^(pl+1)), whether the row sits above its guess, near it,
-    or far below it (guesses from 200 binades below to 200 above, across the
-    largest shift of 127 - pl binades)."""
+    or far below it (guesses from 200 binades below the row to 500 above it,
+    across the largest shift of 127 - pl binades and past the 189 binades
+    that the scores' fp32 bit patterns reach)."""
     f = FORMATS[fmt]
     pl = O.attention.placement_exponent(f)
     rng = np.random.default_rng(41)
     s = rng.normal(0.0, 2.0, (400, 96))
     top = s.max(axis=1)
-    # guess-relative top scores spread over [-200, 200], with rows packed
+    # guess-relative top scores spread over [-500, 200], with rows packed
     # around the low threshold -(127 - pl)
-    off = np.concatenate([rng.uniform(-200, 200, 200), -(127 - pl) + rng.uniform(-2, 2, 200)])
+    off = np.concatenate([rng.uniform(-500, 200, 200), -(127 - pl) + rng.uniform(-2, 2, 200)])
     m = top - off
     vis = np.ones_like(s, bool)
     fp = fused_probabilities(s, m, vis, fmt)

@@ -192,3 +192,20 @@ def random_bf16(shape, seed: int, scale: float = 1.0) -> np.ndarray:
     """Plain N(0, scale^2) bf16 bits for unit tests of arbitrary shapes."""
     x = np.random.default_rng(seed).standard_normal(shape, dtype=np.float32) * np.float32(scale)
     return f32_to_bf16_bits(x)
+
+
+def two_valued_keys(B: int, H: int, S: int, D: int, seed: int, a: float = 1.9,
+                    gain=(1.0, 2.0), noise: float = 0.3):
+    """Q, K, V bf16 bits [B, H, S, D] whose keys take two opposite directions:
+    k_j = +-a (alternating in j) plus N(0, noise^2) per element, and
+    q_i = r_i a with r_i uniform in ``gain``, plus the same noise.  Every
+    row's scores split into a high and a low cluster, a light upper tail: a
+    guess built from the window's mean and spread lands far above the row's
+    top score."""
+    rng = np.random.default_rng(seed)
+    sign = np.where(np.arange(S) % 2 == 0, 1.0, -1.0)[:, None]
+    r = rng.uniform(gain[0], gain[1], size=(B, H, S, 1))
+    q = r * a + noise * rng.standard_normal((B, H, S, D))
+    k = sign * a + noise * rng.standard_normal((B, H, S, D))
+    v = rng.standard_normal((B, H, S, D))
+    return tuple(f32_to_bf16_bits(x.astype(np.float32)) for x in (q, k, v))
