@@ -166,6 +166,20 @@ def test_probability_exact_at_integer_exponents_and_bounded(fmt):
     assert np.all(ratio <= 1.0615 * (1.0 + half_ulp) + 1e-6)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_v_power_of_two_and_column_order(fmt):
+    """V enters only through its MX blocks along the keys: scaled by 2^k it
+    keeps its codes (the output scales exactly), and its columns permuted
+    permute the output's columns.  A V quantised along D instead, or a scale
+    applied to the wrong column, fails one of the two."""
+    q, k, v = _head(96, 64, 600)
+    base = O.fused_attention(q, k, v, fmt, causal=True)
+    for e in (-90, 33):
+        assert np.array_equal(O.fused_attention(q, k, v * 2.0 ** e, fmt, causal=True), base * 2.0 ** e)
+    perm = np.random.default_rng(601).permutation(64)
+    assert np.array_equal(O.fused_attention(q, k, v[:, perm], fmt, causal=True), base[:, perm])
+
+
 def test_causal_row_equals_shorter_noncausal_problem():
     q, k, v = _head(192, 64, 400)
     for fmt in FMTS:
