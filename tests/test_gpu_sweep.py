@@ -10,7 +10,9 @@ whose rows are re-based downwards.  The
 bar is the one of the other parity tests (tests/parity.py).  A second sweep
 draws the same kinds of shapes for each P~ variant (one format per call); a
 third draws extreme score spreads (input scales 0.05 to 6: nearly uniform
-rows up to rows whose scores spread over a hundred binades) in every map; a
+rows up to rows whose scores spread over a hundred binades) in every map,
+and another keys in two opposite clusters (rows up to hundreds of binades
+below their frozen max with no bias; workloads.two_valued_keys); a
 fourth passes each of q, k, v and out in its own layout (contiguous
 [B, H, S, D], a [B, S, H, D] tensor viewed as [B, H, S, D], or rows padded
 to a longer stride); a fifth compares the allocation-free entry point with
@@ -137,6 +139,45 @@ def test_extreme_score_spreads_all_rows(case):
     announce("fsa extreme sweep", _xid(case))
     q, k, v = (W.random_bf16((1, 1, S, D), 1300 + 3 * i + j, scale if j < 2 else 1.0)
                for j in range(3))
+    g, kap, mg = _vrun(q, k, v, fmt, name, causal, guess_bias=bias)
+    _vcheck(g, kap, mg, q, k, v, fmt, okw, pfmt, mode, causal, bias=bias)
+
+
+def _cluster_cases(n=24, seed=2031):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        var = MAPS[int(rng.integers(0, len(MAPS)))]
+        H = int(rng.integers(1, 3))
+        S = int(rng.integers(1, 901))
+        D = int(rng.choice([64, 128]))
+        causal = bool(rng.integers(0, 2))
+        a = float(rng.uniform(0.3, 2.5))
+        period = int(rng.choice([2, 3, 8, 32]))
+        noise = float(rng.choice([0.05, 0.3, 1.0]))
+        bias = float(rng.choice([0.0, 0.0, -8.0, 32.0]))
+        out.append((i, var, H, S, D, causal, a, period, noise, bias))
+    return out
+
+
+TCASES = _cluster_cases()
+
+
+def _tid(c):
+    i, var, H, S, D, causal, a, period, noise, bias = c
+    return "t%02d-%s-%s-H%dS%dD%d%s-a%.2f-p%d-n%g-b%g" % (i, var[0], var[1], H, S, D,
+                                                         "-causal" if causal else "", a, period,
+                                                         noise, bias)
+
+
+@pytest.mark.parametrize("case", TCASES, ids=[_tid(c) for c in TCASES])
+def test_clustered_keys_all_rows(case):
+    """Keys in two opposite clusters (one in ``period`` high): rows from near
+    their frozen max to hundreds of binades below it, with no bias."""
+    i, (name, fmt, okw, pfmt, mode), H, S, D, causal, a, period, noise, bias = case
+    announce("fsa clustered-keys sweep", _tid(case))
+    q, k, v = W.two_valued_keys(1, H, S, D, seed=1700 + i, a=a, gain=(0.2, 2.0), noise=noise,
+                                period=period)
     g, kap, mg = _vrun(q, k, v, fmt, name, causal, guess_bias=bias)
     _vcheck(g, kap, mg, q, k, v, fmt, okw, pfmt, mode, causal, bias=bias)
 

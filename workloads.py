@@ -195,15 +195,15 @@ def random_bf16(shape, seed: int, scale: float = 1.0) -> np.ndarray:
 
 
 def two_valued_keys(B: int, H: int, S: int, D: int, seed: int, a: float = 1.9,
-                    gain=(1.0, 2.0), noise: float = 0.3):
+                    gain=(1.0, 2.0), noise: float = 0.3, period: int = 2):
     """Q, K, V bf16 bits [B, H, S, D] whose keys take two opposite directions:
-    k_j = +-a (alternating in j) plus N(0, noise^2) per element, and
-    q_i = r_i a with r_i uniform in ``gain``, plus the same noise.  Every
-    row's scores split into a high and a low cluster, a light upper tail: a
-    guess built from the window's mean and spread lands far above the row's
-    top score."""
+    k_j = +a for j a multiple of ``period``, -a otherwise, plus N(0, noise^2)
+    per element, and q_i = r_i a with r_i uniform in ``gain``, plus the same
+    noise.  Every row's scores split into a high and a low cluster, a light
+    upper tail: a guess built from the window's mean and spread lands far
+    above the row's top score (with period 2 by about 3.6 times the top)."""
     rng = np.random.default_rng(seed)
-    sign = np.where(np.arange(S) % 2 == 0, 1.0, -1.0)[:, None]
+    sign = np.where(np.arange(S) % period == 0, 1.0, -1.0)[:, None]
     r = rng.uniform(gain[0], gain[1], size=(B, H, S, 1))
     q = r * a + noise * rng.standard_normal((B, H, S, D))
     k = sign * a + noise * rng.standard_normal((B, H, S, D))
