@@ -35,11 +35,16 @@ no formulas, so each step below is a reading:
 2. s_ij = sum_d q'^_id k^_jd (log2-domain scores).  Key j is visible to row i
    if j < S and, when causal, j <= i.
 3. Frozen max (``frozen_max``): from the visible keys among the first 128,
-   m~_i = fp32(max(window max, mean + z_i * std) + bias), population std,
-   z_i = sqrt(2 ln n_i) + 1 with n_i the row's visible keys.  The pages fix
-   no rule; the mean + z*std term is the expected Gaussian extreme over n_i
-   keys plus one standard deviation of margin, so that a well-behaved row
-   rarely exceeds it.  ``bias`` (binades) is a test hook, 0 in normal use.
+   m~_i = fp32(min(max(w, mean + z_i * std), w + 64) + bias) with w the
+   window max, population std, z_i = sqrt(2 ln n_i) + 1 with n_i the row's
+   visible keys.  The pages fix no rule; the mean + z*std term is the
+   expected Gaussian extreme over n_i keys plus one standard deviation of
+   margin, so that a well-behaved row rarely exceeds it.  The cap of 64
+   binades above the window max only binds on rows whose scores fall into
+   far-apart clusters (a light upper tail): the row's top score is at least
+   w, so the cap keeps every row within 65 binades below its guess, where
+   the block shifts place it exactly.  ``bias`` (binades) is a test hook, 0
+   in normal use.
 4. The fast exponential is the bit-pattern one (``mitchell_exp2``): read as
    a float, the integer 2**23 * (127 + x) is 2**floor(x) * (1 + frac(x)),
    i.e. 2**x linearly interpolated between integer exponents.  Because x is
@@ -94,6 +99,7 @@ from .mx import (FORMATS, BLOCK, Format, decode, encode_values, round_to_format,
 
 WINDOW = 128          # keys that feed the frozen-max guess
 Z_MARGIN = 1.0        # standard deviations above the expected Gaussian extreme
+GUESS_CAP = 64.0      # largest lead of the guess over the window max, binades
 LOG2E = 1.0 / math.log(2.0)
 
 
@@ -165,8 +171,8 @@ def frozen_max(s: np.ndarray, vis: np.ndarray, bias: float = 0.0) -> np.ndarray:
     values as float64.  The pages say only that the max is fixed
     speculatively and frozen before the fused product (Moving softmax to
     matrix operations speeds up AI inference by over 2x, "Read it as" and
-    the "How it works" figure); the window, the extreme-value term and its
-    margin are this build's reading.
+    the "How it works" figure); the window, the extreme-value term, its
+    margin and the cap over the window max are the reading taken here.
     """
     w = vis[:, :WINDOW]
     sw = s[:, :WINDOW]
@@ -176,7 +182,7 @@ def frozen_max(s: np.ndarray, vis: np.ndarray, bias: float = 0.0) -> np.ndarray:
     mean = np.where(w, sw, 0.0).sum(axis=1) / cnt
     var = np.where(w, (sw - mean[:, None]) ** 2, 0.0).sum(axis=1) / cnt
     z = np.sqrt(2.0 * np.log(n_vis)) + Z_MARGIN
-    guess = np.maximum(wmax, mean + z * np.sqrt(var)) + bias
+    guess = np.minimum(np.maximum(wmax, mean + z * np.sqrt(var)), wmax + GUESS_CAP) + bias
     return guess.astype(np.float32).astype(np.float64)
 
 

@@ -507,8 +507,12 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int b, const 
     const float sd = __builtin_sqrtf(ss / (float)(cnt > 0 ? cnt : 1));
     const int nvis = CAUSAL ? (q + 1 < S ? q + 1 : S) : S;
     const float z = __builtin_sqrtf(2.0f * __builtin_logf((float)nvis)) + 1.0f;
-    // statistics of 2^23 s (or s), back to binades (exact power-of-two scaling)
-    mg = __builtin_fmaxf(mx, mean + z * sd) * (EXPX ? 1.0f : 0x1p-23f) + a.bias;
+    // statistics of 2^23 s (or s), back to binades (exact power-of-two
+    // scaling); the guess leads the window max by at most GUESS_CAP binades,
+    // so that no row lies beyond the block shifts' reach below it
+    constexpr float CAPU = (float)GUESS_CAP * (EXPX ? 1.0f : 8388608.0f);
+    mg = __builtin_fminf(__builtin_fmaxf(mx, mean + z * sd), mx + CAPU) * (EXPX ? 1.0f : 0x1p-23f) +
+         a.bias;
     // stored now, so that it need not stay live across the sweep
     if (q < S && hh == 0) a.row_mguess[(bh - a.row_bh0) * S + q] = mg;
   }

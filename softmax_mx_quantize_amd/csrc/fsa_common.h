@@ -79,6 +79,13 @@ constexpr int HI_BINADE = 1 << 18;
 // Largest guess-relative block binade the main sweep absorbs by block shifts
 // alone; rows above it go to the re-based fallback pass.
 constexpr int EXT = 64;
+// Largest lead of the frozen max over the row's window max, in binades.  A
+// row's top score is at least its window max, so its top block lies at most
+// GUESS_CAP + 1 binades below the guess: within the largest block shift
+// (127 - pl >= 119 binades for every P~ format), so that only a positive
+// guess bias can send a row of a block map to the downward fallback.
+constexpr int GUESS_CAP = 64;
+static_assert(GUESS_CAP + 1 < 127 - 8, "capped guesses must stay within the block shifts");
 static_assert(HI_BINADE > EXT, "clamped binades must reach the fallback pass");
 // Lowest offset the fallback pass measures: rows down to HI_BINADE binades
 // below their guess (the frozen max can lie far above a row whose scores

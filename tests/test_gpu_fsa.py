@@ -211,17 +211,23 @@ def test_rows_far_above_the_guess_causal(fmt):
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("causal", [False, True])
-def test_rows_far_below_their_frozen_max(fmt, causal):
-    """Keys in two opposite clusters: the window's mean + z * std lies
-    200 to 420 binades above each row's top score (bias 0), beyond the
-    reach of the scores' fp32 bit patterns (189 binades); the fallback pass
-    measures each row's offset from its scores and re-bases it downwards."""
-    announce("fsa far below", fmt, causal)
+def test_clustered_keys_under_the_capped_guess(fmt, causal):
+    """Keys in two opposite clusters: the window's mean + z * std lies 200 to
+    420 binades above each row's top score; the cap holds the guess at 64
+    binades above the window max, so no row falls back.  Raised by a bias of
+    150 binades, the same rows lie about 214 binades below their guess,
+    beyond the reach of the scores' fp32 bit patterns (189 binades): the
+    fallback pass measures their offsets from the scores and re-bases them
+    downwards."""
+    announce("fsa clustered keys", fmt, causal)
     q, k, v = W.two_valued_keys(1, 2, 600, 128, seed=41)
     g, kap, mg = _run(q, k, v, fmt, causal)
     ref, rk, bd, inf = _oracle_heads(q, k, v, [fmt] * 2, causal)
-    assert (rk < -300).any() and np.mean(rk < -189) > 0.9
-    assert np.all(np.isfinite(g))
+    assert np.all(rk == 0) and np.all(kap == 0)
+    _check(g, kap, mg, ref, rk, bd, inf)
+    g, kap, mg = _run(q, k, v, fmt, causal, guess_bias=150.0)
+    ref, rk, bd, inf = _oracle_heads(q, k, v, [fmt] * 2, causal, bias=150.0)
+    assert np.mean(rk < -189) > 0.9 and np.all(np.isfinite(g))
     _check(g, kap, mg, ref, rk, bd, inf)
 
 

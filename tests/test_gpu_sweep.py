@@ -11,8 +11,8 @@ bar is the one of the other parity tests (tests/parity.py).  A second sweep
 draws the same kinds of shapes for each P~ variant (one format per call); a
 third draws extreme score spreads (input scales 0.05 to 6: nearly uniform
 rows up to rows whose scores spread over a hundred binades) in every map,
-and another keys in two opposite clusters (rows up to hundreds of binades
-below their frozen max with no bias; workloads.two_valued_keys); a
+and another keys in two opposite clusters (the guess's extreme-value term
+far above the rows and held by its cap; workloads.two_valued_keys); a
 fourth passes each of q, k, v and out in its own layout (contiguous
 [B, H, S, D], a [B, S, H, D] tensor viewed as [B, H, S, D], or rows padded
 to a longer stride); a fifth compares the allocation-free entry point with
@@ -155,7 +155,7 @@ def _cluster_cases(n=24, seed=2031):
         a = float(rng.uniform(0.3, 2.5))
         period = int(rng.choice([2, 3, 8, 32]))
         noise = float(rng.choice([0.05, 0.3, 1.0]))
-        bias = float(rng.choice([0.0, 0.0, -8.0, 32.0]))
+        bias = float(rng.choice([0.0, 0.0, -8.0, 32.0, 150.0]))
         out.append((i, var, H, S, D, causal, a, period, noise, bias))
     return out
 
@@ -172,8 +172,10 @@ def _tid(c):
 
 @pytest.mark.parametrize("case", TCASES, ids=[_tid(c) for c in TCASES])
 def test_clustered_keys_all_rows(case):
-    """Keys in two opposite clusters (one in ``period`` high): rows from near
-    their frozen max to hundreds of binades below it, with no bias."""
+    """Keys in two opposite clusters (one in ``period`` high): the guess's
+    extreme-value term far above the rows, held by its cap to 64 binades
+    above the window max; with a bias of 150, rows beyond 189 binades below
+    their guess."""
     i, (name, fmt, okw, pfmt, mode), H, S, D, causal, a, period, noise, bias = case
     announce("fsa clustered-keys sweep", _tid(case))
     q, k, v = W.two_valued_keys(1, H, S, D, seed=1700 + i, a=a, gain=(0.2, 2.0), noise=noise,

@@ -168,16 +168,22 @@ def test_guess_230_binades_above_rows(case, causal):
 
 
 @pytest.mark.parametrize("variant", VARIANTS, ids=IDS)
-def test_variant_rows_far_below_their_frozen_max(variant):
-    """Two opposite key clusters (bias 0): every row 200 to 420 binades
-    below its frozen max, re-based downwards by the fallback pass."""
+def test_variant_clustered_keys(variant):
+    """Two opposite key clusters: under the capped guess (64 binades above
+    the window max) no row of a block map falls back, while one scale per
+    row flushes such rows and re-bases them downwards; raised by a bias of
+    150 binades, every row lies beyond 189 binades below its guess and is
+    re-based downwards in every map."""
     name, fmt, okw, pfmt, mode = variant
-    announce("variant far below", name, fmt)
+    announce("variant clustered keys", name, fmt)
     q, k, v = W.two_valued_keys(1, 2, 600, 128, seed=42)
     for causal in (False, True):
         g, kap, mg = _run(q, k, v, fmt, name, causal)
-        assert np.all(np.isfinite(g)) and (kap < -189).any()
+        assert np.all(np.isfinite(g)) and np.all(kap >= -65) and (mode == "row" or np.all(kap == 0))
         _check(g, kap, mg, q, k, v, fmt, okw, pfmt, mode, causal)
+        g, kap, mg = _run(q, k, v, fmt, name, causal, guess_bias=150.0)
+        assert np.all(np.isfinite(g)) and (kap < -189).any()
+        _check(g, kap, mg, q, k, v, fmt, okw, pfmt, mode, causal, bias=150.0)
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m3", "e2m1"])

@@ -89,6 +89,27 @@ def test_frozen_max_worked_example():
     assert frozen_max(s, vis)[0] == 9.0
 
 
+def test_frozen_max_capped_example():
+    """Two far-apart clusters in the window: the extreme-value term would
+    put the guess 440 binades above the window max; the cap holds it at 64
+    above (hand-worked golden), and a bias adds after the cap."""
+    lines = dict(l.split(None, 1) for l in open(os.path.join(GOLDEN, "frozen_max_capped_example.txt"))
+                 if l.strip() and not l.startswith("#"))
+    S = int(lines["S"])
+    expected = float(lines["expected"])
+    s = np.zeros((1, S))
+    s[0, :WINDOW] = np.where(np.arange(WINDOW) % 2 == 0, 100.0, -100.0)
+    s[0, WINDOW:] = -500.0
+    vis = np.ones((1, S), bool)
+    assert frozen_max(s, vis)[0] == expected
+    assert frozen_max(s, vis, bias=-8.0)[0] == expected - 8.0
+    # every row of a block map then stays within its largest shift: no row
+    # falls back, and the top block lands in the placement binade
+    for fmt in FMTS:
+        fp = fused_probabilities(s, frozen_max(s, vis), vis, fmt)
+        assert fp["kappa"][0] == 0 and fp["delta"][0].min() == 64
+
+
 def _mitchell_value(x):
     """2**floor(x) * (1 + frac(x)) via math, not via bit patterns."""
     fl = math.floor(x)
