@@ -123,23 +123,26 @@ __device__ __forceinline__ int swz_k32(int row) {
 }
 __device__ __forceinline__ int swz_v32(int row) { return (row >> 1) & 7; }
 
-// The lane's Q' operand for 64-wide D chunk c of the FP8 score product:
-// elements [64c + 16h, +16) and [64c + 32 + 16h, +16), i.e. half of D block
-// 2c and half of block 2c+1; the other halves are in the lane 32 apart.  Same
+// Columns of the pieces of the lane's FP8 Q' operand for 64-wide D chunk c:
+// elements [64c + 16h, +16) and [64c + 32 + 16h, +16).
+__device__ __forceinline__ void q_cols32(int c, int hh, int (&col)[4]) {
+#pragma unroll
+  for (int ch = 0; ch < 4; ++ch) col[ch] = 64 * c + 16 * hh + (ch < 2 ? 8 * ch : 32 + 8 * (ch - 2));
+}
+
+// The lane's Q' operand for 64-wide D chunk c of the FP8 score product,
+// from the bf16 words of q_words over q_cols32(c, hh): half of D block 2c
+// and half of block 2c+1; the other halves are in the lane 32 apart.  Same
 // rule as the quantiser (OCP floor scale, RNE, saturation, NaN/Inf blocks
 // get scale 0xFF and zero codes), Q' = fp32(q * mult), 2^23 raised onto the
 // E8M0 byte.  `sc` is the byte of block 2c + h, which this lane supplies.
-template <int D, int RAISE>
-__device__ __forceinline__ v8i q_operand32_e4m3(const uint16_t* row, float mult, int c, int hh,
-                                               int& sc) {
+template <int RAISE>
+__device__ __forceinline__ v8i q_operand32_e4m3(const uint4 (&qw)[4], float mult, int hh, int& sc) {
   float v[32];
   bool bad_lo = false, bad_hi = false;
 #pragma unroll
   for (int ch = 0; ch < 4; ++ch) {
-    const int col = 64 * c + 16 * hh + (ch < 2 ? 8 * ch : 32 + 8 * (ch - 2));
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (row != nullptr && col < D) w = *reinterpret_cast<const uint4*>(row + col);
-    const uint32_t hw[4] = {w.x, w.y, w.z, w.w};
+    const uint32_t hw[4] = {qw[ch].x, qw[ch].y, qw[ch].z, qw[ch].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t lo = hw[e] & 0xFFFF, hi = hw[e] >> 16;
@@ -369,11 +372,26 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int b, const 
   // bf16 row with 2^23 on its E8M0 scale
   opv<F> qf[ND];
   int qsc[ND];
+  {
+    // every chunk's words first (one wait for all of them), then the codes;
+    // a padding row reads the last row and zeroes it
+    const uint16_t* qrow = a.q + b * a.q_sb + h * a.q_sh + (int64_t)(q < S ? q : S - 1) * a.q_ss;
+    uint4 qw[ND][4];
 #pragma unroll
-  for (int c = 0; c < ND; ++c) {
-    const uint16_t* qrow = q < S ? a.q + b * a.q_sb + h * a.q_sh + (int64_t)q * a.q_ss : nullptr;
-    if constexpr (BITS == 8) qf[c] = q_operand32_e4m3<D, QRAISE>(qrow, a.qmul, c, hh, qsc[c]);
-    else qf[c] = q_operand<F, D, QRAISE>(qrow, a.qmul, 2 * c + hh, qsc[c]);
+    for (int c = 0; c < ND; ++c) {
+      int col[4];
+      if constexpr (BITS == 8) q_cols32(c, hh, col);
+      else q_cols(2 * c + hh, col);
+      q_words(qrow, q < S, col, qw[c]);
+    }
+    // (left to itself the FP8 schedule issues the second chunk's loads only
+    // after the first chunk's codes)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < ND; ++c) {
+      if constexpr (BITS == 8) qf[c] = q_operand32_e4m3<QRAISE>(qw[c], a.qmul, hh, qsc[c]);
+      else qf[c] = q_operand<F, QRAISE>(qw[c], a.qmul, qsc[c]);
+    }
   }
 
   // ---- lane-constant LDS offsets.  Score product, chunk u, block b, D chunk
@@ -924,6 +942,14 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int b, const 
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
+// Byte i of a byte table in the kernel arguments, read as its aligned
+// dword: a uniform index then gives a scalar load, which the constant cache
+// serves, where a byte load went to memory and back before anything else.
+__device__ __forceinline__ int table_byte(const uint8_t* t, int i) {
+  const uint32_t w = reinterpret_cast<const uint32_t*>(t)[i >> 2];
+  return (int)((w >> (8 * (i & 3))) & 0xFFu);
+}
+
 // The attention kernel over the heads [h0, h0 + hrun) of every batch entry,
 // each in its own element format from FSET (a bit set of FMT_*): one
 // launch for a hybrid schedule.  PM is the P~ variant; PX picks a P~
@@ -953,13 +979,13 @@ fsa_fwd_kernel(AttnArgs a) {
   if (item >= n_items) return;
   const int bs = item / nq;                  // (batch entry, head slot)
   const int b = bs / a.hrun;
-  const int j = a.horder[bs - b * a.hrun];   // head within the launch
+  const int j = table_byte(a.horder, bs - b * a.hrun);   // head within the launch
   const int64_t wi = (int64_t)b * a.hrun + j;
   // causal: a head's query tiles heaviest first (the last tile sees every
   // key), so that the light ones fill the end of the launch
   const int qi = item - bs * nq;
   const int q_wg = (CAUSAL && !REBASE ? nq - 1 - qi : qi) * QW;
-  const int f = (FSET & (FSET - 1)) ? a.hfmt[j] : 0;
+  const int f = (FSET & (FSET - 1)) ? table_byte(a.hfmt, j) : 0;
   with_format<FSET>(f, [&](auto fc) {
     constexpr int FC = decltype(fc)::value;
     constexpr int PF = PX == 1 ? (int)FMT_E4M3 : PX == 2 ? (int)FMT_E3M2 : FC;

@@ -164,25 +164,45 @@ __device__ __forceinline__ v4f row_sum(const v4i& ones, const opv<F>& p, const v
     return mfma_scale_v4(ones, p, c, Fmt<FMT_E2M1>::mfma, Fmt<F>::mfma, 0, 127, 0, sp);
 }
 
+// Raw bf16 words of four 8-element pieces of a Q row, at columns col[0..3]
+// (each inside the row: the callers' chunks lie below D).  The loads are
+// unconditional, a padding row (valid false) reading a real row and zeroing
+// what it got, so that the compiler issues every piece of every chunk
+// before the first wait: branches around them made it wait for each load
+// in turn (vmcnt(0), which also drains the tile DMA in flight).  The mask
+// is opaque, or the compiler would move each load back under a branch.
+__device__ __forceinline__ void q_words(const uint16_t* row, bool valid, const int (&col)[4],
+                                        uint4 (&w)[4]) {
+  uint32_t m = valid ? 0xFFFFFFFFu : 0u;
+  asm volatile("" : "+v"(m));
+#pragma unroll
+  for (int ch = 0; ch < 4; ++ch) {
+    const uint4 x = *reinterpret_cast<const uint4*>(row + col[ch]);
+    w[ch] = make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
+  }
+}
+// Columns of the pieces of MX block g of a Q row (FP6/FP4 operands).
+__device__ __forceinline__ void q_cols(int g, int (&col)[4]) {
+#pragma unroll
+  for (int ch = 0; ch < 4; ++ch) col[ch] = 32 * g + 8 * ch;
+}
+
 // The lane's Q' operand of the score product, MX-quantised here from the
-// bf16 row (the same rule as the quantiser: OCP floor scale, RNE, saturation,
-// NaN/Inf blocks get scale 0xFF and zero codes) with Q' = fp32(q * mult).
-// `row` is null for padding rows.  Returns the codes in operand order and
-// sets `sc` to the E8M0 byte of the block this lane group scales, raised by
-// RAISE (2^23 rides on Q's scale for the bit-pattern exponential; 255 stays
-// NaN).
-template <int F, int D, int RAISE>
-__device__ __forceinline__ opv<F> q_operand(const uint16_t* row, float mult, int g, int& sc) {
+// bf16 words of MX block g (q_words over q_cols(g); the same rule as the
+// quantiser: OCP floor scale, RNE, saturation, NaN/Inf blocks get scale 0xFF
+// and zero codes) with Q' = fp32(q * mult).  Returns the codes in operand
+// order and sets `sc` to the E8M0 byte of the block this lane group scales,
+// raised by RAISE (2^23 rides on Q's scale for the bit-pattern exponential;
+// 255 stays NaN).
+template <int F, int RAISE>
+__device__ __forceinline__ opv<F> q_operand(const uint4 (&qw)[4], float mult, int& sc) {
   static_assert(Fmt<F>::bits != 8, "FP8 Q' operands: q_operand32_e4m3");
   float v[32];
   bool bad = false;
   // element k of the operand: column 32g + k
 #pragma unroll
   for (int c = 0; c < 4; ++c) {                      // four 8-element chunks
-    const int col = 32 * g + 8 * c;
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (row != nullptr && col < D) w = *reinterpret_cast<const uint4*>(row + col);
-    const uint32_t h[4] = {w.x, w.y, w.z, w.w};
+    const uint32_t h[4] = {qw[c].x, qw[c].y, qw[c].z, qw[c].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t lo = h[e] & 0xFFFF, hi = h[e] >> 16;
@@ -203,7 +223,6 @@ __device__ __forceinline__ opv<F> q_operand(const uint16_t* row, float mult, int
   Pack32<F, true>::run(y, w);
   if (bad) { for (int i = 0; i < 8; ++i) w[i] = 0; }
   sc = bad ? 255 : min(x + 127 + RAISE, 254);
-  if (32 * g >= D) sc = 127;                          // blocks past D: zeros
   opv<F> o;
 #pragma unroll
   for (int i = 0; i < Operand<F>::words; ++i) o[i] = (int)w[i];

@@ -40,20 +40,25 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(64, 64))) q_operand_d
   const int hh = lane >> 5, n = lane & 31;
   const int64_t r = (int64_t)blockIdx.x * 32 + n;
   const bool live = r < a.rows;
-  const uint16_t* qrow = live ? a.q + r * D : nullptr;
+  const uint16_t* qrow = a.q + (live ? r : a.rows - 1) * D;
 #pragma unroll
   for (int c = 0; c < ND; ++c) {
     int sc = 0;
     const int blk = 2 * c + hh;
+    int col[4];
+    uint4 qw[4];
+    if constexpr (BITS == 8) q_cols32(c, hh, col);
+    else q_cols(blk, col);
+    q_words(qrow, live, col, qw);
     if constexpr (BITS == 8) {
-      const v8i o = q_operand32_e4m3<D, 23>(qrow, a.qmul, c, hh, sc);
+      const v8i o = q_operand32_e4m3<23>(qw, a.qmul, hh, sc);
       if (live) {
         uint8_t* row = a.codes + r * RB;
         *reinterpret_cast<uint4*>(row + 64 * c + 16 * hh) = make_uint4(o[0], o[1], o[2], o[3]);
         *reinterpret_cast<uint4*>(row + 64 * c + 32 + 16 * hh) = make_uint4(o[4], o[5], o[6], o[7]);
       }
     } else {
-      const opv<F> o = q_operand<F, D, 23>(qrow, a.qmul, blk, sc);
+      const opv<F> o = q_operand<F, 23>(qw, a.qmul, sc);
       if (live) {
         uint8_t* dst = a.codes + r * RB + blk * 4 * BITS;
         if constexpr (BITS == 6) {

@@ -1,6 +1,8 @@
 // Host-visible launch interfaces between the C ABI layer and the kernels.
 #pragma once
 
+#include <cstddef>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -107,6 +109,10 @@ struct AttnArgs {
   uint8_t hfmt[MAX_HEAD_TABLE];  // element format (FMT_*) of head h0 + j
   uint8_t horder[MAX_HEAD_TABLE];  // head slot -> j: the order workgroups take heads in
 };
+// the kernel reads both byte tables a dword at a time
+static_assert(offsetof(AttnArgs, hfmt) % 4 == 0 && offsetof(AttnArgs, horder) % 4 == 0 &&
+                  MAX_HEAD_TABLE % 4 == 0,
+              "byte tables must be dword-aligned");
 
 // LDS stages of the attention kernel (128-byte rows): one 128-key tile of
 // K^ rows plus its scales, and D rows of V^T plus theirs.
