@@ -177,8 +177,9 @@ typedef struct fsa_options {
    * log2(e) * q.k / sqrt(D)).  A negative value of a few binades makes every
    * row fall back, a positive one of more than 127 - pl (pl: the placement
    * exponent of P~'s format) re-bases every row downwards; 0 in normal use.
-   * Finite with |guess_bias| <= 2^17, else FSA_ERR_INVALID_ARG (the fallback
-   * pass measures offsets within 2^18 binades either way). */
+   * Finite with |guess_bias| <= 1024, else FSA_ERR_INVALID_ARG (the fp32
+   * score sums taken from the biased reference stay fine enough to measure
+   * each row's offset exactly up to that bound). */
   float guess_bias;
   /* Optional device int32 [B][H][S]: receives each row's fallback offset in
    * binades (0 for rows whose scores stayed under the frozen max).  Give

@@ -20,9 +20,12 @@
 namespace {
 
 constexpr int kKeyTile = 128;
-// largest |fsa_options::guess_bias|, in binades: half the span of offsets
-// the fallback pass measures, leaving the rest to the rows' own spread
-constexpr float kMaxGuessBias = 131072.0f;
+// largest |fsa_options::guess_bias|, in binades.  The bias cancels out of
+// the re-based sweep, but the first pass and the fallback pass's measure of
+// a row's offset run from the biased reference: their fp32 score sums, about
+// 2^23 (189 + |bias|) in magnitude, keep a spacing below 2^-12 binade up to
+// this bound, far inside the rounding margins of the offset's binade.
+constexpr float kMaxGuessBias = 1024.0f;
 
 int fmt_bits(int fmt) { return fmt == FSA_MXFP8_E4M3 ? 8 : (fmt == FSA_MXFP6_E2M3 ? 6 : 4); }
 bool fmt_ok(int fmt) { return fmt == FSA_MXFP8_E4M3 || fmt == FSA_MXFP6_E2M3 || fmt == FSA_MXFP4_E2M1; }

@@ -231,6 +231,21 @@ def test_clustered_keys_under_the_capped_guess(fmt, causal):
     _check(g, kap, mg, ref, rk, bd, inf)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_largest_accepted_biases(fmt):
+    """Guesses 1024 binades below and above every row (the bounds the
+    library accepts): the first pass and the measure of each row's offset sum
+    the scores around a reference 2^23 * 1213 from them, and every row still
+    matches the oracle, re-based upwards or downwards by about 1024."""
+    announce("fsa largest biases", fmt)
+    q, k, v = (W.random_bf16((1, 1, 300, 128), seed, 1.0) for seed in (61, 62, 63))
+    for bias in (-1024.0, 1024.0):
+        g, kap, mg = _run(q, k, v, fmt, True, guess_bias=bias)
+        ref, rk, bd, inf = _oracle_heads(q, k, v, [fmt], True, bias=bias)
+        assert np.all(np.abs(rk + bias) < 100) and np.all(np.isfinite(g))
+        _check(g, kap, mg, ref, rk, bd, inf)
+
+
 def test_hybrid_heads_two_batches():
     """Per-head formats in one call with B = 2: each run of equal formats is
     quantised and launched per batch entry."""
