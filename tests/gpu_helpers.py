@@ -82,7 +82,8 @@ def kappa_low(pfmt, mode):
 
 def check_frozen_max(gpu_m_tilde, info):
     """The kernel's frozen max against the oracle's.  It is mean + z std (or
-    the window's max) evaluated in fp32 from the kernel's scores, so its
+    the window's max, or that max plus the 64-binade cap) evaluated in fp32
+    from the kernel's scores, so its
     error follows the magnitude of the window's scores, not of the guess
     itself (which can be near zero: two keys at -1.7 and -4.3)."""
     win = info["visible"][:, :128]
