@@ -63,7 +63,8 @@ typedef enum fsa_fmt {
  * fsa_quantize_mx -- MX block quantisation of a bf16 tensor.
  *
  * MX operands of the attention products (Fused-Softmax for efficient
- * quantized attention, summary: "MXFP8, MXFP6 and MXFP4 kernels"); encodings
+ * quantized attention, summary: the pages' kernels take MX operands in three
+ * element widths, 8, 6 and 4 bits); encodings
  * and block-scale rule of the OCP Microscaling Formats v1.0 specification:
  * scale X = clamp(floor(log2(amax)) - emax, -127, 127) (X = -127 for an
  * all-zero block), elements x / 2^X rounded to nearest-even and saturated to
@@ -119,9 +120,9 @@ int fsa_attention_fwd(const void* q, const void* k, const void* v, void* out,
 /*
  * fsa_attention_bf16_ref -- plain BF16 flash attention (in-house baseline).
  *
- * The "BF16 attention" the pages compare against (Fused-Softmax for
- * efficient quantized attention, summary; the "Softmax (Vector)" path of the
- * "How it works" figure): bf16 matrix-core products with fp32 accumulation,
+ * The unquantised attention the pages measure their speedups against
+ * (Fused-Softmax for efficient quantized attention, summary; the vector-unit
+ * softmax path of the "How it works" figure): bf16 matrix-core products with fp32 accumulation,
  * exact exponential, online row max and rescaling on the vector units.
  * V is first transposed into the library workspace (B*H*D*S' bf16, S'
  * being S rounded up to 64), which it shares with fsa_attention_fwd.

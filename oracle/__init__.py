@@ -11,8 +11,8 @@ against its sources:
   (sections "Read it as" and "How it works", with its before/after figure),
   "EFQ-Softmax: Exp-Free Quantization for Softmax" (abstract);
 * the OCP Microscaling Formats (MX) v1.0 specification for the element and
-  scale encodings, which the pages name ("MXFP8, MXFP6 and MXFP4") without
-  defining.
+  scale encodings, which the pages name by format (MX FP8, FP6 and FP4)
+  without defining.
 
 Where the pages leave a step open the oracle takes one plain reading and
 says so in the docstring of the function that implements it.

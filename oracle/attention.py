@@ -5,12 +5,14 @@ arithmetic unless a step says otherwise:
 
 * ``exact_attention`` -- softmax(q k^T / sqrt(D)) v on the unquantised bf16
   inputs: the ground truth the error criterion is measured against.
-* ``plain_mx_attention`` -- the "exp-then-quantize" path on the very same MX
-  operands as the fused path (the pre-scaled q' of step 1, k, v): exact row
-  max, exact exponential, then the probabilities MX-quantised along the keys
-  before the PV product.  Its error is the floor set by quantising the GEMM
-  operands (Fused-Softmax for efficient quantized attention, summary;
-  EFQ-Softmax: Exp-Free Quantization for Softmax, abstract), so that the
+* ``plain_mx_attention`` -- the path that exponentiates, then quantises, on
+  the very same MX operands as the fused path (the pre-scaled q' of step 1,
+  k, v): exact row max, exact exponential, then the probabilities
+  MX-quantised along the keys before the PV product.  Its error is what
+  quantising the products' operands costs on its own, the bar the fused
+  path's extra error is held under (Fused-Softmax for efficient quantized
+  attention, summary; EFQ-Softmax: Exp-Free Quantization for Softmax,
+  abstract), so that the
   fused/plain comparison isolates the approximated exponential and the
   frozen max.
 * ``fused_attention`` -- Fused-Softmax attention as specified below.

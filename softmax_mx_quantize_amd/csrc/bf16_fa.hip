@@ -1,8 +1,8 @@
 // Plain BF16 flash attention on gfx950: the in-house baseline.
 //
-// This is the "BF16 attention" the fused-softmax kernels are compared with
-// (Fused-Softmax for efficient quantized attention, summary) and the
-// "Softmax (Vector)" path of the "How it works" figure in Moving softmax to
+// This is the unquantised attention the fused-softmax kernels are compared
+// with (Fused-Softmax for efficient quantized attention, summary) and the
+// vector-unit softmax path of the "How it works" figure in Moving softmax to
 // matrix operations speeds up AI inference by over 2x: bf16 products on the
 // matrix cores with fp32 accumulation, and a softmax on the vector units with
 // an exact exponential and a running row max that rescales the running output
