@@ -4,7 +4,8 @@ the library's own output rather than the oracle:
 * V scaled by a power of two: the MX blocks of V keep their codes and only
   their E8M0 scales move, P~ and the row sums do not depend on V, so the
   output scales by the same power exactly (while no value leaves bf16's
-  normal range and the fp32 sums stay finite);
+  normal range and the fp32 sums stay finite), also for rows shifted within
+  the sweep or re-based by the fallback pass;
 * V's columns permuted: each output column is the product of P~ with one
   column of V (V is quantised along the keys, column by column), so the
   output's columns follow;
@@ -70,6 +71,24 @@ def test_v_scaled_by_a_power_of_two(case, causal):
         g, kap, mg = _call(q, k, _scaled_bits(v, e), name, fmt, causal)
         _same(g, g0 * 2.0 ** e)
         assert np.array_equal(kap, k0) and np.array_equal(mg, m0)
+
+
+@pytest.mark.parametrize("case", CASES, ids=IDS)
+def test_v_scaled_through_the_fallbacks(case):
+    """The same exactness for rows above their guess: by about 60 binades
+    (their blocks take larger scales within the sweep, so the products sum
+    P~ values near 2^60 before the division) and by about 100 (re-based by
+    the fallback pass)."""
+    name, fmt = case
+    announce("property: V * 2^k, shifted rows", name, fmt)
+    q, k, v = (W.random_bf16((1, 2, 333, 128), seed, 1.0) for seed in (141, 142, 143))
+    for bias in (-60.0, -100.0):
+        g0, k0, m0 = _call(q, k, v, name, fmt, guess_bias=bias)
+        assert np.all(k0 >= 55)
+        for e in (-60, 40):
+            g, kap, mg = _call(q, k, _scaled_bits(v, e), name, fmt, guess_bias=bias)
+            _same(g, g0 * 2.0 ** e)
+            assert np.array_equal(kap, k0) and np.array_equal(mg, m0)
 
 
 @pytest.mark.parametrize("case", CASES, ids=IDS)
