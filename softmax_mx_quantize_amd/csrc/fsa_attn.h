@@ -626,10 +626,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int b, const 
   // 16h + i and 32 + 16h + i); one swap of the half maxima with the lane 32
   // apart gives every lane the maximum of block h, which it scales in the
   // P V product, and a second swap hands it the byte of the other block.
-  // One scale per row (E4M3): no block maxima; every block takes the row's
-  // placement scale, and a value that rounds beyond 448 becomes the NaN
-  // code 0x7F, which the epilogue spots in the packed bytes (the row then
-  // goes to the fallback pass; the products do not carry NaN codes on).  Affine codes (E2M1): the code is
+  // One scale per row (E4M3): every block takes the row's placement scale;
+  // the row's largest pattern tells whether a value rounds beyond 448 (the
+  // row then goes to the fallback pass; the products do not carry the NaN
+  // codes of such values on).  Affine codes (E2M1): the code is
   // clamp(RNE(2 x + 2), 0, 7) of the exponent x relative to the block's
   // placement, formed from the product's output by one FMA and one
   // rounding conversion to a byte.
@@ -642,16 +642,25 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int b, const 
       constexpr int SB0 = 127 - PL;
       uint32_t w[8];
       Pack32<P, false>::run(pv, w, conv_scale(SB0), conv_scale(SB0));
-      // P~ codes are nonnegative, so a value past 448 shows as a byte of
-      // 0x7F (the NaN code): adding 1 to every byte sets its top bit
-      // (no byte carries: every code is at most 0x7F)
-      uint32_t ov = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pw[u][i] = (int)w[i];
-        ov |= w[i] + 0x01010101u;
+      for (int i = 0; i < 8; ++i) pw[u][i] = (int)w[i];
+      // The row overflows once a value reaches 464 (448 plus half its step:
+      // it would round beyond 448), i.e. once a pattern reaches the bits of
+      // 464 times the conversion's divisor.  Compared on the patterns as
+      // integers: a row far above its guess has patterns at or past the
+      // exponent field's top (NaN bit patterns, or the sign bit set), whose
+      // converted codes need not show the overflow.
+      auto uv = [&](int o) __attribute__((always_inline)) { return __float_as_uint(pv[o]); };
+      uint32_t m0 = max(max(uv(0), uv(1)), uv(2));
+      uint32_t m1 = max(max(uv(16), uv(17)), uv(18));
+#pragma unroll
+      for (int p = 3; p < 15; p += 2) {
+        m0 = max(max(m0, uv(p)), uv(p + 1));
+        m1 = max(max(m1, uv(16 + p)), uv(17 + p));
       }
-      over |= ov;
+      m0 = max(max(m0, uv(15)), max(m1, uv(31)));
+      constexpr uint32_t OVER_BITS = __builtin_bit_cast(uint32_t, 464.0f * (float)(1ull << (REF - PL)));
+      over |= m0 >= OVER_BITS ? 0x80u : 0u;
       psc[u] = SB0;
     } else if constexpr (PM == PM_EFQ) {
       float yv[32];
@@ -896,10 +905,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int b, const 
   float lsum;
   if constexpr (L32) lsum = L[0];
   else lsum = __shfl(L[0], n < 16 ? n : n + 16);
-  // one scale per row: a code past the format's range in either half of the
-  // row sends it to the fallback pass, which measures its offset
+  // one scale per row: a value past the format's range in either half of
+  // the row sends it to the fallback pass, which measures its offset
   if constexpr (PM == PM_ROW && !REBASE) {
-    const uint32_t ov = (over | (uint32_t)__shfl_xor((int)over, 32)) & 0x80808080u;
+    const uint32_t ov = (over | (uint32_t)__shfl_xor((int)over, 32)) & 0x80u;
     kap = ov ? KSAT : 0;
   }
   // One scale per row: a row whose every code flushed to zero (a guess more

@@ -30,7 +30,7 @@ from oracle.attention import mitchell_exp2
 from gpu_helpers import (announce, to_dev, from_dev_bf16, rel_l2, workload_tensors, check_kappa,
                          kappa_borderline, check_frozen_max, kappa_free, kappa_rows,
                          kappa_low)
-from parity import excess_rel_l2, eps_rows, kappa_eps
+from parity import excess_rel_l2, eps_rows, kappa_eps, undecided
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
@@ -87,11 +87,13 @@ def _check(g, kap, mg, q, k, v, fmt, okw, pfmt, mode, causal=False, rows=None, b
                                           return_info=True, **okw)
             rws = np.arange(S) if rows is None else np.asarray(rows)
             gr, kr, mr = g[b, h, rws], kap[b, h, rws], mg[b, h, rws]
-            check_frozen_max(mr, info)
-            ex, _ = excess_rel_l2(gr, ref, info, pfmt, eps_rows(mr, info, fmt), mode)
+            check_frozen_max(mr, info, fmt)
+            codes = _borderline(info, rws, S, causal, fmt, pfmt, mode)
+            ex, _ = excess_rel_l2(gr, ref, info, pfmt, eps_rows(mr, info, fmt), mode,
+                                  skip=undecided(codes, kr, info["kappa"]))
             num += (ex * np.linalg.norm(ref)) ** 2
             den += np.linalg.norm(ref) ** 2
-            check_kappa(kr, info["kappa"], _borderline(info, rws, S, causal, fmt, pfmt, mode))
+            check_kappa(kr, info["kappa"], codes)
     err = float(np.sqrt(num / den))
     print("beyond near-tie codes %.2e" % err)
     assert err <= TOL, err
@@ -215,6 +217,34 @@ def test_variant_v_ones(variant):
         assert np.array_equal(g, np.ones_like(g))
 
 
+@pytest.mark.parametrize("lead", [66.5, 67.5, 100.5])
+def test_row_scale_overflow_seen_past_the_pattern_top(lead):
+    """One scale per row: a row whose only value past E4M3's range lies 66 or
+    more binades above its guess.  Its pattern then reaches the top of fp32's
+    exponent field (a NaN bit pattern at 66, the sign bit from 67 on), where
+    the converted code need not show the overflow; the row must still fall
+    back.  One score of row 5 is planted 300 binades above the rest and the
+    bias chosen from the oracle's scores so that it lands ``lead`` binades
+    above the guess, every other value of the row far below."""
+    import oracle.attention as OA
+    announce("row scale overflow past the pattern top", lead)
+    S, D = 200, 64
+    q, k, v = (W.bf16_bits_to_f64(W.random_bf16((1, 1, S, D), seed, 0.3)) for seed in (151, 152, 153))
+    c = OA.score_scale(D)
+    i, j = 5, 150
+    q[0, 0, i] = k[0, 0, j] * (300.0 / (c * float(k[0, 0, j] @ k[0, 0, j])))
+    q, k, v = (W.f32_to_bf16_bits(x.astype(np.float32)) for x in (q, k, v))
+    qh, kh, vh = (W.bf16_bits_to_f64(x[0, 0]) for x in (q, k, v))
+    _, info = O.fused_attention(qh, kh, vh, "e4m3", False, return_info=True, p_mode="row")
+    t = np.sort(info["scores"][i] - info["m_tilde"][i])[::-1]
+    bias = float(np.float32(t[0] - lead))
+    assert t[0] - t[1] > lead + 2.0
+    g, kap, mg = _run(q, k, v, "e4m3", "row", guess_bias=bias)
+    _, info = O.fused_attention(qh, kh, vh, "e4m3", False, return_info=True, p_mode="row", bias=bias)
+    assert info["kappa"][i] >= 66 and kap[0, 0, i] == info["kappa"][i]
+    _check(g, kap, mg, q, k, v, "e4m3", dict(p_mode="row"), "e4m3", "row", bias=bias)
+
+
 def test_variant_rejects_unbuilt_formats():
     import torch
     import softmax_mx_quantize_amd as fsa
@@ -271,10 +301,12 @@ def test_variant_full_size(name, fmt):
         rows = np.arange(n_q) * 128 + (np.arange(n_q) * 37 + h) % 128
         qh, kh, vh = (W.bf16_bits_to_f64(x[0, h]) for x in (q, k, v))
         ref, info = O.fused_attention(qh, kh, vh, fmt, False, rows=rows, return_info=True, **okw)
-        ex, n_allow = excess_rel_l2(g[0, h, rows], ref, info, pfmt, eps_rows(mg[0, h, rows], info, fmt), mode)
+        codes = _borderline(info, rows, w.S, False, fmt, pfmt, mode)
+        ex, n_allow = excess_rel_l2(g[0, h, rows], ref, info, pfmt, eps_rows(mg[0, h, rows], info, fmt), mode,
+                                    skip=undecided(codes, kap[0, h, rows], info["kappa"]))
         print("%s-%s head %d: rel L2 %.2e, beyond near-tie codes %.2e" % (name, fmt, h, rel_l2(g[0, h, rows], ref), ex))
         assert ex <= TOL, (h, ex)
-        check_kappa(kap[0, h, rows], info["kappa"], _borderline(info, rows, w.S, False, fmt, pfmt, mode))
+        check_kappa(kap[0, h, rows], info["kappa"], codes)
 
     def errs(h):
         rows = np.sort(np.random.default_rng([91, h]).choice(w.S, 256, replace=False))
