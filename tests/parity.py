@@ -146,10 +146,25 @@ def tie_allowance(info, fmt, out_ref, eps_x, mode="block"):
     return np.where(num > 0, num / np.maximum(den, 1e-300), 0.0)
 
 
-def excess_rel_l2(gpu_rows, ref_rows, info, fmt, eps_x, mode="block"):
+def excess_rel_l2(gpu_rows, ref_rows, info, fmt, eps_x, mode="block", skip=None):
     """Relative L2 of the part of the difference that near-tie codes cannot
-    explain; also returns the number of rows that got an allowance."""
+    explain; also returns the number of rows that got an allowance.  Rows
+    in ``skip`` (undecided(): the kernel took the other side of a fallback
+    threshold that the row sits on) are not compared."""
     allow = tie_allowance(info, fmt, ref_rows, eps_x, mode)
     d = np.linalg.norm(np.asarray(gpu_rows) - np.asarray(ref_rows), axis=-1)
     ex = np.maximum(0.0, d - allow)
+    if skip is not None:
+        ex = np.where(np.asarray(skip), 0.0, ex)
     return float(np.linalg.norm(ex) / np.linalg.norm(ref_rows)), int(np.count_nonzero(allow))
+
+
+def undecided(codes, gpu_kap, ref_kap):
+    """Rows left free at a fallback threshold (kappa_rows code 2) on which the
+    kernel and the oracle took different sides.  Whether such a row falls
+    back at all hangs on a rounding tie within the kernel's own score error
+    (with one scale per row: whether its top value rounds to the smallest
+    subnormal code or to zero), and the two sides give different outputs,
+    each right for its decision; such rows are compared on neither."""
+    codes = np.asarray(codes).astype(np.int8)
+    return ((codes & 2) != 0) & (np.asarray(gpu_kap) != np.asarray(ref_kap))

@@ -150,3 +150,13 @@ def test_score_errors_within_their_bound_are_absorbed():
     assert ex <= 1e-3 * plain, (ex, plain)
     ex0, _ = excess_rel_l2(k_out, out, info, fmt, EPS_PLACE)
     assert ex0 >= 0.1 * plain, (ex0, plain)
+
+
+def test_undecided_rows_are_free_rows_with_different_offsets():
+    """Only rows left free at a threshold (code 2, also with the borderline
+    bit) whose offsets differ between the two sides escape the comparison."""
+    from parity import undecided
+    codes = np.array([0, 2, 2, 3, 1, 0])
+    gpu = np.array([0, 0, 5, 1, 2, 4])
+    ref = np.array([0, 0, 0, 0, 1, 0])
+    assert undecided(codes, gpu, ref).tolist() == [False, False, True, True, False, False]
