@@ -22,7 +22,8 @@ more cover the public MX quantiser (random ragged shapes, per-row binade
 spreads, both block axes: bit for bit) and the BF16 baseline (random shapes
 against exact attention); a last one checks the attention path's own
 operands (Q'^ from the prologue, K^ and V^T with their tile-ordered scales)
-bit for bit over random shapes.
+bit for bit over random shapes.  A wide sweep reruns the shape, variant,
+extreme and clustered generators with five more seeds (1,600 cases).
 """
 
 import numpy as np
@@ -416,3 +417,26 @@ def test_operands_shapes_bit_exact(case):
     for b in range(B):
         for h in range(H):
             _check_head(got, *(W.bf16_bits_to_f64(x[b, h]) for x in (q, k, v)), fmt, b, h)
+
+
+# Wider runs of the same generators: five more seeds, each generator's cases
+# run in one test item (so that a failure names every case that failed).
+WIDE_SEEDS = [7000, 9000, 11000, 13000, 15000]
+WIDE = [("mixed", lambda sd: _cases(n=120, seed=sd), test_mixed_shapes_all_rows, _id),
+        ("variants", lambda sd: _variant_cases(per=10, seed=sd + 1), test_variant_mixed_shapes_all_rows, _vid),
+        ("extreme", lambda sd: _extreme_cases(n=60, seed=sd + 2), test_extreme_score_spreads_all_rows, _xid),
+        ("clustered", lambda sd: _cluster_cases(n=60, seed=sd + 3), test_clustered_keys_all_rows, _tid)]
+
+
+@pytest.mark.parametrize("seed", WIDE_SEEDS)
+@pytest.mark.parametrize("gen", WIDE, ids=[g[0] for g in WIDE])
+def test_wide_sweep(gen, seed):
+    name, make, run, idf = gen
+    failed = []
+    for c in make(seed):
+        try:
+            run(c)
+        except AssertionError as e:
+            failed.append((idf(c), str(e)[:120]))
+    announce("wide sweep", name, seed, "failed:", len(failed))
+    assert not failed, failed
