@@ -130,7 +130,22 @@ def tie_allowance(info, fmt, out_ref, eps_x, mode="block"):
     tied_el = np.repeat(tied, 32, axis=1)[:, :S] & vis
     if mode == "row":
         tied_el[:] = False                                # no block shifts
-    step = np.where(near, q, 0.0) + np.where(tied_el, 2.0 * q, 0.0)
+    if mode == "efq":
+        # a block one binade up or down moves x by -1 or +1 under twice or
+        # half the scale: the element's value in this block's units becomes
+        # 2 v(x - 1) or v(x + 1) / 2 (clamped codes included, which no code
+        # tie covers)
+        from oracle import decode
+
+        def aff(xx):
+            with np.errstate(invalid="ignore"):
+                cc = np.rint(2.0 ** M * (xx + f.bias))
+            return decode(np.clip(np.where(np.isfinite(cc), cc, 0.0), 0, f.max_code).astype(np.int64), f)
+        v0 = aff(x)
+        tstep = np.maximum(np.abs(2.0 * aff(x - 1.0) - v0), np.abs(0.5 * aff(x + 1.0) - v0))
+    else:
+        tstep = 2.0 * q
+    step = np.where(near, q, 0.0) + np.where(tied_el, tstep, 0.0)
     step = step * np.ldexp(1.0, (-pl - dfull).astype(np.int64))
     # A set of flips delta_j (|delta_j| <= step_j) moves the row to
     # (O + sum delta_j v_j) / (l + sum delta_j), i.e. by

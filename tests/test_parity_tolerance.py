@@ -100,8 +100,8 @@ def test_code_moved_away_from_ties_is_not_absorbed(fmt):
     assert ex > 0.0
 
 
-@pytest.mark.parametrize("fmt", FMTS)
-def test_block_moved_across_its_binade_tie_is_absorbed(fmt):
+@pytest.mark.parametrize("fmt,mode", [(f, "block") for f in FMTS] + [("e2m1", "efq")])
+def test_block_moved_across_its_binade_tie_is_absorbed(fmt, mode):
     """Each row's largest block has its largest value delta/2 above the tie
     that decides its binade, below the guess (so every row's offset stays
     0): a kernel with t lower by delta puts that whole block one binade lower
@@ -115,19 +115,45 @@ def test_block_moved_across_its_binade_tie_is_absorbed(fmt):
     t_tie = -1.0 - 2.0 ** -(M + 1)                 # binade -1 rounds up to 0 above this
     m = s.max(axis=1) - (t_tie + delta / 2)        # the row's largest score at the tie
     top = s.reshape(R, S // 32, 32).max(axis=2).argmax(axis=1)
-    fp = fused_probabilities(s, m, vis, fmt)
+    fp = fused_probabilities(s, m, vis, fmt, mode=mode)
     assert np.all(fp["kappa"] == 0)
     P = fp["P"]
     info = dict(fp)
     info.update(m_tilde=m, l=P.sum(axis=1), scores=s, v_hat=vh, visible=vis)
     out = P @ vh / info["l"][:, None]
-    kp = fused_probabilities(s, m + delta, vis, fmt)
+    kp = fused_probabilities(s, m + delta, vis, fmt, mode=mode)
     rr = np.arange(R)
     assert np.all(kp["delta"][rr, top] == fp["delta"][rr, top] + 1)   # the top blocks moved
     k_out = kp["P"] @ vh / kp["P"].sum(axis=1)[:, None]
     plain = O.rel_l2(k_out, out)
-    ex, _ = excess_rel_l2(k_out, out, info, fmt, EPS)
+    ex, _ = excess_rel_l2(k_out, out, info, fmt, EPS, mode)
     assert plain > 0.0 and ex <= 1e-3 * plain, (ex, plain)
+
+
+def test_affine_block_moved_across_its_binade_tie_is_absorbed():
+    """Affine E2M1 codes: one block whose largest score sits delta/2 below
+    its binade tie, where its code is the clamped top one (no code tie to
+    explain a change), its other scores away from any code tie.  A kernel
+    with t higher by delta moves the whole block one binade up (its codes two
+    steps down the affine line, under twice the scale); the allowance's
+    tied-block term must cover it."""
+    delta = 0.8 * EPS
+    t = np.array([-1.25 - delta / 2, -1.6, -2.1, -3.3, -2.45, -1.9, -4.05, -2.8])
+    s = np.concatenate([t, np.full(24, -9.3)])[None, :]
+    vis = np.ones_like(s, bool)
+    m = np.zeros(1)
+    vh = np.random.default_rng(5).standard_normal((32, 16))
+    fp = fused_probabilities(s, m, vis, "e2m1", mode="efq")
+    kp = fused_probabilities(s, m - delta, vis, "e2m1", mode="efq")
+    assert fp["kappa"][0] == 0 and kp["delta"][0, 0] == fp["delta"][0, 0] - 1
+    assert fp["codes"][0, 0] == 7
+    info = dict(fp)
+    info.update(m_tilde=m, l=fp["P"].sum(axis=1), scores=s, v_hat=vh, visible=vis)
+    out = fp["P"] @ vh / info["l"][:, None]
+    k_out = kp["P"] @ vh / kp["P"].sum(axis=1)[:, None]
+    plain = O.rel_l2(k_out, out)
+    ex, _ = excess_rel_l2(k_out, out, info, "e2m1", EPS, "efq")
+    assert plain > 1e-2 and ex <= 1e-3 * plain, (ex, plain)
 
 
 def test_score_errors_within_their_bound_are_absorbed():
