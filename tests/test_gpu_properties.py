@@ -6,6 +6,8 @@ the library's own output rather than the oracle:
   output scales by the same power exactly (while no value leaves bf16's
   normal range and the fp32 sums stay finite), also for rows shifted within
   the sweep or re-based by the fallback pass;
+* Q scaled by 2^a and K by 2^-a: the codes stay, the block scales move in
+  opposite directions, so every score and result stays the same;
 * V's columns permuted: each output column is the product of P~ with one
   column of V (V is quantised along the keys, column by column), so the
   output's columns follow;
@@ -89,6 +91,23 @@ def test_v_scaled_through_the_fallbacks(case):
             g, kap, mg = _call(q, k, _scaled_bits(v, e), name, fmt, guess_bias=bias)
             _same(g, g0 * 2.0 ** e)
             assert np.array_equal(kap, k0) and np.array_equal(mg, m0)
+
+
+@pytest.mark.parametrize("case", CASES, ids=IDS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_q_and_k_scaled_reciprocally(case, causal):
+    """Q times 2^a and K times 2^-a: both keep their MX codes (Q's softmax
+    scale is applied before its rounding, and a power of two commutes with
+    it), their block scales move by a and -a, and every score, frozen max,
+    offset and output stays the same bit for bit."""
+    name, fmt = case
+    announce("property: Q * 2^a, K * 2^-a", name, fmt, causal)
+    q, k, v = (W.random_bf16((1, 2, 333, 128), seed, 1.0) for seed in (144, 145, 146))
+    g0, k0, m0 = _call(q, k, v, name, fmt, causal)
+    for a in (-40, 7, 40):
+        g, kap, mg = _call(_scaled_bits(q, a), _scaled_bits(k, -a), v, name, fmt, causal)
+        _same(g, g0)
+        assert np.array_equal(kap, k0) and np.array_equal(mg, m0)
 
 
 @pytest.mark.parametrize("case", CASES, ids=IDS)
