@@ -521,3 +521,20 @@ def test_e3m2_probabilities_keep_more_binades_with_coarser_steps():
     p5 = fused_probabilities(s, m, vis, "e3m2")["P"][0, : t.size]
     assert list(p6) == [1.0, 0.9375, 0.0, 0.0, 0.0, 0.25]
     assert list(p5) == [1.0, 1.0, 2.0 ** -6, 0.0, 2.0 ** -8, 0.25]
+
+
+def test_error_criterion_on_clustered_keys():
+    """Keys in two opposite clusters put the extreme-value guess far above
+    every row, where the cap holds it 64 binades over the window max: the
+    rows are placed by block shifts alone, and the fused error stays within
+    1.1x the plain quantised path's on every head and format."""
+    q, k, v = W.two_valued_keys(1, 2, 512, 128, seed=3)
+    rows = np.arange(0, 512, 8)
+    for fmt in FMTS:
+        for h in range(2):
+            qh, kh, vh = (W.bf16_bits_to_f64(x[0, h]) for x in (q, k, v))
+            exa = O.exact_attention(qh, kh, vh, rows=rows)
+            fu, info = O.fused_attention(qh, kh, vh, fmt, rows=rows, return_info=True)
+            pl = O.plain_mx_attention(qh, kh, vh, fmt, rows=rows)
+            assert np.all(info["kappa"] == 0)
+            assert rel_l2(fu, exa) <= 1.1 * rel_l2(pl, exa), (fmt, h)
