@@ -148,25 +148,31 @@ def write_traffic(fetch_db: str, write_db: str, copy_bytes: int) -> dict:
 
 
 def time_fsa(fsa, torch, q, k, v, fmt, steps, warmup, causal=False, **kw):
-    """Whole-step time (ms) and fused-kernel time (ms, from HIP events on the
-    stream the library launches on: recorded by the library between the
-    quantisation and the attention kernels, and after the call)."""
+    """Whole-step time (ms) and fused-kernel time (ms).  The whole steps run
+    back to back with nothing between them; the kernel time comes from a
+    second run of the same steps with HIP events on the stream the library
+    launches on (recorded by the library between the quantisation and the
+    attention kernels, and after the call), because each timing event
+    leaves the GPU idle for a few microseconds."""
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         fsa.attention_fwd(q, k, v, fmt, causal, out=out, **kw)
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fsa.attention_fwd(q, k, v, fmt, causal, out=out, **kw)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     mids = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     for m in mids:          # create the underlying HIP events before the library records them
         m.record(stream)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(steps):
         fsa.attention_fwd(q, k, v, fmt, causal, out=out, event_after_quantize=mids[i], **kw)
         ends[i].record(stream)
     torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     kern_ms = sum(m.elapsed_time(e) for m, e in zip(mids, ends)) / steps
     return wall_ms, kern_ms, out
 
