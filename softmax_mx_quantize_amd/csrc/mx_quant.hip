@@ -24,16 +24,27 @@
 
 namespace fsa {
 
-// Quantise one block of 32 values (already multiplied by a.mult) and write
-// its codes and scale byte: slab w, output row r, block b.
+// The block's largest magnitude and whether it holds NaN or Inf, from the
+// bf16 bit patterns alone: below the exponent field's top, magnitudes order
+// as their low 15 bits do, and a NaN or Inf element has those bits at
+// 0x7F80 or above.  Multiplying the largest magnitude by a.mult gives the
+// largest |x * mult| exactly (rounding is monotone), so the values need no
+// comparisons of their own.
+struct BlockMax {
+  uint32_t m = 0;
+  __device__ __forceinline__ void add(uint32_t bits) { m = max(m, bits & 0x7FFFu); }
+  __device__ __forceinline__ bool bad() const { return m >= 0x7F80u; }
+  __device__ __forceinline__ float amax(float mult) const { return bf16_bits_to_float(m) * mult; }
+};
+
+// Quantise one block of 32 values (already multiplied by a.mult) whose
+// largest magnitude is amax, and write its codes and scale byte: slab w,
+// output row r, block b.
 template <int F>
-__device__ __forceinline__ void quantize_block(const QuantArgs& a, float (&v)[32], bool bad,
+__device__ __forceinline__ void quantize_block(const QuantArgs& a, float (&v)[32], float amax, bool bad,
                                                int64_t w, int64_t r, int64_t b) {
   constexpr int BITS = Fmt<F>::bits;
   constexpr int OUT_BYTES = 4 * BITS;   // 32 elements
-  float amax = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 32; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j]));
   int X = amax > 0.0f ? floor_log2(amax) - Fmt<F>::emax : -127;
   X = X < -127 ? -127 : (X > 127 ? 127 : X);
   float y[32];
@@ -90,7 +101,7 @@ __global__ void __launch_bounds__(256) mx_quant_rows_kernel(QuantArgs a) {
   const int64_t o = t / a.nb_out;
   const int64_t b = t - o * a.nb_out;
   float v[32];
-  bool bad = false;
+  BlockMax bm;
   const int64_t w = o / a.out_rows;
   const int64_t r = o - w * a.out_rows;
   const int64_t c0 = b * 32;
@@ -105,7 +116,8 @@ __global__ void __launch_bounds__(256) mx_quant_rows_kernel(QuantArgs a) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         uint32_t lo = wq[k] & 0xFFFF, hi = wq[k] >> 16;
-        bad |= ((lo & 0x7F80) == 0x7F80) | ((hi & 0x7F80) == 0x7F80);
+        bm.add(lo);
+        bm.add(hi);
         v[8 * i + 2 * k] = bf16_bits_to_float(lo) * a.mult;
         v[8 * i + 2 * k + 1] = bf16_bits_to_float(hi) * a.mult;
       }
@@ -115,13 +127,15 @@ __global__ void __launch_bounds__(256) mx_quant_rows_kernel(QuantArgs a) {
     for (int j = 0; j < 32; ++j) {
       uint32_t bits = 0;
       if (row_ok && c0 + j < a.cols) bits = src[j];
-      bad |= (bits & 0x7F80) == 0x7F80;
+      bm.add(bits);
       v[j] = bf16_bits_to_float(bits) * a.mult;
     }
   }
+  const bool bad = bm.bad();
   if (bad && a.nan_key) atomicMin(reinterpret_cast<unsigned long long*>(a.nan_key + w), (unsigned long long)r);
   const int f = (FSET & (FSET - 1)) ? a.fmt[w % a.nh] : 0;
-  with_format<FSET>(f, [&](auto F) { quantize_block<decltype(F)::value>(a, v, bad, w, r, b); });
+  const float amax = bm.amax(a.mult);
+  with_format<FSET>(f, [&](auto F) { quantize_block<decltype(F)::value>(a, v, amax, bad, w, r, b); });
 }
 
 // Columns mode: blocks run along the row axis and the output is transposed.
@@ -166,15 +180,17 @@ __global__ void __launch_bounds__(128) mx_quant_cols_kernel(QuantArgs a) {
   const int64_t b = (int64_t)blockIdx.x * (QC_ROWS / 32) + kb;
   if (col >= a.cols || b >= a.nb_out) return;
   float v[32];
-  bool bad = false;
+  BlockMax bm;
 #pragma unroll
   for (int j = 0; j < 32; ++j) {
     const uint32_t bits = tile[32 * kb + j][cc];
-    bad |= (bits & 0x7F80) == 0x7F80;
+    bm.add(bits);
     v[j] = bf16_bits_to_float(bits) * a.mult;
   }
+  const bool bad = bm.bad();
+  const float amax = bm.amax(a.mult);
   const int f = (FSET & (FSET - 1)) ? a.fmt[w % a.nh] : 0;
-  with_format<FSET>(f, [&](auto F) { quantize_block<decltype(F)::value>(a, v, bad, w, col, b); });
+  with_format<FSET>(f, [&](auto F) { quantize_block<decltype(F)::value>(a, v, amax, bad, w, col, b); });
 }
 
 template <int FSET>
