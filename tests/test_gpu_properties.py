@@ -16,6 +16,8 @@ the library's own output rather than the oracle:
   wherever it sits in the tiles, with or without the fallback pass;
 * a head placed anywhere in a larger call (other heads of other formats
   around it) gives the result it gives alone;
+* with the causal mask, rows before a whole V block do not depend on the
+  keys from that block on;
 * with the causal mask, row i for i + 1 a multiple of 32 sees exactly the
   problem truncated to its first i + 1 keys (the same V blocks along the
   keys, the same frozen-max window), so it equals the last row of that
@@ -154,6 +156,28 @@ def test_head_placed_in_a_larger_hybrid_call():
                 g1, k1, m1 = _run(*one, fmts[h], causal)
                 _same(g[b, h], g1[0, 0])
                 assert np.array_equal(kap[b, h], k1[0, 0]) and np.array_equal(mg[b, h], m1[0, 0])
+
+
+@pytest.mark.parametrize("case", CASES, ids=IDS)
+def test_causal_rows_ignore_later_key_blocks(case):
+    """With the causal mask, rows before key 160 (five whole 32-key blocks of
+    V) cannot see keys 160 on: replacing those keys' K and V with far larger
+    values leaves every such row's output, offset and frozen max unchanged,
+    also with every row sent through the fallback pass."""
+    name, fmt = case
+    announce("property: causal rows ignore later keys", name, fmt)
+    S, cut = 333, 160
+    q, k, v = (W.random_bf16((1, 2, S, 128), seed, 1.0) for seed in (147, 148, 149))
+    k2, v2 = (x.copy() for x in (k, v))
+    k2[:, :, cut:] = W.random_bf16((1, 2, S - cut, 128), 150, 5.0)
+    v2[:, :, cut:] = W.random_bf16((1, 2, S - cut, 128), 151, 50.0)
+    for bias in (0.0, -100.0):
+        g0, k0, m0 = _call(q, k, v, name, fmt, True, guess_bias=bias)
+        g, kap, mg = _call(q, k2, v2, name, fmt, True, guess_bias=bias)
+        _same(g[:, :, :cut], g0[:, :, :cut])
+        assert np.array_equal(kap[:, :, :cut], k0[:, :, :cut])
+        assert np.array_equal(mg[:, :, :cut], m0[:, :, :cut])
+        assert not np.array_equal(g[:, :, cut:], g0[:, :, cut:])
 
 
 @pytest.mark.parametrize("case", CASES, ids=IDS)
