@@ -244,6 +244,15 @@ def test_strided_layouts_all_rows(case):
     assert o.data_ptr() == out.data_ptr()
     g = from_dev_bf16(o.contiguous())
     _check(g, kap.cpu().numpy(), mg.cpu().numpy(), *_oracle_heads(q, k, v, list(fmts), causal))
+    # the views change addressing only: the contiguous call gives the same bits
+    from gpu_helpers import to_dev
+    oc, kc, mc = fsa.attention_fwd(to_dev(q), to_dev(k), to_dev(v), fmts[0], causal, head_fmt=list(fmts),
+                                   return_rows=True)
+    torch.cuda.synchronize()
+    gc = from_dev_bf16(oc)
+    assert np.array_equal(g, gc) or np.array_equal(np.isnan(g), np.isnan(gc)) and np.array_equal(
+        np.nan_to_num(g), np.nan_to_num(gc))
+    assert np.array_equal(kap.cpu().numpy(), kc.cpu().numpy()) and np.array_equal(mg.cpu().numpy(), mc.cpu().numpy())
 
 
 def _noalloc_cases(n=24, seed=2028):
