@@ -5,7 +5,7 @@ import sys
 import numpy as np
 
 import workloads as W
-from parity import score_eps
+from parity import frozen_max_tol
 
 
 def announce(*what):
@@ -82,23 +82,10 @@ def kappa_low(pfmt, mode):
 
 
 def check_frozen_max(gpu_m_tilde, info, fmt=None):
-    """The kernel's frozen max against the oracle's.  It is mean + z std (or
-    the window's max, or that max plus the 64-binade cap) evaluated in fp32
-    from the kernel's scores, so its error follows the magnitude of the
-    window's scores, not of the guess itself (which can be near zero: two
-    keys at -1.7 and -4.3).  With the operand format ``fmt``, each score
-    also carries its product's own error (tests/parity.py, score_eps); the
-    max, the mean and the spread each move by at most the window's largest,
-    so the guess by at most 1 + z of it."""
-    win = info["visible"][:, :128]
-    mag = np.max(np.where(win, np.abs(info["scores"][:, :128]), 0.0), axis=1)
+    """The kernel's frozen max against the oracle's, within frozen_max_tol
+    (tests/parity.py)."""
     dm = np.abs(np.asarray(gpu_m_tilde, np.float64) - info["m_tilde"])
-    tol = 1e-4 * np.maximum(1.0, np.maximum(np.abs(info["m_tilde"]), mag))
-    se = 0.0 if fmt is None else score_eps(info, fmt)
-    if not np.isscalar(se):
-        n_vis = np.maximum(info["visible"].sum(axis=1), 1)
-        z = np.sqrt(2.0 * np.log(n_vis)) + 1.0
-        tol = tol + (1.0 + z) * np.max(np.where(win, se[:, :128], 0.0), axis=1)
+    tol = frozen_max_tol(info, fmt)
     assert np.all(dm <= tol), (float(dm.max()), int(np.argmax(dm - tol)))
 
 

@@ -12,7 +12,8 @@ draws the same kinds of shapes for each P~ variant (one format per call); a
 third draws extreme score spreads (input scales 0.05 to 6: nearly uniform
 rows up to rows whose scores spread over a hundred binades) in every map,
 and another keys in two opposite clusters (the guess's extreme-value term
-far above the rows and held by its cap; workloads.two_valued_keys); a
+far above the rows and held by its cap; workloads.two_valued_keys), and
+another the workload recipes' heavy-tailed keys and planted outliers; a
 fourth passes each of q, k, v and out in its own layout (contiguous
 [B, H, S, D], a [B, S, H, D] tensor viewed as [B, H, S, D], or rows padded
 to a longer stride); a fifth compares the allocation-free entry point with
@@ -183,6 +184,47 @@ def test_clustered_keys_all_rows(case):
                                 period=period)
     g, kap, mg = _vrun(q, k, v, fmt, name, causal, guess_bias=bias)
     _vcheck(g, kap, mg, q, k, v, fmt, okw, pfmt, mode, causal, bias=bias)
+
+
+def _heavy_cases(n=24, seed=2033):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        H = int(rng.integers(1, 4))
+        S = int(rng.integers(100, 1501))
+        D = int(rng.choice([64, 128]))
+        causal = bool(rng.integers(0, 2))
+        fmts = tuple(FMTS[int(j)] for j in rng.integers(0, 3, size=H))
+        w = W.Workload("heavy", 1, H, S, D, causal, int(rng.integers(0, 1 << 30)), fmts,
+                       gain_range=(float(rng.uniform(0.3, 1.0)), float(rng.uniform(1.0, 3.0))),
+                       outlier_frac=float(rng.choice([0.0, 0.02, 0.1])),
+                       outlier_sigma=float(rng.choice([8.0, 20.0, 60.0])),
+                       heavy_frac=float(rng.choice([0.0, 0.05, 0.3])),
+                       heavy_nu=float(rng.choice([1.5, 2.5, 4.0])))
+        out.append((i, w))
+    return out
+
+
+HCASES = _heavy_cases()
+
+
+def _hid(c):
+    i, w = c
+    return "h%02d-H%dS%dD%d%s-%s-out%g@%g-heavy%g@nu%g" % (
+        i, w.H, w.S, w.D, "-causal" if w.causal else "", "+".join(w.head_fmts), w.outlier_frac,
+        w.outlier_sigma, w.heavy_frac, w.heavy_nu)
+
+
+@pytest.mark.parametrize("case", HCASES, ids=[_hid(c) for c in HCASES])
+def test_heavy_tails_and_outliers_all_rows(case):
+    """The workload recipes' heavy-tailed keys (Student-t down to 1.5 degrees
+    of freedom: scores thousands of binades apart) and planted outlier scores
+    (8 to 60 sigma), at small sizes, per-head formats in one launch."""
+    i, w = case
+    announce("fsa heavy-tail sweep", _hid(case))
+    q, k, v = W.generate(w)
+    g, kap, mg = _run(q, k, v, w.head_fmts[0], w.causal, head_fmt=list(w.head_fmts))
+    _check(g, kap, mg, *_oracle_heads(q, k, v, list(w.head_fmts), w.causal))
 
 
 LAYOUTS = ["bhsd", "bshd", "pad8", "pad16"]

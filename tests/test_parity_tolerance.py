@@ -158,8 +158,9 @@ def test_affine_block_moved_across_its_binade_tie_is_absorbed():
 
 def test_score_errors_within_their_bound_are_absorbed():
     """A simulated FP8 kernel whose every score is off by +-0.8 of its bound
-    (SCORE_REL times sum_d |q'^_d k^_d|): the per-element margin absorbs the
-    flips this causes; the per-row EPS_PLACE alone does not."""
+    (SCORE_REL times the score's largest product, score_eps): the
+    per-element margin absorbs the flips this causes; the per-row EPS_PLACE
+    alone does not."""
     fmt = "e4m3"
     q, k, v = (W.random_bf16((1, 1, 512, 64), 95 + i, 3.0) for i in range(3))
     qh, kh, vh = (W.bf16_bits_to_f64(x[0, 0]) for x in (q, k, v))
