@@ -208,5 +208,5 @@ def undecided(codes, gpu_kap, ref_kap):
     (with one scale per row: whether its top value rounds to the smallest
     subnormal code or to zero), and the two sides give different outputs,
     each right for its decision; such rows are compared on neither."""
-    codes = np.asarray(codes).astype(np.int8)
+    codes = np.asarray(codes).astype(np.int64)
     return ((codes & 2) != 0) & (np.asarray(gpu_kap) != np.asarray(ref_kap))

@@ -49,7 +49,7 @@ def _oracle_heads(q, k, v, fmts, causal=False, rows=None, bias=0.0):
             borders.append(kappa_rows(kappa_borderline(info["scores"], info["m_tilde"], rws, S, causal,
                                                        FORMATS[fmts[h]].mbits, ke,
                                                        low=kappa_low(fmts[h], "block")),
-                                      kappa_free(info, fmts[h], "block", ke)))
+                                      kappa_free(info, fmts[h], "block", ke), ke))
             infos.append((info, fmts[h]))
     return np.stack(outs), np.stack(kaps), np.stack(borders), infos
 
@@ -189,7 +189,7 @@ def test_causal_many_tiles_sampled(fmt):
         ke = kappa_eps(info, fmt)
         border = kappa_rows(kappa_borderline(info["scores"], info["m_tilde"], rows, S, True,
                                              FORMATS[fmt].mbits, ke, low=kappa_low(fmt, "block")),
-                            kappa_free(info, fmt, "block", ke))
+                            kappa_free(info, fmt, "block", ke), ke)
         skip = undecided(border, kap[0, h, rows], info["kappa"])
         assert excess_rel_l2(g[0, h, rows], ref, info, fmt, eps_rows(mg[0, h, rows], info, fmt),
                              skip=skip)[0] <= TOL

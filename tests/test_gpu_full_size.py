@@ -79,7 +79,7 @@ def test_one_row_of_every_query_tile(name, heads):
         ke = kappa_eps(info, fmt)
         border = kappa_rows(kappa_borderline(info["scores"], info["m_tilde"], rows, w.S, w.causal,
                                              FORMATS[fmt].mbits, ke, low=kappa_low(fmt, "block")),
-                            kappa_free(info, fmt, "block", ke))
+                            kappa_free(info, fmt, "block", ke), ke)
         # per row, the part of the difference near-tie codes cannot explain
         # (rows on which the two sides took the two sides of a threshold
         # they sit on are not compared)

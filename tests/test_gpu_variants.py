@@ -74,7 +74,7 @@ def _borderline(info, rows, S, causal, fmt, pfmt, mode):
         e = np.floor(np.log2(thr))
         t_over = e + thr / 2.0 ** e - 1.0 - O.attention.placement_exponent(pfmt)
         border |= np.abs(tmax - t_over) < eps
-    return kappa_rows(border, kappa_free(info, pfmt, mode, eps))
+    return kappa_rows(border, kappa_free(info, pfmt, mode, eps), eps)
 
 
 def _check(g, kap, mg, q, k, v, fmt, okw, pfmt, mode, causal=False, rows=None, bias=0.0):

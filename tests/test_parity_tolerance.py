@@ -187,3 +187,22 @@ def test_undecided_rows_are_free_rows_with_different_offsets():
     gpu = np.array([0, 0, 5, 1, 2, 4])
     ref = np.array([0, 0, 0, 0, 1, 0])
     assert undecided(codes, gpu, ref).tolist() == [False, False, True, True, False, False]
+
+
+def test_offset_slack_follows_the_row_margin():
+    """Borderline rows may differ by one, or by ceil(eps) where the margin
+    spans binades; free rows not at all checked; others exactly."""
+    from gpu_helpers import kappa_rows, check_kappa
+    border = np.array([True, True, False, True])
+    free = np.array([False, False, True, False])
+    eps = np.array([0.3, 2.5, 0.0, 1e-3])
+    codes = kappa_rows(border, free, eps)
+    ref = np.array([100, 7000, 5, 0])
+    check_kappa(ref + np.array([1, -3, 40, 1]), ref, codes)
+    for bad in ([2, 0, 0, 0], [0, 4, 0, 0], [0, 0, 0, 2]):
+        with pytest.raises(AssertionError):
+            check_kappa(ref + np.array(bad), ref, codes)
+    # a row that is neither borderline nor free must agree exactly
+    plain = kappa_rows(np.zeros(4, bool), np.zeros(4, bool))
+    with pytest.raises(AssertionError):
+        check_kappa(ref + np.array([0, 0, 1, 0]), ref, plain)
